@@ -1,0 +1,160 @@
+"""Score-gap enforcement for generated inputs -- TEST INFRASTRUCTURE ONLY.
+
+Bit-exact Top-K parity needs a unique selection that fp32 rounding cannot flip. For
+every checked query whose visible count exceeds K, the K-th and (K+1)-th highest float64
+scores a > b must satisfy  a - b > 1e-3 * max(|a|, |b|, mean|S|);  otherwise the query's
+gate (or, in the tiny workload, its indexer query and gate together) is redrawn from the
+seeded generator with the next attempt number. Scores come from the oracle only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import datagen
+
+from . import csa
+from .pipeline import f64, i64
+
+REL_GAP = 1e-3
+MAX_ATTEMPTS = 2000
+
+
+def gap_ok(scores: np.ndarray, K: int) -> bool:
+    """True when the K-th and (K+1)-th largest scores are separated by the required gap
+    (always true when there are at most K scores)."""
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    if n <= K:
+        return True
+    part = -np.partition(-s, (K - 1, K))
+    a, b = part[K - 1], part[K]
+    return (a - b) > REL_GAP * max(abs(a), abs(b), float(np.abs(s).mean()))
+
+
+def _fix_w(spec, R: np.ndarray, K: int, which: str, b: int, current) -> tuple[object, int]:
+    """Redraw a gate row until the scores R @ w have the gap at rank K."""
+    w = current
+    attempt = 0
+    while not gap_ok(R @ f64(w), K):
+        attempt += 1
+        if attempt > MAX_ATTEMPTS:
+            raise RuntimeError(f"no gap after {MAX_ATTEMPTS} redraws ({which}, row {b})")
+        w = datagen.redraw_w(spec, which, b, attempt)
+    return w, attempt
+
+
+def enforce_decode(case: dict, seqs=None) -> dict:
+    """Decode step inputs: fix w (flat) or w then w2 (hierarchical) per sequence."""
+    spec = case["spec"]
+    m, E = spec.m, spec.entries
+    pos = i64(case["pos"])
+    seqs = range(spec.B) if seqs is None else seqs
+    redraws = {}
+    bias_i = f64(case["bias_i"])
+    for b in seqs:
+        t = int(pos[b])
+        n = csa.n_visible(t, m, E)
+        keys = f64(case["k_idx"][b][:n]).copy()
+        if (t + 1) % m == 0:
+            xi = f64(case["xi_tail"][b]).copy()
+            zi = f64(case["zi_tail"][b]).copy()
+            xi[t % m] = f64(case["xi_new"][b])
+            zi[t % m] = f64(case["zi_new"][b])
+            e = (t + 1) // m - 1
+            if e < n:
+                keys[e] = csa.store(csa.compress(xi, zi, bias_i, m)[0], spec.dtype)
+        R = csa.head_relu(f64(case["q_idx"][b]), keys)
+        if spec.block_size > 0:
+            # stage 1: the block maxima must separate at rank max_blocks
+            def blocks_ok(w):
+                s = R @ f64(w)
+                return gap_ok(csa.block_maxima(s, spec.block_size), spec.max_blocks)
+            w = case["w"][b]
+            attempt = 0
+            while not blocks_ok(w):
+                attempt += 1
+                if attempt > MAX_ATTEMPTS:
+                    raise RuntimeError("no block gap")
+                w = datagen.redraw_w(spec, "w", b, attempt)
+            case["w"][b] = w
+            s1 = R @ f64(w)
+            pool = csa.candidate_pool(s1, spec.block_size, spec.max_blocks)
+            R2 = csa.head_relu(f64(case["q_idx2"][b]), keys[pool])
+            w2, a2 = _fix_w(spec, R2, spec.K, "w2", b, case["w2"][b])
+            case["w2"][b] = w2
+            redraws[b] = (attempt, a2)
+        else:
+            w, a = _fix_w(spec, R, spec.K, "w", b, case["w"][b])
+            case["w"][b] = w
+            redraws[b] = a
+    return redraws
+
+
+def enforce_rows(case: dict, rows, keys_for_row) -> dict:
+    """Per query row (b, i): fix w[b, i] so the visible scores separate at rank K.
+    ``keys_for_row(b, i)`` returns the float64 visible keys of that row."""
+    spec = case["spec"]
+    redraws = {}
+    for b, i in rows:
+        keys = keys_for_row(b, i)
+        R = csa.head_relu(f64(case["q_idx"][b, i]), keys)
+        row_id = b * 1_000_003 + i
+        w = case["w"][b, i]
+        attempt = 0
+        while not gap_ok(R @ f64(w), spec.K):
+            attempt += 1
+            if attempt > MAX_ATTEMPTS:
+                raise RuntimeError("no gap")
+            w = datagen.redraw_w(spec, "w", row_id, attempt)
+        case["w"][b, i] = w
+        redraws[(b, i)] = attempt
+    return redraws
+
+
+def enforce_prefill(case: dict, rows) -> dict:
+    """Chunked prefill: fix the gates of the checked query rows (keys include the chunk's
+    own pooled entries, computed by the oracle)."""
+    spec = case["spec"]
+    ki_c = csa.store(csa.compress(f64(case["xi_chunk"]), f64(case["zi_chunk"]),
+                                  f64(case["bias_i"]), spec.m), spec.dtype)
+    e0 = (spec.L - spec.chunk) // spec.m
+    qp = i64(case["q_pos"])
+    cache = {}
+
+    def keys_for_row(b, i):
+        if b not in cache:
+            k = f64(case["k_idx"][b]).copy()
+            k[e0:e0 + ki_c.shape[1]] = ki_c[b]
+            cache.clear()
+            cache[b] = k
+        n = csa.n_visible(int(qp[b, i]), spec.m, spec.entries)
+        return cache[b][:n]
+
+    return enforce_rows(case, rows, keys_for_row)
+
+
+def enforce_tiny(case: dict, rows=None) -> dict:
+    """Tiny workload: redraw (q_idx row, w row) jointly until the gap holds (with 4 heads an
+    all-zero tie among entries cannot be split by the gate alone)."""
+    spec = case["spec"]
+    qp = i64(case["q_pos"])
+    B, Q = qp.shape
+    rows = rows if rows is not None else [(b, i) for b in range(B) for i in range(Q)]
+    redraws = {}
+    E = spec.L // spec.m
+    for b, i in rows:
+        n = csa.n_visible(int(qp[b, i]), spec.m, E)
+        if n <= spec.K:
+            continue
+        keys = f64(case["k_idx"][b][:n])
+        attempt = 0
+        q, w = case["q_idx"][b, i], case["w"][b, i]
+        while not gap_ok(csa.index_scores(f64(q), f64(w), keys), spec.K):
+            attempt += 1
+            if attempt > MAX_ATTEMPTS:
+                raise RuntimeError("no gap")
+            q, w = datagen.redraw_qw(spec, b * 1_000_003 + i, attempt)
+        case["q_idx"][b, i] = q
+        case["w"][b, i] = w
+        redraws[(b, i)] = attempt
+    return redraws

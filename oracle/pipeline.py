@@ -1,0 +1,244 @@
+"""Row-by-row oracle drivers for the library calls -- TEST INFRASTRUCTURE ONLY.
+
+Each driver loops over sequences and queries and applies the float64 primitives of
+``oracle.csa`` in the order the pages describe: compress -> visibility -> index score
+-> Top-K (or block pre-select -> pool rescoring -> Top-K) -> sparse attention with sink.
+Inputs may be torch CPU tensors or NumPy arrays; they are upcast exactly to float64.
+Sources as in ``oracle.csa``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import csa
+
+
+def f64(a) -> np.ndarray:
+    """Exact upcast of a bf16/fp32 torch tensor or array to a float64 NumPy array."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return a.detach().to("cpu").to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(a, dtype=np.float64)
+
+
+def i64(a) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return a.detach().to("cpu").to(torch.int64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(a, dtype=np.int64)
+
+
+def take_rows(a, ids) -> np.ndarray:
+    """Rows ``a[ids]`` of a torch tensor or array, upcast exactly to float64."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return f64(a[torch.as_tensor(np.asarray(ids, dtype=np.int64))])
+    except ImportError:  # pragma: no cover
+        pass
+    return f64(np.asarray(a)[np.asarray(ids, dtype=np.int64)])
+
+
+def compress(x, z, bias, m: int, dtype: str) -> np.ndarray:
+    """csa_compress: pooled entries rounded to the storage dtype."""
+    return csa.store(csa.compress(f64(x), f64(z), f64(bias), m), dtype)
+
+
+def index_topk_row(q_idx, w, k_idx, t: int, m: int, e_count: int, K: int, cand=None):
+    """One query row of csa_index_topk. Returns (ids ascending -1 padded, float64 scores of
+    the scored candidates, candidate ids scored)."""
+    n = csa.n_visible(t, m, e_count)
+    if cand is None:
+        ids = np.arange(n, dtype=np.int64)
+    else:
+        c = i64(cand)
+        ids = c[(c >= 0) & (c < n)]
+    keys = f64(k_idx)[ids] if ids.size else np.zeros((0, np.asarray(k_idx).shape[-1]))
+    s = csa.index_scores(f64(q_idx), f64(w), keys) if ids.size else np.zeros(0)
+    return csa.select_topk(s, K, index=ids), s, ids
+
+
+def index_topk(q_idx, w, k_idx, q_pos, e_count, m: int, K: int, rows=None, cand=None):
+    """csa_index_topk over (sequence, query) rows. q_idx [B,Q,H_I,d_I], w [B,Q,H_I],
+    k_idx [B,E,d_I], q_pos [B,Q], e_count [B] or None, cand [B,Q,n_cand] or None.
+    ``rows``: optional list of (b, i) to evaluate (default all). Returns dict (b,i) -> ids."""
+    qp = i64(q_pos)
+    B, Q = qp.shape
+    E = k_idx.shape[1]
+    ec = i64(e_count) if e_count is not None else np.full(B, E)
+    rows = rows if rows is not None else [(b, i) for b in range(B) for i in range(Q)]
+    res = {}
+    keys_cache = {}
+    for b, i in rows:
+        if b not in keys_cache:
+            keys_cache = {b: f64(k_idx[b])}
+        c = None if cand is None else cand[b, i]
+        res[(b, i)] = index_topk_row(q_idx[b, i], w[b, i], keys_cache[b], int(qp[b, i]), m,
+                                     int(min(ec[b], E)), K, cand=c)
+    return res
+
+
+def index_blocks_row(q_idx, w, k_idx, t: int, m: int, e_count: int, block_size: int,
+                     max_blocks: int):
+    """One query row of csa_index_blocks: the candidate pool (ascending ids) and the
+    stage-1 scores of the visible entries."""
+    n = csa.n_visible(t, m, e_count)
+    keys = f64(k_idx)[:n]
+    s = csa.index_scores(f64(q_idx), f64(w), keys)
+    return csa.candidate_pool(s, block_size, max_blocks), s
+
+
+def attend_row(q, kv, idx, ring, w_cap: int, window: int, t: int, sink, scale: float):
+    """One query row of csa_sparse_attn (float64, unrounded)."""
+    rows = csa.attention_rows(kv, idx, ring, w_cap, window, t)
+    return csa.sink_attention(f64(q), rows, None if sink is None else f64(sink), scale)
+
+
+def sparse_attn(q, kv, idx, ring, w_cap, window, q_pos, sink, scale, dtype, rows=None):
+    """csa_sparse_attn over rows (b, i); returns dict (b, i) -> stored output [H, D]."""
+    qp = i64(q_pos)
+    B, Q = qp.shape
+    idx = i64(idx)
+    rows = rows if rows is not None else [(b, i) for b in range(B) for i in range(Q)]
+    out = {}
+    for b, i in rows:
+        sel = idx[b, i]
+        sel = sel[sel >= 0]
+        kvr = np.zeros((0, kv.shape[-1])) if sel.size == 0 else take_rows(kv[b], sel)
+        # attention_rows indexes kv by id: pass the gathered rows with local ids
+        o = attend_row(q[b, i], kvr, np.arange(sel.size), f64(ring[b]), w_cap, window,
+                       int(qp[b, i]), sink, scale)
+        out[(b, i)] = csa.store(o, dtype)
+    return out
+
+
+def decode_step(case: dict, seqs=None) -> dict:
+    """The fused decode step for one new token per sequence (oracle side).
+
+    Per sequence b at position t: the new rows enter the compressor tails at slot t % m
+    (and call 0's ring at row t % w_cap when its window rows are the raw main rows); if
+    the block is complete ((t+1) % m == 0) entry (t+1)/m - 1 is pooled from the tails for
+    both streams and stored; then the visible entries are scored, selected (directly, or
+    through the block pre-select and pool rescoring), and every attention call attends to
+    the shared selection plus its own window and sink.
+    Returns a dict with per-sequence results (new entries, scores, pool, ids, outputs).
+    """
+    spec = case["spec"]
+    m, dt, E, K, W, wc = spec.m, spec.dtype, spec.entries, spec.K, spec.W, spec.w_cap
+    pos = i64(case["pos"])
+    seqs = list(range(spec.B)) if seqs is None else list(seqs)
+    ring_raw = spec.m > 1
+    res = {"ids": {}, "out": {}, "kv_new": {}, "ki_new": {}, "scores": {}, "pool": {},
+           "scores2": {}, "n_vis": {}}
+    bias, bias_i = f64(case["bias"]), f64(case["bias_i"])
+    for b in seqs:
+        t = int(pos[b])
+        slot = t % m
+        x_tail = f64(case["x_tail"][b]).copy()
+        z_tail = f64(case["z_tail"][b]).copy()
+        xi_tail = f64(case["xi_tail"][b]).copy()
+        zi_tail = f64(case["zi_tail"][b]).copy()
+        x_tail[slot] = f64(case["x_new"][b])
+        z_tail[slot] = f64(case["z_new"][b])
+        xi_tail[slot] = f64(case["xi_new"][b])
+        zi_tail[slot] = f64(case["zi_new"][b])
+        n_vis = csa.n_visible(t, m, E)
+        keys = f64(case["k_idx"][b][:n_vis]).copy()
+        new_e = None
+        if (t + 1) % m == 0:
+            new_e = (t + 1) // m - 1
+            kv_e = csa.store(csa.compress(x_tail, z_tail, bias, m)[0], dt)
+            ki_e = csa.store(csa.compress(xi_tail, zi_tail, bias_i, m)[0], dt)
+            res["kv_new"][b] = kv_e
+            res["ki_new"][b] = ki_e
+            if new_e < n_vis:
+                keys[new_e] = ki_e
+        res["n_vis"][b] = n_vis
+        s1 = csa.index_scores(f64(case["q_idx"][b]), f64(case["w"][b]), keys)
+        res["scores"][b] = s1
+        if spec.block_size > 0:
+            pool = csa.candidate_pool(s1, spec.block_size, spec.max_blocks)
+            s2 = csa.index_scores(f64(case["q_idx2"][b]), f64(case["w2"][b]), keys[pool])
+            ids = csa.select_topk(s2, K, index=pool)
+            res["pool"][b] = pool
+            res["scores2"][b] = s2
+        else:
+            ids = csa.select_topk(s1, K)
+        res["ids"][b] = ids
+        sel = ids[ids >= 0]
+        kv_rows = take_rows(case["kv"][b], sel) if sel.size else np.zeros((0, spec.D))
+        if new_e is not None:
+            kv_rows[sel == new_e] = res["kv_new"][b]
+        outs = []
+        for c in range(spec.n_attn):
+            ring = f64(case["rings"][c][b]).copy()
+            if c == 0 and ring_raw:
+                ring[t % wc] = f64(case["x_new"][b])
+            o = attend_row(case["q"][c][b], kv_rows, np.arange(sel.size), ring, wc, W, t,
+                           case["sink"][c], case["scale"])
+            outs.append(csa.store(o, dt))
+        res["out"][b] = outs
+    return res
+
+
+def prefill_entries(case: dict):
+    """Entries of a prefill chunk: pooled main entries and indexer keys (stored dtype)."""
+    spec = case["spec"]
+    kv_c = compress(case["x_chunk"], case["z_chunk"], case["bias"], spec.m, spec.dtype)
+    ki_c = compress(case["xi_chunk"], case["zi_chunk"], case["bias_i"], spec.m, spec.dtype)
+    return kv_c, ki_c
+
+
+def prefill_rows(case: dict, rows, kv_c=None, ki_c=None) -> dict:
+    """Chunked prefill, oracle side, for query rows (b, i): ids and stored outputs."""
+    spec = case["spec"]
+    if kv_c is None:
+        kv_c, ki_c = prefill_entries(case)
+    e0 = (spec.L - spec.chunk) // spec.m
+    qp = i64(case["q_pos"])
+    res = {"ids": {}, "out": {}, "scores": {}}
+    cache = {}
+    for b, i in rows:
+        if b not in cache:
+            kv = f64(case["kv"][b]).copy()
+            ki = f64(case["k_idx"][b]).copy()
+            kv[e0:e0 + kv_c.shape[1]] = kv_c[b]
+            ki[e0:e0 + ki_c.shape[1]] = ki_c[b]
+            cache = {b: (kv, ki)}
+        kv, ki = cache[b]
+        t = int(qp[b, i])
+        ids, s, _ = index_topk_row(case["q_idx"][b, i], case["w"][b, i], ki, t, spec.m,
+                                   spec.entries, spec.K)
+        o = attend_row(case["q"][b, i], kv, ids, f64(case["ring"][b]), spec.w_cap, spec.W, t,
+                       case["sink"], case["scale"])
+        res["ids"][(b, i)] = ids
+        res["scores"][(b, i)] = s
+        res["out"][(b, i)] = csa.store(o, spec.dtype)
+    return res
+
+
+def tiny_forward(case: dict, rows=None) -> dict:
+    """The tiny fp32 forward: compress the raw rows, then every query row (b, t) indexes,
+    selects and attends (window rows read from the raw rows themselves)."""
+    spec = case["spec"]
+    kv = compress(case["x"], case["z"], case["bias"], spec.m, spec.dtype)
+    qp = i64(case["q_pos"])
+    B, Q = qp.shape
+    rows = rows if rows is not None else [(b, i) for b in range(B) for i in range(Q)]
+    res = {"kv": kv, "ids": {}, "out": {}, "scores": {}}
+    for b, i in rows:
+        t = int(qp[b, i])
+        ids, s, _ = index_topk_row(case["q_idx"][b, i], case["w"][b, i], f64(case["k_idx"][b]),
+                                   t, spec.m, kv.shape[1], spec.K)
+        o = attend_row(case["q"][b, i], kv[b], ids, f64(case["x"][b]), spec.L, spec.W, t,
+                       case["sink"], case["scale"])
+        res["ids"][(b, i)] = ids
+        res["scores"][(b, i)] = s
+        res["out"][(b, i)] = csa.store(o, spec.dtype)
+    return res

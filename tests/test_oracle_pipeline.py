@@ -1,0 +1,177 @@
+"""Pins of the oracle drivers: the decode step, the prefill chunk and the tiny forward are
+compositions of the pinned primitives; causality and reduction invariants hold."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from oracle import csa, gaps, pipeline
+from oracle.pipeline import f64
+
+
+def small_decode(**kw):
+    base = dict(case_id=901, kind="decode", B=3, L=4096, m=4, H_I=8, d_I=16, H=4, D=32,
+                K=16, W=8, w_cap=16, ragged=True)
+    base.update(kw)
+    return datagen.make_case(datagen.CaseSpec(**base))
+
+
+def test_decode_step_new_entry_is_pooled_tail():
+    case = small_decode()
+    res = pipeline.decode_step(case)
+    spec = case["spec"]
+    for b in range(spec.B):
+        t = int(case["pos"][b])
+        if (t + 1) % spec.m:
+            assert b not in res["kv_new"]
+            continue
+        x = f64(case["x_tail"][b]).copy()
+        z = f64(case["z_tail"][b]).copy()
+        x[t % spec.m] = f64(case["x_new"][b])
+        z[t % spec.m] = f64(case["z_new"][b])
+        np.testing.assert_array_equal(
+            res["kv_new"][b], csa.round_bf16(csa.compress(x, z, f64(case["bias"]), spec.m)[0]))
+
+
+def test_decode_positions_cover_block_phases():
+    case = small_decode(B=8)
+    phases = {int(t) % 4 for t in case["pos"]}
+    assert len(phases) > 1 and 3 in phases     # seq 0 sits at L-1: block completes
+
+
+def test_decode_step_is_the_composition_of_primitives():
+    case = small_decode()
+    spec = case["spec"]
+    res = pipeline.decode_step(case)
+    for b in range(spec.B):
+        t = int(case["pos"][b])
+        n = csa.n_visible(t, spec.m, spec.entries)
+        keys = f64(case["k_idx"][b][:n]).copy()
+        kv = f64(case["kv"][b]).copy()
+        if b in res["ki_new"]:
+            e = (t + 1) // spec.m - 1
+            keys[e] = res["ki_new"][b]
+            kv[e] = res["kv_new"][b]
+        ids = csa.select_topk(csa.index_scores(f64(case["q_idx"][b]), f64(case["w"][b]), keys), spec.K)
+        assert res["ids"][b].tolist() == ids.tolist()
+        ring = f64(case["rings"][0][b]).copy()
+        ring[t % spec.w_cap] = f64(case["x_new"][b])
+        o = csa.sink_attention(f64(case["q"][0][b]),
+                               csa.attention_rows(kv, ids, ring, spec.w_cap, spec.W, t),
+                               f64(case["sink"][0]), case["scale"])
+        np.testing.assert_array_equal(res["out"][b][0], csa.round_bf16(o))
+
+
+def test_decode_step_ignores_invisible_entries_and_old_ring_rows():
+    case = small_decode()
+    spec = case["spec"]
+    base = pipeline.decode_step(case)
+    case2 = dict(case)
+    kv, ki = case["kv"].clone(), case["k_idx"].clone()
+    ring = case["rings"][0].clone()
+    for b in range(spec.B):
+        t = int(case["pos"][b])
+        n = csa.n_visible(t, spec.m, spec.entries)
+        e_new = (t + 1) // spec.m - 1 if (t + 1) % spec.m == 0 else n
+        kv[b, n:] = 50.0
+        ki[b, n:] = 50.0
+        if e_new < n:                      # the entry being completed is recomputed
+            kv[b, e_new] = -50.0
+            ki[b, e_new] = -50.0
+        for p in range(t - spec.w_cap + 1, t - spec.W + 1):
+            ring[b, p % spec.w_cap] = 77.0
+    case2.update(kv=kv, k_idx=ki, rings=[ring])
+    res = pipeline.decode_step(case2)
+    for b in range(spec.B):
+        assert res["ids"][b].tolist() == base["ids"][b].tolist()
+        np.testing.assert_array_equal(res["out"][b][0], base["out"][b][0])
+
+
+def test_hierarchical_with_full_budget_is_flat_with_second_query():
+    case = small_decode(case_id=902, m=1, L=300, block_size=4, max_blocks=100, n_attn=2,
+                        ragged=False)
+    spec = case["spec"]
+    res = pipeline.decode_step(case)
+    for b in range(spec.B):
+        n = res["n_vis"][b]
+        assert res["pool"][b].tolist() == list(range(n))
+        keys = f64(case["k_idx"][b][:n]).copy()
+        keys[n - 1] = res["ki_new"][b]
+        flat = csa.select_topk(csa.index_scores(f64(case["q_idx2"][b]), f64(case["w2"][b]), keys), spec.K)
+        assert res["ids"][b].tolist() == flat.tolist()
+        assert len(res["out"][b]) == 2
+
+
+def test_hierarchical_pool_is_budgeted():
+    case = small_decode(case_id=903, m=1, L=600, block_size=4, max_blocks=10, ragged=False)
+    res = pipeline.decode_step(case)
+    for b, pool in res["pool"].items():
+        assert pool.size == 40
+        assert set(res["ids"][b][res["ids"][b] >= 0].tolist()) <= set(pool.tolist())
+
+
+def test_m1_new_entry_is_the_raw_row():
+    case = small_decode(case_id=904, m=1, L=100, ragged=False)
+    res = pipeline.decode_step(case)
+    for b in range(case["spec"].B):
+        np.testing.assert_array_equal(res["kv_new"][b], f64(case["x_new"][b]))
+        np.testing.assert_array_equal(res["ki_new"][b], f64(case["xi_new"][b]))
+
+
+def test_gap_enforcement_decode():
+    case = small_decode(case_id=905, L=8192, ragged=False)
+    gaps.enforce_decode(case)
+    res = pipeline.decode_step(case)
+    for b, s in res["scores"].items():
+        assert gaps.gap_ok(s, case["spec"].K)
+    again = small_decode(case_id=905, L=8192, ragged=False)
+    gaps.enforce_decode(again)
+    assert torch.equal(case["w"], again["w"])        # redraws are deterministic
+
+
+def test_gap_enforcement_hierarchical():
+    case = small_decode(case_id=906, m=1, L=2000, block_size=4, max_blocks=64, ragged=False, K=32)
+    gaps.enforce_decode(case)
+    res = pipeline.decode_step(case)
+    for b in res["scores"]:
+        assert gaps.gap_ok(csa.block_maxima(res["scores"][b], 4), 64)
+        assert gaps.gap_ok(res["scores2"][b], 32)
+
+
+def test_gap_ok_rule():
+    assert gaps.gap_ok(np.array([3.0, 2.0, 1.0]), 3)
+    assert gaps.gap_ok(np.array([1.0, 0.998, 0.0]), 1)
+    assert not gaps.gap_ok(np.array([1.0, 0.9995, 0.0]), 1)
+    assert not gaps.gap_ok(np.array([0.0, 0.0, 5.0]), 2)     # exact tie at the boundary
+
+
+def test_prefill_rows_and_gaps():
+    spec = datagen.CaseSpec(907, "prefill", B=1, L=512, m=4, H_I=8, d_I=16, H=4, D=32, K=16,
+                            W=8, w_cap=64, chunk=64)
+    case = datagen.make_case(spec)
+    rows = [(0, 0), (0, 17), (0, 63)]
+    gaps.enforce_prefill(case, rows)
+    res = pipeline.prefill_rows(case, rows)
+    kv_c, ki_c = pipeline.prefill_entries(case)
+    assert kv_c.shape == (1, 16, 32)
+    for (b, i), ids in res["ids"].items():
+        t = int(case["q_pos"][b, i])
+        n = csa.n_visible(t, 4, spec.entries)
+        assert ids[ids >= 0].max() < n and (ids >= 0).sum() == min(16, n)
+        assert gaps.gap_ok(res["scores"][(b, i)], 16)
+
+
+def test_tiny_forward_runs_and_gaps():
+    spec = datagen.CaseSpec(908, "tiny", dtype="f32", B=1, L=256, m=4, H_I=4, d_I=32, H=4,
+                            D=64, K=16, W=16, w_cap=256, unit_scale=False, bias_sigma=0.1,
+                            scale=0.125)
+    case = datagen.make_case(spec)
+    gaps.enforce_tiny(case)
+    res = pipeline.tiny_forward(case)
+    for (b, i), s in res["scores"].items():
+        assert gaps.gap_ok(s, 16)
+    # query 0 sees no entry and only its own row: the output is the sink-weighted row 0
+    x0 = f64(case["x"][0, 0])
+    z = 0.125 * (f64(case["q"][0, 0]) @ x0)
+    wgt = 1 / (1 + np.exp(f64(case["sink"]) - z))
+    np.testing.assert_allclose(res["out"][(0, 0)], csa.round_f32(wgt[:, None] * x0), rtol=1e-6)
