@@ -1,0 +1,184 @@
+"""Benchmark of the CSA hot path on one MI355X: the fused decode step at 1M context.
+
+Workload (one step = one call of csa_decode_step over the batch): 4 sequences at position
+1,048,575 with 262,144 compressed entries each (m = 4); the new token completes a block, so
+each step pools one entry per stream, scans all 262,144 indexer keys per sequence (64 heads
+x 128), selects the Top-512 and attends over 512 entries + 128 window rows with 64 heads of
+dim 512 and a per-head sink. Inputs are seeded synthetic tensors of that shape, resident in
+HBM before timing. To keep the 256 MiB Infinity Cache from serving repeat reads, steps
+rotate over several independent copies of the per-sequence state (caches, tails, rings).
+
+Prints one JSON line: queries/s (value), the indexer scan's roofline (HIP events recorded by
+the library around the scan on the launch stream) and the float64 oracle timed on a bounded
+sample on the host cores.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "CSA decode queries/sec at 1M ctx + achieved HBM GB/s and MFMA % of peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles via the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return f.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(case, budget_s):
+    """The float64 oracle's decode step, on the host cores, over whole sequences of the same
+    workload until about budget_s seconds of work."""
+    from oracle import pipeline
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    B = case["spec"].B
+    done, t0 = 0, time.perf_counter()
+    while True:
+        pipeline.decode_step(case, seqs=[done % B])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 64:
+            break
+    return {"value": done / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} decode queries (whole sequences of the same workload: 262,144 "
+                      f"entries scanned, Top-512, 640-row attention) in {el:.1f} s, float64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4, help="state copies rotated across steps")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import datagen
+    import sparse_long_context_csa_amd as csa
+    from sparse_long_context_csa_amd import accounting as acc
+
+    spec = datagen.CONFIGS[4]
+    t0 = time.time()
+    case = datagen.make_case(spec)
+    log(f"generated inputs in {time.time() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    shared = {k: case[k].to(dev) for k in ("pos", "x_new", "z_new", "xi_new", "zi_new", "bias",
+                                            "bias_i", "q_idx", "w")}
+    qs = [x.to(dev) for x in case["q"]]
+    sinks = [x.to(dev) for x in case["sink"]]
+    steps_objs = []
+    for c in range(args.copies):
+        st = {k: case[k].to(dev) for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
+        rings = [r.to(dev) for r in case["rings"]]
+        steps_objs.append(csa.DecodeStep(
+            m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"], q=qs, win=rings,
+            win_new=[shared["x_new"]], sink=sinks, **shared, **st))
+    torch.cuda.synchronize()
+    log(f"device state ready: {args.copies} copies, "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
+
+    ev = HipEvents()
+    n_ev = 5
+    for i in range(args.warmup):
+        steps_objs[i % args.copies]()
+    torch.cuda.synchronize()
+    events = [[ev.create() for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        s = steps_objs[i % args.copies]
+        s.set_events(events[i])
+        s()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    for s in steps_objs:
+        s.set_events([])
+    phases = [[ev.ms(e[j], e[j + 1]) for j in range(n_ev - 1)] for e in events]
+    for e in events:
+        for h in e:
+            ev.destroy(h)
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * 2**20 // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    ms_step = wall * 1e3 / args.steps
+    qps = spec.B * args.steps / wall
+    mean = [sum(p[j] for p in phases) / len(phases) for j in range(n_ev - 1)]
+    scan_ms = mean[1]
+    E = spec.entries
+    scan_bytes = acc.scan_bytes(spec.B, E, spec.H_I, spec.d_I)
+    step_bytes = acc.decode_step_bytes(B=spec.B, n_vis=E, m=spec.m, D=spec.D, H=spec.H,
+                                       H_I=spec.H_I, d_I=spec.d_I, K=spec.K, W=spec.W).total
+    achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": datagen.WORKLOAD_NAMES[4], "batch": spec.B, "context": spec.L,
+                   "entries": E, "m": spec.m, "top_k": spec.K, "window": spec.W,
+                   "heads": spec.H, "head_dim": spec.D, "idx_heads": spec.H_I,
+                   "idx_dim": spec.d_I, "state_copies": args.copies},
+        "roofline": {"bound": "hbm", "kernel": "scan_decode_kernel (indexer scan)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(scan_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": scan_bytes},
+        "step_hbm": {"algorithmic_bytes": step_bytes,
+                     "achieved_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                     "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "phases_us": {"ingest_compress": round(mean[0] * 1e3, 2), "index_scan": round(mean[1] * 1e3, 2),
+                      "select": round(mean[2] * 1e3, 2), "attention": round(mean[3] * 1e3, 2)},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -353,3 +353,12 @@ def make_case(spec: CaseSpec) -> dict:
     if spec.kind == "tiny":
         return make_tiny(spec)
     raise ValueError(spec.kind)
+
+
+def tensor(case_id: int, tid: int, shape, dtype: str = "bf16", scale: float = 1.0,
+           attempt: int = 0, *extra: int) -> torch.Tensor:
+    """An ad-hoc seeded tensor: N(0,1) * scale rounded to the storage dtype."""
+    a = normal(case_id, tid, shape, attempt, *extra)
+    if scale != 1.0:
+        a *= np.float32(scale)
+    return to_storage(a, dtype)

@@ -1,0 +1,242 @@
+/*
+ * libcsa -- the Compressed Sparse Attention (CSA) hot path for AMD MI355X (gfx950).
+ *
+ * Sources (page titles and the sections each call follows):
+ *   [CoD]  "DeepSeek V4-Flash: The Cost of Deciding What to Read" (The Software Frontier)
+ *   [B890] "DeepSeek-V4.1-Flash's KV-Cache Compression, Checked Down to the Byte" (flozi-tech)
+ *   [V41]  "DeepSeek-V4.1-Flash" interactive architecture study (shuhuayu.github.io)
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers to dense row-major arrays (no strides unless an
+ *     argument says so). Scalars and the descriptor struct of csa_decode_step live on the
+ *     host; the pointers inside it are device pointers.
+ *   - dtype selects the storage type of the floating tensors documented as "T": CSA_BF16
+ *     (bfloat16) or CSA_F32. Gates (w), sinks and scores are always fp32; ids int32;
+ *     positions int64. Arithmetic is fp32 throughout; stored results are rounded to T by
+ *     round-to-nearest-even.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream). Arguments are validated on the host before anything is launched:
+ *     a call that returns an error launched nothing. CSA_ERR_HIP reports a failed launch.
+ *     Outputs are valid once the stream has reached the call.
+ *   - The library never allocates, frees or retains device memory. Scratch space is the
+ *     caller's workspace `ws` of at least the bytes the matching *_workspace_size call
+ *     returns (256-byte aligned). A workspace must not be shared by calls that may run
+ *     concurrently. No mutable global state: calls are thread-safe.
+ *   - Values that live on the device (positions, entry counts, ids) cannot be checked on
+ *     the host; kernels clamp them so that no access leaves the documented buffers:
+ *     visible counts are capped at the cache capacity, out-of-range ids are skipped.
+ */
+#ifndef LIBCSA_CSA_H
+#define LIBCSA_CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_NULL = -1,        /* a required pointer is NULL                              */
+  CSA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent                  */
+  CSA_ERR_DTYPE = -3,       /* unknown dtype                                           */
+  CSA_ERR_UNSUPPORTED = -4, /* valid request outside this build's limits               */
+  CSA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required              */
+  CSA_ERR_HIP = -6          /* a HIP launch failed                                     */
+} csa_status;
+
+/* Version of this header's ABI (CSA_ABI_VERSION). */
+int csa_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (host memory, never freed). */
+const char *csa_status_str(int status);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_compress -- learned channel-wise softmax pooling (one stream).
+ *   [CoD "The compressor has two streams and they overlap": per-channel softmax over the
+ *   pooled positions, weighted sum of the rows; CoD CSA/HCA layer tables: positional bias
+ *   of shape m x d; V41 "CSA2: separate producing, selecting, and reading": groups pooled
+ *   by a channel-wise softmax, no overlap.]
+ * For every sequence s, entry e < n_tok/m and channel c:
+ *   a_j = logits[s, e*m+j, c] + bias[j, c]   (j < m),   alpha = softmax_j(a)
+ *   out[s, e, c] = sum_j alpha_j * x[s, e*m+j, c]
+ *   x, logits : T [n_seq, n_tok, dim]      bias : T [m, dim]
+ *   out       : T, entry e of sequence s at out + s*out_seq_stride + e*dim
+ *               (out_seq_stride = 0 means dense: (n_tok/m)*dim). Writing into a cache at
+ *               an entry offset is done by offsetting `out` and passing the cache stride.
+ * Limits: 1 <= m <= 16, n_tok % m == 0, 1 <= dim <= 8192, dim % 8 == 0.
+ * ------------------------------------------------------------------------------------- */
+int csa_compress(const void *x, const void *logits, const void *bias, void *out,
+                 int64_t n_seq, int64_t n_tok, int64_t out_seq_stride, int32_t dim,
+                 int32_t m, int32_t dtype, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_index_topk -- lightning-indexer scores + Top-K selection.
+ *   [CoD "The Lightning Indexer": I(t,s) = sum_h w(t,h) * ReLU(q_I(t,h) . K_s); keep the
+ *   top k (512 in V4-Flash). CoD "The sliding window is not an optimisation": entry i is
+ *   usable by a query at t only if m*(i+1)-1 <= t.]
+ * For query row (s, i) at position t = q_pos[s, i]:
+ *   n_vis = min(e_count[s], floor((t+1)/m), e_cap)   (0 when t < 0; e_count NULL: e_cap)
+ *   candidates = entries 0..n_vis-1, or, when cand != NULL, the ids cand[s, i, 0..n_cand)
+ *                that satisfy 0 <= id < n_vis (others are ignored). cand lists must be
+ *                ascending (a pool from csa_index_blocks is).
+ *   out_idx[s, i, :] = the min(top_k, #candidates) candidates with the highest fp32 score,
+ *                ties to the lower id, written in ascending id order, padded with -1.
+ *   q_idx   : T [n_seq, n_q, idx_heads, idx_dim]     w : f32 [n_seq, n_q, idx_heads]
+ *   k_idx   : T [n_seq, e_cap, idx_dim]               q_pos : i64 [n_seq, n_q]
+ *   e_count : i32 [n_seq] or NULL                     cand  : i32 [n_seq, n_q, n_cand] or NULL
+ *   out_idx : i32 [n_seq, n_q, top_k]
+ *   out_score  : f32 [n_seq, n_q, top_k] or NULL: score of each selected id (-inf for pads)
+ *   scores_all : f32 [n_seq, n_q, n_keys] or NULL: every score (n_keys = n_cand if cand
+ *                else e_cap); positions that are not candidates hold -inf.
+ * Limits: 1 <= idx_heads <= 64, 8 <= idx_dim <= 256, idx_dim % 8 == 0,
+ *   idx_heads*idx_dim <= 8192 (bf16 fast path: 64 x 128), 1 <= top_k <= 2048,
+ *   1 <= m <= 16, 1 <= e_cap < 2^31, 0 <= n_cand <= 65536, n_seq*n_q <= 65535.
+ * ------------------------------------------------------------------------------------- */
+size_t csa_index_topk_workspace_size(int64_t n_seq, int64_t n_q, int64_t n_keys,
+                                     int32_t top_k);
+int csa_index_topk(const void *q_idx, const float *w, const void *k_idx,
+                   const int64_t *q_pos, const int32_t *e_count, const int32_t *cand,
+                   int32_t n_cand, int64_t n_seq, int64_t n_q, int64_t e_cap,
+                   int32_t idx_heads, int32_t idx_dim, int32_t m, int32_t top_k,
+                   int32_t *out_idx, float *out_score, float *scores_all, void *ws,
+                   size_t ws_bytes, int32_t dtype, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_index_blocks -- hierarchical pre-select: full scan -> block maxima -> pool.
+ *   [B890 section 3: the first Full layer scores the whole visible range and selects at
+ *   most 2,048 blocks of 8 positions, a pool of up to 16,384 candidates that later
+ *   Reindex layers rescore. V41 "Hierarchical indexing bounds the deeper searches": each
+ *   8-position block is scored by its maximum; the Full layer also takes its own Top-512.]
+ * For query row (s, i) (visibility as in csa_index_topk):
+ *   Bmax[b]  = max of the fp32 scores of visible entries in [b*block_size, (b+1)*block_size)
+ *   blocks   = the min(max_blocks, #blocks) blocks with the highest Bmax (ties: lower b)
+ *   out_pool[s, i, :] = the visible entries of those blocks, ascending, padded with -1
+ *   out_idx  (optional, NULL to skip) = this row's own Top-top_k as in csa_index_topk.
+ *   out_pool : i32 [n_seq, n_q, max_blocks*block_size]   out_idx : i32 [n_seq, n_q, top_k]
+ * Pass out_pool as `cand` (n_cand = max_blocks*block_size) to csa_index_topk to rescore.
+ * Limits: as csa_index_topk; 1 <= block_size <= 64, max_blocks >= 1,
+ *   block_size*max_blocks <= 32768; 0 <= top_k <= 2048 (ignored when out_idx is NULL).
+ * ------------------------------------------------------------------------------------- */
+size_t csa_index_blocks_workspace_size(int64_t n_seq, int64_t n_q, int64_t e_cap,
+                                       int32_t block_size, int32_t max_blocks,
+                                       int32_t top_k);
+int csa_index_blocks(const void *q_idx, const float *w, const void *k_idx,
+                     const int64_t *q_pos, const int32_t *e_count, int64_t n_seq,
+                     int64_t n_q, int64_t e_cap, int32_t idx_heads, int32_t idx_dim,
+                     int32_t m, int32_t block_size, int32_t max_blocks, int32_t *out_pool,
+                     int32_t top_k, int32_t *out_idx, void *ws, size_t ws_bytes,
+                     int32_t dtype, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_sparse_attn -- attention over supplied selected entries + local window + sink.
+ *   [CoD "Key and value are the same vector": one cached entry serves as key and value;
+ *   "Attention sink, and heads that abstain": exp(z'_h) joins the softmax denominator
+ *   only; "The sliding window is not an optimisation": the window rows are concatenated
+ *   with the selected entries before the softmax. B890 section 5: a query at i reads the
+ *   window [i-W+1, i]. V41 "What this means for existing V4 code": the attention kernel
+ *   gathers local and selected global latents, takes supplied selections, normalises
+ *   with the sink. CoD "Heavily Compressed Attention": top-k = all serves dense HCA.]
+ * For query row (s, i) at t = q_pos[s, i] and head h:
+ *   J   = { kv[s, idx[s,i,k]] : 0 <= idx[s,i,k] < e_cap }           (k < top_k; -1 skipped)
+ *       + { win[s, p % w_cap] : max(0, t-window+1) <= p <= t }         (raw window rows)
+ *   z_j = scale * q[s,i,h,:] . row_j
+ *   out[s,i,h,:] = sum_j e^{z_j} row_j / (sum_j e^{z_j} + e^{sink[h]})   (0 when J empty)
+ *   q   : T [n_seq, n_q, n_heads, head_dim]   kv : T [n_seq, e_cap, head_dim]
+ *   idx : i32 [n_seq, n_q, top_k] (any order; may be NULL when top_k == 0)
+ *   win : T [n_seq, w_cap, head_dim] (may be NULL when window == 0)
+ *   q_pos : i64 [n_seq, n_q]   sink : f32 [n_heads] or NULL (no sink)
+ *   out : T [n_seq, n_q, n_heads, head_dim]
+ * Selected ids are used as given: causality of the selection is the caller's (the ids of
+ * csa_index_topk are causal). The window rows for [t-window+1, t] must be in `win`.
+ * Limits: 1 <= n_heads <= 64, 8 <= head_dim <= 512, head_dim % 8 == 0, 0 <= top_k <= 16384,
+ *   0 <= window <= w_cap (w_cap >= 1 when window > 0), n_seq*n_q <= 65535.
+ *   bf16 fast path: n_heads == 64, head_dim == 512.
+ * ------------------------------------------------------------------------------------- */
+size_t csa_sparse_attn_workspace_size(int64_t n_seq, int64_t n_q, int32_t n_heads,
+                                      int32_t head_dim, int32_t top_k, int32_t window);
+int csa_sparse_attn(const void *q, const void *kv, const int32_t *idx, int32_t top_k,
+                    const void *win, int32_t w_cap, int32_t window, const int64_t *q_pos,
+                    const float *sink, float scale, void *out, int64_t n_seq, int64_t n_q,
+                    int64_t e_cap, int32_t n_heads, int32_t head_dim, void *ws,
+                    size_t ws_bytes, int32_t dtype, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_decode_step -- one new token per sequence through the whole hot path.
+ *   [CoD "The compressor has two streams...", "The Lightning Indexer", "Attention sink",
+ *   "The sliding window is not an optimisation"; CoD "Two cache hierarchies": compressed
+ *   entries in one cache, the window and the compressor's not-yet-pooled tail in a state
+ *   cache; B890 section 3 / V41 "CSA2": a selection shared by several attention calls
+ *   (Reuse layers), the hierarchical pool for deeper indexers.]
+ * Per sequence s at position t = pos[s] (slot = t % m):
+ *   1. x_new, z_new, xi_new, zi_new enter the compressor tails at row `slot`; for every
+ *      attention call c with win_new[c] != NULL, win_new[c][s] enters win[c] at row
+ *      t % w_cap.
+ *   2. If (t+1) % m == 0 the block is complete: entry e = (t+1)/m - 1 (< e_cap, else not
+ *      stored) of kv <- pool(x_tail, z_tail, bias) and of k_idx <- pool(xi_tail, zi_tail,
+ *      bias_i), as csa_compress with n_tok = m.
+ *   3. n_vis = min(floor((t+1)/m), e_cap): the cache must hold entries 0..n_vis-1.
+ *   4. Flat (block_size == 0): out_idx[s] = Top-top_k of csa_index_topk over the visible
+ *      entries with (q_idx, w). Hierarchical (block_size > 0): the pool of
+ *      csa_index_blocks with (q_idx, w), then the Top-top_k of the pool rescored with
+ *      (q_idx2, w2).
+ *   5. For c < n_attn: out[c][s] = csa_sparse_attn of q[c][s] over out_idx[s], window rows
+ *      of win[c] and sink[c] (scale shared). The calls are issued one after another.
+ * Pointers (device unless noted):
+ *   pos i64 [n_seq]; x_new, z_new T [n_seq, dim]; xi_new, zi_new T [n_seq, idx_dim];
+ *   kv T [n_seq, e_cap, dim]; k_idx T [n_seq, e_cap, idx_dim];
+ *   x_tail, z_tail T [n_seq, m, dim]; xi_tail, zi_tail T [n_seq, m, idx_dim];
+ *   bias T [m, dim]; bias_i T [m, idx_dim];
+ *   q_idx, q_idx2 T [n_seq, idx_heads, idx_dim]; w, w2 f32 [n_seq, idx_heads]
+ *   (q_idx2/w2 only when block_size > 0);
+ *   q[c] T [n_seq, n_heads, dim]; win[c] T [n_seq, w_cap, dim]; win_new[c] T [n_seq, dim]
+ *   or NULL; sink[c] f32 [n_heads] or NULL; out[c] T [n_seq, n_heads, dim];
+ *   out_idx i32 [n_seq, top_k].
+ * Limits: as the calls it is made of; 1 <= n_attn <= CSA_MAX_ATTN.
+ * ------------------------------------------------------------------------------------- */
+#define CSA_MAX_ATTN 4
+#define CSA_DECODE_EVENTS 5
+
+typedef struct csa_decode_desc {
+  int32_t dtype;
+  int32_t m, dim, n_heads, idx_heads, idx_dim;
+  int32_t top_k, window, w_cap;
+  int32_t block_size, max_blocks;   /* block_size 0: flat selection */
+  int32_t n_attn;
+  int64_t n_seq, e_cap;
+  float scale;
+  const int64_t *pos;
+  const void *x_new, *z_new, *xi_new, *zi_new;
+  void *kv, *k_idx;
+  void *x_tail, *z_tail, *xi_tail, *zi_tail;
+  const void *bias, *bias_i;
+  const void *q_idx;
+  const float *w;
+  const void *q_idx2;
+  const float *w2;
+  const void *q[CSA_MAX_ATTN];
+  void *win[CSA_MAX_ATTN];
+  const void *win_new[CSA_MAX_ATTN];
+  const float *sink[CSA_MAX_ATTN];
+  void *out[CSA_MAX_ATTN];
+  int32_t *out_idx;
+  /* Optional profiling hooks: hipEvent_t handles (as void*) recorded on `stream` at the
+   * phase boundaries of the step when non-NULL: [0] start, [1] after the ingest/compress
+   * kernel, [2] after the (stage-1) indexer scan, [3] after the selection (incl. the
+   * hierarchical stage 2), [4] after the attention calls. The caller owns the events. */
+  void *events[CSA_DECODE_EVENTS];
+} csa_decode_desc;
+
+size_t csa_decode_step_workspace_size(const csa_decode_desc *d);
+int csa_decode_step(const csa_decode_desc *d, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBCSA_CSA_H */

@@ -1,0 +1,208 @@
+"""Python binding of libcsa, the CSA hot path for MI355X (gfx950).
+
+Argument marshalling only: every step runs in libcsa's HIP kernels. PyTorch provides
+device memory (tensors, workspaces) and the current HIP stream. The functions mirror the
+C ABI of include/csa.h; see there for the exact contract of each call.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _lib
+from ._lib import CsaError, DecodeDesc, check, lib  # noqa: F401
+
+__all__ = ["compress", "index_topk", "index_blocks", "sparse_attn", "DecodeStep", "CsaError",
+           "lib"]
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.CSA_BF16
+    if t.dtype == torch.float32:
+        return _lib.CSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _dev(t, name: str, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _p(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------------------
+def compress(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor, m: int,
+             out: torch.Tensor | None = None, out_seq_stride: int = 0) -> torch.Tensor:
+    """csa_compress: pool every m rows of x [n_seq, n_tok, dim] into one entry."""
+    _dev(x, "x"); _dev(logits, "logits", x.dtype); _dev(bias, "bias", x.dtype)
+    n_seq, n_tok, dim = x.shape
+    if out is None:
+        out = torch.empty(n_seq, n_tok // m, dim, dtype=x.dtype, device=x.device)
+    elif out.dtype != x.dtype or not out.is_cuda:
+        raise TypeError("out must be a GPU tensor of x's dtype")
+    check("csa_compress", lib().csa_compress(_p(x), _p(logits), _p(bias), _p(out), n_seq, n_tok,
+                                             out_seq_stride, dim, m, _dtype(x), _stream()))
+    return out
+
+
+def index_topk(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor, q_pos: torch.Tensor,
+               m: int, top_k: int, e_count: torch.Tensor | None = None,
+               cand: torch.Tensor | None = None, want_scores: bool = False,
+               want_all: bool = False):
+    """csa_index_topk. q_idx [n_seq,n_q,H_I,d_I], w [n_seq,n_q,H_I] f32, k_idx [n_seq,e_cap,d_I],
+    q_pos [n_seq,n_q] i64, optional e_count [n_seq] i32 and cand [n_seq,n_q,n_cand] i32.
+    Returns out_idx (and out_score / scores_all when asked)."""
+    _dev(q_idx, "q_idx"); _dev(w, "w", torch.float32); _dev(k_idx, "k_idx", q_idx.dtype)
+    _dev(q_pos, "q_pos", torch.int64); _dev(e_count, "e_count", torch.int32)
+    _dev(cand, "cand", torch.int32)
+    n_seq, n_q, H, d = q_idx.shape
+    e_cap = k_idx.shape[1]
+    n_cand = 0 if cand is None else cand.shape[-1]
+    n_keys = n_cand if cand is not None else e_cap
+    dev = q_idx.device
+    out_idx = torch.empty(n_seq, n_q, top_k, dtype=torch.int32, device=dev)
+    out_score = torch.empty(n_seq, n_q, top_k, dtype=torch.float32, device=dev) if want_scores else None
+    all_s = torch.empty(n_seq, n_q, n_keys, dtype=torch.float32, device=dev) if want_all else None
+    nb = lib().csa_index_topk_workspace_size(n_seq, n_q, n_keys, top_k)
+    ws = _workspace(nb, dev)
+    check("csa_index_topk", lib().csa_index_topk(
+        _p(q_idx), _p(w), _p(k_idx), _p(q_pos), _p(e_count), _p(cand), n_cand, n_seq, n_q, e_cap,
+        H, d, m, top_k, _p(out_idx), _p(out_score), _p(all_s), _p(ws), ws.numel(), _dtype(q_idx),
+        _stream()))
+    res = [out_idx]
+    if want_scores:
+        res.append(out_score)
+    if want_all:
+        res.append(all_s)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def index_blocks(q_idx, w, k_idx, q_pos, m: int, block_size: int, max_blocks: int,
+                 e_count=None, top_k: int = 0):
+    """csa_index_blocks: candidate pool [n_seq,n_q,max_blocks*block_size] (and the row's own
+    Top-top_k when top_k > 0)."""
+    _dev(q_idx, "q_idx"); _dev(w, "w", torch.float32); _dev(k_idx, "k_idx", q_idx.dtype)
+    _dev(q_pos, "q_pos", torch.int64); _dev(e_count, "e_count", torch.int32)
+    n_seq, n_q, H, d = q_idx.shape
+    e_cap = k_idx.shape[1]
+    dev = q_idx.device
+    pool = torch.empty(n_seq, n_q, max_blocks * block_size, dtype=torch.int32, device=dev)
+    out_idx = torch.empty(n_seq, n_q, top_k, dtype=torch.int32, device=dev) if top_k > 0 else None
+    nb = lib().csa_index_blocks_workspace_size(n_seq, n_q, e_cap, block_size, max_blocks, top_k)
+    ws = _workspace(nb, dev)
+    check("csa_index_blocks", lib().csa_index_blocks(
+        _p(q_idx), _p(w), _p(k_idx), _p(q_pos), _p(e_count), n_seq, n_q, e_cap, H, d, m,
+        block_size, max_blocks, _p(pool), top_k, _p(out_idx), _p(ws), ws.numel(), _dtype(q_idx),
+        _stream()))
+    return pool if out_idx is None else (pool, out_idx)
+
+
+def sparse_attn(q, kv, idx, win, w_cap: int, window: int, q_pos, sink, scale: float,
+                out=None) -> torch.Tensor:
+    """csa_sparse_attn. q [n_seq,n_q,H,D], kv [n_seq,e_cap,D], idx [n_seq,n_q,top_k] i32 or
+    None, win [n_seq,w_cap,D] or None, q_pos [n_seq,n_q] i64, sink [H] f32 or None."""
+    _dev(q, "q"); _dev(kv, "kv", q.dtype); _dev(idx, "idx", torch.int32)
+    _dev(win, "win", q.dtype); _dev(q_pos, "q_pos", torch.int64); _dev(sink, "sink", torch.float32)
+    n_seq, n_q, H, D = q.shape
+    e_cap = kv.shape[1]
+    top_k = 0 if idx is None else idx.shape[-1]
+    if out is None:
+        out = torch.empty_like(q)
+    nb = lib().csa_sparse_attn_workspace_size(n_seq, n_q, H, D, top_k, window)
+    ws = _workspace(nb, q.device) if nb else None
+    check("csa_sparse_attn", lib().csa_sparse_attn(
+        _p(q), _p(kv), _p(idx), top_k, _p(win), w_cap, window, _p(q_pos), _p(sink), float(scale),
+        _p(out), n_seq, n_q, e_cap, H, D, _p(ws), 0 if ws is None else ws.numel(), _dtype(q),
+        _stream()))
+    return out
+
+
+class DecodeStep:
+    """csa_decode_step over caller-owned state. Builds the descriptor and its workspace once;
+    each call runs one step (new token per sequence) on the current stream.
+
+    Tensors (GPU, contiguous): pos, x_new, z_new, xi_new, zi_new, kv, k_idx, x_tail, z_tail,
+    xi_tail, zi_tail, bias, bias_i, q_idx, w, [q_idx2, w2], q (list), win (list),
+    win_new (list, entries may be None), sink (list, entries may be None); out (list) and
+    out_idx are allocated here unless given."""
+
+    def __init__(self, *, m: int, top_k: int, window: int, scale: float, block_size: int = 0,
+                 max_blocks: int = 0, out=None, out_idx=None, **t):
+        self.t = t
+        kv = _dev(t["kv"], "kv")
+        dt = kv.dtype
+        for k in ("x_new", "z_new", "xi_new", "zi_new", "k_idx", "x_tail", "z_tail", "xi_tail",
+                  "zi_tail", "bias", "bias_i", "q_idx"):
+            _dev(t[k], k, dt)
+        _dev(t["pos"], "pos", torch.int64)
+        _dev(t["w"], "w", torch.float32)
+        qs, wins = list(t["q"]), list(t["win"])
+        n_attn = len(qs)
+        win_new = list(t.get("win_new") or [])
+        win_new += [None] * (n_attn - len(win_new))
+        sinks = list(t.get("sink") or [])
+        sinks += [None] * (n_attn - len(sinks))
+        n_seq, e_cap, dim = kv.shape
+        H = qs[0].shape[1]
+        idx_heads, idx_dim = t["q_idx"].shape[1], t["q_idx"].shape[2]
+        w_cap = wins[0].shape[1]
+        if out is None:
+            out = [torch.empty_like(q) for q in qs]
+        if out_idx is None:
+            out_idx = torch.empty(n_seq, top_k, dtype=torch.int32, device=kv.device)
+        self.out, self.out_idx = out, out_idx
+        d = DecodeDesc()
+        d.dtype = _dtype(kv); d.m = m; d.dim = dim; d.n_heads = H; d.idx_heads = idx_heads
+        d.idx_dim = idx_dim; d.top_k = top_k; d.window = window; d.w_cap = w_cap
+        d.block_size = block_size; d.max_blocks = max_blocks; d.n_attn = n_attn
+        d.n_seq = n_seq; d.e_cap = e_cap; d.scale = float(scale)
+        for k in ("pos", "x_new", "z_new", "xi_new", "zi_new", "kv", "k_idx", "x_tail", "z_tail",
+                  "xi_tail", "zi_tail", "bias", "bias_i", "q_idx", "w"):
+            setattr(d, k, t[k].data_ptr())
+        if block_size > 0:
+            _dev(t["q_idx2"], "q_idx2", dt); _dev(t["w2"], "w2", torch.float32)
+            d.q_idx2 = t["q_idx2"].data_ptr(); d.w2 = t["w2"].data_ptr()
+        for c in range(n_attn):
+            _dev(qs[c], "q", dt); _dev(wins[c], "win", dt); _dev(out[c], "out", dt)
+            d.q[c] = qs[c].data_ptr(); d.win[c] = wins[c].data_ptr(); d.out[c] = out[c].data_ptr()
+            if win_new[c] is not None:
+                d.win_new[c] = _dev(win_new[c], "win_new", dt).data_ptr()
+            if sinks[c] is not None:
+                d.sink[c] = _dev(sinks[c], "sink", torch.float32).data_ptr()
+        d.out_idx = out_idx.data_ptr()
+        self.desc = d
+        nb = lib().csa_decode_step_workspace_size(C.byref(d))
+        if nb == 0:
+            check("csa_decode_step_workspace_size", lib().csa_decode_step(C.byref(d), None, 0, None))
+        self.ws = _workspace(nb, kv.device)
+
+    def set_events(self, handles) -> None:
+        """Phase-boundary hipEvent_t handles (ints or None) recorded by the step."""
+        hs = list(handles) + [None] * (_lib.DECODE_EVENTS - len(handles))
+        for i, h in enumerate(hs[:_lib.DECODE_EVENTS]):
+            self.desc.events[i] = h
+
+    def __call__(self, stream: int | None = None):
+        check("csa_decode_step", lib().csa_decode_step(
+            C.byref(self.desc), self.ws.data_ptr(), self.ws.numel(),
+            _stream() if stream is None else stream))
+        return self.out, self.out_idx

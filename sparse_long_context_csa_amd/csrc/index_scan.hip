@@ -1,0 +1,321 @@
+// Lightning-indexer scan: I(t,s) = sum_h w(t,h) * ReLU(q_I(t,h) . K_s) for every candidate.
+//
+// "DeepSeek V4-Flash: The Cost of Deciding What to Read", section "The Lightning Indexer":
+// 64 indexer heads of dim 128 per query, one compressed indexer key per entry, a rectified
+// dot product per head, summed with the per-head gate w; section "The indexer is O(n), and
+// that is the ceiling": the scan touches every visible entry and never becomes sparse.
+//
+// Three kernels:
+//  * scan_decode_kernel (bf16, 64 heads x 128): few query rows, many keys. The contraction
+//    is a [64 heads x 128] x [128 x 16 keys] MFMA (v_mfma_f32_16x16x32_bf16) per tile; the
+//    query stays in VGPRs as the A operand and every key row is read once from HBM straight
+//    into the B operand (no LDS: nothing is reused across waves). The channel order inside
+//    each MFMA is permuted so a lane reads 64 contiguous bytes of its key row. ReLU, gate
+//    and head sum run on the accumulator lanes, two xor-shuffles finish the head sum.
+//  * scan_prefill_kernel (bf16, 64 x 128): many query rows (a prefill chunk). 8 query rows
+//    per workgroup (one per wave, A operand in VGPRs); 64-key tiles are staged in LDS once
+//    and reused by the 8 waves, double-buffered with the next tile's global loads.
+//  * scan_generic_kernel: any head count/dim and fp32; one thread per candidate.
+// Visibility: entry i is usable by a query at t only if m*(i+1)-1 <= t ("The sliding window
+// is not an optimisation"); positions past a row's visible count are never scored.
+#include "csa_common.hpp"
+#include "launch.hpp"
+
+namespace csa {
+
+namespace {
+
+constexpr int kIH = 64;    // indexer heads on the MFMA paths
+constexpr int kID = 128;   // indexer dim on the MFMA paths
+
+__device__ __forceinline__ int64_t row_visible(const ScanArgs& a, int64_t r) {
+  const int64_t sq = r / a.n_q;
+  int64_t cap = a.e_cap;
+  if (a.e_count) {
+    const int64_t ec = a.e_count[sq];
+    cap = ec < cap ? (ec < 0 ? 0 : ec) : cap;
+  }
+  return visible_entries(a.q_pos[r], a.m, cap);
+}
+
+// A operand of one query: heads 16*mt + (lane&15), channels g*32 + ks*8 .. +8 (g = lane>>4)
+__device__ __forceinline__ void load_query_A(const uint16_t* q, int lane, bf16x8_t (&A)[4][4]) {
+  const int g = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const uint16_t* p = q + (16 * mt + col) * kID + g * 32;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) A[mt][ks] = *reinterpret_cast<const bf16x8_t*>(p + ks * 8);
+  }
+}
+
+// gates of the heads held by this lane in the accumulator layout: 16*mt + 4*g + i
+__device__ __forceinline__ void load_gates(const float* w, int lane, float (&wv)[4][4]) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const float4 v = *reinterpret_cast<const float4*>(w + 16 * mt + 4 * g);
+    wv[mt][0] = v.x; wv[mt][1] = v.y; wv[mt][2] = v.z; wv[mt][3] = v.w;
+  }
+}
+
+// 16 MFMAs: acc[mt] = q[16 heads of mt] x key tile; then sum_h w_h * relu(acc)
+__device__ __forceinline__ float tile_score(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
+                                            const float (&wv)[4][4]) {
+  f32x4_t acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][ks], B[ks], acc[mt], 0, 0, 0);
+  }
+  float part = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], fmaxf(acc[mt][i], 0.f), part);
+  part += __shfl_xor(part, 16);
+  part += __shfl_xor(part, 32);
+  return part;
+}
+
+__device__ __forceinline__ void load_key_B(const uint16_t* row, int g, bf16x8_t (&B)[4]) {
+  const bf16x8_t* p = reinterpret_cast<const bf16x8_t*>(row + g * 32);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) B[ks] = __builtin_nontemporal_load(p + ks);
+}
+
+}  // namespace
+
+// grid.x: chunks of `chunk` candidate positions, grid.y: query rows. 4 waves per block, each
+// wave scores 16-key tiles (wave w takes tiles w, w+4, ... of the chunk).
+template <bool kCand>
+__global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk) {
+  const int64_t r = blockIdx.y;
+  const int64_t n_vis = row_visible(a, r);
+  const int64_t n_pos = kCand ? a.n_cand : n_vis;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.n_vis[r] = int32_t(n_vis);
+    a.count[r] = int32_t(n_pos);
+  }
+  const int64_t c0 = int64_t(blockIdx.x) * chunk;
+  if (c0 >= n_pos) return;
+  const int64_t c1 = c0 + chunk < n_pos ? c0 + chunk : n_pos;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t sq = r / a.n_q;
+
+  bf16x8_t A[4][4];
+  load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
+  float wv[4][4];
+  load_gates(a.w + r * kIH, lane, wv);
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
+  const int32_t* cand = kCand ? a.cand + r * a.n_cand : nullptr;
+  float* out = a.scores + r * a.score_stride;
+
+  // key row of position p (invalid positions read a safe row and are masked on store)
+  auto key_row = [&](int64_t p, bool& ok) -> int64_t {
+    if (p >= c1) { ok = false; return kCand ? 0 : c0; }
+    if (kCand) {
+      const int32_t id = cand[p];
+      ok = id >= 0 && id < n_vis;
+      return ok ? id : 0;
+    }
+    ok = true;
+    return p;
+  };
+
+  int64_t tile = c0 + wave * 16;
+  if (tile >= c1) return;
+  bool ok_cur;
+  bf16x8_t Bc[4], Bn[4];
+  load_key_B(kb + key_row(tile + col, ok_cur) * kID, g, Bc);
+  for (;;) {
+    const int64_t next = tile + 64;
+    bool ok_next = false;
+    const bool has_next = next < c1;
+    if (has_next) load_key_B(kb + key_row(next + col, ok_next) * kID, g, Bn);
+    const float s = tile_score(A, Bc, wv);
+    const int64_t p = tile + col;
+    if (g == 0 && p < c1) out[p] = ok_cur ? s : neg_inf();
+    if (!has_next) break;
+    tile = next;
+    ok_cur = ok_next;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) Bc[ks] = Bn[ks];
+  }
+}
+
+// ---- prefill: 8 query rows per block, 64-key tiles staged through LDS ----------------------
+constexpr int kPQ = 8;            // query rows per block (one per wave)
+constexpr int kPT = 64;           // keys per tile
+constexpr int kPRow = 272;        // LDS bytes per key row (256 + 16 pad: conflict-free b128)
+
+__global__ __launch_bounds__(512) void scan_prefill_kernel(ScanArgs a, int keys_per_block) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kPT * kPRow];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t rows = a.n_seq * a.n_q;
+  // query rows of this block: kPQ consecutive rows of one sequence
+  const int64_t groups_per_seq = (a.n_q + kPQ - 1) / kPQ;
+  const int64_t sq = blockIdx.y / groups_per_seq;
+  const int64_t i0 = (blockIdx.y % groups_per_seq) * kPQ;
+  const int64_t qi = i0 + wave;
+  const bool row_ok = qi < a.n_q;
+  const int64_t r = sq * a.n_q + (row_ok ? qi : i0);
+  const int64_t n_vis = row_ok ? row_visible(a, r) : 0;
+  if (row_ok && blockIdx.x == 0 && lane == 0) {
+    a.n_vis[r] = int32_t(n_vis);
+    a.count[r] = int32_t(n_vis);
+  }
+  // block-wide extent: the largest visible count among the block's rows
+  __shared__ int64_t s_nmax[kPQ];
+  if (lane == 0) s_nmax[wave] = n_vis;
+  __syncthreads();
+  int64_t nmax = 0;
+#pragma unroll
+  for (int i = 0; i < kPQ; ++i) nmax = s_nmax[i] > nmax ? s_nmax[i] : nmax;
+  const int64_t k0 = int64_t(blockIdx.x) * keys_per_block;
+  const int64_t k1 = k0 + keys_per_block < nmax ? k0 + keys_per_block : nmax;
+  if (k0 >= k1) return;
+  (void)rows;
+
+  bf16x8_t A[4][4];
+  load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
+  float wv[4][4];
+  load_gates(a.w + r * kIH, lane, wv);
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
+  float* out = a.scores + r * a.score_stride;
+
+  // cooperative tile load: thread t moves 16-byte chunks t and t+512 of the 64x256 B tile
+  const int ch0 = threadIdx.x, ch1 = threadIdx.x + 512;
+  auto gload = [&](int64_t base, bf16x8_t& v0, bf16x8_t& v1) {
+    const int64_t r0 = base + (ch0 >> 4), r1 = base + (ch1 >> 4);
+    const int64_t s0 = r0 < k1 ? r0 : k1 - 1, s1 = r1 < k1 ? r1 : k1 - 1;
+    v0 = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(kb + s0 * kID) + (ch0 & 15));
+    v1 = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(kb + s1 * kID) + (ch1 & 15));
+  };
+  auto lstore = [&](int buf, const bf16x8_t& v0, const bf16x8_t& v1) {
+    *reinterpret_cast<bf16x8_t*>(&lds[buf][(ch0 >> 4) * kPRow + (ch0 & 15) * 16]) = v0;
+    *reinterpret_cast<bf16x8_t*>(&lds[buf][(ch1 >> 4) * kPRow + (ch1 & 15) * 16]) = v1;
+  };
+
+  bf16x8_t v0, v1;
+  gload(k0, v0, v1);
+  lstore(0, v0, v1);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t base = k0; base < k1; base += kPT) {
+    const bool more = base + kPT < k1;
+    if (more) gload(base + kPT, v0, v1);
+    if (base < n_vis) {
+      const unsigned char* tb = lds[buf];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        bf16x8_t B[4];
+        const unsigned char* rp = tb + (nt * 16 + col) * kPRow + g * 64;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) B[ks] = *reinterpret_cast<const bf16x8_t*>(rp + ks * 16);
+        const float s = tile_score(A, B, wv);
+        const int64_t p = base + nt * 16 + col;
+        if (g == 0 && p < n_vis) out[p] = s;
+      }
+    }
+    if (more) {
+      lstore(buf ^ 1, v0, v1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+}
+
+// ---- generic: one thread per candidate position; any H <= 64, d <= 256, fp32 or bf16 ------
+template <typename T>
+__global__ __launch_bounds__(256) void scan_generic_kernel(ScanArgs a) {
+  extern __shared__ float qs[];   // [H*d] query, then [H] gates
+  const int64_t r = blockIdx.y;
+  const int64_t n_vis = row_visible(a, r);
+  const int64_t n_pos = a.cand ? a.n_cand : n_vis;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.n_vis[r] = int32_t(n_vis);
+    a.count[r] = int32_t(n_pos);
+  }
+  const int64_t p = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (int64_t(blockIdx.x) * blockDim.x >= n_pos) return;
+  const int H = a.H, d = a.d;
+  const T* q = reinterpret_cast<const T*>(a.q) + r * H * d;
+  for (int i = threadIdx.x; i < H * d; i += blockDim.x) qs[i] = Elt<T>::load1(q + i);
+  for (int i = threadIdx.x; i < H; i += blockDim.x) qs[H * d + i] = a.w[r * H + i];
+  __syncthreads();
+  if (p >= n_pos) return;
+  int64_t id = p;
+  bool ok = true;
+  if (a.cand) {
+    id = a.cand[r * a.n_cand + p];
+    ok = id >= 0 && id < n_vis;
+  }
+  float* out = a.scores + r * a.score_stride;
+  if (!ok) { out[p] = neg_inf(); return; }
+  const int64_t sq = r / a.n_q;
+  const T* key = reinterpret_cast<const T*>(a.keys) + (sq * a.e_cap + id) * d;
+  float dot[64];
+#pragma unroll
+  for (int h = 0; h < 64; ++h) dot[h] = 0.f;
+  for (int c0 = 0; c0 < d; c0 += 8) {
+    float kv8[8];
+    Elt<T>::load8(key + c0, kv8);
+#pragma unroll
+    for (int h = 0; h < 64; ++h) {
+      if (h < H) {
+        const float* qh = qs + h * d + c0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dot[h] = fmaf(qh[c], kv8[c], dot[h]);
+      }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int h = 0; h < 64; ++h)
+    if (h < H) s = fmaf(qs[H * d + h], fmaxf(dot[h], 0.f), s);
+  out[p] = s;
+}
+
+static bool fast_shape(const ScanArgs& a) { return a.dt == kBF16 && a.H == kIH && a.d == kID; }
+
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
+  const int64_t rows = a.n_seq * a.n_q;
+  if (rows == 0) return hipSuccess;
+  const int64_t max_pos = a.cand ? a.n_cand : a.e_cap;
+  if (fast_shape(a) && a.cand == nullptr && a.n_q >= 16) {
+    const int keys_per_block = 4096;
+    const int64_t groups = a.n_seq * ((a.n_q + kPQ - 1) / kPQ);
+    const dim3 grid(unsigned((a.e_cap + keys_per_block - 1) / keys_per_block), unsigned(groups));
+    hipLaunchKernelGGL(scan_prefill_kernel, grid, dim3(512), 0, s, a, keys_per_block);
+    return hipGetLastError();
+  }
+  if (fast_shape(a)) {
+    const int chunk = 1024;
+    const dim3 grid(unsigned((max_pos + chunk - 1) / chunk), unsigned(rows));
+    if (grid.x == 0) {
+      const dim3 g1(1, unsigned(rows));
+      if (a.cand) hipLaunchKernelGGL(scan_decode_kernel<true>, g1, dim3(256), 0, s, a, chunk);
+      else hipLaunchKernelGGL(scan_decode_kernel<false>, g1, dim3(256), 0, s, a, chunk);
+    } else if (a.cand) {
+      hipLaunchKernelGGL(scan_decode_kernel<true>, grid, dim3(256), 0, s, a, chunk);
+    } else {
+      hipLaunchKernelGGL(scan_decode_kernel<false>, grid, dim3(256), 0, s, a, chunk);
+    }
+    return hipGetLastError();
+  }
+  const unsigned gx = unsigned(max_pos > 0 ? (max_pos + 255) / 256 : 1);
+  const dim3 grid(gx, unsigned(rows));
+  const size_t shm = size_t(a.H) * a.d * 4 + size_t(a.H) * 4;
+  if (a.dt == kBF16)
+    hipLaunchKernelGGL(scan_generic_kernel<uint16_t>, grid, dim3(256), shm, s, a);
+  else
+    hipLaunchKernelGGL(scan_generic_kernel<float>, grid, dim3(256), shm, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa

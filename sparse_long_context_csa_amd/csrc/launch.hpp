@@ -1,0 +1,107 @@
+// Host-side launchers of the libcsa kernels (internal; the public ABI is include/csa.h).
+// Every launcher enqueues on `stream` and returns hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+enum DType : int { kF32 = 0, kBF16 = 1 };
+
+// ---- compressor --------------------------------------------------------------------------
+hipError_t launch_compress(int dt, const void* x, const void* z, const void* bias, void* out,
+                           int64_t n_seq, int64_t n_tok, int64_t out_seq_stride, int dim, int m,
+                           hipStream_t s);
+
+struct IngestArgs {
+  int dt;
+  int64_t n_seq, e_cap;
+  int m, dim, idx_dim, w_cap, n_ring;
+  const int64_t* pos;
+  const void *x_new, *z_new, *xi_new, *zi_new;
+  void *x_tail, *z_tail, *xi_tail, *zi_tail;
+  const void *bias, *bias_i;
+  void *kv, *k_idx;
+  void* win[4];
+  const void* win_new[4];
+};
+hipError_t launch_ingest(const IngestArgs& a, hipStream_t s);
+
+// ---- indexer scan ------------------------------------------------------------------------
+// Scores of query rows r = (seq, query) against their candidates, written to
+// scores[r * score_stride + j] for candidate position j; fp32. Also writes
+// n_vis[r] (visible entries) and count[r] (candidate positions considered).
+struct ScanArgs {
+  int dt;
+  const void* q;          // [rows, H, d]
+  const float* w;         // [rows, H]
+  const void* keys;       // [n_seq, e_cap, d]
+  const int64_t* q_pos;   // [rows]
+  const int32_t* e_count; // [n_seq] or null
+  const int32_t* cand;    // [rows, n_cand] or null
+  int64_t n_cand;
+  int64_t n_seq, n_q, e_cap;
+  int H, d, m;
+  float* scores;          // [rows, score_stride]
+  int64_t score_stride;
+  int32_t* n_vis;         // [rows]
+  int32_t* count;         // [rows]
+};
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+
+// ---- selection ---------------------------------------------------------------------------
+// Top-K of each row's `count[r]` positions; position j has score scores[r*stride + j] and
+// id (ids ? ids[r*id_stride + j] : j); an id is valid iff 0 <= id < id_limit[r] (or id >= 0
+// when id_limit is null). Result ids ascending, -1 padded, in out_idx[r*out_stride + k].
+struct TopkArgs {
+  const float* scores;
+  int64_t stride;
+  const int32_t* ids;
+  int64_t id_stride;
+  const int32_t* id_limit;
+  const int32_t* count;
+  int64_t rows;
+  int64_t max_count;      // upper bound of count[r] (sizes the launch)
+  int K;
+  int32_t* out_idx;
+  float* out_score;       // may be null
+  int64_t out_stride;
+  void* scratch;          // segment buffers (see topk_scratch_bytes)
+};
+size_t topk_scratch_bytes(int64_t rows, int64_t max_count, int K);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+// Block maxima of each row's first count[r] scores; nb[r] = ceil(count/bs).
+hipError_t launch_block_max(const float* scores, int64_t stride, const int32_t* count,
+                            int64_t rows, int64_t max_count, int bs, float* bmax,
+                            int64_t bmax_stride, int32_t* nb, hipStream_t s);
+// Pool of the selected blocks (ascending block ids, -1 padded): entries b*bs.. below n_vis.
+hipError_t launch_pool_build(const int32_t* blocks, int64_t rows, int max_blocks, int bs,
+                             const int32_t* n_vis, int32_t* pool, hipStream_t s);
+
+// Expand a row's scores to the caller's scores_all layout (non-candidates -inf).
+hipError_t launch_fill_scores(const float* scores, int64_t stride, const int32_t* count,
+                              int64_t rows, int64_t n_keys, float* out, hipStream_t s);
+
+// ---- sparse attention --------------------------------------------------------------------
+struct AttnArgs {
+  int dt;
+  const void* q;          // [rows, H, D]
+  const void* kv;         // [n_seq, e_cap, D]
+  const int32_t* idx;     // [rows, top_k]
+  int top_k;
+  const void* win;        // [n_seq, w_cap, D]
+  int w_cap, window;
+  const int64_t* q_pos;   // [rows]
+  const float* sink;      // [H] or null
+  float scale;
+  void* out;              // [rows, H, D]
+  int64_t n_seq, n_q, e_cap;
+  int H, D;
+  void* ws;
+};
+size_t attn_ws_bytes(int64_t rows, int H, int D, int top_k, int window, int dt);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+
+}  // namespace csa

@@ -1,0 +1,100 @@
+"""Shared helpers of the GPU parity tests (inputs from datagen, expectations from the oracle)."""
+import math
+
+import numpy as np
+import torch
+
+import datagen
+from oracle import csa as ocsa
+from oracle import gaps
+from oracle.pipeline import f64, i64
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+T_TEST_W = 40
+
+
+def dev(t):
+    return t.to(DEV) if isinstance(t, torch.Tensor) else t
+
+
+def fix_gaps(case_id, q_idx, w, k_idx, q_pos, e_count, m, K, cand=None, dtype="bf16"):
+    """Redraw gate rows (seeded) until each row's visible scores separate at rank K."""
+    B, Q, H, _ = q_idx.shape
+    qp = i64(q_pos)
+    E = k_idx.shape[1]
+    ec = i64(e_count) if e_count is not None else np.full(B, E)
+    for b in range(B):
+        keys = f64(k_idx[b])
+        for i in range(Q):
+            n = ocsa.n_visible(int(qp[b, i]), m, int(min(ec[b], E)))
+            ids = np.arange(n)
+            if cand is not None:
+                c = i64(cand[b, i])
+                ids = c[(c >= 0) & (c < n)]
+            R = ocsa.head_relu(f64(q_idx[b, i]), keys[ids])
+            attempt = 0
+            while not gaps.gap_ok(R @ f64(w[b, i]), K):
+                attempt += 1
+                assert attempt < 5000
+                w[b, i] = datagen.tensor(case_id, T_TEST_W, (H,), dtype, 1 / math.sqrt(H), attempt,
+                                         b, i).float()
+
+
+def assert_ids(gpu, ref, what=""):
+    g = np.asarray(gpu, dtype=np.int64)
+    r = np.asarray(ref, dtype=np.int64)
+    if not np.array_equal(g, r):
+        bad = np.argwhere(g != r)
+        raise AssertionError(f"{what}: ids differ at {bad[:5].tolist()} "
+                             f"(gpu {g[tuple(bad[0])]}, oracle {r[tuple(bad[0])]})")
+
+
+def assert_scores(gpu, ref, scale, rel=1e-3, what=""):
+    """|S_gpu - S_ref| <= rel * A + tiny, A = sum_h |w| relu(q.k)."""
+    g = np.asarray(gpu, dtype=np.float64)
+    err = np.abs(g - ref)
+    tol = rel * scale + 1e-30
+    if not np.all(err <= tol):
+        k = int(np.argmax(err / tol))
+        raise AssertionError(f"{what}: score error {err[k]:.3e} > {tol[k]:.3e} at {k}")
+
+
+def assert_rows_close(gpu, ref, rel=2e-2, what=""):
+    """Per (query, head) row: max|diff| <= rel * max|ref| (rows of ref that are all zero must be
+    zero on the GPU up to 1e-30)."""
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    err = np.abs(g - r).max(axis=-1)
+    den = np.abs(r).max(axis=-1)
+    ok = err <= rel * den + 1e-30
+    if not np.all(ok):
+        k = np.argwhere(~ok)[0]
+        raise AssertionError(f"{what}: row {k.tolist()} error {err[tuple(k)]:.3e} vs "
+                             f"max|ref| {den[tuple(k)]:.3e}")
+
+
+def bf16_ulp(x):
+    """The spacing of bf16 values at |x| (normal range)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(np.maximum(x, 2.0 ** -126))
+    return np.ldexp(1.0, e - 8)
+
+
+def assert_pooled(got, exact, xabs_max, what=""):
+    """A pooled entry computed in fp32 and stored once by RNE: |got - exact| is at most half a
+    storage spacing at max(|got|, |exact|) plus the fp32 arithmetic error, bounded by
+    (m + 8) * 2^-24 * max_j |x_j| <= 4e-6 * max_j |x_j| for m <= 16."""
+    got = np.asarray(got, dtype=np.float64)
+    exact = np.asarray(exact, dtype=np.float64)
+    tol = 0.5 * bf16_ulp(np.maximum(np.abs(got), np.abs(exact))) + 4e-6 * np.asarray(xabs_max)
+    bad = np.abs(got - exact) > tol
+    if np.any(bad):
+        k = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: pooled value {got[k]} vs exact {exact[k]} (tol {tol[k]:.3e})")
+
+
+def pooled_xmax(x, m):
+    """max_j |x[e*m + j, c]| per (entry, channel) of rows x [..., T, d]."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    sh = a.shape
+    return a.reshape(sh[:-2] + (sh[-2] // m, m, sh[-1])).max(axis=-2)

@@ -1,0 +1,233 @@
+"""GPU parity of each libcsa call against the float64 oracle, at sizes the oracle finishes in
+seconds that still span several tiles and a ragged tail. All calls go through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import sparse_long_context_csa_amd as csa
+from gpu_helpers import (assert_ids, assert_pooled, assert_rows_close, assert_scores, dev,
+                         fix_gaps, pooled_xmax)
+from oracle import csa as ocsa
+from oracle import gaps, pipeline
+from oracle.pipeline import f64, i64
+
+pytestmark = pytest.mark.gpu
+CID = 7000
+
+
+def T(tid, shape, dtype="bf16", scale=1.0, *extra):
+    return datagen.tensor(CID, tid, shape, dtype, scale, 0, *extra)
+
+
+# ------------------------------------------------------------------------------ compress
+@pytest.mark.parametrize("dtype,m,dim,n_tok,n_seq", [
+    ("bf16", 4, 512, 4096, 2), ("bf16", 1, 128, 37, 3), ("bf16", 2, 64, 130, 1),
+    ("bf16", 8, 136, 64, 2), ("f32", 4, 64, 2048, 1), ("f32", 16, 8, 32, 2),
+])
+def test_compress(dtype, m, dim, n_tok, n_seq):
+    x = T(1, (n_seq, n_tok, dim), dtype, 1.0, m, dim)
+    z = T(2, (n_seq, n_tok, dim), dtype, 1.0, m, dim)
+    b = T(3, (m, dim), dtype, 0.5, m, dim)
+    out = csa.compress(dev(x), dev(z), dev(b), m)
+    torch.cuda.synchronize()
+    ref64 = ocsa.compress(f64(x), f64(z), f64(b), m)
+    got = f64(out.cpu())
+    if dtype == "bf16":
+        # fp32 arithmetic then one RNE store
+        assert_pooled(got, ref64, pooled_xmax(f64(x), m), "compress")
+        frac = np.mean(got == ocsa.round_bf16(ref64))
+        assert frac > 0.999, frac
+    else:
+        np.testing.assert_allclose(got, ref64, rtol=2e-6, atol=2e-6 * np.abs(f64(x)).max())
+
+
+def test_compress_into_cache_offset():
+    m, dim, n_tok, e_cap, e0 = 4, 512, 256, 200, 100
+    x, z, b = T(4, (2, n_tok, dim)), T(5, (2, n_tok, dim)), T(6, (m, dim))
+    cache = torch.zeros(2, e_cap, dim, dtype=torch.bfloat16, device="cuda")
+    csa.compress(dev(x), dev(z), dev(b), m, out=cache[:, e0:], out_seq_stride=e_cap * dim)
+    torch.cuda.synchronize()
+    got = f64(cache.cpu())
+    exact = ocsa.compress(f64(x), f64(z), f64(b), m)
+    assert np.all(got[:, :e0] == 0) and np.all(got[:, e0 + n_tok // m:] == 0)
+    assert_pooled(got[:, e0:e0 + n_tok // m], exact, pooled_xmax(f64(x), m), "cache offset")
+
+
+# ------------------------------------------------------------------------------ index + top-k
+def index_case(B, Q, E, H, d, dtype, t_lo, t_hi, m=4, seed=0):
+    q = T(10, (B, Q, H, d), dtype, 1 / math.sqrt(d), seed)
+    w = T(11, (B, Q, H), dtype, 1 / math.sqrt(H), seed).float()
+    k = T(12, (B, E, d), dtype, 1 / math.sqrt(d), seed)
+    g = np.random.default_rng(seed)
+    pos = torch.from_numpy(g.integers(t_lo, t_hi, size=(B, Q)).astype(np.int64))
+    return q, w, k, pos
+
+
+def check_index(q, w, k, pos, m, K, e_count=None, cand=None, dtype="bf16", rows=None):
+    fix_gaps(CID, q, w, k, pos, e_count, m, K, cand=cand, dtype=dtype)
+    res = csa.index_topk(dev(q), dev(w), dev(k), dev(pos), m, K, e_count=dev(e_count),
+                         cand=dev(cand), want_scores=True, want_all=True)
+    idx, osc, alls = [x.cpu() for x in res]
+    B, Q = pos.shape
+    ref = pipeline.index_topk(q, w, k, pos, e_count, m, K, rows=rows, cand=cand)
+    for (b, i), (ids, s, sid) in ref.items():
+        assert_ids(idx[b, i].numpy(), ids, f"row {(b, i)}")
+        A = ocsa.score_scale(f64(q[b, i]), f64(w[b, i]), f64(k[b])[sid]) if sid.size else np.zeros(0)
+        if cand is None:
+            assert_scores(alls[b, i, :sid.size].numpy(), s, A, what=f"scores {(b, i)}")
+            assert np.all(np.isneginf(alls[b, i, sid.size:].numpy()))
+        else:
+            c = i64(cand[b, i])
+            pos_of = {int(v): j for j, v in enumerate(c) if 0 <= v}
+            got = np.array([alls[b, i, pos_of[int(v)]].item() for v in sid])
+            assert_scores(got, s, A, what=f"cand scores {(b, i)}")
+        sel = ids >= 0
+        exp = dict(zip(sid.tolist(), s.tolist()))
+        got_s = osc[b, i].numpy()
+        for j in np.nonzero(sel)[0]:
+            e = exp[int(ids[j])]
+            assert abs(got_s[j] - e) <= 1e-3 * A[list(sid).index(ids[j])] + 1e-30
+        assert np.all(np.isneginf(got_s[~sel]))
+
+
+def test_index_decode_fast_path():
+    # 64x128 bf16, few query rows: MFMA scan; ragged visible counts incl. partial tiles
+    q, w, k, pos = index_case(3, 1, 5000, 64, 128, "bf16", 4 * 700, 4 * 5000)
+    pos[0, 0] = 4 * 5000 - 1      # every entry visible
+    pos[1, 0] = 2049              # 512 visible, K = 512 -> exactly all
+    check_index(q, w, k, pos, 4, 512)
+
+
+def test_index_decode_small_visible():
+    q, w, k, pos = index_case(2, 2, 300, 64, 128, "bf16", -3, 60, seed=1)
+    pos[0, 0] = -1                # nothing visible
+    pos[0, 1] = 2                 # t < m: nothing visible
+    pos[1, 0] = 3                 # one entry
+    check_index(q, w, k, pos, 4, 16)
+
+
+def test_index_e_count_caps_visibility():
+    q, w, k, pos = index_case(2, 1, 3000, 64, 128, "bf16", 11990, 12000, seed=2)
+    e_count = torch.tensor([1000, 2999], dtype=torch.int32)
+    check_index(q, w, k, pos, 4, 128, e_count=e_count)
+
+
+def test_index_long_rows_segmented_select():
+    # more candidates than one workgroup holds (32,768): segment + merge levels
+    q, w, k, pos = index_case(2, 1, 70000, 64, 128, "bf16", 4 * 70000 - 1, 4 * 70000, seed=3)
+    check_index(q, w, k, pos, 4, 512)
+
+
+def test_index_prefill_fast_path():
+    # >= 16 query rows: LDS-tiled MFMA scan; consecutive positions, causal edge inside tiles
+    B, Q, E = 1, 40, 3000
+    q, w, k, _ = index_case(B, Q, E, 64, 128, "bf16", 0, 1, seed=4)
+    pos = torch.arange(4 * E - Q - 5, 4 * E - 5, dtype=torch.int64).view(1, Q)
+    check_index(q, w, k, pos, 4, 512)
+
+
+def test_index_candidates():
+    q, w, k, pos = index_case(2, 1, 4000, 64, 128, "bf16", 15000, 16000, seed=5)
+    g = np.random.default_rng(5)
+    cand = np.full((2, 1, 1500), -1, np.int32)
+    for b in range(2):
+        c = np.sort(g.choice(4000, size=1400, replace=False))
+        cand[b, 0, :1400] = c      # some beyond the visible count: ignored
+    cand = torch.from_numpy(cand)
+    check_index(q, w, k, pos, 4, 256, cand=cand)
+
+
+@pytest.mark.parametrize("H,d,dtype", [(4, 32, "f32"), (16, 64, "bf16"), (64, 128, "f32")])
+def test_index_generic_path(H, d, dtype):
+    q, w, k, pos = index_case(2, 3, 700, H, d, dtype, 4 * 100, 4 * 700, seed=6)
+    check_index(q, w, k, pos, 4, 64, dtype=dtype)
+
+
+def test_index_blocks_pool():
+    B, E, bs, mb = 2, 6000, 8, 64
+    q, w, k, pos = index_case(B, 1, E, 64, 128, "bf16", E - 5, E, m=1, seed=7)
+    pos[1, 0] = 4001                         # partial last block
+    # gap on block maxima at rank mb
+    for b in range(B):
+        n = ocsa.n_visible(int(pos[b, 0]), 1, E)
+        R = ocsa.head_relu(f64(q[b, 0]), f64(k[b, :n]))
+        attempt = 0
+        while not gaps.gap_ok(ocsa.block_maxima(R @ f64(w[b, 0]), bs), mb):
+            attempt += 1
+            w[b, 0] = datagen.tensor(CID, 41, (64,), "bf16", 1 / 8, attempt, b).float()
+    pool = csa.index_blocks(dev(q), dev(w), dev(k), dev(pos), 1, bs, mb, top_k=0).cpu()
+    for b in range(B):
+        ref_pool, s = pipeline.index_blocks_row(q[b, 0], w[b, 0], k[b], int(pos[b, 0]), 1, E, bs, mb)
+        got = pool[b, 0].numpy()
+        n = ref_pool.size
+        assert_ids(got[:n], ref_pool, f"pool {b}")
+        assert np.all(got[n:] == -1)
+
+
+# ------------------------------------------------------------------------------ attention
+def attn_case(B, Q, E, H, D, K, W, w_cap, dtype, seed=0, t_lo=None, t_hi=None):
+    q = T(20, (B, Q, H, D), dtype, 1.0 if dtype == "f32" else 1 / math.sqrt(D), seed)
+    kv = T(21, (B, E, D), dtype, 1.0 if dtype == "f32" else 1.0, seed)
+    win = T(22, (B, w_cap, D), dtype, 1.0, seed)
+    sink = T(23, (H,), "f32", 1.0, seed)
+    g = np.random.default_rng(100 + seed)
+    idx = np.full((B, Q, K), -1, np.int32)
+    for b in range(B):
+        for i in range(Q):
+            n = int(g.integers(0, K + 1))
+            idx[b, i, :n] = np.sort(g.choice(E, size=n, replace=False))
+            g.shuffle(idx[b, i])
+    lo = t_lo if t_lo is not None else 0
+    hi = t_hi if t_hi is not None else 10 * w_cap
+    pos = torch.from_numpy(g.integers(lo, hi, size=(B, Q)).astype(np.int64))
+    return q, kv, torch.from_numpy(idx), win, sink, pos
+
+
+def check_attn(q, kv, idx, win, sink, pos, w_cap, W, scale, dtype):
+    out = csa.sparse_attn(dev(q), dev(kv), dev(idx), dev(win), w_cap, W, dev(pos), dev(sink),
+                          scale).cpu()
+    ref = pipeline.sparse_attn(q, kv, idx, win, w_cap, W, pos, sink, scale, dtype)
+    for (b, i), r in ref.items():
+        assert_rows_close(f64(out[b, i]), r, 2e-2, f"attn {(b, i)}")
+
+
+@pytest.mark.parametrize("B,Q,E,K,W,w_cap", [
+    (4, 1, 5000, 512, 128, 128),       # decode: row splits + combine
+    (2, 3, 3000, 100, 128, 256),       # ragged tiles, ring larger than the window
+    (1, 300, 2000, 512, 128, 4096),    # many rows: one workgroup per row
+    (3, 1, 100, 0, 128, 128),          # window only
+    (2, 2, 1000, 64, 0, 1),            # selection only
+])
+def test_attention_fast_path(B, Q, E, K, W, w_cap):
+    q, kv, idx, win, sink, pos = attn_case(B, Q, E, 64, 512, K, W, w_cap, "bf16",
+                                           seed=B * 7 + Q, t_lo=0, t_hi=5 * w_cap)
+    pos.view(-1)[0] = 5                # a window clamped at position 0
+    check_attn(q, kv, idx, win, sink, pos, w_cap, W, 1 / math.sqrt(512), "bf16")
+
+
+def test_attention_sharp_logits():
+    # scaled queries make the softmax peaked: exercises the running-max rescale
+    q, kv, idx, win, sink, pos = attn_case(2, 1, 3000, 64, 512, 512, 128, 128, "bf16", seed=9)
+    q = (q.float() * 150).to(torch.bfloat16)
+    check_attn(q, kv, idx, win, sink, pos, 128, 128, 1 / math.sqrt(512), "bf16")
+
+
+def test_attention_no_sink_and_empty():
+    q, kv, idx, win, sink, pos = attn_case(2, 1, 500, 64, 512, 64, 16, 16, "bf16", seed=10)
+    idx[0, 0] = -1
+    pos[0, 0] = -1                     # nothing at all: output 0
+    out = csa.sparse_attn(dev(q), dev(kv), dev(idx), dev(win), 16, 16, dev(pos), None, 0.05).cpu()
+    ref = pipeline.sparse_attn(q, kv, idx, win, 16, 16, pos, None, 0.05, "bf16")
+    assert torch.all(out[0, 0] == 0)
+    for (b, i), r in ref.items():
+        assert_rows_close(f64(out[b, i]), r, 2e-2, f"attn {(b, i)}")
+
+
+@pytest.mark.parametrize("H,D,dtype", [(4, 64, "f32"), (8, 128, "bf16"), (64, 512, "f32"),
+                                       (3, 40, "f32")])
+def test_attention_generic_path(H, D, dtype):
+    q, kv, idx, win, sink, pos = attn_case(2, 3, 400, H, D, 64, 32, 64, dtype, seed=11)
+    check_attn(q, kv, idx, win, sink, pos, 64, 32, 1 / math.sqrt(D), dtype)

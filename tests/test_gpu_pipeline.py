@@ -1,0 +1,119 @@
+"""GPU parity of whole paths: the tiny fp32 forward (all 2,048 queries) and the fused decode
+step (flat and hierarchical, several attention calls), against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import sparse_long_context_csa_amd as csa
+from gpu_helpers import assert_ids, assert_pooled, assert_rows_close, dev
+from oracle import csa as ocsa
+from oracle import gaps, pipeline
+from oracle.pipeline import f64
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_forward_fp32():
+    """The tiny workload: compress 2,048 raw rows 4:1, index with 4x32 heads, Top-64 under
+    the causal limit, attend (window 64, sink) for every one of the 2,048 queries."""
+    case = datagen.make_case(datagen.CONFIGS[1])
+    gaps.enforce_tiny(case)
+    spec = case["spec"]
+    ref = pipeline.tiny_forward(case)
+    kv = csa.compress(dev(case["x"]), dev(case["z"]), dev(case["bias"]), spec.m)
+    idx = csa.index_topk(dev(case["q_idx"]), dev(case["w"]), dev(case["k_idx"]),
+                         dev(case["q_pos"]), spec.m, spec.K, e_count=dev(case["e_count"]))
+    out = csa.sparse_attn(dev(case["q"]), kv, idx, dev(case["x"]), spec.L, spec.W,
+                          dev(case["q_pos"]), dev(case["sink"]), spec.softmax_scale)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(f64(kv.cpu()), ref["kv"], rtol=2e-6, atol=1e-6)
+    idx, out = idx.cpu(), out.cpu()
+    for (b, i), ids in ref["ids"].items():
+        assert_ids(idx[b, i].numpy(), ids, f"query {i}")
+        assert_rows_close(f64(out[b, i]), ref["out"][(b, i)], 2e-2, f"query {i}")
+
+
+def run_step(case):
+    spec = case["spec"]
+    g = {k: dev(v) for k, v in case.items() if isinstance(v, torch.Tensor)}
+    rings = [dev(r).clone() for r in case["rings"]]
+    win_new = [g["x_new"] if (c == 0 and datagen.ring_from_raw(spec)) else None
+               for c in range(spec.n_attn)]
+    kw = {}
+    if spec.block_size:
+        kw = dict(block_size=spec.block_size, max_blocks=spec.max_blocks, q_idx2=g["q_idx2"],
+                  w2=g["w2"])
+    st = {k: g[k].clone() for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
+    step = csa.DecodeStep(m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
+                          pos=g["pos"], x_new=g["x_new"], z_new=g["z_new"], xi_new=g["xi_new"],
+                          zi_new=g["zi_new"], bias=g["bias"], bias_i=g["bias_i"],
+                          q_idx=g["q_idx"], w=g["w"], q=[dev(x) for x in case["q"]], win=rings,
+                          win_new=win_new, sink=[dev(x) for x in case["sink"]], **st, **kw)
+    out, idx = step()
+    torch.cuda.synchronize()
+    return step, st, rings, [o.cpu() for o in out], idx.cpu()
+
+
+def check_step(case, ref, st, rings, out, idx):
+    spec = case["spec"]
+    for b in range(spec.B):
+        t = int(case["pos"][b])
+        assert_ids(idx[b].numpy(), ref["ids"][b], f"seq {b}")
+        for c in range(spec.n_attn):
+            assert_rows_close(f64(out[c][b]), ref["out"][b][c], 2e-2, f"seq {b} call {c}")
+        slot = t % spec.m
+        assert torch.equal(st["x_tail"][b, slot].cpu(), case["x_new"][b])
+        assert torch.equal(st["zi_tail"][b, slot].cpu(), case["zi_new"][b])
+        if b in ref["kv_new"]:
+            e = (t + 1) // spec.m - 1
+            for name, xs, zs, xn, zn, bias in (
+                    ("kv", "x_tail", "z_tail", "x_new", "z_new", "bias"),
+                    ("k_idx", "xi_tail", "zi_tail", "xi_new", "zi_new", "bias_i")):
+                x = f64(case[xs][b]).copy()
+                z = f64(case[zs][b]).copy()
+                x[slot] = f64(case[xn][b])
+                z[slot] = f64(case[zn][b])
+                exact = ocsa.compress(x, z, f64(case[bias]), spec.m)[0]
+                assert_pooled(f64(st[name][b, e].cpu()), exact, np.abs(x).max(axis=0),
+                              f"{name} entry {e} of seq {b}")
+        if datagen.ring_from_raw(spec):
+            assert torch.equal(rings[0][b, t % spec.w_cap].cpu(), case["x_new"][b])
+
+
+def test_decode_step_flat_ragged():
+    spec = datagen.CaseSpec(7100, "decode", B=5, L=24000, m=4, w_cap=256, ragged=True)
+    case = datagen.make_case(spec)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    step, st, rings, out, idx = run_step(case)
+    check_step(case, ref, st, rings, out, idx)
+    # the same step again (idempotent state) is bitwise identical
+    out2, idx2 = step()
+    torch.cuda.synchronize()
+    assert torch.equal(idx2.cpu(), idx)
+    assert torch.equal(out2[0].cpu(), out[0])
+
+
+def test_decode_step_hierarchical_three_calls():
+    spec = datagen.CaseSpec(7101, "decode", B=3, L=40000, m=1, w_cap=128, block_size=8,
+                            max_blocks=512, n_attn=3, ragged=True)
+    case = datagen.make_case(spec)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    _, st, rings, out, idx = run_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
+def test_decode_step_incomplete_block_writes_no_entry():
+    spec = datagen.CaseSpec(7102, "decode", B=4, L=9000, m=4, w_cap=128, ragged=True)
+    case = datagen.make_case(spec)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    kv0 = case["kv"].clone()
+    _, st, rings, out, idx = run_step(case)
+    check_step(case, ref, st, rings, out, idx)
+    for b in range(spec.B):
+        t = int(case["pos"][b])
+        if (t + 1) % 4:
+            assert torch.equal(st["kv"][b].cpu(), kv0[b])
