@@ -57,7 +57,7 @@ class HipEvents:
 
 def cpu_baseline(case, budget_s):
     """The float64 oracle's decode step, on the host cores, over whole sequences of the same
-    workload until about budget_s seconds of work."""
+    workload until about budget_s seconds of work (at most 200 queries)."""
     from oracle import pipeline
     try:
         from threadpoolctl import threadpool_info
@@ -70,11 +70,12 @@ def cpu_baseline(case, budget_s):
         pipeline.decode_step(case, seqs=[done % B])
         done += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 64:
+        if el >= budget_s or done >= 200:
             break
     return {"value": done / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} decode queries (whole sequences of the same workload: 262,144 "
-                      f"entries scanned, Top-512, 640-row attention) in {el:.1f} s, float64 NumPy"}
+            "sample": f"{done} decode queries (whole sequences of the same workload, each a "
+                      f"full step: pool, scan of every visible entry, Top-K, attention) in "
+                      f"{el:.1f} s, float64 NumPy"}
 
 
 def main():
@@ -85,6 +86,10 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="state copies rotated across steps")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step from a captured HIP graph instead of launching it")
+    ap.add_argument("--config", type=int, default=4, choices=(2, 4, 5),
+                    help="decode workload (4: the 1M-context headline)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -98,46 +103,77 @@ def main():
     import sparse_long_context_csa_amd as csa
     from sparse_long_context_csa_amd import accounting as acc
 
-    spec = datagen.CONFIGS[4]
+    spec = datagen.CONFIGS[args.config]
     t0 = time.time()
     case = datagen.make_case(spec)
     log(f"generated inputs in {time.time() - t0:.1f} s")
     dev = torch.device("cuda:0")
     shared = {k: case[k].to(dev) for k in ("pos", "x_new", "z_new", "xi_new", "zi_new", "bias",
                                             "bias_i", "q_idx", "w")}
+    hier = {}
+    if spec.block_size:
+        hier = dict(block_size=spec.block_size, max_blocks=spec.max_blocks,
+                    q_idx2=case["q_idx2"].to(dev), w2=case["w2"].to(dev))
     qs = [x.to(dev) for x in case["q"]]
     sinks = [x.to(dev) for x in case["sink"]]
     steps_objs = []
     for c in range(args.copies):
         st = {k: case[k].to(dev) for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
         rings = [r.to(dev) for r in case["rings"]]
+        win_new = [shared["x_new"] if (i == 0 and datagen.ring_from_raw(spec)) else None
+                   for i in range(spec.n_attn)]
         steps_objs.append(csa.DecodeStep(
             m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"], q=qs, win=rings,
-            win_new=[shared["x_new"]], sink=sinks, **shared, **st))
+            win_new=win_new, sink=sinks, **shared, **st, **hier))
     torch.cuda.synchronize()
     log(f"device state ready: {args.copies} copies, "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
 
     ev = HipEvents()
     n_ev = 5
+    stream = torch.cuda.current_stream()
     for i in range(args.warmup):
         steps_objs[i % args.copies]()
     torch.cuda.synchronize()
-    events = [[ev.create() for _ in range(n_ev)] for _ in range(args.steps)]
+    graphs = []
+    if args.graph:
+        # one HIP graph per state copy: the whole fused step (ingest, scan, select, attention)
+        # replays with a single launch
+        for st in steps_objs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                st()
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % args.copies].replay()
+        torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, no profiling hooks
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        s = steps_objs[i % args.copies]
-        s.set_events(events[i])
-        s()
+        if graphs:
+            graphs[i % args.copies].replay()
+        else:
+            steps_objs[i % args.copies]()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    for s in steps_objs:
-        s.set_events([])
+
+    # separate pass: phase boundaries recorded with HIP events on the launch stream
+    n_prof = min(args.steps, 100)
+    events = [[ev.create() for _ in range(n_ev)] for _ in range(n_prof)]
+    for i in range(n_prof):
+        st = steps_objs[i % args.copies]
+        st.set_events(events[i])
+        st()
+    torch.cuda.synchronize()
+    for st in steps_objs:
+        st.set_events([])
     phases = [[ev.ms(e[j], e[j + 1]) for j in range(n_ev - 1)] for e in events]
     for e in events:
         for h in e:
             ev.destroy(h)
+    del stream
     if args.calib_copy_mib:
         n = args.calib_copy_mib * 2**20 // 4
         a = torch.ones(n, dtype=torch.float32, device=dev)
@@ -153,18 +189,23 @@ def main():
     E = spec.entries
     scan_bytes = acc.scan_bytes(spec.B, E, spec.H_I, spec.d_I)
     step_bytes = acc.decode_step_bytes(B=spec.B, n_vis=E, m=spec.m, D=spec.D, H=spec.H,
-                                       H_I=spec.H_I, d_I=spec.d_I, K=spec.K, W=spec.W).total
+                                       H_I=spec.H_I, d_I=spec.d_I, K=spec.K, W=spec.W,
+                                       n_attn=spec.n_attn,
+                                       pool=spec.block_size * spec.max_blocks,
+                                       ring_write=datagen.ring_from_raw(spec)).total
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": datagen.WORKLOAD_NAMES[4], "batch": spec.B, "context": spec.L,
+        "config": {"workload": datagen.WORKLOAD_NAMES[args.config], "batch": spec.B,
+                   "context": spec.L,
                    "entries": E, "m": spec.m, "top_k": spec.K, "window": spec.W,
                    "heads": spec.H, "head_dim": spec.D, "idx_heads": spec.H_I,
-                   "idx_dim": spec.d_I, "state_copies": args.copies},
-        "roofline": {"bound": "hbm", "kernel": "scan_decode_kernel (indexer scan)",
+                   "idx_dim": spec.d_I, "state_copies": args.copies,
+                   "launch": "hip_graph" if args.graph else "eager"},
+        "roofline": {"bound": "hbm", "kernel": "scan_decode_kernel (indexer scan, stage 1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_launch_us": round(scan_ms * 1e3, 2),
@@ -172,9 +213,11 @@ def main():
         "step_hbm": {"algorithmic_bytes": step_bytes,
                      "achieved_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-        "phases_us": {"ingest_compress": round(mean[0] * 1e3, 2), "index_scan": round(mean[1] * 1e3, 2),
+        "phases_us_eager_with_events": {"ingest_compress": round(mean[0] * 1e3, 2), "index_scan": round(mean[1] * 1e3, 2),
                       "select": round(mean[2] * 1e3, 2), "attention": round(mean[3] * 1e3, 2)},
     }
+    if args.config != 4:
+        res["metric"] = f"CSA decode queries/sec ({datagen.WORKLOAD_NAMES[args.config]})"
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     print(json.dumps(res), flush=True)

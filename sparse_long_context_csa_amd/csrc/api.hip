@@ -82,11 +82,17 @@ int check_index_common(int64_t n_seq, int64_t n_q, int64_t e_cap, int32_t H, int
 }
 
 // scan of rows into a TopkWs (shared by the calls and the decode step)
+// The scan also clears the merge tickets of the Top-K (K = top_k) that will read its scores.
 hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, const int64_t* q_pos,
                      const int32_t* e_count, const int32_t* cand, int64_t n_cand, int64_t n_seq,
                      int64_t n_q, int64_t e_cap, int H, int d, int m, const TopkWs& ws,
-                     hipStream_t s) {
+                     int top_k, hipStream_t s) {
   ScanArgs a;
+  const int64_t rows = n_seq * n_q;
+  a.zero = top_k > 0 ? topk_ticket(ws.scratch, rows, cand ? n_cand : e_cap, top_k,
+                                   cand != nullptr)
+                     : nullptr;
+  a.n_zero = a.zero ? rows : 0;
   a.dt = dt; a.q = q; a.w = w; a.keys = keys; a.q_pos = q_pos; a.e_count = e_count;
   a.cand = cand; a.n_cand = n_cand; a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap;
   a.H = H; a.d = d; a.m = m; a.scores = ws.scores; a.score_stride = ws.stride;
@@ -101,20 +107,23 @@ hipError_t select_rows(const TopkWs& ws, int64_t rows, int64_t max_count, const 
   t.scores = ws.scores; t.stride = ws.stride; t.ids = ids; t.id_stride = id_stride;
   t.id_limit = id_limit; t.count = ws.count; t.rows = rows; t.max_count = max_count; t.K = K;
   t.out_idx = out_idx; t.out_score = out_score; t.out_stride = K; t.scratch = scratch;
+  t.tickets_zeroed = true;
   return launch_topk(t, s);
 }
 
 // stage 1 of the hierarchical indexer after the scan: block maxima, top blocks, pool
 hipError_t pool_rows(int64_t rows, int64_t e_cap, int bs, int mb, int32_t* out_pool,
                      const BlocksWs& ws, hipStream_t s) {
+  const int64_t nbmax = (e_cap + bs - 1) / bs;
+  int32_t* tk = topk_ticket(ws.scratch2, rows, nbmax, mb, false);
   hipError_t e = launch_block_max(ws.tk.scores, ws.tk.stride, ws.tk.count, rows, e_cap, bs,
-                                  ws.bmax, ws.bstride, ws.nb, s);
+                                  ws.bmax, ws.bstride, ws.nb, tk, tk ? rows : 0, s);
   if (e != hipSuccess) return e;
   TopkArgs t;
   t.scores = ws.bmax; t.stride = ws.bstride; t.ids = nullptr; t.id_stride = 0;
   t.id_limit = nullptr; t.count = ws.nb; t.rows = rows; t.max_count = (e_cap + bs - 1) / bs;
   t.K = mb; t.out_idx = ws.blocks; t.out_score = nullptr; t.out_stride = mb;
-  t.scratch = ws.scratch2;
+  t.scratch = ws.scratch2; t.tickets_zeroed = true;
   e = launch_topk(t, s);
   if (e != hipSuccess) return e;
   return launch_pool_build(ws.blocks, rows, mb, bs, ws.tk.n_vis, out_pool, s);
@@ -127,7 +136,7 @@ hipError_t blocks_rows(int dt, const void* q, const float* w, const void* keys,
                        int top_k, int32_t* out_idx, const BlocksWs& ws, hipStream_t s) {
   const int64_t rows = n_seq * n_q;
   hipError_t e = scan_rows(dt, q, w, keys, q_pos, e_count, nullptr, 0, n_seq, n_q, e_cap, H, d,
-                           m, ws.tk, s);
+                           m, ws.tk, out_idx ? top_k : 0, s);
   if (e != hipSuccess) return e;
   if (out_idx) {
     e = select_rows(ws.tk, rows, e_cap, nullptr, 0, nullptr, top_k, out_idx, nullptr,
@@ -199,7 +208,7 @@ int csa_index_topk(const void* q_idx, const float* w, const void* k_idx, const i
   Carver c(ws);
   const TopkWs tw = carve_topk(c, n_seq * n_q, n_keys, top_k);
   hipError_t e = scan_rows(dtype, q_idx, w, k_idx, q_pos, e_count, cand, n_cand, n_seq, n_q,
-                           e_cap, idx_heads, idx_dim, m, tw, s);
+                           e_cap, idx_heads, idx_dim, m, tw, top_k, s);
   if (e != hipSuccess) return CSA_ERR_HIP;
   e = select_rows(tw, n_seq * n_q, n_keys, cand, n_cand, cand ? tw.n_vis : nullptr, top_k,
                   out_idx, out_score, tw.scratch, s);
@@ -382,20 +391,20 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   if (d->block_size > 0) {
     const int np = d->block_size * d->max_blocks;
     if (scan_rows(d->dtype, d->q_idx, d->w, d->k_idx, d->pos, nullptr, nullptr, 0, rows, 1,
-                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.blocks.tk, s) != hipSuccess)
+                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.blocks.tk, 0, s) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
     if (pool_rows(rows, d->e_cap, d->block_size, d->max_blocks, w.pool, w.blocks, s) != hipSuccess)
       return CSA_ERR_HIP;
     if (scan_rows(d->dtype, d->q_idx2, d->w2, d->k_idx, d->pos, nullptr, w.pool, np, rows, 1,
-                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, s) != hipSuccess)
+                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, d->top_k, s) != hipSuccess)
       return CSA_ERR_HIP;
     if (select_rows(w.flat, rows, np, w.pool, np, w.flat.n_vis, d->top_k, d->out_idx, nullptr,
                     w.flat.scratch, s) != hipSuccess)
       return CSA_ERR_HIP;
   } else {
     if (scan_rows(d->dtype, d->q_idx, d->w, d->k_idx, d->pos, nullptr, nullptr, 0, rows, 1,
-                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, s) != hipSuccess)
+                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, d->top_k, s) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
     if (select_rows(w.flat, rows, d->e_cap, nullptr, 0, nullptr, d->top_k, d->out_idx, nullptr,

@@ -56,6 +56,7 @@ static int attn_splits(int64_t rows, int top_k, int window, int H, int D, int dt
   if (rows >= 256 || tiles <= 1) return 1;
   int64_t want = 256 / rows;
   if (want > tiles) want = tiles;
+  if (want > 256) want = 256;
   return int(want < 1 ? 1 : want);
 }
 
@@ -100,12 +101,16 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, int nsplit, 
   for (int64_t j = j0; j < j1; j += kTile) {
     const uint16_t* src = row_ptr<uint16_t>(a, r, sq, t, j + grow, int(j1));
     if (gcb == 0) rowok[grow] = src != nullptr;
+    // all 8 loads issued back to back (a missing row reads the query row and is zeroed)
+    const uint16_t* srcc = src ? src : reinterpret_cast<const uint16_t*>(a.q) + r * kAH * kAD;
+    bf16x8_t vv8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      vv8[k] = *reinterpret_cast<const bf16x8_t*>(srcc + (gcb + 8 * k) * 8);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int c = gcb + 8 * k;
-      bf16x8_t v;
-      if (src) v = *reinterpret_cast<const bf16x8_t*>(src + c * 8);
-      else v = bf16x8_t{};
+      const bf16x8_t v = src ? vv8[k] : bf16x8_t{};
       *reinterpret_cast<bf16x8_t*>(&kvs[grow * kKvRow + c * 16]) = v;
       const uint16_t* hv = reinterpret_cast<const uint16_t*>(&v);
 #pragma unroll
@@ -201,34 +206,52 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, int nsplit, 
   }
 }
 
-// Merge the row splits of each (row, head) in split order; grid (H, rows), D threads/2.
+// Merge the row splits of each (row, head) in split order: grid (H, rows). The split
+// weights e^{m_s - M} / den are computed once into LDS; every output element then sums its
+// nsplit partials with independent loads.
+constexpr int kMaxSplit = 256;
+
 template <typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nsplit) {
+  __shared__ float wgt[kMaxSplit];
+  __shared__ float red[2][4];
   const int64_t r = blockIdx.y;
   const int h = blockIdx.x;
   const int H = a.H, D = a.D;
-  const float* part = reinterpret_cast<const float*>(a.ws);
-  float M = a.sink ? a.sink[h] * kLog2e : neg_inf();
-  for (int sp = 0; sp < nsplit; ++sp)
-    M = fmaxf(M, part[((r * nsplit + sp) * H + h) * (D + 2) + D]);
-  float den = 0.f;
-  if (M != neg_inf()) {
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float* ph = part + ((r * nsplit + sp) * H + h) * (D + 2);
-      if (ph[D] != neg_inf()) den += ph[D + 1] * exp2f(ph[D] - M);
-    }
-    if (a.sink) den += exp2f(a.sink[h] * kLog2e - M);
+  const float* part = reinterpret_cast<const float*>(a.ws) + ((r * nsplit) * H + h) * (D + 2);
+  const int64_t sstride = int64_t(H) * (D + 2);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float mi = neg_inf(), li = 0.f;
+  if (tid < nsplit) {
+    mi = part[tid * sstride + D];
+    li = part[tid * sstride + D + 1];
   }
+  const float zs = a.sink ? a.sink[h] * kLog2e : neg_inf();
+  float M = wave_max(mi);
+  if (lane == 0) red[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3])), zs);
+  const float e = (mi == neg_inf() || M == neg_inf()) ? 0.f : exp2f(mi - M);
+  float den = wave_sum(li * e);
+  if (lane == 0) red[1][wave] = den;
+  __syncthreads();
+  den = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  if (zs != neg_inf() && M != neg_inf()) den += exp2f(zs - M);
+  if (tid < nsplit) wgt[tid] = den > 0.f ? e / den : 0.f;
+  __syncthreads();
   T* op = reinterpret_cast<T*>(a.out) + (r * H + h) * D;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+  for (int d = tid; d < D; d += blockDim.x) {
     float acc = 0.f;
-    if (den > 0.f) {
-      for (int sp = 0; sp < nsplit; ++sp) {
-        const float* ph = part + ((r * nsplit + sp) * H + h) * (D + 2);
-        if (ph[D] != neg_inf()) acc += ph[d] * exp2f(ph[D] - M);
-      }
-      acc /= den;
+    int sp = 0;
+    for (; sp + 4 <= nsplit; sp += 4) {
+      const float v0 = part[(sp + 0) * sstride + d], v1 = part[(sp + 1) * sstride + d];
+      const float v2 = part[(sp + 2) * sstride + d], v3 = part[(sp + 3) * sstride + d];
+      acc = fmaf(v0, wgt[sp + 0], acc);
+      acc = fmaf(v1, wgt[sp + 1], acc);
+      acc = fmaf(v2, wgt[sp + 2], acc);
+      acc = fmaf(v3, wgt[sp + 3], acc);
     }
+    for (; sp < nsplit; ++sp) acc = fmaf(part[sp * sstride + d], wgt[sp], acc);
     Elt<T>::store1(op + d, acc);
   }
 }

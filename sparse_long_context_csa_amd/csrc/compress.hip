@@ -17,11 +17,53 @@
 namespace csa {
 
 // Pool 8 channels over m rows. Row j's x/z come from memory (x0 + j*stride) except row
-// `own` whose values are passed in registers (xo, zo).
+// `own` whose values are passed in registers (xo, zo). For m <= kRegM every row is loaded
+// up front (one round trip to memory); longer entries take two passes over the logits.
+constexpr int kRegM = 8;
+
 template <typename T>
 __device__ __forceinline__ void pool8(const T* x0, const T* z0, int64_t stride, const T* b0,
                                       int bstride, int m, int own, const float* xo,
                                       const float* zo, float* out) {
+  if (m <= kRegM) {
+    float a[kRegM][8], xv[kRegM][8];
+#pragma unroll
+    for (int j = 0; j < kRegM; ++j) {
+      if (j < m) {
+        float bb[8];
+        if (j == own) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) { a[j][c] = zo[c]; xv[j][c] = xo[c]; }
+        } else {
+          Elt<T>::load8(z0 + j * stride, a[j]);
+          Elt<T>::load8(x0 + j * stride, xv[j]);
+        }
+        Elt<T>::load8(b0 + j * bstride, bb);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a[j][c] += bb[c];
+      }
+    }
+    float mx[8], sum[8], acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { mx[c] = a[0][c]; sum[c] = 0.f; acc[c] = 0.f; }
+#pragma unroll
+    for (int j = 1; j < kRegM; ++j)
+      if (j < m)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) mx[c] = fmaxf(mx[c], a[j][c]);
+#pragma unroll
+    for (int j = 0; j < kRegM; ++j)
+      if (j < m)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float e = expf(a[j][c] - mx[c]);
+          sum[c] += e;
+          acc[c] = fmaf(e, xv[j][c], acc[c]);
+        }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) out[c] = acc[c] / sum[c];
+    return;
+  }
   float mx[8], a[8], bb[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) mx[c] = neg_inf();

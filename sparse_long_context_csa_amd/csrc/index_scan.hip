@@ -18,6 +18,8 @@
 //  * scan_generic_kernel: any head count/dim and fp32; one thread per candidate.
 // Visibility: entry i is usable by a query at t only if m*(i+1)-1 <= t ("The sliding window
 // is not an optimisation"); positions past a row's visible count are never scored.
+#include <stdlib.h>
+
 #include "csa_common.hpp"
 #include "launch.hpp"
 
@@ -38,14 +40,22 @@ __device__ __forceinline__ int64_t row_visible(const ScanArgs& a, int64_t r) {
   return visible_entries(a.q_pos[r], a.m, cap);
 }
 
-// A operand of one query: heads 16*mt + (lane&15), channels g*32 + ks*8 .. +8 (g = lane>>4)
+// the first block of the grid clears the merge tickets of the Top-K that reads these scores
+__device__ __forceinline__ void clear_tickets(const ScanArgs& a) {
+  if (a.zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int64_t i = threadIdx.x; i < a.n_zero; i += blockDim.x) a.zero[i] = 0;
+}
+
+// A operand of one query: heads 16*mt + (lane&15), channels ks*32 + g*8 .. +8 (g = lane>>4).
+// The same channel order is used for the keys (B operand), so that in one load instruction
+// the four lanes of a key read 64 contiguous bytes of its row.
 __device__ __forceinline__ void load_query_A(const uint16_t* q, int lane, bf16x8_t (&A)[4][4]) {
   const int g = lane >> 4, col = lane & 15;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
-    const uint16_t* p = q + (16 * mt + col) * kID + g * 32;
+    const uint16_t* p = q + (16 * mt + col) * kID + g * 8;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) A[mt][ks] = *reinterpret_cast<const bf16x8_t*>(p + ks * 8);
+    for (int ks = 0; ks < 4; ++ks) A[mt][ks] = *reinterpret_cast<const bf16x8_t*>(p + ks * 32);
   }
 }
 
@@ -80,70 +90,88 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&A)[4][4], const bf1
   return part;
 }
 
+template <bool NT>
 __device__ __forceinline__ void load_key_B(const uint16_t* row, int g, bf16x8_t (&B)[4]) {
-  const bf16x8_t* p = reinterpret_cast<const bf16x8_t*>(row + g * 32);
+  const bf16x8_t* p = reinterpret_cast<const bf16x8_t*>(row + g * 8);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) B[ks] = __builtin_nontemporal_load(p + ks);
+  for (int ks = 0; ks < 4; ++ks) {
+    if (NT) B[ks] = __builtin_nontemporal_load(p + 4 * ks);
+    else B[ks] = p[4 * ks];
+  }
 }
 
 }  // namespace
 
-// grid.x: chunks of `chunk` candidate positions, grid.y: query rows. 4 waves per block, each
-// wave scores 16-key tiles (wave w takes tiles w, w+4, ... of the chunk).
-template <bool kCand>
-__global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk) {
-  const int64_t r = blockIdx.y;
-  const int64_t n_vis = row_visible(a, r);
-  const int64_t n_pos = kCand ? a.n_cand : n_vis;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    a.n_vis[r] = int32_t(n_vis);
-    a.count[r] = int32_t(n_pos);
-  }
-  const int64_t c0 = int64_t(blockIdx.x) * chunk;
-  if (c0 >= n_pos) return;
-  const int64_t c1 = c0 + chunk < n_pos ? c0 + chunk : n_pos;
+// Persistent grid: work item it = (row, chunk) = (it / cpr, it % cpr), chunk positions
+// [c*chunk, (c+1)*chunk); blocks stride over the items, so the grid is sized to the machine
+// rather than to the work (no partially filled last wave of blocks). Within an item, wave w
+// scores 16-key tiles w, w+4, ... and keeps PF further tiles of keys in flight (registers)
+// while the MFMAs of the current tile run.
+template <bool kCand, int PF, bool NT>
+__global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk, int64_t cpr,
+                                                          int64_t n_items) {
+  clear_tickets(a);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
-  const int64_t sq = r / a.n_q;
-
   bf16x8_t A[4][4];
-  load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
   float wv[4][4];
-  load_gates(a.w + r * kIH, lane, wv);
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
-  const int32_t* cand = kCand ? a.cand + r * a.n_cand : nullptr;
-  float* out = a.scores + r * a.score_stride;
-
-  // key row of position p (invalid positions read a safe row and are masked on store)
-  auto key_row = [&](int64_t p, bool& ok) -> int64_t {
-    if (p >= c1) { ok = false; return kCand ? 0 : c0; }
-    if (kCand) {
-      const int32_t id = cand[p];
-      ok = id >= 0 && id < n_vis;
-      return ok ? id : 0;
+  int64_t cur = -1;
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int64_t r = it / cpr, c = it % cpr;
+    const int64_t n_vis = row_visible(a, r);
+    const int64_t n_pos = kCand ? a.n_cand : n_vis;
+    if (c == 0 && threadIdx.x == 0) {
+      a.n_vis[r] = int32_t(n_vis);
+      a.count[r] = int32_t(n_pos);
     }
-    ok = true;
-    return p;
-  };
-
-  int64_t tile = c0 + wave * 16;
-  if (tile >= c1) return;
-  bool ok_cur;
-  bf16x8_t Bc[4], Bn[4];
-  load_key_B(kb + key_row(tile + col, ok_cur) * kID, g, Bc);
-  for (;;) {
-    const int64_t next = tile + 64;
-    bool ok_next = false;
-    const bool has_next = next < c1;
-    if (has_next) load_key_B(kb + key_row(next + col, ok_next) * kID, g, Bn);
-    const float s = tile_score(A, Bc, wv);
-    const int64_t p = tile + col;
-    if (g == 0 && p < c1) out[p] = ok_cur ? s : neg_inf();
-    if (!has_next) break;
-    tile = next;
-    ok_cur = ok_next;
+    const int64_t c0 = c * chunk;
+    if (c0 >= n_pos) continue;
+    const int64_t c1 = c0 + chunk < n_pos ? c0 + chunk : n_pos;
+    if (r != cur) {
+      load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
+      load_gates(a.w + r * kIH, lane, wv);
+      cur = r;
+    }
+    const int64_t sq = r / a.n_q;
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
+    const int32_t* cand = kCand ? a.cand + r * a.n_cand : nullptr;
+    float* out = a.scores + r * a.score_stride;
+    // key row of position p (positions past the chunk read a safe row and are not stored)
+    auto key_row = [&](int64_t p, bool& ok) -> int64_t {
+      if (p >= c1) { ok = false; return kCand ? 0 : c0; }
+      if (kCand) {
+        const int32_t id = cand[p];
+        ok = id >= 0 && id < n_vis;
+        return ok ? id : 0;
+      }
+      ok = true;
+      return p;
+    };
+    const int64_t t0 = c0 + wave * 16;
+    if (t0 >= c1) continue;
+    bf16x8_t buf[PF + 1][4];
+    bool ok[PF + 1];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) Bc[ks] = Bn[ks];
+    for (int u = 0; u <= PF; ++u) {
+      const int64_t tl = t0 + int64_t(u) * 64;
+      load_key_B<NT>(kb + key_row(tl + col, ok[u]) * kID, g, buf[u]);
+    }
+    bool more = true;
+    for (int64_t k = 0; more; k += PF + 1) {
+#pragma unroll
+      for (int u = 0; u <= PF; ++u) {
+        const int64_t tl = t0 + (k + u) * 64;
+        if (more && tl < c1) {
+          const float s = tile_score(A, buf[u], wv);
+          const int64_t p = tl + col;
+          if (g == 0 && p < c1) out[p] = ok[u] ? s : neg_inf();
+          const int64_t nx = tl + int64_t(PF + 1) * 64;
+          if (nx < c1) load_key_B<NT>(kb + key_row(nx + col, ok[u]) * kID, g, buf[u]);
+        } else {
+          more = false;
+        }
+      }
+    }
   }
 }
 
@@ -165,6 +193,7 @@ __global__ __launch_bounds__(512) void scan_prefill_kernel(ScanArgs a, int keys_
   const bool row_ok = qi < a.n_q;
   const int64_t r = sq * a.n_q + (row_ok ? qi : i0);
   const int64_t n_vis = row_ok ? row_visible(a, r) : 0;
+  clear_tickets(a);
   if (row_ok && blockIdx.x == 0 && lane == 0) {
     a.n_vis[r] = int32_t(n_vis);
     a.count[r] = int32_t(n_vis);
@@ -214,9 +243,9 @@ __global__ __launch_bounds__(512) void scan_prefill_kernel(ScanArgs a, int keys_
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         bf16x8_t B[4];
-        const unsigned char* rp = tb + (nt * 16 + col) * kPRow + g * 64;
+        const unsigned char* rp = tb + (nt * 16 + col) * kPRow + g * 16;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) B[ks] = *reinterpret_cast<const bf16x8_t*>(rp + ks * 16);
+        for (int ks = 0; ks < 4; ++ks) B[ks] = *reinterpret_cast<const bf16x8_t*>(rp + ks * 64);
         const float s = tile_score(A, B, wv);
         const int64_t p = base + nt * 16 + col;
         if (g == 0 && p < n_vis) out[p] = s;
@@ -237,6 +266,7 @@ __global__ __launch_bounds__(256) void scan_generic_kernel(ScanArgs a) {
   const int64_t r = blockIdx.y;
   const int64_t n_vis = row_visible(a, r);
   const int64_t n_pos = a.cand ? a.n_cand : n_vis;
+  clear_tickets(a);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.n_vis[r] = int32_t(n_vis);
     a.count[r] = int32_t(n_pos);
@@ -283,6 +313,67 @@ __global__ __launch_bounds__(256) void scan_generic_kernel(ScanArgs a) {
 
 static bool fast_shape(const ScanArgs& a) { return a.dt == kBF16 && a.H == kIH && a.d == kID; }
 
+// Decode-scan launch shape: positions per work item, key tiles in flight per wave beyond the
+// current one, and blocks resident per CU (the persistent grid is n_cu * blocks_per_cu).
+struct ScanTune {
+  int chunk = 2048, pf = 1, blocks_per_cu = 2, nt = 1;
+};
+static int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : dflt;
+}
+static const ScanTune& scan_tune() {
+  static const ScanTune t = [] {
+    ScanTune x;
+    x.chunk = env_int("CSA_TUNE_SCAN_CHUNK", x.chunk);
+    x.pf = env_int("CSA_TUNE_SCAN_PF", x.pf);
+    x.blocks_per_cu = env_int("CSA_TUNE_SCAN_BPC", x.blocks_per_cu);
+    x.nt = env_int("CSA_TUNE_SCAN_NT", x.nt);
+    return x;
+  }();
+  return t;
+}
+static int n_cu() {
+  static const int n = [] {
+    int dev = 0, cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cu = 256;
+    return cu > 0 ? cu : 256;
+  }();
+  return n;
+}
+
+template <bool kCand, int PF, bool NT>
+static void launch_decode(const ScanArgs& a, int64_t rows, int64_t max_pos, hipStream_t s) {
+  const ScanTune& t = scan_tune();
+  const int bpc = t.blocks_per_cu > 0 ? t.blocks_per_cu : 2;
+  int64_t grid = int64_t(n_cu()) * bpc;
+  // chunk: the tuned size, shrunk (to >= 256 positions) until there is at least one work
+  // item per resident block
+  int chunk = t.chunk > 0 ? (t.chunk + 63) / 64 * 64 : 2048;
+  while (chunk > 256 && rows * ((max_pos + chunk - 1) / chunk) < grid) chunk /= 2;
+  chunk = (chunk + 63) / 64 * 64;
+  const int64_t cpr = max_pos > 0 ? (max_pos + chunk - 1) / chunk : 1;
+  const int64_t items = rows * cpr;
+  if (grid > items) grid = items;
+  hipLaunchKernelGGL((scan_decode_kernel<kCand, PF, NT>), dim3(static_cast<unsigned>(grid)),
+                     dim3(256), 0, s, a, chunk, cpr, items);
+}
+
+template <bool kCand>
+static void launch_decode_pf(const ScanArgs& a, int64_t rows, int64_t max_pos, hipStream_t s) {
+  const bool nt = scan_tune().nt != 0;
+  switch (scan_tune().pf) {
+    case 1: nt ? launch_decode<kCand, 1, true>(a, rows, max_pos, s)
+               : launch_decode<kCand, 1, false>(a, rows, max_pos, s); break;
+    case 3: nt ? launch_decode<kCand, 3, true>(a, rows, max_pos, s)
+               : launch_decode<kCand, 3, false>(a, rows, max_pos, s); break;
+    default: nt ? launch_decode<kCand, 2, true>(a, rows, max_pos, s)
+                : launch_decode<kCand, 2, false>(a, rows, max_pos, s); break;
+  }
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   const int64_t rows = a.n_seq * a.n_q;
   if (rows == 0) return hipSuccess;
@@ -290,26 +381,18 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   if (fast_shape(a) && a.cand == nullptr && a.n_q >= 16) {
     const int keys_per_block = 4096;
     const int64_t groups = a.n_seq * ((a.n_q + kPQ - 1) / kPQ);
-    const dim3 grid(unsigned((a.e_cap + keys_per_block - 1) / keys_per_block), unsigned(groups));
+    const dim3 grid(static_cast<unsigned>((a.e_cap + keys_per_block - 1) / keys_per_block),
+                    static_cast<unsigned>(groups));
     hipLaunchKernelGGL(scan_prefill_kernel, grid, dim3(512), 0, s, a, keys_per_block);
     return hipGetLastError();
   }
   if (fast_shape(a)) {
-    const int chunk = 1024;
-    const dim3 grid(unsigned((max_pos + chunk - 1) / chunk), unsigned(rows));
-    if (grid.x == 0) {
-      const dim3 g1(1, unsigned(rows));
-      if (a.cand) hipLaunchKernelGGL(scan_decode_kernel<true>, g1, dim3(256), 0, s, a, chunk);
-      else hipLaunchKernelGGL(scan_decode_kernel<false>, g1, dim3(256), 0, s, a, chunk);
-    } else if (a.cand) {
-      hipLaunchKernelGGL(scan_decode_kernel<true>, grid, dim3(256), 0, s, a, chunk);
-    } else {
-      hipLaunchKernelGGL(scan_decode_kernel<false>, grid, dim3(256), 0, s, a, chunk);
-    }
+    if (a.cand) launch_decode_pf<true>(a, rows, max_pos, s);
+    else launch_decode_pf<false>(a, rows, max_pos, s);
     return hipGetLastError();
   }
   const unsigned gx = unsigned(max_pos > 0 ? (max_pos + 255) / 256 : 1);
-  const dim3 grid(gx, unsigned(rows));
+  const dim3 grid(gx, static_cast<unsigned>(rows));
   const size_t shm = size_t(a.H) * a.d * 4 + size_t(a.H) * 4;
   if (a.dt == kBF16)
     hipLaunchKernelGGL(scan_generic_kernel<uint16_t>, grid, dim3(256), shm, s, a);

@@ -117,3 +117,34 @@ def test_decode_step_incomplete_block_writes_no_entry():
         t = int(case["pos"][b])
         if (t + 1) % 4:
             assert torch.equal(st["kv"][b].cpu(), kv0[b])
+
+
+@pytest.mark.parametrize("hier", [False, True])
+def test_decode_step_graph_replay_matches_eager(hier):
+    """The fused step captured in a HIP graph: every replay (with eager work and
+    synchronisations in between) reproduces the eager result bit for bit."""
+    if hier:
+        spec = datagen.CaseSpec(7103, "decode", B=2, L=20000, m=1, w_cap=128, block_size=8,
+                                max_blocks=256, n_attn=2, ragged=True)
+    else:
+        spec = datagen.CaseSpec(7104, "decode", B=3, L=40000, m=4, w_cap=128, ragged=True)
+    case = datagen.make_case(spec)
+    gaps.enforce_decode(case)
+    step, st, rings, out, idx = run_step(case)
+    ref = pipeline.decode_step(case)
+    check_step(case, ref, st, rings, out, idx)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    junk = torch.randn(1 << 20, device="cuda")
+    for rep in range(4):
+        for o in step.out:
+            o.zero_()
+        step.out_idx.fill_(-7)
+        junk.mul_(1.0001)                      # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out_idx.cpu(), idx), f"replay {rep}: ids differ"
+        for c in range(spec.n_attn):
+            assert torch.equal(step.out[c].cpu(), out[c]), f"replay {rep}: output {c} differs"
