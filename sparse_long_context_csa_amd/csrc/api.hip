@@ -82,17 +82,12 @@ int check_index_common(int64_t n_seq, int64_t n_q, int64_t e_cap, int32_t H, int
 }
 
 // scan of rows into a TopkWs (shared by the calls and the decode step)
-// The scan also clears the merge tickets of the Top-K (K = top_k) that will read its scores.
 hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, const int64_t* q_pos,
                      const int32_t* e_count, const int32_t* cand, int64_t n_cand, int64_t n_seq,
                      int64_t n_q, int64_t e_cap, int H, int d, int m, const TopkWs& ws,
                      int top_k, hipStream_t s) {
+  (void)top_k;
   ScanArgs a;
-  const int64_t rows = n_seq * n_q;
-  a.zero = top_k > 0 ? topk_ticket(ws.scratch, rows, cand ? n_cand : e_cap, top_k,
-                                   cand != nullptr)
-                     : nullptr;
-  a.n_zero = a.zero ? rows : 0;
   a.dt = dt; a.q = q; a.w = w; a.keys = keys; a.q_pos = q_pos; a.e_count = e_count;
   a.cand = cand; a.n_cand = n_cand; a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap;
   a.H = H; a.d = d; a.m = m; a.scores = ws.scores; a.score_stride = ws.stride;
@@ -107,23 +102,20 @@ hipError_t select_rows(const TopkWs& ws, int64_t rows, int64_t max_count, const 
   t.scores = ws.scores; t.stride = ws.stride; t.ids = ids; t.id_stride = id_stride;
   t.id_limit = id_limit; t.count = ws.count; t.rows = rows; t.max_count = max_count; t.K = K;
   t.out_idx = out_idx; t.out_score = out_score; t.out_stride = K; t.scratch = scratch;
-  t.tickets_zeroed = true;
   return launch_topk(t, s);
 }
 
 // stage 1 of the hierarchical indexer after the scan: block maxima, top blocks, pool
 hipError_t pool_rows(int64_t rows, int64_t e_cap, int bs, int mb, int32_t* out_pool,
                      const BlocksWs& ws, hipStream_t s) {
-  const int64_t nbmax = (e_cap + bs - 1) / bs;
-  int32_t* tk = topk_ticket(ws.scratch2, rows, nbmax, mb, false);
   hipError_t e = launch_block_max(ws.tk.scores, ws.tk.stride, ws.tk.count, rows, e_cap, bs,
-                                  ws.bmax, ws.bstride, ws.nb, tk, tk ? rows : 0, s);
+                                  ws.bmax, ws.bstride, ws.nb, s);
   if (e != hipSuccess) return e;
   TopkArgs t;
   t.scores = ws.bmax; t.stride = ws.bstride; t.ids = nullptr; t.id_stride = 0;
   t.id_limit = nullptr; t.count = ws.nb; t.rows = rows; t.max_count = (e_cap + bs - 1) / bs;
   t.K = mb; t.out_idx = ws.blocks; t.out_score = nullptr; t.out_stride = mb;
-  t.scratch = ws.scratch2; t.tickets_zeroed = true;
+  t.scratch = ws.scratch2;
   e = launch_topk(t, s);
   if (e != hipSuccess) return e;
   return launch_pool_build(ws.blocks, rows, mb, bs, ws.tk.n_vis, out_pool, s);

@@ -40,12 +40,6 @@ __device__ __forceinline__ int64_t row_visible(const ScanArgs& a, int64_t r) {
   return visible_entries(a.q_pos[r], a.m, cap);
 }
 
-// the first block of the grid clears the merge tickets of the Top-K that reads these scores
-__device__ __forceinline__ void clear_tickets(const ScanArgs& a) {
-  if (a.zero && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int64_t i = threadIdx.x; i < a.n_zero; i += blockDim.x) a.zero[i] = 0;
-}
-
 // A operand of one query: heads 16*mt + (lane&15), channels ks*32 + g*8 .. +8 (g = lane>>4).
 // The same channel order is used for the keys (B operand), so that in one load instruction
 // the four lanes of a key read 64 contiguous bytes of its row.
@@ -110,7 +104,6 @@ __device__ __forceinline__ void load_key_B(const uint16_t* row, int g, bf16x8_t 
 template <bool kCand, int PF, bool NT>
 __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk, int64_t cpr,
                                                           int64_t n_items) {
-  clear_tickets(a);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
   bf16x8_t A[4][4];
@@ -193,7 +186,6 @@ __global__ __launch_bounds__(512) void scan_prefill_kernel(ScanArgs a, int keys_
   const bool row_ok = qi < a.n_q;
   const int64_t r = sq * a.n_q + (row_ok ? qi : i0);
   const int64_t n_vis = row_ok ? row_visible(a, r) : 0;
-  clear_tickets(a);
   if (row_ok && blockIdx.x == 0 && lane == 0) {
     a.n_vis[r] = int32_t(n_vis);
     a.count[r] = int32_t(n_vis);
@@ -266,7 +258,6 @@ __global__ __launch_bounds__(256) void scan_generic_kernel(ScanArgs a) {
   const int64_t r = blockIdx.y;
   const int64_t n_vis = row_visible(a, r);
   const int64_t n_pos = a.cand ? a.n_cand : n_vis;
-  clear_tickets(a);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.n_vis[r] = int32_t(n_vis);
     a.count[r] = int32_t(n_pos);

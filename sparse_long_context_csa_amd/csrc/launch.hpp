@@ -47,8 +47,6 @@ struct ScanArgs {
   int64_t score_stride;
   int32_t* n_vis;         // [rows]
   int32_t* count;         // [rows]
-  int32_t* zero;          // optional: zero[0..n_zero) cleared before the scan's results are
-  int64_t n_zero;         // used (merge tickets of the Top-K that follows)
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 
@@ -70,19 +68,14 @@ struct TopkArgs {
   float* out_score;       // may be null
   int64_t out_stride;
   void* scratch;          // segment buffers (see topk_scratch_bytes)
-  bool tickets_zeroed;    // topk_ticket(...) was cleared by an earlier kernel on the stream
 };
 size_t topk_scratch_bytes(int64_t rows, int64_t max_count, int K);
-// Merge tickets inside `scratch` (rows int32) that a previous kernel must clear for the
-// single-launch segmented Top-K; null when the Top-K needs none.
-int32_t* topk_ticket(void* scratch, int64_t rows, int64_t max_count, int K, bool has_ids);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 // Block maxima of each row's first count[r] scores; nb[r] = ceil(count/bs).
 hipError_t launch_block_max(const float* scores, int64_t stride, const int32_t* count,
                             int64_t rows, int64_t max_count, int bs, float* bmax,
-                            int64_t bmax_stride, int32_t* nb, int32_t* zero, int64_t n_zero,
-                            hipStream_t s);
+                            int64_t bmax_stride, int32_t* nb, hipStream_t s);
 // Pool of the selected blocks (ascending block ids, -1 padded): entries b*bs.. below n_vis.
 hipError_t launch_pool_build(const int32_t* blocks, int64_t rows, int max_blocks, int bs,
                              const int32_t* n_vis, int32_t* pool, hipStream_t s);
