@@ -17,6 +17,7 @@ from .pipeline import f64, i64
 
 REL_GAP = 1e-3
 MAX_ATTEMPTS = 2000
+MAX_BLOCK_ATTEMPTS = 50000
 
 
 def gap_ok(scores: np.ndarray, K: int) -> bool:
@@ -29,6 +30,20 @@ def gap_ok(scores: np.ndarray, K: int) -> bool:
     part = -np.partition(-s, (K - 1, K))
     a, b = part[K - 1], part[K]
     return (a - b) > REL_GAP * max(abs(a), abs(b), float(np.abs(s).mean()))
+
+
+def _blocks_gap(S: np.ndarray, spec) -> np.ndarray:
+    """gap_ok on the block maxima at rank max_blocks, per column of S [n, k]. The maxima are
+    taken over the whole batch at once here (a search aid); the gate that is kept is checked
+    again with csa.block_maxima itself."""
+    S = csa.round_f32(S)
+    n, k = S.shape
+    bs = spec.block_size
+    nb = (n + bs - 1) // bs
+    P = np.full((nb * bs, k), -np.inf)
+    P[:n] = S
+    bm = P.reshape(nb, bs, k).max(axis=1)
+    return np.array([gap_ok(bm[:, j], spec.max_blocks) for j in range(k)])
 
 
 def _fix_w(spec, R: np.ndarray, K: int, which: str, b: int, current) -> tuple[object, int]:
@@ -65,17 +80,26 @@ def enforce_decode(case: dict, seqs=None) -> dict:
                 keys[e] = csa.store(csa.compress(xi, zi, bias_i, m)[0], spec.dtype)
         R = csa.head_relu(f64(case["q_idx"][b]), keys)
         if spec.block_size > 0:
-            # stage 1: the block maxima must separate at rank max_blocks
-            def blocks_ok(w):
-                s = R @ f64(w)
-                return gap_ok(csa.block_maxima(s, spec.block_size), spec.max_blocks)
+            # stage 1: the block maxima must separate at rank max_blocks. With tens of
+            # thousands of blocks that gap is rare (about one gate in a thousand), so the
+            # redraws are scored in batches; the first passing attempt is kept, as a
+            # one-by-one search would.
             w = case["w"][b]
             attempt = 0
-            while not blocks_ok(w):
-                attempt += 1
-                if attempt > MAX_ATTEMPTS:
-                    raise RuntimeError("no block gap")
-                w = datagen.redraw_w(spec, "w", b, attempt)
+            while not gap_ok(csa.block_maxima(R @ f64(w), spec.block_size), spec.max_blocks):
+                ok = np.zeros(0, bool)
+                base = attempt + 1
+                while base <= MAX_BLOCK_ATTEMPTS:
+                    ws = [datagen.redraw_w(spec, "w", b, a)
+                          for a in range(base, min(base + 64, MAX_BLOCK_ATTEMPTS + 1))]
+                    ok = _blocks_gap(R @ np.stack([f64(x) for x in ws], axis=1), spec)
+                    if ok.any():
+                        break
+                    base += len(ws)
+                if not ok.any():
+                    raise RuntimeError(f"no block gap after {MAX_BLOCK_ATTEMPTS} redraws (row {b})")
+                attempt = base + int(np.argmax(ok))
+                w = ws[int(np.argmax(ok))]
             case["w"][b] = w
             s1 = R @ f64(w)
             pool = csa.candidate_pool(s1, spec.block_size, spec.max_blocks)

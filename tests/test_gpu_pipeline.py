@@ -6,7 +6,7 @@ import torch
 
 import datagen
 import sparse_long_context_csa_amd as csa
-from gpu_helpers import assert_ids, assert_pooled, assert_rows_close, dev
+from gpu_helpers import assert_ids, assert_rows_close, check_step, dev, run_step
 from oracle import csa as ocsa
 from oracle import gaps, pipeline
 from oracle.pipeline import f64
@@ -32,53 +32,6 @@ def test_tiny_forward_fp32():
     for (b, i), ids in ref["ids"].items():
         assert_ids(idx[b, i].numpy(), ids, f"query {i}")
         assert_rows_close(f64(out[b, i]), ref["out"][(b, i)], 2e-2, f"query {i}")
-
-
-def run_step(case):
-    spec = case["spec"]
-    g = {k: dev(v) for k, v in case.items() if isinstance(v, torch.Tensor)}
-    rings = [dev(r).clone() for r in case["rings"]]
-    win_new = [g["x_new"] if (c == 0 and datagen.ring_from_raw(spec)) else None
-               for c in range(spec.n_attn)]
-    kw = {}
-    if spec.block_size:
-        kw = dict(block_size=spec.block_size, max_blocks=spec.max_blocks, q_idx2=g["q_idx2"],
-                  w2=g["w2"])
-    st = {k: g[k].clone() for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
-    step = csa.DecodeStep(m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
-                          pos=g["pos"], x_new=g["x_new"], z_new=g["z_new"], xi_new=g["xi_new"],
-                          zi_new=g["zi_new"], bias=g["bias"], bias_i=g["bias_i"],
-                          q_idx=g["q_idx"], w=g["w"], q=[dev(x) for x in case["q"]], win=rings,
-                          win_new=win_new, sink=[dev(x) for x in case["sink"]], **st, **kw)
-    out, idx = step()
-    torch.cuda.synchronize()
-    return step, st, rings, [o.cpu() for o in out], idx.cpu()
-
-
-def check_step(case, ref, st, rings, out, idx):
-    spec = case["spec"]
-    for b in range(spec.B):
-        t = int(case["pos"][b])
-        assert_ids(idx[b].numpy(), ref["ids"][b], f"seq {b}")
-        for c in range(spec.n_attn):
-            assert_rows_close(f64(out[c][b]), ref["out"][b][c], 2e-2, f"seq {b} call {c}")
-        slot = t % spec.m
-        assert torch.equal(st["x_tail"][b, slot].cpu(), case["x_new"][b])
-        assert torch.equal(st["zi_tail"][b, slot].cpu(), case["zi_new"][b])
-        if b in ref["kv_new"]:
-            e = (t + 1) // spec.m - 1
-            for name, xs, zs, xn, zn, bias in (
-                    ("kv", "x_tail", "z_tail", "x_new", "z_new", "bias"),
-                    ("k_idx", "xi_tail", "zi_tail", "xi_new", "zi_new", "bias_i")):
-                x = f64(case[xs][b]).copy()
-                z = f64(case[zs][b]).copy()
-                x[slot] = f64(case[xn][b])
-                z[slot] = f64(case[zn][b])
-                exact = ocsa.compress(x, z, f64(case[bias]), spec.m)[0]
-                assert_pooled(f64(st[name][b, e].cpu()), exact, np.abs(x).max(axis=0),
-                              f"{name} entry {e} of seq {b}")
-        if datagen.ring_from_raw(spec):
-            assert torch.equal(rings[0][b, t % spec.w_cap].cpu(), case["x_new"][b])
 
 
 def test_decode_step_flat_ragged():
