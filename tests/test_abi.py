@@ -1,0 +1,160 @@
+"""The C ABI on the CPU: libcsa loads, exports exactly the functions include/csa.h declares,
+the binding's descriptor mirrors the header's struct, and host-side validation rejects bad
+calls before anything is launched (none of these calls reaches a kernel)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_long_context_csa_amd as csa
+from sparse_long_context_csa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+def _header() -> str:
+    with open(HEADER) as f:
+        text = f.read()
+    return re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+
+
+def declared_functions() -> set[str]:
+    return set(re.findall(r"^[A-Za-z_][\w \t]*?\**\s*\b(csa_\w+)\s*\(", _header(), flags=re.M))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_long_context_csa_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def test_header_declares_the_calls():
+    assert declared_functions() == {
+        "csa_abi_version", "csa_status_str", "csa_compress", "csa_index_topk_workspace_size",
+        "csa_index_topk", "csa_index_blocks_workspace_size", "csa_index_blocks",
+        "csa_sparse_attn_workspace_size", "csa_sparse_attn", "csa_decode_step_workspace_size",
+        "csa_decode_step"}
+
+
+def test_binding_covers_every_declared_function():
+    assert set(_lib.SIGNATURES) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                        text=True)
+    if nm.returncode == 0:
+        exported = {ln.split()[-1] for ln in nm.stdout.splitlines()
+                    if ln.split() and ln.split()[-1].startswith("csa_")}
+        assert exported == declared_functions()
+
+
+def test_abi_version_and_status_strings(lib):
+    m = re.search(r"#define\s+CSA_ABI_VERSION\s+(\d+)", _header())
+    assert lib.csa_abi_version() == int(m.group(1))
+    for code in _lib.STATUS:
+        s = lib.csa_status_str(code)
+        assert s and isinstance(s, bytes)
+    assert lib.csa_status_str(0) == b"ok"
+    assert lib.csa_status_str(12345) == b"unknown status"
+
+
+def test_decode_desc_mirrors_the_header_struct():
+    body = re.search(r"typedef struct csa_decode_desc \{(.*?)\} csa_decode_desc;", _header(),
+                     flags=re.S).group(1)
+    names = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        for part in decl.split(","):
+            nm = re.search(r"(\w+)\s*(\[[^\]]+\])?\s*$", part.strip())
+            names.append(nm.group(1))
+    assert names == [f[0] for f in _lib.DecodeDesc._fields_]
+    m = re.search(r"#define\s+CSA_MAX_ATTN\s+(\d+)", _header())
+    assert int(m.group(1)) == _lib.MAX_ATTN
+    m = re.search(r"#define\s+CSA_DECODE_EVENTS\s+(\d+)", _header())
+    assert int(m.group(1)) == _lib.DECODE_EVENTS
+    # natural C layout on x86-64: 12 int32 and 2 int64 (64 B), the float padded to 8 B, then
+    # 17 tensor pointers, 5 arrays of CSA_MAX_ATTN pointers, out_idx, the event handles
+    n_ptr = 17 + 5 * _lib.MAX_ATTN + 1 + _lib.DECODE_EVENTS
+    assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr
+
+
+def test_compress_validation(lib):
+    ok = C.c_void_p(16)   # never dereferenced: every call below fails validation or is empty
+    assert lib.csa_compress(ok, ok, ok, ok, 1, 8, 0, 64, 4, 7, None) == -3
+    assert lib.csa_compress(ok, ok, ok, ok, 1, 8, 0, 64, 0, 1, None) == -2
+    assert lib.csa_compress(ok, ok, ok, ok, 1, 8, 0, 64, 17, 1, None) == -2
+    assert lib.csa_compress(ok, ok, ok, ok, 1, 9, 0, 64, 4, 1, None) == -2      # n_tok % m
+    assert lib.csa_compress(ok, ok, ok, ok, 1, 8, 0, 60, 4, 1, None) == -2      # dim % 8
+    assert lib.csa_compress(ok, ok, ok, ok, 1, 8, 64, 64, 4, 1, None) == -2     # stride short
+    assert lib.csa_compress(None, ok, ok, ok, 1, 8, 0, 64, 4, 1, None) == -1
+    assert lib.csa_compress(None, None, None, None, 0, 8, 0, 64, 4, 1, None) == 0  # empty
+
+
+def test_index_and_attention_validation(lib):
+    ok = C.c_void_p(16)
+    args = dict(n_seq=1, n_q=1, e_cap=1024, H=64, d=128, m=4)
+
+    def topk(top_k=512, dtype=1, ws=ok, ws_bytes=1 << 40, q=ok, n_q=1):
+        return lib.csa_index_topk(q, ok, ok, ok, None, None, 0, args["n_seq"], n_q,
+                                  args["e_cap"], args["H"], args["d"], args["m"], top_k, ok,
+                                  None, None, ws, ws_bytes, dtype, None)
+
+    assert topk(dtype=3) == -3
+    assert topk(top_k=0) == -2
+    assert topk(top_k=4096) == -2
+    assert topk(q=None) == -1
+    assert topk(ws=None) == -5
+    assert topk(ws_bytes=16) == -5
+    assert topk(q=None, n_q=0) == 0
+    need = lib.csa_index_topk_workspace_size(1, 1, 1024, 512)
+    assert need > 1024 * 4 and need % 256 == 0
+    assert lib.csa_index_topk_workspace_size(1, 4, 1024, 512) > need
+    assert lib.csa_index_blocks_workspace_size(4, 1, 262144, 8, 2048, 0) > 0
+    # attention: unknown dtype, window above the ring capacity, missing q
+    assert lib.csa_sparse_attn(ok, ok, ok, 512, ok, 128, 128, ok, None, 0.1, ok, 1, 1, 1024,
+                               64, 512, ok, 1 << 40, 9, None) == -3
+    assert lib.csa_sparse_attn(ok, ok, ok, 512, ok, 64, 128, ok, None, 0.1, ok, 1, 1, 1024,
+                               64, 512, ok, 1 << 40, 1, None) == -2      # window > w_cap
+    assert lib.csa_sparse_attn(None, ok, ok, 512, ok, 128, 128, ok, None, 0.1, ok, 1, 1, 1024,
+                               64, 512, ok, 1 << 40, 1, None) == -1
+
+
+def _desc(**kw) -> _lib.DecodeDesc:
+    d = _lib.DecodeDesc()
+    d.dtype, d.m, d.dim, d.n_heads, d.idx_heads, d.idx_dim = 1, 4, 512, 64, 64, 128
+    d.top_k, d.window, d.w_cap, d.n_attn, d.n_seq, d.e_cap, d.scale = 512, 128, 128, 1, 4, 4096, 0.04
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_decode_validation(lib):
+    d = _desc()
+    nb = lib.csa_decode_step_workspace_size(C.byref(d))
+    assert nb > 0 and nb % 256 == 0
+    assert lib.csa_decode_step(C.byref(d), C.c_void_p(16), nb, None) == -1   # null tensors
+    assert lib.csa_decode_step(None, None, 0, None) == -1
+    assert lib.csa_decode_step(C.byref(_desc(n_attn=5)), C.c_void_p(16), nb, None) == -2
+    assert lib.csa_decode_step(C.byref(_desc(dtype=4)), C.c_void_p(16), nb, None) == -3
+    assert lib.csa_decode_step_workspace_size(C.byref(_desc(top_k=0))) == 0
+    assert lib.csa_decode_step(C.byref(_desc(n_seq=0)), None, 0, None) == 0
+    # hierarchical pools above 32,768 entries are outside the limits
+    big = _desc(block_size=64, max_blocks=1024)
+    assert lib.csa_decode_step(C.byref(big), C.c_void_p(16), nb, None) == -4
+
+
+def test_binding_raises_on_errors(lib):
+    with pytest.raises(_lib.CsaError) as e:
+        _lib.check("csa_compress", -2)
+    assert "CSA_ERR_SHAPE" in str(e.value)
+    assert csa.lib() is lib
