@@ -13,6 +13,7 @@ the library around the scan on the launch stream) and the float64 oracle timed o
 sample on the host cores.
 """
 import argparse
+import hashlib
 import ctypes
 import json
 import math
@@ -76,6 +77,34 @@ def cpu_baseline(case, budget_s):
             "sample": f"{done} decode queries (whole sequences of the same workload, each a "
                       f"full step: pool, scan of every visible entry, Top-K, attention) in "
                       f"{el:.1f} s, float64 NumPy"}
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "decode_1m_hbm_traffic.json")
+
+
+def source_digest(files) -> str:
+    """sha256 over the named kernel sources (package-relative), in order."""
+    h = hashlib.sha256()
+    base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_long_context_csa_amd")
+    for f in files:
+        with open(os.path.join(base, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per launch of the stage-1 scan from the committed rocprofv3 counter passes
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a plain copy of known
+    size), or None when the kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if source_digest(t["sources"]) != t["source_sha256"]:
+            return None
+        return int(t["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def bench_prefill(args):
@@ -290,7 +319,8 @@ def main():
                    "launch": "hip_graph" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "kernel": "scan_decode_kernel (indexer scan, stage 1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic() if args.config == 4 else None,
                      "avg_launch_us": round(scan_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": scan_bytes},
         "step_hbm": {"algorithmic_bytes": step_bytes,
