@@ -33,15 +33,18 @@ int status_of(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_HIP; }
 // ---- csa_index_topk workspace ------------------------------------------------------------
 struct TopkWs {
   float* scores;
+  float* gmax;        // maxima of 16 consecutive scores (written by the scan)
   int32_t* n_vis;
   int32_t* count;
   void* scratch;
-  int64_t stride;
+  int64_t stride, gstride;
 };
 TopkWs carve_topk(Carver& c, int64_t rows, int64_t n_keys, int32_t top_k) {
   TopkWs w;
   w.stride = round64(n_keys > 0 ? n_keys : 1);
   w.scores = c.take<float>(size_t(rows) * w.stride * 4);
+  w.gstride = round64((n_keys > 0 ? n_keys : 1) / 16 + 1);
+  w.gmax = c.take<float>(size_t(rows) * w.gstride * 4);
   w.n_vis = c.take<int32_t>(size_t(rows) * 4);
   w.count = c.take<int32_t>(size_t(rows) * 4);
   w.scratch = c.take<char>(topk_scratch_bytes(rows, n_keys, top_k));
@@ -92,6 +95,7 @@ hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, co
   a.cand = cand; a.n_cand = n_cand; a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap;
   a.H = H; a.d = d; a.m = m; a.scores = ws.scores; a.score_stride = ws.stride;
   a.n_vis = ws.n_vis; a.count = ws.count;
+  a.gmax = ws.gmax; a.gmax_stride = ws.gstride;
   return launch_scan(a, s);
 }
 
@@ -100,6 +104,7 @@ hipError_t select_rows(const TopkWs& ws, int64_t rows, int64_t max_count, const 
                        float* out_score, void* scratch, hipStream_t s) {
   TopkArgs t;
   t.scores = ws.scores; t.stride = ws.stride; t.ids = ids; t.id_stride = id_stride;
+  t.gmax = ws.gmax; t.gstride = ws.gstride;
   t.id_limit = id_limit; t.count = ws.count; t.rows = rows; t.max_count = max_count; t.K = K;
   t.out_idx = out_idx; t.out_score = out_score; t.out_stride = K; t.scratch = scratch;
   return launch_topk(t, s);
@@ -113,6 +118,7 @@ hipError_t pool_rows(int64_t rows, int64_t e_cap, int bs, int mb, int32_t* out_p
   if (e != hipSuccess) return e;
   TopkArgs t;
   t.scores = ws.bmax; t.stride = ws.bstride; t.ids = nullptr; t.id_stride = 0;
+  t.gmax = nullptr; t.gstride = 0;
   t.id_limit = nullptr; t.count = ws.nb; t.rows = rows; t.max_count = (e_cap + bs - 1) / bs;
   t.K = mb; t.out_idx = ws.blocks; t.out_score = nullptr; t.out_stride = mb;
   t.scratch = ws.scratch2;

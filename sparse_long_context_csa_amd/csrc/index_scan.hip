@@ -84,6 +84,15 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&A)[4][4], const bf1
   return part;
 }
 
+// maximum over the 16 lanes of this lane's group (lanes 16j .. 16j+15 hold one key tile)
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+
 template <bool NT>
 __device__ __forceinline__ void load_key_B(const uint16_t* row, int g, bf16x8_t (&B)[4]) {
   const bf16x8_t* p = reinterpret_cast<const bf16x8_t*>(row + g * 8);
@@ -129,6 +138,7 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
     const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
     const int32_t* cand = kCand ? a.cand + r * a.n_cand : nullptr;
     float* out = a.scores + r * a.score_stride;
+    float* gmax = a.gmax + r * a.gmax_stride;
     // key row of position p (positions past the chunk read a safe row and are not stored)
     auto key_row = [&](int64_t p, bool& ok) -> int64_t {
       if (p >= c1) { ok = false; return kCand ? 0 : c0; }
@@ -157,7 +167,10 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
         if (more && tl < c1) {
           const float s = tile_score(A, buf[u], wv);
           const int64_t p = tl + col;
-          if (g == 0 && p < c1) out[p] = ok[u] ? s : neg_inf();
+          const float sv = (p < c1 && ok[u]) ? s : neg_inf();
+          if (g == 0 && p < c1) out[p] = sv;
+          const float gm = max16(sv);
+          if (lane == 0) gmax[tl >> 4] = gm;
           const int64_t nx = tl + int64_t(PF + 1) * 64;
           if (nx < c1) load_key_B<NT>(kb + key_row(nx + col, ok[u]) * kID, g, buf[u]);
         } else {
@@ -208,6 +221,7 @@ __global__ __launch_bounds__(512) void scan_prefill_kernel(ScanArgs a, int keys_
   load_gates(a.w + r * kIH, lane, wv);
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
   float* out = a.scores + r * a.score_stride;
+  float* gmax = a.gmax + r * a.gmax_stride;
 
   // cooperative tile load: thread t moves 16-byte chunks t and t+512 of the 64x256 B tile
   const int ch0 = threadIdx.x, ch1 = threadIdx.x + 512;
@@ -241,6 +255,8 @@ __global__ __launch_bounds__(512) void scan_prefill_kernel(ScanArgs a, int keys_
         const float s = tile_score(A, B, wv);
         const int64_t p = base + nt * 16 + col;
         if (g == 0 && p < n_vis) out[p] = s;
+        const float gm = max16(p < n_vis ? s : neg_inf());
+        if (lane == 0) gmax[(base + nt * 16) >> 4] = gm;
       }
     }
     if (more) {
@@ -263,43 +279,47 @@ __global__ __launch_bounds__(256) void scan_generic_kernel(ScanArgs a) {
     a.count[r] = int32_t(n_pos);
   }
   const int64_t p = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (int64_t(blockIdx.x) * blockDim.x >= n_pos) return;
+  if (int64_t(blockIdx.x) * blockDim.x >= n_pos) return;   // uniform per block
   const int H = a.H, d = a.d;
   const T* q = reinterpret_cast<const T*>(a.q) + r * H * d;
   for (int i = threadIdx.x; i < H * d; i += blockDim.x) qs[i] = Elt<T>::load1(q + i);
   for (int i = threadIdx.x; i < H; i += blockDim.x) qs[H * d + i] = a.w[r * H + i];
   __syncthreads();
-  if (p >= n_pos) return;
+  const bool live = p < n_pos;
   int64_t id = p;
-  bool ok = true;
-  if (a.cand) {
+  bool ok = live;
+  if (live && a.cand) {
     id = a.cand[r * a.n_cand + p];
     ok = id >= 0 && id < n_vis;
   }
-  float* out = a.scores + r * a.score_stride;
-  if (!ok) { out[p] = neg_inf(); return; }
-  const int64_t sq = r / a.n_q;
-  const T* key = reinterpret_cast<const T*>(a.keys) + (sq * a.e_cap + id) * d;
-  float dot[64];
+  float s = neg_inf();
+  if (ok) {
+    const int64_t sq = r / a.n_q;
+    const T* key = reinterpret_cast<const T*>(a.keys) + (sq * a.e_cap + id) * d;
+    float dot[64];
 #pragma unroll
-  for (int h = 0; h < 64; ++h) dot[h] = 0.f;
-  for (int c0 = 0; c0 < d; c0 += 8) {
-    float kv8[8];
-    Elt<T>::load8(key + c0, kv8);
+    for (int h = 0; h < 64; ++h) dot[h] = 0.f;
+    for (int c0 = 0; c0 < d; c0 += 8) {
+      float kv8[8];
+      Elt<T>::load8(key + c0, kv8);
 #pragma unroll
-    for (int h = 0; h < 64; ++h) {
-      if (h < H) {
-        const float* qh = qs + h * d + c0;
+      for (int h = 0; h < 64; ++h) {
+        if (h < H) {
+          const float* qh = qs + h * d + c0;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) dot[h] = fmaf(qh[c], kv8[c], dot[h]);
+          for (int c = 0; c < 8; ++c) dot[h] = fmaf(qh[c], kv8[c], dot[h]);
+        }
       }
     }
-  }
-  float s = 0.f;
+    s = 0.f;
 #pragma unroll
-  for (int h = 0; h < 64; ++h)
-    if (h < H) s = fmaf(qs[H * d + h], fmaxf(dot[h], 0.f), s);
-  out[p] = s;
+    for (int h = 0; h < 64; ++h)
+      if (h < H) s = fmaf(qs[H * d + h], fmaxf(dot[h], 0.f), s);
+  }
+  if (live) a.scores[r * a.score_stride + p] = s;
+  // 16 consecutive positions sit in 16 consecutive lanes (block bases are multiples of 256)
+  const float gm = max16(s);
+  if ((threadIdx.x & 15) == 0 && live) a.gmax[r * a.gmax_stride + (p >> 4)] = gm;
 }
 
 static bool fast_shape(const ScanArgs& a) { return a.dt == kBF16 && a.H == kIH && a.d == kID; }

@@ -47,16 +47,21 @@ struct ScanArgs {
   int64_t score_stride;
   int32_t* n_vis;         // [rows]
   int32_t* count;         // [rows]
+  float* gmax;            // [rows, gmax_stride]: max of positions [16j, 16j+16)
+  int64_t gmax_stride;
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 
 // ---- selection ---------------------------------------------------------------------------
 // Top-K of each row's `count[r]` positions; position j has score scores[r*stride + j] and
 // id (ids ? ids[r*id_stride + j] : j); an id is valid iff 0 <= id < id_limit[r] (or id >= 0
-// when id_limit is null). Result ids ascending, -1 padded, in out_idx[r*out_stride + k].
+// when id_limit is null); ids must ascend with position. Result ids ascending, -1 padded,
+// in out_idx[r*out_stride + k]. gmax (optional) holds the maxima of 16 consecutive scores.
 struct TopkArgs {
   const float* scores;
   int64_t stride;
+  const float* gmax;
+  int64_t gstride;
   const int32_t* ids;
   int64_t id_stride;
   const int32_t* id_limit;
@@ -70,6 +75,7 @@ struct TopkArgs {
   void* scratch;          // segment buffers (see topk_scratch_bytes)
 };
 size_t topk_scratch_bytes(int64_t rows, int64_t max_count, int K);
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 // Block maxima of each row's first count[r] scores; nb[r] = ceil(count/bs).

@@ -7,18 +7,30 @@
 // "DeepSeek-V4.1-Flash" study, "Hierarchical indexing bounds the deeper searches": blocks
 // of 8 positions scored by their maximum, at most 2,048 blocks kept as a candidate pool.
 //
-// Selection rule (exact, integer): candidates are ordered by their order-preserving fp32
-// key, then by lower id, i.e. by the 64-bit composite (key << 32 | ~id); every composite is
-// distinct. A 512-thread workgroup holds up to 16,384 candidates in registers (wave w owns
-// a contiguous run of 64*ITEMS positions, item j of lane l is position w*64*ITEMS + j*64 + l:
-// coalesced loads, and position order is (w, j, l)) and runs an MSB-first radix select over
-// LDS histograms of 11-bit digits. The first digit starts at the highest bit of
-// (key - min key) that the segment can set, so the 2048 bins cover the segment's actual
-// score range; selection stops as soon as the bucket holding the K-th candidate is taken
-// whole. Selected candidates are compacted in position order with wave ballots, so ids come
-// out ascending when positions are ascending in id (always the case here). Rows longer than
-// one workgroup's capacity are split into segments whose local Top-K candidates are merged
-// by further launches.
+// Selection rule (exact, integer): positions are ordered by the order-preserving key of their
+// fp32 score, then by lower position (positions ascend with ids), and the chosen ids are
+// written in ascending order, -1 padded.
+//
+// Threshold select.
+//  * The bound: a lower bound T of a row's K-th largest score. The row is cut into G > K
+//    disjoint groups of positions; the K-th largest group maximum is reached by at least K
+//    distinct positions (each of those groups holds its own maximum), so it cannot exceed the
+//    K-th largest score. The groups are built from the 16-position maxima that the scan
+//    writes (long rows) or from the scores themselves, f at a time, so that G falls in
+//    [2K, 8K) when the row is long enough; T then admits only a small fraction of positions
+//    beyond K. T is that group maximum with the key bits below two 11-bit radix digits
+//    cleared (digits taken from the top of the group maxima's key range).
+//  * The candidates: the positions whose key reaches T, kept in position order.
+//  * The select: an exact MSB-first radix select over LDS histograms of the candidates
+//    (digits from the top of their key range); equal keys at the boundary are taken lowest
+//    position first, and the chosen positions are compacted in order. When the candidates
+//    exceed the LDS list, the same select streams over the row's scores instead: exact for
+//    any input, slow only when tens of thousands of scores crowd above T.
+// Rows of up to 32,768 positions take one workgroup each for all three steps
+// (select_row_kernel). Longer rows are cut into slices of 4,096 positions: one workgroup per
+// slice computes the bound and keeps its slice's candidates in a segment of its own
+// (select_slice_kernel), then one workgroup per row concatenates the segments in position
+// order and selects (select_final_kernel).
 #include <limits.h>
 #include <stdlib.h>
 
@@ -29,64 +41,88 @@ namespace csa {
 
 namespace {
 
-constexpr int kTopkThreads = 512;   // 8 waves: up to 256 VGPRs per lane, no spills
-constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kBins = 2048;
-constexpr int kBinsPerThread = kBins / kTopkThreads;
-constexpr int64_t kSegMax = 16384;   // positions per workgroup, implicit ids
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kDigit0 = 14;            // bits of the final select's first digit
+constexpr int kBins0 = 1 << kDigit0;
+constexpr int kDigitB = 12;            // bits of the bound's digit
+constexpr int kBinsB = 1 << kDigitB;   // (its histogram also serves the later digits)
+constexpr int kDigit = 11;             // bits of the later digits
+constexpr int kGroup = 32;             // bins per group count
+constexpr int kSliceItems = 8;                        // positions per thread
+constexpr int kSlice = kSelThreads * kSliceItems;     // positions per workgroup
+constexpr int kSegCap = 512;           // candidates one slice workgroup keeps
+constexpr int kListCap = 8192;         // candidates the final select holds in LDS
+constexpr int kListRun = kListCap / kSelThreads;
+constexpr int kMaxSegLds = 1024;       // segments whose offsets the final select keeps in LDS
+constexpr int kSegPerThread = kMaxSegLds / kSelThreads;
+constexpr int kCoarseCap = 16384;      // group maxima for the bound (< 8K, K <= 2048)
+constexpr int64_t kRowMax = 32768;     // rows up to this length: one workgroup per row
+constexpr int kHead = 32;              // segment entries loaded with the counts
+constexpr int kHeadPerThread = 4;
 
-struct TopkLevel {
+struct SelArgs {
   const float* scores;
-  int64_t s_row;
-  const int32_t* ids;    // null: id = position
-  int64_t i_row;
+  int64_t stride;
+  const float* gmax;      // 16-position maxima of the scores, or null
+  int64_t gstride;
+  const int32_t* ids;     // null: id = position
+  int64_t id_stride;
   const int32_t* id_limit;
-  const int32_t* count;  // null: count_fixed
-  int64_t count_fixed;
-  int64_t seg;           // positions per segment
-  int K;
-  int32_t* o_idx;
-  float* o_score;        // may be null
-  int64_t o_row;         // per-row output stride; segment s writes at + s*K
+  const int32_t* count;
+  int64_t max_count;
+  uint32_t K;
+  int32_t* out_idx;
+  float* out_score;
+  int64_t out_stride;
+  uint2* bound;           // [rows] (T, largest key of the row)
+  int32_t* seg_n;         // [rows][nseg] candidates found (may exceed kSegCap)
+  uint2* seg;             // [rows][nseg][kSegCap] (key, position)
+  int64_t nseg;
 };
 
-// A thread's run of ITEMS consecutive positions sits at LDS words [t*(ITEMS+4), +ITEMS): the
-// 4-word pad makes the 16-byte reads of 16 consecutive lanes hit 64 distinct banks.
-constexpr int kMaxItems = 32;          // implicit ids: 16,384 positions per workgroup
-constexpr int kMaxItemsIds = 16;       // explicit ids: 8,192 (two padded arrays must fit)
-
-constexpr int kListCap = 8192;         // candidate list (position order) of the sampled path
-constexpr int kListPerThread = kListCap / kTopkThreads;
-
-template <bool HAS_IDS>
-struct Shared {
-  static constexpr int kRun = (HAS_IDS ? kMaxItemsIds : kMaxItems) + 4;
-  uint32_t hist[kBins];
-  uint32_t wred[kTopkWaves][3];
-  uint32_t s_digit, s_above, s_last;
-  alignas(16) uint32_t key[kTopkThreads * kRun];            // order keys, padded runs
-  alignas(16) int32_t id[HAS_IDS ? kTopkThreads * kRun : 4]; // explicit ids, padded runs
-  // candidate list (key - kmin, ~id); its first K slots also stage the ordered output
-  alignas(16) uint32_t lkd[kListCap];
-  alignas(16) uint32_t lnid[kListCap];
+struct SelShared {
+  union {
+    uint32_t coarse[kCoarseCap];                                    // the bound
+    struct { uint32_t lk[kListCap]; uint32_t lp[kListCap]; } list;   // the select
+  };
+  uint32_t h0[kBins0];              // first digit of the select
+  uint32_t h0g[kBins0 / kGroup];
+  uint32_t hb[kBinsB];              // digit of the bound; later digits of the select
+  uint32_t hbg[kBinsB / kGroup];
+  uint32_t segoff[kMaxSegLds];
+  uint32_t wred[kSelWaves];
+  uint32_t res[4];                  // search result: bin, items above it, items in it
+  uint32_t red[4];                  // block reductions: min, max, count
+  uint32_t flag;
 };
 
-// exclusive prefix sum over the block of v; *total receives the block sum
-template <typename SH>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SH& sh, uint32_t* total) {
+__device__ __forceinline__ int64_t row_count(const SelArgs& a, int64_t r) {
+  const int64_t n = a.count[r];
+  return n < 0 ? 0 : (n > a.max_count ? a.max_count : n);
+}
+
+__device__ __forceinline__ int64_t row_limit(const SelArgs& a, int64_t r) {
+  return a.id_limit ? int64_t(a.id_limit[r]) : int64_t(INT_MAX);
+}
+
+__device__ __forceinline__ int key_bits(uint32_t range) { return range ? 32 - __clz(range) : 1; }
+
+// exclusive prefix sum over the block; *total receives the block sum
+__device__ __forceinline__ uint32_t excl_scan(uint32_t v, uint32_t* wred, uint32_t* total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
+  for (int o = 1; o < kWave; o <<= 1) {
     const uint32_t u = __shfl_up(x, o);
     if (lane >= o) x += u;
   }
-  if (lane == 63) sh.wred[wave][0] = x;
+  if (lane == kWave - 1) wred[wave] = x;
   __syncthreads();
   uint32_t add = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    const uint32_t t = sh.wred[w][0];
+  for (int w = 0; w < kSelWaves; ++w) {
+    const uint32_t t = wred[w];
     if (w < wave) add += t;
     tot += t;
   }
@@ -95,478 +131,672 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SH& sh, uint32_t
   return x - v + add;
 }
 
-template <typename SH>
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, SH& sh) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  if (lane == 0) sh.wred[wave][0] = v;
-  __syncthreads();
-  uint32_t t = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) t += sh.wred[w][0];
-  __syncthreads();
-  return t;
+__device__ __forceinline__ void clear_words(uint32_t* p, int n) {
+  for (int b = threadIdx.x * 4; b < n; b += kSelThreads * 4)
+    *reinterpret_cast<uint4*>(p + b) = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Digit [lo, lo + w) of the composite (kd << 32 | nid), with 32-bit operations only.
-__device__ __forceinline__ uint32_t digit_at(uint32_t kd, uint32_t nid, int lo, uint32_t msk) {
-  const uint32_t v = lo >= 32 ? (kd >> (lo - 32)) : __builtin_amdgcn_alignbit(kd, nid, lo);
-  return v & msk;
-}
-// (kd << 32 | nid) >> lo as 64 bits
-__device__ __forceinline__ uint64_t prefix_at(uint32_t kd, uint32_t nid, int lo) {
-  const uint64_t u = (uint64_t(kd) << 32) | nid;
-  return lo >= 64 ? 0 : (u >> lo);
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t* g, uint32_t bin) {
+  atomicAdd(&h[bin], 1u);
+  atomicAdd(&g[bin / kGroup], 1u);
 }
 
-// Bin (of the histogram just built) holding the need-th largest: thread t owns bins
-// 2047-4t .. 2044-4t (descending over threads). Sets sh.s_digit / sh.s_above.
-template <typename SH>
-__device__ __forceinline__ void find_bin(SH& sh, uint32_t need) {
-  const int btop = kBins - 1 - kBinsPerThread * int(threadIdx.x);
-  uint32_t hb[kBinsPerThread], loc = 0;
+// Search of a histogram of nbins = 2^w bins (and its 32-bin group counts) for the bin that
+// holds the need-th largest item (1 <= need <= total). Wave 0 alone: each lane sums up to 8
+// group counts from the top, a wave scan finds the group, a second one the bin. Results in
+// sh.res after the barrier that ends the call.
+__device__ __forceinline__ void wave_find(SelShared& sh, const uint32_t* h, const uint32_t* g,
+                                          int nbins, uint32_t need) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int gsz = nbins < kGroup ? nbins : kGroup;
+    const int ng = nbins / gsz;
+    const int gpl = (ng + kWave - 1) / kWave;   // <= 8
+    uint32_t c[8], sum = 0;
 #pragma unroll
-  for (int q = 0; q < kBinsPerThread; ++q) { hb[q] = sh.hist[btop - q]; loc += hb[q]; }
-  uint32_t tot;
-  uint32_t above = block_excl_scan(loc, sh, &tot);
+    for (int i = 0; i < 8; ++i) {
+      const int gi = ng - 1 - lane * gpl - i;
+      c[i] = (i < gpl && gi >= 0) ? g[gi] : 0u;
+      sum += c[i];
+    }
+    uint32_t x = sum;
 #pragma unroll
-  for (int q = 0; q < kBinsPerThread; ++q) {
-    if (above < need && need <= above + hb[q]) { sh.s_digit = btop - q; sh.s_above = above; }
-    above += hb[q];
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t u = __shfl_up(x, o);
+      if (lane >= o) x += u;
+    }
+    uint32_t acc = x - sum, gab = 0;
+    int gsel = -1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (gsel < 0 && acc < need && need <= acc + c[i]) { gsel = ng - 1 - lane * gpl - i; gab = acc; }
+      acc += c[i];
+    }
+    const uint64_t m = __ballot(gsel >= 0);
+    const int src = m ? __ffsll(static_cast<unsigned long long>(m)) - 1 : 0;
+    const int G = __shfl(gsel, src);
+    const uint32_t GA = __shfl(gab, src);
+    const int bin = (G < 0 ? 0 : G) * gsz + gsz - 1 - lane;
+    const uint32_t hv = lane < gsz ? h[bin] : 0u;
+    uint32_t y = hv;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t u = __shfl_up(y, o);
+      if (lane >= o) y += u;
+    }
+    const uint32_t ex = GA + y - hv;
+    if (lane < gsz && ex < need && need <= ex + hv) {
+      sh.res[0] = uint32_t(bin); sh.res[1] = ex; sh.res[2] = hv;
+    }
   }
   __syncthreads();
 }
 
-struct Thresh {
-  int lo;          // selected: composite >> lo  >  P, or == P (all when done)
-  uint64_t P;
-  uint32_t need;   // when !done: how many of the items equal to P are taken (lowest positions)
+// Radix state: items with ((key - kmin) >> lo) > P are taken, those equal to P too when
+// done, else the first `need` of them in position order.
+struct Radix {
+  uint32_t P;
+  int lo;
+  uint32_t need;
   bool done;
 };
 
-// Select the Top-K of positions [base, end) of one row; ordered output with -1 padding.
-// The segment lives in LDS in position order; thread t owns positions t*ITEMS .. +ITEMS,
-// so per-thread masks (32-bit) track validity, candidacy and selection, and the ordered
-// compaction is one block scan of per-thread counts.
-// Requires end - base <= ITEMS * kTopkThreads, ITEMS in {4, 8, 16, 32}, K <= 2048.
-template <int ITEMS, bool HAS_IDS>
-__device__ void select_items(Shared<HAS_IDS>& sh, const float* sc, const int32_t* ids,
-                             int64_t base, int64_t end, int64_t lim, uint32_t K, int32_t* oi,
-                             float* os) {
-  static_assert(ITEMS % 4 == 0 && ITEMS <= (HAS_IDS ? kMaxItemsIds : kMaxItems), "items");
-  constexpr int RUN = ITEMS + 4;                 // padded run stride (words)
-  const int tid = threadIdx.x;
-  const int64_t nseg = end > base ? end - base : 0;
-  // 1. coalesced copy of the segment into LDS: 16-byte loads of 4 positions (same run)
-  for (int q = 0; q < ITEMS / 4; ++q) {
-    const int i0 = 4 * (tid + kTopkThreads * q);
-    if (i0 >= nseg) continue;
-    const int l0 = (i0 / ITEMS) * RUN + (i0 % ITEMS);
-    if (i0 + 3 < nseg) {
-      const float4 v = *reinterpret_cast<const float4*>(sc + base + i0);
-      *reinterpret_cast<uint4*>(&sh.key[l0]) =
-          make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
-                     __float_as_uint(v.w));
-      if (HAS_IDS) {
-        // ids are caller memory: element loads (no read past the row)
-        int4 iv;
-        iv.x = ids[base + i0]; iv.y = ids[base + i0 + 1];
-        iv.z = ids[base + i0 + 2]; iv.w = ids[base + i0 + 3];
-        *reinterpret_cast<int4*>(&sh.id[l0]) = iv;
-      }
-    } else {
-      for (int e = 0; e < 4 && i0 + e < nseg; ++e) {
-        sh.key[l0 + e] = __float_as_uint(sc[base + i0 + e]);
-        if (HAS_IDS) sh.id[l0 + e] = ids[base + i0 + e];
-      }
-    }
+// state after a first-digit search (bin, above, count in sh.res) at shift lo
+__device__ __forceinline__ Radix radix_first(const SelShared& sh, uint32_t K, int lo) {
+  Radix st;
+  st.P = sh.res[0];
+  st.lo = lo;
+  st.need = K - sh.res[1];
+  st.done = sh.res[2] == st.need;
+  return st;
+}
+
+// Further 11-bit digits over the items that `each(fn)` presents (fn(key) per item of this
+// thread) until the bin of the K-th item is taken whole or all bits are resolved.
+template <typename Each>
+__device__ __forceinline__ void radix_more(SelShared& sh, Each each, uint32_t kmin, Radix& st) {
+#pragma unroll 1
+  while (!st.done && st.lo > 0) {
+    const int w = st.lo < kDigit ? st.lo : kDigit;
+    const int lw = st.lo, l = lw - w;
+    const int nbins = 1 << w;
+    clear_words(sh.hb, nbins < 4 ? 4 : nbins);
+    if (threadIdx.x < kBinsB / kGroup) sh.hbg[threadIdx.x] = 0u;
+    __syncthreads();
+    const uint32_t P = st.P;
+    each([&](uint32_t k) {
+      const uint32_t v = k - kmin;
+      if ((v >> lw) == P) hist_add(sh.hb, sh.hbg, (v >> l) & uint32_t(nbins - 1));
+    });
+    __syncthreads();
+    wave_find(sh, sh.hb, sh.hbg, nbins, st.need);
+    st.need -= sh.res[1];
+    st.P = (st.P << w) | sh.res[0];
+    st.lo = l;
+    st.done = sh.res[2] == st.need;
+    __syncthreads();
   }
-  __syncthreads();
-  const int i_own = tid * ITEMS;                 // first position of this thread's run
-  uint32_t* krun = &sh.key[tid * RUN];
-  const int32_t* irun = HAS_IDS ? &sh.id[tid * RUN] : nullptr;
-  // reads of the own run, 4 items per 16-byte LDS access
-  auto read_keys = [&](uint32_t (&k)[ITEMS]) {
-#pragma unroll
-    for (int q = 0; q < ITEMS / 4; ++q) {
-      const uint4 v = *reinterpret_cast<const uint4*>(krun + 4 * q);
-      k[4 * q] = v.x; k[4 * q + 1] = v.y; k[4 * q + 2] = v.z; k[4 * q + 3] = v.w;
-    }
-  };
-  auto read_nids = [&](uint32_t (&nd)[ITEMS]) {
-#pragma unroll
-    for (int q = 0; q < ITEMS / 4; ++q) {
-      if (HAS_IDS) {
-        const int4 v = *reinterpret_cast<const int4*>(irun + 4 * q);
-        nd[4 * q] = ~uint32_t(v.x); nd[4 * q + 1] = ~uint32_t(v.y);
-        nd[4 * q + 2] = ~uint32_t(v.z); nd[4 * q + 3] = ~uint32_t(v.w);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) nd[4 * q + e] = ~uint32_t(base + i_own + 4 * q + e);
-      }
-    }
-  };
-  // 2. decode own run: validity, order keys (written back), key range
-  uint32_t valid = 0;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  {
-    uint32_t k[ITEMS], nd[ITEMS];
-    read_keys(k);
-    read_nids(nd);
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      const int32_t v = int32_t(~nd[i]);
-      const bool ok = i_own + i < nseg && v >= 0 && v < lim;
-      k[i] = ok ? order_key(__uint_as_float(k[i])) : 0u;
-      if (ok) {
-        valid |= 1u << i;
-        kmin = k[i] < kmin ? k[i] : kmin;
-        kmax = k[i] > kmax ? k[i] : kmax;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < ITEMS / 4; ++q)
-      *reinterpret_cast<uint4*>(krun + 4 * q) =
-          make_uint4(k[4 * q], k[4 * q + 1], k[4 * q + 2], k[4 * q + 3]);
+}
+
+__device__ __forceinline__ void write_out(const SelArgs& a, int64_t r, uint32_t o, uint32_t pos,
+                                          uint32_t key) {
+  a.out_idx[r * a.out_stride + o] = a.ids ? a.ids[r * a.id_stride + pos] : int32_t(pos);
+  if (a.out_score) a.out_score[r * a.out_stride + o] = key_to_score(key);
+}
+
+__device__ __forceinline__ void pad_out(const SelArgs& a, int64_t r, uint32_t from) {
+  for (uint32_t k = from + threadIdx.x; k < a.K; k += kSelThreads) {
+    a.out_idx[r * a.out_stride + k] = -1;
+    if (a.out_score) a.out_score[r * a.out_stride + k] = neg_inf();
   }
-  const int lane = lane_id(), wave = tid >> 6;
-  uint32_t nv = __popc(valid);
+}
+
+// block min / max / count through sh.red (initialised, and made visible, beforehand)
+__device__ __forceinline__ void red_add(SelShared& sh, uint32_t kmin, uint32_t kmax, uint32_t c) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    nv += __shfl_xor(nv, o);
-    const uint32_t x = __shfl_xor(kmin, o), y = __shfl_xor(kmax, o);
-    kmin = x < kmin ? x : kmin;
-    kmax = y > kmax ? y : kmax;
+    const uint32_t x = __shfl_xor(kmax, o), y = __shfl_xor(kmin, o);
+    kmax = x > kmax ? x : kmax;
+    kmin = y < kmin ? y : kmin;
+    c += __shfl_xor(c, o);
   }
-  if (lane == 0) { sh.wred[wave][0] = nv; sh.wred[wave][1] = kmin; sh.wred[wave][2] = kmax; }
-  __syncthreads();
-  uint32_t n = 0;
-  kmin = 0xffffffffu;
-  kmax = 0u;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    n += sh.wred[w][0];
-    kmin = sh.wred[w][1] < kmin ? sh.wred[w][1] : kmin;
-    kmax = sh.wred[w][2] > kmax ? sh.wred[w][2] : kmax;
+  if (lane_id() == 0) {
+    atomicMin(&sh.red[0], kmin);
+    atomicMax(&sh.red[1], kmax);
+    atomicAdd(&sh.red[2], c);
   }
-  __syncthreads();
+}
+__device__ __forceinline__ void red_init(SelShared& sh) {
+  if (threadIdx.x == 0) { sh.red[0] = 0xffffffffu; sh.red[1] = 0u; sh.red[2] = 0u; }
+}
 
-  uint32_t sel = valid;
-  if (n > K) {
-    const uint32_t range = kmax - kmin;
-    const int bl = range ? 32 - __clz(range) : 0;
-    int hi = bl ? 31 + bl : 31;   // highest bit any composite (key - kmin) << 32 | ~id can set
-    uint32_t cm = valid;
-    // sampled bound: histogram the first ITEMS/8 items of every run on the first digit, take
-    // the bin whose upper tail should hold ~2K items; when that verifiably leaves between K
-    // and kListCap candidates (the K-th largest is then among them), gather them (position
-    // order) into the LDS list and finish on the list alone
-    uint32_t list_n = 0;
-    if (ITEMS >= 8) {
-      constexpr int JS = ITEMS / 8;
-      const int w0 = hi + 1 < 11 ? hi + 1 : 11;
-      const int lo0 = hi + 1 - w0;
-      const uint32_t msk0 = (1u << w0) - 1u;
-      for (int b = tid; b < kBins; b += kTopkThreads) sh.hist[b] = 0;
-      __syncthreads();
-      uint32_t k[ITEMS], nd[ITEMS];
-      read_keys(k);
-      read_nids(nd);
-      uint32_t ns = 0;
+// ---- the bound ---------------------------------------------------------------------------
+// T and the row's largest key (all-ones when unknown). Needs sh.hb/hbg clear and sh.red
+// initialised (and a barrier since); ends with a barrier.
+__device__ uint2 row_bound(const SelArgs& a, SelShared& sh, int64_t r, int64_t n) {
+  const int tid = threadIdx.x;
+  const int64_t K = a.K;
+  if (n <= K) return make_uint2(0u, 0xffffffffu);
+  const int64_t n16 = (n + 15) / 16;
+  const bool use_g = a.gmax != nullptr && n16 >= 2 * K;
+  const float* src = use_g ? a.gmax + r * a.gstride : a.scores + r * a.stride;
+  const int64_t nb = use_g ? n16 : n;
+  int64_t f = nb / (4 * K);
+  if (f < 1) f = 1;
+  const int64_t G = (nb + f - 1) / f;   // K < G < 8K
+  const uint32_t kninf = order_key(neg_inf());
+  uint32_t kmax = 0u, kmin = 0xffffffffu, cf = 0;
+  auto note = [&](int64_t j, uint32_t k) {
+    sh.coarse[j] = k;
+    if (k > kninf) {
+      kmax = k > kmax ? k : kmax;
+      kmin = k < kmin ? k : kmin;
+      ++cf;
+    }
+  };
+  if (f == 8) {
+    // the long-row case: two 16-byte loads per group, 4 groups per thread in flight
+    constexpr int kPer = 4;
+    for (int64_t j0 = 0; j0 < G; j0 += int64_t(kPer) * kSelThreads) {
+      float4 v[kPer][2];
 #pragma unroll
-      for (int i = 0; i < JS; ++i)
-        if ((valid >> i) & 1u) {
-          atomicAdd(&sh.hist[digit_at(k[i] - kmin, nd[i], lo0, msk0)], 1u);
-          ++ns;
+      for (int q = 0; q < kPer; ++q) {
+        const int64_t j = j0 + tid + int64_t(q) * kSelThreads;
+        const int64_t p0 = j * 8;
+        const float ni = neg_inf();
+        v[q][0] = make_float4(ni, ni, ni, ni);
+        v[q][1] = v[q][0];
+        if (j < G && p0 + 8 <= nb) {
+          v[q][0] = *reinterpret_cast<const float4*>(src + p0);
+          v[q][1] = *reinterpret_cast<const float4*>(src + p0 + 4);
+        } else if (j < G) {
+          float* e8 = reinterpret_cast<float*>(&v[q][0]);
+          float* e8b = reinterpret_cast<float*>(&v[q][1]);
+          for (int e = 0; e < 8 && p0 + e < nb; ++e) (e < 4 ? e8[e] : e8b[e - 4]) = src[p0 + e];
         }
-      ns = block_sum(ns, sh);
-      uint32_t t = uint32_t((2ull * K * ns + n - 1) / n) + 16u;
-      if (t > ns) t = ns;
-      if (t > 0) {
-        find_bin(sh, t);
-        const uint32_t Ds = sh.s_digit;
-        uint32_t c2 = 0;
+      }
 #pragma unroll
-        for (int i = 0; i < ITEMS; ++i)
-          if (((valid >> i) & 1u) && digit_at(k[i] - kmin, nd[i], lo0, msk0) >= Ds) c2 |= 1u << i;
-        uint32_t tot;
-        uint32_t off = block_excl_scan(__popc(c2), sh, &tot);
-        if (tot >= K && tot <= uint32_t(kListCap)) {
-#pragma unroll
-          for (int i = 0; i < ITEMS; ++i)
-            if ((c2 >> i) & 1u) { sh.lkd[off] = k[i] - kmin; sh.lnid[off] = nd[i]; ++off; }
-          list_n = tot;
-          __syncthreads();
-        } else if (tot >= K) {
-          cm = c2;
+      for (int q = 0; q < kPer; ++q) {
+        const int64_t j = j0 + tid + int64_t(q) * kSelThreads;
+        if (j < G) {
+          const float m = fmaxf(fmaxf(fmaxf(v[q][0].x, v[q][0].y), fmaxf(v[q][0].z, v[q][0].w)),
+                                fmaxf(fmaxf(v[q][1].x, v[q][1].y), fmaxf(v[q][1].z, v[q][1].w)));
+          note(j, order_key(m));
         }
       }
     }
-    if (list_n) {
-      // ---- list path: thread t owns list items [t*L, (t+1)*L), L <= kListPerThread
-      const int L = int((list_n + kTopkThreads - 1) / kTopkThreads);
-      const int j0 = tid * L;
-      int jn = int(list_n) - j0;
-      jn = jn < 0 ? 0 : (jn > L ? L : jn);
-      uint32_t lm = jn >= 32 ? 0xffffffffu : ((1u << jn) - 1u);
-      Thresh T{hi + 1, 0, K, false};
-      while (!T.done && hi >= 0) {
-        const int w = hi + 1 < 11 ? hi + 1 : 11;
-        const int lo = hi + 1 - w;
-        const uint32_t msk = (1u << w) - 1u;
-        for (int b = tid; b < kBins; b += kTopkThreads) sh.hist[b] = 0;
-        __syncthreads();
-        for (int q = 0; q < jn; ++q)
-          if ((lm >> q) & 1u) atomicAdd(&sh.hist[digit_at(sh.lkd[j0 + q], sh.lnid[j0 + q], lo, msk)], 1u);
-        __syncthreads();
-        find_bin(sh, T.need);
-        const uint32_t D = sh.s_digit;
-        T.need -= sh.s_above;
-        if (sh.hist[D] == T.need) T.done = true;
-        T.P = (T.P << w) | D;
-        T.lo = lo;
-        for (int q = 0; q < jn; ++q)
-          if (((lm >> q) & 1u) && digit_at(sh.lkd[j0 + q], sh.lnid[j0 + q], lo, msk) != D)
-            lm &= ~(1u << q);
-        hi = lo - 1;
-        __syncthreads();
+  } else {
+    for (int64_t j = tid; j < G; j += kSelThreads) {
+      const int64_t p0 = j * f;
+      const int64_t p1 = p0 + f < nb ? p0 + f : nb;
+      uint32_t m = 0u;
+      for (int64_t p = p0; p < p1; ++p) {
+        const uint32_t k = order_key(src[p]);
+        m = k > m ? k : m;
       }
-      // select list items at or above the threshold, then compact them (list order is
-      // position order); items are read into registers before any staging write
-      uint32_t ls = 0, leq = 0;
-      uint32_t rk[kListPerThread], rn[kListPerThread];
+      note(j, m);
+    }
+  }
+  red_add(sh, kmin, kmax, cf);
+  __syncthreads();
+  kmin = sh.red[0];
+  kmax = sh.red[1];
+  cf = sh.red[2];
+  // fewer than K finite groups: every valid position is a candidate
+  if (cf < uint32_t(K)) return make_uint2(0u, kmax);
+  // one 12-bit digit of (key - kmin): T within 2^(bits - 12) below the K-th group maximum
+  const int bits = key_bits(kmax - kmin);
+  const int w = bits < kDigitB ? bits : kDigitB;
+  const int lo = bits - w;
+  for (int64_t j = tid; j < G; j += kSelThreads) {
+    const uint32_t k = sh.coarse[j];
+    if (k > kninf) hist_add(sh.hb, sh.hbg, (k - kmin) >> lo);
+  }
+  __syncthreads();
+  wave_find(sh, sh.hb, sh.hbg, 1 << w, uint32_t(K));
+  return make_uint2(kmin + (sh.res[0] << lo), kmax);
+}
+
+// ---- the select --------------------------------------------------------------------------
+// Candidates in LDS (position order), more than K of them, first digit (14 bits at lo0 over
+// key - kmin) already histogrammed in sh.h0: thread t owns list items [t*L, t*L + L).
+__device__ void select_list(const SelArgs& a, SelShared& sh, int64_t r, uint32_t total,
+                            uint32_t kmin, int lo0, int nb0) {
+  const int tid = threadIdx.x;
+  const uint32_t K = a.K;
+  const uint32_t L = (total + kSelThreads - 1) / kSelThreads;   // <= kListRun
+  const uint32_t j0 = uint32_t(tid) * L;
+  const uint32_t jn = j0 < total ? (total - j0 < L ? total - j0 : L) : 0u;
+  uint32_t k[kListRun];
 #pragma unroll
-      for (int q = 0; q < kListPerThread; ++q) {
-        rk[q] = 0; rn[q] = 0;
-        if (q < jn) {
-          rk[q] = sh.lkd[j0 + q];
-          rn[q] = sh.lnid[j0 + q];
-          const uint64_t v = prefix_at(rk[q], rn[q], T.lo);
-          if (v > T.P) ls |= 1u << q;
-          else if (v == T.P) leq |= 1u << q;
+  for (int i = 0; i < kListRun; ++i) k[i] = uint32_t(i) < jn ? sh.list.lk[j0 + i] : 0u;
+  wave_find(sh, sh.h0, sh.h0g, nb0, K);
+  Radix st = radix_first(sh, K, lo0);
+  __syncthreads();
+  radix_more(sh, [&](auto fn) {
+#pragma unroll
+    for (int i = 0; i < kListRun; ++i)
+      if (uint32_t(i) < jn) fn(k[i]);
+  }, kmin, st);
+  uint32_t sel = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < kListRun; ++i) {
+    if (uint32_t(i) < jn) {
+      const uint32_t v = (k[i] - kmin) >> st.lo;
+      if (v > st.P) sel |= 1u << i;
+      else if (v == st.P) eq |= 1u << i;
+    }
+  }
+  if (st.done) {
+    sel |= eq;
+  } else {
+    uint32_t tot;
+    uint32_t before = excl_scan(__popc(eq), sh.wred, &tot);
+#pragma unroll
+    for (int i = 0; i < kListRun; ++i)
+      if ((eq >> i) & 1u) {
+        if (before < st.need) sel |= 1u << i;
+        ++before;
+      }
+  }
+  uint32_t nsel;
+  uint32_t o = excl_scan(__popc(sel), sh.wred, &nsel);
+#pragma unroll
+  for (int i = 0; i < kListRun; ++i)
+    if ((sel >> i) & 1u) {
+      write_out(a, r, o, sh.list.lp[j0 + i], k[i]);
+      ++o;
+    }
+  pad_out(a, r, nsel);
+}
+
+// the first `total` (<= K) list items, in order
+__device__ void select_all(const SelArgs& a, SelShared& sh, int64_t r, uint32_t total) {
+  for (uint32_t j = threadIdx.x; j < total; j += kSelThreads)
+    write_out(a, r, j, sh.list.lp[j], sh.list.lk[j]);
+  pad_out(a, r, total);
+}
+
+// Streaming select over the row's scores (valid positions whose key reaches T): for rows
+// whose candidates do not fit the LDS list. Uses every histogram; needs nothing set up.
+__device__ void select_stream(const SelArgs& a, SelShared& sh, int64_t r, int64_t n,
+                              uint32_t T) {
+  const int tid = threadIdx.x;
+  const int64_t lim = row_limit(a, r);
+  const float* sr = a.scores + r * a.stride;
+  auto item = [&](int64_t p, uint32_t& k) -> bool {
+    if (p >= n) return false;
+    k = order_key(sr[p]);
+    if (k < T) return false;
+    const int64_t id = a.ids ? int64_t(a.ids[r * a.id_stride + p]) : p;
+    return id >= 0 && id < lim;
+  };
+  __syncthreads();
+  red_init(sh);
+  clear_words(sh.h0, kBins0);
+  clear_words(sh.h0g, kBins0 / kGroup);
+  __syncthreads();
+  uint32_t cnt = 0, kmin = 0xffffffffu, kmax = 0u;
+  for (int64_t p = tid; p < n; p += kSelThreads) {
+    uint32_t k;
+    if (item(p, k)) {
+      ++cnt;
+      kmin = k < kmin ? k : kmin;
+      kmax = k > kmax ? k : kmax;
+    }
+  }
+  red_add(sh, kmin, kmax, cnt);
+  __syncthreads();
+  kmin = sh.red[0];
+  kmax = sh.red[1];
+  const uint32_t total = sh.red[2];
+  Radix st{0u, 32, 0u, true};   // lo = 32: every candidate taken
+  if (total > a.K) {
+    const int bits = key_bits(kmax - kmin);
+    const int w = bits < kDigit0 ? bits : kDigit0;
+    const int lo0 = bits - w;
+    for (int64_t p = tid; p < n; p += kSelThreads) {
+      uint32_t k;
+      if (item(p, k)) hist_add(sh.h0, sh.h0g, (k - kmin) >> lo0);
+    }
+    __syncthreads();
+    wave_find(sh, sh.h0, sh.h0g, 1 << w, a.K);
+    st = radix_first(sh, a.K, lo0);
+    __syncthreads();
+    radix_more(sh, [&](auto fn) {
+      for (int64_t p = tid; p < n; p += kSelThreads) {
+        uint32_t k;
+        if (item(p, k)) fn(k);
+      }
+    }, kmin, st);
+  }
+  // ordered compaction, tile by tile
+  uint32_t out_base = 0, eq_base = 0;
+  for (int64_t t0 = 0; t0 < n; t0 += kSlice) {
+    const int64_t q0 = t0 + int64_t(tid) * kSliceItems;
+    uint32_t k[kSliceItems];
+    uint32_t sel = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < kSliceItems; ++i) {
+      k[i] = 0u;
+      if (item(q0 + i, k[i])) {
+        if (st.lo >= 32) {
+          sel |= 1u << i;
+        } else {
+          const uint32_t v = (k[i] - kmin) >> st.lo;
+          if (v > st.P) sel |= 1u << i;
+          else if (v == st.P) eq |= 1u << i;
         }
       }
-      if (T.done) {
-        ls |= leq;
-      } else {
-        uint32_t tot;
-        uint32_t before = block_excl_scan(__popc(leq), sh, &tot);
-#pragma unroll
-        for (int q = 0; q < kListPerThread; ++q)
-          if ((leq >> q) & 1u) {
-            if (before < T.need) ls |= 1u << q;
-            ++before;
-          }
-      }
-      uint32_t total;
-      uint32_t o = block_excl_scan(__popc(ls), sh, &total);   // (barriers inside)
-#pragma unroll
-      for (int q = 0; q < kListPerThread; ++q)
-        if ((ls >> q) & 1u) {
-          sh.lnid[o] = rn[q];
-          sh.lkd[o] = rk[q] + kmin;
-          ++o;
-        }
-      __syncthreads();
-      for (uint32_t kk = tid; kk < K; kk += kTopkThreads) {
-        const bool has = kk < total;
-        oi[kk] = has ? int32_t(~sh.lnid[kk]) : -1;
-        if (os) os[kk] = has ? key_to_score(sh.lkd[kk]) : neg_inf();
-      }
-      __syncthreads();
-      return;
     }
-    // exact MSB-first radix over the candidates (every run)
-    Thresh T{hi + 1, 0, K, false};
-    while (!T.done && hi >= 0) {
-      const int w = hi + 1 < 11 ? hi + 1 : 11;
-      const int lo = hi + 1 - w;
-      const uint32_t msk = (1u << w) - 1u;
-      for (int b = tid; b < kBins; b += kTopkThreads) sh.hist[b] = 0;
-      __syncthreads();
-      uint32_t k[ITEMS], nd[ITEMS];
-      read_keys(k);
-      read_nids(nd);
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i)
-        if ((cm >> i) & 1u) atomicAdd(&sh.hist[digit_at(k[i] - kmin, nd[i], lo, msk)], 1u);
-      __syncthreads();
-      find_bin(sh, T.need);
-      const uint32_t D = sh.s_digit;
-      T.need -= sh.s_above;
-      if (sh.hist[D] == T.need) T.done = true;
-      T.P = (T.P << w) | D;
-      T.lo = lo;
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i)
-        if (((cm >> i) & 1u) && digit_at(k[i] - kmin, nd[i], lo, msk) != D) cm &= ~(1u << i);
-      hi = lo - 1;
-      __syncthreads();
-    }
-    // final selection against the exact threshold
-    sel = 0;
-    uint32_t eq = 0;
-    {
-      uint32_t k[ITEMS], nd[ITEMS];
-      read_keys(k);
-      read_nids(nd);
-#pragma unroll
-      for (int i = 0; i < ITEMS; ++i) {
-        if ((valid >> i) & 1u) {
-          const uint64_t v = prefix_at(k[i] - kmin, nd[i], T.lo);
-          if (v > T.P) sel |= 1u << i;
-          else if (v == T.P) eq |= 1u << i;
-        }
-      }
-    }
-    if (T.done) {
+    if (st.done) {
       sel |= eq;
     } else {
-      // duplicate ids left equal composites: keep the first T.need of them in position order
       uint32_t tot;
-      uint32_t before = block_excl_scan(__popc(eq), sh, &tot);
+      uint32_t before = eq_base + excl_scan(__popc(eq), sh.wred, &tot);
 #pragma unroll
-      for (int i = 0; i < ITEMS; ++i)
+      for (int i = 0; i < kSliceItems; ++i)
         if ((eq >> i) & 1u) {
-          if (before < T.need) sel |= 1u << i;
+          if (before < st.need) sel |= 1u << i;
           ++before;
         }
+      eq_base += tot;
     }
-  }
-
-  // ordered compaction (positions ascend with thread and item), staged in the list arrays
-  uint32_t total;
-  uint32_t o = block_excl_scan(__popc(sel), sh, &total);
-  if (sel) {
-    uint32_t k[ITEMS], nd[ITEMS];
-    read_keys(k);
-    read_nids(nd);
+    uint32_t tsel;
+    uint32_t o = out_base + excl_scan(__popc(sel), sh.wred, &tsel);
 #pragma unroll
-    for (int i = 0; i < ITEMS; ++i)
+    for (int i = 0; i < kSliceItems; ++i)
       if ((sel >> i) & 1u) {
-        sh.lnid[o] = nd[i];
-        sh.lkd[o] = k[i];
+        write_out(a, r, o, uint32_t(q0 + i), k[i]);
         ++o;
       }
+    out_base += tsel;
+  }
+  pad_out(a, r, out_base);
+}
+
+// first-digit layout of the select over candidates with keys in [kmin, kmax]
+struct Digit0 {
+  int lo, nbins;
+};
+__device__ __forceinline__ Digit0 digit0(uint32_t kmin, uint32_t kmax) {
+  const int bits = key_bits(kmax > kmin ? kmax - kmin : 0u);
+  const int w = bits < kDigit0 ? bits : kDigit0;
+  return Digit0{bits - w, 1 << w};
+}
+__device__ __forceinline__ uint32_t bin0(uint32_t k, uint32_t kmin, const Digit0& d0) {
+  const uint32_t b = (k > kmin ? k - kmin : 0u) >> d0.lo;
+  return b < uint32_t(d0.nbins) ? b : uint32_t(d0.nbins - 1);
+}
+
+// load kSliceItems scores of positions q0.. (0 beyond n)
+__device__ __forceinline__ void load_slice(const float* sr, int64_t q0, int64_t n,
+                                           float (&x)[kSliceItems]) {
+  if (q0 + kSliceItems <= n) {
+#pragma unroll
+    for (int v = 0; v < kSliceItems / 4; ++v) {
+      const float4 y = *reinterpret_cast<const float4*>(sr + q0 + 4 * v);
+      x[4 * v] = y.x; x[4 * v + 1] = y.y; x[4 * v + 2] = y.z; x[4 * v + 3] = y.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSliceItems; ++i) x[i] = q0 + i < n ? sr[q0 + i] : 0.f;
+  }
+}
+
+// candidate flags of positions q0.. : valid and key >= T
+__device__ __forceinline__ uint32_t slice_flags(const SelArgs& a, int64_t r, int64_t q0,
+                                                int64_t n, int64_t lim, uint32_t T,
+                                                const float (&x)[kSliceItems],
+                                                uint32_t (&key)[kSliceItems]) {
+  uint32_t flags = 0;
+#pragma unroll
+  for (int i = 0; i < kSliceItems; ++i) {
+    const int64_t p = q0 + i;
+    key[i] = order_key(x[i]);
+    bool ok = p < n && key[i] >= T;
+    if (ok) {
+      const int64_t id = a.ids ? int64_t(a.ids[r * a.id_stride + p]) : p;
+      ok = id >= 0 && id < lim;
+    }
+    if (ok) flags |= 1u << i;
+  }
+  return flags;
+}
+
+// One workgroup per row (rows of up to kRowMax positions): bound, candidates into the LDS
+// list tile by tile (first digit histogrammed on the way; the next tile's scores load while
+// this one is compacted), select.
+__global__ __launch_bounds__(kSelThreads) void select_row_kernel(SelArgs a) {
+  __shared__ SelShared sh;
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t n = row_count(a, r);
+  const float* sr = a.scores + r * a.stride;
+  float x[kSliceItems];
+  load_slice(sr, int64_t(tid) * kSliceItems, n, x);
+  clear_words(sh.h0, kBins0);
+  clear_words(sh.h0g, kBins0 / kGroup);
+  clear_words(sh.hb, kBinsB);
+  clear_words(sh.hbg, kBinsB / kGroup);
+  red_init(sh);
+  __syncthreads();
+  const uint2 B = row_bound(a, sh, r, n);
+  const uint32_t T = B.x;
+  const Digit0 d0 = digit0(T, B.y);
+  const int64_t lim = row_limit(a, r);
+  uint32_t total = 0;
+  bool over = false;
+  for (int64_t t0 = 0; t0 < n; t0 += kSlice) {
+    const int64_t q0 = t0 + int64_t(tid) * kSliceItems;
+    uint32_t key[kSliceItems];
+    const uint32_t flags = slice_flags(a, r, q0, n, lim, T, x, key);
+    if (t0 + kSlice < n) load_slice(sr, q0 + kSlice, n, x);
+    uint32_t tot;
+    uint32_t off = total + excl_scan(__popc(flags), sh.wred, &tot);
+    if (total + tot <= uint32_t(kListCap)) {
+#pragma unroll
+      for (int i = 0; i < kSliceItems; ++i)
+        if ((flags >> i) & 1u) {
+          sh.list.lk[off] = key[i];
+          sh.list.lp[off] = uint32_t(q0 + i);
+          hist_add(sh.h0, sh.h0g, bin0(key[i], T, d0));
+          ++off;
+        }
+    } else {
+      over = true;
+    }
+    total += tot;
   }
   __syncthreads();
-  for (uint32_t k = tid; k < K; k += kTopkThreads) {
-    const bool has = k < total;
-    oi[k] = has ? int32_t(~sh.lnid[k]) : -1;
-    if (os) os[k] = has ? key_to_score(sh.lkd[k]) : neg_inf();
+  if (over) select_stream(a, sh, r, n, T);
+  else if (total <= a.K) select_all(a, sh, r, total);
+  else select_list(a, sh, r, total, T, d0.lo, d0.nbins);
+}
+
+// Long rows, step 1: one workgroup per slice computes the row's bound and keeps its slice's
+// candidates (position order) in its segment; workgroup 0 of the row records the bound.
+__global__ __launch_bounds__(kSelThreads) void select_slice_kernel(SelArgs a) {
+  __shared__ SelShared sh;
+  const int64_t r = blockIdx.y, b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t n = row_count(a, r);
+  const int64_t p0 = b * kSlice;
+  if (p0 >= n) {
+    if (tid == 0) {
+      a.seg_n[r * a.nseg + b] = 0;
+      if (b == 0) a.bound[r] = make_uint2(0u, 0xffffffffu);
+    }
+    return;
   }
+  const int64_t q0 = p0 + int64_t(tid) * kSliceItems;
+  const float* sr = a.scores + r * a.stride;
+  float x[kSliceItems];
+  load_slice(sr, q0, n, x);
+  clear_words(sh.hb, kBinsB);
+  clear_words(sh.hbg, kBinsB / kGroup);
+  red_init(sh);
   __syncthreads();
-}
-
-template <int ITEMS, bool HAS_IDS>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkLevel L) {
-  __shared__ Shared<HAS_IDS> sh;
-  const int64_t r = blockIdx.y;
-  const int64_t cnt = L.count ? int64_t(L.count[r]) : L.count_fixed;
-  const int64_t base = int64_t(blockIdx.x) * L.seg;
-  const int64_t end = base + L.seg < cnt ? base + L.seg : cnt;
-  const int64_t lim = L.id_limit ? int64_t(L.id_limit[r]) : int64_t(INT_MAX);
-  int32_t* oi = L.o_idx + r * L.o_row + int64_t(blockIdx.x) * L.K;
-  float* os = L.o_score ? L.o_score + r * L.o_row + int64_t(blockIdx.x) * L.K : nullptr;
-  select_items<ITEMS, HAS_IDS>(sh, L.scores + r * L.s_row,
-                               HAS_IDS ? L.ids + r * L.i_row : nullptr, base, end, lim,
-                               uint32_t(L.K), oi, os);
-}
-
-template <int ITEMS, bool HAS_IDS>
-hipError_t launch_level(const TopkLevel& L, int64_t rows, int64_t nseg, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(nseg), static_cast<unsigned>(rows));
-  hipLaunchKernelGGL((topk_kernel<ITEMS, HAS_IDS>), grid, dim3(kTopkThreads), 0, s, L);
-  return hipGetLastError();
-}
-
-hipError_t run_level(const TopkLevel& L, int64_t rows, int64_t nseg, hipStream_t s) {
-  const int64_t seg = L.seg;
-  if (L.ids) {
-    if (seg <= 4 * kTopkThreads) return launch_level<4, true>(L, rows, nseg, s);
-    if (seg <= 8 * kTopkThreads) return launch_level<8, true>(L, rows, nseg, s);
-    return launch_level<16, true>(L, rows, nseg, s);
+  const uint2 B = row_bound(a, sh, r, n);
+  uint32_t key[kSliceItems];
+  const uint32_t flags = slice_flags(a, r, q0, n, row_limit(a, r), B.x, x, key);
+  uint32_t tot;
+  uint32_t off = excl_scan(__popc(flags), sh.wred, &tot);
+  uint2* seg = a.seg + (r * a.nseg + b) * kSegCap;
+#pragma unroll
+  for (int i = 0; i < kSliceItems; ++i)
+    if ((flags >> i) & 1u) {
+      if (off < uint32_t(kSegCap)) seg[off] = make_uint2(key[i], uint32_t(q0 + i));
+      ++off;
+    }
+  if (tid == 0) {
+    a.seg_n[r * a.nseg + b] = int32_t(tot);
+    if (b == 0) a.bound[r] = B;
   }
-  if (seg <= 4 * kTopkThreads) return launch_level<4, false>(L, rows, nseg, s);
-  if (seg <= 8 * kTopkThreads) return launch_level<8, false>(L, rows, nseg, s);
-  if (seg <= 16 * kTopkThreads) return launch_level<16, false>(L, rows, nseg, s);
-  return launch_level<32, false>(L, rows, nseg, s);
+}
+
+// Long rows, step 2: one workgroup per row gathers the segments in position order (their
+// first kHead entries load together with the counts; the first digit is histogrammed on the
+// way) and selects; overflowing rows stream.
+__global__ __launch_bounds__(kSelThreads) void select_final_kernel(SelArgs a) {
+  __shared__ SelShared sh;
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t n = row_count(a, r);
+  const int64_t ns = (n + kSlice - 1) / kSlice;
+  const uint2 B = a.bound[r];
+  if (ns <= kMaxSegLds) {
+    const bool spec = ns * kHead <= int64_t(kSelThreads) * kHeadPerThread;
+    uint2 hv[kHeadPerThread];
+    if (spec) {
+#pragma unroll
+      for (int q = 0; q < kHeadPerThread; ++q) {
+        const int idx = tid + q * kSelThreads;
+        const int64_t sb = idx / kHead;
+        hv[q] = sb < ns ? a.seg[(r * a.nseg + sb) * kSegCap + idx % kHead] : make_uint2(0u, 0u);
+      }
+    }
+    uint32_t c[kSegPerThread], loc = 0;
+    bool over = false, longseg = false;
+#pragma unroll
+    for (int q = 0; q < kSegPerThread; ++q) {
+      const int64_t j = int64_t(tid) * kSegPerThread + q;
+      c[q] = j < ns ? uint32_t(a.seg_n[r * a.nseg + j]) : 0u;
+      over |= c[q] > uint32_t(kSegCap);
+      longseg |= c[q] > uint32_t(kHead);
+      loc += c[q];
+    }
+    clear_words(sh.h0, kBins0);
+    clear_words(sh.h0g, kBins0 / kGroup);
+    if (tid == 0) sh.flag = 0u;
+    __syncthreads();
+    if (over) atomicOr(&sh.flag, 1u);
+    if (longseg) atomicOr(&sh.flag, 2u);
+    uint32_t total;
+    uint32_t off = excl_scan(loc, sh.wred, &total);
+#pragma unroll
+    for (int q = 0; q < kSegPerThread; ++q) {
+      const int64_t j = int64_t(tid) * kSegPerThread + q;
+      if (j < ns) sh.segoff[j] = off;
+      off += c[q];
+    }
+    __syncthreads();
+    const uint32_t flag = sh.flag;
+    if ((flag & 1u) == 0u && total <= uint32_t(kListCap)) {
+      const uint32_t T = B.x;
+      const Digit0 d0 = digit0(T, B.y);
+      const bool hist = total > a.K;
+      if (spec) {
+#pragma unroll
+        for (int q = 0; q < kHeadPerThread; ++q) {
+          const int idx = tid + q * kSelThreads;
+          const int64_t sb = idx / kHead;
+          if (sb < ns) {
+            const uint32_t o0 = sh.segoff[sb];
+            const uint32_t cb = (sb + 1 < ns ? sh.segoff[sb + 1] : total) - o0;
+            const uint32_t e = uint32_t(idx % kHead);
+            if (e < cb) {
+              sh.list.lk[o0 + e] = hv[q].x;
+              sh.list.lp[o0 + e] = hv[q].y;
+              if (hist) hist_add(sh.h0, sh.h0g, bin0(hv[q].x, T, d0));
+            }
+          }
+        }
+      }
+      if (!spec || (flag & 2u)) {
+        // list slot j comes from the last segment whose offset is <= j
+        for (uint32_t j = tid; j < total; j += kSelThreads) {
+          int lo = 0, hi = int(ns) - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sh.segoff[mid] <= j) lo = mid;
+            else hi = mid - 1;
+          }
+          const uint32_t e = j - sh.segoff[lo];
+          if (spec && e < uint32_t(kHead)) continue;
+          const uint2 v = a.seg[(r * a.nseg + lo) * kSegCap + e];
+          sh.list.lk[j] = v.x;
+          sh.list.lp[j] = v.y;
+          if (hist) hist_add(sh.h0, sh.h0g, bin0(v.x, T, d0));
+        }
+      }
+      __syncthreads();
+      if (!hist) select_all(a, sh, r, total);
+      else select_list(a, sh, r, total, T, d0.lo, d0.nbins);
+      return;
+    }
+  }
+  select_stream(a, sh, r, n, B.x);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : dflt;
-}
-// Tuning override (read once): positions per segment.
-int64_t tune_seg() {
-  static const int64_t v = [] {
-    int64_t x = env_int("CSA_TUNE_TOPK_SEG", int(kSegMax));
-    return x >= 2048 && x <= kSegMax ? (x + 2047) / 2048 * 2048 : kSegMax;
-  }();
-  return v;
-}
-
-// Scratch layout: two ping-pong candidate buffers (ids, scores) sized by the first level.
-struct Plan {
-  int64_t seg, nseg;
+struct SelPlan {
+  bool split;
+  int64_t nseg;
+  size_t off_seg_n, off_seg, bytes;
 };
-constexpr int64_t kSegIds = int64_t(kMaxItemsIds) * kTopkThreads;
-Plan plan(int64_t n, bool has_ids) {
-  Plan p{};
-  p.seg = has_ids ? kSegIds : tune_seg();
-  if (n <= p.seg) return p;
-  p.nseg = ceil_div(n, p.seg);
+SelPlan sel_plan(int64_t rows, int64_t max_count) {
+  SelPlan p{};
+  p.split = max_count > kRowMax;
+  p.nseg = p.split ? ceil_div(max_count, kSlice) : 0;
+  p.off_seg_n = round256(size_t(rows) * 8);
+  p.off_seg = p.off_seg_n + round256(size_t(rows) * p.nseg * 4);
+  p.bytes = p.off_seg + size_t(rows) * p.nseg * kSegCap * 8;
   return p;
 }
 
 }  // namespace
 
 size_t topk_scratch_bytes(int64_t rows, int64_t max_count, int K) {
-  // the larger of the two plans (implicit / explicit ids)
-  const Plan a = plan(max_count, false), b = plan(max_count, true);
-  const int64_t ns = a.nseg > b.nseg ? a.nseg : b.nseg;
-  return size_t(4) * rows * ns * K * 4;
+  (void)K;
+  return sel_plan(rows, max_count).bytes;
 }
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  if (a.rows == 0) return hipSuccess;
-  const int64_t n = a.max_count < 1 ? 1 : a.max_count;
-  const Plan p = plan(n, a.ids != nullptr);
-  if (p.nseg == 0) {
-    TopkLevel L{a.scores, a.stride, a.ids, a.id_stride, a.id_limit, a.count, n, n, a.K,
-                a.out_idx, a.out_score, a.out_stride};
-    return run_level(L, a.rows, 1, s);
+hipError_t launch_topk(const TopkArgs& t, hipStream_t s) {
+  if (t.rows == 0) return hipSuccess;
+  const int64_t mc = t.max_count > 0 ? t.max_count : 0;
+  const SelPlan p = sel_plan(t.rows, mc);
+  char* base = reinterpret_cast<char*>(t.scratch);
+  SelArgs a;
+  a.scores = t.scores; a.stride = t.stride; a.gmax = t.gmax; a.gstride = t.gstride;
+  a.ids = t.ids; a.id_stride = t.id_stride; a.id_limit = t.id_limit; a.count = t.count;
+  a.max_count = mc; a.K = uint32_t(t.K); a.out_idx = t.out_idx; a.out_score = t.out_score;
+  a.out_stride = t.out_stride;
+  a.bound = reinterpret_cast<uint2*>(base);
+  a.seg_n = reinterpret_cast<int32_t*>(base + p.off_seg_n);
+  a.seg = reinterpret_cast<uint2*>(base + p.off_seg);
+  a.nseg = p.nseg;
+  const unsigned rows = static_cast<unsigned>(t.rows);
+  if (!p.split) {
+    hipLaunchKernelGGL(select_row_kernel, dim3(rows), dim3(kSelThreads), 0, s, a);
+    return hipGetLastError();
   }
-  const int64_t per = a.rows * p.nseg * a.K;
-  char* base = reinterpret_cast<char*>(a.scratch);
-  int32_t* idb[2] = {reinterpret_cast<int32_t*>(base),
-                     reinterpret_cast<int32_t*>(base + per * 4)};
-  float* scb[2] = {reinterpret_cast<float*>(base + 2 * per * 4),
-                   reinterpret_cast<float*>(base + 3 * per * 4)};
-  // level 0: segments of the rows
-  TopkLevel L0{a.scores, a.stride, a.ids, a.id_stride, a.id_limit, a.count, n, p.seg, a.K,
-               idb[0], scb[0], p.nseg * a.K};
-  hipError_t e = run_level(L0, a.rows, p.nseg, s);
-  if (e != hipSuccess) return e;
-  int cur = 0;
-  int64_t m = p.nseg * a.K;   // candidates per row at the current level
-  while (true) {
-    if (m <= kSegIds) {
-      TopkLevel Lf{scb[cur], m, idb[cur], m, nullptr, nullptr, m, m, a.K, a.out_idx,
-                   a.out_score, a.out_stride};
-      return run_level(Lf, a.rows, 1, s);
-    }
-    const int64_t ns = ceil_div(m, kSegIds);
-    TopkLevel Lm{scb[cur], m, idb[cur], m, nullptr, nullptr, m, kSegIds, a.K, idb[cur ^ 1],
-                 scb[cur ^ 1], ns * a.K};
-    e = run_level(Lm, a.rows, ns, s);
-    if (e != hipSuccess) return e;
-    cur ^= 1;
-    m = ns * a.K;
-  }
+  hipLaunchKernelGGL(select_slice_kernel, dim3(static_cast<unsigned>(p.nseg), rows),
+                     dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(select_final_kernel, dim3(rows), dim3(kSelThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 // ---- block maxima ------------------------------------------------------------------------

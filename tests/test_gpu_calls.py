@@ -121,6 +121,31 @@ def test_index_long_rows_segmented_select():
     check_index(q, w, k, pos, 4, 512)
 
 
+@pytest.mark.parametrize("n_dup,contiguous", [(600, False), (600, True), (9000, False)])
+def test_index_exact_ties(n_dup, contiguous):
+    """Exact score ties across the K-th place: n_dup copies of the best key row (scaled by 2,
+    exact in bf16) score identically on both sides, so the K places go to the lowest ids.
+    Spread copies exercise the LDS list; a contiguous run overflows one filter segment and a
+    9,000-copy spread overflows the list: both take the streaming select."""
+    E, K = 40000, 512
+    q, w, k, pos = index_case(1, 1, E, 64, 128, "bf16", 4 * E - 1, 4 * E, seed=11)
+    s = ocsa.index_scores(f64(q[0, 0]), f64(w[0, 0]), f64(k[0]))
+    best = int(np.argmax(s))
+    g = np.random.default_rng(11)
+    if contiguous:
+        at = np.arange(7000, 7000 + n_dup)
+    else:
+        at = np.sort(g.choice(E, size=n_dup, replace=False))
+    k[0, at] = (k[0, best].float() * 2).to(k.dtype)
+    res = csa.index_topk(dev(q), dev(w), dev(k), dev(pos), 4, K, want_scores=True)
+    idx, osc = [x.cpu() for x in res]
+    ref = pipeline.index_topk(q, w, k, pos, None, 4, K)
+    ids = ref[(0, 0)][0]
+    assert np.array_equal(ids, np.sort(at)[:K])
+    assert_ids(idx[0, 0].numpy(), ids, "ties")
+    assert np.all(osc[0, 0].numpy() == osc[0, 0, 0].item())
+
+
 def test_index_prefill_fast_path():
     # >= 16 query rows: LDS-tiled MFMA scan; consecutive positions, causal edge inside tiles
     B, Q, E = 1, 40, 3000
