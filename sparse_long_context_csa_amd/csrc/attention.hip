@@ -49,21 +49,29 @@ __device__ __forceinline__ const T* row_ptr(const AttnArgs& a, int64_t r, int64_
 
 }  // namespace
 
-// Number of row splits per query row (workgroups sharing one query's rows).
+// Number of row splits per query row (workgroups sharing one query's rows): few query rows
+// (decode) spread each row list over up to 256 workgroups in all, one tile or more each:
+// a wave's chain of LDS reads and MFMAs per tile is latency-bound, so tiles run in
+// parallel workgroups and the partial results are merged afterwards.
+constexpr int kMinTilesPerSplit = 1;
 static int attn_splits(int64_t rows, int top_k, int window, int H, int D, int dt) {
   if (!(dt == kBF16 && H == kAH && D == kAD)) return 1;
   const int64_t tiles = ceil_div(int64_t(top_k) + window, kTile);
-  if (rows >= 256 || tiles <= 1) return 1;
-  int64_t want = 256 / rows;
-  if (want > tiles) want = tiles;
-  if (want > 256) want = 256;
+  if (rows >= 256 || tiles < 2) return 1;
+  int64_t want = ceil_div(tiles, kMinTilesPerSplit);
+  const int64_t cap = 256 / rows;
+  if (want > cap) want = cap;
   return int(want < 1 ? 1 : want);
 }
+
+// Partials of split s of row r: the unnormalised output in the MFMA accumulator layout,
+// [wave][nt][lane] float4 (64 heads x 512 dims), then (max, sum) per head in base 2.
+constexpr int64_t kPartO = int64_t(kAH) * kAD;   // floats per (row, split)
 
 size_t attn_ws_bytes(int64_t rows, int H, int D, int top_k, int window, int dt) {
   const int ns = attn_splits(rows, top_k, window, H, D, dt);
   if (ns <= 1) return 0;
-  return size_t(rows) * ns * H * (D + 2) * 4;
+  return size_t(rows) * ns * (kPartO + 2 * kAH) * 4;
 }
 
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, int nsplit, int tiles_per_split) {
@@ -83,51 +91,92 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, int nsplit, 
   const int g = lane >> 4, col = lane & 15;
   const int head = 16 * wave + col;   // head of this lane in the score layout
 
-  // Q^T as B operand: head `head`, dims ks*32 + g*8 .. +8
+  // gather assignment: thread -> rows 4*ra .. 4*ra+3 (ra = tid & 7), 16-byte chunks cp and
+  // cp + 32 (cp = tid >> 3); rows past the list read the query row and are zeroed
+  const int ra = tid & 7, cp = tid >> 3;
+  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + r * kAH * kAD;
+  bf16x8_t vv[4][2];
+  bool okr[4];
+  const uint16_t* srcs[4];
+  auto locate = [&](int64_t j) {   // row pointers of tile j (the ids load here)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      srcs[i] = row_ptr<uint16_t>(a, r, sq, t, j + 4 * ra + i, int(j1));
+      okr[i] = srcs[i] != nullptr;
+    }
+  };
+  auto gather = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* sc = okr[i] ? srcs[i] : qrow;
+      vv[i][0] = *reinterpret_cast<const bf16x8_t*>(sc + cp * 8);
+      vv[i][1] = *reinterpret_cast<const bf16x8_t*>(sc + (cp + 32) * 8);
+    }
+  };
+  if (j0 < j1) locate(j0);
+  // Q^T as B operand: head `head`, dims ks*32 + g*8 .. +8 (loads while the ids arrive)
   bf16x8_t Qf[16];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (r * kAH + head) * kAD + g * 8;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) Qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 32);
   }
+  if (j0 < j1) gather();
   const float sl2 = a.scale * kLog2e;
   float m_run = neg_inf(), l_run = 0.f;
   f32x4_t O[32];
 #pragma unroll
   for (int nt = 0; nt < 32; ++nt) O[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // gather assignment: thread -> row (tid & 31), 16-byte chunks (tid >> 5) + 8k, k < 8
-  const int grow = tid & 31, gcb = tid >> 5;
   for (int64_t j = j0; j < j1; j += kTile) {
-    const uint16_t* src = row_ptr<uint16_t>(a, r, sq, t, j + grow, int(j1));
-    if (gcb == 0) rowok[grow] = src != nullptr;
-    // all 8 loads issued back to back (a missing row reads the query row and is zeroed)
-    const uint16_t* srcc = src ? src : reinterpret_cast<const uint16_t*>(a.q) + r * kAH * kAD;
-    bf16x8_t vv8[8];
+    // tile j to LDS: row-major (A operand of S^T) and transposed, 4 rows per 8-byte store
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      vv8[k] = *reinterpret_cast<const bf16x8_t*>(srcc + (gcb + 8 * k) * 8);
+    for (int i = 0; i < 4; ++i) {
+      if (!okr[i]) { vv[i][0] = bf16x8_t{}; vv[i][1] = bf16x8_t{}; }
+      if (cp == 0) rowok[4 * ra + i] = okr[i];
+      *reinterpret_cast<bf16x8_t*>(&kvs[(4 * ra + i) * kKvRow + cp * 16]) = vv[i][0];
+      *reinterpret_cast<bf16x8_t*>(&kvs[(4 * ra + i) * kKvRow + (cp + 32) * 16]) = vv[i][1];
+    }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = gcb + 8 * k;
-      const bf16x8_t v = src ? vv8[k] : bf16x8_t{};
-      *reinterpret_cast<bf16x8_t*>(&kvs[grow * kKvRow + c * 16]) = v;
-      const uint16_t* hv = reinterpret_cast<const uint16_t*>(&v);
+    for (int h = 0; h < 2; ++h) {
+      const int c = cp + 32 * h;
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vv[0][h]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vv[1][h]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vv[2][h]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vv[3][h]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint16_t*>(&vts[(c * 8 + e) * kVtRow + grow * 2]) = hv[e];
+      for (int e2 = 0; e2 < 4; ++e2) {
+        // dims 2*e2 (low halves) and 2*e2+1 (high halves) of the 4 rows
+        const uint32_t lo01 = __builtin_amdgcn_perm(w1[e2], w0[e2], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(w3[e2], w2[e2], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(w1[e2], w0[e2], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(w3[e2], w2[e2], 0x07060302u);
+        *reinterpret_cast<uint2*>(&vts[(c * 8 + 2 * e2) * kVtRow + ra * 8]) = make_uint2(lo01, lo23);
+        *reinterpret_cast<uint2*>(&vts[(c * 8 + 2 * e2 + 1) * kVtRow + ra * 8]) = make_uint2(hi01, hi23);
+      }
     }
     __syncthreads();
+    // the next tile's rows load while this one computes
+    if (j + kTile < j1) {
+      locate(j + kTile);
+      gather();
+    }
 
     // S^T: rows (4g+i) and (16+4g+i) against head `head`
-    f32x4_t S0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S1 = S0;
+    // four independent accumulator chains (even / odd K steps of both 16-row halves)
+    f32x4_t S0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S1 = S0, S2 = S0, S3 = S0;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
+    for (int ks = 0; ks < 16; ks += 2) {
       const bf16x8_t A0 = *reinterpret_cast<const bf16x8_t*>(&kvs[col * kKvRow + ks * 64 + g * 16]);
       const bf16x8_t A1 = *reinterpret_cast<const bf16x8_t*>(&kvs[(16 + col) * kKvRow + ks * 64 + g * 16]);
+      const bf16x8_t A2 = *reinterpret_cast<const bf16x8_t*>(&kvs[col * kKvRow + ks * 64 + 64 + g * 16]);
+      const bf16x8_t A3 = *reinterpret_cast<const bf16x8_t*>(&kvs[(16 + col) * kKvRow + ks * 64 + 64 + g * 16]);
       S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Qf[ks], S0, 0, 0, 0);
       S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Qf[ks], S1, 0, 0, 0);
+      S2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, Qf[ks + 1], S2, 0, 0, 0);
+      S3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3, Qf[ks + 1], S3, 0, 0, 0);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { S0[i] += S2[i]; S1[i] += S3[i]; }
     float s[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -167,8 +216,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, int nsplit, 
       const uint2 lo = *reinterpret_cast<const uint2*>(vp + 8 * g);
       const uint2 hi = *reinterpret_cast<const uint2*>(vp + 32 + 8 * g);
       bf16x8_t Vf;
-      const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      Vf = *reinterpret_cast<const bf16x8_t*>(&vv);
+      const uint4 vv4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      Vf = *reinterpret_cast<const bf16x8_t*>(&vv4);
       O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pf, Vf, O[nt], 0, 0, 0);
     }
     __syncthreads();
@@ -193,67 +242,80 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, int nsplit, 
       for (int i = 0; i < 4; ++i)
         op[(4 * g + i) * kAD + nt * 16 + col] = f32_to_bf16(O[nt][i] * fi[i]);
   } else {
-    // partial: [row][split][head][D + 2] = unnormalised O, then (max, sum) in base 2
-    float* pp = reinterpret_cast<float*>(a.ws) + ((r * nsplit + split) * kAH + 16 * wave) * (kAD + 2);
+    // partial in the accumulator layout (16-byte stores), then (max, sum) per head
+    const int64_t rs = r * nsplit + split;
+    f32x4_t* pp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.ws) + rs * kPartO) +
+                  wave * 32 * kWave + lane;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pp[(4 * g + i) * (kAD + 2) + nt * 16 + col] = O[nt][i];
+    for (int nt = 0; nt < 32; ++nt) pp[nt * kWave] = O[nt];
     if (g == 0) {
-      pp[col * (kAD + 2) + kAD] = m_run;
-      pp[col * (kAD + 2) + kAD + 1] = l_run;
+      float2* ml = reinterpret_cast<float2*>(reinterpret_cast<float*>(a.ws) +
+                                             int64_t(gridDim.y) * nsplit * kPartO) + rs * kAH;
+      ml[head] = make_float2(m_run, l_run);
     }
   }
 }
 
-// Merge the row splits of each (row, head) in split order: grid (H, rows). The split
-// weights e^{m_s - M} / den are computed once into LDS; every output element then sums its
-// nsplit partials with independent loads.
+// Merge the row splits in split order. Grid (32, rows): workgroup x covers the heads of
+// accumulator wave w = x / 8 and the dims of 4 accumulator columns; its first 16 threads
+// compute the split weights e^{m_s - M} / den of those 16 heads into LDS, then every thread
+// sums its float4 (4 heads, 1 dim) over the splits with independent loads.
 constexpr int kMaxSplit = 256;
 
-template <typename T>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nsplit) {
-  __shared__ float wgt[kMaxSplit];
-  __shared__ float red[2][4];
+  __shared__ float wgt[kMaxSplit][16];
+  __shared__ float2 mls[kMaxSplit][16];
   const int64_t r = blockIdx.y;
-  const int h = blockIdx.x;
-  const int H = a.H, D = a.D;
-  const float* part = reinterpret_cast<const float*>(a.ws) + ((r * nsplit) * H + h) * (D + 2);
-  const int64_t sstride = int64_t(H) * (D + 2);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float mi = neg_inf(), li = 0.f;
-  if (tid < nsplit) {
-    mi = part[tid * sstride + D];
-    li = part[tid * sstride + D + 1];
-  }
-  const float zs = a.sink ? a.sink[h] * kLog2e : neg_inf();
-  float M = wave_max(mi);
-  if (lane == 0) red[0][wave] = M;
+  const int w = blockIdx.x >> 3;
+  const int nt = (blockIdx.x & 7) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = gridDim.y;
+  const float* base = reinterpret_cast<const float*>(a.ws);
+  const float2* ml = reinterpret_cast<const float2*>(base + rows * nsplit * kPartO) +
+                     r * nsplit * kAH;
+  const f32x4_t* part = reinterpret_cast<const f32x4_t*>(base + r * nsplit * kPartO) +
+                        (w * 32 + nt) * kWave + lane;
+  constexpr int64_t sstride = kPartO / 4;   // float4 per split
+  // the first kSplitRegs partials load first, together with the (max, sum) pairs
+  constexpr int kSplitRegs = 32;
+  f32x4_t v[kSplitRegs];
+#pragma unroll
+  for (int sp = 0; sp < kSplitRegs; ++sp)
+    v[sp] = sp < nsplit ? part[sp * sstride] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int q = threadIdx.x; q < nsplit * 16; q += blockDim.x)
+    mls[q >> 4][q & 15] = ml[(q >> 4) * kAH + 16 * w + (q & 15)];
   __syncthreads();
-  M = fmaxf(fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3])), zs);
-  const float e = (mi == neg_inf() || M == neg_inf()) ? 0.f : exp2f(mi - M);
-  float den = wave_sum(li * e);
-  if (lane == 0) red[1][wave] = den;
-  __syncthreads();
-  den = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-  if (zs != neg_inf() && M != neg_inf()) den += exp2f(zs - M);
-  if (tid < nsplit) wgt[tid] = den > 0.f ? e / den : 0.f;
-  __syncthreads();
-  T* op = reinterpret_cast<T*>(a.out) + (r * H + h) * D;
-  for (int d = tid; d < D; d += blockDim.x) {
-    float acc = 0.f;
-    int sp = 0;
-    for (; sp + 4 <= nsplit; sp += 4) {
-      const float v0 = part[(sp + 0) * sstride + d], v1 = part[(sp + 1) * sstride + d];
-      const float v2 = part[(sp + 2) * sstride + d], v3 = part[(sp + 3) * sstride + d];
-      acc = fmaf(v0, wgt[sp + 0], acc);
-      acc = fmaf(v1, wgt[sp + 1], acc);
-      acc = fmaf(v2, wgt[sp + 2], acc);
-      acc = fmaf(v3, wgt[sp + 3], acc);
+  if (threadIdx.x < 16) {
+    const int h = 16 * w + threadIdx.x;
+    const float zs = a.sink ? a.sink[h] * kLog2e : neg_inf();
+    float M = zs;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mls[sp][threadIdx.x].x);
+    float den = (zs == neg_inf() || M == neg_inf()) ? 0.f : exp2f(zs - M);
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float2 m2 = mls[sp][threadIdx.x];
+      const float e = (m2.x == neg_inf() || M == neg_inf()) ? 0.f : exp2f(m2.x - M);
+      wgt[sp][threadIdx.x] = e;
+      den += m2.y * e;
     }
-    for (; sp < nsplit; ++sp) acc = fmaf(part[sp * sstride + d], wgt[sp], acc);
-    Elt<T>::store1(op + d, acc);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) wgt[sp][threadIdx.x] *= inv;
   }
+  __syncthreads();
+  const int g = lane >> 4, col = lane & 15;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sp = 0; sp < kSplitRegs; ++sp)
+    if (sp < nsplit)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(v[sp][i], wgt[sp][4 * g + i], acc[i]);
+  for (int sp = kSplitRegs; sp < nsplit; ++sp) {
+    const f32x4_t x = part[sp * sstride];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(x[i], wgt[sp][4 * g + i], acc[i]);
+  }
+  uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (r * kAH + 16 * w + 4 * g) * kAD + nt * 16 + col;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) op[i * kAD] = f32_to_bf16(acc[i]);
 }
 
 // ---- generic: one wave per (row, head); lanes hold 8 dims each --------------------------
@@ -324,8 +386,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (ns > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 g2(static_cast<unsigned>(a.H), static_cast<unsigned>(rows));
-    hipLaunchKernelGGL(attn_combine_kernel<uint16_t>, g2, dim3(256), 0, s, a, ns);
+    const dim3 g2(32u, static_cast<unsigned>(rows));
+    hipLaunchKernelGGL(attn_combine_kernel, g2, dim3(256), 0, s, a, ns);
   }
   return hipGetLastError();
 }
