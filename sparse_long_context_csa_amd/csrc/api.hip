@@ -88,25 +88,27 @@ int check_index_common(int64_t n_seq, int64_t n_q, int64_t e_cap, int32_t H, int
 hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, const int64_t* q_pos,
                      const int32_t* e_count, const int32_t* cand, int64_t n_cand, int64_t n_seq,
                      int64_t n_q, int64_t e_cap, int H, int d, int m, const TopkWs& ws,
-                     int top_k, hipStream_t s) {
-  (void)top_k;
+                     hipStream_t s, const IngestArgs* ingest = nullptr) {
   ScanArgs a;
   a.dt = dt; a.q = q; a.w = w; a.keys = keys; a.q_pos = q_pos; a.e_count = e_count;
   a.cand = cand; a.n_cand = n_cand; a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap;
   a.H = H; a.d = d; a.m = m; a.scores = ws.scores; a.score_stride = ws.stride;
   a.n_vis = ws.n_vis; a.count = ws.count;
   a.gmax = ws.gmax; a.gmax_stride = ws.gstride;
+  a.ingest = ingest ? *ingest : IngestArgs{};
   return launch_scan(a, s);
 }
 
 hipError_t select_rows(const TopkWs& ws, int64_t rows, int64_t max_count, const int32_t* ids,
                        int64_t id_stride, const int32_t* id_limit, int K, int32_t* out_idx,
-                       float* out_score, void* scratch, hipStream_t s) {
+                       float* out_score, void* scratch, hipStream_t s,
+                       const IngestArgs* side = nullptr) {
   TopkArgs t;
   t.scores = ws.scores; t.stride = ws.stride; t.ids = ids; t.id_stride = id_stride;
   t.gmax = ws.gmax; t.gstride = ws.gstride;
   t.id_limit = id_limit; t.count = ws.count; t.rows = rows; t.max_count = max_count; t.K = K;
   t.out_idx = out_idx; t.out_score = out_score; t.out_stride = K; t.scratch = scratch;
+  t.side = side;
   return launch_topk(t, s);
 }
 
@@ -118,7 +120,7 @@ hipError_t pool_rows(int64_t rows, int64_t e_cap, int bs, int mb, int32_t* out_p
   if (e != hipSuccess) return e;
   TopkArgs t;
   t.scores = ws.bmax; t.stride = ws.bstride; t.ids = nullptr; t.id_stride = 0;
-  t.gmax = nullptr; t.gstride = 0;
+  t.gmax = nullptr; t.gstride = 0; t.side = nullptr;
   t.id_limit = nullptr; t.count = ws.nb; t.rows = rows; t.max_count = (e_cap + bs - 1) / bs;
   t.K = mb; t.out_idx = ws.blocks; t.out_score = nullptr; t.out_stride = mb;
   t.scratch = ws.scratch2;
@@ -134,7 +136,7 @@ hipError_t blocks_rows(int dt, const void* q, const float* w, const void* keys,
                        int top_k, int32_t* out_idx, const BlocksWs& ws, hipStream_t s) {
   const int64_t rows = n_seq * n_q;
   hipError_t e = scan_rows(dt, q, w, keys, q_pos, e_count, nullptr, 0, n_seq, n_q, e_cap, H, d,
-                           m, ws.tk, out_idx ? top_k : 0, s);
+                           m, ws.tk, s);
   if (e != hipSuccess) return e;
   if (out_idx) {
     e = select_rows(ws.tk, rows, e_cap, nullptr, 0, nullptr, top_k, out_idx, nullptr,
@@ -206,7 +208,7 @@ int csa_index_topk(const void* q_idx, const float* w, const void* k_idx, const i
   Carver c(ws);
   const TopkWs tw = carve_topk(c, n_seq * n_q, n_keys, top_k);
   hipError_t e = scan_rows(dtype, q_idx, w, k_idx, q_pos, e_count, cand, n_cand, n_seq, n_q,
-                           e_cap, idx_heads, idx_dim, m, tw, top_k, s);
+                           e_cap, idx_heads, idx_dim, m, tw, s);
   if (e != hipSuccess) return CSA_ERR_HIP;
   e = select_rows(tw, n_seq * n_q, n_keys, cand, n_cand, cand ? tw.n_vis : nullptr, top_k,
                   out_idx, out_score, tw.scratch, s);
@@ -382,31 +384,37 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
     in.win[c2] = c2 < d->n_attn ? d->win[c2] : nullptr;
     in.win_new[c2] = (c2 < d->n_attn && d->w_cap > 0) ? d->win_new[c2] : nullptr;
   }
-  if (launch_ingest(in, s) != hipSuccess) return CSA_ERR_HIP;
+  // Where the decode scan can take it, the ingest is split between the stage-1 scan (the
+  // completed entry's indexer key, which that scan scores) and extra workgroups of the last
+  // select launch (tails, rings, main entry: read only by the attention). Otherwise it runs
+  // first as a kernel of its own. Event 1 then marks the end of that kernel (or event 0).
+  const bool fuse = scan_fuses_ingest(d->dtype, d->idx_heads, d->idx_dim, d->m);
+  if (!fuse && launch_ingest(in, s) != hipSuccess) return CSA_ERR_HIP;
+  const IngestArgs* split_ingest = fuse ? &in : nullptr;
   mark(1);
 
   // 3-4. index + select
   if (d->block_size > 0) {
     const int np = d->block_size * d->max_blocks;
     if (scan_rows(d->dtype, d->q_idx, d->w, d->k_idx, d->pos, nullptr, nullptr, 0, rows, 1,
-                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.blocks.tk, 0, s) != hipSuccess)
+                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.blocks.tk, s, split_ingest) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
     if (pool_rows(rows, d->e_cap, d->block_size, d->max_blocks, w.pool, w.blocks, s) != hipSuccess)
       return CSA_ERR_HIP;
     if (scan_rows(d->dtype, d->q_idx2, d->w2, d->k_idx, d->pos, nullptr, w.pool, np, rows, 1,
-                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, d->top_k, s) != hipSuccess)
+                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, s) != hipSuccess)
       return CSA_ERR_HIP;
     if (select_rows(w.flat, rows, np, w.pool, np, w.flat.n_vis, d->top_k, d->out_idx, nullptr,
-                    w.flat.scratch, s) != hipSuccess)
+                    w.flat.scratch, s, split_ingest) != hipSuccess)
       return CSA_ERR_HIP;
   } else {
     if (scan_rows(d->dtype, d->q_idx, d->w, d->k_idx, d->pos, nullptr, nullptr, 0, rows, 1,
-                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, d->top_k, s) != hipSuccess)
+                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, s, split_ingest) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
     if (select_rows(w.flat, rows, d->e_cap, nullptr, 0, nullptr, d->top_k, d->out_idx, nullptr,
-                    w.flat.scratch, s) != hipSuccess)
+                    w.flat.scratch, s, split_ingest) != hipSuccess)
       return CSA_ERR_HIP;
   }
 

@@ -21,6 +21,7 @@
 #include <stdlib.h>
 
 #include "csa_common.hpp"
+#include "ingest.hpp"
 #include "launch.hpp"
 
 namespace csa {
@@ -103,6 +104,52 @@ __device__ __forceinline__ void load_key_B(const uint16_t* row, int g, bf16x8_t 
   }
 }
 
+// Pool the new entry's indexer key from the values a lane holds (channels 2*lane and
+// 2*lane+1 of m rows, the new row in `slot`), store it to the cache, and when `mine` put it
+// into this lane's B operand: channels ks*32 + g*8 .. +8 come from lanes ks*16 + g*4 + 0..3.
+constexpr int kFuseM = 8;   // entries of up to 8 rows are pooled this way
+__device__ __forceinline__ void fuse_new_key(const IngestArgs& ig, int64_t r, int64_t e, int slot,
+                                             int lane, int g, bool mine, uint32_t xn, uint32_t zn,
+                                             const uint32_t (&xt)[kFuseM],
+                                             const uint32_t (&zt)[kFuseM],
+                                             const uint32_t (&bb)[kFuseM], bf16x8_t (&B)[4]) {
+  const int m = ig.m;
+  float res[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    auto half = [&](uint32_t w2) {
+      return bf16_to_f32(uint16_t(h ? (w2 >> 16) : (w2 & 0xffffu)));
+    };
+    float av[kFuseM], mx = neg_inf();
+#pragma unroll
+    for (int j = 0; j < kFuseM; ++j) {
+      av[j] = neg_inf();
+      if (j < m) {
+        av[j] = half(j == slot ? zn : zt[j]) + half(bb[j]);
+        mx = fmaxf(mx, av[j]);
+      }
+    }
+    float sum = 0.f, acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kFuseM; ++j)
+      if (j < m) {
+        const float ex = expf(av[j] - mx);
+        sum += ex;
+        acc = fmaf(ex, half(j == slot ? xn : xt[j]), acc);
+      }
+    res[h] = acc / sum;
+  }
+  const uint32_t pk = uint32_t(f32_to_bf16(res[0])) | (uint32_t(f32_to_bf16(res[1])) << 16);
+  reinterpret_cast<uint32_t*>(ig.k_idx)[(r * ig.e_cap + e) * (kID / 2) + lane] = pk;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint32_t wds[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wds[k] = uint32_t(__shfl(int(pk), ks * 16 + g * 4 + k));
+    if (mine) B[ks] = *reinterpret_cast<const bf16x8_t*>(wds);
+  }
+}
+
 }  // namespace
 
 // Persistent grid: work item it = (row, chunk) = (it / cpr, it % cpr), chunk positions
@@ -118,6 +165,7 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
   bf16x8_t A[4][4];
   float wv[4][4];
   int64_t cur = -1;
+  const bool fuse = !kCand && a.ingest.pos != nullptr;
   for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
     const int64_t r = it / cpr, c = it % cpr;
     const int64_t n_vis = row_visible(a, r);
@@ -150,6 +198,35 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
       ok = true;
       return p;
     };
+    // Decode ingest folded in: the entry that the step's token completes is pooled by the
+    // wave that scores it. Its inputs (2 channels per lane) load now, the pooling runs at
+    // that tile, and lane shuffles place the key in the B operand of its column.
+    int64_t e_new = -1;
+    int slot = 0;
+    uint32_t pxn = 0, pzn = 0, pxt[kFuseM], pzt[kFuseM], pb[kFuseM];
+#pragma unroll
+    for (int j = 0; j < kFuseM; ++j) pxt[j] = pzt[j] = pb[j] = 0u;
+    if (fuse) {
+      const int64_t t = a.ingest.pos[r];
+      const int64_t e = (t + 1) / a.ingest.m - 1;
+      if (t >= 0 && (t + 1) % a.ingest.m == 0 && e >= c0 && e < c1 &&
+          int((e - c0) >> 4) % 4 == wave) {
+        e_new = e;
+        slot = int(t % a.ingest.m);
+        const IngestArgs& ig = a.ingest;
+        const int m = ig.m;
+        pxn = reinterpret_cast<const uint32_t*>(ig.xi_new)[r * (kID / 2) + lane];
+        pzn = reinterpret_cast<const uint32_t*>(ig.zi_new)[r * (kID / 2) + lane];
+#pragma unroll
+        for (int j = 0; j < kFuseM; ++j) {
+          if (j < m && j != slot) {
+            pxt[j] = reinterpret_cast<const uint32_t*>(ig.xi_tail)[(r * m + j) * (kID / 2) + lane];
+            pzt[j] = reinterpret_cast<const uint32_t*>(ig.zi_tail)[(r * m + j) * (kID / 2) + lane];
+          }
+          if (j < m) pb[j] = reinterpret_cast<const uint32_t*>(ig.bias_i)[j * (kID / 2) + lane];
+        }
+      }
+    }
     const int64_t t0 = c0 + wave * 16;
     if (t0 >= c1) continue;
     bf16x8_t buf[PF + 1][4];
@@ -165,6 +242,9 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
       for (int u = 0; u <= PF; ++u) {
         const int64_t tl = t0 + (k + u) * 64;
         if (more && tl < c1) {
+          if (e_new >= tl && e_new < tl + 16)
+            fuse_new_key(a.ingest, r, e_new, slot, lane, g, col == int(e_new - tl), pxn, pzn, pxt,
+                         pzt, pb, buf[u]);
           const float s = tile_score(A, buf[u], wv);
           const int64_t p = tl + col;
           const float sv = (p < c1 && ok[u]) ? s : neg_inf();
@@ -383,6 +463,10 @@ static void launch_decode_pf(const ScanArgs& a, int64_t rows, int64_t max_pos, h
     default: nt ? launch_decode<kCand, 2, true>(a, rows, max_pos, s)
                 : launch_decode<kCand, 2, false>(a, rows, max_pos, s); break;
   }
+}
+
+bool scan_fuses_ingest(int dt, int H, int d, int m) {
+  return dt == kBF16 && H == kIH && d == kID && m <= kFuseM;
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {

@@ -1,0 +1,165 @@
+// Decode-step ingest of one new token per sequence: the new rows go into the compressor
+// tails and the window rings, and when the token completes an entry's m positions the
+// entry is pooled into the caches ("DeepSeek V4-Flash: The Cost of Deciding What to Read",
+// section "The compressor has two streams and they overlap": per-channel softmax pooling
+// with a positional bias). Shared by the ingest kernel and the decode scan, which folds the
+// same work into its own launch.
+#pragma once
+
+#include "csa_common.hpp"
+#include "launch.hpp"
+
+namespace csa {
+
+// Pool 8 channels over m rows. Row j's x/z come from memory (x0 + j*stride) except row
+// `own` whose values are passed in registers (xo, zo). For m <= kRegM every row is loaded
+// up front (one round trip to memory); longer entries take two passes over the logits.
+constexpr int kRegM = 8;
+
+// kRegs = false keeps to the two-pass form for every m (few registers: for callers that
+// must not raise their own register budget).
+template <typename T, bool kRegs = true>
+__device__ __forceinline__ void pool8(const T* x0, const T* z0, int64_t stride, const T* b0,
+                                      int bstride, int m, int own, const float* xo,
+                                      const float* zo, float* out) {
+  if (kRegs && m <= kRegM) {
+    float a[kRegM][8], xv[kRegM][8];
+#pragma unroll
+    for (int j = 0; j < kRegM; ++j) {
+      if (j < m) {
+        float bb[8];
+        if (j == own) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) { a[j][c] = zo[c]; xv[j][c] = xo[c]; }
+        } else {
+          Elt<T>::load8(z0 + j * stride, a[j]);
+          Elt<T>::load8(x0 + j * stride, xv[j]);
+        }
+        Elt<T>::load8(b0 + j * bstride, bb);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) a[j][c] += bb[c];
+      }
+    }
+    float mx[8], sum[8], acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { mx[c] = a[0][c]; sum[c] = 0.f; acc[c] = 0.f; }
+#pragma unroll
+    for (int j = 1; j < kRegM; ++j)
+      if (j < m)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) mx[c] = fmaxf(mx[c], a[j][c]);
+#pragma unroll
+    for (int j = 0; j < kRegM; ++j)
+      if (j < m)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float e = expf(a[j][c] - mx[c]);
+          sum[c] += e;
+          acc[c] = fmaf(e, xv[j][c], acc[c]);
+        }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) out[c] = acc[c] / sum[c];
+    return;
+  }
+  float mx[8], a[8], bb[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) mx[c] = neg_inf();
+  for (int j = 0; j < m; ++j) {
+    if (j == own) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a[c] = zo[c];
+    } else {
+      Elt<T>::load8(z0 + j * stride, a);
+    }
+    Elt<T>::load8(b0 + j * bstride, bb);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) mx[c] = fmaxf(mx[c], a[c] + bb[c]);
+  }
+  float sum[8], acc[8], xv[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) { sum[c] = 0.f; acc[c] = 0.f; }
+  for (int j = 0; j < m; ++j) {
+    if (j == own) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) { a[c] = zo[c]; xv[c] = xo[c]; }
+    } else {
+      Elt<T>::load8(z0 + j * stride, a);
+      Elt<T>::load8(x0 + j * stride, xv);
+    }
+    Elt<T>::load8(b0 + j * bstride, bb);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float e = expf(a[c] + bb[c] - mx[c]);
+      sum[c] += e;
+      acc[c] = fmaf(e, xv[c], acc[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) out[c] = acc[c] / sum[c];
+}
+
+// Vectors of 8 channels one sequence's ingest covers: main stream, indexer stream, rings.
+__device__ __forceinline__ int ingest_vectors(const IngestArgs& a) {
+  return (a.dim >> 3) + (a.idx_dim >> 3) + a.n_ring * (a.dim >> 3);
+}
+
+// Vector v of sequence sq: [0, vd) main stream (tail row, pooled entry when complete),
+// [vd, vd+vi) indexer stream (tail row; pooled key when complete and pool_index), then
+// n_ring * vd window-ring vectors (row t % w_cap of ring c from win_new[c], when given).
+template <typename T, bool kRegs = true>
+__device__ __forceinline__ void ingest_vector(const IngestArgs& a, int64_t sq, int v,
+                                              bool pool_index) {
+  const int vd = a.dim >> 3, vi = a.idx_dim >> 3;
+  const int64_t t = a.pos[sq];
+  if (t < 0) return;
+  const int m = a.m;
+  const int slot = int(t % m);
+  const bool complete = ((t + 1) % m) == 0;
+  const int64_t e = (t + 1) / m - 1;
+  if (v < vd + vi) {
+    const bool main = v < vd;
+    const int d = main ? a.dim : a.idx_dim;
+    const int c0 = (main ? v : v - vd) << 3;
+    const T* xn = (const T*)(main ? a.x_new : a.xi_new) + sq * d + c0;
+    const T* zn = (const T*)(main ? a.z_new : a.zi_new) + sq * d + c0;
+    T* xt = (T*)(main ? a.x_tail : a.xi_tail) + sq * m * d + c0;
+    T* zt = (T*)(main ? a.z_tail : a.zi_tail) + sq * m * d + c0;
+    float xo[8], zo[8];
+    Elt<T>::load8(xn, xo);
+    Elt<T>::load8(zn, zo);
+    Elt<T>::store8(xt + slot * d, xo);
+    Elt<T>::store8(zt + slot * d, zo);
+    if (complete && e < a.e_cap && (main || pool_index)) {
+      float res[8];
+      pool8<T, kRegs>(xt, zt, d, (const T*)(main ? a.bias : a.bias_i) + c0, d, m, slot, xo, zo,
+                      res);
+      T* dst = (T*)(main ? a.kv : a.k_idx) + (sq * a.e_cap + e) * d + c0;
+      Elt<T>::store8(dst, res);
+    }
+    return;
+  }
+  const int r = v - vd - vi;
+  const int c = r / vd;
+  const int c0 = (r % vd) << 3;
+  const T* src = (const T*)a.win_new[c];
+  if (src == nullptr) return;
+  float w8[8];
+  Elt<T>::load8(src + sq * a.dim + c0, w8);
+  Elt<T>::store8((T*)a.win[c] + (sq * a.w_cap + t % a.w_cap) * a.dim + c0, w8);
+}
+
+// The pooled indexer key vector v (8 channels) of the entry that position t completes,
+// computed from the tails and the new row (the tail slot of t is not read).
+template <typename T, bool kRegs = true>
+__device__ __forceinline__ void pool_index_vector(const IngestArgs& a, int64_t sq, int64_t t,
+                                                  int v, float* res) {
+  const int m = a.m, d = a.idx_dim, c0 = v << 3;
+  const int slot = int(t % m);
+  float xo[8], zo[8];
+  Elt<T>::load8((const T*)a.xi_new + sq * d + c0, xo);
+  Elt<T>::load8((const T*)a.zi_new + sq * d + c0, zo);
+  pool8<T, kRegs>((const T*)a.xi_tail + sq * m * d + c0, (const T*)a.zi_tail + sq * m * d + c0,
+                  d, (const T*)a.bias_i + c0, d, m, slot, xo, zo, res);
+}
+
+}  // namespace csa

@@ -49,8 +49,14 @@ struct ScanArgs {
   int32_t* count;         // [rows]
   float* gmax;            // [rows, gmax_stride]: max of positions [16j, 16j+16)
   int64_t gmax_stride;
+  // Decode step (rows are sequences) with its ingest split between the scan and the select
+  // (ingest.pos non-null): the scan pools the indexer key of the entry the token completes;
+  // the select's ingest workgroups do the rest. Only when scan_fuses_ingest() holds.
+  IngestArgs ingest;
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+// Whether the decode scan for this shape takes the indexer-key part of the ingest.
+bool scan_fuses_ingest(int dt, int H, int d, int m);
 
 // ---- selection ---------------------------------------------------------------------------
 // Top-K of each row's `count[r]` positions; position j has score scores[r*stride + j] and
@@ -73,6 +79,9 @@ struct TopkArgs {
   float* out_score;       // may be null
   int64_t out_stride;
   void* scratch;          // segment buffers (see topk_scratch_bytes)
+  // optional: the rest of a decode step's ingest (tails, rings, main entry), run by extra
+  // workgroups of the select's last launch (indexer keys are the scan's part)
+  const IngestArgs* side;
 };
 size_t topk_scratch_bytes(int64_t rows, int64_t max_count, int K);
 

@@ -35,6 +35,7 @@
 #include <stdlib.h>
 
 #include "csa_common.hpp"
+#include "ingest.hpp"
 #include "launch.hpp"
 
 namespace csa {
@@ -79,7 +80,18 @@ struct SelArgs {
   int32_t* seg_n;         // [rows][nseg] candidates found (may exceed kSegCap)
   uint2* seg;             // [rows][nseg][kSegCap] (key, position)
   int64_t nseg;
+  int64_t rows;
+  int64_t n_side;         // ingest workgroups after the rows' (0: none)
+  IngestArgs side;
 };
+
+// A decode step's ingest (without the indexer keys) for sequence sq, by one workgroup.
+__device__ __forceinline__ void side_ingest(const SelArgs& a, int64_t sq) {
+  for (int v = threadIdx.x; v < ingest_vectors(a.side); v += blockDim.x) {
+    if (a.side.dt == kBF16) ingest_vector<uint16_t>(a.side, sq, v, false);
+    else ingest_vector<float>(a.side, sq, v, false);
+  }
+}
 
 struct SelShared {
   union {
@@ -569,6 +581,10 @@ __device__ __forceinline__ uint32_t slice_flags(const SelArgs& a, int64_t r, int
 // this one is compacted), select.
 __global__ __launch_bounds__(kSelThreads) void select_row_kernel(SelArgs a) {
   __shared__ SelShared sh;
+  if (int64_t(blockIdx.x) >= a.rows) {
+    side_ingest(a, int64_t(blockIdx.x) - a.rows);
+    return;
+  }
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t n = row_count(a, r);
@@ -660,6 +676,10 @@ __global__ __launch_bounds__(kSelThreads) void select_slice_kernel(SelArgs a) {
 // way) and selects; overflowing rows stream.
 __global__ __launch_bounds__(kSelThreads) void select_final_kernel(SelArgs a) {
   __shared__ SelShared sh;
+  if (int64_t(blockIdx.x) >= a.rows) {
+    side_ingest(a, int64_t(blockIdx.x) - a.rows);
+    return;
+  }
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t n = row_count(a, r);
@@ -788,14 +808,18 @@ hipError_t launch_topk(const TopkArgs& t, hipStream_t s) {
   a.seg_n = reinterpret_cast<int32_t*>(base + p.off_seg_n);
   a.seg = reinterpret_cast<uint2*>(base + p.off_seg);
   a.nseg = p.nseg;
+  a.rows = t.rows;
+  a.n_side = t.side ? t.side->n_seq : 0;
+  a.side = t.side ? *t.side : IngestArgs{};
   const unsigned rows = static_cast<unsigned>(t.rows);
+  const unsigned last = static_cast<unsigned>(t.rows + a.n_side);   // + ingest workgroups
   if (!p.split) {
-    hipLaunchKernelGGL(select_row_kernel, dim3(rows), dim3(kSelThreads), 0, s, a);
+    hipLaunchKernelGGL(select_row_kernel, dim3(last), dim3(kSelThreads), 0, s, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(select_slice_kernel, dim3(static_cast<unsigned>(p.nseg), rows),
                      dim3(kSelThreads), 0, s, a);
-  hipLaunchKernelGGL(select_final_kernel, dim3(rows), dim3(kSelThreads), 0, s, a);
+  hipLaunchKernelGGL(select_final_kernel, dim3(last), dim3(kSelThreads), 0, s, a);
   return hipGetLastError();
 }
 
