@@ -317,7 +317,7 @@ def main():
                    "heads": spec.H, "head_dim": spec.D, "idx_heads": spec.H_I,
                    "idx_dim": spec.d_I, "state_copies": args.copies,
                    "launch": "hip_graph" if args.graph else "eager"},
-        "roofline": {"bound": "hbm", "kernel": "scan_decode_kernel (indexer scan, stage 1)",
+        "roofline": {"bound": "hbm", "kernel": "scan_stream_kernel (indexer scan, stage 1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic() if args.config == 4 else None,

@@ -37,9 +37,12 @@ struct TopkWs {
   int32_t* n_vis;
   int32_t* count;
   void* scratch;
+  void* seg;          // candidate segments of long decode rows (null when not carved)
   int64_t stride, gstride;
 };
-TopkWs carve_topk(Carver& c, int64_t rows, int64_t n_keys, int32_t top_k) {
+// few query rows per sequence: the scan is the decode kernel (as in launch_scan)
+bool decode_rows(int64_t n_q) { return n_q < 16; }
+TopkWs carve_topk(Carver& c, int64_t rows, int64_t n_keys, int32_t top_k, int64_t n_q) {
   TopkWs w;
   w.stride = round64(n_keys > 0 ? n_keys : 1);
   w.scores = c.take<float>(size_t(rows) * w.stride * 4);
@@ -48,7 +51,20 @@ TopkWs carve_topk(Carver& c, int64_t rows, int64_t n_keys, int32_t top_k) {
   w.n_vis = c.take<int32_t>(size_t(rows) * 4);
   w.count = c.take<int32_t>(size_t(rows) * 4);
   w.scratch = c.take<char>(topk_scratch_bytes(rows, n_keys, top_k));
+  w.seg = nullptr;
+  if (decode_rows(n_q) && n_keys > kSegRowMin) w.seg = c.take<char>(seg_bytes(rows, n_keys));
   return w;
+}
+
+// Segments of the decode scan for the select, when the scan is the bf16 64x128 decode kernel
+// over the whole cache (no candidate list) and rows are long; both the scan and the select
+// call this with the same arguments.
+SegArgs segments_for(const TopkWs& ws, int dt, int H, int d, int64_t n_q, bool cand,
+                     int64_t rows, int64_t n_keys, int K) {
+  SegArgs g{};
+  if (ws.seg == nullptr || cand || !decode_rows(n_q) || n_keys <= kSegRowMin) return g;
+  if (!(dt == kBF16 && H == 64 && d == 128)) return g;
+  return seg_carve(ws.seg, rows, n_keys, K);
 }
 
 // ---- csa_index_blocks workspace ----------------------------------------------------------
@@ -61,9 +77,9 @@ struct BlocksWs {
   int64_t bstride;
 };
 BlocksWs carve_blocks(Carver& c, int64_t rows, int64_t e_cap, int32_t bs, int32_t mb,
-                      int32_t top_k) {
+                      int32_t top_k, int64_t n_q) {
   BlocksWs w;
-  w.tk = carve_topk(c, rows, e_cap, top_k > 0 ? top_k : 1);
+  w.tk = carve_topk(c, rows, e_cap, top_k > 0 ? top_k : 1, n_q);
   const int64_t nbmax = (e_cap + bs - 1) / bs;
   w.bstride = round64(nbmax);
   w.bmax = c.take<float>(size_t(rows) * w.bstride * 4);
@@ -88,27 +104,30 @@ int check_index_common(int64_t n_seq, int64_t n_q, int64_t e_cap, int32_t H, int
 hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, const int64_t* q_pos,
                      const int32_t* e_count, const int32_t* cand, int64_t n_cand, int64_t n_seq,
                      int64_t n_q, int64_t e_cap, int H, int d, int m, const TopkWs& ws,
-                     hipStream_t s, const IngestArgs* ingest = nullptr) {
-  ScanArgs a;
+                     hipStream_t s, const IngestArgs* ingest = nullptr, int seg_k = 0) {
+  ScanArgs a{};
   a.dt = dt; a.q = q; a.w = w; a.keys = keys; a.q_pos = q_pos; a.e_count = e_count;
   a.cand = cand; a.n_cand = n_cand; a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap;
   a.H = H; a.d = d; a.m = m; a.scores = ws.scores; a.score_stride = ws.stride;
   a.n_vis = ws.n_vis; a.count = ws.count;
   a.gmax = ws.gmax; a.gmax_stride = ws.gstride;
   a.ingest = ingest ? *ingest : IngestArgs{};
+  a.seg = seg_k > 0 ? segments_for(ws, dt, H, d, n_q, cand != nullptr, n_seq * n_q, e_cap, seg_k)
+                    : SegArgs{};
   return launch_scan(a, s);
 }
 
 hipError_t select_rows(const TopkWs& ws, int64_t rows, int64_t max_count, const int32_t* ids,
                        int64_t id_stride, const int32_t* id_limit, int K, int32_t* out_idx,
                        float* out_score, void* scratch, hipStream_t s,
-                       const IngestArgs* side = nullptr) {
-  TopkArgs t;
+                       const IngestArgs* side = nullptr, const SegArgs& seg = SegArgs{}) {
+  TopkArgs t{};
   t.scores = ws.scores; t.stride = ws.stride; t.ids = ids; t.id_stride = id_stride;
   t.gmax = ws.gmax; t.gstride = ws.gstride;
   t.id_limit = id_limit; t.count = ws.count; t.rows = rows; t.max_count = max_count; t.K = K;
   t.out_idx = out_idx; t.out_score = out_score; t.out_stride = K; t.scratch = scratch;
   t.side = side;
+  t.seg = seg;
   return launch_topk(t, s);
 }
 
@@ -118,7 +137,7 @@ hipError_t pool_rows(int64_t rows, int64_t e_cap, int bs, int mb, int32_t* out_p
   hipError_t e = launch_block_max(ws.tk.scores, ws.tk.stride, ws.tk.count, rows, e_cap, bs,
                                   ws.bmax, ws.bstride, ws.nb, s);
   if (e != hipSuccess) return e;
-  TopkArgs t;
+  TopkArgs t{};
   t.scores = ws.bmax; t.stride = ws.bstride; t.ids = nullptr; t.id_stride = 0;
   t.gmax = nullptr; t.gstride = 0; t.side = nullptr;
   t.id_limit = nullptr; t.count = ws.nb; t.rows = rows; t.max_count = (e_cap + bs - 1) / bs;
@@ -136,11 +155,12 @@ hipError_t blocks_rows(int dt, const void* q, const float* w, const void* keys,
                        int top_k, int32_t* out_idx, const BlocksWs& ws, hipStream_t s) {
   const int64_t rows = n_seq * n_q;
   hipError_t e = scan_rows(dt, q, w, keys, q_pos, e_count, nullptr, 0, n_seq, n_q, e_cap, H, d,
-                           m, ws.tk, s);
+                           m, ws.tk, s, nullptr, out_idx ? top_k : 0);
   if (e != hipSuccess) return e;
   if (out_idx) {
     e = select_rows(ws.tk, rows, e_cap, nullptr, 0, nullptr, top_k, out_idx, nullptr,
-                    ws.tk.scratch, s);
+                    ws.tk.scratch, s, nullptr,
+                    segments_for(ws.tk, dt, H, d, n_q, false, rows, e_cap, top_k));
     if (e != hipSuccess) return e;
   }
   return pool_rows(rows, e_cap, bs, mb, out_pool, ws, s);
@@ -185,7 +205,7 @@ int csa_compress(const void* x, const void* logits, const void* bias, void* out,
 size_t csa_index_topk_workspace_size(int64_t n_seq, int64_t n_q, int64_t n_keys, int32_t top_k) {
   if (n_seq < 0 || n_q < 0 || n_keys < 0 || top_k < 1) return 0;
   Carver c(nullptr);
-  carve_topk(c, n_seq * n_q, n_keys, top_k);
+  carve_topk(c, n_seq * n_q, n_keys, top_k, n_q);
   return c.off;
 }
 
@@ -206,12 +226,14 @@ int csa_index_topk(const void* q_idx, const float* w, const void* k_idx, const i
   if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carver c(ws);
-  const TopkWs tw = carve_topk(c, n_seq * n_q, n_keys, top_k);
+  const TopkWs tw = carve_topk(c, n_seq * n_q, n_keys, top_k, n_q);
   hipError_t e = scan_rows(dtype, q_idx, w, k_idx, q_pos, e_count, cand, n_cand, n_seq, n_q,
-                           e_cap, idx_heads, idx_dim, m, tw, s);
+                           e_cap, idx_heads, idx_dim, m, tw, s, nullptr, top_k);
   if (e != hipSuccess) return CSA_ERR_HIP;
   e = select_rows(tw, n_seq * n_q, n_keys, cand, n_cand, cand ? tw.n_vis : nullptr, top_k,
-                  out_idx, out_score, tw.scratch, s);
+                  out_idx, out_score, tw.scratch, s, nullptr,
+                  segments_for(tw, dtype, idx_heads, idx_dim, n_q, cand != nullptr, n_seq * n_q,
+                               n_keys, top_k));
   if (e != hipSuccess) return CSA_ERR_HIP;
   if (scores_all) {
     e = launch_fill_scores(tw.scores, tw.stride, tw.count, n_seq * n_q, n_keys, scores_all, s);
@@ -225,7 +247,7 @@ size_t csa_index_blocks_workspace_size(int64_t n_seq, int64_t n_q, int64_t e_cap
                                        int32_t block_size, int32_t max_blocks, int32_t top_k) {
   if (n_seq < 0 || n_q < 0 || e_cap < 1 || block_size < 1 || max_blocks < 1) return 0;
   Carver c(nullptr);
-  carve_blocks(c, n_seq * n_q, e_cap, block_size, max_blocks, top_k);
+  carve_blocks(c, n_seq * n_q, e_cap, block_size, max_blocks, top_k, n_q);
   return c.off;
 }
 
@@ -246,7 +268,7 @@ int csa_index_blocks(const void* q_idx, const float* w, const void* k_idx, const
   const size_t need = csa_index_blocks_workspace_size(n_seq, n_q, e_cap, block_size, max_blocks, tk);
   if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
   Carver c(ws);
-  const BlocksWs bw = carve_blocks(c, n_seq * n_q, e_cap, block_size, max_blocks, tk);
+  const BlocksWs bw = carve_blocks(c, n_seq * n_q, e_cap, block_size, max_blocks, tk, n_q);
   return status_of(blocks_rows(dtype, q_idx, w, k_idx, q_pos, e_count, n_seq, n_q, e_cap,
                                idx_heads, idx_dim, m, block_size, max_blocks, out_pool, tk,
                                out_idx, bw, static_cast<hipStream_t>(stream)));
@@ -284,7 +306,7 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, int32_t t
   if (window > 0 && !win) return CSA_ERR_NULL;
   const size_t need = csa_sparse_attn_workspace_size(n_seq, n_q, n_heads, head_dim, top_k, window);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
-  AttnArgs a;
+  AttnArgs a{};
   a.dt = dtype; a.q = q; a.kv = kv; a.idx = idx; a.top_k = top_k; a.win = win; a.w_cap = w_cap;
   a.window = window; a.q_pos = q_pos; a.sink = sink; a.scale = scale; a.out = out;
   a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap; a.H = n_heads; a.D = head_dim; a.ws = ws;
@@ -304,11 +326,11 @@ DecodeWs carve_decode(Carver& c, const csa_decode_desc* d) {
   const int64_t rows = d->n_seq;
   if (d->block_size > 0) {
     const int64_t np = int64_t(d->block_size) * d->max_blocks;
-    w.blocks = carve_blocks(c, rows, d->e_cap, d->block_size, d->max_blocks, 0);
+    w.blocks = carve_blocks(c, rows, d->e_cap, d->block_size, d->max_blocks, 0, 1);
     w.pool = c.take<int32_t>(size_t(rows) * np * 4);
-    w.flat = carve_topk(c, rows, np, d->top_k);
+    w.flat = carve_topk(c, rows, np, d->top_k, 1);
   } else {
-    w.flat = carve_topk(c, rows, d->e_cap, d->top_k);
+    w.flat = carve_topk(c, rows, d->e_cap, d->top_k, 1);
   }
   w.attn = c.take<char>(attn_ws_bytes(rows, d->n_heads, d->dim, d->top_k, d->window, CSA_BF16));
   return w;
@@ -374,7 +396,7 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   mark(0);
 
   // 1-2. new rows into tails / rings; pool the block when it completes
-  IngestArgs in;
+  IngestArgs in{};
   in.dt = d->dtype; in.n_seq = d->n_seq; in.e_cap = d->e_cap; in.m = d->m; in.dim = d->dim;
   in.idx_dim = d->idx_dim; in.w_cap = d->w_cap; in.n_ring = d->n_attn; in.pos = d->pos;
   in.x_new = d->x_new; in.z_new = d->z_new; in.xi_new = d->xi_new; in.zi_new = d->zi_new;
@@ -410,18 +432,21 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
       return CSA_ERR_HIP;
   } else {
     if (scan_rows(d->dtype, d->q_idx, d->w, d->k_idx, d->pos, nullptr, nullptr, 0, rows, 1,
-                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, s, split_ingest) != hipSuccess)
+                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, s, split_ingest,
+                  d->top_k) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
     if (select_rows(w.flat, rows, d->e_cap, nullptr, 0, nullptr, d->top_k, d->out_idx, nullptr,
-                    w.flat.scratch, s, split_ingest) != hipSuccess)
+                    w.flat.scratch, s, split_ingest,
+                    segments_for(w.flat, d->dtype, d->idx_heads, d->idx_dim, 1, false, rows,
+                                 d->e_cap, d->top_k)) != hipSuccess)
       return CSA_ERR_HIP;
   }
 
   mark(3);
   // 5. attention calls sharing the selection, one after another
   for (int c2 = 0; c2 < d->n_attn; ++c2) {
-    AttnArgs a;
+    AttnArgs a{};
     a.dt = d->dtype; a.q = d->q[c2]; a.kv = d->kv; a.idx = d->out_idx; a.top_k = d->top_k;
     a.win = d->win[c2]; a.w_cap = d->w_cap; a.window = d->window; a.q_pos = d->pos;
     a.sink = d->sink[c2]; a.scale = d->scale; a.out = d->out[c2]; a.n_seq = d->n_seq;

@@ -150,6 +150,115 @@ __device__ __forceinline__ void fuse_new_key(const IngestArgs& ig, int64_t r, in
   }
 }
 
+// Candidate segment of one work item (row r, chunk c = positions [c0, c1)), from the scores
+// the item left in LDS. tau = the J-th largest 16-position maximum with its low 12 bits
+// cleared (J from the row's chunk count, well above the mean share K / chunks of the row's
+// Top-K); every position whose key reaches tau is kept, in position order. Called by all
+// threads of the block; ends with a barrier.
+struct SegLds {
+  float sc[kSegMaxChunk];
+  uint32_t gm[kSegMaxChunk / 16];
+  uint32_t red[8];
+};
+__device__ __forceinline__ void emit_segment(const SegArgs& sg, SegLds& L, int64_t r, int64_t c,
+                                             int64_t c0, int64_t c1, int64_t n_pos,
+                                             float* scores_row = nullptr) {
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = int(c1 - c0);
+  const int ng = (n + 15) >> 4;
+  const uint32_t kninf = order_key(neg_inf());
+  // keys of 8 consecutive positions per thread (n <= 2048 = 256 threads x 8); the maximum
+  // of a 16-position group from this thread and its neighbour
+  const int i0 = threadIdx.x * 8;
+  uint32_t k[8];
+  uint32_t km = 0u;
+  if (i0 + 8 <= n) {
+    const float4 a0 = *reinterpret_cast<const float4*>(&L.sc[i0]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&L.sc[i0 + 4]);
+    if (scores_row) {
+      float4* o = reinterpret_cast<float4*>(scores_row + c0 + i0);
+      o[0] = a0;
+      o[1] = a1;
+    }
+    k[0] = order_key(a0.x); k[1] = order_key(a0.y); k[2] = order_key(a0.z); k[3] = order_key(a0.w);
+    k[4] = order_key(a1.x); k[5] = order_key(a1.y); k[6] = order_key(a1.z); k[7] = order_key(a1.w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      k[i] = i0 + i < n ? order_key(L.sc[i0 + i]) : 0u;
+      if (scores_row && i0 + i < n) scores_row[c0 + i0 + i] = L.sc[i0 + i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) km = k[i] > km ? k[i] : km;
+  const uint32_t kn = uint32_t(__shfl_xor(int(km), 1));
+  km = kn > km ? kn : km;
+  if ((threadIdx.x & 1) == 0 && (i0 >> 4) < ng) L.gm[i0 >> 4] = km;
+  __syncthreads();
+  if (wave == 0) {
+    // lambda = K / chunks is the mean count of the row's Top-K per chunk (positions are
+    // exchangeable); J = lambda + 4 sqrt(lambda) + 8 sits far in the Poisson tail
+    const int nch = int((n_pos + sg.chunk - 1) / sg.chunk);
+    const float lam = float(sg.K) / float(nch);
+    int J = int(lam + 4.f * sqrtf(lam)) + 9;
+    const int jmax = ng / 2 < 64 ? ng / 2 : 64;
+    J = J > jmax ? jmax : J;
+    J = J < 1 ? 1 : J;
+    const uint32_t v0 = lane < ng ? L.gm[lane] : 0u;
+    const uint32_t v1 = lane + 64 < ng ? L.gm[lane + 64] : 0u;
+    uint32_t x = 0u;
+#pragma unroll
+    for (int b = 31; b >= 12; --b) {
+      const uint32_t y = x | (1u << b);
+      const int cnt = __popcll(__ballot(v0 >= y)) + __popcll(__ballot(v1 >= y));
+      if (cnt >= J) x = y;
+    }
+    uint32_t mx = v0 > v1 ? v0 : v1;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint32_t u = uint32_t(__shfl_xor(int(mx), o));
+      mx = u > mx ? u : mx;
+    }
+    if (lane == 0) { L.red[0] = x; L.red[1] = mx; }
+  }
+  __syncthreads();
+  const uint32_t tau = L.red[0];
+  uint32_t flags = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i0 + i < n && k[i] >= tau && k[i] > kninf) flags |= 1u << i;
+  const uint32_t cnt = __popc(flags);
+  uint32_t x = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t u = uint32_t(__shfl_up(int(x), o));
+    if (lane >= o) x += u;
+  }
+  if (lane == 63) L.red[2 + wave] = x;
+  __syncthreads();
+  uint32_t off = x - cnt, total = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < 4; ++w2) {
+    const uint32_t t = L.red[2 + w2];
+    if (w2 < wave) off += t;
+    total += t;
+  }
+  const int64_t sidx = r * sg.nseg + c;
+  uint2* dst = sg.seg + sidx * kChunkSegCap;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if ((flags >> i) & 1u) {
+      if (off < uint32_t(kChunkSegCap)) dst[off] = make_uint2(k[i], uint32_t(c0 + i0 + i));
+      ++off;
+    }
+  if (threadIdx.x == 0) {
+    sg.seg_n[sidx] = int32_t(total);
+    sg.seg_info[sidx] = make_uint2(tau, L.red[1]);
+  }
+  __syncthreads();
+}
+
 }  // namespace
 
 // Persistent grid: work item it = (row, chunk) = (it / cpr, it % cpr), chunk positions
@@ -157,9 +266,12 @@ __device__ __forceinline__ void fuse_new_key(const IngestArgs& ig, int64_t r, in
 // rather than to the work (no partially filled last wave of blocks). Within an item, wave w
 // scores 16-key tiles w, w+4, ... and keeps PF further tiles of keys in flight (registers)
 // while the MFMAs of the current tile run.
-template <bool kCand, int PF, bool NT>
+// kSeg: the item's scores also go to LDS and the item ends with its candidate segment
+// (emit_segment) instead of 16-position maxima in global memory.
+template <bool kCand, int PF, bool NT, bool kSeg>
 __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk, int64_t cpr,
                                                           int64_t n_items) {
+  __shared__ SegLds segl;   // used only when kSeg
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
   bf16x8_t A[4][4];
@@ -228,35 +340,217 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
       }
     }
     const int64_t t0 = c0 + wave * 16;
-    if (t0 >= c1) continue;
-    bf16x8_t buf[PF + 1][4];
-    bool ok[PF + 1];
-#pragma unroll
-    for (int u = 0; u <= PF; ++u) {
-      const int64_t tl = t0 + int64_t(u) * 64;
-      load_key_B<NT>(kb + key_row(tl + col, ok[u]) * kID, g, buf[u]);
-    }
-    bool more = true;
-    for (int64_t k = 0; more; k += PF + 1) {
+    if (t0 < c1) {
+      bf16x8_t buf[PF + 1][4];
+      bool ok[PF + 1];
 #pragma unroll
       for (int u = 0; u <= PF; ++u) {
-        const int64_t tl = t0 + (k + u) * 64;
-        if (more && tl < c1) {
-          if (e_new >= tl && e_new < tl + 16)
-            fuse_new_key(a.ingest, r, e_new, slot, lane, g, col == int(e_new - tl), pxn, pzn, pxt,
-                         pzt, pb, buf[u]);
-          const float s = tile_score(A, buf[u], wv);
-          const int64_t p = tl + col;
-          const float sv = (p < c1 && ok[u]) ? s : neg_inf();
-          if (g == 0 && p < c1) out[p] = sv;
-          const float gm = max16(sv);
-          if (lane == 0) gmax[tl >> 4] = gm;
-          const int64_t nx = tl + int64_t(PF + 1) * 64;
-          if (nx < c1) load_key_B<NT>(kb + key_row(nx + col, ok[u]) * kID, g, buf[u]);
-        } else {
-          more = false;
+        const int64_t tl = t0 + int64_t(u) * 64;
+        load_key_B<NT>(kb + key_row(tl + col, ok[u]) * kID, g, buf[u]);
+      }
+      bool more = true;
+      for (int64_t k = 0; more; k += PF + 1) {
+#pragma unroll
+        for (int u = 0; u <= PF; ++u) {
+          const int64_t tl = t0 + (k + u) * 64;
+          if (more && tl < c1) {
+            if (e_new >= tl && e_new < tl + 16)
+              fuse_new_key(a.ingest, r, e_new, slot, lane, g, col == int(e_new - tl), pxn, pzn,
+                           pxt, pzt, pb, buf[u]);
+            const float s = tile_score(A, buf[u], wv);
+            const int64_t p = tl + col;
+            const float sv = (p < c1 && ok[u]) ? s : neg_inf();
+            if (g == 0 && p < c1) {
+              out[p] = sv;
+              if (kSeg) segl.sc[p - c0] = sv;
+            }
+            if (!kSeg) {
+              const float gm = max16(sv);
+              if (lane == 0) gmax[tl >> 4] = gm;
+            }
+            const int64_t nx = tl + int64_t(PF + 1) * 64;
+            if (nx < c1) load_key_B<NT>(kb + key_row(nx + col, ok[u]) * kID, g, buf[u]);
+          } else {
+            more = false;
+          }
         }
       }
+    }
+    if (kSeg) emit_segment(a.seg, segl, r, c, c0, c1, n_pos);
+  }
+}
+
+// ---- decode scan with keys staged through LDS ------------------------------------------------
+// The same contraction as scan_decode_kernel, for the whole visible range of each row (no
+// candidate list), with the key rows moved by global_load_lds_dwordx4: each instruction
+// reads 1 KiB of consecutive memory (4 key rows) straight into LDS, so every request covers
+// whole cache lines, and no VGPRs hold keys in flight. A wave keeps kSD 16-key tiles in
+// flight in a ring of LDS slots. Lane l of instruction i of a tile loads the 16-byte chunk
+// l >> 2 of key 4i + (l & 3) into slot byte 16 l of the instruction's 1 KiB block; blocks are
+// 1,088 bytes apart, which makes the B-operand reads (lane (g, col) of k-step ks reads chunk
+// 4 ks + g of key col) hit 16 distinct 4-bank groups per quarter-wave. The channel order
+// is that of load_key_B, so the query operand is unchanged. A tile is read only after the
+// wave's memory counter shows its loads done (loads complete in issue order; every wait
+// counts only the tile loads issued after it, so any other memory operation in between only
+// makes it wait longer). Scores stay in LDS and leave in one coalesced pass per item, then the
+// item's candidate segment (kSeg) or its 16-position maxima.
+constexpr int kBlk = 1024 + 64;            // LDS bytes per 4-key block
+constexpr int kTileLds = 4 * kBlk;         // LDS bytes per 16-key tile
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <bool NT>
+__device__ __forceinline__ void issue_tile(const uint16_t* kb, int64_t tb, int64_t lim,
+                                           unsigned char* slot, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int64_t key = tb + 4 * i + (lane & 3);
+    key = key < lim ? key : lim - 1;   // rows past the item read its last row (discarded)
+    __builtin_amdgcn_global_load_lds(kb + key * kID + (lane >> 2) * 8,
+                                     (lds_void*)(slot + i * kBlk), 16, 0, NT ? 2 : 0);
+  }
+}
+
+// B operand of the tile in `slot` once at most 4 n tile loads of this wave are outstanding
+// (n = tiles issued after this one, 0 <= n < kSD, wave-uniform). The wait and the four LDS
+// reads are one asm block: the compiler's own wait insertion would otherwise wait for every
+// outstanding load before any read of LDS written by global_load_lds.
+#define CSA_TILE_READ(VM)                                                                   \
+  asm volatile("s_waitcnt vmcnt(" #VM ")\n\t"                                              \
+               "ds_read_b128 %0, %4\n\t"                                                   \
+               "ds_read_b128 %1, %4 offset:256\n\t"                                        \
+               "ds_read_b128 %2, %4 offset:512\n\t"                                        \
+               "ds_read_b128 %3, %4 offset:768\n\t"                                        \
+               "s_waitcnt lgkmcnt(0)"                                                      \
+               : "=v"(B[0]), "=v"(B[1]), "=v"(B[2]), "=v"(B[3])                            \
+               : "v"(addr)                                                                 \
+               : "memory")
+__device__ __forceinline__ void read_tile_B(const unsigned char* slot, int g, int col, int n,
+                                            bf16x8_t (&B)[4]) {
+  const unsigned char* base = slot + (col >> 2) * kBlk + (col & 3) * 16 + g * 64;
+  const uint32_t addr = uint32_t(size_t((const __attribute__((address_space(3))) unsigned char*)base));
+  switch (__builtin_amdgcn_readfirstlane(n)) {
+    case 0: CSA_TILE_READ(0); break;
+    case 1: CSA_TILE_READ(4); break;
+    case 2: CSA_TILE_READ(8); break;
+    default: CSA_TILE_READ(12); break;
+  }
+}
+#undef CSA_TILE_READ
+
+template <bool NT, bool kSeg, int kSD>
+__global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk, int64_t cpr,
+                                                          int64_t n_items, int rot) {
+  __shared__ __attribute__((aligned(16))) unsigned char ring[4][kSD][kTileLds];
+  __shared__ SegLds segl;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  bf16x8_t A[4][4];
+  float wv[4][4];
+  int64_t cur = -1;
+  const bool fuse = a.ingest.pos != nullptr;
+  for (int64_t it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int64_t r = it / cpr, c = it % cpr;
+    const int64_t sq = r / a.n_q;
+    const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
+    const int64_t c0 = c * chunk;
+    const int64_t lim = c0 + chunk < a.e_cap ? c0 + chunk : a.e_cap;
+    // the first tiles go out before the row's visible count is known. Wave w takes the
+    // 16-key tiles w, w + 4, ... of the item in the order that starts at tile `r0` (a per-block
+    // rotation, so that blocks do not walk memory in step)
+    const int64_t t0 = c0 + wave * 16;
+    const int nt_item = int((lim - t0 + 63) / 64);   // tiles of this wave in the item
+    const int r0 = nt_item > 0 ? int((int64_t(blockIdx.x) * rot) % nt_item) : 0;
+    auto tile_base = [&](int t) -> int64_t {
+      int u = t + r0;
+      u = u >= nt_item ? u - nt_item : u;
+      return t0 + int64_t(u) * 64;
+    };
+    int issued = 0;
+#pragma unroll
+    for (int j = 0; j < kSD; ++j) {
+      if (j < nt_item) {
+        issue_tile<NT>(kb, tile_base(j), lim, ring[wave][j], lane);
+        ++issued;
+      }
+    }
+    const int64_t n_pos = row_visible(a, r);
+    if (c == 0 && threadIdx.x == 0) {
+      a.n_vis[r] = int32_t(n_pos);
+      a.count[r] = int32_t(n_pos);
+    }
+    const int64_t c1 = lim < n_pos ? lim : n_pos;
+    if (c0 < c1) {
+      if (r != cur) {
+        load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
+        load_gates(a.w + r * kIH, lane, wv);
+        cur = r;
+      }
+      // the entry this step's token completes is pooled by the wave that scores it
+      int64_t e_new = -1;
+      int slot_new = 0;
+      uint32_t pxn = 0, pzn = 0, pxt[kFuseM], pzt[kFuseM], pb[kFuseM];
+#pragma unroll
+      for (int j = 0; j < kFuseM; ++j) pxt[j] = pzt[j] = pb[j] = 0u;
+      if (fuse) {
+        const int64_t t = a.ingest.pos[r];
+        const int64_t e = (t + 1) / a.ingest.m - 1;
+        if (t >= 0 && (t + 1) % a.ingest.m == 0 && e >= c0 && e < c1 &&
+            int((e - c0) >> 4) % 4 == wave) {
+          e_new = e;
+          slot_new = int(t % a.ingest.m);
+          const IngestArgs& ig = a.ingest;
+          const int m = ig.m;
+          pxn = reinterpret_cast<const uint32_t*>(ig.xi_new)[r * (kID / 2) + lane];
+          pzn = reinterpret_cast<const uint32_t*>(ig.zi_new)[r * (kID / 2) + lane];
+#pragma unroll
+          for (int j = 0; j < kFuseM; ++j) {
+            if (j < m && j != slot_new) {
+              pxt[j] = reinterpret_cast<const uint32_t*>(ig.xi_tail)[(r * m + j) * (kID / 2) + lane];
+              pzt[j] = reinterpret_cast<const uint32_t*>(ig.zi_tail)[(r * m + j) * (kID / 2) + lane];
+            }
+            if (j < m) pb[j] = reinterpret_cast<const uint32_t*>(ig.bias_i)[j * (kID / 2) + lane];
+          }
+        }
+      }
+      // every tile of the item is loaded (in order), so the counts of the waits are exact;
+      // tiles past the visible range are not scored
+      for (int t = 0; t < nt_item; ++t) {
+        const int64_t tb = tile_base(t);
+        unsigned char* slot = ring[wave][t % kSD];
+        bf16x8_t B[4];
+        read_tile_B(slot, g, col, issued - t - 1, B);
+        if (tb < c1) {
+          if (e_new >= tb && e_new < tb + 16)
+            fuse_new_key(a.ingest, r, e_new, slot_new, lane, g, col == int(e_new - tb), pxn, pzn,
+                         pxt, pzt, pb, B);
+          const float sc = tile_score(A, B, wv);
+          const int64_t p = tb + col;
+          if (g == 0 && p < c1) segl.sc[p - c0] = sc;
+        }
+        if (t + kSD < nt_item) {
+          issue_tile<NT>(kb, tile_base(t + kSD), lim, slot, lane);
+          ++issued;
+        }
+      }
+    }
+    // tiles loaded past the visible range (or a row with none) must land before reuse
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (c0 >= c1) continue;   // uniform over the block
+    if (kSeg) {
+      emit_segment(a.seg, segl, r, c, c0, c1, n_pos, a.scores + r * a.score_stride);
+    } else {
+      __syncthreads();
+      float* out = a.scores + r * a.score_stride;
+      const int n = int(c1 - c0);
+      for (int i = threadIdx.x; i < n; i += 256) out[c0 + i] = segl.sc[i];
+      float* gmax = a.gmax + r * a.gmax_stride;
+      for (int gi = threadIdx.x; gi * 16 < n; gi += 256) {
+        float mx = neg_inf();
+        for (int i = gi * 16; i < gi * 16 + 16 && i < n; ++i) mx = fmaxf(mx, segl.sc[i]);
+        gmax[(c0 >> 4) + gi] = mx;
+      }
+      __syncthreads();
     }
   }
 }
@@ -407,7 +701,7 @@ static bool fast_shape(const ScanArgs& a) { return a.dt == kBF16 && a.H == kIH &
 // Decode-scan launch shape: positions per work item, key tiles in flight per wave beyond the
 // current one, and blocks resident per CU (the persistent grid is n_cu * blocks_per_cu).
 struct ScanTune {
-  int chunk = 2048, pf = 1, blocks_per_cu = 2, nt = 1;
+  int chunk = 2048, pf = 1, blocks_per_cu = 2, nt = 1, sd = 2, rot = 0;
 };
 static int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
@@ -420,6 +714,8 @@ static const ScanTune& scan_tune() {
     x.pf = env_int("CSA_TUNE_SCAN_PF", x.pf);
     x.blocks_per_cu = env_int("CSA_TUNE_SCAN_BPC", x.blocks_per_cu);
     x.nt = env_int("CSA_TUNE_SCAN_NT", x.nt);
+    x.sd = env_int("CSA_TUNE_SCAN_SD", x.sd);
+    x.rot = env_int("CSA_TUNE_SCAN_ROT", x.rot);
     return x;
   }();
   return t;
@@ -435,33 +731,65 @@ static int n_cu() {
   return n;
 }
 
-template <bool kCand, int PF, bool NT>
-static void launch_decode(const ScanArgs& a, int64_t rows, int64_t max_pos, hipStream_t s) {
+static int64_t scan_grid() {
+  const int bpc = scan_tune().blocks_per_cu > 0 ? scan_tune().blocks_per_cu : 2;
+  return int64_t(n_cu()) * bpc;
+}
+
+// chunk: the tuned size (at most kSegMaxChunk with segments), shrunk (to >= 256 positions)
+// until there is at least one work item per resident block
+int decode_scan_chunk(int64_t rows, int64_t max_pos, bool segments) {
   const ScanTune& t = scan_tune();
-  const int bpc = t.blocks_per_cu > 0 ? t.blocks_per_cu : 2;
-  int64_t grid = int64_t(n_cu()) * bpc;
-  // chunk: the tuned size, shrunk (to >= 256 positions) until there is at least one work
-  // item per resident block
   int chunk = t.chunk > 0 ? (t.chunk + 63) / 64 * 64 : 2048;
+  if (segments && chunk > kSegMaxChunk) chunk = kSegMaxChunk;
+  const int64_t grid = scan_grid();
   while (chunk > 256 && rows * ((max_pos + chunk - 1) / chunk) < grid) chunk /= 2;
-  chunk = (chunk + 63) / 64 * 64;
+  return (chunk + 63) / 64 * 64;
+}
+
+static size_t r256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t seg_bytes(int64_t rows, int64_t max_pos) {
+  const int chunk = decode_scan_chunk(rows, max_pos, true);
+  const int64_t nseg = max_pos > 0 ? (max_pos + chunk - 1) / chunk : 1;
+  const size_t ns = size_t(rows) * size_t(nseg);
+  return r256(ns * kChunkSegCap * 8) + r256(ns * 4) + r256(ns * 8);
+}
+
+SegArgs seg_carve(void* base, int64_t rows, int64_t max_pos, int K) {
+  SegArgs g;
+  g.chunk = decode_scan_chunk(rows, max_pos, true);
+  g.nseg = max_pos > 0 ? (max_pos + g.chunk - 1) / g.chunk : 1;
+  g.K = K;
+  const size_t ns = size_t(rows) * size_t(g.nseg);
+  char* p = static_cast<char*>(base);
+  g.seg = reinterpret_cast<uint2*>(p);
+  g.seg_n = reinterpret_cast<int32_t*>(p + r256(ns * kChunkSegCap * 8));
+  g.seg_info = reinterpret_cast<uint2*>(p + r256(ns * kChunkSegCap * 8) + r256(ns * 4));
+  return g;
+}
+
+template <bool kCand, int PF, bool NT, bool kSeg>
+static void launch_decode(const ScanArgs& a, int64_t rows, int64_t max_pos, hipStream_t s) {
+  int64_t grid = scan_grid();
+  const int chunk = kSeg ? a.seg.chunk : decode_scan_chunk(rows, max_pos, false);
   const int64_t cpr = max_pos > 0 ? (max_pos + chunk - 1) / chunk : 1;
   const int64_t items = rows * cpr;
   if (grid > items) grid = items;
-  hipLaunchKernelGGL((scan_decode_kernel<kCand, PF, NT>), dim3(static_cast<unsigned>(grid)),
+  hipLaunchKernelGGL((scan_decode_kernel<kCand, PF, NT, kSeg>), dim3(static_cast<unsigned>(grid)),
                      dim3(256), 0, s, a, chunk, cpr, items);
 }
 
-template <bool kCand>
+template <bool kCand, bool kSeg>
 static void launch_decode_pf(const ScanArgs& a, int64_t rows, int64_t max_pos, hipStream_t s) {
   const bool nt = scan_tune().nt != 0;
   switch (scan_tune().pf) {
-    case 1: nt ? launch_decode<kCand, 1, true>(a, rows, max_pos, s)
-               : launch_decode<kCand, 1, false>(a, rows, max_pos, s); break;
-    case 3: nt ? launch_decode<kCand, 3, true>(a, rows, max_pos, s)
-               : launch_decode<kCand, 3, false>(a, rows, max_pos, s); break;
-    default: nt ? launch_decode<kCand, 2, true>(a, rows, max_pos, s)
-                : launch_decode<kCand, 2, false>(a, rows, max_pos, s); break;
+    case 1: nt ? launch_decode<kCand, 1, true, kSeg>(a, rows, max_pos, s)
+               : launch_decode<kCand, 1, false, kSeg>(a, rows, max_pos, s); break;
+    case 3: nt ? launch_decode<kCand, 3, true, kSeg>(a, rows, max_pos, s)
+               : launch_decode<kCand, 3, false, kSeg>(a, rows, max_pos, s); break;
+    default: nt ? launch_decode<kCand, 2, true, kSeg>(a, rows, max_pos, s)
+                : launch_decode<kCand, 2, false, kSeg>(a, rows, max_pos, s); break;
   }
 }
 
@@ -482,8 +810,32 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (fast_shape(a)) {
-    if (a.cand) launch_decode_pf<true>(a, rows, max_pos, s);
-    else launch_decode_pf<false>(a, rows, max_pos, s);
+    if (a.cand) {
+      launch_decode_pf<true, false>(a, rows, max_pos, s);
+    } else {
+      const bool segs = a.seg.seg != nullptr;
+      const int chunk = segs ? a.seg.chunk : decode_scan_chunk(rows, max_pos, true);
+      if (chunk > kSegMaxChunk) return hipErrorInvalidValue;
+      const int64_t cpr = (max_pos + chunk - 1) / chunk;
+      const int64_t items = rows * cpr;
+      int64_t grid = scan_grid();
+      if (grid > items) grid = items;
+      const dim3 gd(static_cast<unsigned>(grid)), bd(256);
+      const int rot = scan_tune().rot;
+      const int sd = scan_tune().sd;
+#define CSA_STREAM(SEG, SD)                                                                  \
+  hipLaunchKernelGGL((scan_stream_kernel<true, SEG, SD>), gd, bd, 0, s, a, chunk, cpr, items, rot)
+      if (segs) {
+        if (sd == 2) CSA_STREAM(true, 2);
+        else if (sd == 3) CSA_STREAM(true, 3);
+        else CSA_STREAM(true, 4);
+      } else {
+        if (sd == 2) CSA_STREAM(false, 2);
+        else if (sd == 3) CSA_STREAM(false, 3);
+        else CSA_STREAM(false, 4);
+      }
+#undef CSA_STREAM
+    }
     return hipGetLastError();
   }
   const unsigned gx = unsigned(max_pos > 0 ? (max_pos + 255) / 256 : 1);

@@ -28,6 +28,31 @@ struct IngestArgs {
 };
 hipError_t launch_ingest(const IngestArgs& a, hipStream_t s);
 
+// ---- candidate segments of long decode rows -----------------------------------------------
+// The decode scan cuts each row into chunks of positions (its work items). For rows longer
+// than kSegRowMin it can also leave, per chunk c, the positions whose score key reaches a
+// threshold tau_c of its own (the J-th largest of the chunk's 16-position maxima), in
+// position order: seg[c][0 .. min(n_c, kChunkSegCap)), n_c in seg_n[c], (tau_c, the chunk's
+// largest key) in seg_info[c]. The select then works on the segments alone and checks that
+// every tau_c lies at or below the K-th key it finds (see topk.hip).
+constexpr int64_t kSegRowMin = 32768;
+constexpr int kChunkSegCap = 128;
+constexpr int kSegMaxChunk = 2048;
+struct SegArgs {
+  uint2* seg;             // [rows][nseg][kChunkSegCap] (key, position); null: no segments
+  int32_t* seg_n;         // [rows][nseg]
+  uint2* seg_info;        // [rows][nseg]
+  int64_t nseg;           // chunks per row (row stride of the arrays)
+  int chunk;              // positions per chunk
+  int K;
+};
+// Positions per decode-scan work item for `rows` rows of up to `max_pos` positions (segment
+// chunks when segments are written), and the buffer sizes of the segments.
+int decode_scan_chunk(int64_t rows, int64_t max_pos, bool segments);
+size_t seg_bytes(int64_t rows, int64_t max_pos);
+// carves the three arrays out of `base` (seg_bytes long); sets nseg and chunk
+SegArgs seg_carve(void* base, int64_t rows, int64_t max_pos, int K);
+
 // ---- indexer scan ------------------------------------------------------------------------
 // Scores of query rows r = (seq, query) against their candidates, written to
 // scores[r * score_stride + j] for candidate position j; fp32. Also writes
@@ -53,6 +78,7 @@ struct ScanArgs {
   // (ingest.pos non-null): the scan pools the indexer key of the entry the token completes;
   // the select's ingest workgroups do the rest. Only when scan_fuses_ingest() holds.
   IngestArgs ingest;
+  SegArgs seg;            // decode scan without candidates: candidate segments (optional)
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
 // Whether the decode scan for this shape takes the indexer-key part of the ingest.
@@ -82,6 +108,7 @@ struct TopkArgs {
   // optional: the rest of a decode step's ingest (tails, rings, main entry), run by extra
   // workgroups of the select's last launch (indexer keys are the scan's part)
   const IngestArgs* side;
+  SegArgs seg;            // segments left by the scan (seg.seg non-null: the select uses them)
 };
 size_t topk_scratch_bytes(int64_t rows, int64_t max_count, int K);
 

@@ -83,6 +83,7 @@ struct SelArgs {
   int64_t rows;
   int64_t n_side;         // ingest workgroups after the rows' (0: none)
   IngestArgs side;
+  SegArgs cseg;           // candidate segments of the decode scan (cseg.seg null: none)
 };
 
 // A decode step's ingest (without the indexer keys) for sequence sq, by one workgroup.
@@ -102,7 +103,7 @@ struct SelShared {
   uint32_t h0g[kBins0 / kGroup];
   uint32_t hb[kBinsB];              // digit of the bound; later digits of the select
   uint32_t hbg[kBinsB / kGroup];
-  uint32_t segoff[kMaxSegLds];
+  uint32_t segoff[kMaxSegLds + 4];
   uint32_t wred[kSelWaves];
   uint32_t res[4];                  // search result: bin, items above it, items in it
   uint32_t red[4];                  // block reductions: min, max, count
@@ -285,7 +286,7 @@ __device__ __forceinline__ void red_init(SelShared& sh) {
 // ---- the bound ---------------------------------------------------------------------------
 // T and the row's largest key (all-ones when unknown). Needs sh.hb/hbg clear and sh.red
 // initialised (and a barrier since); ends with a barrier.
-__device__ uint2 row_bound(const SelArgs& a, SelShared& sh, int64_t r, int64_t n) {
+__device__ __forceinline__ uint2 row_bound(const SelArgs& a, SelShared& sh, int64_t r, int64_t n) {
   const int tid = threadIdx.x;
   const int64_t K = a.K;
   if (n <= K) return make_uint2(0u, 0xffffffffu);
@@ -372,8 +373,17 @@ __device__ uint2 row_bound(const SelArgs& a, SelShared& sh, int64_t r, int64_t n
 // ---- the select --------------------------------------------------------------------------
 // Candidates in LDS (position order), more than K of them, first digit (14 bits at lo0 over
 // key - kmin) already histogrammed in sh.h0: thread t owns list items [t*L, t*L + L).
-__device__ void select_list(const SelArgs& a, SelShared& sh, int64_t r, uint32_t total,
-                            uint32_t kmin, int lo0, int nb0) {
+// `unsafe(T)` (per thread; any thread true rejects) is asked, once the radix has fixed the
+// K-th key's prefix, whether the list may miss positions whose key reaches T = kmin + (that
+// prefix << its shift), a lower bound of the K-th key. Then nothing is written and the call
+// returns false with T in *t_lb.
+struct NeverUnsafe {
+  __device__ bool operator()(uint32_t) const { return false; }
+};
+template <typename Unsafe = NeverUnsafe>
+__device__ __forceinline__ bool select_list(const SelArgs& a, SelShared& sh, int64_t r, uint32_t total,
+                            uint32_t kmin, int lo0, int nb0, Unsafe unsafe = Unsafe(),
+                            uint32_t* t_lb = nullptr) {
   const int tid = threadIdx.x;
   const uint32_t K = a.K;
   const uint32_t L = (total + kSelThreads - 1) / kSelThreads;   // <= kListRun
@@ -390,6 +400,17 @@ __device__ void select_list(const SelArgs& a, SelShared& sh, int64_t r, uint32_t
     for (int i = 0; i < kListRun; ++i)
       if (uint32_t(i) < jn) fn(k[i]);
   }, kmin, st);
+  if (t_lb) {
+    const uint32_t T = kmin + (st.lo >= 32 ? 0u : (st.P << st.lo));
+    if (tid == 0) sh.flag = 0u;
+    __syncthreads();
+    if (unsafe(T)) atomicOr(&sh.flag, 1u);
+    __syncthreads();
+    if (sh.flag) {
+      *t_lb = T;
+      return false;
+    }
+  }
   uint32_t sel = 0, eq = 0;
 #pragma unroll
   for (int i = 0; i < kListRun; ++i) {
@@ -420,10 +441,11 @@ __device__ void select_list(const SelArgs& a, SelShared& sh, int64_t r, uint32_t
       ++o;
     }
   pad_out(a, r, nsel);
+  return true;
 }
 
 // the first `total` (<= K) list items, in order
-__device__ void select_all(const SelArgs& a, SelShared& sh, int64_t r, uint32_t total) {
+__device__ __forceinline__ void select_all(const SelArgs& a, SelShared& sh, int64_t r, uint32_t total) {
   for (uint32_t j = threadIdx.x; j < total; j += kSelThreads)
     write_out(a, r, j, sh.list.lp[j], sh.list.lk[j]);
   pad_out(a, r, total);
@@ -431,7 +453,7 @@ __device__ void select_all(const SelArgs& a, SelShared& sh, int64_t r, uint32_t 
 
 // Streaming select over the row's scores (valid positions whose key reaches T): for rows
 // whose candidates do not fit the LDS list. Uses every histogram; needs nothing set up.
-__device__ void select_stream(const SelArgs& a, SelShared& sh, int64_t r, int64_t n,
+__device__ __forceinline__ void select_stream(const SelArgs& a, SelShared& sh, int64_t r, int64_t n,
                               uint32_t T) {
   const int tid = threadIdx.x;
   const int64_t lim = row_limit(a, r);
@@ -579,15 +601,8 @@ __device__ __forceinline__ uint32_t slice_flags(const SelArgs& a, int64_t r, int
 // One workgroup per row (rows of up to kRowMax positions): bound, candidates into the LDS
 // list tile by tile (first digit histogrammed on the way; the next tile's scores load while
 // this one is compacted), select.
-__global__ __launch_bounds__(kSelThreads) void select_row_kernel(SelArgs a) {
-  __shared__ SelShared sh;
-  if (int64_t(blockIdx.x) >= a.rows) {
-    side_ingest(a, int64_t(blockIdx.x) - a.rows);
-    return;
-  }
-  const int64_t r = blockIdx.x;
+__device__ __forceinline__ void select_row_body(const SelArgs& a, SelShared& sh, int64_t r, int64_t n) {
   const int tid = threadIdx.x;
-  const int64_t n = row_count(a, r);
   const float* sr = a.scores + r * a.stride;
   float x[kSliceItems];
   load_slice(sr, int64_t(tid) * kSliceItems, n, x);
@@ -628,6 +643,272 @@ __global__ __launch_bounds__(kSelThreads) void select_row_kernel(SelArgs a) {
   if (over) select_stream(a, sh, r, n, T);
   else if (total <= a.K) select_all(a, sh, r, total);
   else select_list(a, sh, r, total, T, d0.lo, d0.nbins);
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_row_kernel(SelArgs a) {
+  __shared__ SelShared sh;
+  if (int64_t(blockIdx.x) >= a.rows) {
+    side_ingest(a, int64_t(blockIdx.x) - a.rows);
+    return;
+  }
+  select_row_body(a, sh, blockIdx.x, row_count(a, blockIdx.x));
+}
+
+// Rows whose decode scan left candidate segments (SegArgs): one workgroup per row. Chunk c
+// holds every position of the chunk whose key reaches its tau_c, so the segments
+// concatenated in chunk order form a list in position order; thread t holds the run
+// [t*L, t*L + L) of it in registers. An MSB-first radix select with 11-bit digits over a
+// 2,048-bin LDS histogram finds the K-th key of the list; the chosen positions leave in
+// list order (ascending), equal keys at the boundary lowest position first.
+// The result is the row's exact Top-K when every tau_c is at or below the K-th key of the
+// list: a position missing from the list then lies below that key, hence outside the row's
+// Top-K as well. The check uses the lower bound kmin + (prefix << shift) of the K-th key that
+// the radix has fixed. A chunk that fails it sends the row to the streaming select with that
+// bound; an overflowing segment or a list longer than the registers hold, with bound 0.
+// Short rows of the batch (<= kRowMax) take the single-row select.
+constexpr int kSegDigit = 11;
+constexpr int kSegBins = 1 << kSegDigit;
+constexpr int kSegRun = 16;                          // list items per thread
+constexpr int kSegList = kSelThreads * kSegRun;      // 8,192
+constexpr int kSegHead = 32;                         // entries fetched with the counts
+constexpr int kSegHeadIters = 8;                     // rounds of 32 chunks fetched that way
+constexpr int kSegHeadChunks = kSegHeadIters * (kSelThreads / 16);
+
+// bin (of nbins, counted from the top by thread order: thread t owns the 4 bins
+// [nbins - 4t - 4, nbins - 4t)) that holds the need-th largest item; writes (bin, items above
+// it, items in it) to sh.res. All threads; ends with a barrier.
+__device__ __forceinline__ void seg_find(SelShared& sh, const uint32_t* h, int nbins,
+                                         uint32_t need) {
+  const int tid = threadIdx.x;
+  const int b0 = nbins - 4 * tid - 1;                // this thread's highest bin
+  uint32_t c[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = b0 - i >= 0 ? h[b0 - i] : 0u;
+    sum += c[i];
+  }
+  uint32_t tot;
+  uint32_t acc = excl_scan(sum, sh.wred, &tot);
+  if (acc < need && need <= acc + sum) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (acc < need && need <= acc + c[i]) {
+        sh.res[0] = uint32_t(b0 - i); sh.res[1] = acc; sh.res[2] = c[i];
+      }
+      acc += c[i];
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
+  __shared__ SelShared sh;
+  if (int64_t(blockIdx.x) >= a.rows) {
+    side_ingest(a, int64_t(blockIdx.x) - a.rows);
+    return;
+  }
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t n = row_count(a, r);
+  if (n <= kRowMax) {
+    select_row_body(a, sh, r, n);
+    return;
+  }
+  const SegArgs& sg = a.cseg;
+  const int64_t nch = (n + sg.chunk - 1) / sg.chunk;
+  if (nch > kMaxSegLds) {
+    select_stream(a, sh, r, n, 0u);
+    return;
+  }
+  const uint32_t K = a.K;
+  const uint32_t kninf = order_key(neg_inf());
+  // 1. one round of independent loads: the counts and thresholds of the chunks (2 per
+  //    thread) and the first kSegHead entries of the first kSegHeadChunks chunks (16 lanes per
+  //    chunk, 2 entries per lane)
+  const int lane16 = tid & 15;
+  uint4 hv[kSegHeadIters];
+#pragma unroll
+  for (int it = 0; it < kSegHeadIters; ++it) {
+    const int64_t ch = int64_t(it) * (kSelThreads / 16) + (tid >> 4);
+    hv[it] = make_uint4(0u, 0u, 0u, 0u);
+    if (ch < nch)
+      hv[it] = *reinterpret_cast<const uint4*>(sg.seg + (r * sg.nseg + ch) * kChunkSegCap +
+                                               2 * lane16);
+  }
+  uint32_t c[kSegPerThread], tau[kSegPerThread], loc = 0;
+  uint32_t tmin = 0xffffffffu, tmax = 0u;
+  bool over = false;
+#pragma unroll
+  for (int q = 0; q < kSegPerThread; ++q) {
+    const int64_t j = int64_t(tid) * kSegPerThread + q;
+    c[q] = 0u;
+    tau[q] = 0u;
+    if (j < nch) {
+      const uint32_t cn = uint32_t(sg.seg_n[r * sg.nseg + j]);
+      const uint2 info = sg.seg_info[r * sg.nseg + j];
+      over |= cn > uint32_t(kChunkSegCap);
+      c[q] = cn < uint32_t(kChunkSegCap) ? cn : uint32_t(kChunkSegCap);
+      tau[q] = info.x;
+      tmin = info.x < tmin ? info.x : tmin;
+      tmax = info.y > tmax ? info.y : tmax;
+      loc += c[q];
+    }
+  }
+  for (int b = tid; b < kSegBins; b += kSelThreads) sh.hb[b] = 0u;
+  red_init(sh);
+  if (tid == 0) sh.flag = 0u;
+  __syncthreads();
+  bool rest = false;   // a chunk with entries past the fetched heads
+#pragma unroll
+  for (int q = 0; q < kSegPerThread; ++q) {
+    const int64_t j = int64_t(tid) * kSegPerThread + q;
+    if (j < nch && (c[q] > uint32_t(kSegHead) || j >= kSegHeadChunks)) rest = true;
+  }
+  if (over) atomicOr(&sh.flag, 1u);
+  if (rest) atomicOr(&sh.flag, 2u);
+  red_add(sh, tmin, tmax, 0u);
+  uint32_t total;
+  uint32_t off = excl_scan(loc, sh.wred, &total);
+#pragma unroll
+  for (int q = 0; q < kSegPerThread; ++q) {
+    const int64_t j = int64_t(tid) * kSegPerThread + q;
+    if (j < nch) sh.segoff[j] = off;
+    off += c[q];
+  }
+  if (tid == 0) sh.segoff[nch] = total;
+  __syncthreads();
+  // list keys are finite (above kninf) and reach their chunk's tau
+  const uint32_t kmin = sh.red[0] > kninf ? sh.red[0] : kninf + 1u;
+  const uint32_t kmax = sh.red[1] > kmin ? sh.red[1] : kmin;
+  const uint32_t flag = sh.flag;
+  if ((flag & 1u) != 0u || total > uint32_t(kSegList)) {
+    select_stream(a, sh, r, n, 0u);
+    return;
+  }
+  // 2. the list in LDS, in position order: the fetched heads, then (rarely) the rest
+#pragma unroll
+  for (int it = 0; it < kSegHeadIters; ++it) {
+    const int64_t ch = int64_t(it) * (kSelThreads / 16) + (tid >> 4);
+    if (ch < nch) {
+      const uint32_t o0 = sh.segoff[ch], cn = sh.segoff[ch + 1] - o0;
+      const uint32_t e = 2u * uint32_t(lane16);
+      if (e < cn) { sh.list.lk[o0 + e] = hv[it].x; sh.list.lp[o0 + e] = hv[it].y; }
+      if (e + 1 < cn) { sh.list.lk[o0 + e + 1] = hv[it].z; sh.list.lp[o0 + e + 1] = hv[it].w; }
+    }
+  }
+  if (flag & 2u) {
+    // entries past the heads: one wave per chunk
+    const int wv = tid >> 6, ln = tid & 63;
+    for (int64_t ch = wv; ch < nch; ch += kSelWaves) {
+      const uint32_t o0 = sh.segoff[ch], cn = sh.segoff[ch + 1] - o0;
+      const uint32_t e0 = ch < kSegHeadChunks ? uint32_t(kSegHead) : 0u;
+      for (uint32_t e = e0 + ln; e < cn; e += 64) {
+        const uint2 v = sg.seg[(r * sg.nseg + ch) * kChunkSegCap + e];
+        sh.list.lk[o0 + e] = v.x;
+        sh.list.lp[o0 + e] = v.y;
+      }
+    }
+  }
+  __syncthreads();
+  // this thread's run of the list into registers; first-digit histogram
+  const uint32_t L = (total + kSelThreads - 1) / kSelThreads;
+  const uint32_t j0 = uint32_t(tid) * L;
+  const uint32_t jn = j0 < total ? (total - j0 < L ? total - j0 : L) : 0u;
+  const int bits = key_bits(kmax - kmin);
+  int lo = bits > kSegDigit ? bits - kSegDigit : 0;
+  uint32_t k[kSegRun], pos[kSegRun];
+#pragma unroll
+  for (int i = 0; i < kSegRun; ++i) {
+    k[i] = 0u;
+    pos[i] = 0u;
+    if (uint32_t(i) < jn) {
+      k[i] = sh.list.lk[j0 + i];
+      pos[i] = sh.list.lp[j0 + i];
+      atomicAdd(&sh.hb[(k[i] - kmin) >> lo], 1u);
+    }
+  }
+  __syncthreads();
+  if (total <= K) {
+    // the list is the row's Top-K only if every chunk kept all its valid positions
+#pragma unroll
+    for (int q = 0; q < kSegPerThread; ++q)
+      if (int64_t(tid) * kSegPerThread + q < nch && tau[q] > kninf + 1u) atomicOr(&sh.flag, 1u);
+    __syncthreads();
+    if (sh.flag != 0u) {
+      select_stream(a, sh, r, n, 0u);
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < kSegRun; ++i)
+      if (uint32_t(i) < jn) write_out(a, r, j0 + i, pos[i], k[i]);
+    pad_out(a, r, total);
+    return;
+  }
+  // 3. radix select: P = prefix of the K-th key at shift lo, need = items of it to take
+  seg_find(sh, sh.hb, 1 << (bits - lo), K);
+  uint32_t P = sh.res[0], need = K - sh.res[1];
+  bool done = sh.res[2] == need;
+#pragma unroll 1
+  while (!done && lo > 0) {
+    const int w = lo < kSegDigit ? lo : kSegDigit;
+    const int l2 = lo - w;
+    __syncthreads();
+    for (int b = tid; b < (1 << w); b += kSelThreads) sh.hb[b] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSegRun; ++i) {
+      const uint32_t v = k[i] - kmin;
+      if (uint32_t(i) < jn && (v >> lo) == P) atomicAdd(&sh.hb[(v >> l2) & ((1u << w) - 1u)], 1u);
+    }
+    __syncthreads();
+    seg_find(sh, sh.hb, 1 << w, need);
+    P = (P << w) | sh.res[0];
+    need -= sh.res[1];
+    done = sh.res[2] == need;
+    lo = l2;
+  }
+  // 4. exactness: every chunk's tau at or below the K-th key's lower bound
+  const uint32_t T = kmin + (P << lo);
+  if (tid == 0) sh.flag = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kSegPerThread; ++q)
+    if (int64_t(tid) * kSegPerThread + q < nch && tau[q] > T) atomicOr(&sh.flag, 1u);
+  __syncthreads();
+  if (sh.flag != 0u) {
+    select_stream(a, sh, r, n, T);
+    return;
+  }
+  // 5. chosen items in list order
+  uint32_t sel = 0, eq = 0;
+#pragma unroll
+  for (int i = 0; i < kSegRun; ++i)
+    if (uint32_t(i) < jn) {
+      const uint32_t v = (k[i] - kmin) >> lo;
+      if (v > P) sel |= 1u << i;
+      else if (v == P) eq |= 1u << i;
+    }
+  if (done) {
+    sel |= eq;
+  } else {
+    uint32_t tot;
+    uint32_t before = excl_scan(__popc(eq), sh.wred, &tot);
+#pragma unroll
+    for (int i = 0; i < kSegRun; ++i)
+      if ((eq >> i) & 1u) {
+        if (before < need) sel |= 1u << i;
+        ++before;
+      }
+  }
+  uint32_t nsel;
+  uint32_t o = excl_scan(__popc(sel), sh.wred, &nsel);
+#pragma unroll
+  for (int i = 0; i < kSegRun; ++i)
+    if ((sel >> i) & 1u) {
+      write_out(a, r, o, pos[i], k[i]);
+      ++o;
+    }
+  pad_out(a, r, nsel);
 }
 
 // Long rows, step 1: one workgroup per slice computes the row's bound and keeps its slice's
@@ -799,7 +1080,7 @@ hipError_t launch_topk(const TopkArgs& t, hipStream_t s) {
   const int64_t mc = t.max_count > 0 ? t.max_count : 0;
   const SelPlan p = sel_plan(t.rows, mc);
   char* base = reinterpret_cast<char*>(t.scratch);
-  SelArgs a;
+  SelArgs a{};
   a.scores = t.scores; a.stride = t.stride; a.gmax = t.gmax; a.gstride = t.gstride;
   a.ids = t.ids; a.id_stride = t.id_stride; a.id_limit = t.id_limit; a.count = t.count;
   a.max_count = mc; a.K = uint32_t(t.K); a.out_idx = t.out_idx; a.out_score = t.out_score;
@@ -811,8 +1092,15 @@ hipError_t launch_topk(const TopkArgs& t, hipStream_t s) {
   a.rows = t.rows;
   a.n_side = t.side ? t.side->n_seq : 0;
   a.side = t.side ? *t.side : IngestArgs{};
+  a.cseg = t.seg;
+  // with segments the scan leaves no 16-position maxima: short rows bound from the scores
+  if (t.seg.seg != nullptr) a.gmax = nullptr;
   const unsigned rows = static_cast<unsigned>(t.rows);
   const unsigned last = static_cast<unsigned>(t.rows + a.n_side);   // + ingest workgroups
+  if (t.seg.seg != nullptr) {
+    hipLaunchKernelGGL(select_chunks_kernel, dim3(last), dim3(kSelThreads), 0, s, a);
+    return hipGetLastError();
+  }
   if (!p.split) {
     hipLaunchKernelGGL(select_row_kernel, dim3(last), dim3(kSelThreads), 0, s, a);
     return hipGetLastError();

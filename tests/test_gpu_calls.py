@@ -121,6 +121,40 @@ def test_index_long_rows_segmented_select():
     check_index(q, w, k, pos, 4, 512)
 
 
+def test_index_segments_ragged_rows():
+    # long decode rows leave candidate segments from the scan; a short row of the same batch
+    # (<= 32,768 visible) takes the single-row select inside the same launch
+    E = 100000
+    q, w, k, pos = index_case(3, 1, E, 64, 128, "bf16", 0, 1, seed=12)
+    pos[0, 0] = 4 * 20000 - 1
+    pos[1, 0] = 4 * 50000 + 2
+    pos[2, 0] = 4 * E - 1
+    check_index(q, w, k, pos, 4, 512)
+
+
+def test_index_segments_clustered_winners():
+    # keys of one stretch doubled (ReLU is positively homogeneous: exactly doubled scores), so
+    # most of the Top-512 sit in a few chunks whose own thresholds lie above the K-th key:
+    # the select must notice and fall back to streaming the row above its bound
+    E = 90000
+    q, w, k, pos = index_case(2, 1, E, 64, 128, "bf16", 4 * E - 1, 4 * E, seed=13)
+    k[0, 30000:31500] = (k[0, 30000:31500].float() * 2).to(k.dtype)
+    k[1, 100:400] = (k[1, 100:400].float() * 2).to(k.dtype)
+    check_index(q, w, k, pos, 4, 512)
+
+
+def test_index_blocks_own_topk_segments():
+    # stage 1 of the hierarchical indexer with the row's own Top-K over long rows
+    B, E, bs, mb, K = 2, 50000, 8, 64, 512
+    q, w, k, pos = index_case(B, 1, E, 64, 128, "bf16", E - 5, E, m=1, seed=14)
+    fix_gaps(CID, q, w, k, pos, None, 1, K)
+    pool, idx = csa.index_blocks(dev(q), dev(w), dev(k), dev(pos), 1, bs, mb, top_k=K)
+    idx = idx.cpu()
+    ref = pipeline.index_topk(q, w, k, pos, None, 1, K)
+    for (b, i), (ids, _, _) in ref.items():
+        assert_ids(idx[b, i].numpy(), ids, f"row {(b, i)}")
+
+
 @pytest.mark.parametrize("n_dup,contiguous", [(600, False), (600, True), (9000, False)])
 def test_index_exact_ties(n_dup, contiguous):
     """Exact score ties across the K-th place: n_dup copies of the best key row (scaled by 2,
