@@ -436,10 +436,10 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
                   d->top_k) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
+    const SegArgs seg = segments_for(w.flat, d->dtype, d->idx_heads, d->idx_dim, 1, false, rows,
+                                     d->e_cap, d->top_k);
     if (select_rows(w.flat, rows, d->e_cap, nullptr, 0, nullptr, d->top_k, d->out_idx, nullptr,
-                    w.flat.scratch, s, split_ingest,
-                    segments_for(w.flat, d->dtype, d->idx_heads, d->idx_dim, 1, false, rows,
-                                 d->e_cap, d->top_k)) != hipSuccess)
+                    w.flat.scratch, s, split_ingest, seg) != hipSuccess)
       return CSA_ERR_HIP;
   }
 

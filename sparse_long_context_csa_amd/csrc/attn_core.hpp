@@ -1,0 +1,221 @@
+// MFMA core of the sparse attention (bf16, 64 heads x 512): one workgroup of 4 waves (16
+// heads each) over one split of a query row's list of cached rows.
+//
+// "DeepSeek V4-Flash: The Cost of Deciding What to Read": sections "Key and value are the
+// same vector", "Attention sink, and heads that abstain" and "The sliding window is not an
+// optimisation" (the selected entries and the window rows form one softmax with the sink).
+//
+// The split's rows are walked in tiles of 32; each tile is gathered once into LDS twice:
+// row-major (A operand of S^T = KV.Q^T, v_mfma_f32_16x16x32_bf16, M = 32 rows, N = 16 heads,
+// K = 512) and transposed (B operand of O = P.V, K = 32 rows). The score accumulator layout
+// puts, in every lane, 8 rows of one head; those 8 rows are exactly the lane's K slots of the
+// P.V product, so P passes from the score registers to the A operand with no data movement.
+// Online softmax in base 2. With one split the output is normalised (with the sink) and
+// stored; with several, the split's (max, sum, unnormalised output) go to the workspace for
+// attn_combine_kernel. row_src(j, nrows) gives the address of list row j (null: no row),
+// which may point to global memory or LDS.
+#pragma once
+
+#include "csa_common.hpp"
+#include "launch.hpp"
+
+namespace csa {
+
+constexpr int kAH = 64;          // heads on the MFMA path
+constexpr int kAD = 512;         // head dim on the MFMA path
+constexpr int kTile = 32;        // rows per tile
+constexpr int kKvRow = 1040;     // LDS bytes per row of the row-major tile (1024 + 16)
+constexpr int kVtRow = 80;       // LDS bytes per dim of the transposed tile (64 + 16)
+
+// Partials of split s of row r: the unnormalised output in the MFMA accumulator layout,
+// [wave][nt][lane] float4 (64 heads x 512 dims), then (max, sum) per head in base 2.
+constexpr int64_t kPartO = int64_t(kAH) * kAD;   // floats per (row, split)
+
+struct AttnLds {
+  __attribute__((aligned(16))) unsigned char kvs[kTile * kKvRow];
+  __attribute__((aligned(16))) unsigned char vts[kAD * kVtRow];
+  int rowok[kTile];
+};
+
+template <class RowFn>
+__device__ __forceinline__ void attn_split_mfma(const AttnArgs& a, AttnLds& L, int64_t r,
+                                                int split, int nsplit, int tiles_per_split,
+                                                int64_t n_rows_total, RowFn row_src) {
+  unsigned char* kvs = L.kvs;
+  unsigned char* vts = L.vts;
+  int* rowok = L.rowok;
+  const int nrows = a.top_k + a.window;
+  const int64_t j0 = int64_t(split) * tiles_per_split * kTile;
+  int64_t j1 = j0 + int64_t(tiles_per_split) * kTile;
+  if (j1 > nrows) j1 = nrows;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int head = 16 * wave + col;   // head of this lane in the score layout
+
+  // gather assignment: thread -> rows 4*ra .. 4*ra+3 (ra = tid & 7), 16-byte chunks cp and
+  // cp + 32 (cp = tid >> 3); rows past the list read the query row and are zeroed
+  const int ra = tid & 7, cp = tid >> 3;
+  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + r * kAH * kAD;
+  bf16x8_t vv[4][2];
+  bool okr[4];
+  const uint16_t* srcs[4];
+  auto locate = [&](int64_t j) {   // row pointers of tile j (the ids load here)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      srcs[i] = row_src(j + 4 * ra + i, int(j1));
+      okr[i] = srcs[i] != nullptr;
+    }
+  };
+  auto gather = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* sc = okr[i] ? srcs[i] : qrow;
+      vv[i][0] = *reinterpret_cast<const bf16x8_t*>(sc + cp * 8);
+      vv[i][1] = *reinterpret_cast<const bf16x8_t*>(sc + (cp + 32) * 8);
+    }
+  };
+  if (j0 < j1) locate(j0);
+  // Q^T as B operand: head `head`, dims ks*32 + g*8 .. +8 (loads while the ids arrive)
+  bf16x8_t Qf[16];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (r * kAH + head) * kAD + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) Qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 32);
+  }
+  if (j0 < j1) gather();
+  const float sl2 = a.scale * kLog2e;
+  float m_run = neg_inf(), l_run = 0.f;
+  f32x4_t O[32];
+#pragma unroll
+  for (int nt = 0; nt < 32; ++nt) O[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int64_t j = j0; j < j1; j += kTile) {
+    // tile j to LDS: row-major (A operand of S^T) and transposed, 4 rows per 8-byte store
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!okr[i]) { vv[i][0] = bf16x8_t{}; vv[i][1] = bf16x8_t{}; }
+      if (cp == 0) rowok[4 * ra + i] = okr[i];
+      *reinterpret_cast<bf16x8_t*>(&kvs[(4 * ra + i) * kKvRow + cp * 16]) = vv[i][0];
+      *reinterpret_cast<bf16x8_t*>(&kvs[(4 * ra + i) * kKvRow + (cp + 32) * 16]) = vv[i][1];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = cp + 32 * h;
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vv[0][h]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vv[1][h]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vv[2][h]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vv[3][h]);
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        // dims 2*e2 (low halves) and 2*e2+1 (high halves) of the 4 rows
+        const uint32_t lo01 = __builtin_amdgcn_perm(w1[e2], w0[e2], 0x05040100u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(w3[e2], w2[e2], 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(w1[e2], w0[e2], 0x07060302u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(w3[e2], w2[e2], 0x07060302u);
+        *reinterpret_cast<uint2*>(&vts[(c * 8 + 2 * e2) * kVtRow + ra * 8]) = make_uint2(lo01, lo23);
+        *reinterpret_cast<uint2*>(&vts[(c * 8 + 2 * e2 + 1) * kVtRow + ra * 8]) = make_uint2(hi01, hi23);
+      }
+    }
+    __syncthreads();
+    // the next tile's rows load while this one computes
+    if (j + kTile < j1) {
+      locate(j + kTile);
+      gather();
+    }
+
+    // S^T: rows (4g+i) and (16+4g+i) against head `head`
+    // four independent accumulator chains (even / odd K steps of both 16-row halves)
+    f32x4_t S0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S1 = S0, S2 = S0, S3 = S0;
+#pragma unroll
+    for (int ks = 0; ks < 16; ks += 2) {
+      const bf16x8_t A0 = *reinterpret_cast<const bf16x8_t*>(&kvs[col * kKvRow + ks * 64 + g * 16]);
+      const bf16x8_t A1 = *reinterpret_cast<const bf16x8_t*>(&kvs[(16 + col) * kKvRow + ks * 64 + g * 16]);
+      const bf16x8_t A2 = *reinterpret_cast<const bf16x8_t*>(&kvs[col * kKvRow + ks * 64 + 64 + g * 16]);
+      const bf16x8_t A3 = *reinterpret_cast<const bf16x8_t*>(&kvs[(16 + col) * kKvRow + ks * 64 + 64 + g * 16]);
+      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Qf[ks], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Qf[ks], S1, 0, 0, 0);
+      S2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, Qf[ks + 1], S2, 0, 0, 0);
+      S3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3, Qf[ks + 1], S3, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { S0[i] += S2[i]; S1[i] += S3[i]; }
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = rowok[4 * g + i] ? S0[i] * sl2 : neg_inf();
+      s[4 + i] = rowok[16 + 4 * g + i] ? S1[i] * sl2 : neg_inf();
+    }
+    float tmax = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, s[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == neg_inf()) ? 1.f : exp2f(m_run - m_new);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = (s[i] == neg_inf()) ? 0.f : exp2f(s[i] - m_new);
+      psum += p[i];
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // P as the A operand: row = head `col`, K slots (g, i) <-> rows {4g..4g+3, 16+4g..16+4g+3}
+    bf16x8_t Pf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Pf[i] = (__bf16)p[i];
+    // output rows are heads 4g+i of this wave: fetch their rescale factors
+    float ai[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[nt][i] *= ai[i];
+      const unsigned char* vp = &vts[(nt * 16 + col) * kVtRow];
+      const uint2 lo = *reinterpret_cast<const uint2*>(vp + 8 * g);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vp + 32 + 8 * g);
+      bf16x8_t Vf;
+      const uint4 vv4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      Vf = *reinterpret_cast<const bf16x8_t*>(&vv4);
+      O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pf, Vf, O[nt], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  if (nsplit == 1) {
+    const float zs = a.sink ? a.sink[head] * kLog2e : neg_inf();
+    const float M = fmaxf(m_run, zs);
+    float f = 0.f;
+    if (M != neg_inf()) {
+      const float em = (m_run == neg_inf()) ? 0.f : exp2f(m_run - M);
+      const float den = l_run * em + ((zs == neg_inf()) ? 0.f : exp2f(zs - M));
+      f = den > 0.f ? em / den : 0.f;
+    }
+    float fi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fi[i] = __shfl(f, 4 * g + i);
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (r * kAH + 16 * wave) * kAD;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        op[(4 * g + i) * kAD + nt * 16 + col] = f32_to_bf16(O[nt][i] * fi[i]);
+  } else {
+    // partial in the accumulator layout (16-byte stores), then (max, sum) per head
+    const int64_t rs = r * nsplit + split;
+    f32x4_t* pp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.ws) + rs * kPartO) +
+                  wave * 32 * kWave + lane;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) pp[nt * kWave] = O[nt];
+    if (g == 0) {
+      float2* ml = reinterpret_cast<float2*>(reinterpret_cast<float*>(a.ws) +
+                                             n_rows_total * nsplit * kPartO) + rs * kAH;
+      ml[head] = make_float2(m_run, l_run);
+    }
+  }
+}
+
+
+}  // namespace csa

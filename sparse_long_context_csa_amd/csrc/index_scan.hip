@@ -198,10 +198,10 @@ __device__ __forceinline__ void emit_segment(const SegArgs& sg, SegLds& L, int64
   __syncthreads();
   if (wave == 0) {
     // lambda = K / chunks is the mean count of the row's Top-K per chunk (positions are
-    // exchangeable); J = lambda + 4 sqrt(lambda) + 8 sits far in the Poisson tail
+    // exchangeable); J = lambda + 4 sqrt(lambda) + 5 sits far in the Poisson tail
     const int nch = int((n_pos + sg.chunk - 1) / sg.chunk);
     const float lam = float(sg.K) / float(nch);
-    int J = int(lam + 4.f * sqrtf(lam)) + 9;
+    int J = int(lam + 4.f * sqrtf(lam)) + 5;
     const int jmax = ng / 2 < 64 ? ng / 2 : 64;
     J = J > jmax ? jmax : J;
     J = J < 1 ? 1 : J;

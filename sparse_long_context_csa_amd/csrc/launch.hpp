@@ -145,5 +145,7 @@ struct AttnArgs {
 };
 size_t attn_ws_bytes(int64_t rows, int H, int D, int top_k, int window, int dt);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);
+// merge of the split partials that launch_attn left in a.ws
+hipError_t launch_attn_combine(const AttnArgs& a, int nsplit, hipStream_t s);
 
 }  // namespace csa

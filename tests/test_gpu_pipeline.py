@@ -72,15 +72,68 @@ def test_decode_step_incomplete_block_writes_no_entry():
             assert torch.equal(st["kv"][b].cpu(), kv0[b])
 
 
-@pytest.mark.parametrize("hier", [False, True])
-def test_decode_step_graph_replay_matches_eager(hier):
+# Flat steps over caches of more than 32,768 entries: the scan leaves per-chunk candidate
+# segments and the select works on them.
+def test_decode_step_segments_ragged():
+    spec = datagen.CaseSpec(7110, "decode", B=3, L=4 * 60000, m=4, w_cap=256, ragged=True)
+    case = datagen.make_case(spec)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    _, st, rings, out, idx = run_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
+def test_decode_step_segments_short_rows():
+    # a cache of 40,000 entries holding 300 to 600 visible ones: some rows see fewer than
+    # K = 512 (all selected, -1 padded), the others take the segments of a few chunks
+    spec = datagen.CaseSpec(7111, "decode", B=4, L=2400, e_cap=40000, m=4, w_cap=128,
+                            ragged=True)
+    case = datagen.make_case(spec)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    assert any(int(ref["ids"][b][-1]) == -1 for b in range(spec.B))
+    _, st, rings, out, idx = run_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
+def test_decode_step_segments_clustered_winners():
+    # a doubled stretch of indexer keys (exactly doubled scores) concentrates the Top-K in a
+    # few chunks whose own thresholds exceed the K-th key: the streaming select takes over
+    spec = datagen.CaseSpec(7112, "decode", B=2, L=4 * 50000, m=4, w_cap=128)
+    case = datagen.make_case(spec)
+    k = case["k_idx"]
+    k[0, 20000:21500] = (k[0, 20000:21500].float() * 2).to(k.dtype)
+    k[1, 7000:7300] = (k[1, 7000:7300].float() * 2).to(k.dtype)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    ids0 = ref["ids"][0]
+    assert np.sum((ids0 >= 20000) & (ids0 < 21500)) > 200
+    _, st, rings, out, idx = run_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
+def test_decode_step_segments_odd_k_and_window():
+    # K = 500 and W = 100: one tile holds the last selected ids and the first window rows
+    spec = datagen.CaseSpec(7113, "decode", B=2, L=4 * 40000, m=4, K=500, W=100, w_cap=128,
+                            ragged=True)
+    case = datagen.make_case(spec)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    _, st, rings, out, idx = run_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
+@pytest.mark.parametrize("variant", ["flat", "hier", "segments"])
+def test_decode_step_graph_replay_matches_eager(variant):
     """The fused step captured in a HIP graph: every replay (with eager work and
     synchronisations in between) reproduces the eager result bit for bit."""
-    if hier:
+    if variant == "hier":
         spec = datagen.CaseSpec(7103, "decode", B=2, L=20000, m=1, w_cap=128, block_size=8,
                                 max_blocks=256, n_attn=2, ragged=True)
-    else:
+    elif variant == "flat":
         spec = datagen.CaseSpec(7104, "decode", B=3, L=40000, m=4, w_cap=128, ragged=True)
+    else:
+        spec = datagen.CaseSpec(7105, "decode", B=2, L=4 * 45000, m=4, w_cap=128, ragged=True)
     case = datagen.make_case(spec)
     gaps.enforce_decode(case)
     step, st, rings, out, idx = run_step(case)
