@@ -33,7 +33,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? CSA_OK : CSA_ERR_HIP; }
 // ---- csa_index_topk workspace ------------------------------------------------------------
 struct TopkWs {
   float* scores;
-  float* gmax;        // maxima of 16 consecutive scores (written by the scan)
+  uint32_t* gmax;     // order keys of the maxima of 16 consecutive scores (written by the scan)
   int32_t* n_vis;
   int32_t* count;
   void* scratch;
@@ -47,7 +47,7 @@ TopkWs carve_topk(Carver& c, int64_t rows, int64_t n_keys, int32_t top_k, int64_
   w.stride = round64(n_keys > 0 ? n_keys : 1);
   w.scores = c.take<float>(size_t(rows) * w.stride * 4);
   w.gstride = round64((n_keys > 0 ? n_keys : 1) / 16 + 1);
-  w.gmax = c.take<float>(size_t(rows) * w.gstride * 4);
+  w.gmax = c.take<uint32_t>(size_t(rows) * w.gstride * 4);
   w.n_vis = c.take<int32_t>(size_t(rows) * 4);
   w.count = c.take<int32_t>(size_t(rows) * 4);
   w.scratch = c.take<char>(topk_scratch_bytes(rows, n_keys, top_k));

@@ -64,6 +64,27 @@ __device__ __forceinline__ void load_gates(const float* w, int lane, float (&wv)
   }
 }
 
+// x[l] + x[l ^ 16] + x[l ^ 32] + x[l ^ 48] on every lane, with the gfx950 row swaps
+// (v_permlane16_swap exchanges the odd 16-lane rows of one operand with the even rows of the
+// other, v_permlane32_swap the upper half of one with the lower half of the other): a VALU
+// exchange instead of LDS permutes. Each step adds a lane's value and its partner's, in
+// either order (the same sum).
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// max(x, 0) as a signed-integer max of the bit pattern: non-negative floats keep their bits,
+// negative ones (-0 included) become +0. One integer instruction (a float max would first
+// quiet each operand in IEEE mode).
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(__builtin_elementwise_max(__float_as_int(x), 0));
+}
+
 // 16 MFMAs: acc[mt] = q[16 heads of mt] x key tile; then sum_h w_h * relu(acc)
 __device__ __forceinline__ float tile_score(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
                                             const float (&wv)[4][4]) {
@@ -79,20 +100,21 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&A)[4][4], const bf1
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], fmaxf(acc[mt][i], 0.f), part);
-  part += __shfl_xor(part, 16);
-  part += __shfl_xor(part, 32);
-  return part;
+    for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], relu_bits(acc[mt][i]), part);
+  return sum_rows4(part);
 }
 
-// maximum over the 16 lanes of this lane's group (lanes 16j .. 16j+15 hold one key tile)
-__device__ __forceinline__ float max16(float v) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  return v;
+// maximum over the 16 lanes of this lane's row (lanes 16j .. 16j+15 hold one key tile):
+// integer maxima of order-preserving keys under rotations within the row (DPP row_ror), no
+// LDS traffic; -0 comes back as +0
+__device__ __forceinline__ uint32_t max16_key(uint32_t k) {
+  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x121, 0xf, 0xf, false)));
+  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x122, 0xf, 0xf, false)));
+  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x124, 0xf, 0xf, false)));
+  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x128, 0xf, 0xf, false)));
+  return k;
 }
+
 
 template <bool NT>
 __device__ __forceinline__ void load_key_B(const uint16_t* row, int g, bf16x8_t (&B)[4]) {
@@ -298,7 +320,7 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
     const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
     const int32_t* cand = kCand ? a.cand + r * a.n_cand : nullptr;
     float* out = a.scores + r * a.score_stride;
-    float* gmax = a.gmax + r * a.gmax_stride;
+    uint32_t* gmax = a.gmax + r * a.gmax_stride;
     // key row of position p (positions past the chunk read a safe row and are not stored)
     auto key_row = [&](int64_t p, bool& ok) -> int64_t {
       if (p >= c1) { ok = false; return kCand ? 0 : c0; }
@@ -365,7 +387,7 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
               if (kSeg) segl.sc[p - c0] = sv;
             }
             if (!kSeg) {
-              const float gm = max16(sv);
+              const uint32_t gm = max16_key(order_key(sv));
               if (lane == 0) gmax[tl >> 4] = gm;
             }
             const int64_t nx = tl + int64_t(PF + 1) * 64;
@@ -422,7 +444,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* kb, int64_t tb, int64
                "ds_read_b128 %2, %4 offset:512\n\t"                                        \
                "ds_read_b128 %3, %4 offset:768\n\t"                                        \
                "s_waitcnt lgkmcnt(0)"                                                      \
-               : "=v"(B[0]), "=v"(B[1]), "=v"(B[2]), "=v"(B[3])                            \
+               : "=&v"(B[0]), "=&v"(B[1]), "=&v"(B[2]), "=&v"(B[3])                            \
                : "v"(addr)                                                                 \
                : "memory")
 __device__ __forceinline__ void read_tile_B(const unsigned char* slot, int g, int col, int n,
@@ -544,10 +566,13 @@ __global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk,
       float* out = a.scores + r * a.score_stride;
       const int n = int(c1 - c0);
       for (int i = threadIdx.x; i < n; i += 256) out[c0 + i] = segl.sc[i];
-      float* gmax = a.gmax + r * a.gmax_stride;
+      uint32_t* gmax = a.gmax + r * a.gmax_stride;
       for (int gi = threadIdx.x; gi * 16 < n; gi += 256) {
-        float mx = neg_inf();
-        for (int i = gi * 16; i < gi * 16 + 16 && i < n; ++i) mx = fmaxf(mx, segl.sc[i]);
+        uint32_t mx = 0u;
+        for (int i = gi * 16; i < gi * 16 + 16 && i < n; ++i) {
+          const uint32_t k = order_key(segl.sc[i]);
+          mx = k > mx ? k : mx;
+        }
         gmax[(c0 >> 4) + gi] = mx;
       }
       __syncthreads();
@@ -555,16 +580,51 @@ __global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk,
   }
 }
 
-// ---- prefill: 8 query rows per block, 64-key tiles staged through LDS ----------------------
-constexpr int kPQ = 8;            // query rows per block (one per wave)
-constexpr int kPT = 64;           // keys per tile
-constexpr int kPRow = 272;        // LDS bytes per key row (256 + 16 pad: conflict-free b128)
+// ---- prefill: kPQ query rows per block, 128-key tiles staged through LDS ------------------
+// One wave per query row (its 64 heads x 128 as the A operand in VGPRs); the block's key tiles
+// are shared by its rows. The next tile's 32 KiB load into VGPRs (coalesced, 16 bytes per lane,
+// non-temporal) while the current one is scored from LDS, then go to the other LDS buffer
+// (272-byte rows: the B-operand reads are free of bank conflicts); one barrier per tile. Within
+// a tile the MFMAs of 16-key group u+1 are issued (into the other accumulator set) before the
+// ReLU, gate and head sum of group u, so the matrix pipe works while the VALU reduces.
+constexpr int kPT = 128;          // keys per tile
+constexpr int kPRow = 272;        // LDS bytes per key row (256 + 16 pad)
 
-__global__ __launch_bounds__(512) void scan_prefill_kernel(ScanArgs a, int keys_per_block) {
+__device__ __forceinline__ void tile_mfma(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
+                                          f32x4_t (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][ks], B[ks], acc[mt], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ float tile_reduce(const f32x4_t (&acc)[4], const float (&wv)[4][4]) {
+  float part = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], relu_bits(acc[mt][i]), part);
+  return sum_rows4(part);
+}
+
+__device__ __forceinline__ void read_group_B(const unsigned char* tile, int u, int g, int col,
+                                             bf16x8_t (&B)[4]) {
+  const unsigned char* rp = tile + (u * 16 + col) * kPRow + g * 16;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) B[ks] = *reinterpret_cast<const bf16x8_t*>(rp + ks * 64);
+}
+
+template <int kPQ>
+__global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int keys_per_block) {
+  constexpr int kThreads = kPQ * 64;
+  constexpr int kChunks = kPT * 16;                                  // 16-byte chunks per tile
+  constexpr int kPChunks = (kChunks + kThreads - 1) / kThreads;     // per thread
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][kPT * kPRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
-  const int64_t rows = a.n_seq * a.n_q;
   // query rows of this block: kPQ consecutive rows of one sequence
   const int64_t groups_per_seq = (a.n_q + kPQ - 1) / kPQ;
   const int64_t sq = blockIdx.y / groups_per_seq;
@@ -587,54 +647,74 @@ __global__ __launch_bounds__(512) void scan_prefill_kernel(ScanArgs a, int keys_
   const int64_t k0 = int64_t(blockIdx.x) * keys_per_block;
   const int64_t k1 = k0 + keys_per_block < nmax ? k0 + keys_per_block : nmax;
   if (k0 >= k1) return;
-  (void)rows;
 
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
+  // thread t moves the 16-byte chunks t + kThreads j of a 128 x 256-byte tile (rows past k1
+  // read the block's last row and are not scored)
+  bf16x8_t v[kPChunks];
+  auto gload = [&](int64_t base) {
+#pragma unroll
+    for (int j = 0; j < kPChunks; ++j) {
+      const int ch = int(threadIdx.x) + kThreads * j;
+      if (kChunks % kThreads == 0 || ch < kChunks) {
+        int64_t row = base + (ch >> 4);
+        row = row < k1 ? row : k1 - 1;
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(kb + row * kID) + (ch & 15));
+      }
+    }
+  };
+  auto lstore = [&](unsigned char* tile) {
+#pragma unroll
+    for (int j = 0; j < kPChunks; ++j) {
+      const int ch = int(threadIdx.x) + kThreads * j;
+      if (kChunks % kThreads == 0 || ch < kChunks)
+        *reinterpret_cast<bf16x8_t*>(tile + (ch >> 4) * kPRow + (ch & 15) * 16) = v[j];
+    }
+  };
+  gload(k0);
   bf16x8_t A[4][4];
   load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
   float wv[4][4];
   load_gates(a.w + r * kIH, lane, wv);
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
   float* out = a.scores + r * a.score_stride;
-  float* gmax = a.gmax + r * a.gmax_stride;
-
-  // cooperative tile load: thread t moves 16-byte chunks t and t+512 of the 64x256 B tile
-  const int ch0 = threadIdx.x, ch1 = threadIdx.x + 512;
-  auto gload = [&](int64_t base, bf16x8_t& v0, bf16x8_t& v1) {
-    const int64_t r0 = base + (ch0 >> 4), r1 = base + (ch1 >> 4);
-    const int64_t s0 = r0 < k1 ? r0 : k1 - 1, s1 = r1 < k1 ? r1 : k1 - 1;
-    v0 = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(kb + s0 * kID) + (ch0 & 15));
-    v1 = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(kb + s1 * kID) + (ch1 & 15));
-  };
-  auto lstore = [&](int buf, const bf16x8_t& v0, const bf16x8_t& v1) {
-    *reinterpret_cast<bf16x8_t*>(&lds[buf][(ch0 >> 4) * kPRow + (ch0 & 15) * 16]) = v0;
-    *reinterpret_cast<bf16x8_t*>(&lds[buf][(ch1 >> 4) * kPRow + (ch1 & 15) * 16]) = v1;
-  };
-
-  bf16x8_t v0, v1;
-  gload(k0, v0, v1);
-  lstore(0, v0, v1);
+  uint32_t* gmax = a.gmax + r * a.gmax_stride;
+  lstore(lds[0]);
   __syncthreads();
+
   int buf = 0;
   for (int64_t base = k0; base < k1; base += kPT) {
     const bool more = base + kPT < k1;
-    if (more) gload(base + kPT, v0, v1);
+    if (more) gload(base + kPT);
     if (base < n_vis) {
-      const unsigned char* tb = lds[buf];
+      const unsigned char* tile = lds[buf];
+      const int nv = int(n_vis - base < kPT ? n_vis - base : kPT);   // visible in this tile
+      float* ob = out + base;
+      uint32_t* gb = gmax + (base >> 4);
+      bf16x8_t B[4];
+      f32x4_t acc[2][4];
+      read_group_B(tile, 0, g, col, B);
+      tile_mfma(A, B, acc[0]);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        bf16x8_t B[4];
-        const unsigned char* rp = tb + (nt * 16 + col) * kPRow + g * 16;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) B[ks] = *reinterpret_cast<const bf16x8_t*>(rp + ks * 64);
-        const float s = tile_score(A, B, wv);
-        const int64_t p = base + nt * 16 + col;
-        if (g == 0 && p < n_vis) out[p] = s;
-        const float gm = max16(p < n_vis ? s : neg_inf());
-        if (lane == 0) gmax[(base + nt * 16) >> 4] = gm;
+      for (int u = 0; u < kPT / 16; ++u) {
+        if (u + 1 < kPT / 16) {
+          read_group_B(tile, u + 1, g, col, B);
+          tile_mfma(A, B, acc[(u + 1) & 1]);
+        }
+        const float sc = tile_reduce(acc[u & 1], wv);
+        const int p = u * 16 + col;
+        if (u * 16 + 16 <= nv) {
+          if (g == 0) ob[p] = sc;
+          const uint32_t gk = max16_key(order_key(sc));
+          if (lane == 0) gb[u] = gk;
+        } else if (u * 16 < nv) {
+          if (g == 0 && p < nv) ob[p] = sc;
+          const uint32_t gk = max16_key(p < nv ? order_key(sc) : order_key(neg_inf()));
+          if (lane == 0) gb[u] = gk;
+        }
       }
     }
     if (more) {
-      lstore(buf ^ 1, v0, v1);
+      lstore(lds[buf ^ 1]);
       __syncthreads();
       buf ^= 1;
     }
@@ -692,7 +772,7 @@ __global__ __launch_bounds__(256) void scan_generic_kernel(ScanArgs a) {
   }
   if (live) a.scores[r * a.score_stride + p] = s;
   // 16 consecutive positions sit in 16 consecutive lanes (block bases are multiples of 256)
-  const float gm = max16(s);
+  const uint32_t gm = max16_key(order_key(s));
   if ((threadIdx.x & 15) == 0 && live) a.gmax[r * a.gmax_stride + (p >> 4)] = gm;
 }
 
@@ -702,6 +782,7 @@ static bool fast_shape(const ScanArgs& a) { return a.dt == kBF16 && a.H == kIH &
 // current one, and blocks resident per CU (the persistent grid is n_cu * blocks_per_cu).
 struct ScanTune {
   int chunk = 2048, pf = 1, blocks_per_cu = 2, nt = 1, sd = 2, rot = 0;
+  int prefill_q = 12, prefill_keys = 4096;
 };
 static int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
@@ -716,6 +797,9 @@ static const ScanTune& scan_tune() {
     x.nt = env_int("CSA_TUNE_SCAN_NT", x.nt);
     x.sd = env_int("CSA_TUNE_SCAN_SD", x.sd);
     x.rot = env_int("CSA_TUNE_SCAN_ROT", x.rot);
+    x.prefill_q = env_int("CSA_TUNE_PREFILL_Q", x.prefill_q);
+    x.prefill_keys = (env_int("CSA_TUNE_PREFILL_KEYS", x.prefill_keys) + 127) / 128 * 128;
+    if (x.prefill_keys < 128) x.prefill_keys = 128;
     return x;
   }();
   return t;
@@ -802,11 +886,15 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int64_t max_pos = a.cand ? a.n_cand : a.e_cap;
   if (fast_shape(a) && a.cand == nullptr && a.n_q >= 16) {
-    const int keys_per_block = 4096;
-    const int64_t groups = a.n_seq * ((a.n_q + kPQ - 1) / kPQ);
+    const int keys_per_block = scan_tune().prefill_keys;
+    const int pq = scan_tune().prefill_q == 8 ? 8 : 12;
+    const int64_t groups = a.n_seq * ((a.n_q + pq - 1) / pq);
     const dim3 grid(static_cast<unsigned>((a.e_cap + keys_per_block - 1) / keys_per_block),
                     static_cast<unsigned>(groups));
-    hipLaunchKernelGGL(scan_prefill_kernel, grid, dim3(512), 0, s, a, keys_per_block);
+    if (pq == 8)
+      hipLaunchKernelGGL(scan_prefill_kernel<8>, grid, dim3(8 * 64), 0, s, a, keys_per_block);
+    else
+      hipLaunchKernelGGL(scan_prefill_kernel<12>, grid, dim3(12 * 64), 0, s, a, keys_per_block);
     return hipGetLastError();
   }
   if (fast_shape(a)) {

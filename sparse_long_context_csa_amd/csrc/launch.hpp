@@ -72,7 +72,7 @@ struct ScanArgs {
   int64_t score_stride;
   int32_t* n_vis;         // [rows]
   int32_t* count;         // [rows]
-  float* gmax;            // [rows, gmax_stride]: max of positions [16j, 16j+16)
+  uint32_t* gmax;         // [rows, gmax_stride]: order key of the max of positions [16j, 16j+16)
   int64_t gmax_stride;
   // Decode step (rows are sequences) with its ingest split between the scan and the select
   // (ingest.pos non-null): the scan pools the indexer key of the entry the token completes;
@@ -88,11 +88,12 @@ bool scan_fuses_ingest(int dt, int H, int d, int m);
 // Top-K of each row's `count[r]` positions; position j has score scores[r*stride + j] and
 // id (ids ? ids[r*id_stride + j] : j); an id is valid iff 0 <= id < id_limit[r] (or id >= 0
 // when id_limit is null); ids must ascend with position. Result ids ascending, -1 padded,
-// in out_idx[r*out_stride + k]. gmax (optional) holds the maxima of 16 consecutive scores.
+// in out_idx[r*out_stride + k]. gmax (optional) holds the order keys of the maxima of 16
+// consecutive scores.
 struct TopkArgs {
   const float* scores;
   int64_t stride;
-  const float* gmax;
+  const uint32_t* gmax;   // order keys of 16-position maxima (optional)
   int64_t gstride;
   const int32_t* ids;
   int64_t id_stride;

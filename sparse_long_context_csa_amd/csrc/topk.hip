@@ -65,7 +65,7 @@ constexpr int kHeadPerThread = 4;
 struct SelArgs {
   const float* scores;
   int64_t stride;
-  const float* gmax;      // 16-position maxima of the scores, or null
+  const uint32_t* gmax;   // 16-position maxima of the scores as order keys, or null
   int64_t gstride;
   const int32_t* ids;     // null: id = position
   int64_t id_stride;
@@ -292,7 +292,8 @@ __device__ __forceinline__ uint2 row_bound(const SelArgs& a, SelShared& sh, int6
   if (n <= K) return make_uint2(0u, 0xffffffffu);
   const int64_t n16 = (n + 15) / 16;
   const bool use_g = a.gmax != nullptr && n16 >= 2 * K;
-  const float* src = use_g ? a.gmax + r * a.gstride : a.scores + r * a.stride;
+  const uint32_t* gsrc = use_g ? a.gmax + r * a.gstride : nullptr;   // keys
+  const float* ssrc = a.scores + r * a.stride;                       // scores
   const int64_t nb = use_g ? n16 : n;
   int64_t f = nb / (4 * K);
   if (f < 1) f = 1;
@@ -307,34 +308,42 @@ __device__ __forceinline__ uint2 row_bound(const SelArgs& a, SelShared& sh, int6
       ++cf;
     }
   };
+  // key of source element p (a 16-position maximum, or one score)
+  auto key_at = [&](int64_t p) -> uint32_t { return use_g ? gsrc[p] : order_key(ssrc[p]); };
   if (f == 8) {
     // the long-row case: two 16-byte loads per group, 4 groups per thread in flight
     constexpr int kPer = 4;
     for (int64_t j0 = 0; j0 < G; j0 += int64_t(kPer) * kSelThreads) {
-      float4 v[kPer][2];
+      uint4 v[kPer][2];
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
         const int64_t j = j0 + tid + int64_t(q) * kSelThreads;
         const int64_t p0 = j * 8;
-        const float ni = neg_inf();
-        v[q][0] = make_float4(ni, ni, ni, ni);
+        v[q][0] = make_uint4(kninf, kninf, kninf, kninf);
         v[q][1] = v[q][0];
         if (j < G && p0 + 8 <= nb) {
-          v[q][0] = *reinterpret_cast<const float4*>(src + p0);
-          v[q][1] = *reinterpret_cast<const float4*>(src + p0 + 4);
+          if (use_g) {
+            v[q][0] = *reinterpret_cast<const uint4*>(gsrc + p0);
+            v[q][1] = *reinterpret_cast<const uint4*>(gsrc + p0 + 4);
+          } else {
+            const float4 x0 = *reinterpret_cast<const float4*>(ssrc + p0);
+            const float4 x1 = *reinterpret_cast<const float4*>(ssrc + p0 + 4);
+            v[q][0] = make_uint4(order_key(x0.x), order_key(x0.y), order_key(x0.z), order_key(x0.w));
+            v[q][1] = make_uint4(order_key(x1.x), order_key(x1.y), order_key(x1.z), order_key(x1.w));
+          }
         } else if (j < G) {
-          float* e8 = reinterpret_cast<float*>(&v[q][0]);
-          float* e8b = reinterpret_cast<float*>(&v[q][1]);
-          for (int e = 0; e < 8 && p0 + e < nb; ++e) (e < 4 ? e8[e] : e8b[e - 4]) = src[p0 + e];
+          uint32_t* e8 = reinterpret_cast<uint32_t*>(&v[q][0]);
+          uint32_t* e8b = reinterpret_cast<uint32_t*>(&v[q][1]);
+          for (int e = 0; e < 8 && p0 + e < nb; ++e) (e < 4 ? e8[e] : e8b[e - 4]) = key_at(p0 + e);
         }
       }
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
         const int64_t j = j0 + tid + int64_t(q) * kSelThreads;
         if (j < G) {
-          const float m = fmaxf(fmaxf(fmaxf(v[q][0].x, v[q][0].y), fmaxf(v[q][0].z, v[q][0].w)),
-                                fmaxf(fmaxf(v[q][1].x, v[q][1].y), fmaxf(v[q][1].z, v[q][1].w)));
-          note(j, order_key(m));
+          const uint32_t m0 = max(max(v[q][0].x, v[q][0].y), max(v[q][0].z, v[q][0].w));
+          const uint32_t m1 = max(max(v[q][1].x, v[q][1].y), max(v[q][1].z, v[q][1].w));
+          note(j, max(m0, m1));
         }
       }
     }
@@ -344,7 +353,7 @@ __device__ __forceinline__ uint2 row_bound(const SelArgs& a, SelShared& sh, int6
       const int64_t p1 = p0 + f < nb ? p0 + f : nb;
       uint32_t m = 0u;
       for (int64_t p = p0; p < p1; ++p) {
-        const uint32_t k = order_key(src[p]);
+        const uint32_t k = key_at(p);
         m = k > m ? k : m;
       }
       note(j, m);
