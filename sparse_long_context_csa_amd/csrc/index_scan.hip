@@ -85,6 +85,13 @@ __device__ __forceinline__ float relu_bits(float x) {
   return __int_as_float(__builtin_elementwise_max(__float_as_int(x), 0));
 }
 
+// order_key without folding -0 onto +0: a -0 maps just below +0. For maxima that feed a lower
+// bound this is harmless (a maximum can only come out lower).
+__device__ __forceinline__ uint32_t order_key_nz(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
+}
+
 // 16 MFMAs: acc[mt] = q[16 heads of mt] x key tile; then sum_h w_h * relu(acc)
 __device__ __forceinline__ float tile_score(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
                                             const float (&wv)[4][4]) {
@@ -588,6 +595,7 @@ __global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk,
 // a tile the MFMAs of 16-key group u+1 are issued (into the other accumulator set) before the
 // ReLU, gate and head sum of group u, so the matrix pipe works while the VALU reduces.
 constexpr int kPT = 128;          // keys per tile
+static_assert(kPT % 64 == 0, "the score epilogue works on 4 groups of 16 keys at a time");
 constexpr int kPRow = 272;        // LDS bytes per key row (256 + 16 pad)
 
 __device__ __forceinline__ void tile_mfma(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
@@ -692,6 +700,7 @@ __global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int 
       uint32_t* gb = gmax + (base >> 4);
       bf16x8_t B[4];
       f32x4_t acc[2][4];
+      float scb[4];
       read_group_B(tile, 0, g, col, B);
       tile_mfma(A, B, acc[0]);
 #pragma unroll
@@ -700,16 +709,20 @@ __global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int 
           read_group_B(tile, u + 1, g, col, B);
           tile_mfma(A, B, acc[(u + 1) & 1]);
         }
-        const float sc = tile_reduce(acc[u & 1], wv);
-        const int p = u * 16 + col;
-        if (u * 16 + 16 <= nv) {
-          if (g == 0) ob[p] = sc;
-          const uint32_t gk = max16_key(order_key(sc));
-          if (lane == 0) gb[u] = gk;
-        } else if (u * 16 < nv) {
-          if (g == 0 && p < nv) ob[p] = sc;
-          const uint32_t gk = max16_key(p < nv ? order_key(sc) : order_key(neg_inf()));
-          if (lane == 0) gb[u] = gk;
+        scb[u & 3] = tile_reduce(acc[u & 1], wv);   // the 16 scores, in every 16-lane row
+        if ((u & 3) == 3) {
+          // groups u-3 .. u: row g takes group u-3+g, so lane l holds position 16 (u-3) + l
+          const float sv = g == 0 ? scb[0] : (g == 1 ? scb[1] : (g == 2 ? scb[2] : scb[3]));
+          const int p = (u - 3) * 16 + lane;
+          if ((u - 3) * 16 + 64 <= nv) {
+            ob[p] = sv;
+            const uint32_t gk = max16_key(order_key_nz(sv));
+            if (col == 0) gb[u - 3 + g] = gk;
+          } else if ((u - 3) * 16 < nv) {
+            if (p < nv) ob[p] = sv;
+            const uint32_t gk = max16_key(p < nv ? order_key_nz(sv) : order_key(neg_inf()));
+            if (col == 0 && (u - 3 + g) * 16 < nv) gb[u - 3 + g] = gk;
+          }
         }
       }
     }
