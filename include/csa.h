@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -230,6 +230,11 @@ typedef struct csa_decode_desc {
    * kernel, [2] after the (stage-1) indexer scan, [3] after the selection (incl. the
    * hierarchical stage 2), [4] after the attention calls. The caller owns the events. */
   void *events[CSA_DECODE_EVENTS];
+  /* Optional: hipEvent_t handles (as void*) that the (stage-1) indexer scan kernel takes as
+   * the start and stop events of its own dispatch (hipExtLaunchKernel), so that their
+   * interval is that kernel's run time alone, with no marker packets around it. Both NULL or
+   * both set; the caller owns them. */
+  void *scan_events[2];
 } csa_decode_desc;
 
 size_t csa_decode_step_workspace_size(const csa_decode_desc *d);

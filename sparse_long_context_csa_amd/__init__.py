@@ -11,6 +11,7 @@ import ctypes as C
 import torch
 
 from . import _lib
+from ._events import HipEvents  # noqa: F401
 from ._lib import CsaError, DecodeDesc, check, lib  # noqa: F401
 
 __all__ = ["compress", "index_topk", "index_blocks", "sparse_attn", "DecodeStep", "CsaError",
@@ -200,6 +201,13 @@ class DecodeStep:
         hs = list(handles) + [None] * (_lib.DECODE_EVENTS - len(handles))
         for i, h in enumerate(hs[:_lib.DECODE_EVENTS]):
             self.desc.events[i] = h
+
+    def set_scan_events(self, start=None, stop=None) -> None:
+        """hipEvent_t handles (ints or None) taken by the indexer scan kernel's own dispatch."""
+        if (start is None) != (stop is None):
+            raise ValueError("set both scan events or neither")
+        self.desc.scan_events[0] = start
+        self.desc.scan_events[1] = stop
 
     def __call__(self, stream: int | None = None):
         check("csa_decode_step", lib().csa_decode_step(

@@ -28,7 +28,7 @@ class DecodeDesc(C.Structure):
         ("zi_tail", vp), ("bias", vp), ("bias_i", vp), ("q_idx", vp), ("w", vp),
         ("q_idx2", vp), ("w2", vp), ("q", vp * MAX_ATTN), ("win", vp * MAX_ATTN),
         ("win_new", vp * MAX_ATTN), ("sink", vp * MAX_ATTN), ("out", vp * MAX_ATTN),
-        ("out_idx", vp), ("events", vp * DECODE_EVENTS),
+        ("out_idx", vp), ("events", vp * DECODE_EVENTS), ("scan_events", vp * 2),
     ]
 
 

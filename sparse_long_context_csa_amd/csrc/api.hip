@@ -104,7 +104,8 @@ int check_index_common(int64_t n_seq, int64_t n_q, int64_t e_cap, int32_t H, int
 hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, const int64_t* q_pos,
                      const int32_t* e_count, const int32_t* cand, int64_t n_cand, int64_t n_seq,
                      int64_t n_q, int64_t e_cap, int H, int d, int m, const TopkWs& ws,
-                     hipStream_t s, const IngestArgs* ingest = nullptr, int seg_k = 0) {
+                     hipStream_t s, const IngestArgs* ingest = nullptr, int seg_k = 0,
+                     void* const* kernel_events = nullptr) {
   ScanArgs a{};
   a.dt = dt; a.q = q; a.w = w; a.keys = keys; a.q_pos = q_pos; a.e_count = e_count;
   a.cand = cand; a.n_cand = n_cand; a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap;
@@ -114,7 +115,8 @@ hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, co
   a.ingest = ingest ? *ingest : IngestArgs{};
   a.seg = seg_k > 0 ? segments_for(ws, dt, H, d, n_q, cand != nullptr, n_seq * n_q, e_cap, seg_k)
                     : SegArgs{};
-  return launch_scan(a, s);
+  return launch_scan(a, s, kernel_events ? static_cast<hipEvent_t>(kernel_events[0]) : nullptr,
+                     kernel_events ? static_cast<hipEvent_t>(kernel_events[1]) : nullptr);
 }
 
 hipError_t select_rows(const TopkWs& ws, int64_t rows, int64_t max_count, const int32_t* ids,
@@ -348,6 +350,7 @@ int check_decode_shapes(const csa_decode_desc* d) {
   if (d->top_k < 1 || d->top_k > 2048) return CSA_ERR_SHAPE;
   if (d->n_attn < 1 || d->n_attn > CSA_MAX_ATTN) return CSA_ERR_SHAPE;
   if (d->block_size < 0) return CSA_ERR_SHAPE;
+  if ((d->scan_events[0] == nullptr) != (d->scan_events[1] == nullptr)) return CSA_ERR_NULL;
   if (d->block_size > 0) {
     if (d->block_size > 64 || d->max_blocks < 1 || d->max_blocks > 2048) return CSA_ERR_SHAPE;
     if (int64_t(d->block_size) * d->max_blocks > 32768) return CSA_ERR_UNSUPPORTED;
@@ -419,7 +422,8 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   if (d->block_size > 0) {
     const int np = d->block_size * d->max_blocks;
     if (scan_rows(d->dtype, d->q_idx, d->w, d->k_idx, d->pos, nullptr, nullptr, 0, rows, 1,
-                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.blocks.tk, s, split_ingest) != hipSuccess)
+                  d->e_cap, d->idx_heads, d->idx_dim, d->m, w.blocks.tk, s, split_ingest, 0,
+                  d->scan_events) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
     if (pool_rows(rows, d->e_cap, d->block_size, d->max_blocks, w.pool, w.blocks, s) != hipSuccess)
@@ -433,7 +437,7 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   } else {
     if (scan_rows(d->dtype, d->q_idx, d->w, d->k_idx, d->pos, nullptr, nullptr, 0, rows, 1,
                   d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, s, split_ingest,
-                  d->top_k) != hipSuccess)
+                  d->top_k, d->scan_events) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
     const SegArgs seg = segments_for(w.flat, d->dtype, d->idx_heads, d->idx_dim, 1, false, rows,

@@ -18,6 +18,7 @@
 //  * scan_generic_kernel: any head count/dim and fp32; one thread per candidate.
 // Visibility: entry i is usable by a query at t only if m*(i+1)-1 <= t ("The sliding window
 // is not an optimisation"); positions past a row's visible count are never scored.
+#include <hip/hip_ext.h>
 #include <stdlib.h>
 
 #include "csa_common.hpp"
@@ -866,27 +867,40 @@ SegArgs seg_carve(void* base, int64_t rows, int64_t max_pos, int K) {
   return g;
 }
 
+// hipLaunchKernelGGL, or hipExtLaunchKernelGGL when the caller wants the dispatch's own
+// start and stop events.
+template <typename... KArgs, typename... Args>
+static void launch_k(void (*kernel)(KArgs...), dim3 g, dim3 b, size_t shm, hipStream_t s,
+                     hipEvent_t e0, hipEvent_t e1, Args... args) {
+  if (e0 != nullptr && e1 != nullptr)
+    hipExtLaunchKernelGGL(kernel, g, b, uint32_t(shm), s, e0, e1, 0u, KArgs(args)...);
+  else
+    hipLaunchKernelGGL(kernel, g, b, shm, s, KArgs(args)...);
+}
+
 template <bool kCand, int PF, bool NT, bool kSeg>
-static void launch_decode(const ScanArgs& a, int64_t rows, int64_t max_pos, hipStream_t s) {
+static void launch_decode(const ScanArgs& a, int64_t rows, int64_t max_pos, hipStream_t s,
+                          hipEvent_t e0, hipEvent_t e1) {
   int64_t grid = scan_grid();
   const int chunk = kSeg ? a.seg.chunk : decode_scan_chunk(rows, max_pos, false);
   const int64_t cpr = max_pos > 0 ? (max_pos + chunk - 1) / chunk : 1;
   const int64_t items = rows * cpr;
   if (grid > items) grid = items;
-  hipLaunchKernelGGL((scan_decode_kernel<kCand, PF, NT, kSeg>), dim3(static_cast<unsigned>(grid)),
-                     dim3(256), 0, s, a, chunk, cpr, items);
+  launch_k(scan_decode_kernel<kCand, PF, NT, kSeg>, dim3(static_cast<unsigned>(grid)), dim3(256),
+           0, s, e0, e1, a, chunk, cpr, items);
 }
 
 template <bool kCand, bool kSeg>
-static void launch_decode_pf(const ScanArgs& a, int64_t rows, int64_t max_pos, hipStream_t s) {
+static void launch_decode_pf(const ScanArgs& a, int64_t rows, int64_t max_pos, hipStream_t s,
+                             hipEvent_t e0, hipEvent_t e1) {
   const bool nt = scan_tune().nt != 0;
   switch (scan_tune().pf) {
-    case 1: nt ? launch_decode<kCand, 1, true, kSeg>(a, rows, max_pos, s)
-               : launch_decode<kCand, 1, false, kSeg>(a, rows, max_pos, s); break;
-    case 3: nt ? launch_decode<kCand, 3, true, kSeg>(a, rows, max_pos, s)
-               : launch_decode<kCand, 3, false, kSeg>(a, rows, max_pos, s); break;
-    default: nt ? launch_decode<kCand, 2, true, kSeg>(a, rows, max_pos, s)
-                : launch_decode<kCand, 2, false, kSeg>(a, rows, max_pos, s); break;
+    case 1: nt ? launch_decode<kCand, 1, true, kSeg>(a, rows, max_pos, s, e0, e1)
+               : launch_decode<kCand, 1, false, kSeg>(a, rows, max_pos, s, e0, e1); break;
+    case 3: nt ? launch_decode<kCand, 3, true, kSeg>(a, rows, max_pos, s, e0, e1)
+               : launch_decode<kCand, 3, false, kSeg>(a, rows, max_pos, s, e0, e1); break;
+    default: nt ? launch_decode<kCand, 2, true, kSeg>(a, rows, max_pos, s, e0, e1)
+                : launch_decode<kCand, 2, false, kSeg>(a, rows, max_pos, s, e0, e1); break;
   }
 }
 
@@ -894,7 +908,7 @@ bool scan_fuses_ingest(int dt, int H, int d, int m) {
   return dt == kBF16 && H == kIH && d == kID && m <= kFuseM;
 }
 
-hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int64_t rows = a.n_seq * a.n_q;
   if (rows == 0) return hipSuccess;
   const int64_t max_pos = a.cand ? a.n_cand : a.e_cap;
@@ -905,14 +919,14 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>((a.e_cap + keys_per_block - 1) / keys_per_block),
                     static_cast<unsigned>(groups));
     if (pq == 8)
-      hipLaunchKernelGGL(scan_prefill_kernel<8>, grid, dim3(8 * 64), 0, s, a, keys_per_block);
+      launch_k(scan_prefill_kernel<8>, grid, dim3(8 * 64), 0, s, e0, e1, a, keys_per_block);
     else
-      hipLaunchKernelGGL(scan_prefill_kernel<12>, grid, dim3(12 * 64), 0, s, a, keys_per_block);
+      launch_k(scan_prefill_kernel<12>, grid, dim3(12 * 64), 0, s, e0, e1, a, keys_per_block);
     return hipGetLastError();
   }
   if (fast_shape(a)) {
     if (a.cand) {
-      launch_decode_pf<true, false>(a, rows, max_pos, s);
+      launch_decode_pf<true, false>(a, rows, max_pos, s, e0, e1);
     } else {
       const bool segs = a.seg.seg != nullptr;
       const int chunk = segs ? a.seg.chunk : decode_scan_chunk(rows, max_pos, true);
@@ -925,7 +939,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
       const int rot = scan_tune().rot;
       const int sd = scan_tune().sd;
 #define CSA_STREAM(SEG, SD)                                                                  \
-  hipLaunchKernelGGL((scan_stream_kernel<true, SEG, SD>), gd, bd, 0, s, a, chunk, cpr, items, rot)
+  launch_k(scan_stream_kernel<true, SEG, SD>, gd, bd, 0, s, e0, e1, a, chunk, cpr, items, rot)
       if (segs) {
         if (sd == 2) CSA_STREAM(true, 2);
         else if (sd == 3) CSA_STREAM(true, 3);
@@ -943,9 +957,9 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   const dim3 grid(gx, static_cast<unsigned>(rows));
   const size_t shm = size_t(a.H) * a.d * 4 + size_t(a.H) * 4;
   if (a.dt == kBF16)
-    hipLaunchKernelGGL(scan_generic_kernel<uint16_t>, grid, dim3(256), shm, s, a);
+    launch_k(scan_generic_kernel<uint16_t>, grid, dim3(256), shm, s, e0, e1, a);
   else
-    hipLaunchKernelGGL(scan_generic_kernel<float>, grid, dim3(256), shm, s, a);
+    launch_k(scan_generic_kernel<float>, grid, dim3(256), shm, s, e0, e1, a);
   return hipGetLastError();
 }
 

@@ -80,7 +80,10 @@ struct ScanArgs {
   IngestArgs ingest;
   SegArgs seg;            // decode scan without candidates: candidate segments (optional)
 };
-hipError_t launch_scan(const ScanArgs& a, hipStream_t s);
+// ev_start / ev_stop (both or neither): the start and stop events of the scan kernel's own
+// dispatch (a scan is one kernel).
+hipError_t launch_scan(const ScanArgs& a, hipStream_t s, hipEvent_t ev_start = nullptr,
+                       hipEvent_t ev_stop = nullptr);
 // Whether the decode scan for this shape takes the indexer-key part of the ingest.
 bool scan_fuses_ingest(int dt, int H, int d, int m);
 

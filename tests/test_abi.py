@@ -83,8 +83,9 @@ def test_decode_desc_mirrors_the_header_struct():
     m = re.search(r"#define\s+CSA_DECODE_EVENTS\s+(\d+)", _header())
     assert int(m.group(1)) == _lib.DECODE_EVENTS
     # natural C layout on x86-64: 12 int32 and 2 int64 (64 B), the float padded to 8 B, then
-    # 17 tensor pointers, 5 arrays of CSA_MAX_ATTN pointers, out_idx, the event handles
-    n_ptr = 17 + 5 * _lib.MAX_ATTN + 1 + _lib.DECODE_EVENTS
+    # 17 tensor pointers, 5 arrays of CSA_MAX_ATTN pointers, out_idx, the phase events, the
+    # scan kernel's start and stop events
+    n_ptr = 17 + 5 * _lib.MAX_ATTN + 1 + _lib.DECODE_EVENTS + 2
     assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr
 
 
@@ -151,6 +152,16 @@ def test_decode_validation(lib):
     # hierarchical pools above 32,768 entries are outside the limits
     big = _desc(block_size=64, max_blocks=1024)
     assert lib.csa_decode_step(C.byref(big), C.c_void_p(16), nb, None) == -4
+    # every pointer set (never dereferenced): one scan event without the other is refused
+    # before anything is launched
+    full = _desc()
+    for name, typ in _lib.DecodeDesc._fields_:
+        if typ is C.c_void_p:
+            setattr(full, name, 16)
+        elif name in ("q", "win", "win_new", "sink", "out"):
+            getattr(full, name)[0] = 16
+    full.scan_events[0] = 16
+    assert lib.csa_decode_step(C.byref(full), C.c_void_p(16), nb, None) == -1
 
 
 def test_binding_raises_on_errors(lib):

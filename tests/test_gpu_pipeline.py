@@ -123,6 +123,36 @@ def test_decode_step_segments_odd_k_and_window():
     check_step(case, ref, st, rings, out, idx)
 
 
+def test_decode_step_scan_events():
+    """The scan kernel's dispatch takes the step's scan events: the result is unchanged and
+    their interval lies inside the step's own (marker events 0 and 4)."""
+    spec = datagen.CaseSpec(7114, "decode", B=2, L=4 * 40000, m=4, w_cap=128)
+    case = datagen.make_case(spec)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    step, st, rings, out, idx = run_step(case)
+    check_step(case, ref, st, rings, out, idx)
+    ev = csa.HipEvents()
+    marks = [ev.create() for _ in range(5)]
+    s0, s1 = ev.create(), ev.create()
+    try:
+        step.set_events(marks)
+        step.set_scan_events(s0, s1)
+        out2, idx2 = step()
+        torch.cuda.synchronize()
+        assert torch.equal(idx2.cpu(), idx)
+        scan = ev.ms(s0, s1)
+        whole = ev.ms(marks[0], marks[4])
+        assert 0.0 < scan < whole
+        with pytest.raises(ValueError):
+            step.set_scan_events(s0, None)
+    finally:
+        step.set_events([])
+        step.set_scan_events()
+        for e in marks + [s0, s1]:
+            ev.destroy(e)
+
+
 @pytest.mark.parametrize("variant", ["flat", "hier", "segments"])
 def test_decode_step_graph_replay_matches_eager(variant):
     """The fused step captured in a HIP graph: every replay (with eager work and
