@@ -5,16 +5,20 @@
 // dot product per head, summed with the per-head gate w; section "The indexer is O(n), and
 // that is the ceiling": the scan touches every visible entry and never becomes sparse.
 //
-// Three kernels:
-//  * scan_decode_kernel (bf16, 64 heads x 128): few query rows, many keys. The contraction
-//    is a [64 heads x 128] x [128 x 16 keys] MFMA (v_mfma_f32_16x16x32_bf16) per tile; the
-//    query stays in VGPRs as the A operand and every key row is read once from HBM straight
-//    into the B operand (no LDS: nothing is reused across waves). The channel order inside
-//    each MFMA is permuted so a lane reads 64 contiguous bytes of its key row. ReLU, gate
-//    and head sum run on the accumulator lanes, two xor-shuffles finish the head sum.
-//  * scan_prefill_kernel (bf16, 64 x 128): many query rows (a prefill chunk). 8 query rows
-//    per workgroup (one per wave, A operand in VGPRs); 64-key tiles are staged in LDS once
-//    and reused by the 8 waves, double-buffered with the next tile's global loads.
+// Kernels:
+//  * scan_stream_kernel (bf16, 64 heads x 128, whole visible rows): few query rows, many keys
+//    (decode). The contraction is a [64 heads x 128] x [128 x 16 keys] MFMA
+//    (v_mfma_f32_16x16x32_bf16) per tile with the query in VGPRs as the A operand; key rows
+//    move HBM -> LDS by global_load_lds_dwordx4 (1 KiB of consecutive memory per
+//    instruction, no VGPRs held by loads in flight) through a ring of LDS slots per wave, and
+//    each key row is read once. ReLU, gate and head sum run on the accumulator lanes; two
+//    row swaps finish the head sum. For long rows an item (a chunk of positions) also leaves
+//    its candidate segment for the select.
+//  * scan_decode_kernel: the same contraction with key rows loaded straight into the B
+//    operand; serves rows restricted to a candidate list (the hierarchical stage 2).
+//  * scan_prefill_kernel (bf16, 64 x 128): many query rows (a prefill chunk), the one dense
+//    contraction of the path. kPQ query rows per workgroup (one per wave, A in VGPRs); 128-key
+//    tiles are staged in LDS once and reused by every wave of the workgroup.
 //  * scan_generic_kernel: any head count/dim and fp32; one thread per candidate.
 // Visibility: entry i is usable by a query at t only if m*(i+1)-1 <= t ("The sliding window
 // is not an optimisation"); positions past a row's visible count are never scored.

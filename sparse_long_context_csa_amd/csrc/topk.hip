@@ -27,10 +27,12 @@
 //    exceed the LDS list, the same select streams over the row's scores instead: exact for
 //    any input, slow only when tens of thousands of scores crowd above T.
 // Rows of up to 32,768 positions take one workgroup each for all three steps
-// (select_row_kernel). Longer rows are cut into slices of 4,096 positions: one workgroup per
-// slice computes the bound and keeps its slice's candidates in a segment of its own
-// (select_slice_kernel), then one workgroup per row concatenates the segments in position
-// order and selects (select_final_kernel).
+// (select_row_kernel). Longer rows whose scan left per-chunk candidate segments take one
+// workgroup each over those segments (select_chunks_kernel, exactness checked against the
+// chunks' own thresholds, see there). Other long rows are cut into slices of 4,096
+// positions: one workgroup per slice computes the bound and keeps its slice's candidates in a
+// segment of its own (select_slice_kernel), then one workgroup per row concatenates the
+// segments in position order and selects (select_final_kernel).
 #include <limits.h>
 #include <stdlib.h>
 
