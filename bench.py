@@ -62,12 +62,17 @@ TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profile
 
 
 def source_digest(files) -> str:
-    """sha256 over the named kernel sources (package-relative), in order."""
+    """sha256 over the code of the named kernel sources (package-relative), in order: line
+    comments, surrounding blanks and empty lines are dropped, so a comment edit leaves it
+    unchanged while any change to the code changes it."""
     h = hashlib.sha256()
     base = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_long_context_csa_amd")
     for f in files:
-        with open(os.path.join(base, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(base, f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 
