@@ -630,6 +630,61 @@ __device__ __forceinline__ void read_group_B(const unsigned char* tile, int u, i
   for (int ks = 0; ks < 4; ++ks) B[ks] = *reinterpret_cast<const bf16x8_t*>(rp + ks * 64);
 }
 
+// Transposed form: keys as the MFMA's A operand, the query as B (the same registers, the
+// operands swapped), so lane (g, col) holds keys 4 g + i (i < 4) against head 16 mt + col and
+// needs only the 4 gates of heads 16 mt + col (4 VGPRs instead of 16).
+__device__ __forceinline__ void tile_mfma_t(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
+                                            f32x4_t (&acc)[4]) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(B[ks], A[mt][ks], acc[mt], 0, 0, 0);
+  }
+}
+
+#define CSA_DPP_F(x, ctrl) \
+  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (ctrl), 0xf, 0xf, false))
+
+// sum_h w_h relu(acc) for the 16 keys of a group: the gated ReLU sums over the lane's 4 heads
+// (4 independent chains), then a reduce-scatter over the 16 lanes of the row: lanes col and
+// col ^ 8 (row rotation by 8) split keys {0,1} / {2,3}, lanes col and its mirror in the
+// 8-lane half split the pair, the quad sums. Lane (g, col) ends with key 4 g + (col >> 2).
+__device__ __forceinline__ float tile_reduce_t(const f32x4_t (&acc)[4], const float (&wq)[4],
+                                               int col) {
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = wq[0] * relu_bits(acc[0][i]);
+#pragma unroll
+    for (int mt = 1; mt < 4; ++mt) s[i] = fmaf(wq[mt], relu_bits(acc[mt][i]), s[i]);
+  }
+  const bool h8 = (col & 8) != 0;
+  float k0 = h8 ? s[2] : s[0], k1 = h8 ? s[3] : s[1];
+  const float t0 = h8 ? s[0] : s[2], t1 = h8 ? s[1] : s[3];
+  k0 += CSA_DPP_F(t0, 0x128);                 // row_ror:8
+  k1 += CSA_DPP_F(t1, 0x128);
+  const bool h4 = (col & 4) != 0;
+  float k = h4 ? k1 : k0;
+  const float t = h4 ? k0 : k1;
+  k += CSA_DPP_F(t, 0x141);                   // row_half_mirror
+  k += CSA_DPP_F(k, 0xB1);                    // quad_perm [1,0,3,2]
+  k += CSA_DPP_F(k, 0x4E);                    // quad_perm [2,3,0,1]
+  return k;
+}
+
+// max over the 16 lanes (g, col) with col & 3 equal: rotations by 4 and 8 within the row,
+// then the row swaps
+__device__ __forceinline__ uint32_t max_col4_key(uint32_t k) {
+  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x124, 0xf, 0xf, false)));
+  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x128, 0xf, 0xf, false)));
+  const auto p = __builtin_amdgcn_permlane16_swap(k, k, false, false);
+  k = __builtin_elementwise_max(uint32_t(p[0]), uint32_t(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(k, k, false, false);
+  return __builtin_elementwise_max(uint32_t(q[0]), uint32_t(q[1]));
+}
+
 template <int kPQ>
 __global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int keys_per_block) {
   constexpr int kThreads = kPQ * 64;
@@ -684,11 +739,15 @@ __global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int 
         *reinterpret_cast<bf16x8_t*>(tile + (ch >> 4) * kPRow + (ch & 15) * 16) = v[j];
     }
   };
-  gload(k0);
+  // the query and gates load before the first tile, so that the first tile's LDS store waits
+  // for them too: no load from before the loop is then outstanding inside it, and the loop's
+  // waits only ever cover its own tile loads
   bf16x8_t A[4][4];
   load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
-  float wv[4][4];
-  load_gates(a.w + r * kIH, lane, wv);
+  float wq[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) wq[mt] = a.w[r * kIH + 16 * mt + col];
+  gload(k0);
   float* out = a.scores + r * a.score_stride;
   uint32_t* gmax = a.gmax + r * a.gmax_stride;
   lstore(lds[0]);
@@ -707,26 +766,28 @@ __global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int 
       f32x4_t acc[2][4];
       float scb[4];
       read_group_B(tile, 0, g, col, B);
-      tile_mfma(A, B, acc[0]);
+      tile_mfma_t(A, B, acc[0]);
 #pragma unroll
       for (int u = 0; u < kPT / 16; ++u) {
         if (u + 1 < kPT / 16) {
           read_group_B(tile, u + 1, g, col, B);
-          tile_mfma(A, B, acc[(u + 1) & 1]);
+          tile_mfma_t(A, B, acc[(u + 1) & 1]);
         }
-        scb[u & 3] = tile_reduce(acc[u & 1], wv);   // the 16 scores, in every 16-lane row
+        scb[u & 3] = tile_reduce_t(acc[u & 1], wq, col);   // key 4 g + (col >> 2) of group u
         if ((u & 3) == 3) {
-          // groups u-3 .. u: row g takes group u-3+g, so lane l holds position 16 (u-3) + l
-          const float sv = g == 0 ? scb[0] : (g == 1 ? scb[1] : (g == 2 ? scb[2] : scb[3]));
-          const int p = (u - 3) * 16 + lane;
+          // groups u-3 .. u: lane (g, col) takes group u-3+j, j = col & 3, so the wave's 64
+          // lanes hold the 64 positions (a permutation within 256 bytes)
+          const int j = col & 3;
+          const float sv = j == 0 ? scb[0] : (j == 1 ? scb[1] : (j == 2 ? scb[2] : scb[3]));
+          const int p = (u - 3) * 16 + 16 * j + 4 * g + (col >> 2);
           if ((u - 3) * 16 + 64 <= nv) {
             ob[p] = sv;
-            const uint32_t gk = max16_key(order_key_nz(sv));
-            if (col == 0) gb[u - 3 + g] = gk;
+            const uint32_t gk = max_col4_key(order_key_nz(sv));
+            if (lane < 4) gb[u - 3 + lane] = gk;
           } else if ((u - 3) * 16 < nv) {
             if (p < nv) ob[p] = sv;
-            const uint32_t gk = max16_key(p < nv ? order_key_nz(sv) : order_key(neg_inf()));
-            if (col == 0 && (u - 3 + g) * 16 < nv) gb[u - 3 + g] = gk;
+            const uint32_t gk = max_col4_key(p < nv ? order_key_nz(sv) : order_key(neg_inf()));
+            if (lane < 4 && (u - 3 + lane) * 16 < nv) gb[u - 3 + lane] = gk;
           }
         }
       }
