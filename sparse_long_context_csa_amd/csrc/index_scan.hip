@@ -685,12 +685,66 @@ __device__ __forceinline__ uint32_t max_col4_key(uint32_t k) {
   return __builtin_elementwise_max(uint32_t(q[0]), uint32_t(q[1]));
 }
 
+// Gated ReLU sum over the lane's 16 heads (heads 16 mt + 4 g + i of key col), in two chains.
+__device__ __forceinline__ float lane_part(const f32x4_t (&acc)[4], const float (&wv)[4][4]) {
+  float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 4; mt += 2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p0 = fmaf(wv[mt][i], relu_bits(acc[mt][i]), p0);
+      p1 = fmaf(wv[mt + 1][i], relu_bits(acc[mt + 1][i]), p1);
+    }
+  return p0 + p1;
+}
+
+// Head sums of four 16-key groups at once from the lanes' partial sums x0..x3 (each over
+// the lane's 16 heads; the 4 rows of the wave hold the 4 head quarters): a row-half swap
+// adds rows g and g + 2 of two groups into one register (lanes 0-31 one group, 32-63 the
+// other), a row swap then adds rows g and g + 1. Row 0 ends with group 0, row 1 with group
+// 2, row 2 with group 1, row 3 with group 3: six instructions for 64 scores.
+__device__ __forceinline__ float sum_groups4(float x0, float x1, float x2, float x3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1),
+                                                  false, false);
+  const float s01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x2), __float_as_uint(x3),
+                                                  false, false);
+  const float s23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s01), __float_as_uint(s23),
+                                                  false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Tile layout in LDS: blocks of 4 keys, 1,088 bytes apart; byte 16 l of block b holds the
+// 16-byte chunk l >> 2 of key 4 b + (l & 3) (the layout of one LDS-DMA instruction).
+constexpr int kPTBlocks = kPT / 4;
+constexpr int kPTileBytes = kPTBlocks * kBlk;
+
+__device__ __forceinline__ void read_group_Bd(const unsigned char* tile, int u, int g, int col,
+                                              bf16x8_t (&B)[4]) {
+  const unsigned char* rp = tile + (4 * u + (col >> 2)) * kBlk + (col & 3) * 16 + g * 64;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) B[ks] = *reinterpret_cast<const bf16x8_t*>(rp + ks * 256);
+}
+
+// LDS-DMA of block b of a tile (1 KiB: keys key0 .. key0 + 3). Issued from inline asm: the
+// compiler's wait insertion, which cannot tell which LDS bytes a pending LDS-DMA writes, would
+// otherwise make every read of the other tile buffer wait for this load. The issuing wave
+// waits for its loads itself (vmcnt(0)) before the barrier that publishes the tile.
+__device__ __forceinline__ void dma_block(const uint16_t* kb, int64_t key, unsigned char* dst,
+                                          int lane) {
+  const uint16_t* src = kb + key * kID + (lane >> 2) * 8;
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      uint32_t(size_t((const __attribute__((address_space(3))) unsigned char*)dst)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "s"(m0v)
+               : "memory", "m0");
+}
+
 template <int kPQ>
 __global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int keys_per_block) {
-  constexpr int kThreads = kPQ * 64;
-  constexpr int kChunks = kPT * 16;                                  // 16-byte chunks per tile
-  constexpr int kPChunks = (kChunks + kThreads - 1) / kThreads;     // per thread
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kPT * kPRow];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kPTileBytes];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
   // query rows of this block: kPQ consecutive rows of one sequence
@@ -717,46 +771,30 @@ __global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int 
   if (k0 >= k1) return;
 
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
-  // thread t moves the 16-byte chunks t + kThreads j of a 128 x 256-byte tile (rows past k1
-  // read the block's last row and are not scored)
-  bf16x8_t v[kPChunks];
-  auto gload = [&](int64_t base) {
-#pragma unroll
-    for (int j = 0; j < kPChunks; ++j) {
-      const int ch = int(threadIdx.x) + kThreads * j;
-      if (kChunks % kThreads == 0 || ch < kChunks) {
-        int64_t row = base + (ch >> 4);
-        row = row < k1 ? row : k1 - 1;
-        v[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(kb + row * kID) + (ch & 15));
-      }
+  // wave w moves blocks w, w + kPQ, ... of a tile (rows past k1 read the block's last row and
+  // are not scored)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto tload = [&](int64_t base, unsigned char* tile) {
+    for (int b = wave_u; b < kPTBlocks; b += kPQ) {
+      int64_t key = base + 4 * b + (lane & 3);
+      key = key < k1 ? key : k1 - 1;
+      dma_block(kb, key, tile + b * kBlk, lane);
     }
   };
-  auto lstore = [&](unsigned char* tile) {
-#pragma unroll
-    for (int j = 0; j < kPChunks; ++j) {
-      const int ch = int(threadIdx.x) + kThreads * j;
-      if (kChunks % kThreads == 0 || ch < kChunks)
-        *reinterpret_cast<bf16x8_t*>(tile + (ch >> 4) * kPRow + (ch & 15) * 16) = v[j];
-    }
-  };
-  // the query and gates load before the first tile, so that the first tile's LDS store waits
-  // for them too: no load from before the loop is then outstanding inside it, and the loop's
-  // waits only ever cover its own tile loads
   bf16x8_t A[4][4];
   load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
-  float wq[4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) wq[mt] = a.w[r * kIH + 16 * mt + col];
-  gload(k0);
+  float wv[4][4];
+  load_gates(a.w + r * kIH, lane, wv);
+  tload(k0, lds[0]);
   float* out = a.scores + r * a.score_stride;
   uint32_t* gmax = a.gmax + r * a.gmax_stride;
-  lstore(lds[0]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   int buf = 0;
   for (int64_t base = k0; base < k1; base += kPT) {
     const bool more = base + kPT < k1;
-    if (more) gload(base + kPT);
+    if (more) tload(base + kPT, lds[buf ^ 1]);
     if (base < n_vis) {
       const unsigned char* tile = lds[buf];
       const int nv = int(n_vis - base < kPT ? n_vis - base : kPT);   // visible in this tile
@@ -765,35 +803,33 @@ __global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int 
       bf16x8_t B[4];
       f32x4_t acc[2][4];
       float scb[4];
-      read_group_B(tile, 0, g, col, B);
-      tile_mfma_t(A, B, acc[0]);
+      read_group_Bd(tile, 0, g, col, B);
+      tile_mfma(A, B, acc[0]);
+      const int grp = (g & 1) * 2 + (g >> 1);   // rows 0,1,2,3 hold groups 0,2,1,3
 #pragma unroll
       for (int u = 0; u < kPT / 16; ++u) {
         if (u + 1 < kPT / 16) {
-          read_group_B(tile, u + 1, g, col, B);
-          tile_mfma_t(A, B, acc[(u + 1) & 1]);
+          read_group_Bd(tile, u + 1, g, col, B);
+          tile_mfma(A, B, acc[(u + 1) & 1]);
         }
-        scb[u & 3] = tile_reduce_t(acc[u & 1], wq, col);   // key 4 g + (col >> 2) of group u
+        scb[u & 3] = lane_part(acc[u & 1], wv);
         if ((u & 3) == 3) {
-          // groups u-3 .. u: lane (g, col) takes group u-3+j, j = col & 3, so the wave's 64
-          // lanes hold the 64 positions (a permutation within 256 bytes)
-          const int j = col & 3;
-          const float sv = j == 0 ? scb[0] : (j == 1 ? scb[1] : (j == 2 ? scb[2] : scb[3]));
-          const int p = (u - 3) * 16 + 16 * j + 4 * g + (col >> 2);
+          const float sv = sum_groups4(scb[0], scb[1], scb[2], scb[3]);
+          const int p = (u - 3) * 16 + 16 * grp + col;
           if ((u - 3) * 16 + 64 <= nv) {
             ob[p] = sv;
-            const uint32_t gk = max_col4_key(order_key_nz(sv));
-            if (lane < 4) gb[u - 3 + lane] = gk;
+            const uint32_t gk = max16_key(order_key_nz(sv));
+            if (col == 0) gb[u - 3 + grp] = gk;
           } else if ((u - 3) * 16 < nv) {
             if (p < nv) ob[p] = sv;
-            const uint32_t gk = max_col4_key(p < nv ? order_key_nz(sv) : order_key(neg_inf()));
-            if (lane < 4 && (u - 3 + lane) * 16 < nv) gb[u - 3 + lane] = gk;
+            const uint32_t gk = max16_key(p < nv ? order_key_nz(sv) : order_key(neg_inf()));
+            if (col == 0 && (u - 3 + grp) * 16 < nv) gb[u - 3 + grp] = gk;
           }
         }
       }
     }
     if (more) {
-      lstore(lds[buf ^ 1]);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       buf ^= 1;
     }
