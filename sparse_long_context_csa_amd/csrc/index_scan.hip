@@ -813,6 +813,16 @@ __global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int 
           tile_mfma(A, B, acc[(u + 1) & 1]);
         }
         scb[u & 3] = lane_part(acc[u & 1], wv);
+        if (u + 1 < kPT / 16) {
+          // issue order: the next group's 4 B reads, then each of its 16 MFMAs followed by
+          // two VALU instructions of this group's epilogue
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+          }
+        }
         if ((u & 3) == 3) {
           const float sv = sum_groups4(scb[0], scb[1], scb[2], scb[3]);
           const int p = (u - 3) * 16 + 16 * grp + col;
