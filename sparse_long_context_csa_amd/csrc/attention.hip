@@ -74,6 +74,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, int nsplit, 
                   [&](int64_t j, int nrows) { return row_ptr<uint16_t>(a, r, sq, t, j, nrows); });
 }
 
+__global__ __launch_bounds__(256, 2) void attn_dma_kernel(AttnArgs a, int nsplit, int tiles_per_split) {
+  __shared__ AttnDmaLds lds;
+  const int64_t r = blockIdx.y;
+  const int64_t sq = r / a.n_q;
+  const int64_t t = a.q_pos[r];
+  attn_split_dma(a, lds, r, blockIdx.x, nsplit, tiles_per_split, gridDim.y,
+                 [&](int64_t j, int nrows) { return row_ptr<uint16_t>(a, r, sq, t, j, nrows); });
+}
+
 // Merge the row splits in split order. Grid (32, rows): workgroup x covers the heads of
 // accumulator wave w = x / 8 and the dims of 4 accumulator columns; its first 16 threads
 // compute the split weights e^{m_s - M} / den of those 16 heads into LDS, then every thread
@@ -200,7 +209,10 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   const int64_t tiles = ceil_div(int64_t(a.top_k) + a.window, kTile);
   const int tps = int(ceil_div(tiles > 0 ? tiles : 1, ns));
   const dim3 grid(static_cast<unsigned>(ns), static_cast<unsigned>(rows));
-  hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(256), 0, s, a, ns, tps);
+  if (int64_t(tps) * kTile <= kMaxRowsLds)
+    hipLaunchKernelGGL(attn_dma_kernel, grid, dim3(256), 0, s, a, ns, tps);
+  else
+    hipLaunchKernelGGL(attn_mfma_kernel, grid, dim3(256), 0, s, a, ns, tps);
   if (ns > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -218,4 +218,183 @@ __device__ __forceinline__ void attn_split_mfma(const AttnArgs& a, AttnLds& L, i
 }
 
 
+// ---- LDS-DMA tiles and transpose loads ----------------------------------------------------
+// The same computation over tiles that arrive by LDS-DMA: each wave moves 8 of the tile's 32
+// rows, one global_load_lds_dwordx4 per row (the row's 1 KiB lands contiguously, 1,040
+// bytes apart), into one of two tile buffers while the other is computed. The list's row
+// addresses are resolved once into LDS. S = KV.Q^T reads the row-major tile as before; the
+// P.V operand (32 rows of one dim per lane) comes from the same row-major tile through the
+// gfx950 transpose load ds_read_b64_tr_b16: within a 16-lane group, lane i supplies the
+// address of row r0 + (i >> 2), dims d0 + 4 (i & 3), and lane j receives rows r0 .. r0 + 3
+// of dim d0 + j. No transposed copy is built.
+constexpr int kMaxRowsLds = 1024;   // list rows of one split whose addresses fit in LDS
+
+struct AttnDmaLds {
+  __attribute__((aligned(16))) unsigned char kv[2][kTile * kKvRow];
+  const uint16_t* rowp[kMaxRowsLds];
+  int rowok[2][kTile];
+};
+
+// one LDS-DMA row: 64 lanes x 16 bytes from src (per lane) to dst (uniform). From inline asm:
+// the compiler's own wait insertion cannot tell which LDS bytes a pending LDS-DMA writes and
+// would hold every read of the other tile buffer until it lands. The caller waits for its
+// loads (vmcnt(0)) before the barrier that publishes the tile.
+__device__ __forceinline__ void dma_row(const uint16_t* src, unsigned char* dst) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      uint32_t(size_t((const __attribute__((address_space(3))) unsigned char*)dst)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0v)
+               : "memory", "m0");
+}
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+
+template <class RowFn>
+__device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L, int64_t r,
+                                               int split, int nsplit, int tiles_per_split,
+                                               int64_t n_rows_total, RowFn row_src) {
+  const int nrows = a.top_k + a.window;
+  const int64_t j0 = int64_t(split) * tiles_per_split * kTile;
+  int64_t j1 = j0 + int64_t(tiles_per_split) * kTile;
+  if (j1 > nrows) j1 = nrows;
+  const int nl = j1 > j0 ? int(j1 - j0) : 0;   // list rows of this split
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int g = lane >> 4, col = lane & 15;
+  const int head = 16 * wave + col;   // head of this lane in the score layout
+  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + r * kAH * kAD;
+
+  for (int i = tid; i < nl; i += blockDim.x) L.rowp[i] = row_src(j0 + i, int(j1));
+  // Q^T as B operand: head `head`, dims ks*32 + g*8 .. +8
+  bf16x8_t Qf[16];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + (r * kAH + head) * kAD + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) Qf[ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 32);
+  }
+  __syncthreads();
+  // rows 8 w .. 8 w + 7 of tile t into buffer b; rows past the list (and rows without a
+  // valid address) read the query row and are masked
+  auto issue = [&](int t, int b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tr = 8 * wave_u + i;
+      const int jr = t * kTile + tr;
+      const uint16_t* p = jr < nl ? L.rowp[jr] : nullptr;
+      dma_row((p != nullptr ? p : qrow) + lane * 8, &L.kv[b][tr * kKvRow]);
+      if (lane == 0) L.rowok[b][tr] = p != nullptr;
+    }
+  };
+  const int ntiles = (nl + kTile - 1) / kTile;
+  if (ntiles > 0) issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  const float sl2 = a.scale * kLog2e;
+  float m_run = neg_inf(), l_run = 0.f;
+  f32x4_t O[32];
+#pragma unroll
+  for (int nt = 0; nt < 32; ++nt) O[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = t & 1;
+    if (t + 1 < ntiles) issue(t + 1, b ^ 1);
+    const unsigned char* kvs = L.kv[b];
+    const int* rowok = L.rowok[b];
+
+    // S^T: rows (4g+i) and (16+4g+i) against head `head`, four accumulator chains
+    f32x4_t S0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S1 = S0, S2 = S0, S3 = S0;
+#pragma unroll
+    for (int ks = 0; ks < 16; ks += 2) {
+      const bf16x8_t A0 = *reinterpret_cast<const bf16x8_t*>(&kvs[col * kKvRow + ks * 64 + g * 16]);
+      const bf16x8_t A1 = *reinterpret_cast<const bf16x8_t*>(&kvs[(16 + col) * kKvRow + ks * 64 + g * 16]);
+      const bf16x8_t A2 = *reinterpret_cast<const bf16x8_t*>(&kvs[col * kKvRow + ks * 64 + 64 + g * 16]);
+      const bf16x8_t A3 = *reinterpret_cast<const bf16x8_t*>(&kvs[(16 + col) * kKvRow + ks * 64 + 64 + g * 16]);
+      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Qf[ks], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Qf[ks], S1, 0, 0, 0);
+      S2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, Qf[ks + 1], S2, 0, 0, 0);
+      S3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A3, Qf[ks + 1], S3, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { S0[i] += S2[i]; S1[i] += S3[i]; }
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = rowok[4 * g + i] ? S0[i] * sl2 : neg_inf();
+      s[4 + i] = rowok[16 + 4 * g + i] ? S1[i] * sl2 : neg_inf();
+    }
+    float tmax = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, s[i]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_new == neg_inf()) ? 1.f : exp2f(m_run - m_new);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = (s[i] == neg_inf()) ? 0.f : exp2f(s[i] - m_new);
+      psum += p[i];
+    }
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // P as the A operand: row = head `col`, K slots (g, i) <-> rows {4g..4g+3, 16+4g..16+4g+3}
+    bf16x8_t Pf;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Pf[i] = (__bf16)p[i];
+    float ai[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i);
+    // V operand: slots 0-3 rows 4g .. 4g+3, slots 4-7 rows 16+4g .. 16+4g+3 of dim 16 nt + col
+    const unsigned char* vb = kvs + (4 * g + (col >> 2)) * kKvRow + (col & 3) * 8;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[nt][i] *= ai[i];
+      const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s_t*)(vb + nt * 32));
+      const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s_t*)(vb + 16 * kKvRow + nt * 32));
+      const v4s_t v8[2] = {lo, hi};
+      const bf16x8_t Vf = *reinterpret_cast<const bf16x8_t*>(v8);
+      O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pf, Vf, O[nt], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  if (nsplit == 1) {
+    const float zs = a.sink ? a.sink[head] * kLog2e : neg_inf();
+    const float M = fmaxf(m_run, zs);
+    float f = 0.f;
+    if (M != neg_inf()) {
+      const float em = (m_run == neg_inf()) ? 0.f : exp2f(m_run - M);
+      const float den = l_run * em + ((zs == neg_inf()) ? 0.f : exp2f(zs - M));
+      f = den > 0.f ? em / den : 0.f;
+    }
+    float fi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fi[i] = __shfl(f, 4 * g + i);
+    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (r * kAH + 16 * wave) * kAD;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        op[(4 * g + i) * kAD + nt * 16 + col] = f32_to_bf16(O[nt][i] * fi[i]);
+  } else {
+    const int64_t rs = r * nsplit + split;
+    f32x4_t* pp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.ws) + rs * kPartO) +
+                  wave * 32 * kWave + lane;
+#pragma unroll
+    for (int nt = 0; nt < 32; ++nt) pp[nt * kWave] = O[nt];
+    if (g == 0) {
+      float2* ml = reinterpret_cast<float2*>(reinterpret_cast<float*>(a.ws) +
+                                             n_rows_total * nsplit * kPartO) + rs * kAH;
+      ml[head] = make_float2(m_run, l_run);
+    }
+  }
+}
+
 }  // namespace csa
