@@ -26,6 +26,7 @@ constexpr int kAD = 512;         // head dim on the MFMA path
 constexpr int kTile = 32;        // rows per tile
 constexpr int kKvRow = 1040;     // LDS bytes per row of the row-major tile (1024 + 16)
 constexpr int kVtRow = 80;       // LDS bytes per dim of the transposed tile (64 + 16)
+constexpr float kLazyMax = 8.f;  // log2 headroom of the running softmax maximum
 
 // Partials of split s of row r: the unnormalised output in the MFMA accumulator layout,
 // [wave][nt][lane] float4 (64 heads x 512 dims), then (max, sum) per head in base 2.
@@ -328,8 +329,13 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
     for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, s[i]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_new == neg_inf()) ? 1.f : exp2f(m_run - m_new);
+    // The running maximum moves only when some head's tile maximum exceeds it by more than
+    // kLazyMax (log2 units); below that p = 2^(s - m_run) <= 2^kLazyMax stays well inside the
+    // fp32 and bf16 ranges and the output needs no rescale: the wave skips its 128 products.
+    // Exact up to rounding: the sum and the output share the same m_run.
+    const bool move = __builtin_amdgcn_ballot_w64(tmax > m_run + kLazyMax) != 0;
+    const float m_new = move ? fmaxf(m_run, tmax) : m_run;
+    const float alpha = (m_new == neg_inf() || m_new == m_run) ? 1.f : exp2f(m_run - m_new);
     float p[8], psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -344,15 +350,19 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
     bf16x8_t Pf;
 #pragma unroll
     for (int i = 0; i < 8; ++i) Pf[i] = (__bf16)p[i];
-    float ai[4];
+    if (move) {
+      float ai[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i);
+      for (int i = 0; i < 4; ++i) ai[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int nt = 0; nt < 32; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[nt][i] *= ai[i];
+    }
     // V operand: slots 0-3 rows 4g .. 4g+3, slots 4-7 rows 16+4g .. 16+4g+3 of dim 16 nt + col
     const unsigned char* vb = kvs + (4 * g + (col >> 2)) * kKvRow + (col & 3) * 8;
 #pragma unroll
     for (int nt = 0; nt < 32; ++nt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) O[nt][i] *= ai[i];
       const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) v4s_t*)(vb + nt * 32));
       const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
