@@ -228,10 +228,18 @@ __device__ __forceinline__ void attn_split_mfma(const AttnArgs& a, AttnLds& L, i
 // gfx950 transpose load ds_read_b64_tr_b16: within a 16-lane group, lane i supplies the
 // address of row r0 + (i >> 2), dims d0 + 4 (i & 3), and lane j receives rows r0 .. r0 + 3
 // of dim d0 + j. No transposed copy is built.
+// Rows are 1,056 bytes apart (8 banks of shift per row), and the 16-byte chunk c of row r sits
+// at chunk c ^ swz(r), swz(r) = (r >> 2) & 1, chosen by each DMA lane through its source
+// address. The 16 lanes of a transpose load (rows 4k .. 4k+3, 32 bytes each) then cover the
+// 32 banks once, and so do the 8 lanes of a score-operand read (rows r .. r+7, one chunk:
+// rows 4 apart share a bank shift and differ in the swizzle).
 constexpr int kMaxRowsLds = 1024;   // list rows of one split whose addresses fit in LDS
+constexpr int kKvRowD = 1056;       // LDS bytes per row of a DMA tile
+
+__device__ __forceinline__ int kv_swz(int row) { return (row >> 2) & 1; }
 
 struct AttnDmaLds {
-  __attribute__((aligned(16))) unsigned char kv[2][kTile * kKvRow];
+  __attribute__((aligned(16))) unsigned char kv[2][kTile * kKvRowD];
   const uint16_t* rowp[kMaxRowsLds];
   int rowok[2][kTile];
 };
@@ -283,7 +291,7 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
       const int tr = 8 * wave_u + i;
       const int jr = t * kTile + tr;
       const uint16_t* p = jr < nl ? L.rowp[jr] : nullptr;
-      dma_row((p != nullptr ? p : qrow) + lane * 8, &L.kv[b][tr * kKvRow]);
+      dma_row((p != nullptr ? p : qrow) + (lane ^ kv_swz(tr)) * 8, &L.kv[b][tr * kKvRowD]);
       if (lane == 0) L.rowok[b][tr] = p != nullptr;
     }
   };
@@ -303,14 +311,17 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
     const unsigned char* kvs = L.kv[b];
     const int* rowok = L.rowok[b];
 
-    // S^T: rows (4g+i) and (16+4g+i) against head `head`, four accumulator chains
+    // S^T: rows (4g+i) and (16+4g+i) against head `head`, four accumulator chains; lane
+    // (g, col) reads chunk 4 ks + g of rows col and 16 + col (same swizzle)
+    // (chunk 4 ks + g sits at 4 ks + (g ^ swz): one lane offset, the step is an immediate)
+    const unsigned char* ra0 = kvs + col * kKvRowD + (g ^ kv_swz(col)) * 16;
     f32x4_t S0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, S1 = S0, S2 = S0, S3 = S0;
 #pragma unroll
     for (int ks = 0; ks < 16; ks += 2) {
-      const bf16x8_t A0 = *reinterpret_cast<const bf16x8_t*>(&kvs[col * kKvRow + ks * 64 + g * 16]);
-      const bf16x8_t A1 = *reinterpret_cast<const bf16x8_t*>(&kvs[(16 + col) * kKvRow + ks * 64 + g * 16]);
-      const bf16x8_t A2 = *reinterpret_cast<const bf16x8_t*>(&kvs[col * kKvRow + ks * 64 + 64 + g * 16]);
-      const bf16x8_t A3 = *reinterpret_cast<const bf16x8_t*>(&kvs[(16 + col) * kKvRow + ks * 64 + 64 + g * 16]);
+      const bf16x8_t A0 = *reinterpret_cast<const bf16x8_t*>(ra0 + ks * 64);
+      const bf16x8_t A1 = *reinterpret_cast<const bf16x8_t*>(ra0 + 16 * kKvRowD + ks * 64);
+      const bf16x8_t A2 = *reinterpret_cast<const bf16x8_t*>(ra0 + ks * 64 + 64);
+      const bf16x8_t A3 = *reinterpret_cast<const bf16x8_t*>(ra0 + 16 * kKvRowD + ks * 64 + 64);
       S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0, Qf[ks], S0, 0, 0, 0);
       S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, Qf[ks], S1, 0, 0, 0);
       S2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, Qf[ks + 1], S2, 0, 0, 0);
@@ -359,14 +370,20 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[nt][i] *= ai[i];
     }
-    // V operand: slots 0-3 rows 4g .. 4g+3, slots 4-7 rows 16+4g .. 16+4g+3 of dim 16 nt + col
-    const unsigned char* vb = kvs + (4 * g + (col >> 2)) * kKvRow + (col & 3) * 8;
+    // V operand: slots 0-3 rows 4g .. 4g+3, slots 4-7 rows 16+4g .. 16+4g+3 of dim 16 nt + col;
+    // this lane supplies row 4g + (col >> 2) (+16), dims 16 nt + 4 (col & 3) .. + 3: chunk
+    // 2 nt + ((col & 3) >> 1), half col & 1
+    // (chunk 2 nt + q sits at 2 nt + (q ^ swz): one lane offset, the step is an immediate)
+    const int vrow = 4 * g + (col >> 2);   // rows vrow and vrow + 16 share the swizzle
+    const unsigned char* vb0 =
+        kvs + vrow * kKvRowD + (col & 1) * 8 + (((col & 3) >> 1) ^ kv_swz(vrow)) * 16;
 #pragma unroll
     for (int nt = 0; nt < 32; ++nt) {
+      const unsigned char* vb = vb0 + nt * 32;
       const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s_t*)(vb + nt * 32));
+          (__attribute__((address_space(3))) v4s_t*)(vb));
       const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s_t*)(vb + 16 * kKvRow + nt * 32));
+          (__attribute__((address_space(3))) v4s_t*)(vb + 16 * kKvRowD));
       const v4s_t v8[2] = {lo, hi};
       const bf16x8_t Vf = *reinterpret_cast<const bf16x8_t*>(v8);
       O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pf, Vf, O[nt], 0, 0, 0);
