@@ -48,7 +48,7 @@ __device__ __forceinline__ const T* row_ptr(const AttnArgs& a, int64_t r, int64_
 // (decode) spread each row list over up to 256 workgroups in all, one tile or more each:
 // a wave's chain of LDS reads and MFMAs per tile is latency-bound, so tiles run in
 // parallel workgroups and the partial results are merged afterwards.
-constexpr int kMinTilesPerSplit = 1;
+constexpr int kMinTilesPerSplit = 2;
 static int attn_splits(int64_t rows, int top_k, int window, int H, int D, int dt) {
   if (!(dt == kBF16 && H == kAH && D == kAD)) return 1;
   const int64_t tiles = ceil_div(int64_t(top_k) + window, kTile);
