@@ -25,7 +25,8 @@ HIPFLAGS = [
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["compress.hip", "index_scan.hip", "topk.hip", "attention.hip", "api.hip"]
+SOURCES = ["compress.hip", "index_scan.hip", "index_prefill.hip", "topk.hip", "attention.hip",
+           "api.hip"]
 
 
 def hipcc() -> str:

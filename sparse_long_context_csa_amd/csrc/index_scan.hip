@@ -16,9 +16,8 @@
 //    its candidate segment for the select.
 //  * scan_decode_kernel: the same contraction with key rows loaded straight into the B
 //    operand; serves rows restricted to a candidate list (the hierarchical stage 2).
-//  * scan_prefill_kernel (bf16, 64 x 128): many query rows (a prefill chunk), the one dense
-//    contraction of the path. kPQ query rows per workgroup (one per wave, A in VGPRs); 128-key
-//    tiles are staged in LDS once and reused by every wave of the workgroup.
+//  * scan_prefill_kernel (index_prefill.hip): many query rows (a prefill chunk), the one
+//    dense contraction of the path.
 //  * scan_generic_kernel: any head count/dim and fp32; one thread per candidate.
 // Visibility: entry i is usable by a query at t only if m*(i+1)-1 <= t ("The sliding window
 // is not an optimisation"); positions past a row's visible count are never scored.
@@ -26,76 +25,13 @@
 #include <stdlib.h>
 
 #include "csa_common.hpp"
+#include "index_common.hpp"
 #include "ingest.hpp"
 #include "launch.hpp"
 
 namespace csa {
 
 namespace {
-
-constexpr int kIH = 64;    // indexer heads on the MFMA paths
-constexpr int kID = 128;   // indexer dim on the MFMA paths
-
-__device__ __forceinline__ int64_t row_visible(const ScanArgs& a, int64_t r) {
-  const int64_t sq = r / a.n_q;
-  int64_t cap = a.e_cap;
-  if (a.e_count) {
-    const int64_t ec = a.e_count[sq];
-    cap = ec < cap ? (ec < 0 ? 0 : ec) : cap;
-  }
-  return visible_entries(a.q_pos[r], a.m, cap);
-}
-
-// A operand of one query: heads 16*mt + (lane&15), channels ks*32 + g*8 .. +8 (g = lane>>4).
-// The same channel order is used for the keys (B operand), so that in one load instruction
-// the four lanes of a key read 64 contiguous bytes of its row.
-__device__ __forceinline__ void load_query_A(const uint16_t* q, int lane, bf16x8_t (&A)[4][4]) {
-  const int g = lane >> 4, col = lane & 15;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const uint16_t* p = q + (16 * mt + col) * kID + g * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) A[mt][ks] = *reinterpret_cast<const bf16x8_t*>(p + ks * 32);
-  }
-}
-
-// gates of the heads held by this lane in the accumulator layout: 16*mt + 4*g + i
-__device__ __forceinline__ void load_gates(const float* w, int lane, float (&wv)[4][4]) {
-  const int g = lane >> 4;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const float4 v = *reinterpret_cast<const float4*>(w + 16 * mt + 4 * g);
-    wv[mt][0] = v.x; wv[mt][1] = v.y; wv[mt][2] = v.z; wv[mt][3] = v.w;
-  }
-}
-
-// x[l] + x[l ^ 16] + x[l ^ 32] + x[l ^ 48] on every lane, with the gfx950 row swaps
-// (v_permlane16_swap exchanges the odd 16-lane rows of one operand with the even rows of the
-// other, v_permlane32_swap the upper half of one with the lower half of the other): a VALU
-// exchange instead of LDS permutes. Each step adds a lane's value and its partner's, in
-// either order (the same sum).
-__device__ __forceinline__ float sum_rows4(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
-
-// max(x, 0) as a signed-integer max of the bit pattern: non-negative floats keep their bits,
-// negative ones (-0 included) become +0. One integer instruction (a float max would first
-// quiet each operand in IEEE mode).
-__device__ __forceinline__ float relu_bits(float x) {
-  return __int_as_float(__builtin_elementwise_max(__float_as_int(x), 0));
-}
-
-// order_key without folding -0 onto +0: a -0 maps just below +0. For maxima that feed a lower
-// bound this is harmless (a maximum can only come out lower).
-__device__ __forceinline__ uint32_t order_key_nz(float s) {
-  const uint32_t u = __float_as_uint(s);
-  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
-}
 
 // 16 MFMAs: acc[mt] = q[16 heads of mt] x key tile; then sum_h w_h * relu(acc)
 __device__ __forceinline__ float tile_score(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
@@ -115,18 +51,6 @@ __device__ __forceinline__ float tile_score(const bf16x8_t (&A)[4][4], const bf1
     for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], relu_bits(acc[mt][i]), part);
   return sum_rows4(part);
 }
-
-// maximum over the 16 lanes of this lane's row (lanes 16j .. 16j+15 hold one key tile):
-// integer maxima of order-preserving keys under rotations within the row (DPP row_ror), no
-// LDS traffic; -0 comes back as +0
-__device__ __forceinline__ uint32_t max16_key(uint32_t k) {
-  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x121, 0xf, 0xf, false)));
-  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x122, 0xf, 0xf, false)));
-  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x124, 0xf, 0xf, false)));
-  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x128, 0xf, 0xf, false)));
-  return k;
-}
-
 
 template <bool NT>
 __device__ __forceinline__ void load_key_B(const uint16_t* row, int g, bf16x8_t (&B)[4]) {
@@ -428,7 +352,6 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
 // counts only the tile loads issued after it, so any other memory operation in between only
 // makes it wait longer). Scores stay in LDS and leave in one coalesced pass per item, then the
 // item's candidate segment (kSeg) or its 16-position maxima.
-constexpr int kBlk = 1024 + 64;            // LDS bytes per 4-key block
 constexpr int kTileLds = 4 * kBlk;         // LDS bytes per 16-key tile
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -592,260 +515,6 @@ __global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk,
   }
 }
 
-// ---- prefill: kPQ query rows per block, 128-key tiles staged through LDS ------------------
-// One wave per query row (its 64 heads x 128 as the A operand in VGPRs); the block's key tiles
-// are shared by its rows. The next tile's 32 KiB load into VGPRs (coalesced, 16 bytes per lane,
-// non-temporal) while the current one is scored from LDS, then go to the other LDS buffer
-// (272-byte rows: the B-operand reads are free of bank conflicts); one barrier per tile. Within
-// a tile the MFMAs of 16-key group u+1 are issued (into the other accumulator set) before the
-// ReLU, gate and head sum of group u, so the matrix pipe works while the VALU reduces.
-constexpr int kPT = 128;          // keys per tile
-static_assert(kPT % 64 == 0, "the score epilogue works on 4 groups of 16 keys at a time");
-constexpr int kPRow = 272;        // LDS bytes per key row (256 + 16 pad)
-
-__device__ __forceinline__ void tile_mfma(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
-                                          f32x4_t (&acc)[4]) {
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][ks], B[ks], acc[mt], 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ float tile_reduce(const f32x4_t (&acc)[4], const float (&wv)[4][4]) {
-  float part = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part = fmaf(wv[mt][i], relu_bits(acc[mt][i]), part);
-  return sum_rows4(part);
-}
-
-__device__ __forceinline__ void read_group_B(const unsigned char* tile, int u, int g, int col,
-                                             bf16x8_t (&B)[4]) {
-  const unsigned char* rp = tile + (u * 16 + col) * kPRow + g * 16;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) B[ks] = *reinterpret_cast<const bf16x8_t*>(rp + ks * 64);
-}
-
-// Transposed form: keys as the MFMA's A operand, the query as B (the same registers, the
-// operands swapped), so lane (g, col) holds keys 4 g + i (i < 4) against head 16 mt + col and
-// needs only the 4 gates of heads 16 mt + col (4 VGPRs instead of 16).
-__device__ __forceinline__ void tile_mfma_t(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
-                                            f32x4_t (&acc)[4]) {
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(B[ks], A[mt][ks], acc[mt], 0, 0, 0);
-  }
-}
-
-#define CSA_DPP_F(x, ctrl) \
-  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (ctrl), 0xf, 0xf, false))
-
-// sum_h w_h relu(acc) for the 16 keys of a group: the gated ReLU sums over the lane's 4 heads
-// (4 independent chains), then a reduce-scatter over the 16 lanes of the row: lanes col and
-// col ^ 8 (row rotation by 8) split keys {0,1} / {2,3}, lanes col and its mirror in the
-// 8-lane half split the pair, the quad sums. Lane (g, col) ends with key 4 g + (col >> 2).
-__device__ __forceinline__ float tile_reduce_t(const f32x4_t (&acc)[4], const float (&wq)[4],
-                                               int col) {
-  float s[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s[i] = wq[0] * relu_bits(acc[0][i]);
-#pragma unroll
-    for (int mt = 1; mt < 4; ++mt) s[i] = fmaf(wq[mt], relu_bits(acc[mt][i]), s[i]);
-  }
-  const bool h8 = (col & 8) != 0;
-  float k0 = h8 ? s[2] : s[0], k1 = h8 ? s[3] : s[1];
-  const float t0 = h8 ? s[0] : s[2], t1 = h8 ? s[1] : s[3];
-  k0 += CSA_DPP_F(t0, 0x128);                 // row_ror:8
-  k1 += CSA_DPP_F(t1, 0x128);
-  const bool h4 = (col & 4) != 0;
-  float k = h4 ? k1 : k0;
-  const float t = h4 ? k0 : k1;
-  k += CSA_DPP_F(t, 0x141);                   // row_half_mirror
-  k += CSA_DPP_F(k, 0xB1);                    // quad_perm [1,0,3,2]
-  k += CSA_DPP_F(k, 0x4E);                    // quad_perm [2,3,0,1]
-  return k;
-}
-
-// max over the 16 lanes (g, col) with col & 3 equal: rotations by 4 and 8 within the row,
-// then the row swaps
-__device__ __forceinline__ uint32_t max_col4_key(uint32_t k) {
-  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x124, 0xf, 0xf, false)));
-  k = __builtin_elementwise_max(k, uint32_t(__builtin_amdgcn_update_dpp(0, int(k), 0x128, 0xf, 0xf, false)));
-  const auto p = __builtin_amdgcn_permlane16_swap(k, k, false, false);
-  k = __builtin_elementwise_max(uint32_t(p[0]), uint32_t(p[1]));
-  const auto q = __builtin_amdgcn_permlane32_swap(k, k, false, false);
-  return __builtin_elementwise_max(uint32_t(q[0]), uint32_t(q[1]));
-}
-
-// Gated ReLU sum over the lane's 16 heads (heads 16 mt + 4 g + i of key col), in two chains.
-__device__ __forceinline__ float lane_part(const f32x4_t (&acc)[4], const float (&wv)[4][4]) {
-  float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < 4; mt += 2)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p0 = fmaf(wv[mt][i], relu_bits(acc[mt][i]), p0);
-      p1 = fmaf(wv[mt + 1][i], relu_bits(acc[mt + 1][i]), p1);
-    }
-  return p0 + p1;
-}
-
-// Head sums of four 16-key groups at once from the lanes' partial sums x0..x3 (each over
-// the lane's 16 heads; the 4 rows of the wave hold the 4 head quarters): a row-half swap
-// adds rows g and g + 2 of two groups into one register (lanes 0-31 one group, 32-63 the
-// other), a row swap then adds rows g and g + 1. Row 0 ends with group 0, row 1 with group
-// 2, row 2 with group 1, row 3 with group 3: six instructions for 64 scores.
-__device__ __forceinline__ float sum_groups4(float x0, float x1, float x2, float x3) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1),
-                                                  false, false);
-  const float s01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x2), __float_as_uint(x3),
-                                                  false, false);
-  const float s23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s01), __float_as_uint(s23),
-                                                  false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
-// Tile layout in LDS: blocks of 4 keys, 1,088 bytes apart; byte 16 l of block b holds the
-// 16-byte chunk l >> 2 of key 4 b + (l & 3) (the layout of one LDS-DMA instruction).
-constexpr int kPTBlocks = kPT / 4;
-constexpr int kPTileBytes = kPTBlocks * kBlk;
-
-__device__ __forceinline__ void read_group_Bd(const unsigned char* tile, int u, int g, int col,
-                                              bf16x8_t (&B)[4]) {
-  const unsigned char* rp = tile + (4 * u + (col >> 2)) * kBlk + (col & 3) * 16 + g * 64;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) B[ks] = *reinterpret_cast<const bf16x8_t*>(rp + ks * 256);
-}
-
-// LDS-DMA of block b of a tile (1 KiB: keys key0 .. key0 + 3). Issued from inline asm: the
-// compiler's wait insertion, which cannot tell which LDS bytes a pending LDS-DMA writes, would
-// otherwise make every read of the other tile buffer wait for this load. The issuing wave
-// waits for its loads itself (vmcnt(0)) before the barrier that publishes the tile.
-__device__ __forceinline__ void dma_block(const uint16_t* kb, int64_t key, unsigned char* dst,
-                                          int lane) {
-  const uint16_t* src = kb + key * kID + (lane >> 2) * 8;
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-      uint32_t(size_t((const __attribute__((address_space(3))) unsigned char*)dst)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-               :
-               : "v"(src), "s"(m0v)
-               : "memory", "m0");
-}
-
-template <int kPQ>
-__global__ __launch_bounds__(kPQ * 64) void scan_prefill_kernel(ScanArgs a, int keys_per_block) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kPTileBytes];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, col = lane & 15;
-  // query rows of this block: kPQ consecutive rows of one sequence
-  const int64_t groups_per_seq = (a.n_q + kPQ - 1) / kPQ;
-  const int64_t sq = blockIdx.y / groups_per_seq;
-  const int64_t i0 = (blockIdx.y % groups_per_seq) * kPQ;
-  const int64_t qi = i0 + wave;
-  const bool row_ok = qi < a.n_q;
-  const int64_t r = sq * a.n_q + (row_ok ? qi : i0);
-  const int64_t n_vis = row_ok ? row_visible(a, r) : 0;
-  if (row_ok && blockIdx.x == 0 && lane == 0) {
-    a.n_vis[r] = int32_t(n_vis);
-    a.count[r] = int32_t(n_vis);
-  }
-  // block-wide extent: the largest visible count among the block's rows
-  __shared__ int64_t s_nmax[kPQ];
-  if (lane == 0) s_nmax[wave] = n_vis;
-  __syncthreads();
-  int64_t nmax = 0;
-#pragma unroll
-  for (int i = 0; i < kPQ; ++i) nmax = s_nmax[i] > nmax ? s_nmax[i] : nmax;
-  const int64_t k0 = int64_t(blockIdx.x) * keys_per_block;
-  const int64_t k1 = k0 + keys_per_block < nmax ? k0 + keys_per_block : nmax;
-  if (k0 >= k1) return;
-
-  const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
-  // wave w moves blocks w, w + kPQ, ... of a tile (rows past k1 read the block's last row and
-  // are not scored)
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto tload = [&](int64_t base, unsigned char* tile) {
-    for (int b = wave_u; b < kPTBlocks; b += kPQ) {
-      int64_t key = base + 4 * b + (lane & 3);
-      key = key < k1 ? key : k1 - 1;
-      dma_block(kb, key, tile + b * kBlk, lane);
-    }
-  };
-  bf16x8_t A[4][4];
-  load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
-  float wv[4][4];
-  load_gates(a.w + r * kIH, lane, wv);
-  tload(k0, lds[0]);
-  float* out = a.scores + r * a.score_stride;
-  uint32_t* gmax = a.gmax + r * a.gmax_stride;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  int buf = 0;
-  for (int64_t base = k0; base < k1; base += kPT) {
-    const bool more = base + kPT < k1;
-    if (more) tload(base + kPT, lds[buf ^ 1]);
-    if (base < n_vis) {
-      const unsigned char* tile = lds[buf];
-      const int nv = int(n_vis - base < kPT ? n_vis - base : kPT);   // visible in this tile
-      float* ob = out + base;
-      uint32_t* gb = gmax + (base >> 4);
-      bf16x8_t B[4];
-      f32x4_t acc[2][4];
-      float scb[4];
-      read_group_Bd(tile, 0, g, col, B);
-      tile_mfma(A, B, acc[0]);
-      const int grp = (g & 1) * 2 + (g >> 1);   // rows 0,1,2,3 hold groups 0,2,1,3
-#pragma unroll
-      for (int u = 0; u < kPT / 16; ++u) {
-        if (u + 1 < kPT / 16) {
-          read_group_Bd(tile, u + 1, g, col, B);
-          tile_mfma(A, B, acc[(u + 1) & 1]);
-        }
-        scb[u & 3] = lane_part(acc[u & 1], wv);
-        if (u + 1 < kPT / 16) {
-          // issue order: the next group's 4 B reads, then each of its 16 MFMAs followed by
-          // two VALU instructions of this group's epilogue
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-          }
-        }
-        if ((u & 3) == 3) {
-          const float sv = sum_groups4(scb[0], scb[1], scb[2], scb[3]);
-          const int p = (u - 3) * 16 + 16 * grp + col;
-          if ((u - 3) * 16 + 64 <= nv) {
-            ob[p] = sv;
-            const uint32_t gk = max16_key(order_key_nz(sv));
-            if (col == 0) gb[u - 3 + grp] = gk;
-          } else if ((u - 3) * 16 < nv) {
-            if (p < nv) ob[p] = sv;
-            const uint32_t gk = max16_key(p < nv ? order_key_nz(sv) : order_key(neg_inf()));
-            if (col == 0 && (u - 3 + grp) * 16 < nv) gb[u - 3 + grp] = gk;
-          }
-        }
-      }
-    }
-    if (more) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      buf ^= 1;
-    }
-  }
-}
-
 // ---- generic: one thread per candidate position; any H <= 64, d <= 256, fp32 or bf16 ------
 template <typename T>
 __global__ __launch_bounds__(256) void scan_generic_kernel(ScanArgs a) {
@@ -978,17 +647,6 @@ SegArgs seg_carve(void* base, int64_t rows, int64_t max_pos, int K) {
   return g;
 }
 
-// hipLaunchKernelGGL, or hipExtLaunchKernelGGL when the caller wants the dispatch's own
-// start and stop events.
-template <typename... KArgs, typename... Args>
-static void launch_k(void (*kernel)(KArgs...), dim3 g, dim3 b, size_t shm, hipStream_t s,
-                     hipEvent_t e0, hipEvent_t e1, Args... args) {
-  if (e0 != nullptr && e1 != nullptr)
-    hipExtLaunchKernelGGL(kernel, g, b, uint32_t(shm), s, e0, e1, 0u, KArgs(args)...);
-  else
-    hipLaunchKernelGGL(kernel, g, b, shm, s, KArgs(args)...);
-}
-
 template <bool kCand, int PF, bool NT, bool kSeg>
 static void launch_decode(const ScanArgs& a, int64_t rows, int64_t max_pos, hipStream_t s,
                           hipEvent_t e0, hipEvent_t e1) {
@@ -1029,11 +687,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s, hipEvent_t e0, hipEvent
     const int64_t groups = a.n_seq * ((a.n_q + pq - 1) / pq);
     const dim3 grid(static_cast<unsigned>((a.e_cap + keys_per_block - 1) / keys_per_block),
                     static_cast<unsigned>(groups));
-    if (pq == 8)
-      launch_k(scan_prefill_kernel<8>, grid, dim3(8 * 64), 0, s, e0, e1, a, keys_per_block);
-    else
-      launch_k(scan_prefill_kernel<12>, grid, dim3(12 * 64), 0, s, e0, e1, a, keys_per_block);
-    return hipGetLastError();
+    return launch_scan_prefill(a, pq, keys_per_block, grid, s, e0, e1);
   }
   if (fast_shape(a)) {
     if (a.cand) {

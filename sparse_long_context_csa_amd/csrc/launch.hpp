@@ -84,6 +84,10 @@ struct ScanArgs {
 // dispatch (a scan is one kernel).
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s, hipEvent_t ev_start = nullptr,
                        hipEvent_t ev_stop = nullptr);
+// The many-query scan (prefill) for bf16 64 x 128: pq (8 or 12) query rows and
+// keys_per_block keys per workgroup, grid (key blocks, query groups).
+hipError_t launch_scan_prefill(const ScanArgs& a, int pq, int keys_per_block, dim3 grid,
+                               hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 // Whether the decode scan for this shape takes the indexer-key part of the ingest.
 bool scan_fuses_ingest(int dt, int H, int d, int m);
 
