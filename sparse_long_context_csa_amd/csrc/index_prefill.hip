@@ -13,14 +13,14 @@ namespace csa {
 
 namespace {
 
-// ---- kPQ query rows per workgroup, 128-key tiles staged through LDS ------------------------
+// ---- kPQ query rows per workgroup, 256-key tiles staged through LDS ------------------------
 // One wave per query row (its 64 heads x 128 as the A operand in VGPRs); the workgroup's key
 // tiles are shared by its rows. The next tile moves HBM -> LDS by LDS-DMA (issued from inline
 // asm, no staging registers) while the current one is scored; one barrier per tile. Within a
 // tile the MFMAs of 16-key group u+1 are issued (into the other accumulator set) before the
 // ReLU, gate and head sum of group u, so the matrix pipe works while the VALU reduces, and the
 // head sums of four groups are finished together with three row swaps.
-constexpr int kPT = 128;          // keys per tile
+constexpr int kPT = 256;          // keys per tile
 static_assert(kPT % 64 == 0, "the score epilogue works on 4 groups of 16 keys at a time");
 
 __device__ __forceinline__ void tile_mfma(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
