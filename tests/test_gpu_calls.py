@@ -259,6 +259,8 @@ def check_attn(q, kv, idx, win, sink, pos, w_cap, W, scale, dtype):
     (1, 300, 2000, 512, 128, 4096),    # many rows: one workgroup per row
     (3, 1, 100, 0, 128, 128),          # window only
     (2, 2, 1000, 64, 0, 1),            # selection only
+    (1, 256, 3000, 896, 128, 128),     # 32 tiles per row: the longest list held in LDS
+    (1, 260, 4000, 2048, 128, 128),    # 68 tiles per row: register-staged tiles
 ])
 def test_attention_fast_path(B, Q, E, K, W, w_cap):
     q, kv, idx, win, sink, pos = attn_case(B, Q, E, 64, 512, K, W, w_cap, "bf16",
@@ -267,9 +269,11 @@ def test_attention_fast_path(B, Q, E, K, W, w_cap):
     check_attn(q, kv, idx, win, sink, pos, w_cap, W, 1 / math.sqrt(512), "bf16")
 
 
-def test_attention_sharp_logits():
-    # scaled queries make the softmax peaked: exercises the running-max rescale
-    q, kv, idx, win, sink, pos = attn_case(2, 1, 3000, 64, 512, 512, 128, 128, "bf16", seed=9)
+@pytest.mark.parametrize("B,Q", [(2, 1), (1, 260)])
+def test_attention_sharp_logits(B, Q):
+    # scaled queries make the softmax peaked: exercises the running-max rescale (one split of
+    # 20 tiles per row when there are many rows)
+    q, kv, idx, win, sink, pos = attn_case(B, Q, 3000, 64, 512, 512, 128, 128, "bf16", seed=9)
     q = (q.float() * 150).to(torch.bfloat16)
     check_attn(q, kv, idx, win, sink, pos, 128, 128, 1 / math.sqrt(512), "bf16")
 
