@@ -431,6 +431,13 @@ __global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk,
         ++issued;
       }
     }
+    // the row's query and gates load together with its visible count (not after it): the
+    // first tile's MFMAs then wait for one round trip, not two
+    if (r != cur) {
+      load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
+      load_gates(a.w + r * kIH, lane, wv);
+      cur = r;
+    }
     const int64_t n_pos = row_visible(a, r);
     if (c == 0 && threadIdx.x == 0) {
       a.n_vis[r] = int32_t(n_pos);
@@ -438,11 +445,6 @@ __global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk,
     }
     const int64_t c1 = lim < n_pos ? lim : n_pos;
     if (c0 < c1) {
-      if (r != cur) {
-        load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
-        load_gates(a.w + r * kIH, lane, wv);
-        cur = r;
-      }
       // the entry this step's token completes is pooled by the wave that scores it
       int64_t e_new = -1;
       int slot_new = 0;
