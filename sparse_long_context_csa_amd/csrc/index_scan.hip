@@ -118,6 +118,28 @@ struct SegLds {
   uint32_t gm[kSegMaxChunk / 16];
   uint32_t red[8];
 };
+// Inclusive prefix sum over the 64 lanes with DPP: shifts by 1, 2, 4, 8 within each 16-lane
+// row, then the row totals are carried by the row broadcasts (lane 15 into rows 1 and 3, lane
+// 31 into rows 2 and 3). No LDS permutes.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x111, 0xf, 0xf, false));   // row_shr:1
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x112, 0xf, 0xf, false));   // row_shr:2
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x114, 0xf, 0xf, false));   // row_shr:4
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x118, 0xf, 0xf, false));   // row_shr:8
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x142, 0xa, 0xf, false));   // row_bcast:15
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x143, 0xc, 0xf, false));   // row_bcast:31
+  return x;
+}
+
+// maximum over the 64 lanes: the 16-lane row maximum, then the two row swaps
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
+  k = max16_key(k);
+  const auto p = __builtin_amdgcn_permlane16_swap(k, k, false, false);
+  k = __builtin_elementwise_max(uint32_t(p[0]), uint32_t(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(k, k, false, false);
+  return __builtin_elementwise_max(uint32_t(q[0]), uint32_t(q[1]));
+}
+
 __device__ __forceinline__ void emit_segment(const SegArgs& sg, SegLds& L, int64_t r, int64_t c,
                                              int64_t c0, int64_t c1, int64_t n_pos,
                                              float* scores_row = nullptr) {
@@ -150,8 +172,8 @@ __device__ __forceinline__ void emit_segment(const SegArgs& sg, SegLds& L, int64
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) km = k[i] > km ? k[i] : km;
-  const uint32_t kn = uint32_t(__shfl_xor(int(km), 1));
-  km = kn > km ? kn : km;
+  const uint32_t kn = uint32_t(__builtin_amdgcn_update_dpp(0, int(km), 0xb1, 0xf, 0xf, false));
+  km = kn > km ? kn : km;   // quad_perm [1,0,3,2]: the neighbour lane
   if ((threadIdx.x & 1) == 0 && (i0 >> 4) < ng) L.gm[i0 >> 4] = km;
   __syncthreads();
   if (wave == 0) {
@@ -172,12 +194,7 @@ __device__ __forceinline__ void emit_segment(const SegArgs& sg, SegLds& L, int64
       const int cnt = __popcll(__ballot(v0 >= y)) + __popcll(__ballot(v1 >= y));
       if (cnt >= J) x = y;
     }
-    uint32_t mx = v0 > v1 ? v0 : v1;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint32_t u = uint32_t(__shfl_xor(int(mx), o));
-      mx = u > mx ? u : mx;
-    }
+    const uint32_t mx = wave_max_u32(v0 > v1 ? v0 : v1);
     if (lane == 0) { L.red[0] = x; L.red[1] = mx; }
   }
   __syncthreads();
@@ -187,12 +204,7 @@ __device__ __forceinline__ void emit_segment(const SegArgs& sg, SegLds& L, int64
   for (int i = 0; i < 8; ++i)
     if (i0 + i < n && k[i] >= tau && k[i] > kninf) flags |= 1u << i;
   const uint32_t cnt = __popc(flags);
-  uint32_t x = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t u = uint32_t(__shfl_up(int(x), o));
-    if (lane >= o) x += u;
-  }
+  const uint32_t x = wave_incl_scan(cnt);
   if (lane == 63) L.red[2 + wave] = x;
   __syncthreads();
   uint32_t off = x - cnt, total = 0;
