@@ -66,12 +66,24 @@ __device__ __forceinline__ void load_key_B(const uint16_t* row, int g, bf16x8_t 
 // 2*lane+1 of m rows, the new row in `slot`), store it to the cache, and when `mine` put it
 // into this lane's B operand: channels ks*32 + g*8 .. +8 come from lanes ks*16 + g*4 + 0..3.
 constexpr int kFuseM = 8;   // entries of up to 8 rows are pooled this way
-__device__ __forceinline__ void fuse_new_key(const IngestArgs& ig, int64_t r, int64_t e, int slot,
-                                             int lane, int g, bool mine, uint32_t xn, uint32_t zn,
-                                             const uint32_t (&xt)[kFuseM],
-                                             const uint32_t (&zt)[kFuseM],
-                                             const uint32_t (&bb)[kFuseM], bf16x8_t (&B)[4]) {
+// The pooled indexer key of entry e (row r): the channel-wise softmax over the block's m rows
+// (the new token's row in slot `slot`, the tail's in the others), stored to the cache; lane
+// holds channels 2 lane, 2 lane + 1 of the packed result.
+__device__ __forceinline__ uint32_t fuse_new_key(const IngestArgs& ig, int64_t r, int64_t e,
+                                                 int slot, int lane) {
   const int m = ig.m;
+  const uint32_t xn = reinterpret_cast<const uint32_t*>(ig.xi_new)[r * (kID / 2) + lane];
+  const uint32_t zn = reinterpret_cast<const uint32_t*>(ig.zi_new)[r * (kID / 2) + lane];
+  uint32_t xt[kFuseM], zt[kFuseM], bb[kFuseM];
+#pragma unroll
+  for (int j = 0; j < kFuseM; ++j) {
+    xt[j] = zt[j] = bb[j] = 0u;
+    if (j < m && j != slot) {
+      xt[j] = reinterpret_cast<const uint32_t*>(ig.xi_tail)[(r * m + j) * (kID / 2) + lane];
+      zt[j] = reinterpret_cast<const uint32_t*>(ig.zi_tail)[(r * m + j) * (kID / 2) + lane];
+    }
+    if (j < m) bb[j] = reinterpret_cast<const uint32_t*>(ig.bias_i)[j * (kID / 2) + lane];
+  }
   float res[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -99,6 +111,12 @@ __device__ __forceinline__ void fuse_new_key(const IngestArgs& ig, int64_t r, in
   }
   const uint32_t pk = uint32_t(f32_to_bf16(res[0])) | (uint32_t(f32_to_bf16(res[1])) << 16);
   reinterpret_cast<uint32_t*>(ig.k_idx)[(r * ig.e_cap + e) * (kID / 2) + lane] = pk;
+  return pk;
+}
+
+// The B operand of the lanes that hold the new entry's key (mine: its column) from the packed
+// key pk (channels 2 l, 2 l + 1 in lane l): the tile was loaded before the key was written.
+__device__ __forceinline__ void patch_new_key(uint32_t pk, int g, bool mine, bf16x8_t (&B)[4]) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     uint32_t wds[4];
@@ -280,33 +298,17 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
       ok = true;
       return p;
     };
-    // Decode ingest folded in: the entry that the step's token completes is pooled by the
-    // wave that scores it. Its inputs (2 channels per lane) load now, the pooling runs at
-    // that tile, and lane shuffles place the key in the B operand of its column.
+    // Decode ingest folded in: the entry that the step's token completes is pooled (now) by
+    // the wave that scores it; lane shuffles place the key in the B operand of its column.
     int64_t e_new = -1;
-    int slot = 0;
-    uint32_t pxn = 0, pzn = 0, pxt[kFuseM], pzt[kFuseM], pb[kFuseM];
-#pragma unroll
-    for (int j = 0; j < kFuseM; ++j) pxt[j] = pzt[j] = pb[j] = 0u;
+    uint32_t pk_new = 0u;
     if (fuse) {
       const int64_t t = a.ingest.pos[r];
       const int64_t e = (t + 1) / a.ingest.m - 1;
       if (t >= 0 && (t + 1) % a.ingest.m == 0 && e >= c0 && e < c1 &&
           int((e - c0) >> 4) % 4 == wave) {
         e_new = e;
-        slot = int(t % a.ingest.m);
-        const IngestArgs& ig = a.ingest;
-        const int m = ig.m;
-        pxn = reinterpret_cast<const uint32_t*>(ig.xi_new)[r * (kID / 2) + lane];
-        pzn = reinterpret_cast<const uint32_t*>(ig.zi_new)[r * (kID / 2) + lane];
-#pragma unroll
-        for (int j = 0; j < kFuseM; ++j) {
-          if (j < m && j != slot) {
-            pxt[j] = reinterpret_cast<const uint32_t*>(ig.xi_tail)[(r * m + j) * (kID / 2) + lane];
-            pzt[j] = reinterpret_cast<const uint32_t*>(ig.zi_tail)[(r * m + j) * (kID / 2) + lane];
-          }
-          if (j < m) pb[j] = reinterpret_cast<const uint32_t*>(ig.bias_i)[j * (kID / 2) + lane];
-        }
+        pk_new = fuse_new_key(a.ingest, r, e, int(t % a.ingest.m), lane);
       }
     }
     const int64_t t0 = c0 + wave * 16;
@@ -325,8 +327,7 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(ScanArgs a, int chunk,
           const int64_t tl = t0 + (k + u) * 64;
           if (more && tl < c1) {
             if (e_new >= tl && e_new < tl + 16)
-              fuse_new_key(a.ingest, r, e_new, slot, lane, g, col == int(e_new - tl), pxn, pzn,
-                           pxt, pzt, pb, buf[u]);
+              patch_new_key(pk_new, g, col == int(e_new - tl), buf[u]);
             const float s = tile_score(A, buf[u], wv);
             const int64_t p = tl + col;
             const float sv = (p < c1 && ok[u]) ? s : neg_inf();
@@ -457,31 +458,17 @@ __global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk,
     }
     const int64_t c1 = lim < n_pos ? lim : n_pos;
     if (c0 < c1) {
-      // the entry this step's token completes is pooled by the wave that scores it
+      // the entry this step's token completes is pooled (before the tile loop, its loads
+      // beside the query's) by the wave that scores it
       int64_t e_new = -1;
-      int slot_new = 0;
-      uint32_t pxn = 0, pzn = 0, pxt[kFuseM], pzt[kFuseM], pb[kFuseM];
-#pragma unroll
-      for (int j = 0; j < kFuseM; ++j) pxt[j] = pzt[j] = pb[j] = 0u;
+      uint32_t pk_new = 0u;
       if (fuse) {
         const int64_t t = a.ingest.pos[r];
         const int64_t e = (t + 1) / a.ingest.m - 1;
         if (t >= 0 && (t + 1) % a.ingest.m == 0 && e >= c0 && e < c1 &&
             int((e - c0) >> 4) % 4 == wave) {
           e_new = e;
-          slot_new = int(t % a.ingest.m);
-          const IngestArgs& ig = a.ingest;
-          const int m = ig.m;
-          pxn = reinterpret_cast<const uint32_t*>(ig.xi_new)[r * (kID / 2) + lane];
-          pzn = reinterpret_cast<const uint32_t*>(ig.zi_new)[r * (kID / 2) + lane];
-#pragma unroll
-          for (int j = 0; j < kFuseM; ++j) {
-            if (j < m && j != slot_new) {
-              pxt[j] = reinterpret_cast<const uint32_t*>(ig.xi_tail)[(r * m + j) * (kID / 2) + lane];
-              pzt[j] = reinterpret_cast<const uint32_t*>(ig.zi_tail)[(r * m + j) * (kID / 2) + lane];
-            }
-            if (j < m) pb[j] = reinterpret_cast<const uint32_t*>(ig.bias_i)[j * (kID / 2) + lane];
-          }
+          pk_new = fuse_new_key(a.ingest, r, e, int(t % a.ingest.m), lane);
         }
       }
       // every tile of the item is loaded (in order), so the counts of the waits are exact;
@@ -492,9 +479,7 @@ __global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk,
         bf16x8_t B[4];
         read_tile_B(slot, g, col, issued - t - 1, B);
         if (tb < c1) {
-          if (e_new >= tb && e_new < tb + 16)
-            fuse_new_key(a.ingest, r, e_new, slot_new, lane, g, col == int(e_new - tb), pxn, pzn,
-                         pxt, pzt, pb, B);
+          if (e_new >= tb && e_new < tb + 16) patch_new_key(pk_new, g, col == int(e_new - tb), B);
           const float sc = tile_score(A, B, wv);
           const int64_t p = tb + col;
           if (g == 0 && p < c1) segl.sc[p - c0] = sc;
