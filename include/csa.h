@@ -76,6 +76,23 @@ int csa_compress(const void *x, const void *logits, const void *bias, void *out,
                  int32_t m, int32_t dtype, void *stream);
 
 /* ---------------------------------------------------------------------------------------
+ * csa_quantize_mxfp4 -- MXFP4 storage of indexer keys (production precision).
+ *   [CoD "Rebuilding the model from its constants": the indexer cache is FP4, 64 bytes per
+ *   128-channel key; CoD "FP4, down to the index scores": 1 x 32 MXFP4 sub-blocks.]
+ * Elements E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6), one E8M0 scale 2^(s - 127) per 32 consecutive channels. For each block:
+ * s = floor(log2 max|x|) - 2 clamped to [-127, 127] (-127 for an all-zero block); each x / 2^s
+ * rounds to the nearest magnitude, ties to the even code, magnitudes past 6 to 6; a zero
+ * magnitude is code 0.
+ *   x      : T [n_rows, dim]             (dtype CSA_BF16 or CSA_F32)
+ *   codes  : uint8 [n_rows, dim / 2]     element 2i in the low nibble of byte i
+ *   scales : uint8 [n_rows, dim / 32]    the bytes s
+ * Limits: 32 <= dim <= 8192, dim % 32 == 0. Device pointers; asynchronous on `stream`.
+ * ------------------------------------------------------------------------------------- */
+int csa_quantize_mxfp4(const void *x, void *codes, void *scales, int64_t n_rows, int32_t dim,
+                       int32_t dtype, void *stream);
+
+/* ---------------------------------------------------------------------------------------
  * csa_index_topk -- lightning-indexer scores + Top-K selection.
  *   [CoD "The Lightning Indexer": I(t,s) = sum_h w(t,h) * ReLU(q_I(t,h) . K_s); keep the
  *   top k (512 in V4-Flash). CoD "The sliding window is not an optimisation": entry i is

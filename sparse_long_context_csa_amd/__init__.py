@@ -65,6 +65,23 @@ def compress(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor, m: int,
     return out
 
 
+def quantize_mxfp4(x: torch.Tensor, codes: torch.Tensor | None = None,
+                   scales: torch.Tensor | None = None):
+    """csa_quantize_mxfp4: rows x [..., dim] -> (codes uint8 [..., dim/2], scales uint8 [..., dim/32])."""
+    _dev(x, "x")
+    dim = x.shape[-1]
+    n_rows = x.numel() // dim if dim else 0
+    if codes is None:
+        codes = torch.empty(*x.shape[:-1], dim // 2, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(*x.shape[:-1], dim // 32, dtype=torch.uint8, device=x.device)
+    _dev(codes, "codes", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    check("csa_quantize_mxfp4", lib().csa_quantize_mxfp4(_p(x), _p(codes), _p(scales), n_rows, dim,
+                                                         _dtype(x), _stream()))
+    return codes, scales
+
+
 def index_topk(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor, q_pos: torch.Tensor,
                m: int, top_k: int, e_count: torch.Tensor | None = None,
                cand: torch.Tensor | None = None, want_scores: bool = False,

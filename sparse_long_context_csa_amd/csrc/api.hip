@@ -203,6 +203,16 @@ int csa_compress(const void* x, const void* logits, const void* bias, void* out,
                                    dim, m, static_cast<hipStream_t>(stream)));
 }
 
+int csa_quantize_mxfp4(const void* x, void* codes, void* scales, int64_t n_rows, int32_t dim,
+                       int32_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return CSA_ERR_DTYPE;
+  if (n_rows < 0 || dim < 32 || dim > 8192 || dim % 32 != 0) return CSA_ERR_SHAPE;
+  if (n_rows == 0) return CSA_OK;
+  if (!x || !codes || !scales) return CSA_ERR_NULL;
+  return status_of(launch_quantize_mxfp4(dtype, x, codes, scales, n_rows, dim,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------------------------------
 size_t csa_index_topk_workspace_size(int64_t n_seq, int64_t n_q, int64_t n_keys, int32_t top_k) {
   if (n_seq < 0 || n_q < 0 || n_keys < 0 || top_k < 1) return 0;

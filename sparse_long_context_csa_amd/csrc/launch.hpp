@@ -91,6 +91,11 @@ hipError_t launch_scan_prefill(const ScanArgs& a, int pq, int keys_per_block, di
 // Whether the decode scan for this shape takes the indexer-key part of the ingest.
 bool scan_fuses_ingest(int dt, int H, int d, int m);
 
+// ---- MXFP4 storage of indexer keys (mxfp4.hpp) --------------------------------------------
+// x [n_rows, dim] (dim % 32 == 0) -> codes [n_rows, dim / 2] bytes, scales [n_rows, dim / 32]
+hipError_t launch_quantize_mxfp4(int dt, const void* x, void* codes, void* scales, int64_t n_rows,
+                                 int dim, hipStream_t s);
+
 // ---- selection ---------------------------------------------------------------------------
 // Top-K of each row's `count[r]` positions; position j has score scores[r*stride + j] and
 // id (ids ? ids[r*id_stride + j] : j); an id is valid iff 0 <= id < id_limit[r] (or id >= 0

@@ -38,7 +38,7 @@ def test_header_declares_the_calls():
         "csa_abi_version", "csa_status_str", "csa_compress", "csa_index_topk_workspace_size",
         "csa_index_topk", "csa_index_blocks_workspace_size", "csa_index_blocks",
         "csa_sparse_attn_workspace_size", "csa_sparse_attn", "csa_decode_step_workspace_size",
-        "csa_decode_step"}
+        "csa_decode_step", "csa_quantize_mxfp4"}
 
 
 def test_binding_covers_every_declared_function():
@@ -137,6 +137,15 @@ def _desc(**kw) -> _lib.DecodeDesc:
     for k, v in kw.items():
         setattr(d, k, v)
     return d
+
+
+def test_quantize_mxfp4_validation(lib):
+    ok = C.c_void_p(16)   # never dereferenced: every call below fails validation or is empty
+    assert lib.csa_quantize_mxfp4(ok, ok, ok, 4, 128, 7, None) == -3       # dtype
+    assert lib.csa_quantize_mxfp4(ok, ok, ok, 4, 100, 1, None) == -2       # dim % 32
+    assert lib.csa_quantize_mxfp4(ok, ok, ok, -1, 128, 1, None) == -2
+    assert lib.csa_quantize_mxfp4(None, ok, ok, 4, 128, 1, None) == -1
+    assert lib.csa_quantize_mxfp4(ok, ok, ok, 0, 128, 1, None) == 0        # nothing to do
 
 
 def test_decode_validation(lib):

@@ -294,3 +294,33 @@ def test_attention_no_sink_and_empty():
 def test_attention_generic_path(H, D, dtype):
     q, kv, idx, win, sink, pos = attn_case(2, 3, 400, H, D, 64, 32, 64, dtype, seed=11)
     check_attn(q, kv, idx, win, sink, pos, 64, 32, 1 / math.sqrt(D), dtype)
+
+
+# ------------------------------------------------------------------------------ MXFP4 keys
+def _mx_tie_rows():
+    """Rows of bf16-exact values that sit on the E2M1 rounding midpoints of their block."""
+    from oracle import mx as omx
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, 0.5, 6.0]
+    rows = []
+    for k in (-6, -3, 0, 4):
+        r = np.zeros(128)
+        for b in range(4):
+            blk = np.array([(mids[(b + j) % len(mids)]) * (-1) ** j for j in range(32)])
+            blk[0] = 6.0                       # block maximum 6 * 2^k -> scale 2^k
+            r[32 * b:32 * b + 32] = blk * 2.0 ** k
+        rows.append(r)
+    rows.append(np.zeros(128))                 # zero blocks
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_mxfp4_bit_exact(dtype):
+    from oracle import mx as omx
+    g = np.random.default_rng(31)
+    x = g.standard_normal((300, 128)) / math.sqrt(128) * np.exp(0.5 * g.standard_normal((300, 1)))
+    x = np.concatenate([x, _mx_tie_rows()])
+    xt = torch.from_numpy(x).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    codes, scales = csa.quantize_mxfp4(dev(xt))
+    ref_c, ref_s = omx.quantize(f64(xt))
+    assert np.array_equal(scales.cpu().numpy(), ref_s)
+    assert np.array_equal(codes.cpu().numpy(), omx.pack(ref_c))
