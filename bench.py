@@ -185,6 +185,10 @@ def main():
                     help="replay the step from a captured HIP graph instead of launching it")
     ap.add_argument("--config", type=int, default=4, choices=(2, 3, 4, 5),
                     help="workload (4: the 1M-context decode headline; 3: chunked prefill)")
+    ap.add_argument("--idx-format", default="bf16", choices=("bf16", "mxfp4"),
+                    help="indexer-key cache of the decode workloads: bf16 keys, or MXFP4 codes "
+                         "with one scale byte per 32 channels (csa_quantize_mxfp4 of the same "
+                         "keys, made before the timed region)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -213,9 +217,19 @@ def main():
                     q_idx2=case["q_idx2"].to(dev), w2=case["w2"].to(dev))
     qs = [x.to(dev) for x in case["q"]]
     sinks = [x.to(dev) for x in case["sink"]]
+    mx = args.idx_format == "mxfp4"
+    if mx and (spec.block_size or spec.H_I != 64 or spec.d_I != 128):
+        print(json.dumps({"error": "MXFP4 indexer keys: flat 64 x 128 decode workloads only"}))
+        sys.exit(2)
+    if mx:
+        codes, scales = csa.quantize_mxfp4(case["k_idx"].to(dev))
+        torch.cuda.synchronize()
     steps_objs = []
     for c in range(args.copies):
         st = {k: case[k].to(dev) for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
+        if mx:
+            st["k_idx"] = codes.clone()
+            st["k_idx_scale"] = scales.clone()
         rings = [r.to(dev) for r in case["rings"]]
         win_new = [shared["x_new"] if (i == 0 and datagen.ring_from_raw(spec)) else None
                    for i in range(spec.n_attn)]
@@ -307,12 +321,14 @@ def main():
     mean = [sum(p[j] for p in phases) / len(phases) for j in range(n_ev - 1)]
     scan_ms = sum(scan_launch) / len(scan_launch)
     E = spec.entries
-    scan_bytes = acc.scan_bytes(spec.B, E, spec.H_I, spec.d_I)
+    key_bytes = acc.mxfp4_key_bytes(spec.d_I) if mx else None
+    scan_bytes = acc.scan_bytes(spec.B, E, spec.H_I, spec.d_I, key_bytes=key_bytes)
     step_bytes = acc.decode_step_bytes(B=spec.B, n_vis=E, m=spec.m, D=spec.D, H=spec.H,
                                        H_I=spec.H_I, d_I=spec.d_I, K=spec.K, W=spec.W,
                                        n_attn=spec.n_attn,
                                        pool=spec.block_size * spec.max_blocks,
-                                       ring_write=datagen.ring_from_raw(spec)).total
+                                       ring_write=datagen.ring_from_raw(spec),
+                                       key_bytes=key_bytes).total
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
@@ -323,12 +339,13 @@ def main():
                    "context": spec.L,
                    "entries": E, "m": spec.m, "top_k": spec.K, "window": spec.W,
                    "heads": spec.H, "head_dim": spec.D, "idx_heads": spec.H_I,
-                   "idx_dim": spec.d_I, "state_copies": args.copies,
+                   "idx_dim": spec.d_I, "idx_keys": args.idx_format,
+                   "state_copies": args.copies,
                    "launch": "hip_graph" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "kernel": "scan_stream_kernel (indexer scan, stage 1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic() if args.config == 4 else None,
+                     "traffic": counter_traffic() if args.config == 4 and not mx else None,
                      "avg_launch_us": round(scan_ms * 1e3, 2),
                      "launch_us_min_max": [round(min(scan_launch) * 1e3, 2),
                                            round(max(scan_launch) * 1e3, 2)],
@@ -345,8 +362,17 @@ def main():
     }
     if args.config != 4:
         res["metric"] = f"CSA decode queries/sec ({datagen.WORKLOAD_NAMES[args.config]})"
+    if mx:
+        res["metric"] += ", MXFP4 indexer keys"
     if not args.no_cpu:
+        if mx:
+            # the oracle's step with an MXFP4 cache (the new entry's key quantised); the cached
+            # keys are scored as generated, which is the same work as scoring their MXFP4 values
+            case["idx_format"] = "mxfp4"
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+        if mx:
+            res["cpu_baseline"]["sample"] += (" with an MXFP4 cache (new key quantised; cached "
+                                              "keys scored as generated)")
     print(json.dumps(res), flush=True)
 
 

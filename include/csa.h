@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -218,6 +218,8 @@ int csa_sparse_attn(const void *q, const void *kv, const int32_t *idx, int32_t t
  * ------------------------------------------------------------------------------------- */
 #define CSA_MAX_ATTN 4
 #define CSA_DECODE_EVENTS 5
+#define CSA_IDX_DTYPE 0   /* csa_decode_desc.idx_format: indexer keys in the step's dtype */
+#define CSA_IDX_MXFP4 1   /* indexer keys as MXFP4 codes + scale bytes                    */
 
 typedef struct csa_decode_desc {
   int32_t dtype;
@@ -252,6 +254,17 @@ typedef struct csa_decode_desc {
    * interval is that kernel's run time alone, with no marker packets around it. Both NULL or
    * both set; the caller owns them. */
   void *scan_events[2];
+  /* Storage of the indexer keys: CSA_IDX_DTYPE keeps k_idx in T as above; CSA_IDX_MXFP4 keeps
+   * them in csa_quantize_mxfp4's form, k_idx = codes uint8 [n_seq, e_cap, idx_dim / 2] (16-byte
+   * aligned) and k_idx_scale = scale bytes uint8 [n_seq, e_cap, idx_dim / 32] (4-byte
+   * aligned). The scan scores the keys' exact values; the entry a step completes is pooled,
+   * rounded to T and stored quantised. MXFP4 needs T = bf16, idx_heads 64, idx_dim 128, the
+   * flat selection (block_size 0) and m <= 8; otherwise CSA_ERR_UNSUPPORTED.
+   *   [CoD "Rebuilding the model from its constants": the indexer cache is FP4, 64 bytes per
+   *   128-channel key; CoD "FP4, down to the index scores": the indexer's query-key path
+   *   loads its keys in FP4, 1 x 32 MXFP4 sub-blocks.] */
+  int32_t idx_format;
+  void *k_idx_scale;
 } csa_decode_desc;
 
 size_t csa_decode_step_workspace_size(const csa_decode_desc *d);

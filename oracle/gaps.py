@@ -13,7 +13,7 @@ import numpy as np
 import datagen
 
 from . import csa
-from .pipeline import f64, i64
+from .pipeline import cached_index_key, f64, i64
 
 REL_GAP = 1e-3
 MAX_ATTEMPTS = 2000
@@ -77,7 +77,8 @@ def enforce_decode(case: dict, seqs=None) -> dict:
             zi[t % m] = f64(case["zi_new"][b])
             e = (t + 1) // m - 1
             if e < n:
-                keys[e] = csa.store(csa.compress(xi, zi, bias_i, m)[0], spec.dtype)
+                keys[e] = cached_index_key(
+                    case, csa.store(csa.compress(xi, zi, bias_i, m)[0], spec.dtype))
         R = csa.head_relu(f64(case["q_idx"][b]), keys)
         if spec.block_size > 0:
             # stage 1: the block maxima must separate at rank max_blocks. With tens of

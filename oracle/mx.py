@@ -58,20 +58,29 @@ def round_e2m1(v: float) -> int:
 
 
 def quantize(x) -> tuple[np.ndarray, np.ndarray]:
-    """Codes (one uint8 per element, 0..15) and scale bytes of rows x[..., dim], dim % 32 == 0."""
+    """Codes (one uint8 per element, 0..15) and scale bytes of rows x[..., dim], dim % 32 == 0.
+
+    The rounding of round_e2m1, for all elements at once: the distance of |x| / 2^s to each of
+    the 8 magnitudes, the nearest one, and among two equally near the one with the even code."""
     x = np.asarray(x, dtype=np.float64)
     dim = x.shape[-1]
     assert dim % BLOCK == 0
-    flat = x.reshape(-1, dim)
-    codes = np.zeros(flat.shape, dtype=np.uint8)
-    scales = np.zeros((flat.shape[0], dim // BLOCK), dtype=np.uint8)
-    for i in range(flat.shape[0]):
-        for b in range(dim // BLOCK):
-            blk = flat[i, b * BLOCK:(b + 1) * BLOCK]
-            s = shared_exponent(blk)
-            scales[i, b] = s + 127
-            for j, v in enumerate(blk):
-                codes[i, b * BLOCK + j] = round_e2m1(float(v) * 2.0 ** (-s))
+    blocks = x.reshape(-1, BLOCK)
+    codes = np.empty(blocks.shape, dtype=np.uint8)
+    scales = np.empty(blocks.shape[0], dtype=np.uint8)
+    even = (np.arange(8) & 1) == 0
+    for i0 in range(0, blocks.shape[0], 1 << 15):      # bounded temporaries
+        blk = blocks[i0:i0 + (1 << 15)]
+        amax = np.abs(blk).max(axis=-1)
+        _, e = np.frexp(amax)
+        s = np.where(amax == 0.0, -127, np.clip((e - 1) - E2M1_EMAX, -127, 127)).astype(np.int64)
+        y = blk * np.ldexp(1.0, -s)[:, None]           # exact: a power-of-two scaling
+        dist = np.abs(np.abs(y)[..., None] - E2M1_MAGNITUDES)
+        nearest = dist == dist.min(axis=-1, keepdims=True)
+        # one nearest magnitude, or two neighbours (one even code, one odd): the even one
+        c = np.argmax(nearest * np.where(even, 2, 1), axis=-1)
+        codes[i0:i0 + blk.shape[0]] = np.where((c != 0) & (y < 0), c | 8, c)
+        scales[i0:i0 + blk.shape[0]] = s + 127
     return codes.reshape(x.shape), scales.reshape(x.shape[:-1] + (dim // BLOCK,))
 
 

@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import csa
+from . import csa, mx
 
 
 def f64(a) -> np.ndarray:
@@ -118,6 +118,15 @@ def sparse_attn(q, kv, idx, ring, w_cap, window, q_pos, sink, scale, dtype, rows
     return out
 
 
+def cached_index_key(case: dict, key) -> np.ndarray:
+    """The indexer key of a new entry as the cache holds it: the pooled key in the step's
+    dtype, then, for an MXFP4 cache (case["idx_format"] == "mxfp4"), its MXFP4 value
+    ("FP4, down to the index scores": the indexer's keys are cached in FP4)."""
+    if case.get("idx_format") == "mxfp4":
+        return mx.dequantize(*mx.quantize(key))
+    return key
+
+
 def decode_step(case: dict, seqs=None) -> dict:
     """The fused decode step for one new token per sequence (oracle side).
 
@@ -126,7 +135,9 @@ def decode_step(case: dict, seqs=None) -> dict:
     the block is complete ((t+1) % m == 0) entry (t+1)/m - 1 is pooled from the tails for
     both streams and stored; then the visible entries are scored, selected (directly, or
     through the block pre-select and pool rescoring), and every attention call attends to
-    the shared selection plus its own window and sink.
+    the shared selection plus its own window and sink. With case["idx_format"] == "mxfp4",
+    case["k_idx"] holds the MXFP4 values of the cached keys and the new entry's key is
+    quantised before it is scored (``cached_index_key``).
     Returns a dict with per-sequence results (new entries, scores, pool, ids, outputs).
     """
     spec = case["spec"]
@@ -158,7 +169,7 @@ def decode_step(case: dict, seqs=None) -> dict:
             res["kv_new"][b] = kv_e
             res["ki_new"][b] = ki_e
             if new_e < n_vis:
-                keys[new_e] = ki_e
+                keys[new_e] = cached_index_key(case, ki_e)
         res["n_vis"][b] = n_vis
         s1 = csa.index_scores(f64(case["q_idx"][b]), f64(case["w"][b]), keys)
         res["scores"][b] = s1

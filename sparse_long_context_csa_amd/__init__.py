@@ -161,16 +161,20 @@ class DecodeStep:
     Tensors (GPU, contiguous): pos, x_new, z_new, xi_new, zi_new, kv, k_idx, x_tail, z_tail,
     xi_tail, zi_tail, bias, bias_i, q_idx, w, [q_idx2, w2], q (list), win (list),
     win_new (list, entries may be None), sink (list, entries may be None); out (list) and
-    out_idx are allocated here unless given."""
+    out_idx are allocated here unless given. With k_idx_scale (uint8 [n_seq, e_cap,
+    idx_dim / 32]) the indexer cache is MXFP4: k_idx holds the codes, uint8 [n_seq, e_cap,
+    idx_dim / 2], as quantize_mxfp4 writes them."""
 
     def __init__(self, *, m: int, top_k: int, window: int, scale: float, block_size: int = 0,
                  max_blocks: int = 0, out=None, out_idx=None, **t):
         self.t = t
         kv = _dev(t["kv"], "kv")
         dt = kv.dtype
-        for k in ("x_new", "z_new", "xi_new", "zi_new", "k_idx", "x_tail", "z_tail", "xi_tail",
+        mx = t.get("k_idx_scale") is not None
+        for k in ("x_new", "z_new", "xi_new", "zi_new", "x_tail", "z_tail", "xi_tail",
                   "zi_tail", "bias", "bias_i", "q_idx"):
             _dev(t[k], k, dt)
+        _dev(t["k_idx"], "k_idx", torch.uint8 if mx else dt)
         _dev(t["pos"], "pos", torch.int64)
         _dev(t["w"], "w", torch.float32)
         qs, wins = list(t["q"]), list(t["win"])
@@ -196,6 +200,13 @@ class DecodeStep:
         for k in ("pos", "x_new", "z_new", "xi_new", "zi_new", "kv", "k_idx", "x_tail", "z_tail",
                   "xi_tail", "zi_tail", "bias", "bias_i", "q_idx", "w"):
             setattr(d, k, t[k].data_ptr())
+        if mx:
+            ks = _dev(t["k_idx_scale"], "k_idx_scale", torch.uint8)
+            if (tuple(t["k_idx"].shape) != (n_seq, e_cap, idx_dim // 2)
+                    or tuple(ks.shape) != (n_seq, e_cap, idx_dim // 32)):
+                raise ValueError("MXFP4 k_idx / k_idx_scale shapes do not match kv and q_idx")
+            d.idx_format = _lib.IDX_MXFP4
+            d.k_idx_scale = ks.data_ptr()
         if block_size > 0:
             _dev(t["q_idx2"], "q_idx2", dt); _dev(t["w2"], "w2", torch.float32)
             d.q_idx2 = t["q_idx2"].data_ptr(); d.w2 = t["w2"].data_ptr()

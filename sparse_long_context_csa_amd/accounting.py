@@ -57,11 +57,13 @@ class StepBytes:
 
 def decode_step_bytes(B: int, n_vis: int, m: int, D: int, H: int, H_I: int, d_I: int, K: int,
                       W: int, n_attn: int = 1, pool: int = 0, elt: int = BF16,
-                      ring_write: bool = True) -> StepBytes:
+                      ring_write: bool = True, key_bytes: int | None = None) -> StepBytes:
     """Algorithmic HBM bytes of one fused decode step over B sequences, each with n_vis
     visible entries (all sequences at a block boundary, so one entry is pooled per stream).
-    pool > 0: hierarchical (stage-1 scan of n_vis keys, then ``pool`` rescored keys)."""
-    keys = B * n_vis * d_I * elt + B * pool * d_I * elt
+    pool > 0: hierarchical (stage-1 scan of n_vis keys, then ``pool`` rescored keys).
+    key_bytes: bytes of one cached indexer key (default d_I * elt; MXFP4: mxfp4_key_bytes)."""
+    kb = d_I * elt if key_bytes is None else key_bytes
+    keys = B * n_vis * kb + B * pool * kb
     sel = min(K, pool if pool else n_vis)
     gather = n_attn * B * (sel + W) * D * elt
     queries = B * (H_I * d_I * elt + H_I * F32) * (2 if pool else 1) + n_attn * B * H * D * elt \
@@ -70,15 +72,24 @@ def decode_step_bytes(B: int, n_vis: int, m: int, D: int, H: int, H_I: int, d_I:
     # compressor: m tail rows + the new row for both streams (x, z, xi, zi) read, the new
     # row written to the tails, one entry per stream written, the ring row written
     per_row = (2 * D + 2 * d_I) * elt
-    compress = B * (m * per_row + per_row + (D + d_I) * elt + (D * elt if ring_write else 0)) \
+    compress = B * (m * per_row + per_row + D * elt + kb + (D * elt if ring_write else 0)) \
         + m * (D + d_I) * elt
     return StepBytes(keys, gather, queries, outputs, compress)
 
 
-def scan_bytes(rows: int, n_keys: int, H_I: int, d_I: int, elt: int = BF16) -> int:
-    """Algorithmic bytes of one indexer-scan launch: the keys of every scanned entry plus each
-    row's query and gate (scores are an intermediate and earn nothing)."""
-    return rows * (n_keys * d_I * elt + H_I * d_I * elt + H_I * F32)
+def mxfp4_key_bytes(d_I: int) -> int:
+    """Bytes of one MXFP4 indexer key: a 4-bit code per channel and one scale byte per 32
+    channels ("Rebuilding the model from its constants": 64 bytes of codes per 128-channel key)."""
+    return d_I // 2 + d_I // 32
+
+
+def scan_bytes(rows: int, n_keys: int, H_I: int, d_I: int, elt: int = BF16,
+               key_bytes: int | None = None) -> int:
+    """Algorithmic bytes of one indexer-scan launch: the keys of every scanned entry (d_I * elt
+    each, or key_bytes) plus each row's query and gate (scores are an intermediate and earn
+    nothing)."""
+    kb = d_I * elt if key_bytes is None else key_bytes
+    return rows * (n_keys * kb + H_I * d_I * elt + H_I * F32)
 
 
 def prefill_indexer_flops(sum_visible: int, H_I: int, d_I: int) -> int:

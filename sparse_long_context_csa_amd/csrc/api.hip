@@ -105,9 +105,10 @@ hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, co
                      const int32_t* e_count, const int32_t* cand, int64_t n_cand, int64_t n_seq,
                      int64_t n_q, int64_t e_cap, int H, int d, int m, const TopkWs& ws,
                      hipStream_t s, const IngestArgs* ingest = nullptr, int seg_k = 0,
-                     void* const* kernel_events = nullptr) {
+                     void* const* kernel_events = nullptr, const void* key_scales = nullptr) {
   ScanArgs a{};
   a.dt = dt; a.q = q; a.w = w; a.keys = keys; a.q_pos = q_pos; a.e_count = e_count;
+  a.key_scales = static_cast<const uint8_t*>(key_scales);
   a.cand = cand; a.n_cand = n_cand; a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap;
   a.H = H; a.d = d; a.m = m; a.scores = ws.scores; a.score_stride = ws.stride;
   a.n_vis = ws.n_vis; a.count = ws.count;
@@ -365,6 +366,11 @@ int check_decode_shapes(const csa_decode_desc* d) {
     if (d->block_size > 64 || d->max_blocks < 1 || d->max_blocks > 2048) return CSA_ERR_SHAPE;
     if (int64_t(d->block_size) * d->max_blocks > 32768) return CSA_ERR_UNSUPPORTED;
   }
+  if (d->idx_format != CSA_IDX_DTYPE && d->idx_format != CSA_IDX_MXFP4) return CSA_ERR_SHAPE;
+  if (d->idx_format == CSA_IDX_MXFP4 &&
+      (d->block_size != 0 || !scan_fuses_ingest(d->dtype, d->idx_heads, d->idx_dim, d->m) ||
+       !scan_reads_mxfp4(d->dtype, d->idx_heads, d->idx_dim, 1, false)))
+    return CSA_ERR_UNSUPPORTED;
   return CSA_OK;
 }
 
@@ -377,6 +383,12 @@ int check_decode(const csa_decode_desc* d) {
       !d->q_idx || !d->w || !d->out_idx)
     return CSA_ERR_NULL;
   if (d->block_size > 0 && (!d->q_idx2 || !d->w2)) return CSA_ERR_NULL;
+  if (d->idx_format == CSA_IDX_MXFP4) {
+    if (!d->k_idx_scale) return CSA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(d->k_idx) % 16 != 0 ||
+        reinterpret_cast<uintptr_t>(d->k_idx_scale) % 4 != 0)
+      return CSA_ERR_SHAPE;
+  }
   for (int c = 0; c < d->n_attn; ++c) {
     if (!d->q[c] || !d->out[c]) return CSA_ERR_NULL;
     if (d->window > 0 && !d->win[c]) return CSA_ERR_NULL;
@@ -415,6 +427,8 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   in.x_new = d->x_new; in.z_new = d->z_new; in.xi_new = d->xi_new; in.zi_new = d->zi_new;
   in.x_tail = d->x_tail; in.z_tail = d->z_tail; in.xi_tail = d->xi_tail; in.zi_tail = d->zi_tail;
   in.bias = d->bias; in.bias_i = d->bias_i; in.kv = d->kv; in.k_idx = d->k_idx;
+  void* key_scales = d->idx_format == CSA_IDX_MXFP4 ? d->k_idx_scale : nullptr;
+  in.k_scale = key_scales;
   for (int c2 = 0; c2 < 4; ++c2) {
     in.win[c2] = c2 < d->n_attn ? d->win[c2] : nullptr;
     in.win_new[c2] = (c2 < d->n_attn && d->w_cap > 0) ? d->win_new[c2] : nullptr;
@@ -447,7 +461,7 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   } else {
     if (scan_rows(d->dtype, d->q_idx, d->w, d->k_idx, d->pos, nullptr, nullptr, 0, rows, 1,
                   d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, s, split_ingest,
-                  d->top_k, d->scan_events) != hipSuccess)
+                  d->top_k, d->scan_events, key_scales) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
     const SegArgs seg = segments_for(w.flat, d->dtype, d->idx_heads, d->idx_dim, 1, false, rows,

@@ -23,47 +23,6 @@ namespace {
 constexpr int kPT = 256;          // keys per tile
 static_assert(kPT % 64 == 0, "the score epilogue works on 4 groups of 16 keys at a time");
 
-__device__ __forceinline__ void tile_mfma(const bf16x8_t (&A)[4][4], const bf16x8_t (&B)[4],
-                                          f32x4_t (&acc)[4]) {
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mt][ks], B[ks], acc[mt], 0, 0, 0);
-  }
-}
-
-// Gated ReLU sum over the lane's 16 heads (heads 16 mt + 4 g + i of key col), in two chains.
-__device__ __forceinline__ float lane_part(const f32x4_t (&acc)[4], const float (&wv)[4][4]) {
-  float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < 4; mt += 2)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p0 = fmaf(wv[mt][i], relu_bits(acc[mt][i]), p0);
-      p1 = fmaf(wv[mt + 1][i], relu_bits(acc[mt + 1][i]), p1);
-    }
-  return p0 + p1;
-}
-
-// Head sums of four 16-key groups at once from the lanes' partial sums x0..x3 (each over
-// the lane's 16 heads; the 4 rows of the wave hold the 4 head quarters): a row-half swap
-// adds rows g and g + 2 of two groups into one register (lanes 0-31 one group, 32-63 the
-// other), a row swap then adds rows g and g + 1. Row 0 ends with group 0, row 1 with group
-// 2, row 2 with group 1, row 3 with group 3: six instructions for 64 scores.
-__device__ __forceinline__ float sum_groups4(float x0, float x1, float x2, float x3) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1),
-                                                  false, false);
-  const float s01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x2), __float_as_uint(x3),
-                                                  false, false);
-  const float s23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s01), __float_as_uint(s23),
-                                                  false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
 // Tile layout in LDS: blocks of 4 keys, 1,088 bytes apart; byte 16 l of block b holds the
 // 16-byte chunk l >> 2 of key 4 b + (l & 3) (the layout of one LDS-DMA instruction).
 constexpr int kPTBlocks = kPT / 4;

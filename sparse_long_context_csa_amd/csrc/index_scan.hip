@@ -28,6 +28,7 @@
 #include "index_common.hpp"
 #include "ingest.hpp"
 #include "launch.hpp"
+#include "mxfp4.hpp"
 
 namespace csa {
 
@@ -62,28 +63,35 @@ __device__ __forceinline__ void load_key_B(const uint16_t* row, int g, bf16x8_t 
   }
 }
 
-// Pool the new entry's indexer key from the values a lane holds (channels 2*lane and
-// 2*lane+1 of m rows, the new row in `slot`), store it to the cache, and when `mine` put it
-// into this lane's B operand: channels ks*32 + g*8 .. +8 come from lanes ks*16 + g*4 + 0..3.
+// The wave that scores the entry a decode step completes pools its indexer key from the values
+// a lane holds (channels 2*lane and 2*lane+1 of m rows, the new row in `slot`), stores it to
+// the cache and puts it into the B operand of the key's column (patch_new_key; for an MXFP4
+// cache into the code chunks and scale bytes read for it, patch_new_key_q4).
 constexpr int kFuseM = 8;   // entries of up to 8 rows are pooled this way
 // The pooled indexer key of entry e (row r): the channel-wise softmax over the block's m rows
-// (the new token's row in slot `slot`, the tail's in the others), stored to the cache; lane
-// holds channels 2 lane, 2 lane + 1 of the packed result.
-__device__ __forceinline__ uint32_t fuse_new_key(const IngestArgs& ig, int64_t r, int64_t e,
-                                                 int slot, int lane) {
+// (the new token's row in slot `slot`, the tail's in the others), rounded to bf16; lane holds
+// channels 2 lane, 2 lane + 1 of the packed result. The loads (load_new_key) and the
+// arithmetic (pool_loaded_key) are separate steps, so that a caller can issue the loads
+// before other memory traffic.
+struct NewKeyIn {
+  uint32_t xn, zn, xt[kFuseM], zt[kFuseM], bb[kFuseM];
+};
+__device__ __forceinline__ void load_new_key(const IngestArgs& ig, int64_t r, int slot, int lane,
+                                             NewKeyIn& in) {
   const int m = ig.m;
-  const uint32_t xn = reinterpret_cast<const uint32_t*>(ig.xi_new)[r * (kID / 2) + lane];
-  const uint32_t zn = reinterpret_cast<const uint32_t*>(ig.zi_new)[r * (kID / 2) + lane];
-  uint32_t xt[kFuseM], zt[kFuseM], bb[kFuseM];
+  in.xn = reinterpret_cast<const uint32_t*>(ig.xi_new)[r * (kID / 2) + lane];
+  in.zn = reinterpret_cast<const uint32_t*>(ig.zi_new)[r * (kID / 2) + lane];
 #pragma unroll
   for (int j = 0; j < kFuseM; ++j) {
-    xt[j] = zt[j] = bb[j] = 0u;
+    in.xt[j] = in.zt[j] = in.bb[j] = 0u;
     if (j < m && j != slot) {
-      xt[j] = reinterpret_cast<const uint32_t*>(ig.xi_tail)[(r * m + j) * (kID / 2) + lane];
-      zt[j] = reinterpret_cast<const uint32_t*>(ig.zi_tail)[(r * m + j) * (kID / 2) + lane];
+      in.xt[j] = reinterpret_cast<const uint32_t*>(ig.xi_tail)[(r * m + j) * (kID / 2) + lane];
+      in.zt[j] = reinterpret_cast<const uint32_t*>(ig.zi_tail)[(r * m + j) * (kID / 2) + lane];
     }
-    if (j < m) bb[j] = reinterpret_cast<const uint32_t*>(ig.bias_i)[j * (kID / 2) + lane];
+    if (j < m) in.bb[j] = reinterpret_cast<const uint32_t*>(ig.bias_i)[j * (kID / 2) + lane];
   }
+}
+__device__ __forceinline__ uint32_t pool_loaded_key(const NewKeyIn& in, int m, int slot) {
   float res[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -95,7 +103,7 @@ __device__ __forceinline__ uint32_t fuse_new_key(const IngestArgs& ig, int64_t r
     for (int j = 0; j < kFuseM; ++j) {
       av[j] = neg_inf();
       if (j < m) {
-        av[j] = half(j == slot ? zn : zt[j]) + half(bb[j]);
+        av[j] = half(j == slot ? in.zn : in.zt[j]) + half(in.bb[j]);
         mx = fmaxf(mx, av[j]);
       }
     }
@@ -105,17 +113,51 @@ __device__ __forceinline__ uint32_t fuse_new_key(const IngestArgs& ig, int64_t r
       if (j < m) {
         const float ex = expf(av[j] - mx);
         sum += ex;
-        acc = fmaf(ex, half(j == slot ? xn : xt[j]), acc);
+        acc = fmaf(ex, half(j == slot ? in.xn : in.xt[j]), acc);
       }
     res[h] = acc / sum;
   }
-  const uint32_t pk = uint32_t(f32_to_bf16(res[0])) | (uint32_t(f32_to_bf16(res[1])) << 16);
+  return uint32_t(f32_to_bf16(res[0])) | (uint32_t(f32_to_bf16(res[1])) << 16);
+}
+__device__ __forceinline__ uint32_t pool_new_key(const IngestArgs& ig, int64_t r, int slot,
+                                                 int lane) {
+  NewKeyIn in;
+  load_new_key(ig, r, slot, lane, in);
+  return pool_loaded_key(in, ig.m, slot);
+}
+
+// bf16 cache: the pooled key is stored as it is
+__device__ __forceinline__ uint32_t store_new_key(const IngestArgs& ig, int64_t r, int64_t e,
+                                                  uint32_t pk, int lane) {
   reinterpret_cast<uint32_t*>(ig.k_idx)[(r * ig.e_cap + e) * (kID / 2) + lane] = pk;
   return pk;
+}
+__device__ __forceinline__ uint32_t fuse_new_key(const IngestArgs& ig, int64_t r, int64_t e,
+                                                 int slot, int lane) {
+  return store_new_key(ig, r, e, pool_new_key(ig, r, slot, lane), lane);
+}
+
+// MXFP4 cache: the pooled (bf16) key is quantised as csa_quantize_mxfp4 does it -- block b =
+// channels 32 b .. 32 b + 31 = lanes 16 b .. 16 b + 15, whose maximum is a 16-lane DPP maximum
+// of the magnitudes' bits -- and stored (lane l writes code byte l, lane 16 b the scale byte of
+// block b). Returns code byte l in bits 0-7 and the scale byte of the lane's block in bits 8-15.
+__device__ __forceinline__ uint32_t store_new_key_q4(const IngestArgs& ig, int64_t r, int64_t e,
+                                                     uint32_t pk, int lane) {
+  const float lo = bf16_to_f32(uint16_t(pk & 0xffffu)), hi = bf16_to_f32(uint16_t(pk >> 16));
+  const uint32_t am = max16_key(__builtin_elementwise_max(__float_as_uint(fabsf(lo)),
+                                                          __float_as_uint(fabsf(hi))));
+  const int s = mx_shared_exp(__uint_as_float(am));
+  const uint32_t code = e2m1_code(ldexpf(lo, -s)) | (e2m1_code(ldexpf(hi, -s)) << 4);
+  const uint32_t sb = uint32_t(s + 127);
+  const int64_t key = r * ig.e_cap + e;
+  static_cast<uint8_t*>(ig.k_idx)[key * (kID / 2) + lane] = uint8_t(code);
+  if ((lane & 15) == 0) static_cast<uint8_t*>(ig.k_scale)[key * (kID / 32) + (lane >> 4)] = uint8_t(sb);
+  return code | (sb << 8);
 }
 
 // The B operand of the lanes that hold the new entry's key (mine: its column) from the packed
 // key pk (channels 2 l, 2 l + 1 in lane l): the tile was loaded before the key was written.
+// Lane (g, col) of k-step ks holds channels ks*32 + g*8 .. +8, from lanes ks*16 + g*4 + 0..3.
 __device__ __forceinline__ void patch_new_key(uint32_t pk, int g, bool mine, bf16x8_t (&B)[4]) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -408,9 +450,131 @@ __device__ __forceinline__ void read_tile_B(const unsigned char* slot, int g, in
 }
 #undef CSA_TILE_READ
 
-template <bool NT, bool kSeg, int kSD>
-__global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk, int64_t cpr,
+// ---- MXFP4 keys: 64-key tiles ---------------------------------------------------------------
+// Keys as csa_quantize_mxfp4 stores them: 64 code bytes per key (element 2i in the low nibble
+// of byte i) and 4 scale bytes (one per 32 channels). A wave's tile is 64 keys: 4 KiB of codes
+// by four global_load_lds_dwordx4 (one per 16-key group) and the 256 scale bytes by one
+// global_load_lds_dword -- the LDS footprint of a bf16 tile, four times the keys. In the MFMA
+// lane (g, col) of k-step ks takes channels 32 g + 8 ks .. + 8, so a lane's four k-steps are one
+// 16-byte chunk of key col's codes (chunk g) under one scale (block g); the query operand takes
+// the same channel order (load_query_A_q4). Chunk g of key col of a group sits in 16-byte slot
+// 4 col + ((col >> 2) + g) % 4: the 16 lanes of a quarter-wave (one g) read 16 distinct slots
+// mod 16. Dequantisation is exact (an E2M1 value times a power of two is a bf16 value) by
+// v_cvt_scalef32_pk_bf16_fp4, whose result holds the low nibble's value in its low half.
+constexpr int kQ4Keys = 64;
+constexpr int kQ4Codes = kQ4Keys * kID / 2;   // 4,096 code bytes, then 256 scale bytes
+static_assert(kQ4Codes + kQ4Keys * kID / 32 <= kTileLds, "an MXFP4 tile fits a ring slot");
+
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+// A operand of one query in the MXFP4 channel order: heads 16*mt + (lane&15), channels
+// 32 g + 8 ks .. + 8 (g = lane >> 4)
+__device__ __forceinline__ void load_query_A_q4(const uint16_t* q, int lane, bf16x8_t (&A)[4][4]) {
+  const int g = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const uint16_t* p = q + (16 * mt + col) * kID + g * 32;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) A[mt][ks] = *reinterpret_cast<const bf16x8_t*>(p + ks * 8);
+  }
+}
+
+// codes of key tb + 16 i + (lane >> 2), chunk ((lane & 3) - (lane >> 4)) % 4, into slot byte
+// 1024 i + 16 lane; scales of key tb + lane into byte 4096 + 4 lane. Keys at or past lim read
+// the item's last key (discarded).
+template <bool NT>
+__device__ __forceinline__ void issue_tile_q4(const uint8_t* cb, const uint8_t* sb, int64_t tb,
+                                              int64_t lim, unsigned char* slot, int lane) {
+  const int kc = lane >> 2;
+  const int ch = ((lane & 3) - (kc >> 2)) & 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int64_t key = tb + 16 * i + kc;
+    key = key < lim ? key : lim - 1;
+    __builtin_amdgcn_global_load_lds(cb + key * (kID / 2) + ch * 16,
+                                     (lds_void*)(slot + i * 1024), 16, 0, NT ? 2 : 0);
+  }
+  int64_t key = tb + lane;
+  key = key < lim ? key : lim - 1;
+  __builtin_amdgcn_global_load_lds(sb + key * (kID / 32), (lds_void*)(slot + kQ4Codes), 4, 0,
+                                   NT ? 2 : 0);
+}
+
+// The codes chunk and scale byte of this lane for the four 16-key groups of the tile in `slot`,
+// once at most 5 n tile loads of this wave are outstanding (n tiles issued after this one).
+#define CSA_Q4_READ(VM)                                                                      \
+  asm volatile("s_waitcnt vmcnt(" #VM ")\n\t"                                               \
+               "ds_read_b128 %0, %8\n\t"                                                    \
+               "ds_read_b128 %1, %8 offset:1024\n\t"                                        \
+               "ds_read_b128 %2, %8 offset:2048\n\t"                                        \
+               "ds_read_b128 %3, %8 offset:3072\n\t"                                        \
+               "ds_read_u8 %4, %9\n\t"                                                      \
+               "ds_read_u8 %5, %9 offset:64\n\t"                                            \
+               "ds_read_u8 %6, %9 offset:128\n\t"                                           \
+               "ds_read_u8 %7, %9 offset:192\n\t"                                           \
+               "s_waitcnt lgkmcnt(0)"                                                       \
+               : "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(cw[2]), "=&v"(cw[3]), "=&v"(sc[0]),     \
+                 "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(sc[3])                                   \
+               : "v"(caddr), "v"(saddr)                                                     \
+               : "memory")
+__device__ __forceinline__ void read_tile_q4(const unsigned char* slot, int g, int col, int n,
+                                             u32x4_t (&cw)[4], uint32_t (&sc)[4]) {
+  typedef const __attribute__((address_space(3))) unsigned char* lds_cptr;
+  const uint32_t caddr = uint32_t(size_t((lds_cptr)(slot + 16 * (4 * col + (((col >> 2) + g) & 3)))));
+  const uint32_t saddr = uint32_t(size_t((lds_cptr)(slot + kQ4Codes + 4 * col + g)));
+  switch (__builtin_amdgcn_readfirstlane(n)) {
+    case 0: CSA_Q4_READ(0); break;
+    case 1: CSA_Q4_READ(5); break;
+    case 2: CSA_Q4_READ(10); break;
+    default: CSA_Q4_READ(15); break;
+  }
+}
+#undef CSA_Q4_READ
+
+// B operand (bf16) of one 16-key group from this lane's code chunk and scale byte (a scale
+// byte of 0 is 2^-127, a subnormal float)
+__device__ __forceinline__ void dequant_B(const u32x4_t cw, uint32_t sbyte, bf16x8_t (&B)[4]) {
+  const float s = __uint_as_float(sbyte ? sbyte << 23 : 0x00400000u);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t w = cw[ks];
+    uint32_t o[4];
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
+    B[ks] = __builtin_bit_cast(bf16x8_t, o);
+  }
+}
+
+// The code chunk and scale byte of the lanes that hold the new entry (its group and column,
+// from its offset off in the tile): the tile was loaded before the entry was written. v holds
+// code byte l of the entry in lane l and the scale byte of the lane's block; lane (g, col)
+// takes bytes 16 g .. 16 g + 15 (lanes 16 g + 4 ks + k) and the scale of block g, its own.
+__device__ __forceinline__ void patch_new_key_q4(uint32_t v, int off, int g, int col,
+                                                 u32x4_t (&cw)[4], uint32_t (&sc)[4]) {
+  u32x4_t w;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint32_t x = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x |= (uint32_t(__shfl(int(v), g * 16 + ks * 4 + k)) & 0xffu) << (8 * k);
+    w[ks] = x;
+  }
+  const bool mine = col == (off & 15);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (mine && j == (off >> 4)) {
+      cw[j] = w;
+      sc[j] = v >> 8;
+    }
+}
+
+// kQ4: MXFP4 keys (a.key_scales), 64-key tiles; else bf16 keys, 16-key tiles.
+template <bool NT, bool kSeg, int kSD, bool kQ4>
+__global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chunk, int64_t cpr,
                                                           int64_t n_items, int rot) {
+  constexpr int kTK = kQ4 ? kQ4Keys : 16;   // keys per wave tile
   __shared__ __attribute__((aligned(16))) unsigned char ring[4][kSD][kTileLds];
   __shared__ SegLds segl;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -423,69 +587,124 @@ __global__ __launch_bounds__(256) void scan_stream_kernel(ScanArgs a, int chunk,
     const int64_t r = it / cpr, c = it % cpr;
     const int64_t sq = r / a.n_q;
     const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.keys) + sq * a.e_cap * kID;
+    const uint8_t* cb = reinterpret_cast<const uint8_t*>(a.keys) + sq * a.e_cap * (kID / 2);
+    const uint8_t* sb = a.key_scales + sq * a.e_cap * (kID / 32);
     const int64_t c0 = c * chunk;
     const int64_t lim = c0 + chunk < a.e_cap ? c0 + chunk : a.e_cap;
-    // the first tiles go out before the row's visible count is known. Wave w takes the
-    // 16-key tiles w, w + 4, ... of the item in the order that starts at tile `r0` (a per-block
-    // rotation, so that blocks do not walk memory in step)
-    const int64_t t0 = c0 + wave * 16;
-    const int nt_item = int((lim - t0 + 63) / 64);   // tiles of this wave in the item
+    // wave w takes the tiles w, w + 4, ... of the item in the order that starts at tile `r0`
+    // (a per-block rotation, so that blocks do not walk memory in step)
+    const int64_t t0 = c0 + wave * kTK;
+    const int nt_item = int((lim - t0 + 4 * kTK - 1) / (4 * kTK));   // tiles of this wave
     const int r0 = nt_item > 0 ? int((int64_t(blockIdx.x) * rot) % nt_item) : 0;
     auto tile_base = [&](int t) -> int64_t {
       int u = t + r0;
       u = u >= nt_item ? u - nt_item : u;
-      return t0 + int64_t(u) * 64;
+      return t0 + int64_t(u) * (4 * kTK);
     };
+    auto issue = [&](int t, unsigned char* slot) {
+      if (kQ4) issue_tile_q4<NT>(cb, sb, tile_base(t), lim, slot, lane);
+      else issue_tile<NT>(kb, tile_base(t), lim, slot, lane);
+    };
+    // The row's visible count, query and gates, and the inputs of the entry this step's token
+    // completes (pooled by the wave that scores it), are loaded before the first tiles: a wave's
+    // loads return in issue order, so loads issued after the tiles would wait for them.
+    const int64_t n_pos = row_visible(a, r);
+    if (r != cur) {
+      const uint16_t* qr = reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID;
+      if (kQ4) load_query_A_q4(qr, lane, A);
+      else load_query_A(qr, lane, A);
+      load_gates(a.w + r * kIH, lane, wv);
+      cur = r;
+    }
+    const int64_t c1 = lim < n_pos ? lim : n_pos;
+    int64_t e_new = -1;
+    int new_slot = 0;
+    NewKeyIn nk;
+    if (fuse && c0 < c1) {
+      const int64_t t = a.ingest.pos[r];
+      const int64_t e = (t + 1) / a.ingest.m - 1;
+      if (t >= 0 && (t + 1) % a.ingest.m == 0 && e >= c0 && e < c1 &&
+          int((e - c0) / kTK) % 4 == wave) {
+        e_new = e;
+        new_slot = int(t % a.ingest.m);
+        load_new_key(a.ingest, r, new_slot, lane, nk);
+      }
+    }
     int issued = 0;
 #pragma unroll
     for (int j = 0; j < kSD; ++j) {
       if (j < nt_item) {
-        issue_tile<NT>(kb, tile_base(j), lim, ring[wave][j], lane);
+        issue(j, ring[wave][j]);
         ++issued;
       }
     }
-    // the row's query and gates load together with its visible count (not after it): the
-    // first tile's MFMAs then wait for one round trip, not two
-    if (r != cur) {
-      load_query_A(reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID, lane, A);
-      load_gates(a.w + r * kIH, lane, wv);
-      cur = r;
-    }
-    const int64_t n_pos = row_visible(a, r);
     if (c == 0 && threadIdx.x == 0) {
       a.n_vis[r] = int32_t(n_pos);
       a.count[r] = int32_t(n_pos);
     }
-    const int64_t c1 = lim < n_pos ? lim : n_pos;
     if (c0 < c1) {
-      // the entry this step's token completes is pooled (before the tile loop, its loads
-      // beside the query's) by the wave that scores it
-      int64_t e_new = -1;
       uint32_t pk_new = 0u;
-      if (fuse) {
-        const int64_t t = a.ingest.pos[r];
-        const int64_t e = (t + 1) / a.ingest.m - 1;
-        if (t >= 0 && (t + 1) % a.ingest.m == 0 && e >= c0 && e < c1 &&
-            int((e - c0) >> 4) % 4 == wave) {
-          e_new = e;
-          pk_new = fuse_new_key(a.ingest, r, e, int(t % a.ingest.m), lane);
-        }
+      if (e_new >= 0) {
+        const uint32_t pk = pool_loaded_key(nk, a.ingest.m, new_slot);
+        pk_new = kQ4 ? store_new_key_q4(a.ingest, r, e_new, pk, lane)
+                     : store_new_key(a.ingest, r, e_new, pk, lane);
       }
       // every tile of the item is loaded (in order), so the counts of the waits are exact;
       // tiles past the visible range are not scored
       for (int t = 0; t < nt_item; ++t) {
         const int64_t tb = tile_base(t);
         unsigned char* slot = ring[wave][t % kSD];
-        bf16x8_t B[4];
-        read_tile_B(slot, g, col, issued - t - 1, B);
-        if (tb < c1) {
-          if (e_new >= tb && e_new < tb + 16) patch_new_key(pk_new, g, col == int(e_new - tb), B);
-          const float sc = tile_score(A, B, wv);
-          const int64_t p = tb + col;
-          if (g == 0 && p < c1) segl.sc[p - c0] = sc;
+        if constexpr (kQ4) {
+          u32x4_t cw[4];
+          uint32_t sc4[4];
+          read_tile_q4(slot, g, col, issued - t - 1, cw, sc4);
+          if (tb < c1) {
+            if (e_new >= tb && e_new < tb + kQ4Keys)
+              patch_new_key_q4(pk_new, int(e_new - tb), g, col, cw, sc4);
+            // group j's MFMAs go out (into the other accumulator set) before the epilogue of
+            // group j - 1, so the matrix pipe works while the VALU reduces; the head sums of
+            // the four groups finish together (sum_groups4). Groups past the visible range
+            // are scored too (their keys are the item's last one) and not stored.
+            f32x4_t acc[2][4];
+            float scb[4];
+            bf16x8_t B[4];
+            dequant_B(cw[0], sc4[0], B);
+            tile_mfma(A, B, acc[0]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (j + 1 < 4) {
+                dequant_B(cw[j + 1], sc4[j + 1], B);
+                tile_mfma(A, B, acc[(j + 1) & 1]);
+              }
+              scb[j] = lane_part(acc[j & 1], wv);
+              if (j + 1 < 4) {
+                // issue order: the next group's 16 conversions, then each of its 16 MFMAs
+                // followed by two VALU instructions of this group's epilogue
+                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                  __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                }
+              }
+            }
+            const float sv = sum_groups4(scb[0], scb[1], scb[2], scb[3]);
+            const int64_t p = tb + 16 * ((g & 1) * 2 + (g >> 1)) + col;   // row g: group grp
+            if (p < c1) segl.sc[p - c0] = sv;
+          }
+        } else {
+          bf16x8_t B[4];
+          read_tile_B(slot, g, col, issued - t - 1, B);
+          if (tb < c1) {
+            if (e_new >= tb && e_new < tb + 16)
+              patch_new_key(pk_new, g, col == int(e_new - tb), B);
+            const float sc = tile_score(A, B, wv);
+            const int64_t p = tb + col;
+            if (g == 0 && p < c1) segl.sc[p - c0] = sc;
+          }
         }
         if (t + kSD < nt_item) {
-          issue_tile<NT>(kb, tile_base(t + kSD), lim, slot, lane);
+          issue(t + kSD, slot);
           ++issued;
         }
       }
@@ -574,7 +793,7 @@ static bool fast_shape(const ScanArgs& a) { return a.dt == kBF16 && a.H == kIH &
 // Decode-scan launch shape: positions per work item, key tiles in flight per wave beyond the
 // current one, and blocks resident per CU (the persistent grid is n_cu * blocks_per_cu).
 struct ScanTune {
-  int chunk = 2048, pf = 1, blocks_per_cu = 2, nt = 1, sd = 2, rot = 0;
+  int chunk = 2048, pf = 1, blocks_per_cu = 2, nt = 1, sd = 2, sd4 = 3, rot = 0;
   int prefill_q = 12, prefill_keys = 4096;
 };
 static int env_int(const char* name, int dflt) {
@@ -589,6 +808,7 @@ static const ScanTune& scan_tune() {
     x.blocks_per_cu = env_int("CSA_TUNE_SCAN_BPC", x.blocks_per_cu);
     x.nt = env_int("CSA_TUNE_SCAN_NT", x.nt);
     x.sd = env_int("CSA_TUNE_SCAN_SD", x.sd);
+    x.sd4 = env_int("CSA_TUNE_SCAN_SD4", x.sd4);
     x.rot = env_int("CSA_TUNE_SCAN_ROT", x.rot);
     x.prefill_q = env_int("CSA_TUNE_PREFILL_Q", x.prefill_q);
     x.prefill_keys = (env_int("CSA_TUNE_PREFILL_KEYS", x.prefill_keys) + 127) / 128 * 128;
@@ -676,11 +896,41 @@ bool scan_fuses_ingest(int dt, int H, int d, int m) {
   return dt == kBF16 && H == kIH && d == kID && m <= kFuseM;
 }
 
+bool scan_reads_mxfp4(int dt, int H, int d, int64_t n_q, bool cand) {
+  return dt == kBF16 && H == kIH && d == kID && n_q < 16 && !cand;
+}
+
+template <bool kQ4>
+static void launch_stream(const ScanArgs& a, int chunk, int64_t cpr, int64_t items, hipStream_t s,
+                          hipEvent_t e0, hipEvent_t e1) {
+  int64_t grid = scan_grid();
+  if (grid > items) grid = items;
+  const dim3 gd(static_cast<unsigned>(grid)), bd(256);
+  const int rot = scan_tune().rot;
+  const int sd = kQ4 ? scan_tune().sd4 : scan_tune().sd;
+  const bool segs = a.seg.seg != nullptr;
+#define CSA_STREAM(SEG, SD)                                                                  \
+  launch_k(scan_stream_kernel<true, SEG, SD, kQ4>, gd, bd, 0, s, e0, e1, a, chunk, cpr, items, rot)
+  if (segs) {
+    if (sd == 2) CSA_STREAM(true, 2);
+    else if (sd == 3) CSA_STREAM(true, 3);
+    else CSA_STREAM(true, 4);
+  } else {
+    if (sd == 2) CSA_STREAM(false, 2);
+    else if (sd == 3) CSA_STREAM(false, 3);
+    else CSA_STREAM(false, 4);
+  }
+#undef CSA_STREAM
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int64_t rows = a.n_seq * a.n_q;
   if (rows == 0) return hipSuccess;
   const int64_t max_pos = a.cand ? a.n_cand : a.e_cap;
-  if (fast_shape(a) && a.cand == nullptr && a.n_q >= 16) {
+  const bool q4 = a.key_scales != nullptr;
+  if (q4 && !scan_reads_mxfp4(a.dt, a.H, a.d, a.n_q, a.cand != nullptr))
+    return hipErrorInvalidValue;
+  if (!q4 && fast_shape(a) && a.cand == nullptr && a.n_q >= 16) {
     const int keys_per_block = scan_tune().prefill_keys;
     const int pq = scan_tune().prefill_q == 8 ? 8 : 12;
     const int64_t groups = a.n_seq * ((a.n_q + pq - 1) / pq);
@@ -692,28 +942,12 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s, hipEvent_t e0, hipEvent
     if (a.cand) {
       launch_decode_pf<true, false>(a, rows, max_pos, s, e0, e1);
     } else {
-      const bool segs = a.seg.seg != nullptr;
-      const int chunk = segs ? a.seg.chunk : decode_scan_chunk(rows, max_pos, true);
+      const int chunk = a.seg.seg ? a.seg.chunk : decode_scan_chunk(rows, max_pos, true);
       if (chunk > kSegMaxChunk) return hipErrorInvalidValue;
       const int64_t cpr = (max_pos + chunk - 1) / chunk;
       const int64_t items = rows * cpr;
-      int64_t grid = scan_grid();
-      if (grid > items) grid = items;
-      const dim3 gd(static_cast<unsigned>(grid)), bd(256);
-      const int rot = scan_tune().rot;
-      const int sd = scan_tune().sd;
-#define CSA_STREAM(SEG, SD)                                                                  \
-  launch_k(scan_stream_kernel<true, SEG, SD>, gd, bd, 0, s, e0, e1, a, chunk, cpr, items, rot)
-      if (segs) {
-        if (sd == 2) CSA_STREAM(true, 2);
-        else if (sd == 3) CSA_STREAM(true, 3);
-        else CSA_STREAM(true, 4);
-      } else {
-        if (sd == 2) CSA_STREAM(false, 2);
-        else if (sd == 3) CSA_STREAM(false, 3);
-        else CSA_STREAM(false, 4);
-      }
-#undef CSA_STREAM
+      if (q4) launch_stream<true>(a, chunk, cpr, items, s, e0, e1);
+      else launch_stream<false>(a, chunk, cpr, items, s, e0, e1);
     }
     return hipGetLastError();
   }

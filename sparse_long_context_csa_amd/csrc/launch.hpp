@@ -23,6 +23,7 @@ struct IngestArgs {
   void *x_tail, *z_tail, *xi_tail, *zi_tail;
   const void *bias, *bias_i;
   void *kv, *k_idx;
+  void* k_scale;          // non-null: k_idx holds MXFP4 codes, k_scale their scale bytes
   void* win[4];
   const void* win_new[4];
 };
@@ -61,7 +62,8 @@ struct ScanArgs {
   int dt;
   const void* q;          // [rows, H, d]
   const float* w;         // [rows, H]
-  const void* keys;       // [n_seq, e_cap, d]
+  const void* keys;       // [n_seq, e_cap, d]; MXFP4 codes [n_seq, e_cap, d / 2] when
+  const uint8_t* key_scales;  // ... key_scales [n_seq, e_cap, d / 32] is non-null
   const int64_t* q_pos;   // [rows]
   const int32_t* e_count; // [n_seq] or null
   const int32_t* cand;    // [rows, n_cand] or null
@@ -90,6 +92,9 @@ hipError_t launch_scan_prefill(const ScanArgs& a, int pq, int keys_per_block, di
                                hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 // Whether the decode scan for this shape takes the indexer-key part of the ingest.
 bool scan_fuses_ingest(int dt, int H, int d, int m);
+// Whether the scan reads MXFP4 keys for this shape (bf16 queries, 64 heads x 128, one or a few
+// query rows per sequence, no candidate list).
+bool scan_reads_mxfp4(int dt, int H, int d, int64_t n_q, bool cand);
 
 // ---- MXFP4 storage of indexer keys (mxfp4.hpp) --------------------------------------------
 // x [n_rows, dim] (dim % 32 == 0) -> codes [n_rows, dim / 2] bytes, scales [n_rows, dim / 32]

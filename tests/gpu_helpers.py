@@ -7,7 +7,7 @@ import torch
 import datagen
 import sparse_long_context_csa_amd as csa_lib
 from oracle import csa as ocsa
-from oracle import gaps
+from oracle import gaps, mx
 from oracle.pipeline import f64, i64
 
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
@@ -94,6 +94,34 @@ def assert_pooled(got, exact, xabs_max, what=""):
         raise AssertionError(f"{what}: pooled value {got[k]} vs exact {exact[k]} (tol {tol[k]:.3e})")
 
 
+def assert_mx_entry(codes, scales, exact, xabs_max, what=""):
+    """The MXFP4 form of a pooled key. The oracle's cached key is quantise(round_bf16(exact));
+    the GPU rounds its fp32 pooling to bf16, which can land on the other bf16 neighbour only
+    where exact lies within the fp32 error (4e-6 max_j |x_j|) of a rounding midpoint. Blocks
+    without such an element must match the oracle's codes and scale byte exactly; the others
+    must hold a valid MXFP4 rounding of a value within that error: off by at most half an E2M1
+    gap (at most 2^s) or, for magnitudes past 6 x 2^s, by the saturation to 6 x 2^s, plus one
+    bf16 spacing."""
+    kb = ocsa.store(exact, "bf16")
+    tol = 4e-6 * np.asarray(xabs_max)
+    near_mid = np.abs(exact - kb) >= 0.5 * bf16_ulp(kb) - tol
+    oc, osc = mx.quantize(kb)
+    gc = mx.unpack(np.asarray(codes, dtype=np.uint8))
+    gs = np.asarray(scales, dtype=np.uint8)
+    deq = mx.dequantize(gc, gs)
+    for blk in range(gs.size):
+        sl = slice(32 * blk, 32 * blk + 32)
+        if not near_mid[sl].any():
+            assert gs[blk] == osc[blk] and np.array_equal(gc[sl], oc[sl]), \
+                f"{what}: block {blk} codes/scale differ from the oracle's"
+            continue
+        step = 2.0 ** (float(gs[blk]) - 127)
+        assert abs(int(gs[blk]) - int(osc[blk])) <= 1, f"{what}: block {blk} scale"
+        err = np.abs(deq[sl] - exact[sl])
+        bound = np.maximum(step, np.abs(exact[sl]) - 6 * step)
+        assert np.all(err <= bound + bf16_ulp(kb[sl]) + tol[sl]), f"{what}: block {blk} values"
+
+
 def pooled_xmax(x, m):
     """max_j |x[e*m + j, c]| per (entry, channel) of rows x [..., T, d]."""
     a = np.abs(np.asarray(x, dtype=np.float64))
@@ -101,7 +129,25 @@ def pooled_xmax(x, m):
     return a.reshape(sh[:-2] + (sh[-2] // m, m, sh[-1])).max(axis=-2)
 
 
-def run_step(case):
+def mxfp4_case(spec):
+    """A decode case with an MXFP4 indexer cache. The oracle's case holds the MXFP4 values of
+    the generated bf16 keys (oracle quantiser); the GPU gets the codes and scale bytes that
+    csa_quantize_mxfp4 makes of the same bf16 keys (returned, on the device)."""
+    case = datagen.make_case(spec)
+    k = case["k_idx"]
+    codes, scales = mx.quantize(f64(k))
+    case["k_idx"] = torch.from_numpy(mx.dequantize(codes, scales)).to(k.dtype)
+    case["idx_format"] = "mxfp4"
+    kc, ks = csa_lib.quantize_mxfp4(dev(k))
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), mx.pack(codes))
+    assert np.array_equal(ks.cpu().numpy(), scales)
+    return case, {"k_idx": kc, "k_idx_scale": ks}
+
+
+def run_step(case, idx_state=None):
+    """One csa_decode_step over copies of the case's state (idx_state: the MXFP4 indexer cache
+    {"k_idx": codes, "k_idx_scale": scales} on the device, replacing case["k_idx"])."""
     spec = case["spec"]
     g = {k: dev(v) for k, v in case.items() if isinstance(v, torch.Tensor)}
     rings = [dev(r).clone() for r in case["rings"]]
@@ -112,6 +158,8 @@ def run_step(case):
         kw = dict(block_size=spec.block_size, max_blocks=spec.max_blocks, q_idx2=g["q_idx2"],
                   w2=g["w2"])
     st = {k: g[k].clone() for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
+    if idx_state is not None:
+        st.update({k: v.clone() for k, v in idx_state.items()})
     step = csa_lib.DecodeStep(m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
                           pos=g["pos"], x_new=g["x_new"], z_new=g["z_new"], xi_new=g["xi_new"],
                           zi_new=g["zi_new"], bias=g["bias"], bias_i=g["bias_i"],
@@ -142,6 +190,11 @@ def check_step(case, ref, st, rings, out, idx):
                 x[slot] = f64(case[xn][b])
                 z[slot] = f64(case[zn][b])
                 exact = ocsa.compress(x, z, f64(case[bias]), spec.m)[0]
+                if name == "k_idx" and case.get("idx_format") == "mxfp4":
+                    assert_mx_entry(st["k_idx"][b, e].cpu().numpy(),
+                                    st["k_idx_scale"][b, e].cpu().numpy(), exact,
+                                    np.abs(x).max(axis=0), f"MXFP4 key entry {e} of seq {b}")
+                    continue
                 assert_pooled(f64(st[name][b, e].cpu()), exact, np.abs(x).max(axis=0),
                               f"{name} entry {e} of seq {b}")
         if datagen.ring_from_raw(spec):

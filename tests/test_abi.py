@@ -84,9 +84,11 @@ def test_decode_desc_mirrors_the_header_struct():
     assert int(m.group(1)) == _lib.DECODE_EVENTS
     # natural C layout on x86-64: 12 int32 and 2 int64 (64 B), the float padded to 8 B, then
     # 17 tensor pointers, 5 arrays of CSA_MAX_ATTN pointers, out_idx, the phase events, the
-    # scan kernel's start and stop events
+    # scan kernel's start and stop events; idx_format padded to 8 B and k_idx_scale
     n_ptr = 17 + 5 * _lib.MAX_ATTN + 1 + _lib.DECODE_EVENTS + 2
-    assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr
+    assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr + 8 + 8
+    for name, val in (("CSA_IDX_DTYPE", _lib.IDX_DTYPE), ("CSA_IDX_MXFP4", _lib.IDX_MXFP4)):
+        assert int(re.search(rf"#define\s+{name}\s+(\d+)", _header()).group(1)) == val
 
 
 def test_compress_validation(lib):
@@ -171,6 +173,44 @@ def test_decode_validation(lib):
             getattr(full, name)[0] = 16
     full.scan_events[0] = 16
     assert lib.csa_decode_step(C.byref(full), C.c_void_p(16), nb, None) == -1
+    full.scan_events[0] = 0
+
+
+def test_decode_mxfp4_validation(lib):
+    def full(**kw):
+        d = _desc(**{"idx_format": _lib.IDX_MXFP4, **kw})
+        for name, typ in _lib.DecodeDesc._fields_:
+            if typ is C.c_void_p:
+                setattr(d, name, 256)
+            elif name in ("q", "win", "win_new", "sink", "out"):
+                getattr(d, name)[0] = 256
+        d.scan_events[0] = d.scan_events[1] = None
+        for i in range(_lib.DECODE_EVENTS):
+            d.events[i] = None
+        return d
+
+    nb = lib.csa_decode_step_workspace_size(C.byref(_desc()))
+    ws = C.c_void_p(256)
+
+    def step(d):
+        return lib.csa_decode_step(C.byref(d), ws, nb, None)
+
+    # every call below is refused before anything is launched
+    assert step(full(idx_format=2)) == -2
+    assert step(full(block_size=8, max_blocks=64)) == -4      # hierarchical: not with MXFP4
+    assert step(full(m=16)) == -4                             # the scan pools m <= 8 only
+    assert step(full(idx_dim=64)) == -4
+    assert step(full(dtype=0)) == -4                          # fp32 step
+    d = full()
+    d.k_idx_scale = None
+    assert step(d) == -1
+    d = full()
+    d.k_idx = 256 + 8                                         # codes not 16-byte aligned
+    assert step(d) == -2
+    d = full()
+    d.k_idx_scale = 256 + 2
+    assert step(d) == -2
+    assert lib.csa_decode_step_workspace_size(C.byref(full(m=16))) == 0
 
 
 def test_binding_raises_on_errors(lib):

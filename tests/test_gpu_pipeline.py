@@ -6,7 +6,7 @@ import torch
 
 import datagen
 import sparse_long_context_csa_amd as csa
-from gpu_helpers import assert_ids, assert_rows_close, check_step, dev, run_step
+from gpu_helpers import assert_ids, assert_rows_close, check_step, dev, mxfp4_case, run_step
 from oracle import csa as ocsa
 from oracle import gaps, pipeline
 from oracle.pipeline import f64
@@ -121,6 +121,34 @@ def test_decode_step_segments_odd_k_and_window():
     ref = pipeline.decode_step(case)
     _, st, rings, out, idx = run_step(case)
     check_step(case, ref, st, rings, out, idx)
+
+
+# MXFP4 indexer cache: the scan dequantises 64-key tiles of codes and scale bytes; the entry a
+# step completes is pooled, quantised and stored by the scan.
+@pytest.mark.parametrize("spec", [
+    datagen.CaseSpec(7120, "decode", B=5, L=24000, m=4, w_cap=256, ragged=True),
+    datagen.CaseSpec(7121, "decode", B=3, L=4 * 60000, m=4, w_cap=256, ragged=True),
+    datagen.CaseSpec(7122, "decode", B=4, L=2400, e_cap=40000, m=4, w_cap=128, ragged=True),
+    datagen.CaseSpec(7123, "decode", B=3, L=20000, m=1, w_cap=128, ragged=True),
+], ids=["flat", "segments", "short_rows", "m1"])
+def test_decode_step_mxfp4_keys(spec):
+    case, idx_state = mxfp4_case(spec)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    step, st, rings, out, idx = run_step(case, idx_state)
+    check_step(case, ref, st, rings, out, idx)
+    # entries the step did not complete are untouched
+    for b in range(spec.B):
+        t = int(case["pos"][b])
+        keep = np.ones(st["k_idx"].shape[1], bool)
+        if (t + 1) % spec.m == 0:
+            keep[(t + 1) // spec.m - 1] = False
+        assert torch.equal(st["k_idx"][b].cpu()[keep], idx_state["k_idx"][b].cpu()[keep])
+        assert torch.equal(st["k_idx_scale"][b].cpu()[keep],
+                           idx_state["k_idx_scale"][b].cpu()[keep])
+    out2, idx2 = step()
+    torch.cuda.synchronize()
+    assert torch.equal(idx2.cpu(), idx)
 
 
 def test_decode_step_scan_events():

@@ -84,3 +84,20 @@ def test_pack_nibble_order():
     p = mx.pack(c)
     assert p.tolist() == [[0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]]
     assert np.array_equal(mx.unpack(p), c)
+
+
+def test_quantize_matches_the_scalar_rounding():
+    # every element through round_e2m1 one by one: random values and every tie of the grid
+    g = np.random.default_rng(7)
+    x = g.standard_normal((4, 128)) * np.exp(2 * g.standard_normal((4, 1)))
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+    x[:, 1:17] = np.concatenate([ties, -ties]) * 2.0 ** (mx.shared_exponent(x[0, :32]))
+    x[:, 0] = 7.0 * 2.0 ** mx.shared_exponent(x[0, :32])      # the first block's maximum
+    codes, scales = mx.quantize(x)
+    for i in range(x.shape[0]):
+        for b in range(4):
+            blk = x[i, 32 * b:32 * b + 32]
+            s = mx.shared_exponent(blk)
+            assert scales[i, b] == s + 127
+            assert [int(c) for c in codes[i, 32 * b:32 * b + 32]] == \
+                [mx.round_e2m1(v * 2.0 ** -s) for v in blk]

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import datagen
-from oracle import csa, gaps, pipeline
+from oracle import csa, gaps, mx, pipeline
 from oracle.pipeline import f64
 
 
@@ -116,6 +116,32 @@ def test_m1_new_entry_is_the_raw_row():
     for b in range(case["spec"].B):
         np.testing.assert_array_equal(res["kv_new"][b], f64(case["x_new"][b]))
         np.testing.assert_array_equal(res["ki_new"][b], f64(case["xi_new"][b]))
+
+
+def test_mxfp4_cache_scores_the_new_key_on_the_grid():
+    # m = 1: the new entry's key is the raw row xi_new; with an MXFP4 cache it is scored at its
+    # E2M1 x 2^s value, every other entry as case["k_idx"] holds it
+    case = small_decode(case_id=905, m=1, L=300, d_I=64, ragged=False)
+    spec = case["spec"]
+    bf = pipeline.decode_step(case)
+    case["idx_format"] = "mxfp4"
+    res = pipeline.decode_step(case)
+    for b in range(spec.B):
+        e = int(case["pos"][b])
+        k = f64(case["xi_new"][b])
+        km = mx.dequantize(*mx.quantize(k))
+        assert not np.array_equal(km, k)
+        # on the grid: each block's values are multiples of 2^(s-1) of magnitude <= 6 * 2^s
+        for blk in range(2):
+            v = km[32 * blk:32 * blk + 32]
+            s = mx.shared_exponent(k[32 * blk:32 * blk + 32])
+            assert np.all(np.abs(v) <= 6 * 2.0 ** s)
+            assert np.all(np.mod(v, 2.0 ** (s - 1)) == 0)
+        s_mx, s_bf = res["scores"][b], bf["scores"][b]
+        keep = np.arange(s_mx.size) != e
+        np.testing.assert_array_equal(s_mx[keep], s_bf[keep])
+        want = csa.index_scores(f64(case["q_idx"][b]), f64(case["w"][b]), km[None])[0]
+        assert s_mx[e] == want
 
 
 def test_gap_enforcement_decode():
