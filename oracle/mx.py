@@ -60,25 +60,27 @@ def round_e2m1(v: float) -> int:
 def quantize(x) -> tuple[np.ndarray, np.ndarray]:
     """Codes (one uint8 per element, 0..15) and scale bytes of rows x[..., dim], dim % 32 == 0.
 
-    The rounding of round_e2m1, for all elements at once: the distance of |x| / 2^s to each of
-    the 8 magnitudes, the nearest one, and among two equally near the one with the even code."""
+    The rounding of round_e2m1, for all elements at once: |x| / 2^s lies between two adjacent
+    magnitudes, and the midpoints between neighbours are the decision points -- the count of
+    midpoints below it is the nearest magnitude's code; a value on a midpoint is a tie and
+    goes to the even code of the two."""
     x = np.asarray(x, dtype=np.float64)
     dim = x.shape[-1]
     assert dim % BLOCK == 0
     blocks = x.reshape(-1, BLOCK)
     codes = np.empty(blocks.shape, dtype=np.uint8)
     scales = np.empty(blocks.shape[0], dtype=np.uint8)
-    even = (np.arange(8) & 1) == 0
-    for i0 in range(0, blocks.shape[0], 1 << 15):      # bounded temporaries
-        blk = blocks[i0:i0 + (1 << 15)]
+    mids = (E2M1_MAGNITUDES[:-1] + E2M1_MAGNITUDES[1:]) / 2     # 0.25, 0.75, ..., 5
+    for i0 in range(0, blocks.shape[0], 1 << 16):      # bounded temporaries
+        blk = blocks[i0:i0 + (1 << 16)]
         amax = np.abs(blk).max(axis=-1)
         _, e = np.frexp(amax)
         s = np.where(amax == 0.0, -127, np.clip((e - 1) - E2M1_EMAX, -127, 127)).astype(np.int64)
         y = blk * np.ldexp(1.0, -s)[:, None]           # exact: a power-of-two scaling
-        dist = np.abs(np.abs(y)[..., None] - E2M1_MAGNITUDES)
-        nearest = dist == dist.min(axis=-1, keepdims=True)
-        # one nearest magnitude, or two neighbours (one even code, one odd): the even one
-        c = np.argmax(nearest * np.where(even, 2, 1), axis=-1)
+        a = np.abs(y)
+        c = np.searchsorted(mids, a, side="left")       # midpoints strictly below a
+        tie = (c < mids.size) & (a == mids[np.minimum(c, mids.size - 1)])
+        c = np.where(tie & ((c & 1) == 1), c + 1, c)    # on a midpoint: the even code
         codes[i0:i0 + blk.shape[0]] = np.where((c != 0) & (y < 0), c | 8, c)
         scales[i0:i0 + blk.shape[0]] = s + 127
     return codes.reshape(x.shape), scales.reshape(x.shape[:-1] + (dim // BLOCK,))
@@ -87,9 +89,10 @@ def quantize(x) -> tuple[np.ndarray, np.ndarray]:
 def dequantize(codes, scales) -> np.ndarray:
     codes = np.asarray(codes, dtype=np.uint8)
     dim = codes.shape[-1]
-    vals = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)[codes]
-    s = np.asarray(scales, dtype=np.float64) - 127.0
-    return vals * np.repeat(2.0 ** s, BLOCK, axis=-1)[..., :dim]
+    vals = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+    v = np.take(vals, codes).reshape(codes.shape[:-1] + (dim // BLOCK, BLOCK))
+    s = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    return (v * s[..., None]).reshape(codes.shape)
 
 
 def pack(codes) -> np.ndarray:

@@ -793,7 +793,7 @@ static bool fast_shape(const ScanArgs& a) { return a.dt == kBF16 && a.H == kIH &
 // Decode-scan launch shape: positions per work item, key tiles in flight per wave beyond the
 // current one, and blocks resident per CU (the persistent grid is n_cu * blocks_per_cu).
 struct ScanTune {
-  int chunk = 2048, pf = 1, blocks_per_cu = 2, nt = 1, sd = 2, sd4 = 3, rot = 0;
+  int chunk = 2048, pf = 1, blocks_per_cu = 2, nt = 1, sd = 2, sd4 = 2, rot = 0;
   int prefill_q = 12, prefill_keys = 4096;
 };
 static int env_int(const char* name, int dflt) {

@@ -8,7 +8,7 @@ import torch
 import datagen
 import sparse_long_context_csa_amd as csa
 from gpu_helpers import (assert_ids, assert_pooled, assert_rows_close, check_step, dev,
-                         pooled_xmax, run_step)
+                         mxfp4_case, pooled_xmax, run_step)
 from oracle import csa as ocsa
 from oracle import gaps, pipeline
 from oracle.pipeline import f64
@@ -22,6 +22,18 @@ def test_decode_workload_fullsize(cfg):
     print(f"config {cfg}: inputs ready", flush=True)
     gaps.enforce_decode(case)
     _, st, rings, out, idx = run_step(case)
+    ref = pipeline.decode_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_decode_workload_fullsize_mxfp4_keys(cfg):
+    """The flat decode workloads with the indexer cache in MXFP4 (the bench's --idx-format
+    mxfp4 line): the GPU quantises the generated keys, the oracle scores their MXFP4 values."""
+    case, idx_state = mxfp4_case(datagen.CONFIGS[cfg])
+    print(f"config {cfg} (MXFP4 keys): inputs ready", flush=True)
+    gaps.enforce_decode(case)
+    _, st, rings, out, idx = run_step(case, idx_state)
     ref = pipeline.decode_step(case)
     check_step(case, ref, st, rings, out, idx)
 
