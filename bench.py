@@ -57,8 +57,10 @@ def cpu_baseline(case, budget_s):
                       f"{el:.1f} s, float64 NumPy"}
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "decode_1m_hbm_traffic.json")
+TRAFFIC_FILES = {
+    fmt: os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", name)
+    for fmt, name in (("bf16", "decode_1m_hbm_traffic.json"),
+                      ("mxfp4", "decode_1m_mxfp4_hbm_traffic.json"))}
 
 
 def source_digest(files) -> str:
@@ -76,12 +78,12 @@ def source_digest(files) -> str:
     return h.hexdigest()
 
 
-def counter_traffic():
+def counter_traffic(idx_format="bf16"):
     """HBM bytes per launch of the stage-1 scan from the committed rocprofv3 counter passes
     (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter on a plain copy of known
     size), or None when the kernel's sources changed since the counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[idx_format]) as f:
             t = json.load(f)
         if source_digest(t["sources"]) != t["source_sha256"]:
             return None
@@ -345,7 +347,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "scan_stream_kernel (indexer scan, stage 1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic() if args.config == 4 and not mx else None,
+                     "traffic": counter_traffic(args.idx_format) if args.config == 4 else None,
                      "avg_launch_us": round(scan_ms * 1e3, 2),
                      "launch_us_min_max": [round(min(scan_launch) * 1e3, 2),
                                            round(max(scan_launch) * 1e3, 2)],
