@@ -23,6 +23,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -191,6 +193,9 @@ def main():
                     help="indexer-key cache of the decode workloads: bf16 keys, or MXFP4 codes "
                          "with one scale byte per 32 channels (csa_quantize_mxfp4 of the same "
                          "keys, made before the timed region)")
+    ap.add_argument("--score-format", default="f32", choices=("f32", "bf16"),
+                    help="index scores the selection ranks: fp32, or rounded to bf16 (the "
+                         "line then also reports the recall of the fp32 selection)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -226,7 +231,7 @@ def main():
     if mx:
         codes, scales = csa.quantize_mxfp4(case["k_idx"].to(dev))
         torch.cuda.synchronize()
-    steps_objs = []
+    steps_objs, states = [], []
     for c in range(args.copies):
         st = {k: case[k].to(dev) for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
         if mx:
@@ -235,9 +240,10 @@ def main():
         rings = [r.to(dev) for r in case["rings"]]
         win_new = [shared["x_new"] if (i == 0 and datagen.ring_from_raw(spec)) else None
                    for i in range(spec.n_attn)]
+        states.append(dict(q=qs, win=rings, win_new=win_new, sink=sinks, **shared, **st, **hier))
         steps_objs.append(csa.DecodeStep(
-            m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"], q=qs, win=rings,
-            win_new=win_new, sink=sinks, **shared, **st, **hier))
+            m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
+            score_format=args.score_format, **states[-1]))
     torch.cuda.synchronize()
     log(f"device state ready: {args.copies} copies, "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
@@ -366,6 +372,22 @@ def main():
         res["metric"] = f"CSA decode queries/sec ({datagen.WORKLOAD_NAMES[args.config]})"
     if mx:
         res["metric"] += ", MXFP4 indexer keys"
+    if args.score_format == "bf16":
+        # recall of the fp32 selection: the same step (idempotent: it rewrites the same tail
+        # slot and entry) ranked on fp32 scores, over state copy 0
+        ref = csa.DecodeStep(m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
+                             score_format="f32", **states[0])
+        _, ids_bf = steps_objs[0]()
+        ids_bf = ids_bf.clone()
+        _, ids_f32 = ref()
+        torch.cuda.synchronize()
+        a, b = ids_bf.cpu().numpy(), ids_f32.cpu().numpy()
+        rec = [float(np.isin(b[i][b[i] >= 0], a[i]).mean()) for i in range(spec.B)]
+        res["metric"] += ", BF16 index scores"
+        res["config"]["scores"] = "bf16"
+        res["selection_recall_vs_fp32"] = {"mean": round(float(np.mean(rec)), 5),
+                                           "min": round(float(np.min(rec)), 5),
+                                           "rows": spec.B}
     if not args.no_cpu:
         if mx:
             # the oracle's step with an MXFP4 cache (the new entry's key quantised); the cached

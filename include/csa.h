@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -220,6 +220,8 @@ int csa_sparse_attn(const void *q, const void *kv, const int32_t *idx, int32_t t
 #define CSA_DECODE_EVENTS 5
 #define CSA_IDX_DTYPE 0   /* csa_decode_desc.idx_format: indexer keys in the step's dtype */
 #define CSA_IDX_MXFP4 1   /* indexer keys as MXFP4 codes + scale bytes                    */
+#define CSA_SCORE_F32 0   /* csa_decode_desc.score_format: rank fp32 index scores           */
+#define CSA_SCORE_BF16 1  /* rank the scores rounded to bf16                               */
 
 typedef struct csa_decode_desc {
   int32_t dtype;
@@ -265,6 +267,14 @@ typedef struct csa_decode_desc {
    *   loads its keys in FP4, 1 x 32 MXFP4 sub-blocks.] */
   int32_t idx_format;
   void *k_idx_scale;
+  /* Precision of the index scores the selection ranks: CSA_SCORE_F32 (as in steps 4 above) or
+   * CSA_SCORE_BF16, every fp32 score rounded to the nearest bf16 value (ties to even) before
+   * the Top-K, ties at the K-th value still going to the lower id. CSA_SCORE_BF16 needs
+   * T = bf16, idx_heads 64, idx_dim 128 and the flat selection; otherwise
+   * CSA_ERR_UNSUPPORTED.
+   *   [CoD "FP4, down to the index scores": the indexer's output scores are quantised from
+   *   FP32 to BF16 ahead of the top-k selector.] */
+  int32_t score_format;
 } csa_decode_desc;
 
 size_t csa_decode_step_workspace_size(const csa_decode_desc *d);

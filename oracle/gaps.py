@@ -32,6 +32,36 @@ def gap_ok(scores: np.ndarray, K: int) -> bool:
     return (a - b) > REL_GAP * max(abs(a), abs(b), float(np.abs(s).mean()))
 
 
+REL_MID = 1e-4
+
+
+def gap_ok_bf16(scores: np.ndarray, K: int) -> bool:
+    """For a selection over BF16-rounded scores: ties at the K-th bf16 value are broken by id,
+    so the selection is unique; it is robust to fp32 rounding when no score that rounds to
+    the K-th bf16 value or a neighbour of it lies within REL_MID * max(|s|, mean|S|) of a bf16
+    rounding midpoint (always true when there are at most K scores)."""
+    s = csa.round_f32(np.asarray(scores, dtype=np.float64))
+    n = s.shape[0]
+    if n <= K:
+        return True
+    b = csa.round_bf16(s)
+    vk = -np.partition(-b, K - 1)[K - 1]
+    _, e = np.frexp(max(abs(vk), 2.0 ** -126))
+    ulp = np.ldexp(1.0, e - 8)
+    near = np.abs(s - vk) <= 2.5 * ulp
+    if not near.any():
+        return True
+    sn, bn = s[near], b[near]
+    _, eb = np.frexp(np.maximum(np.abs(bn), 2.0 ** -126))
+    q = np.ldexp(1.0, eb - 8)                 # spacing at |b|; below a power of two it halves
+    lo_q = np.where(np.abs(bn) == np.ldexp(0.5, eb), q / 2, q)
+    up = np.where(bn >= 0, q, lo_q)
+    down = np.where(bn >= 0, lo_q, q)
+    dist = np.minimum(np.abs(sn - (bn + up / 2)), np.abs(sn - (bn - down / 2)))
+    scale = np.maximum(np.abs(sn), float(np.abs(s).mean()))
+    return bool(np.all(dist > REL_MID * scale))
+
+
 def _blocks_gap(S: np.ndarray, spec) -> np.ndarray:
     """gap_ok on the block maxima at rank max_blocks, per column of S [n, k]. The maxima are
     taken over the whole batch at once here (a search aid); the gate that is kept is checked
@@ -46,11 +76,11 @@ def _blocks_gap(S: np.ndarray, spec) -> np.ndarray:
     return np.array([gap_ok(bm[:, j], spec.max_blocks) for j in range(k)])
 
 
-def _fix_w(spec, R: np.ndarray, K: int, which: str, b: int, current) -> tuple[object, int]:
-    """Redraw a gate row until the scores R @ w have the gap at rank K."""
+def _fix_w(spec, R: np.ndarray, K: int, which: str, b: int, current, ok=gap_ok) -> tuple[object, int]:
+    """Redraw a gate row until the scores R @ w have the gap at rank K (``ok`` the rule)."""
     w = current
     attempt = 0
-    while not gap_ok(R @ f64(w), K):
+    while not ok(R @ f64(w), K):
         attempt += 1
         if attempt > MAX_ATTEMPTS:
             raise RuntimeError(f"no gap after {MAX_ATTEMPTS} redraws ({which}, row {b})")
@@ -109,7 +139,8 @@ def enforce_decode(case: dict, seqs=None) -> dict:
             case["w2"][b] = w2
             redraws[b] = (attempt, a2)
         else:
-            w, a = _fix_w(spec, R, spec.K, "w", b, case["w"][b])
+            rule = gap_ok_bf16 if case.get("score_format") == "bf16" else gap_ok
+            w, a = _fix_w(spec, R, spec.K, "w", b, case["w"][b], rule)
             case["w"][b] = w
             redraws[b] = a
     return redraws

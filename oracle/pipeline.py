@@ -137,7 +137,8 @@ def decode_step(case: dict, seqs=None) -> dict:
     through the block pre-select and pool rescoring), and every attention call attends to
     the shared selection plus its own window and sink. With case["idx_format"] == "mxfp4",
     case["k_idx"] holds the MXFP4 values of the cached keys and the new entry's key is
-    quantised before it is scored (``cached_index_key``).
+    quantised before it is scored (``cached_index_key``). With case["score_format"] == "bf16"
+    the flat selection ranks the scores rounded fp64 -> fp32 -> bf16.
     Returns a dict with per-sequence results (new entries, scores, pool, ids, outputs).
     """
     spec = case["spec"]
@@ -172,6 +173,10 @@ def decode_step(case: dict, seqs=None) -> dict:
                 keys[new_e] = cached_index_key(case, ki_e)
         res["n_vis"][b] = n_vis
         s1 = csa.index_scores(f64(case["q_idx"][b]), f64(case["w"][b]), keys)
+        if case.get("score_format") == "bf16":
+            # the fp32 scores quantised to BF16 ahead of the selection ([CoD] "FP4, down to
+            # the index scores"); ties at the K-th value go to the lower id as before
+            s1 = csa.round_bf16(csa.round_f32(s1))
         res["scores"][b] = s1
         if spec.block_size > 0:
             pool = csa.candidate_pool(s1, spec.block_size, spec.max_blocks)

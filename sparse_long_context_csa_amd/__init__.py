@@ -163,10 +163,11 @@ class DecodeStep:
     win_new (list, entries may be None), sink (list, entries may be None); out (list) and
     out_idx are allocated here unless given. With k_idx_scale (uint8 [n_seq, e_cap,
     idx_dim / 32]) the indexer cache is MXFP4: k_idx holds the codes, uint8 [n_seq, e_cap,
-    idx_dim / 2], as quantize_mxfp4 writes them."""
+    idx_dim / 2], as quantize_mxfp4 writes them. score_format "bf16" ranks the index scores
+    rounded to bf16."""
 
     def __init__(self, *, m: int, top_k: int, window: int, scale: float, block_size: int = 0,
-                 max_blocks: int = 0, out=None, out_idx=None, **t):
+                 max_blocks: int = 0, out=None, out_idx=None, score_format: str = "f32", **t):
         self.t = t
         kv = _dev(t["kv"], "kv")
         dt = kv.dtype
@@ -217,6 +218,9 @@ class DecodeStep:
                 d.win_new[c] = _dev(win_new[c], "win_new", dt).data_ptr()
             if sinks[c] is not None:
                 d.sink[c] = _dev(sinks[c], "sink", torch.float32).data_ptr()
+        if score_format not in ("f32", "bf16"):
+            raise ValueError("score_format must be 'f32' or 'bf16'")
+        d.score_format = _lib.SCORE_BF16 if score_format == "bf16" else _lib.SCORE_F32
         d.out_idx = out_idx.data_ptr()
         self.desc = d
         nb = lib().csa_decode_step_workspace_size(C.byref(d))

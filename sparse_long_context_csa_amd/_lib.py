@@ -13,6 +13,7 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_NULL", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTY
 MAX_ATTN = 4
 DECODE_EVENTS = 5
 IDX_DTYPE, IDX_MXFP4 = 0, 1
+SCORE_F32, SCORE_BF16 = 0, 1
 
 vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
 
@@ -30,7 +31,7 @@ class DecodeDesc(C.Structure):
         ("q_idx2", vp), ("w2", vp), ("q", vp * MAX_ATTN), ("win", vp * MAX_ATTN),
         ("win_new", vp * MAX_ATTN), ("sink", vp * MAX_ATTN), ("out", vp * MAX_ATTN),
         ("out_idx", vp), ("events", vp * DECODE_EVENTS), ("scan_events", vp * 2),
-        ("idx_format", i32), ("k_idx_scale", vp),
+        ("idx_format", i32), ("k_idx_scale", vp), ("score_format", i32),
     ]
 
 

@@ -105,10 +105,12 @@ hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, co
                      const int32_t* e_count, const int32_t* cand, int64_t n_cand, int64_t n_seq,
                      int64_t n_q, int64_t e_cap, int H, int d, int m, const TopkWs& ws,
                      hipStream_t s, const IngestArgs* ingest = nullptr, int seg_k = 0,
-                     void* const* kernel_events = nullptr, const void* key_scales = nullptr) {
+                     void* const* kernel_events = nullptr, const void* key_scales = nullptr,
+                     bool score_bf16 = false) {
   ScanArgs a{};
   a.dt = dt; a.q = q; a.w = w; a.keys = keys; a.q_pos = q_pos; a.e_count = e_count;
   a.key_scales = static_cast<const uint8_t*>(key_scales);
+  a.score_bf16 = score_bf16 ? 1 : 0;
   a.cand = cand; a.n_cand = n_cand; a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap;
   a.H = H; a.d = d; a.m = m; a.scores = ws.scores; a.score_stride = ws.stride;
   a.n_vis = ws.n_vis; a.count = ws.count;
@@ -371,6 +373,10 @@ int check_decode_shapes(const csa_decode_desc* d) {
       (d->block_size != 0 || !scan_fuses_ingest(d->dtype, d->idx_heads, d->idx_dim, d->m) ||
        !scan_reads_mxfp4(d->dtype, d->idx_heads, d->idx_dim, 1, false)))
     return CSA_ERR_UNSUPPORTED;
+  if (d->score_format != CSA_SCORE_F32 && d->score_format != CSA_SCORE_BF16) return CSA_ERR_SHAPE;
+  if (d->score_format == CSA_SCORE_BF16 &&
+      (d->block_size != 0 || !scan_reads_mxfp4(d->dtype, d->idx_heads, d->idx_dim, 1, false)))
+    return CSA_ERR_UNSUPPORTED;
   return CSA_OK;
 }
 
@@ -461,7 +467,8 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   } else {
     if (scan_rows(d->dtype, d->q_idx, d->w, d->k_idx, d->pos, nullptr, nullptr, 0, rows, 1,
                   d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, s, split_ingest,
-                  d->top_k, d->scan_events, key_scales) != hipSuccess)
+                  d->top_k, d->scan_events, key_scales,
+                  d->score_format == CSA_SCORE_BF16) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
     const SegArgs seg = segments_for(w.flat, d->dtype, d->idx_heads, d->idx_dim, 1, false, rows,

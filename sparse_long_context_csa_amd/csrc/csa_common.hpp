@@ -26,6 +26,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t(u >> 16);
 }
 
+// f rounded to the nearest bf16 value (ties to even), as a float
+__device__ __forceinline__ float round_to_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
 // Storage-type traits: load/store 8 consecutive elements as fp32.
 template <typename T> struct Elt;
 template <> struct Elt<float> {

@@ -690,7 +690,7 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
             }
             const float sv = sum_groups4(scb[0], scb[1], scb[2], scb[3]);
             const int64_t p = tb + 16 * ((g & 1) * 2 + (g >> 1)) + col;   // row g: group grp
-            if (p < c1) segl.sc[p - c0] = sv;
+            if (p < c1) segl.sc[p - c0] = a.score_bf16 ? round_to_bf16(sv) : sv;
           }
         } else {
           bf16x8_t B[4];
@@ -700,7 +700,7 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
               patch_new_key(pk_new, g, col == int(e_new - tb), B);
             const float sc = tile_score(A, B, wv);
             const int64_t p = tb + col;
-            if (g == 0 && p < c1) segl.sc[p - c0] = sc;
+            if (g == 0 && p < c1) segl.sc[p - c0] = a.score_bf16 ? round_to_bf16(sc) : sc;
           }
         }
         if (t + kSD < nt_item) {
@@ -928,7 +928,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s, hipEvent_t e0, hipEvent
   if (rows == 0) return hipSuccess;
   const int64_t max_pos = a.cand ? a.n_cand : a.e_cap;
   const bool q4 = a.key_scales != nullptr;
-  if (q4 && !scan_reads_mxfp4(a.dt, a.H, a.d, a.n_q, a.cand != nullptr))
+  if ((q4 || a.score_bf16) && !scan_reads_mxfp4(a.dt, a.H, a.d, a.n_q, a.cand != nullptr))
     return hipErrorInvalidValue;
   if (!q4 && fast_shape(a) && a.cand == nullptr && a.n_q >= 16) {
     const int keys_per_block = scan_tune().prefill_keys;

@@ -81,6 +81,7 @@ struct ScanArgs {
   // the select's ingest workgroups do the rest. Only when scan_fuses_ingest() holds.
   IngestArgs ingest;
   SegArgs seg;            // decode scan without candidates: candidate segments (optional)
+  int score_bf16;         // the stream scan rounds every score to bf16 before it leaves
 };
 // ev_start / ev_stop (both or neither): the start and stop events of the scan kernel's own
 // dispatch (a scan is one kernel).
@@ -92,8 +93,9 @@ hipError_t launch_scan_prefill(const ScanArgs& a, int pq, int keys_per_block, di
                                hipStream_t s, hipEvent_t e0, hipEvent_t e1);
 // Whether the decode scan for this shape takes the indexer-key part of the ingest.
 bool scan_fuses_ingest(int dt, int H, int d, int m);
-// Whether the scan reads MXFP4 keys for this shape (bf16 queries, 64 heads x 128, one or a few
-// query rows per sequence, no candidate list).
+// Whether the stream scan serves this shape, the one that reads MXFP4 keys and rounds scores
+// to bf16 (bf16 queries, 64 heads x 128, one or a few query rows per sequence, no candidate
+// list).
 bool scan_reads_mxfp4(int dt, int H, int d, int64_t n_q, bool cand);
 
 // ---- MXFP4 storage of indexer keys (mxfp4.hpp) --------------------------------------------

@@ -164,7 +164,8 @@ def run_step(case, idx_state=None):
                           pos=g["pos"], x_new=g["x_new"], z_new=g["z_new"], xi_new=g["xi_new"],
                           zi_new=g["zi_new"], bias=g["bias"], bias_i=g["bias_i"],
                           q_idx=g["q_idx"], w=g["w"], q=[dev(x) for x in case["q"]], win=rings,
-                          win_new=win_new, sink=[dev(x) for x in case["sink"]], **st, **kw)
+                          win_new=win_new, sink=[dev(x) for x in case["sink"]],
+                          score_format=case.get("score_format", "f32"), **st, **kw)
     out, idx = step()
     torch.cuda.synchronize()
     return step, st, rings, [o.cpu() for o in out], idx.cpu()

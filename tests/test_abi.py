@@ -84,10 +84,12 @@ def test_decode_desc_mirrors_the_header_struct():
     assert int(m.group(1)) == _lib.DECODE_EVENTS
     # natural C layout on x86-64: 12 int32 and 2 int64 (64 B), the float padded to 8 B, then
     # 17 tensor pointers, 5 arrays of CSA_MAX_ATTN pointers, out_idx, the phase events, the
-    # scan kernel's start and stop events; idx_format padded to 8 B and k_idx_scale
+    # scan kernel's start and stop events; idx_format padded to 8 B, k_idx_scale, score_format
+    # padded to 8 B
     n_ptr = 17 + 5 * _lib.MAX_ATTN + 1 + _lib.DECODE_EVENTS + 2
-    assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr + 8 + 8
-    for name, val in (("CSA_IDX_DTYPE", _lib.IDX_DTYPE), ("CSA_IDX_MXFP4", _lib.IDX_MXFP4)):
+    assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr + 8 + 8 + 8
+    for name, val in (("CSA_IDX_DTYPE", _lib.IDX_DTYPE), ("CSA_IDX_MXFP4", _lib.IDX_MXFP4),
+                      ("CSA_SCORE_F32", _lib.SCORE_F32), ("CSA_SCORE_BF16", _lib.SCORE_BF16)):
         assert int(re.search(rf"#define\s+{name}\s+(\d+)", _header()).group(1)) == val
 
 
@@ -211,6 +213,12 @@ def test_decode_mxfp4_validation(lib):
     d.k_idx_scale = 256 + 2
     assert step(d) == -2
     assert lib.csa_decode_step_workspace_size(C.byref(full(m=16))) == 0
+    # BF16 scores: flat selection and the stream scan's shapes only
+    d = full(idx_format=_lib.IDX_DTYPE, score_format=_lib.SCORE_BF16, block_size=8,
+             max_blocks=64)
+    assert step(d) == -4
+    assert step(full(idx_format=_lib.IDX_DTYPE, score_format=_lib.SCORE_BF16, idx_dim=64)) == -4
+    assert step(full(idx_format=_lib.IDX_DTYPE, score_format=3)) == -2
 
 
 def test_binding_raises_on_errors(lib):

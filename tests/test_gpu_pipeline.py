@@ -151,6 +151,27 @@ def test_decode_step_mxfp4_keys(spec):
     assert torch.equal(idx2.cpu(), idx)
 
 
+# BF16 index scores: the scan rounds every score to bf16 before it leaves; the selection (ties
+# at the K-th value to the lower id) must match the oracle's ranking of its fp32 scores rounded
+# to bf16, id for id.
+@pytest.mark.parametrize("keys", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("spec", [
+    datagen.CaseSpec(7130, "decode", B=5, L=24000, m=4, w_cap=256, ragged=True),
+    datagen.CaseSpec(7131, "decode", B=3, L=4 * 60000, m=4, w_cap=256, ragged=True),
+    datagen.CaseSpec(7132, "decode", B=4, L=2400, e_cap=40000, m=4, w_cap=128, ragged=True),
+], ids=["flat", "segments", "short_rows"])
+def test_decode_step_bf16_scores(spec, keys):
+    if keys == "mxfp4":
+        case, idx_state = mxfp4_case(spec)
+    else:
+        case, idx_state = datagen.make_case(spec), None
+    case["score_format"] = "bf16"
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    _, st, rings, out, idx = run_step(case, idx_state)
+    check_step(case, ref, st, rings, out, idx)
+
+
 def test_decode_step_scan_events():
     """The scan kernel's dispatch takes the step's scan events: the result is unchanged and
     their interval lies inside the step's own (marker events 0 and 4)."""

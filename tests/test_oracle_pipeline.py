@@ -201,3 +201,51 @@ def test_tiny_forward_runs_and_gaps():
     z = 0.125 * (f64(case["q"][0, 0]) @ x0)
     wgt = 1 / (1 + np.exp(f64(case["sink"]) - z))
     np.testing.assert_allclose(res["out"][(0, 0)], csa.round_f32(wgt[:, None] * x0), rtol=1e-6)
+
+
+def test_bf16_scores_rank_rounded_values_ties_to_lower_id():
+    # scores 1.0 + 2^-10 and 1.0 round to the same bf16 value 1.0 (spacing 2^-7): with BF16
+    # scores the lower id wins the last place, with fp32 scores the larger score does
+    s = np.array([0.5, 1.0, 3.0, 1.0 + 2.0 ** -10, 0.25])
+    assert csa.select_topk(s, 2).tolist() == [2, 3]
+    sb = csa.round_bf16(csa.round_f32(s))
+    assert sb[1] == sb[3] == 1.0
+    assert csa.select_topk(sb, 2).tolist() == [1, 2]
+
+
+def test_gap_rule_bf16():
+    # K = 2 over 4 scores; the 2nd bf16 value is 1.0; a score on the midpoint 1 + 2^-8 between
+    # 1.0 and its upper neighbour 1 + 2^-7 is ambiguous, one 2^-12 away from it is not
+    base = np.array([3.0, 1.0, 0.25, 0.125])
+    assert gaps.gap_ok_bf16(base, 2)
+    amb = base.copy(); amb[3] = 1.0 + 2.0 ** -8
+    assert not gaps.gap_ok_bf16(amb, 2)
+    ok = base.copy(); ok[3] = 1.0 + 2.0 ** -8 + 2.0 ** -12
+    assert gaps.gap_ok_bf16(ok, 2)
+    # below a power of two the spacing halves: the midpoint under 1.0 is 1 - 2^-9
+    low = base.copy(); low[3] = 1.0 - 2.0 ** -9
+    assert not gaps.gap_ok_bf16(low, 2)
+    assert gaps.gap_ok_bf16(np.array([1.0, 2.0]), 2)       # no more scores than K
+
+
+def test_decode_step_bf16_scores():
+    case = small_decode(case_id=906, B=4, L=8192, d_I=64, H_I=8, K=64, ragged=False)
+    spec = case["spec"]
+    case["score_format"] = "bf16"
+    gaps.enforce_decode(case)
+    res = pipeline.decode_step(case)
+    for b in range(spec.B):
+        s = res["scores"][b]
+        assert np.array_equal(s, csa.round_bf16(s))          # ranked on bf16 values
+        ids = res["ids"][b]
+        sel = np.zeros(s.size, bool); sel[ids] = True
+        # every selected score reaches every unselected one, and at the K-th value the
+        # selected ids are the lowest of that value
+        assert s[sel].min() >= s[~sel].max()
+        v = s[sel].min()
+        tie_sel = np.flatnonzero(sel & (s == v)); tie_out = np.flatnonzero(~sel & (s == v))
+        assert tie_out.size == 0 or tie_sel.max() < tie_out.min()
+    # the same inputs ranked on fp32 scores keep most of the same entries
+    f32b = pipeline.decode_step({**case, "score_format": "f32"})
+    rec = np.mean([np.isin(res["ids"][b], f32b["ids"][b]).mean() for b in range(spec.B)])
+    assert rec > 0.9
