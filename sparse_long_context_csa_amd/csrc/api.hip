@@ -125,7 +125,8 @@ hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, co
 hipError_t select_rows(const TopkWs& ws, int64_t rows, int64_t max_count, const int32_t* ids,
                        int64_t id_stride, const int32_t* id_limit, int K, int32_t* out_idx,
                        float* out_score, void* scratch, hipStream_t s,
-                       const IngestArgs* side = nullptr, const SegArgs& seg = SegArgs{}) {
+                       const IngestArgs* side = nullptr, const SegArgs& seg = SegArgs{},
+                       bool bf16_scores = false) {
   TopkArgs t{};
   t.scores = ws.scores; t.stride = ws.stride; t.ids = ids; t.id_stride = id_stride;
   t.gmax = ws.gmax; t.gstride = ws.gstride;
@@ -133,6 +134,7 @@ hipError_t select_rows(const TopkWs& ws, int64_t rows, int64_t max_count, const 
   t.out_idx = out_idx; t.out_score = out_score; t.out_stride = K; t.scratch = scratch;
   t.side = side;
   t.seg = seg;
+  t.bf16_scores = bf16_scores;
   return launch_topk(t, s);
 }
 
@@ -474,7 +476,8 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
     const SegArgs seg = segments_for(w.flat, d->dtype, d->idx_heads, d->idx_dim, 1, false, rows,
                                      d->e_cap, d->top_k);
     if (select_rows(w.flat, rows, d->e_cap, nullptr, 0, nullptr, d->top_k, d->out_idx, nullptr,
-                    w.flat.scratch, s, split_ingest, seg) != hipSuccess)
+                    w.flat.scratch, s, split_ingest, seg,
+                    d->score_format == CSA_SCORE_BF16) != hipSuccess)
       return CSA_ERR_HIP;
   }
 

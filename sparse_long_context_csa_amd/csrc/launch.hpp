@@ -129,6 +129,7 @@ struct TopkArgs {
   // workgroups of the select's last launch (indexer keys are the scan's part)
   const IngestArgs* side;
   SegArgs seg;            // segments left by the scan (seg.seg non-null: the select uses them)
+  bool bf16_scores;       // every score is a bf16 value (the scan rounded them)
 };
 size_t topk_scratch_bytes(int64_t rows, int64_t max_count, int K);
 

@@ -86,6 +86,8 @@ struct SelArgs {
   int64_t n_side;         // ingest workgroups after the rows' (0: none)
   IngestArgs side;
   SegArgs cseg;           // candidate segments of the decode scan (cseg.seg null: none)
+  int key_floor;          // 16 when every score is a bf16 value: keys differing below bit 16
+                          // of their offset from the list minimum are equal
 };
 
 // A decode step's ingest (without the indexer keys) for sequence sq, by one workgroup.
@@ -859,9 +861,11 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
   seg_find(sh, sh.hb, 1 << (bits - lo), K);
   uint32_t P = sh.res[0], need = K - sh.res[1];
   bool done = sh.res[2] == need;
+  // with bf16-valued scores two different keys differ by at least 2^16 (their low 16 bits
+  // depend only on the sign, and -0 reads as +0), so the bin at shift key_floor holds one key
 #pragma unroll 1
-  while (!done && lo > 0) {
-    const int w = lo < kSegDigit ? lo : kSegDigit;
+  while (!done && lo > a.key_floor) {
+    const int w = lo - a.key_floor < kSegDigit ? lo - a.key_floor : kSegDigit;
     const int l2 = lo - w;
     __syncthreads();
     for (int b = tid; b < (1 << w); b += kSelThreads) sh.hb[b] = 0u;
@@ -1104,6 +1108,7 @@ hipError_t launch_topk(const TopkArgs& t, hipStream_t s) {
   a.n_side = t.side ? t.side->n_seq : 0;
   a.side = t.side ? *t.side : IngestArgs{};
   a.cseg = t.seg;
+  a.key_floor = t.bf16_scores ? 16 : 0;
   // with segments the scan leaves no 16-position maxima: short rows bound from the scores
   if (t.seg.seg != nullptr) a.gmax = nullptr;
   const unsigned rows = static_cast<unsigned>(t.rows);
