@@ -111,6 +111,57 @@ def compress(X, Z, bias, m: int) -> np.ndarray:
     return (P * Xb).sum(axis=-2)
 
 
+def compress_c4a(Xa, Za, Xb, Zb, bias_a, bias_b, m: int, Xb_prev=None, Zb_prev=None) -> np.ndarray:
+    """The overlapped two-stream compressor (vLLM's "c4a" at m = 4).
+
+    [CoD "The compressor has two streams and they overlap": two independent projections C^a
+    and C^b with their own compression logits Z^a and Z^b; entry i takes C^a from positions
+    [m i, m(i+1)) and C^b from [m(i-1), m i) (the page prints closed brackets; half-open as in
+    the single-stream reading), a softmax over the concatenated 2m logits per channel and a
+    weighted sum over both streams -- eight tokens at stride four for m = 4.]
+    [CoD "Rebuilding the model from its constants", CSA layer table: positional biases B^a,
+    B^b of shape m x 512, one per stream.]
+
+    Xa, Za, Xb, Zb: [..., T, d] rows of positions p0 .. p0 + T - 1 (p0 a multiple of m), T % m
+    == 0; bias_a, bias_b: [m, d]. Xb_prev, Zb_prev: [..., m, d] the b-stream rows of the m
+    positions before p0, or None when p0 = 0 -- entry 0 of a sequence has no b-part (reading:
+    positions before the sequence are masked, so its softmax runs over its m a-logits only).
+    For chunk entry e and channel c, with lists over j < m:
+        logits  = [Za[m e + j] + bias_a[j]] + [Zb[m(e-1) + j] + bias_b[j]]   (b-part: the
+                  previous block, from Xb_prev/Zb_prev for e = 0)
+        alpha   = softmax over all of them
+        out[e]  = sum of alpha times the matching rows Xa[m e + j] and Xb[m(e-1) + j]
+    Returns float64 [..., T/m, d] (unrounded).
+    """
+    Xa, Za, Xb, Zb = (np.asarray(t, dtype=np.float64) for t in (Xa, Za, Xb, Zb))
+    ba, bb = np.asarray(bias_a, dtype=np.float64), np.asarray(bias_b, dtype=np.float64)
+    T, d = Xa.shape[-2], Xa.shape[-1]
+    if T % m != 0:
+        raise ValueError("token count must be a multiple of m")
+    E = T // m
+    lead = Xa.shape[:-2]
+    if (Xb_prev is None) != (Zb_prev is None):
+        raise ValueError("give both previous b-stream blocks or neither")
+    out = np.empty(lead + (E, d))
+    for e in range(E):
+        la = Za[..., m * e:m * e + m, :] + ba                    # [..., m, d]
+        xa = Xa[..., m * e:m * e + m, :]
+        if e > 0:
+            lb = Zb[..., m * (e - 1):m * e, :] + bb
+            xb = Xb[..., m * (e - 1):m * e, :]
+        elif Xb_prev is not None:
+            lb = np.asarray(Zb_prev, dtype=np.float64) + bb
+            xb = np.asarray(Xb_prev, dtype=np.float64)
+        else:
+            lb = xb = None
+        L = la if lb is None else np.concatenate([la, lb], axis=-2)
+        X = xa if xb is None else np.concatenate([xa, xb], axis=-2)
+        P = np.exp(L - L.max(axis=-2, keepdims=True))
+        P /= P.sum(axis=-2, keepdims=True)                      # softmax over 2m (or m)
+        out[..., e, :] = (P * X).sum(axis=-2)
+    return out
+
+
 # ----------------------------------------------------------------------------------------
 # causal visibility of compressed entries
 # ----------------------------------------------------------------------------------------
