@@ -115,11 +115,35 @@ def bench_prefill(args):
     kvs = [g["kv"].clone() for _ in range(copies)]
     kis = [g["k_idx"].clone() for _ in range(copies)]
 
-    def step(c):
+    c4a = args.compressor == "c4a"
+    if c4a:
+        # the b-stream rows, logits and bias of both caches (the a stream is the chunk's rows
+        # above), and the b rows of the block before the chunk
+        cid, tb = spec.case_id, 30
+        for nm, d in (("", spec.D), ("i", spec.d_I)):
+            g[f"x{nm}b"] = datagen.tensor(cid, tb, (1, spec.chunk, d), "bf16", 1 / math.sqrt(d)).to(dev)
+            g[f"z{nm}b"] = datagen.tensor(cid, tb + 1, (1, spec.chunk, d), "bf16", 1.0).to(dev)
+            g[f"b{nm}b"] = datagen.tensor(cid, tb + 2, (spec.m, d), "bf16", 0.1).to(dev)
+            g[f"x{nm}p"] = datagen.tensor(cid, tb + 3, (1, spec.m, d), "bf16", 1 / math.sqrt(d)).to(dev)
+            g[f"z{nm}p"] = datagen.tensor(cid, tb + 4, (1, spec.m, d), "bf16", 1.0).to(dev)
+            tb += 5
+
+    def compress_chunk(c):
+        if c4a:
+            csa.compress_c4a(g["x_chunk"], g["z_chunk"], g["xb"], g["zb"], g["bias"], g["bb"],
+                             spec.m, xb_prev=g["xp"], zb_prev=g["zp"],
+                             out=kvs[c][:, e0:e0 + ne], out_seq_stride=E * spec.D)
+            csa.compress_c4a(g["xi_chunk"], g["zi_chunk"], g["xib"], g["zib"], g["bias_i"],
+                             g["bib"], spec.m, xb_prev=g["xip"], zb_prev=g["zip"],
+                             out=kis[c][:, e0:e0 + ne], out_seq_stride=E * spec.d_I)
+            return
         csa.compress(g["x_chunk"], g["z_chunk"], g["bias"], spec.m, out=kvs[c][:, e0:e0 + ne],
                      out_seq_stride=E * spec.D)
         csa.compress(g["xi_chunk"], g["zi_chunk"], g["bias_i"], spec.m, out=kis[c][:, e0:e0 + ne],
                      out_seq_stride=E * spec.d_I)
+
+    def step(c):
+        compress_chunk(c)
         idx = csa.index_topk(g["q_idx"], g["w"], kis[c], g["q_pos"], spec.m, spec.K,
                              e_count=g["e_count"])
         return csa.sparse_attn(g["q"], kvs[c], idx, g["ring"], spec.w_cap, spec.W, g["q_pos"],
@@ -140,10 +164,7 @@ def bench_prefill(args):
     for i in range(steps):
         c = i % copies
         evs[0].record()
-        csa.compress(g["x_chunk"], g["z_chunk"], g["bias"], spec.m, out=kvs[c][:, e0:e0 + ne],
-                     out_seq_stride=E * spec.D)
-        csa.compress(g["xi_chunk"], g["zi_chunk"], g["bias_i"], spec.m, out=kis[c][:, e0:e0 + ne],
-                     out_seq_stride=E * spec.d_I)
+        compress_chunk(c)
         evs[1].record()
         idx = csa.index_topk(g["q_idx"], g["w"], kis[c], g["q_pos"], spec.m, spec.K,
                              e_count=g["e_count"])
@@ -172,6 +193,16 @@ def bench_prefill(args):
         "phases_ms": {"compress": round(ph[0], 4), "index_topk": round(ph[1], 4),
                       "sparse_attn": round(ph[2], 4)},
     }
+    # the chunk's compression (both caches): every input row read once, the entries written
+    n_in = 4 if c4a else 2
+    cbytes = sum(n_in * spec.chunk * d * 2 + (2 * spec.m * d * 2 if c4a else 0)
+                 + n_in // 2 * spec.m * d * 2 + ne * d * 2 for d in (spec.D, spec.d_I))
+    res["compress"] = {"compressor": args.compressor, "bound": "hbm", "bytes": cbytes,
+                       "ms_incl_launches": round(ph[0], 4),
+                       "gbs": round(cbytes / (ph[0] * 1e-3) / 1e9, 1)}
+    if c4a:
+        res["metric"] += ", overlapped two-stream compressor"
+        res["config"]["compressor"] = "c4a"
     print(json.dumps(res), flush=True)
 
 
@@ -196,6 +227,9 @@ def main():
     ap.add_argument("--score-format", default="f32", choices=("f32", "bf16"),
                     help="index scores the selection ranks: fp32, or rounded to bf16 (the "
                          "line then also reports the recall of the fp32 selection)")
+    ap.add_argument("--compressor", default="single", choices=("single", "c4a"),
+                    help="chunked prefill (--config 3): the single-stream compressor, or the "
+                         "overlapped two-stream one for both caches")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()

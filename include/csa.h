@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 4
+#define CSA_ABI_VERSION 5
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -74,6 +74,35 @@ const char *csa_status_str(int status);
 int csa_compress(const void *x, const void *logits, const void *bias, void *out,
                  int64_t n_seq, int64_t n_tok, int64_t out_seq_stride, int32_t dim,
                  int32_t m, int32_t dtype, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_compress_c4a -- the overlapped two-stream compressor (vLLM's "c4a" at m = 4).
+ *   [CoD "The compressor has two streams and they overlap": two independent projections C^a
+ *   and C^b with their own compression logits; entry i draws C^a from the positions of its
+ *   own block and C^b from the block before, one softmax across the 2m logits per channel,
+ *   a weighted sum over both streams (eight tokens at stride four for m = 4); CoD CSA layer
+ *   table: positional biases B^a, B^b of shape m x d.]
+ * For every sequence s, chunk entry e < n_tok/m and channel c, with j < m:
+ *   logits = { za[s, m e + j, c] + bias_a[j, c] }  U  { zb'[s, j, c] + bias_b[j, c] }
+ *   alpha  = softmax over all 2m of them
+ *   out[s, e, c] = sum of alpha times xa[s, m e + j, c] and xb'[s, j, c] respectively
+ * where (xb', zb') are the b-stream rows of the block before: rows m(e-1) + j of xb, zb for
+ * e > 0, and for e = 0 rows j of xb_prev, zb_prev -- or, when both are NULL (the chunk starts
+ * the sequence), no b-part: entry 0 of a sequence pools its m a-rows only.
+ *   xa, za, xb, zb : T [n_seq, n_tok, dim]  rows of positions p0 .. p0 + n_tok - 1
+ *                    (p0 a multiple of m: the chunk starts on a block boundary)
+ *   bias_a, bias_b : T [m, dim]
+ *   xb_prev, zb_prev : T [n_seq, m, dim] the b rows of positions p0 - m .. p0 - 1, or NULL
+ *   out            : T, chunk entry e of sequence s at out + s*out_seq_stride + e*dim
+ *                    (out_seq_stride = 0 means dense: (n_tok/m)*dim)
+ * Limits: as csa_compress (1 <= m <= 16, n_tok % m == 0, 8 <= dim <= 8192, dim % 8 == 0);
+ * xb_prev and zb_prev both NULL or both set (else CSA_ERR_NULL).
+ * ------------------------------------------------------------------------------------- */
+int csa_compress_c4a(const void *xa, const void *za, const void *xb, const void *zb,
+                     const void *bias_a, const void *bias_b, const void *xb_prev,
+                     const void *zb_prev, void *out, int64_t n_seq, int64_t n_tok,
+                     int64_t out_seq_stride, int32_t dim, int32_t m, int32_t dtype,
+                     void *stream);
 
 /* ---------------------------------------------------------------------------------------
  * csa_quantize_mxfp4 -- MXFP4 storage of indexer keys (production precision).

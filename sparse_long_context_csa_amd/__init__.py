@@ -65,6 +65,28 @@ def compress(x: torch.Tensor, logits: torch.Tensor, bias: torch.Tensor, m: int,
     return out
 
 
+def compress_c4a(xa: torch.Tensor, za: torch.Tensor, xb: torch.Tensor, zb: torch.Tensor,
+                 bias_a: torch.Tensor, bias_b: torch.Tensor, m: int, xb_prev=None, zb_prev=None,
+                 out: torch.Tensor | None = None, out_seq_stride: int = 0) -> torch.Tensor:
+    """csa_compress_c4a: rows [n_seq, n_tok, dim] of both streams -> entries [n_seq, n_tok/m,
+    dim]; xb_prev/zb_prev [n_seq, m, dim] the b rows of the block before the chunk, or None at
+    the start of a sequence."""
+    for nm, t in (("xa", xa), ("za", za), ("xb", xb), ("zb", zb), ("bias_a", bias_a),
+                  ("bias_b", bias_b)):
+        _dev(t, nm, xa.dtype)
+    _dev(xb_prev, "xb_prev", xa.dtype); _dev(zb_prev, "zb_prev", xa.dtype)
+    n_seq, n_tok, dim = xa.shape
+    for t in (za, xb, zb):
+        if tuple(t.shape) != (n_seq, n_tok, dim):
+            raise ValueError("xa, za, xb and zb must have the same shape")
+    if out is None:
+        out = torch.empty(n_seq, n_tok // m, dim, dtype=xa.dtype, device=xa.device)
+    check("csa_compress_c4a", lib().csa_compress_c4a(
+        _p(xa), _p(za), _p(xb), _p(zb), _p(bias_a), _p(bias_b), _p(xb_prev), _p(zb_prev),
+        _p(out), n_seq, n_tok, out_seq_stride, dim, m, _dtype(xa), _stream()))
+    return out
+
+
 def quantize_mxfp4(x: torch.Tensor, codes: torch.Tensor | None = None,
                    scales: torch.Tensor | None = None):
     """csa_quantize_mxfp4: rows x [..., dim] -> (codes uint8 [..., dim/2], scales uint8 [..., dim/32])."""

@@ -39,6 +39,7 @@ SIGNATURES = {
     "csa_abi_version": (i32, []),
     "csa_status_str": (C.c_char_p, [i32]),
     "csa_compress": (i32, [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]),
+    "csa_compress_c4a": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]),
     "csa_quantize_mxfp4": (i32, [vp, vp, vp, i64, i32, i32, vp]),
     "csa_index_topk_workspace_size": (sz, [i64, i64, i64, i32]),
     "csa_index_topk": (i32, [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, i32, i32,

@@ -208,6 +208,25 @@ int csa_compress(const void* x, const void* logits, const void* bias, void* out,
                                    dim, m, static_cast<hipStream_t>(stream)));
 }
 
+int csa_compress_c4a(const void* xa, const void* za, const void* xb, const void* zb,
+                     const void* bias_a, const void* bias_b, const void* xb_prev,
+                     const void* zb_prev, void* out, int64_t n_seq, int64_t n_tok,
+                     int64_t out_seq_stride, int32_t dim, int32_t m, int32_t dtype,
+                     void* stream) {
+  if (!dtype_ok(dtype)) return CSA_ERR_DTYPE;
+  if (n_seq < 0 || n_tok < 0 || m < 1 || m > 16 || dim < 8 || dim > 8192 || (dim % 8) != 0)
+    return CSA_ERR_SHAPE;
+  if (n_tok % m != 0) return CSA_ERR_SHAPE;
+  if (out_seq_stride != 0 && out_seq_stride < (n_tok / m) * dim) return CSA_ERR_SHAPE;
+  if (out_seq_stride % 8 != 0) return CSA_ERR_SHAPE;
+  if ((xb_prev == nullptr) != (zb_prev == nullptr)) return CSA_ERR_NULL;
+  if (n_seq * n_tok == 0) return CSA_OK;
+  if (!xa || !za || !xb || !zb || !bias_a || !bias_b || !out) return CSA_ERR_NULL;
+  return status_of(launch_compress_c4a(dtype, xa, za, xb, zb, bias_a, bias_b, xb_prev, zb_prev,
+                                       out, n_seq, n_tok, out_seq_stride, dim, m,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int csa_quantize_mxfp4(const void* x, void* codes, void* scales, int64_t n_rows, int32_t dim,
                        int32_t dtype, void* stream) {
   if (!dtype_ok(dtype)) return CSA_ERR_DTYPE;

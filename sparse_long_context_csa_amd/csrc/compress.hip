@@ -57,6 +57,162 @@ hipError_t launch_compress(int dt, const void* x, const void* z, const void* bia
   return hipGetLastError();
 }
 
+// ---- overlapped two-stream compressor ("c4a" at m = 4) ----------------------------------
+// Entry e of the chunk pools the a-stream rows of its own block [m e, m e + m) and the
+// b-stream rows of the block before [m(e-1), m e) (for e = 0 the caller's previous rows, or
+// none at the start of a sequence) under one softmax over the 2m logits per channel. Each
+// thread owns 8 channels of one entry; the rows stream through an online softmax (a running
+// maximum, the sum and the weighted sum rescaled when the maximum rises), so the registers do
+// not grow with m. All 2m rows' loads of a thread are independent and issue together.
+template <typename T>
+__device__ __forceinline__ void c4a_row(const T* x, const T* z, const T* b, float (&mx)[8],
+                                        float (&sum)[8], float (&acc)[8]) {
+  float xv[8], zv[8], bv[8];
+  Elt<T>::load8(x, xv);
+  Elt<T>::load8(z, zv);
+  Elt<T>::load8(b, bv);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float l = zv[c] + bv[c];
+    if (l > mx[c]) {
+      const float r = expf(mx[c] - l);        // 0 when mx is -inf (first row)
+      sum[c] *= r;
+      acc[c] *= r;
+      mx[c] = l;
+    }
+    const float p = expf(l - mx[c]);
+    sum[c] += p;
+    acc[c] = fmaf(p, xv[c], acc[c]);
+  }
+}
+
+// Rows of the entry: a-part (its block) then b-part (the block before, or the caller's
+// previous rows for e = 0, or none at the start of a sequence).
+template <typename T>
+struct C4aRows {
+  const T *xa, *za, *xb, *zb;
+  bool has_b;
+};
+template <typename T>
+__device__ __forceinline__ C4aRows<T> c4a_rows(const T* xa, const T* za, const T* xb,
+                                               const T* zb, const T* xb_prev, const T* zb_prev,
+                                               int64_t sq, int64_t e, int64_t n_tok, int m,
+                                               int dim, int c0) {
+  C4aRows<T> r;
+  const int64_t ra = sq * n_tok + e * m;
+  r.xa = xa + ra * dim + c0;
+  r.za = za + ra * dim + c0;
+  r.has_b = e > 0 || xb_prev != nullptr;
+  const int64_t rb = e > 0 ? sq * n_tok + (e - 1) * m : sq * m;
+  r.xb = (e > 0 ? xb : xb_prev) + rb * dim + c0;
+  r.zb = (e > 0 ? zb : zb_prev) + rb * dim + c0;
+  return r;
+}
+
+// kM > 0: m == kM rows per part, all 2 kM rows loaded before any arithmetic (one round trip),
+// then a two-pass softmax in registers; kM == 0: any m, the online softmax above.
+template <typename T, int kM>
+__global__ __launch_bounds__(256) void compress_c4a_kernel(
+    const T* __restrict__ xa, const T* __restrict__ za, const T* __restrict__ xb,
+    const T* __restrict__ zb, const T* __restrict__ ba, const T* __restrict__ bb,
+    const T* __restrict__ xb_prev, const T* __restrict__ zb_prev, T* __restrict__ out,
+    int64_t n_seq, int64_t n_ent, int64_t out_seq_stride, int dim, int m) {
+  const int vpe = dim >> 3;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= n_seq * n_ent * vpe) return;
+  const int v = int(gid % vpe);
+  const int64_t se = gid / vpe;
+  const int64_t e = se % n_ent, sq = se / n_ent;
+  const int c0 = v << 3;
+  const C4aRows<T> R = c4a_rows(xa, za, xb, zb, xb_prev, zb_prev, sq, e, n_ent * m, m, dim, c0);
+  float res[8];
+  if constexpr (kM > 0) {
+    float xv[2 * kM][8], lv[2 * kM][8];
+#pragma unroll
+    for (int j = 0; j < kM; ++j) {
+      Elt<T>::load8(R.xa + j * dim, xv[j]);
+      Elt<T>::load8(R.za + j * dim, lv[j]);
+      if (R.has_b) {
+        Elt<T>::load8(R.xb + j * dim, xv[kM + j]);
+        Elt<T>::load8(R.zb + j * dim, lv[kM + j]);
+      }
+    }
+    float mx[8], sum[8], acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { mx[c] = neg_inf(); sum[c] = 0.f; acc[c] = 0.f; }
+#pragma unroll
+    for (int j = 0; j < 2 * kM; ++j) {
+      if (j >= kM && !R.has_b) break;
+      float bv[8];
+      Elt<T>::load8((j < kM ? ba : bb) + (j % kM) * dim + c0, bv);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        lv[j][c] += bv[c];
+        mx[c] = fmaxf(mx[c], lv[j][c]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * kM; ++j) {
+      if (j >= kM && !R.has_b) break;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float p = expf(lv[j][c] - mx[c]);
+        sum[c] += p;
+        acc[c] = fmaf(p, xv[j][c], acc[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) res[c] = acc[c] / sum[c];
+  } else {
+    float mx[8], sum[8], acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { mx[c] = neg_inf(); sum[c] = 0.f; acc[c] = 0.f; }
+#pragma unroll 4
+    for (int j = 0; j < m; ++j)
+      c4a_row<T>(R.xa + j * dim, R.za + j * dim, ba + j * dim + c0, mx, sum, acc);
+    if (R.has_b) {
+#pragma unroll 4
+      for (int j = 0; j < m; ++j)
+        c4a_row<T>(R.xb + j * dim, R.zb + j * dim, bb + j * dim + c0, mx, sum, acc);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) res[c] = acc[c] / sum[c];
+  }
+  Elt<T>::store8(out + sq * out_seq_stride + e * dim + c0, res);
+}
+
+hipError_t launch_compress_c4a(int dt, const void* xa, const void* za, const void* xb,
+                               const void* zb, const void* ba, const void* bb,
+                               const void* xb_prev, const void* zb_prev, void* out,
+                               int64_t n_seq, int64_t n_tok, int64_t out_seq_stride, int dim,
+                               int m, hipStream_t s) {
+  const int64_t n_ent = n_tok / m;
+  const int64_t total = n_seq * n_ent * (dim / 8);
+  if (total == 0) return hipSuccess;
+  const int64_t stride = out_seq_stride ? out_seq_stride : n_ent * dim;
+  const dim3 grid(unsigned((total + 255) / 256)), block(256);
+#define CSA_C4A(TT, KM)                                                                      \
+  do {                                                                                       \
+    auto* kfn = &compress_c4a_kernel<TT, KM>;                                                \
+    hipLaunchKernelGGL(kfn, grid, block, 0, s, (const TT*)xa, (const TT*)za, (const TT*)xb, \
+                       (const TT*)zb, (const TT*)ba, (const TT*)bb, (const TT*)xb_prev,      \
+                       (const TT*)zb_prev, (TT*)out, n_seq, n_ent, stride, dim, m);          \
+  } while (0)
+  if (dt == kBF16) {
+    if (m == 4) CSA_C4A(uint16_t, 4);
+    else if (m == 2) CSA_C4A(uint16_t, 2);
+    else if (m == 1) CSA_C4A(uint16_t, 1);
+    else CSA_C4A(uint16_t, 0);
+  } else {
+    if (m == 4) CSA_C4A(float, 4);
+    else if (m == 2) CSA_C4A(float, 2);
+    else if (m == 1) CSA_C4A(float, 1);
+    else CSA_C4A(float, 0);
+  }
+#undef CSA_C4A
+  return hipGetLastError();
+}
+
 // ---- decode ingest: new rows -> tails / rings, pool the block when it completes ---------
 // One thread per 8-channel vector (see ingest_vector). blockIdx.y = sequence.
 template <typename T>

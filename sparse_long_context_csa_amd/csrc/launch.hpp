@@ -14,6 +14,14 @@ hipError_t launch_compress(int dt, const void* x, const void* z, const void* bia
                            int64_t n_seq, int64_t n_tok, int64_t out_seq_stride, int dim, int m,
                            hipStream_t s);
 
+// overlapped two-stream compressor: entry e pools a-rows [m e, m e + m) and b-rows
+// [m(e-1), m e) (xb_prev/zb_prev [n_seq, m, dim] for e = 0, or none when null)
+hipError_t launch_compress_c4a(int dt, const void* xa, const void* za, const void* xb,
+                               const void* zb, const void* ba, const void* bb,
+                               const void* xb_prev, const void* zb_prev, void* out,
+                               int64_t n_seq, int64_t n_tok, int64_t out_seq_stride, int dim,
+                               int m, hipStream_t s);
+
 struct IngestArgs {
   int dt;
   int64_t n_seq, e_cap;

@@ -38,7 +38,7 @@ def test_header_declares_the_calls():
         "csa_abi_version", "csa_status_str", "csa_compress", "csa_index_topk_workspace_size",
         "csa_index_topk", "csa_index_blocks_workspace_size", "csa_index_blocks",
         "csa_sparse_attn_workspace_size", "csa_sparse_attn", "csa_decode_step_workspace_size",
-        "csa_decode_step", "csa_quantize_mxfp4"}
+        "csa_decode_step", "csa_quantize_mxfp4", "csa_compress_c4a"}
 
 
 def test_binding_covers_every_declared_function():
@@ -141,6 +141,22 @@ def _desc(**kw) -> _lib.DecodeDesc:
     for k, v in kw.items():
         setattr(d, k, v)
     return d
+
+
+def test_compress_c4a_validation(lib):
+    ok = C.c_void_p(16)   # never dereferenced: every call below fails validation or is empty
+    def call(xb_prev=None, zb_prev=None, n_tok=8, dim=64, m=4, dtype=1, stride=0, xa=ok):
+        return lib.csa_compress_c4a(xa, ok, ok, ok, ok, ok, xb_prev, zb_prev, ok, 1, n_tok,
+                                    stride, dim, m, dtype, None)
+    assert call(dtype=7) == -3
+    assert call(m=0) == -2 and call(m=17) == -2
+    assert call(n_tok=9) == -2                     # n_tok % m
+    assert call(dim=60) == -2
+    assert call(stride=64) == -2                   # stride below 2 entries x 64
+    assert call(xb_prev=ok) == -1                  # one previous block pointer without the other
+    assert call(xa=None) == -1
+    assert lib.csa_compress_c4a(None, None, None, None, None, None, None, None, None, 0, 8, 0,
+                                64, 4, 1, None) == 0   # empty
 
 
 def test_quantize_mxfp4_validation(lib):

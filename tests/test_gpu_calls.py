@@ -56,6 +56,72 @@ def test_compress_into_cache_offset():
     assert_pooled(got[:, e0:e0 + n_tok // m], exact, pooled_xmax(f64(x), m), "cache offset")
 
 
+# ---------------------------------------------------------- overlapped two-stream compressor
+@pytest.mark.parametrize("dtype,m,dim,n_tok,n_seq,prev", [
+    ("bf16", 4, 512, 4096, 2, False),      # the prefill chunk's shape, start of the sequence
+    ("bf16", 4, 512, 1024, 3, True),       # a chunk in the middle of the sequence
+    ("bf16", 1, 128, 96, 2, True),
+    ("bf16", 2, 256, 128, 2, True),
+    ("bf16", 2, 256, 128, 1, False),
+    ("bf16", 8, 64, 512, 1, False),
+    ("bf16", 16, 136, 256, 2, True),       # m = 16, dim not a multiple of 64
+    ("f32", 4, 64, 256, 2, True),
+    ("f32", 3, 8, 48, 1, False),
+])
+def test_compress_c4a(dtype, m, dim, n_tok, n_seq, prev):
+    sh = (n_seq, n_tok, dim)
+    xa, za = T(40, sh, dtype, 1.0, m, dim), T(41, sh, dtype, 2.0, m, dim)
+    xb, zb = T(42, sh, dtype, 1.0, m, dim), T(43, sh, dtype, 2.0, m, dim)
+    ba, bb = T(44, (m, dim), dtype, 0.5, m, dim), T(45, (m, dim), dtype, 0.5, m, dim)
+    xp = T(46, (n_seq, m, dim), dtype, 1.0, m, dim) if prev else None
+    zp = T(47, (n_seq, m, dim), dtype, 2.0, m, dim) if prev else None
+    out = csa.compress_c4a(dev(xa), dev(za), dev(xb), dev(zb), dev(ba), dev(bb), m,
+                           xb_prev=dev(xp), zb_prev=dev(zp))
+    torch.cuda.synchronize()
+    ref64 = ocsa.compress_c4a(f64(xa), f64(za), f64(xb), f64(zb), f64(ba), f64(bb), m,
+                              None if xp is None else f64(xp), None if zp is None else f64(zp))
+    got = f64(out.cpu())
+    # each entry's 2m rows: a-part of its block, b-part of the block before
+    xab = np.abs(f64(xa)).reshape(n_seq, n_tok // m, m, dim).max(axis=2)
+    xbb = np.abs(f64(xb)).reshape(n_seq, n_tok // m, m, dim).max(axis=2)
+    xmax = xab.copy()
+    xmax[:, 1:] = np.maximum(xmax[:, 1:], xbb[:, :-1])
+    if xp is not None:
+        xmax[:, 0] = np.maximum(xmax[:, 0], np.abs(f64(xp)).max(axis=1))
+    if dtype == "bf16":
+        assert_pooled(got, ref64, xmax, "compress_c4a")
+        frac = np.mean(got == ocsa.round_bf16(ref64))
+        assert frac > 0.999, frac
+    else:
+        # fp32 online softmax over 2m rows: a few ulp of the largest row per entry
+        ratio = float((np.abs(got - ref64) / xmax).max())
+        assert ratio < 4e-6, ratio
+
+
+def test_compress_c4a_chunks_into_a_cache():
+    """Two chunks of one sequence written into a cache at entry offsets, the second with the
+    first chunk's last b-stream block as its previous block: the cache equals the whole."""
+    m, dim, n_tok, e_cap = 4, 512, 512, 300
+    sh = (1, 2 * n_tok, dim)
+    xa, za, xb, zb = (T(50 + i, sh) for i in range(4))
+    ba, bb = T(54, (m, dim), "bf16", 0.5), T(55, (m, dim), "bf16", 0.5)
+    cache = torch.zeros(1, e_cap, dim, dtype=torch.bfloat16, device="cuda")
+    g = [dev(t) for t in (xa, za, xb, zb)]
+    n_ent = n_tok // m
+    csa.compress_c4a(*(t[:, :n_tok] for t in g), dev(ba), dev(bb), m, out=cache,
+                     out_seq_stride=e_cap * dim)
+    csa.compress_c4a(*(t[:, n_tok:] for t in g), dev(ba), dev(bb), m,
+                     xb_prev=g[2][:, n_tok - m:n_tok].contiguous(),
+                     zb_prev=g[3][:, n_tok - m:n_tok].contiguous(),
+                     out=cache[:, n_ent:], out_seq_stride=e_cap * dim)
+    torch.cuda.synchronize()
+    got = f64(cache.cpu())
+    exact = ocsa.compress_c4a(f64(xa), f64(za), f64(xb), f64(zb), f64(ba), f64(bb), m)
+    assert np.all(got[:, 2 * n_ent:] == 0)
+    xm = np.abs(np.concatenate([f64(xa), f64(xb)], axis=-1)).max()
+    assert_pooled(got[:, :2 * n_ent], exact, xm, "c4a chunks")
+
+
 # ------------------------------------------------------------------------------ index + top-k
 def index_case(B, Q, E, H, d, dtype, t_lo, t_hi, m=4, seed=0):
     q = T(10, (B, Q, H, d), dtype, 1 / math.sqrt(d), seed)
