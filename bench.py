@@ -206,6 +206,90 @@ def bench_prefill(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_hca(args):
+    """Heavily Compressed Attention decode at 1M context (batch 4, m' = 128, 8,192 entries per
+    sequence, no indexer): per step the completed 128-row block of every sequence is pooled
+    into its cache (csa_compress) and every query attends densely to all visible entries, the
+    window and the sink (csa_sparse_attn with top_k = all). The ring already holds the new
+    token's row (prepared before timing), so steps repeat the same work."""
+    import torch
+
+    import datagen
+    import sparse_long_context_csa_amd as csa
+
+    spec = datagen.HCA_DECODE
+    case = datagen.make_case(spec)
+    dev = torch.device("cuda:0")
+    B, m, E, D, H = spec.B, spec.m, spec.entries, spec.D, spec.H
+    pos = case["pos"]
+    t = int(pos[0])
+    e_new = (t + 1) // m - 1
+    copies = max(1, args.copies)
+    states = []
+    for _ in range(copies):
+        xb, zb = case["x_tail"].clone(), case["z_tail"].clone()
+        ring = case["rings"][0].clone()
+        for b in range(B):
+            xb[b, t % m] = case["x_new"][b]
+            zb[b, t % m] = case["z_new"][b]
+            ring[b, t % spec.w_cap] = case["x_new"][b]
+        states.append({"x": xb.to(dev), "z": zb.to(dev), "kv": case["kv"].to(dev),
+                       "ring": ring.to(dev)})
+    q = case["q"][0].unsqueeze(1).contiguous().to(dev)
+    sink = case["sink"][0].to(dev)
+    bias = case["bias"].to(dev)
+    qp = pos.view(B, 1).to(dev)
+    idx = torch.arange(E, dtype=torch.int32).repeat(B, 1, 1).contiguous().to(dev)
+    outs = [torch.empty(B, 1, H, D, dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+
+    def step(c, evs=None):
+        st = states[c]
+        if evs: evs[0].record()
+        csa.compress(st["x"], st["z"], bias, m, out=st["kv"][:, e_new:], out_seq_stride=E * D)
+        if evs: evs[1].record()
+        csa.sparse_attn(q, st["kv"], idx, st["ring"], spec.w_cap, spec.W, qp, sink,
+                        case["scale"], out=outs[c])
+        if evs: evs[2].record()
+
+    for i in range(args.warmup):
+        step(i % copies)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % copies)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n_prof = min(args.steps, 100)
+    ph = [0.0, 0.0]
+    for i in range(n_prof):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        step(i % copies, evs)
+        torch.cuda.synchronize()
+        ph[0] += evs[0].elapsed_time(evs[1]) / n_prof
+        ph[1] += evs[1].elapsed_time(evs[2]) / n_prof
+    attn_bytes = B * (E + spec.W) * D * 2 + 2 * B * H * D * 2 + B * E * 4 + H * 4
+    comp_bytes = B * (2 * m * D * 2 + D * 2) + m * D * 2
+    achieved = attn_bytes / (ph[1] * 1e-3) / 1e9
+    res = {
+        "metric": "HCA decode queries/sec at 1M ctx (dense attention over 8,192 entries)",
+        "value": round(B * args.steps / wall, 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": datagen.WORKLOAD_NAMES[6], "batch": B, "context": spec.L,
+                   "m": m, "entries": E, "top_k": "all", "window": spec.W, "heads": H,
+                   "head_dim": D, "state_copies": copies},
+        "roofline": {"bound": "hbm", "kernel": "attn_dma_kernel + attn_combine_kernel",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_call": attn_bytes,
+                     "timing": "torch events around the csa_sparse_attn call (launches included)"},
+        "phases_us": {"compress": round(ph[0] * 1e3, 2), "attention": round(ph[1] * 1e3, 2)},
+        "compress_bytes": comp_bytes,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,8 +302,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step from a captured HIP graph instead of launching it")
-    ap.add_argument("--config", type=int, default=4, choices=(2, 3, 4, 5),
-                    help="workload (4: the 1M-context decode headline; 3: chunked prefill)")
+    ap.add_argument("--config", type=int, default=4, choices=(2, 3, 4, 5, 6),
+                    help="workload (4: the 1M-context decode headline; 3: chunked prefill; "
+                         "6: HCA decode, dense attention over 8,192 entries)")
     ap.add_argument("--idx-format", default="bf16", choices=("bf16", "mxfp4"),
                     help="indexer-key cache of the decode workloads: bf16 keys, or MXFP4 codes "
                          "with one scale byte per 32 channels (csa_quantize_mxfp4 of the same "
@@ -245,6 +330,8 @@ def main():
 
     if args.config == 3:
         return bench_prefill(args)
+    if args.config == 6:
+        return bench_hca(args)
     spec = datagen.CONFIGS[args.config]
     t0 = time.time()
     case = datagen.make_case(spec)

@@ -128,12 +128,17 @@ CONFIGS = {
     5: CaseSpec(5, "decode", B=4, L=262144, m=1, w_cap=128, block_size=8, max_blocks=2048, n_attn=3),
 }
 
+# A second workload beyond the five: Heavily Compressed Attention at 1M context (m' = 128, one
+# stream, no indexer: dense attention over every entry, 8,192 per sequence, plus the window).
+HCA_DECODE = CaseSpec(6, "decode", B=4, L=1048576, m=128, K=8192, w_cap=128, key_sigma=0.5)
+
 WORKLOAD_NAMES = {
     1: "tiny CSA forward fp32, 2048 tokens, 512 entries, 4x32 indexer, 4x64 heads",
     2: "decode bf16, batch 8, 65,536 ctx (16,384 entries)",
     3: "chunked prefill bf16, 4,096 queries at the end of 131,072 ctx (32,768 entries)",
     4: "1M-ctx decode bf16, batch 4, 1,048,576 ctx (262,144 entries), log-normal key norms",
     5: "hierarchical decode bf16, batch 4, 262,144 ctx 1:1, pool 2,048x8, 3 attention calls",
+    6: "HCA decode bf16, batch 4, 1,048,576 ctx 128:1 (8,192 entries), dense attention",
 }
 
 

@@ -69,7 +69,8 @@ const char *csa_status_str(int status);
  *   out       : T, entry e of sequence s at out + s*out_seq_stride + e*dim
  *               (out_seq_stride = 0 means dense: (n_tok/m)*dim). Writing into a cache at
  *               an entry offset is done by offsetting `out` and passing the cache stride.
- * Limits: 1 <= m <= 16, n_tok % m == 0, 1 <= dim <= 8192, dim % 8 == 0.
+ * Limits: 1 <= m <= 128 (HCA pools m' = 128: [CoD] "Heavily Compressed Attention"),
+ * n_tok % m == 0, 8 <= dim <= 8192, dim % 8 == 0.
  * ------------------------------------------------------------------------------------- */
 int csa_compress(const void *x, const void *logits, const void *bias, void *out,
                  int64_t n_seq, int64_t n_tok, int64_t out_seq_stride, int32_t dim,

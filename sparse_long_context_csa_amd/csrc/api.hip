@@ -197,7 +197,7 @@ int csa_compress(const void* x, const void* logits, const void* bias, void* out,
                  int64_t n_tok, int64_t out_seq_stride, int32_t dim, int32_t m, int32_t dtype,
                  void* stream) {
   if (!dtype_ok(dtype)) return CSA_ERR_DTYPE;
-  if (n_seq < 0 || n_tok < 0 || m < 1 || m > 16 || dim < 8 || dim > 8192 || (dim % 8) != 0)
+  if (n_seq < 0 || n_tok < 0 || m < 1 || m > 128 || dim < 8 || dim > 8192 || (dim % 8) != 0)
     return CSA_ERR_SHAPE;
   if (n_tok % m != 0) return CSA_ERR_SHAPE;
   if (out_seq_stride != 0 && out_seq_stride < (n_tok / m) * dim) return CSA_ERR_SHAPE;

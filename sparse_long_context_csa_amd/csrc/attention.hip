@@ -17,6 +17,8 @@
 // Few query rows (decode): the row list is split over workgroups; partial (max, sum,
 // unnormalised output) go to the workspace and attn_combine_kernel merges them in split
 // order (deterministic). attn_generic_kernel covers fp32 and other head shapes.
+#include <stdlib.h>
+
 #include "attn_core.hpp"
 #include "csa_common.hpp"
 #include "launch.hpp"
@@ -49,12 +51,18 @@ __device__ __forceinline__ const T* row_ptr(const AttnArgs& a, int64_t r, int64_
 // a wave's chain of LDS reads and MFMAs per tile is latency-bound, so tiles run in
 // parallel workgroups and the partial results are merged afterwards.
 constexpr int kMinTilesPerSplit = 2;
+static int attn_tune(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : dflt;
+}
 static int attn_splits(int64_t rows, int top_k, int window, int H, int D, int dt) {
   if (!(dt == kBF16 && H == kAH && D == kAD)) return 1;
   const int64_t tiles = ceil_div(int64_t(top_k) + window, kTile);
   if (rows >= 256 || tiles < 2) return 1;
-  int64_t want = ceil_div(tiles, kMinTilesPerSplit);
-  const int64_t cap = 256 / rows;
+  static const int min_tiles = attn_tune("CSA_TUNE_ATTN_MIN_TILES", kMinTilesPerSplit);
+  static const int total = attn_tune("CSA_TUNE_ATTN_WGS", 256);
+  int64_t want = ceil_div(tiles, min_tiles > 0 ? min_tiles : kMinTilesPerSplit);
+  const int64_t cap = (total > 0 ? total : 256) / rows;
   if (want > cap) want = cap;
   return int(want < 1 ? 1 : want);
 }

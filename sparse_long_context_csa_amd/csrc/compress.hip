@@ -38,6 +38,90 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ x,
   Elt<T>::store8(out + sq * out_seq_stride + e * dim + c0, res);
 }
 
+// Long entries (m > 16, HCA's m' = 128): a workgroup pools one entry for 16 vectors (128
+// channels) with 16 row groups -- thread (group g, vector v) takes rows g, g + 16, ... < m,
+// all loaded before any arithmetic, and keeps a partial softmax (maximum, sum, weighted sum);
+// the 16 partials of a vector merge in LDS. Every input row is read once.
+constexpr int kWideGroups = 16;
+constexpr int kWideVecs = 16;
+template <typename T>
+__global__ __launch_bounds__(256) void compress_wide_kernel(const T* __restrict__ x,
+                                                            const T* __restrict__ z,
+                                                            const T* __restrict__ bias,
+                                                            T* __restrict__ out, int64_t n_ent,
+                                                            int64_t out_seq_stride, int dim,
+                                                            int m) {
+  __shared__ float part[3][kWideGroups][kWideVecs][8];
+  const int vl = threadIdx.x % kWideVecs, grp = threadIdx.x / kWideVecs;
+  const int nvb = (dim / 8 + kWideVecs - 1) / kWideVecs;   // channel blocks per entry
+  const int64_t bid = blockIdx.x;
+  const int v = int(bid % nvb) * kWideVecs + vl;
+  const int64_t e = (bid / nvb) % n_ent, sq = bid / nvb / n_ent;
+  const bool live = v * 8 < dim;
+  const int c0 = v * 8;
+  const int64_t row0 = (sq * n_ent + e) * m;
+  float mx[8], sum[8], acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) { mx[c] = neg_inf(); sum[c] = 0.f; acc[c] = 0.f; }
+  if (live) {
+    constexpr int kR = 8;   // rows per thread held in registers at once (m <= 128)
+    for (int j0 = grp; j0 < m; j0 += kR * kWideGroups) {
+      float xv[kR][8], lv[kR][8];
+#pragma unroll
+      for (int i = 0; i < kR; ++i) {
+        const int j = j0 + i * kWideGroups;
+        if (j < m) {
+          Elt<T>::load8(x + (row0 + j) * dim + c0, xv[i]);
+          Elt<T>::load8(z + (row0 + j) * dim + c0, lv[i]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kR; ++i) {
+        const int j = j0 + i * kWideGroups;
+        if (j < m) {
+          float bv[8];
+          Elt<T>::load8(bias + j * dim + c0, bv);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float l = lv[i][c] + bv[c];
+            if (l > mx[c]) {
+              const float r = expf(mx[c] - l);
+              sum[c] *= r;
+              acc[c] *= r;
+              mx[c] = l;
+            }
+            const float p = expf(l - mx[c]);
+            sum[c] += p;
+            acc[c] = fmaf(p, xv[i][c], acc[c]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    part[0][grp][vl][c] = mx[c];
+    part[1][grp][vl][c] = sum[c];
+    part[2][grp][vl][c] = acc[c];
+  }
+  __syncthreads();
+  // thread (g, vl) merges channel g & 7 of vector vl for g < 8
+  if (grp < 8 && live) {
+    const int c = grp;
+    float M = neg_inf();
+#pragma unroll
+    for (int g2 = 0; g2 < kWideGroups; ++g2) M = fmaxf(M, part[0][g2][vl][c]);
+    float S = 0.f, A = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < kWideGroups; ++g2) {
+      const float w = part[1][g2][vl][c] > 0.f ? expf(part[0][g2][vl][c] - M) : 0.f;
+      S = fmaf(part[1][g2][vl][c], w, S);
+      A = fmaf(part[2][g2][vl][c], w, A);
+    }
+    Elt<T>::store1(out + sq * out_seq_stride + e * dim + c0 + c, A / S);
+  }
+}
+
 hipError_t launch_compress(int dt, const void* x, const void* z, const void* bias, void* out,
                            int64_t n_seq, int64_t n_tok, int64_t out_seq_stride, int dim, int m,
                            hipStream_t s) {
@@ -45,6 +129,18 @@ hipError_t launch_compress(int dt, const void* x, const void* z, const void* bia
   const int64_t total = n_seq * n_ent * (dim / 8);
   if (total == 0) return hipSuccess;
   const int64_t stride = out_seq_stride ? out_seq_stride : n_ent * dim;
+  if (m > 16) {
+    const dim3 gw(unsigned(int64_t((dim / 8 + kWideVecs - 1) / kWideVecs) * n_ent * n_seq));
+    if (dt == kBF16)
+      hipLaunchKernelGGL(compress_wide_kernel<uint16_t>, gw, dim3(256), 0, s,
+                         (const uint16_t*)x, (const uint16_t*)z, (const uint16_t*)bias,
+                         (uint16_t*)out, n_ent, stride, dim, m);
+    else
+      hipLaunchKernelGGL(compress_wide_kernel<float>, gw, dim3(256), 0, s, (const float*)x,
+                         (const float*)z, (const float*)bias, (float*)out, n_ent, stride, dim,
+                         m);
+    return hipGetLastError();
+  }
   const dim3 grid(unsigned((total + 255) / 256)), block(256);
   if (dt == kBF16)
     hipLaunchKernelGGL(compress_kernel<uint16_t>, grid, block, 0, s, (const uint16_t*)x,

@@ -97,7 +97,7 @@ def test_compress_validation(lib):
     ok = C.c_void_p(16)   # never dereferenced: every call below fails validation or is empty
     assert lib.csa_compress(ok, ok, ok, ok, 1, 8, 0, 64, 4, 7, None) == -3
     assert lib.csa_compress(ok, ok, ok, ok, 1, 8, 0, 64, 0, 1, None) == -2
-    assert lib.csa_compress(ok, ok, ok, ok, 1, 8, 0, 64, 17, 1, None) == -2
+    assert lib.csa_compress(ok, ok, ok, ok, 1, 256, 0, 64, 129, 1, None) == -2
     assert lib.csa_compress(ok, ok, ok, ok, 1, 9, 0, 64, 4, 1, None) == -2      # n_tok % m
     assert lib.csa_compress(ok, ok, ok, ok, 1, 8, 0, 60, 4, 1, None) == -2      # dim % 8
     assert lib.csa_compress(ok, ok, ok, ok, 1, 8, 64, 64, 4, 1, None) == -2     # stride short

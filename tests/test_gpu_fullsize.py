@@ -74,3 +74,45 @@ def test_prefill_workload_fullsize():
     for (b, i), ids in ref["ids"].items():
         assert_ids(idx[b, i].numpy(), ids, f"query row {i}")
         assert_rows_close(f64(out[b, i]), ref["out"][(b, i)], 2e-2, f"query row {i}")
+
+
+def test_hca_decode_fullsize():
+    """Heavily Compressed Attention at 1M context (m' = 128, 8,192 entries per sequence): the
+    completed 128-row block is pooled by csa_compress into the cache, then csa_sparse_attn
+    attends to every visible entry (top_k = all 8,192) plus the window and the sink. The oracle's
+    decode step with K >= the visible count selects every entry, which is the dense form."""
+    spec = datagen.HCA_DECODE
+    case = datagen.make_case(spec)
+    print("HCA: inputs ready", flush=True)
+    ref = pipeline.decode_step(case)
+    g = {k: dev(v) for k, v in case.items() if isinstance(v, torch.Tensor)}
+    B, m, E, D = spec.B, spec.m, spec.entries, spec.D
+    pos = case["pos"]
+    kv = g["kv"].clone()
+    ring = dev(case["rings"][0]).clone()
+    xb, zb = g["x_tail"].clone(), g["z_tail"].clone()
+    n_vis = []
+    for b in range(B):
+        t = int(pos[b])
+        xb[b, t % m] = g["x_new"][b]
+        zb[b, t % m] = g["z_new"][b]
+        ring[b, t % spec.w_cap] = g["x_new"][b]
+        n_vis.append(ocsa.n_visible(t, m, E))
+    e_new = [(int(pos[b]) + 1) // m - 1 for b in range(B)]
+    assert len(set(e_new)) == 1 and all((int(pos[b]) + 1) % m == 0 for b in range(B))
+    csa.compress(xb, zb, g["bias"], m, out=kv[:, e_new[0]:], out_seq_stride=E * D)
+    idx = torch.full((B, 1, E), -1, dtype=torch.int32)
+    for b in range(B):
+        idx[b, 0, :n_vis[b]] = torch.arange(n_vis[b], dtype=torch.int32)
+    out = csa.sparse_attn(dev(case["q"][0]).unsqueeze(1), kv, dev(idx), ring, spec.w_cap,
+                          spec.W, g["pos"].view(B, 1), dev(case["sink"][0]), case["scale"])
+    torch.cuda.synchronize()
+    for b in range(B):
+        assert ref["ids"][b].tolist() == list(range(n_vis[b])) + [-1] * (E - n_vis[b])
+        x = f64(case["x_tail"][b]).copy()
+        x[int(pos[b]) % m] = f64(case["x_new"][b])
+        assert_pooled(f64(kv[b, e_new[b]].cpu()), ocsa.compress(
+            x, np.where(np.arange(m)[:, None] == int(pos[b]) % m, f64(case["z_new"][b]),
+                        f64(case["z_tail"][b])), f64(case["bias"]), m)[0],
+            np.abs(x).max(axis=0), f"HCA entry of seq {b}", m=m)
+        assert_rows_close(f64(out[b, 0].cpu()), ref["out"][b][0], 2e-2, f"HCA seq {b}")
