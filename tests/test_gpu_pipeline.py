@@ -151,6 +151,50 @@ def test_decode_step_mxfp4_keys(spec):
     assert torch.equal(idx2.cpu(), idx)
 
 
+@pytest.mark.parametrize("spec", [
+    # a cache capacity that is not a multiple of the 64-key tile, rows ragged below it
+    datagen.CaseSpec(7124, "decode", B=3, L=4 * 40003, e_cap=40003, m=4, w_cap=128,
+                     ragged=True),
+    datagen.CaseSpec(7125, "decode", B=2, L=8 * 5000, m=8, w_cap=128, ragged=True),
+    datagen.CaseSpec(7126, "decode", B=2, L=2 * 30000, m=2, K=500, W=100, w_cap=128,
+                     ragged=True),
+], ids=["e_cap_40003", "m8", "m2_odd_k"])
+def test_decode_step_mxfp4_keys_edges(spec):
+    case, idx_state = mxfp4_case(spec)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    _, st, rings, out, idx = run_step(case, idx_state)
+    check_step(case, ref, st, rings, out, idx)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4_keys", "bf16_scores"])
+def test_decode_step_clustered_winners_formats(fmt):
+    # the Top-K concentrated in a few chunks (their thresholds exceed the K-th key): the select
+    # streams over the full scores, with MXFP4 keys or with bf16 scores
+    spec = datagen.CaseSpec(7112, "decode", B=2, L=4 * 50000, m=4, w_cap=128)
+    case = datagen.make_case(spec)
+    k = case["k_idx"]
+    k[0, 20000:21500] = (k[0, 20000:21500].float() * 2).to(k.dtype)
+    k[1, 7000:7300] = (k[1, 7000:7300].float() * 2).to(k.dtype)
+    idx_state = None
+    if fmt == "mxfp4_keys":
+        from oracle import mx
+        codes, scales = mx.quantize(f64(k))
+        kq = torch.from_numpy(mx.dequantize(codes, scales)).to(k.dtype)
+        kc, ks = csa.quantize_mxfp4(dev(k))
+        case["k_idx"] = kq
+        case["idx_format"] = "mxfp4"
+        idx_state = {"k_idx": kc, "k_idx_scale": ks}
+    else:
+        case["score_format"] = "bf16"
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    ids0 = ref["ids"][0]
+    assert np.sum((ids0 >= 20000) & (ids0 < 21500)) > 100   # far above 512 / 25 chunks
+    _, st, rings, out, idx = run_step(case, idx_state)
+    check_step(case, ref, st, rings, out, idx)
+
+
 # BF16 index scores: the scan rounds every score to bf16 before it leaves; the selection (ties
 # at the K-th value to the lower id) must match the oracle's ranking of its fp32 scores rounded
 # to bf16, id for id.
