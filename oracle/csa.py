@@ -162,6 +162,39 @@ def compress_c4a(Xa, Za, Xb, Zb, bias_a, bias_b, m: int, Xb_prev=None, Zb_prev=N
     return out
 
 
+def rms_norm(x, gamma, eps: float = 1e-6) -> np.ndarray:
+    """Per-vector RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * gamma.
+
+    [CoD "Key and value are the same vector" (the output-projection passage): RMSNorm per head
+    on the queries and on the single head of the compressed KV entries, just before the core
+    attention; the norm weights are learned.] eps is not printed on the pages:
+    1e-6 (reading)."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * g
+
+
+def rope(x, pos, rope_dim: int = 64, base: float = 10000.0) -> np.ndarray:
+    """Rotary position embedding on the last rope_dim channels of each vector.
+
+    [CoD "Key and value are the same vector": RoPE on the last 64 dimensions of each head;
+    applying it with position -i to the output undoes a rotation R(i) because R is orthogonal
+    and R(t)^-1 R(s) = R(s-t).] Not printed on the pages (reading): channel pairs (2j, 2j+1)
+    of the rotated part, angle pos * base^(-2j/rope_dim), base 10000 -- the original RoPE form.
+    x [..., d]; pos broadcastable to x[..., 0] (per vector). Returns float64."""
+    x = np.asarray(x, dtype=np.float64).copy()
+    d = x.shape[-1]
+    p = np.asarray(pos, dtype=np.float64)[..., None]
+    j = np.arange(rope_dim // 2, dtype=np.float64)
+    ang = p * base ** (-2.0 * j / rope_dim)
+    c, s_ = np.cos(ang), np.sin(ang)
+    a = x[..., d - rope_dim::2].copy()
+    b = x[..., d - rope_dim + 1::2].copy()
+    x[..., d - rope_dim::2] = a * c - b * s_
+    x[..., d - rope_dim + 1::2] = a * s_ + b * c
+    return x
+
+
 # ----------------------------------------------------------------------------------------
 # causal visibility of compressed entries
 # ----------------------------------------------------------------------------------------
