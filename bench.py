@@ -290,6 +290,47 @@ def bench_hca(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_norm_rope(args):
+    """Per-head RMSNorm + partial RoPE (one fused pass) over a prefill chunk's queries: 4,096
+    rows x 64 heads x 512 (256 MiB in, 256 MiB out), positions at the end of a 131,072-token
+    context. HBM-bound: reported against 8 TB/s."""
+    import torch
+
+    import datagen
+    import sparse_long_context_csa_amd as csa
+
+    rows, heads, dim = 4096, 64, 512
+    dev = torch.device("cuda:0")
+    xs = [datagen.tensor(7, 70 + c, (rows, heads, dim), "bf16", 1.0 / math.sqrt(dim)).to(dev)
+          for c in range(2)]
+    gamma = datagen.tensor(7, 72, (dim,), "bf16", 0.5).to(dev)
+    pos = torch.arange(131072 - rows, 131072, dtype=torch.int64, device=dev)
+    outs = [torch.empty_like(x) for x in xs]
+    for i in range(args.warmup):
+        csa.norm_rope(xs[i % 2], gamma, pos, out=outs[i % 2])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        csa.norm_rope(xs[i % 2], gamma, pos, out=outs[i % 2])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nbytes = 2 * rows * heads * dim * 2 + dim * 2 + rows * 8
+    gbs = nbytes * args.steps / wall / 1e9
+    print(json.dumps({
+        "metric": "per-head RMSNorm + partial RoPE, one pass (4,096 x 64 x 512 queries)",
+        "value": round(rows * args.steps / wall, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill-chunk queries, 4,096 rows x 64 heads x 512, RoPE on the "
+                               "last 64 dims at positions 126,976..131,071",
+                   "launch": "eager, back-to-back"},
+        "roofline": {"bound": "hbm", "kernel": "norm_rope_kernel", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": nbytes,
+                     "timing": "wall clock over back-to-back launches"}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,9 +343,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step from a captured HIP graph instead of launching it")
-    ap.add_argument("--config", type=int, default=4, choices=(2, 3, 4, 5, 6),
+    ap.add_argument("--config", type=int, default=4, choices=(2, 3, 4, 5, 6, 7),
                     help="workload (4: the 1M-context decode headline; 3: chunked prefill; "
-                         "6: HCA decode, dense attention over 8,192 entries)")
+                         "6: HCA decode, dense attention over 8,192 entries; 7: the fused "
+                         "RMSNorm + RoPE pass over a prefill chunk's queries)")
     ap.add_argument("--idx-format", default="bf16", choices=("bf16", "mxfp4"),
                     help="indexer-key cache of the decode workloads: bf16 keys, or MXFP4 codes "
                          "with one scale byte per 32 channels (csa_quantize_mxfp4 of the same "
@@ -332,6 +374,8 @@ def main():
         return bench_prefill(args)
     if args.config == 6:
         return bench_hca(args)
+    if args.config == 7:
+        return bench_norm_rope(args)
     spec = datagen.CONFIGS[args.config]
     t0 = time.time()
     case = datagen.make_case(spec)

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 5
+#define CSA_ABI_VERSION 6
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -104,6 +104,30 @@ int csa_compress_c4a(const void *xa, const void *za, const void *xb, const void 
                      const void *zb_prev, void *out, int64_t n_seq, int64_t n_tok,
                      int64_t out_seq_stride, int32_t dim, int32_t m, int32_t dtype,
                      void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_norm_rope -- per-head RMSNorm and partial RoPE in one pass.
+ *   [CoD "Key and value are the same vector": RMSNorm per head on the queries and on the
+ *   single head of the compressed KV entries just before the core attention; RoPE on the last
+ *   64 dimensions of each head; RoPE with position -i on each head's output undoes the
+ *   rotation a shared key/value carries.]
+ * For row r, head h and vector v = x[r, h, :] (dim channels):
+ *   flags & CSA_NR_NORM:    v <- v / sqrt(mean(v^2) + eps) * gamma
+ *   flags & CSA_NR_ROPE:    the last rope_dim channels rotate in pairs (2j, 2j+1) (counted from
+ *                           channel dim - rope_dim) by the angle p * rope_base^(-2j/rope_dim),
+ *                           p = pos[r], or p = -pos[r] with CSA_NR_INVERSE as well
+ *   out[r, h, :] <- v (rounded once to T; out may be x)
+ *   x, out : T [n_rows, n_heads, dim]    gamma : T [dim] (with CSA_NR_NORM) or NULL
+ *   pos    : i64 [n_rows] (with CSA_NR_ROPE) or NULL
+ * Limits: 8 <= dim <= 512, dim % 8 == 0; 0 <= rope_dim <= dim, rope_dim even; rope_base > 1;
+ * eps >= 0; flags within the three bits.
+ * ------------------------------------------------------------------------------------- */
+#define CSA_NR_NORM 1
+#define CSA_NR_ROPE 2
+#define CSA_NR_INVERSE 4
+int csa_norm_rope(const void *x, const void *gamma, const int64_t *pos, void *out,
+                  int64_t n_rows, int32_t n_heads, int32_t dim, int32_t rope_dim,
+                  float rope_base, float eps, int32_t flags, int32_t dtype, void *stream);
 
 /* ---------------------------------------------------------------------------------------
  * csa_quantize_mxfp4 -- MXFP4 storage of indexer keys (production precision).

@@ -87,6 +87,24 @@ def compress_c4a(xa: torch.Tensor, za: torch.Tensor, xb: torch.Tensor, zb: torch
     return out
 
 
+def norm_rope(x: torch.Tensor, gamma: torch.Tensor | None = None,
+              pos: torch.Tensor | None = None, rope_dim: int = 64, rope_base: float = 10000.0,
+              eps: float = 1e-6, inverse: bool = False, out: torch.Tensor | None = None):
+    """csa_norm_rope over x [n_rows, n_heads, dim]: RMSNorm when gamma [dim] is given, RoPE on
+    the last rope_dim channels when pos [n_rows] (i64) is given (at -pos with inverse)."""
+    _dev(x, "x"); _dev(gamma, "gamma", x.dtype); _dev(pos, "pos", torch.int64)
+    n_rows, n_heads, dim = x.shape
+    flags = (_lib.NR_NORM if gamma is not None else 0) | (_lib.NR_ROPE if pos is not None else 0)
+    if inverse:
+        flags |= _lib.NR_INVERSE
+    if out is None:
+        out = torch.empty_like(x)
+    check("csa_norm_rope", lib().csa_norm_rope(_p(x), _p(gamma), _p(pos), _p(out), n_rows, n_heads,
+                                               dim, rope_dim, float(rope_base), float(eps), flags,
+                                               _dtype(x), _stream()))
+    return out
+
+
 def quantize_mxfp4(x: torch.Tensor, codes: torch.Tensor | None = None,
                    scales: torch.Tensor | None = None):
     """csa_quantize_mxfp4: rows x [..., dim] -> (codes uint8 [..., dim/2], scales uint8 [..., dim/32])."""

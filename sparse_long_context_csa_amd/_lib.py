@@ -14,6 +14,7 @@ MAX_ATTN = 4
 DECODE_EVENTS = 5
 IDX_DTYPE, IDX_MXFP4 = 0, 1
 SCORE_F32, SCORE_BF16 = 0, 1
+NR_NORM, NR_ROPE, NR_INVERSE = 1, 2, 4
 
 vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
 
@@ -40,6 +41,7 @@ SIGNATURES = {
     "csa_status_str": (C.c_char_p, [i32]),
     "csa_compress": (i32, [vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]),
     "csa_compress_c4a": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]),
+    "csa_norm_rope": (i32, [vp, vp, vp, vp, i64, i32, i32, i32, f32, f32, i32, i32, vp]),
     "csa_quantize_mxfp4": (i32, [vp, vp, vp, i64, i32, i32, vp]),
     "csa_index_topk_workspace_size": (sz, [i64, i64, i64, i32]),
     "csa_index_topk": (i32, [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, i32, i32,

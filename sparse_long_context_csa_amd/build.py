@@ -25,7 +25,7 @@ HIPFLAGS = [
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["compress.hip", "index_scan.hip", "index_prefill.hip", "topk.hip", "attention.hip",
+SOURCES = ["compress.hip", "index_scan.hip", "index_prefill.hip", "topk.hip", "attention.hip", "norm_rope.hip",
            "mxfp4.hip", "api.hip"]
 
 

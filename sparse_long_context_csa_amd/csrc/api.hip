@@ -227,6 +227,22 @@ int csa_compress_c4a(const void* xa, const void* za, const void* xb, const void*
                                        static_cast<hipStream_t>(stream)));
 }
 
+int csa_norm_rope(const void* x, const void* gamma, const int64_t* pos, void* out,
+                  int64_t n_rows, int32_t n_heads, int32_t dim, int32_t rope_dim,
+                  float rope_base, float eps, int32_t flags, int32_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return CSA_ERR_DTYPE;
+  if (n_rows < 0 || n_heads < 1 || dim < 8 || dim > 512 || dim % 8 != 0) return CSA_ERR_SHAPE;
+  if (rope_dim < 0 || rope_dim > dim || rope_dim % 2 != 0) return CSA_ERR_SHAPE;
+  if (!(rope_base > 1.f) || !(eps >= 0.f) || (flags & ~7) != 0) return CSA_ERR_SHAPE;
+  if ((flags & CSA_NR_INVERSE) && !(flags & CSA_NR_ROPE)) return CSA_ERR_SHAPE;
+  if (n_rows == 0) return CSA_OK;
+  if (!x || !out) return CSA_ERR_NULL;
+  if ((flags & CSA_NR_NORM) && !gamma) return CSA_ERR_NULL;
+  if ((flags & CSA_NR_ROPE) && !pos) return CSA_ERR_NULL;
+  return status_of(launch_norm_rope(dtype, x, gamma, pos, out, n_rows, n_heads, dim, rope_dim,
+                                    rope_base, eps, flags, static_cast<hipStream_t>(stream)));
+}
+
 int csa_quantize_mxfp4(const void* x, void* codes, void* scales, int64_t n_rows, int32_t dim,
                        int32_t dtype, void* stream) {
   if (!dtype_ok(dtype)) return CSA_ERR_DTYPE;

@@ -106,6 +106,13 @@ bool scan_fuses_ingest(int dt, int H, int d, int m);
 // list).
 bool scan_reads_mxfp4(int dt, int H, int d, int64_t n_q, bool cand);
 
+// ---- per-head RMSNorm and partial RoPE (norm_rope.hip) ------------------------------------
+// x, out [n_rows, n_heads, dim]; flags 1 RMSNorm (gamma [dim]), 2 RoPE on the last rope_dim
+// channels at pos[row], 4 with -pos
+hipError_t launch_norm_rope(int dt, const void* x, const void* gamma, const int64_t* pos,
+                            void* out, int64_t n_rows, int n_heads, int dim, int rope_dim,
+                            float base, float eps, int flags, hipStream_t s);
+
 // ---- MXFP4 storage of indexer keys (mxfp4.hpp) --------------------------------------------
 // x [n_rows, dim] (dim % 32 == 0) -> codes [n_rows, dim / 2] bytes, scales [n_rows, dim / 32]
 hipError_t launch_quantize_mxfp4(int dt, const void* x, void* codes, void* scales, int64_t n_rows,

@@ -38,7 +38,7 @@ def test_header_declares_the_calls():
         "csa_abi_version", "csa_status_str", "csa_compress", "csa_index_topk_workspace_size",
         "csa_index_topk", "csa_index_blocks_workspace_size", "csa_index_blocks",
         "csa_sparse_attn_workspace_size", "csa_sparse_attn", "csa_decode_step_workspace_size",
-        "csa_decode_step", "csa_quantize_mxfp4", "csa_compress_c4a"}
+        "csa_decode_step", "csa_quantize_mxfp4", "csa_compress_c4a", "csa_norm_rope"}
 
 
 def test_binding_covers_every_declared_function():
@@ -157,6 +157,20 @@ def test_compress_c4a_validation(lib):
     assert call(xa=None) == -1
     assert lib.csa_compress_c4a(None, None, None, None, None, None, None, None, None, 0, 8, 0,
                                 64, 4, 1, None) == 0   # empty
+
+
+def test_norm_rope_validation(lib):
+    ok = C.c_void_p(16)   # never dereferenced: every call below fails validation or is empty
+    def call(dim=512, rope=64, base=1e4, eps=1e-6, flags=3, dtype=1, gamma=ok, pos=ok, n=2):
+        return lib.csa_norm_rope(ok, gamma, pos, ok, n, 64, dim, rope, base, eps, flags, dtype,
+                                 None)
+    assert call(dtype=5) == -3
+    assert call(dim=520) == -2 and call(dim=12) == -2
+    assert call(rope=63) == -2 and call(rope=600) == -2
+    assert call(base=1.0) == -2 and call(eps=-1.0) == -2 and call(flags=8) == -2
+    assert call(flags=5) == -2                     # inverse without RoPE
+    assert call(gamma=None) == -1 and call(pos=None) == -1
+    assert call(n=0) == 0
 
 
 def test_quantize_mxfp4_validation(lib):

@@ -8,7 +8,7 @@ import torch
 
 import datagen
 import sparse_long_context_csa_amd as csa
-from gpu_helpers import (assert_ids, assert_pooled, assert_rows_close, assert_scores, dev,
+from gpu_helpers import (assert_ids, assert_pooled, assert_rows_close, assert_scores, bf16_ulp, dev,
                          fix_gaps, pooled_xmax)
 from oracle import csa as ocsa
 from oracle import gaps, pipeline
@@ -124,6 +124,55 @@ def test_compress_c4a_chunks_into_a_cache():
     assert np.all(got[:, 2 * n_ent:] == 0)
     xm = np.abs(np.concatenate([f64(xa), f64(xb)], axis=-1)).max()
     assert_pooled(got[:, :2 * n_ent], exact, xm, "c4a chunks")
+
+
+# ------------------------------------------------------------- per-head RMSNorm + partial RoPE
+@pytest.mark.parametrize("dtype,rows,heads,dim,rope_dim,flags", [
+    ("bf16", 4, 64, 512, 64, "norm+rope"),     # decode queries at 1M positions
+    ("bf16", 300, 1, 512, 64, "norm+rope"),    # compressed entries (one head)
+    ("bf16", 4, 64, 512, 64, "inverse"),       # the attention output
+    ("bf16", 7, 3, 136, 32, "rope"),
+    ("bf16", 5, 2, 64, 64, "norm"),
+    ("f32", 9, 4, 128, 64, "norm+rope"),
+    ("f32", 3, 2, 8, 2, "inverse"),
+])
+def test_norm_rope(dtype, rows, heads, dim, rope_dim, flags):
+    x = T(60, (rows, heads, dim), dtype, 1.0, dim)
+    gamma = T(61, (dim,), dtype, 0.5, dim) if "norm" in flags else None
+    g = np.random.default_rng(dim + rows)
+    pos = torch.from_numpy(g.integers(0, 1 << 20, size=rows).astype(np.int64))
+    use_pos = "rope" in flags or flags == "inverse"
+    out = csa.norm_rope(dev(x), dev(gamma), dev(pos) if use_pos else None, rope_dim=rope_dim,
+                        inverse=flags == "inverse")
+    torch.cuda.synchronize()
+    ref = f64(x)
+    if gamma is not None:
+        ref = ocsa.rms_norm(ref, f64(gamma), 1e-6)
+    if use_pos:
+        p = f64(pos)[:, None] * (-1.0 if flags == "inverse" else 1.0)
+        ref = ocsa.rope(ref, p, rope_dim)
+    got = f64(out.cpu())
+    # fp32 arithmetic then one rounding to T: half a storage spacing plus the fp32 error of
+    # the mean square (at most dim * 2^-24 relative, halved by the square root) on the largest
+    # magnitude in the vector
+    vmax = np.abs(ref).max(axis=-1, keepdims=True)
+    spacing = bf16_ulp(np.maximum(np.abs(got), np.abs(ref))) if dtype == "bf16" else 0.0
+    tol = 0.5 * spacing + (dim * 2.0 ** -24 + 1e-6) * vmax
+    assert np.all(np.abs(got - ref) <= tol), float(np.max(np.abs(got - ref) - tol))
+
+
+def test_norm_rope_in_place_round_trip():
+    # rotate in place, then rotate back at -pos: the rotated part returns to the input within
+    # two roundings; the rest is untouched bit for bit
+    x = T(62, (8, 64, 512), "f32", 1.0)
+    pos = torch.from_numpy(np.arange(8, dtype=np.int64) * 131071)
+    y = dev(x).clone()
+    csa.norm_rope(y, pos=dev(pos), out=y)
+    csa.norm_rope(y, pos=dev(pos), inverse=True, out=y)
+    torch.cuda.synchronize()
+    got = y.cpu()
+    assert torch.equal(got[..., :448], x[..., :448])
+    assert torch.allclose(got[..., 448:], x[..., 448:], rtol=0, atol=2e-6)
 
 
 # ------------------------------------------------------------------------------ index + top-k
