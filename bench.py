@@ -354,6 +354,9 @@ def main():
     ap.add_argument("--score-format", default="f32", choices=("f32", "bf16"),
                     help="index scores the selection ranks: fp32, or rounded to bf16 (the "
                          "line then also reports the recall of the fp32 selection)")
+    ap.add_argument("--out-rope-dim", type=int, default=0,
+                    help="decode workloads: inverse RoPE on the last N channels of every output "
+                         "head, fused into the attention's output store (0: off)")
     ap.add_argument("--compressor", default="single", choices=("single", "c4a"),
                     help="chunked prefill (--config 3): the single-stream compressor, or the "
                          "overlapped two-stream one for both caches")
@@ -408,7 +411,7 @@ def main():
         states.append(dict(q=qs, win=rings, win_new=win_new, sink=sinks, **shared, **st, **hier))
         steps_objs.append(csa.DecodeStep(
             m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
-            score_format=args.score_format, **states[-1]))
+            score_format=args.score_format, out_rope_dim=args.out_rope_dim, **states[-1]))
     torch.cuda.synchronize()
     log(f"device state ready: {args.copies} copies, "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
@@ -537,6 +540,9 @@ def main():
         res["metric"] = f"CSA decode queries/sec ({datagen.WORKLOAD_NAMES[args.config]})"
     if mx:
         res["metric"] += ", MXFP4 indexer keys"
+    if args.out_rope_dim:
+        res["metric"] += f", inverse RoPE on the last {args.out_rope_dim} output channels"
+        res["config"]["out_rope_dim"] = args.out_rope_dim
     if args.score_format == "bf16":
         # recall of the fp32 selection: the same step (idempotent: it rewrites the same tail
         # slot and entry) ranked on fp32 scores, over state copy 0

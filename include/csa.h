@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 6
+#define CSA_ABI_VERSION 7
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -329,6 +329,15 @@ typedef struct csa_decode_desc {
    *   [CoD "FP4, down to the index scores": the indexer's output scores are quantised from
    *   FP32 to BF16 ahead of the top-k selector.] */
   int32_t score_format;
+  /* Inverse RoPE on every attention call's output: when out_rope_dim > 0, the last
+   * out_rope_dim channels of each head's output rotate in pairs (2j, 2j+1) by the angle
+   * -t * rope_base^(-2j/out_rope_dim) before the store (as csa_norm_rope with
+   * CSA_NR_ROPE | CSA_NR_INVERSE at pos = t), fused into the attention's output store.
+   * out_rope_dim even, <= dim, and a multiple of 16 for bf16 64 x 512 heads; rope_base > 1.
+   *   [CoD "Key and value are the same vector": RoPE with position -i on the last 64
+   *   dimensions of each head's output restores relative positions.] */
+  int32_t out_rope_dim;
+  float rope_base;
 } csa_decode_desc;
 
 size_t csa_decode_step_workspace_size(const csa_decode_desc *d);

@@ -138,7 +138,9 @@ def decode_step(case: dict, seqs=None) -> dict:
     the shared selection plus its own window and sink. With case["idx_format"] == "mxfp4",
     case["k_idx"] holds the MXFP4 values of the cached keys and the new entry's key is
     quantised before it is scored (``cached_index_key``). With case["score_format"] == "bf16"
-    the flat selection ranks the scores rounded fp64 -> fp32 -> bf16.
+    the flat selection ranks the scores rounded fp64 -> fp32 -> bf16. With
+    case["out_rope_dim"] > 0 every output head's last channels are turned back by RoPE at -t
+    ([CoD] "Key and value are the same vector") before the store.
     Returns a dict with per-sequence results (new entries, scores, pool, ids, outputs).
     """
     spec = case["spec"]
@@ -198,6 +200,9 @@ def decode_step(case: dict, seqs=None) -> dict:
                 ring[t % wc] = f64(case["x_new"][b])
             o = attend_row(case["q"][c][b], kv_rows, np.arange(sel.size), ring, wc, W, t,
                            case["sink"][c], case["scale"])
+            if case.get("out_rope_dim"):
+                # RoPE at -t on the last out_rope_dim channels of each head's output
+                o = csa.rope(o, -float(t), int(case["out_rope_dim"]))
             outs.append(csa.store(o, dt))
         res["out"][b] = outs
     return res

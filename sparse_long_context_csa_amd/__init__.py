@@ -204,10 +204,12 @@ class DecodeStep:
     out_idx are allocated here unless given. With k_idx_scale (uint8 [n_seq, e_cap,
     idx_dim / 32]) the indexer cache is MXFP4: k_idx holds the codes, uint8 [n_seq, e_cap,
     idx_dim / 2], as quantize_mxfp4 writes them. score_format "bf16" ranks the index scores
-    rounded to bf16."""
+    rounded to bf16. out_rope_dim > 0 applies the inverse RoPE (at -pos) to the last
+    out_rope_dim channels of every output head, in the attention's output store."""
 
     def __init__(self, *, m: int, top_k: int, window: int, scale: float, block_size: int = 0,
-                 max_blocks: int = 0, out=None, out_idx=None, score_format: str = "f32", **t):
+                 max_blocks: int = 0, out=None, out_idx=None, score_format: str = "f32",
+                 out_rope_dim: int = 0, rope_base: float = 10000.0, **t):
         self.t = t
         kv = _dev(t["kv"], "kv")
         dt = kv.dtype
@@ -261,6 +263,8 @@ class DecodeStep:
         if score_format not in ("f32", "bf16"):
             raise ValueError("score_format must be 'f32' or 'bf16'")
         d.score_format = _lib.SCORE_BF16 if score_format == "bf16" else _lib.SCORE_F32
+        d.out_rope_dim = int(out_rope_dim)
+        d.rope_base = float(rope_base)
         d.out_idx = out_idx.data_ptr()
         self.desc = d
         nb = lib().csa_decode_step_workspace_size(C.byref(d))

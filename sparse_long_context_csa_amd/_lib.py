@@ -33,6 +33,7 @@ class DecodeDesc(C.Structure):
         ("win_new", vp * MAX_ATTN), ("sink", vp * MAX_ATTN), ("out", vp * MAX_ATTN),
         ("out_idx", vp), ("events", vp * DECODE_EVENTS), ("scan_events", vp * 2),
         ("idx_format", i32), ("k_idx_scale", vp), ("score_format", i32),
+        ("out_rope_dim", i32), ("rope_base", f32),
     ]
 
 

@@ -1,6 +1,7 @@
 // C ABI of libcsa: argument validation (host, before any launch), workspace layout and the
 // order of launches for each entry point. See include/csa.h for the contract.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -410,6 +411,13 @@ int check_decode_shapes(const csa_decode_desc* d) {
       (d->block_size != 0 || !scan_fuses_ingest(d->dtype, d->idx_heads, d->idx_dim, d->m) ||
        !scan_reads_mxfp4(d->dtype, d->idx_heads, d->idx_dim, 1, false)))
     return CSA_ERR_UNSUPPORTED;
+  if (d->out_rope_dim < 0 || d->out_rope_dim > d->dim || d->out_rope_dim % 2 != 0)
+    return CSA_ERR_SHAPE;
+  if (d->out_rope_dim > 0) {
+    if (!(d->rope_base > 1.f)) return CSA_ERR_SHAPE;
+    if (d->dtype == CSA_BF16 && d->n_heads == 64 && d->dim == 512 && d->out_rope_dim % 16 != 0)
+      return CSA_ERR_UNSUPPORTED;
+  }
   if (d->score_format != CSA_SCORE_F32 && d->score_format != CSA_SCORE_BF16) return CSA_ERR_SHAPE;
   if (d->score_format == CSA_SCORE_BF16 &&
       (d->block_size != 0 || !scan_reads_mxfp4(d->dtype, d->idx_heads, d->idx_dim, 1, false)))
@@ -524,6 +532,8 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
     a.win = d->win[c2]; a.w_cap = d->w_cap; a.window = d->window; a.q_pos = d->pos;
     a.sink = d->sink[c2]; a.scale = d->scale; a.out = d->out[c2]; a.n_seq = d->n_seq;
     a.n_q = 1; a.e_cap = d->e_cap; a.H = d->n_heads; a.D = d->dim; a.ws = w.attn;
+    a.out_rope_dim = d->out_rope_dim;
+    a.rope_log2_base = d->out_rope_dim > 0 ? log2(double(d->rope_base)) : 0.0;
     if (launch_attn(a, s) != hipSuccess) return CSA_ERR_HIP;
   }
   mark(4);

@@ -149,6 +149,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(x[i], wgt[sp][4 * g + i], acc[i]);
   }
   uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (r * kAH + 16 * w + 4 * g) * kAD + nt * 16 + col;
+  if (a.out_rope_dim > 0 && nt * 16 >= kAD - a.out_rope_dim) {   // uniform over the wave
+    const int d = nt * 16 + col;
+    float c, sn;
+    rope_cos_sin(-double(a.q_pos[r]), (d - (kAD - a.out_rope_dim)) >> 1, a.out_rope_dim,
+                 a.rope_log2_base, c, sn);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = rope_pair_lane(acc[i], (col & 1) != 0, c, sn);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) op[i * kAD] = f32_to_bf16(acc[i]);
 }
@@ -199,6 +207,18 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a) {
     float o[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) o[c] = acc[c] * f;
+    if (a.out_rope_dim > 0) {
+      const int r0 = D - a.out_rope_dim;
+#pragma unroll
+      for (int c = 0; c < 8; c += 2)
+        if (c0 + c >= r0) {
+          float cs, sn;
+          rope_cos_sin(-double(t), (c0 + c - r0) >> 1, a.out_rope_dim, a.rope_log2_base, cs, sn);
+          const float x0 = o[c], x1 = o[c + 1];
+          o[c] = x0 * cs - x1 * sn;
+          o[c + 1] = x0 * sn + x1 * cs;
+        }
+    }
     Elt<T>::store8(reinterpret_cast<T*>(a.out) + (r * a.H + h) * D + c0, o);
   }
 }

@@ -198,11 +198,20 @@ __device__ __forceinline__ void attn_split_mfma(const AttnArgs& a, AttnLds& L, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) fi[i] = __shfl(f, 4 * g + i);
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (r * kAH + 16 * wave) * kAD;
+    const int rope0 = a.out_rope_dim > 0 ? kAD - a.out_rope_dim : kAD;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt)
+    for (int nt = 0; nt < 32; ++nt) {
+      float cs = 1.f, sn = 0.f;
+      if (nt * 16 >= rope0)
+        rope_cos_sin(-double(a.q_pos[r]), (nt * 16 + col - rope0) >> 1, a.out_rope_dim,
+                     a.rope_log2_base, cs, sn);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        op[(4 * g + i) * kAD + nt * 16 + col] = f32_to_bf16(O[nt][i] * fi[i]);
+      for (int i = 0; i < 4; ++i) {
+        float y = O[nt][i] * fi[i];
+        if (nt * 16 >= rope0) y = rope_pair_lane(y, (col & 1) != 0, cs, sn);
+        op[(4 * g + i) * kAD + nt * 16 + col] = f32_to_bf16(y);
+      }
+    }
   } else {
     // partial in the accumulator layout (16-byte stores), then (max, sum) per head
     const int64_t rs = r * nsplit + split;
@@ -405,11 +414,20 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
 #pragma unroll
     for (int i = 0; i < 4; ++i) fi[i] = __shfl(f, 4 * g + i);
     uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (r * kAH + 16 * wave) * kAD;
+    const int rope0 = a.out_rope_dim > 0 ? kAD - a.out_rope_dim : kAD;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt)
+    for (int nt = 0; nt < 32; ++nt) {
+      float cs = 1.f, sn = 0.f;
+      if (nt * 16 >= rope0)
+        rope_cos_sin(-double(a.q_pos[r]), (nt * 16 + col - rope0) >> 1, a.out_rope_dim,
+                     a.rope_log2_base, cs, sn);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        op[(4 * g + i) * kAD + nt * 16 + col] = f32_to_bf16(O[nt][i] * fi[i]);
+      for (int i = 0; i < 4; ++i) {
+        float y = O[nt][i] * fi[i];
+        if (nt * 16 >= rope0) y = rope_pair_lane(y, (col & 1) != 0, cs, sn);
+        op[(4 * g + i) * kAD + nt * 16 + col] = f32_to_bf16(y);
+      }
+    }
   } else {
     const int64_t rs = r * nsplit + split;
     f32x4_t* pp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.ws) + rs * kPartO) +

@@ -29,6 +29,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // f rounded to the nearest bf16 value (ties to even), as a float
 __device__ __forceinline__ float round_to_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
+// cos and sin of the RoPE angle p * base^(-2j/rope_dim) (p may be negative): formed and reduced
+// to [-pi, pi] in double precision, since positions reach millions of radians
+__device__ __forceinline__ void rope_cos_sin(double p, int j, int rope_dim, double log2_base,
+                                             float& c, float& s) {
+  constexpr double kTwoPi = 6.283185307179586476925286766559;
+  const double ang = p * exp2(-2.0 * double(j) / double(rope_dim) * log2_base);
+  sincosf(float(ang - kTwoPi * rint(ang / kTwoPi)), &s, &c);
+}
+
+// x0, x1: channels 2j and 2j+1 held by adjacent lanes (this lane holds x, its DPP neighbour in
+// [1,0,3,2] order the other one); returns this lane's rotated value
+__device__ __forceinline__ float rope_pair_lane(float x, bool odd, float c, float s) {
+  const float other = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xb1, 0xf, 0xf, false));
+  return odd ? other * s + x * c : x * c - other * s;
+}
+
 // Storage-type traits: load/store 8 consecutive elements as fp32.
 template <typename T> struct Elt;
 template <> struct Elt<float> {

@@ -178,6 +178,10 @@ struct AttnArgs {
   int64_t n_seq, n_q, e_cap;
   int H, D;
   void* ws;
+  // inverse RoPE on the output: the last out_rope_dim channels of each head rotate in pairs
+  // (2j, 2j+1) by -q_pos * base^(-2j/out_rope_dim) before the store (0: off)
+  int out_rope_dim;
+  double rope_log2_base;
 };
 size_t attn_ws_bytes(int64_t rows, int H, int D, int top_k, int window, int dt);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);

@@ -84,10 +84,10 @@ def test_decode_desc_mirrors_the_header_struct():
     assert int(m.group(1)) == _lib.DECODE_EVENTS
     # natural C layout on x86-64: 12 int32 and 2 int64 (64 B), the float padded to 8 B, then
     # 17 tensor pointers, 5 arrays of CSA_MAX_ATTN pointers, out_idx, the phase events, the
-    # scan kernel's start and stop events; idx_format padded to 8 B, k_idx_scale, score_format
-    # padded to 8 B
+    # scan kernel's start and stop events; idx_format padded to 8 B, k_idx_scale, then
+    # score_format, out_rope_dim and rope_base (12 B, padded to 16)
     n_ptr = 17 + 5 * _lib.MAX_ATTN + 1 + _lib.DECODE_EVENTS + 2
-    assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr + 8 + 8 + 8
+    assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr + 8 + 8 + 16
     for name, val in (("CSA_IDX_DTYPE", _lib.IDX_DTYPE), ("CSA_IDX_MXFP4", _lib.IDX_MXFP4),
                       ("CSA_SCORE_F32", _lib.SCORE_F32), ("CSA_SCORE_BF16", _lib.SCORE_BF16)):
         assert int(re.search(rf"#define\s+{name}\s+(\d+)", _header()).group(1)) == val
@@ -249,6 +249,11 @@ def test_decode_mxfp4_validation(lib):
     assert step(d) == -4
     assert step(full(idx_format=_lib.IDX_DTYPE, score_format=_lib.SCORE_BF16, idx_dim=64)) == -4
     assert step(full(idx_format=_lib.IDX_DTYPE, score_format=3)) == -2
+    # inverse RoPE on the output: even, within dim, a multiple of 16 on the 64 x 512 path
+    assert step(full(idx_format=_lib.IDX_DTYPE, out_rope_dim=63, rope_base=1e4)) == -2
+    assert step(full(idx_format=_lib.IDX_DTYPE, out_rope_dim=600, rope_base=1e4)) == -2
+    assert step(full(idx_format=_lib.IDX_DTYPE, out_rope_dim=64, rope_base=1.0)) == -2
+    assert step(full(idx_format=_lib.IDX_DTYPE, out_rope_dim=40, rope_base=1e4)) == -4
 
 
 def test_binding_raises_on_errors(lib):

@@ -216,6 +216,25 @@ def test_decode_step_bf16_scores(spec, keys):
     check_step(case, ref, st, rings, out, idx)
 
 
+@pytest.mark.parametrize("spec", [
+    datagen.CaseSpec(7140, "decode", B=5, L=24000, m=4, w_cap=256, ragged=True),      # splits
+    datagen.CaseSpec(7141, "decode", B=3, L=40000, m=1, w_cap=128, block_size=8,
+                     max_blocks=512, n_attn=3, ragged=True),
+    # 260 rows: one workgroup per row, the output leaves from the attention kernel itself
+    datagen.CaseSpec(7142, "decode", B=260, L=3000, m=4, w_cap=128, ragged=True),
+    datagen.CaseSpec(7143, "decode", dtype="f32", B=2, L=5000, m=4, w_cap=128, ragged=True),
+], ids=["flat", "hier_three_calls", "rows_260", "f32_generic"])
+def test_decode_step_output_rope(spec):
+    """The inverse RoPE (at -t, last 64 channels of each head) fused into the attention's
+    output store: outputs against the oracle's rotated outputs."""
+    case = datagen.make_case(spec)
+    case["out_rope_dim"] = 64
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    _, st, rings, out, idx = run_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
 def test_decode_step_scan_events():
     """The scan kernel's dispatch takes the step's scan events: the result is unchanged and
     their interval lies inside the step's own (marker events 0 and 4)."""
