@@ -354,9 +354,10 @@ def main():
     ap.add_argument("--score-format", default="f32", choices=("f32", "bf16"),
                     help="index scores the selection ranks: fp32, or rounded to bf16 (the "
                          "line then also reports the recall of the fp32 selection)")
-    ap.add_argument("--out-rope-dim", type=int, default=0,
-                    help="decode workloads: inverse RoPE on the last N channels of every output "
-                         "head, fused into the attention's output store (0: off)")
+    ap.add_argument("--rope-dim", type=int, default=0,
+                    help="decode workloads: each query's per-head RMSNorm and RoPE on its last N "
+                         "channels fused into the attention's query load, and the inverse RoPE "
+                         "on the output fused into its store (0: off)")
     ap.add_argument("--compressor", default="single", choices=("single", "c4a"),
                     help="chunked prefill (--config 3): the single-stream compressor, or the "
                          "overlapped two-stream one for both caches")
@@ -399,6 +400,10 @@ def main():
     if mx:
         codes, scales = csa.quantize_mxfp4(case["k_idx"].to(dev))
         torch.cuda.synchronize()
+    q_gammas = None
+    if args.rope_dim:
+        q_gammas = [(datagen.tensor(spec.case_id, 90 + c, (spec.D,), spec.dtype, 0.3) + 1.0).to(dev)
+                    for c in range(spec.n_attn)]
     steps_objs, states = [], []
     for c in range(args.copies):
         st = {k: case[k].to(dev) for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
@@ -411,7 +416,8 @@ def main():
         states.append(dict(q=qs, win=rings, win_new=win_new, sink=sinks, **shared, **st, **hier))
         steps_objs.append(csa.DecodeStep(
             m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
-            score_format=args.score_format, out_rope_dim=args.out_rope_dim, **states[-1]))
+            score_format=args.score_format, out_rope_dim=args.rope_dim, q_rope_dim=args.rope_dim,
+            q_gamma=q_gammas, **states[-1]))
     torch.cuda.synchronize()
     log(f"device state ready: {args.copies} copies, "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
@@ -540,9 +546,10 @@ def main():
         res["metric"] = f"CSA decode queries/sec ({datagen.WORKLOAD_NAMES[args.config]})"
     if mx:
         res["metric"] += ", MXFP4 indexer keys"
-    if args.out_rope_dim:
-        res["metric"] += f", inverse RoPE on the last {args.out_rope_dim} output channels"
-        res["config"]["out_rope_dim"] = args.out_rope_dim
+    if args.rope_dim:
+        res["metric"] += (f", query RMSNorm + RoPE and output inverse RoPE on the last "
+                          f"{args.rope_dim} channels")
+        res["config"]["rope_dim"] = args.rope_dim
     if args.score_format == "bf16":
         # recall of the fp32 selection: the same step (idempotent: it rewrites the same tail
         # slot and entry) ranked on fp32 scores, over state copy 0

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 7
+#define CSA_ABI_VERSION 8
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -338,6 +338,17 @@ typedef struct csa_decode_desc {
    *   dimensions of each head's output restores relative positions.] */
   int32_t out_rope_dim;
   float rope_base;
+  /* Query preparation: q_gamma[c] (T [dim]) or NULL applies the per-head RMSNorm (eps 1e-6)
+   * to call c's query; q_rope_dim > 0 then turns the last q_rope_dim channels of every head by
+   * RoPE at +t (base rope_base); the prepared query (rounded to T, as csa_norm_rope stores it)
+   * goes to the workspace and the call attends with it; q itself is not written. The
+   * preparation runs in the workgroups of the selection launch that do the rest of the ingest
+   * (off the attention's path), or as one csa_norm_rope pass per call when the ingest is a
+   * kernel of its own. q_rope_dim even and at most 64, dim <= 512 (else CSA_ERR_UNSUPPORTED).
+   *   [CoD "Key and value are the same vector": RMSNorm per head on the queries; RoPE on the
+   *   last 64 dimensions.] */
+  const void *q_gamma[CSA_MAX_ATTN];
+  int32_t q_rope_dim;
 } csa_decode_desc;
 
 size_t csa_decode_step_workspace_size(const csa_decode_desc *d);

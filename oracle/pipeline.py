@@ -140,7 +140,8 @@ def decode_step(case: dict, seqs=None) -> dict:
     quantised before it is scored (``cached_index_key``). With case["score_format"] == "bf16"
     the flat selection ranks the scores rounded fp64 -> fp32 -> bf16. With
     case["out_rope_dim"] > 0 every output head's last channels are turned back by RoPE at -t
-    ([CoD] "Key and value are the same vector") before the store.
+    ([CoD] "Key and value are the same vector") before the store; case["q_gamma"] (per call, or
+    None) and case["q_rope_dim"] prepare each call's query (RMSNorm, RoPE at +t) first.
     Returns a dict with per-sequence results (new entries, scores, pool, ids, outputs).
     """
     spec = case["spec"]
@@ -198,7 +199,18 @@ def decode_step(case: dict, seqs=None) -> dict:
             ring = f64(case["rings"][c][b]).copy()
             if c == 0 and ring_raw:
                 ring[t % wc] = f64(case["x_new"][b])
-            o = attend_row(case["q"][c][b], kv_rows, np.arange(sel.size), ring, wc, W, t,
+            q = case["q"][c][b]
+            qg = (case.get("q_gamma") or [None] * spec.n_attn)[c]
+            qr = int(case.get("q_rope_dim", 0))
+            if qg is not None or qr:
+                # the query's per-head RMSNorm and RoPE at +t, stored at the step's precision
+                q = f64(q)
+                if qg is not None:
+                    q = csa.rms_norm(q, f64(qg), 1e-6)
+                if qr:
+                    q = csa.rope(q, float(t), qr)
+                q = csa.store(q, dt)
+            o = attend_row(q, kv_rows, np.arange(sel.size), ring, wc, W, t,
                            case["sink"][c], case["scale"])
             if case.get("out_rope_dim"):
                 # RoPE at -t on the last out_rope_dim channels of each head's output

@@ -205,11 +205,14 @@ class DecodeStep:
     idx_dim / 32]) the indexer cache is MXFP4: k_idx holds the codes, uint8 [n_seq, e_cap,
     idx_dim / 2], as quantize_mxfp4 writes them. score_format "bf16" ranks the index scores
     rounded to bf16. out_rope_dim > 0 applies the inverse RoPE (at -pos) to the last
-    out_rope_dim channels of every output head, in the attention's output store."""
+    out_rope_dim channels of every output head, in the attention's output store. q_gamma (a
+    list of [dim] tensors or None per call) and q_rope_dim prepare each call's query (RMSNorm,
+    RoPE at +pos) as the attention loads it."""
 
     def __init__(self, *, m: int, top_k: int, window: int, scale: float, block_size: int = 0,
                  max_blocks: int = 0, out=None, out_idx=None, score_format: str = "f32",
-                 out_rope_dim: int = 0, rope_base: float = 10000.0, **t):
+                 out_rope_dim: int = 0, rope_base: float = 10000.0, q_gamma=None,
+                 q_rope_dim: int = 0, **t):
         self.t = t
         kv = _dev(t["kv"], "kv")
         dt = kv.dtype
@@ -265,6 +268,11 @@ class DecodeStep:
         d.score_format = _lib.SCORE_BF16 if score_format == "bf16" else _lib.SCORE_F32
         d.out_rope_dim = int(out_rope_dim)
         d.rope_base = float(rope_base)
+        d.q_rope_dim = int(q_rope_dim)
+        self.q_gamma = list(q_gamma or [])   # the descriptor holds their addresses
+        for c, gq in enumerate(self.q_gamma[:n_attn]):
+            if gq is not None:
+                d.q_gamma[c] = _dev(gq, "q_gamma", dt).data_ptr()
         d.out_idx = out_idx.data_ptr()
         self.desc = d
         nb = lib().csa_decode_step_workspace_size(C.byref(d))

@@ -34,6 +34,7 @@ class DecodeDesc(C.Structure):
         ("out_idx", vp), ("events", vp * DECODE_EVENTS), ("scan_events", vp * 2),
         ("idx_format", i32), ("k_idx_scale", vp), ("score_format", i32),
         ("out_rope_dim", i32), ("rope_base", f32),
+        ("q_gamma", vp * MAX_ATTN), ("q_rope_dim", i32),
     ]
 
 

@@ -373,7 +373,18 @@ struct DecodeWs {
   BlocksWs blocks;    // hierarchical stage 1
   int32_t* pool;
   void* attn;
+  char* qprep;        // prepared queries [n_attn][n_seq, n_heads, dim] (when asked for)
 };
+
+bool wants_qprep(const csa_decode_desc* d) {
+  if (d->q_rope_dim > 0) return true;
+  for (int c = 0; c < d->n_attn && c < CSA_MAX_ATTN; ++c)
+    if (d->q_gamma[c] != nullptr) return true;
+  return false;
+}
+size_t q_bytes(const csa_decode_desc* d) {
+  return size_t(d->n_seq) * d->n_heads * d->dim * (d->dtype == CSA_BF16 ? 2 : 4);
+}
 DecodeWs carve_decode(Carver& c, const csa_decode_desc* d) {
   DecodeWs w{};
   const int64_t rows = d->n_seq;
@@ -386,6 +397,7 @@ DecodeWs carve_decode(Carver& c, const csa_decode_desc* d) {
     w.flat = carve_topk(c, rows, d->e_cap, d->top_k, 1);
   }
   w.attn = c.take<char>(attn_ws_bytes(rows, d->n_heads, d->dim, d->top_k, d->window, CSA_BF16));
+  if (wants_qprep(d)) w.qprep = c.take<char>(q_bytes(d) * size_t(d->n_attn));
   return w;
 }
 
@@ -413,6 +425,11 @@ int check_decode_shapes(const csa_decode_desc* d) {
     return CSA_ERR_UNSUPPORTED;
   if (d->out_rope_dim < 0 || d->out_rope_dim > d->dim || d->out_rope_dim % 2 != 0)
     return CSA_ERR_SHAPE;
+  if (d->q_rope_dim < 0 || d->q_rope_dim > d->dim || d->q_rope_dim % 2 != 0)
+    return CSA_ERR_SHAPE;
+  if (d->q_rope_dim > 0 && !(d->rope_base > 1.f)) return CSA_ERR_SHAPE;
+  if (d->q_rope_dim > 64) return CSA_ERR_UNSUPPORTED;   // 32 pair angles per row at most
+  if (wants_qprep(d) && d->dim > 512) return CSA_ERR_UNSUPPORTED;
   if (d->out_rope_dim > 0) {
     if (!(d->rope_base > 1.f)) return CSA_ERR_SHAPE;
     if (d->dtype == CSA_BF16 && d->n_heads == 64 && d->dim == 512 && d->out_rope_dim % 16 != 0)
@@ -488,8 +505,30 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   // completed entry's indexer key, which that scan scores) and extra workgroups of the last
   // select launch (tails, rings, main entry: read only by the attention). Otherwise it runs
   // first as a kernel of its own. Event 1 then marks the end of that kernel (or event 0).
+  // the attention calls' queries, prepared by the ingest workgroups of the select launch (or
+  // by one csa_norm_rope pass each when the ingest runs as a kernel of its own)
+  if (w.qprep) {
+    in.n_qprep = d->n_attn; in.q_heads = d->n_heads; in.q_dim = d->dim;
+    in.q_rope_dim = d->q_rope_dim;
+    in.rope_log2_base = d->q_rope_dim > 0 ? log2(double(d->rope_base)) : 0.0;
+    for (int c2 = 0; c2 < d->n_attn; ++c2) {
+      in.qsrc[c2] = d->q[c2];
+      in.qgamma[c2] = d->q_gamma[c2];
+      in.qdst[c2] = w.qprep + size_t(c2) * q_bytes(d);
+    }
+  }
   const bool fuse = scan_fuses_ingest(d->dtype, d->idx_heads, d->idx_dim, d->m);
   if (!fuse && launch_ingest(in, s) != hipSuccess) return CSA_ERR_HIP;
+  if (!fuse && w.qprep) {
+    for (int c2 = 0; c2 < d->n_attn; ++c2) {
+      const int flags = (d->q_gamma[c2] ? CSA_NR_NORM : 0) | (d->q_rope_dim > 0 ? CSA_NR_ROPE : 0);
+      if (flags != 0 &&
+          launch_norm_rope(d->dtype, d->q[c2], d->q_gamma[c2], d->pos, in.qdst[c2], d->n_seq,
+                           d->n_heads, d->dim, d->q_rope_dim, d->rope_base, 1e-6f, flags, s) !=
+              hipSuccess)
+        return CSA_ERR_HIP;
+    }
+  }
   const IngestArgs* split_ingest = fuse ? &in : nullptr;
   mark(1);
 
@@ -533,6 +572,8 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
     a.sink = d->sink[c2]; a.scale = d->scale; a.out = d->out[c2]; a.n_seq = d->n_seq;
     a.n_q = 1; a.e_cap = d->e_cap; a.H = d->n_heads; a.D = d->dim; a.ws = w.attn;
     a.out_rope_dim = d->out_rope_dim;
+    if (w.qprep && (d->q_gamma[c2] != nullptr || d->q_rope_dim > 0))
+      a.q = w.qprep + size_t(c2) * q_bytes(d);   // this call's prepared query
     a.rope_log2_base = d->out_rope_dim > 0 ? log2(double(d->rope_base)) : 0.0;
     if (launch_attn(a, s) != hipSuccess) return CSA_ERR_HIP;
   }

@@ -32,6 +32,7 @@ constexpr float kLazyMax = 8.f;  // log2 headroom of the running softmax maximum
 // [wave][nt][lane] float4 (64 heads x 512 dims), then (max, sum) per head in base 2.
 constexpr int64_t kPartO = int64_t(kAH) * kAD;   // floats per (row, split)
 
+
 struct AttnLds {
   __attribute__((aligned(16))) unsigned char kvs[kTile * kKvRow];
   __attribute__((aligned(16))) unsigned char vts[kAD * kVtRow];

@@ -60,6 +60,7 @@ template <> struct Elt<float> {
   }
   __device__ __forceinline__ static float load1(const float* p) { return *p; }
   __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
+  __device__ __forceinline__ static float round(float v) { return v; }
 };
 template <> struct Elt<uint16_t> {   // bfloat16 storage
   static constexpr int kBytes = 2;
@@ -78,6 +79,7 @@ template <> struct Elt<uint16_t> {   // bfloat16 storage
   }
   __device__ __forceinline__ static float load1(const uint16_t* p) { return bf16_to_f32(*p); }
   __device__ __forceinline__ static void store1(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+  __device__ __forceinline__ static float round(float v) { return round_to_bf16(v); }
 };
 
 // ---- causal visibility of compressed entries --------------------------------------------

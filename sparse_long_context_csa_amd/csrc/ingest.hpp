@@ -148,6 +148,73 @@ __device__ __forceinline__ void ingest_vector(const IngestArgs& a, int64_t sq, i
   Elt<T>::store8((T*)a.win[c] + (sq * a.w_cap + t % a.w_cap) * a.dim + c0, w8);
 }
 
+// Query preparation of sequence sq for every attention call (IngestArgs::n_qprep), share `part`
+// of `parts` workgroups: one wave per (call, head) vector (lane l: channels 8 l .. 8 l + 7,
+// q_dim <= 512), kB vectors loaded together: the per-head
+// RMSNorm (eps 1e-6) when the call has a gamma, then RoPE at +pos on the last q_rope_dim
+// channels, stored once in the storage dtype. The row's pair angles (q_rope_dim <= 64) are
+// formed once per wave, lane l taking pair l & 31, and fetched by shuffles.
+template <typename T>
+__device__ __forceinline__ void prep_queries(const IngestArgs& a, int64_t sq, int part,
+                                             int parts) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int64_t t = a.pos[sq];
+  float cs_l = 1.f, sn_l = 0.f;
+  if (a.q_rope_dim > 0 && (lane & 31) < a.q_rope_dim / 2)
+    rope_cos_sin(double(t), lane & 31, a.q_rope_dim, a.rope_log2_base, cs_l, sn_l);
+  const int c0 = lane * 8, r0 = a.q_dim - a.q_rope_dim;
+  const bool live = c0 < a.q_dim;
+  constexpr int kB = 2;
+  const int n_jobs = a.n_qprep * a.q_heads;
+  for (int j0 = (part * nw + wave) * kB; j0 < n_jobs; j0 += parts * nw * kB) {
+    float v[kB][8];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[i][k] = 0.f;
+      const int job = j0 + i;
+      if (job < n_jobs && live) {
+        const int c = job / a.q_heads, h = job % a.q_heads;
+        Elt<T>::load8(static_cast<const T*>(a.qsrc[c]) + (sq * a.q_heads + h) * a.q_dim + c0,
+                      v[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const int job = j0 + i;
+      if (job >= n_jobs) break;   // uniform
+      const int c = job / a.q_heads, h = job % a.q_heads;
+      if (a.qgamma[c] == nullptr && a.q_rope_dim == 0) continue;   // call c uses its own query
+      if (a.qgamma[c] != nullptr) {   // uniform
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ss = fmaf(v[i][k], v[i][k], ss);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+        const float scale = 1.f / sqrtf(ss / float(a.q_dim) + 1e-6f);
+        float g[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (live) Elt<T>::load8(static_cast<const T*>(a.qgamma[c]) + c0, g);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[i][k] = v[i][k] * scale * g[k];
+      }
+      if (a.q_rope_dim > 0) {
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+          const int j = (c0 + k - r0) >> 1;
+          const float cs = __shfl(cs_l, j & 31), sn = __shfl(sn_l, j & 31);
+          if (live && c0 + k >= r0) {
+            const float x0 = v[i][k], x1 = v[i][k + 1];
+            v[i][k] = x0 * cs - x1 * sn;
+            v[i][k + 1] = x0 * sn + x1 * cs;
+          }
+        }
+      }
+      if (live)
+        Elt<T>::store8(static_cast<T*>(a.qdst[c]) + (sq * a.q_heads + h) * a.q_dim + c0, v[i]);
+    }
+  }
+}
+
 // The pooled indexer key vector v (8 channels) of the entry that position t completes,
 // computed from the tails and the new row (the tail slot of t is not read).
 template <typename T, bool kRegs = true>

@@ -34,6 +34,14 @@ struct IngestArgs {
   void* k_scale;          // non-null: k_idx holds MXFP4 codes, k_scale their scale bytes
   void* win[4];
   const void* win_new[4];
+  // query preparation for the attention calls, done by the workgroups that run this ingest:
+  // call c's query qsrc[c] [n_seq, q_heads, q_dim] gets the per-head RMSNorm (qgamma[c], or
+  // none when null) and RoPE at +pos on its last q_rope_dim channels, into qdst[c]
+  int n_qprep, q_heads, q_dim, q_rope_dim;
+  double rope_log2_base;
+  const void* qsrc[4];
+  const void* qgamma[4];
+  void* qdst[4];
 };
 hipError_t launch_ingest(const IngestArgs& a, hipStream_t s);
 

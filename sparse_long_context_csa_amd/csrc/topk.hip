@@ -33,6 +33,7 @@
 // positions: one workgroup per slice computes the bound and keeps its slice's candidates in a
 // segment of its own (select_slice_kernel), then one workgroup per row concatenates the
 // segments in position order and selects (select_final_kernel).
+#include <algorithm>
 #include <limits.h>
 #include <stdlib.h>
 
@@ -84,17 +85,29 @@ struct SelArgs {
   int64_t nseg;
   int64_t rows;
   int64_t n_side;         // ingest workgroups after the rows' (0: none)
+  int side_parts;         // ... side_parts per sequence: the first runs the ingest, all of
+                          // them share the query preparation
   IngestArgs side;
   SegArgs cseg;           // candidate segments of the decode scan (cseg.seg null: none)
   int key_floor;          // 16 when every score is a bf16 value: keys differing below bit 16
                           // of their offset from the list minimum are equal
 };
 
-// A decode step's ingest (without the indexer keys) for sequence sq, by one workgroup.
-__device__ __forceinline__ void side_ingest(const SelArgs& a, int64_t sq) {
-  for (int v = threadIdx.x; v < ingest_vectors(a.side); v += blockDim.x) {
-    if (a.side.dt == kBF16) ingest_vector<uint16_t>(a.side, sq, v, false);
-    else ingest_vector<float>(a.side, sq, v, false);
+// Side workgroup i of a decode step: sequence i % n_seq, part i / n_seq. Part 0 runs the
+// sequence's ingest (without the indexer keys); every part takes its share of the preparation
+// of the attention calls' queries when the step asks for it.
+__device__ __forceinline__ void side_ingest(const SelArgs& a, int64_t i) {
+  const int64_t sq = i % a.side.n_seq;
+  const int part = int(i / a.side.n_seq);
+  if (part == 0) {
+    for (int v = threadIdx.x; v < ingest_vectors(a.side); v += blockDim.x) {
+      if (a.side.dt == kBF16) ingest_vector<uint16_t>(a.side, sq, v, false);
+      else ingest_vector<float>(a.side, sq, v, false);
+    }
+  }
+  if (a.side.n_qprep > 0) {   // the attention calls' queries, off the attention's path
+    if (a.side.dt == kBF16) prep_queries<uint16_t>(a.side, sq, part, a.side_parts);
+    else prep_queries<float>(a.side, sq, part, a.side_parts);
   }
 }
 
@@ -1105,7 +1118,15 @@ hipError_t launch_topk(const TopkArgs& t, hipStream_t s) {
   a.seg = reinterpret_cast<uint2*>(base + p.off_seg);
   a.nseg = p.nseg;
   a.rows = t.rows;
-  a.n_side = t.side ? t.side->n_seq : 0;
+  // query preparation: about two vectors per wave, so that no sequence's share waits on one
+  // workgroup's bandwidth
+  a.side_parts = 1;
+  if (t.side && t.side->n_qprep > 0) {
+    const int per_wg = 2 * (kSelThreads / 64);
+    const int jobs = t.side->n_qprep * t.side->q_heads;
+    a.side_parts = std::min(32, std::max(1, (jobs + per_wg - 1) / per_wg));
+  }
+  a.n_side = t.side ? t.side->n_seq * a.side_parts : 0;
   a.side = t.side ? *t.side : IngestArgs{};
   a.cseg = t.seg;
   a.key_floor = t.bf16_scores ? 16 : 0;

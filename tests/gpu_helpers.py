@@ -168,7 +168,10 @@ def run_step(case, idx_state=None):
                           q_idx=g["q_idx"], w=g["w"], q=[dev(x) for x in case["q"]], win=rings,
                           win_new=win_new, sink=[dev(x) for x in case["sink"]],
                           score_format=case.get("score_format", "f32"),
-                          out_rope_dim=int(case.get("out_rope_dim", 0)), **st, **kw)
+                          out_rope_dim=int(case.get("out_rope_dim", 0)),
+                          q_gamma=[dev(x) if x is not None else None
+                                   for x in (case.get("q_gamma") or [])],
+                          q_rope_dim=int(case.get("q_rope_dim", 0)), **st, **kw)
     out, idx = step()
     torch.cuda.synchronize()
     return step, st, rings, [o.cpu() for o in out], idx.cpu()

@@ -85,9 +85,10 @@ def test_decode_desc_mirrors_the_header_struct():
     # natural C layout on x86-64: 12 int32 and 2 int64 (64 B), the float padded to 8 B, then
     # 17 tensor pointers, 5 arrays of CSA_MAX_ATTN pointers, out_idx, the phase events, the
     # scan kernel's start and stop events; idx_format padded to 8 B, k_idx_scale, then
-    # score_format, out_rope_dim and rope_base (12 B, padded to 16)
+    # score_format, out_rope_dim and rope_base (12 B, padded to 16), the CSA_MAX_ATTN query
+    # gammas, q_rope_dim padded to 8 B
     n_ptr = 17 + 5 * _lib.MAX_ATTN + 1 + _lib.DECODE_EVENTS + 2
-    assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr + 8 + 8 + 16
+    assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr + 8 + 8 + 16 + 8 * _lib.MAX_ATTN + 8
     for name, val in (("CSA_IDX_DTYPE", _lib.IDX_DTYPE), ("CSA_IDX_MXFP4", _lib.IDX_MXFP4),
                       ("CSA_SCORE_F32", _lib.SCORE_F32), ("CSA_SCORE_BF16", _lib.SCORE_BF16)):
         assert int(re.search(rf"#define\s+{name}\s+(\d+)", _header()).group(1)) == val
@@ -254,6 +255,8 @@ def test_decode_mxfp4_validation(lib):
     assert step(full(idx_format=_lib.IDX_DTYPE, out_rope_dim=600, rope_base=1e4)) == -2
     assert step(full(idx_format=_lib.IDX_DTYPE, out_rope_dim=64, rope_base=1.0)) == -2
     assert step(full(idx_format=_lib.IDX_DTYPE, out_rope_dim=40, rope_base=1e4)) == -4
+    assert step(full(idx_format=_lib.IDX_DTYPE, q_rope_dim=7, rope_base=1e4)) == -2
+    assert step(full(idx_format=_lib.IDX_DTYPE, q_rope_dim=64, rope_base=0.5)) == -2
 
 
 def test_binding_raises_on_errors(lib):

@@ -225,10 +225,15 @@ def test_decode_step_bf16_scores(spec, keys):
     datagen.CaseSpec(7143, "decode", dtype="f32", B=2, L=5000, m=4, w_cap=128, ragged=True),
 ], ids=["flat", "hier_three_calls", "rows_260", "f32_generic"])
 def test_decode_step_output_rope(spec):
-    """The inverse RoPE (at -t, last 64 channels of each head) fused into the attention's
-    output store: outputs against the oracle's rotated outputs."""
+    """The query's RMSNorm and RoPE (at +t) fused into the attention's query load and the
+    inverse RoPE (at -t, last 64 channels of each head) into its output store: outputs against
+    the oracle's."""
     case = datagen.make_case(spec)
     case["out_rope_dim"] = 64
+    case["q_rope_dim"] = 64
+    case["q_gamma"] = [datagen.tensor(spec.case_id, 90 + c, (spec.D,), spec.dtype, 0.3) + 1.0
+                       for c in range(spec.n_attn)]
+    case["q_gamma"][0] = case["q_gamma"][0].to(case["q"][0].dtype)
     gaps.enforce_decode(case)
     ref = pipeline.decode_step(case)
     _, st, rings, out, idx = run_step(case)
