@@ -225,15 +225,34 @@ def test_decode_step_bf16_scores(spec, keys):
     datagen.CaseSpec(7143, "decode", dtype="f32", B=2, L=5000, m=4, w_cap=128, ragged=True),
 ], ids=["flat", "hier_three_calls", "rows_260", "f32_generic"])
 def test_decode_step_output_rope(spec):
-    """The query's RMSNorm and RoPE (at +t) fused into the attention's query load and the
-    inverse RoPE (at -t, last 64 channels of each head) into its output store: outputs against
-    the oracle's."""
+    """The queries' RMSNorm and RoPE (at +t), prepared by the selection launch's side
+    workgroups, and the inverse RoPE (at -t, last 64 channels of each head) fused into the
+    attention's output store: outputs against the oracle's."""
     case = datagen.make_case(spec)
     case["out_rope_dim"] = 64
     case["q_rope_dim"] = 64
     case["q_gamma"] = [datagen.tensor(spec.case_id, 90 + c, (spec.D,), spec.dtype, 0.3) + 1.0
                        for c in range(spec.n_attn)]
     case["q_gamma"][0] = case["q_gamma"][0].to(case["q"][0].dtype)
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    _, st, rings, out, idx = run_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["side_workgroups", "separate_ingest"])
+def test_decode_step_query_norm_some_calls(fused):
+    """RMSNorm on the queries of calls 0 and 2 only, no query RoPE: call 1 attends with its own
+    query unchanged. bf16 64 x 128 runs the prep in the selection launch; the fp32 case (no
+    fused ingest) runs it as separate passes."""
+    spec = (datagen.CaseSpec(7144, "decode", B=3, L=30000, m=4, w_cap=128, block_size=8,
+                             max_blocks=512, n_attn=3, ragged=True) if fused else
+            datagen.CaseSpec(7145, "decode", dtype="f32", B=2, L=6000, m=4, w_cap=128,
+                             n_attn=3, ragged=True))
+    case = datagen.make_case(spec)
+    g = [datagen.tensor(spec.case_id, 90 + c, (spec.D,), spec.dtype, 0.3) + 1.0
+         for c in range(spec.n_attn)]
+    case["q_gamma"] = [g[0].to(case["q"][0].dtype), None, g[2].to(case["q"][0].dtype)]
     gaps.enforce_decode(case)
     ref = pipeline.decode_step(case)
     _, st, rings, out, idx = run_step(case)
