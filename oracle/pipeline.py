@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import csa, mx
+from . import csa, fp8, mx
 
 
 def f64(a) -> np.ndarray:
@@ -141,7 +141,9 @@ def decode_step(case: dict, seqs=None) -> dict:
     the flat selection ranks the scores rounded fp64 -> fp32 -> bf16. With
     case["out_rope_dim"] > 0 every output head's last channels are turned back by RoPE at -t
     ([CoD] "Key and value are the same vector") before the store; case["q_gamma"] (per call, or
-    None) and case["q_rope_dim"] prepare each call's query (RMSNorm, RoPE at +t) first.
+    None) and case["q_rope_dim"] prepare each call's query (RMSNorm, RoPE at +t) first. With
+    case["kv_format"] == "fp8", case["kv"] holds the values of an FP8 main cache (576-byte
+    entries, oracle/fp8.py) and the new entry is attended at its cached value.
     Returns a dict with per-sequence results (new entries, scores, pool, ids, outputs).
     """
     spec = case["spec"]
@@ -193,7 +195,8 @@ def decode_step(case: dict, seqs=None) -> dict:
         sel = ids[ids >= 0]
         kv_rows = take_rows(case["kv"][b], sel) if sel.size else np.zeros((0, spec.D))
         if new_e is not None:
-            kv_rows[sel == new_e] = res["kv_new"][b]
+            kv_rows[sel == new_e] = (fp8.cached_entries(res["kv_new"][b])
+                                     if case.get("kv_format") == "fp8" else res["kv_new"][b])
         outs = []
         for c in range(spec.n_attn):
             ring = f64(case["rings"][c][b]).copy()

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import datagen
-from oracle import csa, gaps, mx, pipeline
+from oracle import csa, fp8, gaps, mx, pipeline
 from oracle.pipeline import f64
 
 
@@ -249,3 +249,27 @@ def test_decode_step_bf16_scores():
     f32b = pipeline.decode_step({**case, "score_format": "f32"})
     rec = np.mean([np.isin(res["ids"][b], f32b["ids"][b]).mean() for b in range(spec.B)])
     assert rec > 0.9
+
+
+def test_fp8_cache_attends_the_new_entry_at_its_fp8_value():
+    # m = 1: the new entry is the raw row x_new (a softmax over one logit). With an FP8 main
+    # cache the step must attend to it at its E4M3 / bf16 value: the same outputs as the dtype
+    # path given that value as x_new, and not those of the unquantised entry
+    case = small_decode(case_id=906, m=1, L=12, D=512, H=2, ragged=False)   # K >= entries
+    spec = case["spec"]
+    case["kv"] = torch.from_numpy(fp8.cached_entries(f64(case["kv"]))).to(case["kv"].dtype)
+    plain = pipeline.decode_step(case)
+    case8 = dict(case, kv_format="fp8")
+    res = pipeline.decode_step(case8)
+    xq = fp8.cached_entries(f64(case["x_new"]))
+    assert not np.array_equal(xq, f64(case["x_new"]))
+    moved = dict(case, x_new=torch.from_numpy(xq).to(case["x_new"].dtype))
+    want = pipeline.decode_step(moved)
+    differs = False
+    for b in range(spec.B):
+        np.testing.assert_array_equal(res["kv_new"][b], plain["kv_new"][b])
+        np.testing.assert_array_equal(res["ids"][b], plain["ids"][b])
+        for c in range(spec.n_attn):
+            np.testing.assert_array_equal(res["out"][b][c], want["out"][b][c])
+            differs |= not np.array_equal(res["out"][b][c], plain["out"][b][c])
+    assert differs
