@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 8
+#define CSA_ABI_VERSION 9
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -147,6 +147,27 @@ int csa_quantize_mxfp4(const void *x, void *codes, void *scales, int64_t n_rows,
                        int32_t dtype, void *stream);
 
 /* ---------------------------------------------------------------------------------------
+ * csa_quantize_kv_fp8 / csa_dequantize_kv_fp8 -- FP8 storage of main KV entries.
+ *   [CoD "Rebuilding the model from its constants": the 64 rotary dimensions of a shared
+ *   key/value entry stay in bf16 and the other 448 go to FP8: 64 * 2 + 448 = 576 bytes per
+ *   512-dim entry; CoD "The FP4 precision budget": the main attention runs in FP8.]
+ * Entry layout (CSA_KV_FP8_BYTES = 576): bytes 0..447 are the E4M3 codes of channels 0..447,
+ * bytes 448..575 channels 448..511 as little-endian bf16 (nearest-even). E4M3 is the OCP
+ * format (sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is
+ * NaN, so the largest finite magnitude is 448; exponent field 0: subnormals m * 2^-9). Each
+ * value rounds to the nearest E4M3 value, ties to the even code, magnitudes past 448 to 448; a
+ * zero magnitude is code 0x00. There is no scale.
+ *   quantize:   x T [n_rows, 512] (CSA_BF16 or CSA_F32, rounded directly) -> out uint8
+ *               [n_rows, 576] (16-byte aligned)
+ *   dequantize: in uint8 [n_rows, 576] -> out bf16 [n_rows, 512] (exact: every E4M3 value is a
+ *               bf16 value)
+ * Device pointers; asynchronous on `stream`.
+ * ------------------------------------------------------------------------------------- */
+#define CSA_KV_FP8_BYTES 576
+int csa_quantize_kv_fp8(const void *x, void *out, int64_t n_rows, int32_t dtype, void *stream);
+int csa_dequantize_kv_fp8(const void *in, void *out, int64_t n_rows, void *stream);
+
+/* ---------------------------------------------------------------------------------------
  * csa_index_topk -- lightning-indexer scores + Top-K selection.
  *   [CoD "The Lightning Indexer": I(t,s) = sum_h w(t,h) * ReLU(q_I(t,h) . K_s); keep the
  *   top k (512 in V4-Flash). CoD "The sliding window is not an optimisation": entry i is
@@ -237,6 +258,17 @@ int csa_sparse_attn(const void *q, const void *kv, const int32_t *idx, int32_t t
                     int64_t e_cap, int32_t n_heads, int32_t head_dim, void *ws,
                     size_t ws_bytes, int32_t dtype, void *stream);
 
+/* csa_sparse_attn_fp8 -- csa_sparse_attn over an FP8 main cache: kv is uint8
+ * [n_seq, e_cap, 576] in csa_quantize_kv_fp8's layout (16-byte aligned) and each selected
+ * entry takes part at its exact value; q, the window rows, out and the arithmetic are those of
+ * csa_sparse_attn. Needs dtype CSA_BF16, n_heads 64, head_dim 512 (else CSA_ERR_UNSUPPORTED);
+ * the workspace is csa_sparse_attn_workspace_size's. */
+int csa_sparse_attn_fp8(const void *q, const void *kv, const int32_t *idx, int32_t top_k,
+                        const void *win, int32_t w_cap, int32_t window, const int64_t *q_pos,
+                        const float *sink, float scale, void *out, int64_t n_seq, int64_t n_q,
+                        int64_t e_cap, int32_t n_heads, int32_t head_dim, void *ws,
+                        size_t ws_bytes, int32_t dtype, void *stream);
+
 /* ---------------------------------------------------------------------------------------
  * csa_decode_step -- one new token per sequence through the whole hot path.
  *   [CoD "The compressor has two streams...", "The Lightning Indexer", "Attention sink",
@@ -276,6 +308,8 @@ int csa_sparse_attn(const void *q, const void *kv, const int32_t *idx, int32_t t
 #define CSA_IDX_MXFP4 1   /* indexer keys as MXFP4 codes + scale bytes                    */
 #define CSA_SCORE_F32 0   /* csa_decode_desc.score_format: rank fp32 index scores           */
 #define CSA_SCORE_BF16 1  /* rank the scores rounded to bf16                               */
+#define CSA_KV_DTYPE 0    /* csa_decode_desc.kv_format: main entries in the step's dtype      */
+#define CSA_KV_FP8 1      /* main entries as 576-byte FP8 entries (csa_quantize_kv_fp8)       */
 
 typedef struct csa_decode_desc {
   int32_t dtype;
@@ -349,6 +383,14 @@ typedef struct csa_decode_desc {
    *   last 64 dimensions.] */
   const void *q_gamma[CSA_MAX_ATTN];
   int32_t q_rope_dim;
+  /* Storage of the main KV entries: CSA_KV_DTYPE keeps kv in T as above; CSA_KV_FP8 keeps
+   * them in csa_quantize_kv_fp8's form, kv = uint8 [n_seq, e_cap, 576] (16-byte aligned): the
+   * entry a step completes is pooled, rounded to T and stored as an FP8 entry, and the
+   * attention reads every selected entry at its exact value. Needs T = bf16, n_heads 64 and
+   * dim 512; otherwise CSA_ERR_UNSUPPORTED.
+   *   [CoD "Rebuilding the model from its constants": 448 FP8 + 64 bf16 rotary dims =
+   *   576 bytes per entry.] */
+  int32_t kv_format;
 } csa_decode_desc;
 
 size_t csa_decode_step_workspace_size(const csa_decode_desc *d);

@@ -122,6 +122,33 @@ def quantize_mxfp4(x: torch.Tensor, codes: torch.Tensor | None = None,
     return codes, scales
 
 
+def quantize_kv_fp8(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """csa_quantize_kv_fp8: entries x [..., 512] -> FP8 entries uint8 [..., 576]."""
+    _dev(x, "x")
+    if x.shape[-1] != 512:
+        raise ValueError("FP8 entries are 512 channels wide")
+    n_rows = x.numel() // 512
+    if out is None:
+        out = torch.empty(*x.shape[:-1], _lib.KV_FP8_BYTES, dtype=torch.uint8, device=x.device)
+    _dev(out, "out", torch.uint8)
+    check("csa_quantize_kv_fp8", lib().csa_quantize_kv_fp8(_p(x), _p(out), n_rows, _dtype(x),
+                                                           _stream()))
+    return out
+
+
+def dequantize_kv_fp8(e: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """csa_dequantize_kv_fp8: FP8 entries uint8 [..., 576] -> bf16 [..., 512]."""
+    _dev(e, "e", torch.uint8)
+    if e.shape[-1] != _lib.KV_FP8_BYTES:
+        raise ValueError("FP8 entries are 576 bytes")
+    n_rows = e.numel() // _lib.KV_FP8_BYTES
+    if out is None:
+        out = torch.empty(*e.shape[:-1], 512, dtype=torch.bfloat16, device=e.device)
+    _dev(out, "out", torch.bfloat16)
+    check("csa_dequantize_kv_fp8", lib().csa_dequantize_kv_fp8(_p(e), _p(out), n_rows, _stream()))
+    return out
+
+
 def index_topk(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor, q_pos: torch.Tensor,
                m: int, top_k: int, e_count: torch.Tensor | None = None,
                cand: torch.Tensor | None = None, want_scores: bool = False,
@@ -177,8 +204,10 @@ def index_blocks(q_idx, w, k_idx, q_pos, m: int, block_size: int, max_blocks: in
 def sparse_attn(q, kv, idx, win, w_cap: int, window: int, q_pos, sink, scale: float,
                 out=None) -> torch.Tensor:
     """csa_sparse_attn. q [n_seq,n_q,H,D], kv [n_seq,e_cap,D], idx [n_seq,n_q,top_k] i32 or
-    None, win [n_seq,w_cap,D] or None, q_pos [n_seq,n_q] i64, sink [H] f32 or None."""
-    _dev(q, "q"); _dev(kv, "kv", q.dtype); _dev(idx, "idx", torch.int32)
+    None, win [n_seq,w_cap,D] or None, q_pos [n_seq,n_q] i64, sink [H] f32 or None. A uint8 kv
+    [n_seq,e_cap,576] is an FP8 main cache (quantize_kv_fp8's entries): csa_sparse_attn_fp8."""
+    kv8 = kv is not None and kv.dtype == torch.uint8
+    _dev(q, "q"); _dev(kv, "kv", torch.uint8 if kv8 else q.dtype); _dev(idx, "idx", torch.int32)
     _dev(win, "win", q.dtype); _dev(q_pos, "q_pos", torch.int64); _dev(sink, "sink", torch.float32)
     n_seq, n_q, H, D = q.shape
     e_cap = kv.shape[1]
@@ -187,7 +216,8 @@ def sparse_attn(q, kv, idx, win, w_cap: int, window: int, q_pos, sink, scale: fl
         out = torch.empty_like(q)
     nb = lib().csa_sparse_attn_workspace_size(n_seq, n_q, H, D, top_k, window)
     ws = _workspace(nb, q.device) if nb else None
-    check("csa_sparse_attn", lib().csa_sparse_attn(
+    name = "csa_sparse_attn_fp8" if kv8 else "csa_sparse_attn"
+    check(name, getattr(lib(), name)(
         _p(q), _p(kv), _p(idx), top_k, _p(win), w_cap, window, _p(q_pos), _p(sink), float(scale),
         _p(out), n_seq, n_q, e_cap, H, D, _p(ws), 0 if ws is None else ws.numel(), _dtype(q),
         _stream()))
@@ -207,7 +237,8 @@ class DecodeStep:
     rounded to bf16. out_rope_dim > 0 applies the inverse RoPE (at -pos) to the last
     out_rope_dim channels of every output head, in the attention's output store. q_gamma (a
     list of [dim] tensors or None per call) and q_rope_dim prepare each call's query (RMSNorm,
-    RoPE at +pos) as the attention loads it."""
+    RoPE at +pos) in the selection launch. A uint8 kv [n_seq, e_cap, 576] is an FP8 main
+    cache (quantize_kv_fp8's entries; kv_format CSA_KV_FP8)."""
 
     def __init__(self, *, m: int, top_k: int, window: int, scale: float, block_size: int = 0,
                  max_blocks: int = 0, out=None, out_idx=None, score_format: str = "f32",
@@ -215,7 +246,8 @@ class DecodeStep:
                  q_rope_dim: int = 0, **t):
         self.t = t
         kv = _dev(t["kv"], "kv")
-        dt = kv.dtype
+        kv8 = kv.dtype == torch.uint8
+        dt = _dev(t["x_new"], "x_new").dtype if kv8 else kv.dtype
         mx = t.get("k_idx_scale") is not None
         for k in ("x_new", "z_new", "xi_new", "zi_new", "x_tail", "z_tail", "xi_tail",
                   "zi_tail", "bias", "bias_i", "q_idx"):
@@ -230,6 +262,10 @@ class DecodeStep:
         sinks = list(t.get("sink") or [])
         sinks += [None] * (n_attn - len(sinks))
         n_seq, e_cap, dim = kv.shape
+        if kv8:
+            if dim != _lib.KV_FP8_BYTES:
+                raise ValueError("an FP8 kv holds 576-byte entries")
+            dim = 512
         H = qs[0].shape[1]
         idx_heads, idx_dim = t["q_idx"].shape[1], t["q_idx"].shape[2]
         w_cap = wins[0].shape[1]
@@ -239,7 +275,7 @@ class DecodeStep:
             out_idx = torch.empty(n_seq, top_k, dtype=torch.int32, device=kv.device)
         self.out, self.out_idx = out, out_idx
         d = DecodeDesc()
-        d.dtype = _dtype(kv); d.m = m; d.dim = dim; d.n_heads = H; d.idx_heads = idx_heads
+        d.dtype = _dtype(t["x_new"]); d.m = m; d.dim = dim; d.n_heads = H; d.idx_heads = idx_heads
         d.idx_dim = idx_dim; d.top_k = top_k; d.window = window; d.w_cap = w_cap
         d.block_size = block_size; d.max_blocks = max_blocks; d.n_attn = n_attn
         d.n_seq = n_seq; d.e_cap = e_cap; d.scale = float(scale)
@@ -273,6 +309,7 @@ class DecodeStep:
         for c, gq in enumerate(self.q_gamma[:n_attn]):
             if gq is not None:
                 d.q_gamma[c] = _dev(gq, "q_gamma", dt).data_ptr()
+        d.kv_format = _lib.KV_FP8 if kv8 else _lib.KV_DTYPE
         d.out_idx = out_idx.data_ptr()
         self.desc = d
         nb = lib().csa_decode_step_workspace_size(C.byref(d))

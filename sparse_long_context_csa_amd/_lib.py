@@ -14,6 +14,8 @@ MAX_ATTN = 4
 DECODE_EVENTS = 5
 IDX_DTYPE, IDX_MXFP4 = 0, 1
 SCORE_F32, SCORE_BF16 = 0, 1
+KV_DTYPE, KV_FP8 = 0, 1
+KV_FP8_BYTES = 576
 NR_NORM, NR_ROPE, NR_INVERSE = 1, 2, 4
 
 vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
@@ -34,7 +36,7 @@ class DecodeDesc(C.Structure):
         ("out_idx", vp), ("events", vp * DECODE_EVENTS), ("scan_events", vp * 2),
         ("idx_format", i32), ("k_idx_scale", vp), ("score_format", i32),
         ("out_rope_dim", i32), ("rope_base", f32),
-        ("q_gamma", vp * MAX_ATTN), ("q_rope_dim", i32),
+        ("q_gamma", vp * MAX_ATTN), ("q_rope_dim", i32), ("kv_format", i32),
     ]
 
 
@@ -45,6 +47,8 @@ SIGNATURES = {
     "csa_compress_c4a": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]),
     "csa_norm_rope": (i32, [vp, vp, vp, vp, i64, i32, i32, i32, f32, f32, i32, i32, vp]),
     "csa_quantize_mxfp4": (i32, [vp, vp, vp, i64, i32, i32, vp]),
+    "csa_quantize_kv_fp8": (i32, [vp, vp, i64, i32, vp]),
+    "csa_dequantize_kv_fp8": (i32, [vp, vp, i64, vp]),
     "csa_index_topk_workspace_size": (sz, [i64, i64, i64, i32]),
     "csa_index_topk": (i32, [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, i32, i32,
                              vp, vp, vp, vp, sz, i32, vp]),
@@ -54,6 +58,8 @@ SIGNATURES = {
     "csa_sparse_attn_workspace_size": (sz, [i64, i64, i32, i32, i32, i32]),
     "csa_sparse_attn": (i32, [vp, vp, vp, i32, vp, i32, i32, vp, vp, f32, vp, i64, i64, i64,
                               i32, i32, vp, sz, i32, vp]),
+    "csa_sparse_attn_fp8": (i32, [vp, vp, vp, i32, vp, i32, i32, vp, vp, f32, vp, i64, i64,
+                                  i64, i32, i32, vp, sz, i32, vp]),
     "csa_decode_step_workspace_size": (sz, [C.POINTER(DecodeDesc)]),
     "csa_decode_step": (i32, [C.POINTER(DecodeDesc), vp, sz, vp]),
 }

@@ -254,6 +254,24 @@ int csa_quantize_mxfp4(const void* x, void* codes, void* scales, int64_t n_rows,
                                          static_cast<hipStream_t>(stream)));
 }
 
+int csa_quantize_kv_fp8(const void* x, void* out, int64_t n_rows, int32_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return CSA_ERR_DTYPE;
+  if (n_rows < 0) return CSA_ERR_SHAPE;
+  if (n_rows == 0) return CSA_OK;
+  if (!x || !out) return CSA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return CSA_ERR_SHAPE;
+  return status_of(launch_quantize_kv_fp8(dtype, x, out, n_rows, static_cast<hipStream_t>(stream)));
+}
+
+int csa_dequantize_kv_fp8(const void* in, void* out, int64_t n_rows, void* stream) {
+  if (n_rows < 0) return CSA_ERR_SHAPE;
+  if (n_rows == 0) return CSA_OK;
+  if (!in || !out) return CSA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(in) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
+    return CSA_ERR_SHAPE;
+  return status_of(launch_dequantize_kv_fp8(in, out, n_rows, static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------------------------------
 size_t csa_index_topk_workspace_size(int64_t n_seq, int64_t n_q, int64_t n_keys, int32_t top_k) {
   if (n_seq < 0 || n_q < 0 || n_keys < 0 || top_k < 1) return 0;
@@ -346,13 +364,18 @@ static int check_attn(int64_t n_seq, int64_t n_q, int64_t e_cap, int32_t H, int3
   return CSA_OK;
 }
 
-int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, int32_t top_k,
-                    const void* win, int32_t w_cap, int32_t window, const int64_t* q_pos,
-                    const float* sink, float scale, void* out, int64_t n_seq, int64_t n_q,
-                    int64_t e_cap, int32_t n_heads, int32_t head_dim, void* ws, size_t ws_bytes,
-                    int32_t dtype, void* stream) {
+static int sparse_attn_impl(const void* q, const void* kv, const int32_t* idx, int32_t top_k,
+                            const void* win, int32_t w_cap, int32_t window,
+                            const int64_t* q_pos, const float* sink, float scale, void* out,
+                            int64_t n_seq, int64_t n_q, int64_t e_cap, int32_t n_heads,
+                            int32_t head_dim, void* ws, size_t ws_bytes, int32_t dtype,
+                            bool kv_fp8, void* stream) {
   int st = check_attn(n_seq, n_q, e_cap, n_heads, head_dim, top_k, w_cap, window, dtype);
   if (st != CSA_OK) return st;
+  if (kv_fp8) {
+    if (dtype != CSA_BF16 || n_heads != 64 || head_dim != 512) return CSA_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(kv) % 16 != 0) return CSA_ERR_SHAPE;
+  }
   if (n_seq * n_q == 0) return CSA_OK;
   if (!q || !q_pos || !out) return CSA_ERR_NULL;
   if (top_k > 0 && (!idx || !kv)) return CSA_ERR_NULL;
@@ -363,7 +386,26 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, int32_t t
   a.dt = dtype; a.q = q; a.kv = kv; a.idx = idx; a.top_k = top_k; a.win = win; a.w_cap = w_cap;
   a.window = window; a.q_pos = q_pos; a.sink = sink; a.scale = scale; a.out = out;
   a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap; a.H = n_heads; a.D = head_dim; a.ws = ws;
+  a.kv_fp8 = kv_fp8 ? 1 : 0;
   return status_of(launch_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, int32_t top_k,
+                    const void* win, int32_t w_cap, int32_t window, const int64_t* q_pos,
+                    const float* sink, float scale, void* out, int64_t n_seq, int64_t n_q,
+                    int64_t e_cap, int32_t n_heads, int32_t head_dim, void* ws, size_t ws_bytes,
+                    int32_t dtype, void* stream) {
+  return sparse_attn_impl(q, kv, idx, top_k, win, w_cap, window, q_pos, sink, scale, out, n_seq,
+                          n_q, e_cap, n_heads, head_dim, ws, ws_bytes, dtype, false, stream);
+}
+
+int csa_sparse_attn_fp8(const void* q, const void* kv, const int32_t* idx, int32_t top_k,
+                        const void* win, int32_t w_cap, int32_t window, const int64_t* q_pos,
+                        const float* sink, float scale, void* out, int64_t n_seq, int64_t n_q,
+                        int64_t e_cap, int32_t n_heads, int32_t head_dim, void* ws,
+                        size_t ws_bytes, int32_t dtype, void* stream) {
+  return sparse_attn_impl(q, kv, idx, top_k, win, w_cap, window, q_pos, sink, scale, out, n_seq,
+                          n_q, e_cap, n_heads, head_dim, ws, ws_bytes, dtype, true, stream);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -435,6 +477,9 @@ int check_decode_shapes(const csa_decode_desc* d) {
     if (d->dtype == CSA_BF16 && d->n_heads == 64 && d->dim == 512 && d->out_rope_dim % 16 != 0)
       return CSA_ERR_UNSUPPORTED;
   }
+  if (d->kv_format != CSA_KV_DTYPE && d->kv_format != CSA_KV_FP8) return CSA_ERR_SHAPE;
+  if (d->kv_format == CSA_KV_FP8 && (d->dtype != CSA_BF16 || d->n_heads != 64 || d->dim != 512))
+    return CSA_ERR_UNSUPPORTED;
   if (d->score_format != CSA_SCORE_F32 && d->score_format != CSA_SCORE_BF16) return CSA_ERR_SHAPE;
   if (d->score_format == CSA_SCORE_BF16 &&
       (d->block_size != 0 || !scan_reads_mxfp4(d->dtype, d->idx_heads, d->idx_dim, 1, false)))
@@ -457,6 +502,8 @@ int check_decode(const csa_decode_desc* d) {
         reinterpret_cast<uintptr_t>(d->k_idx_scale) % 4 != 0)
       return CSA_ERR_SHAPE;
   }
+  if (d->kv_format == CSA_KV_FP8 && reinterpret_cast<uintptr_t>(d->kv) % 16 != 0)
+    return CSA_ERR_SHAPE;
   for (int c = 0; c < d->n_attn; ++c) {
     if (!d->q[c] || !d->out[c]) return CSA_ERR_NULL;
     if (d->window > 0 && !d->win[c]) return CSA_ERR_NULL;
@@ -497,6 +544,7 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   in.bias = d->bias; in.bias_i = d->bias_i; in.kv = d->kv; in.k_idx = d->k_idx;
   void* key_scales = d->idx_format == CSA_IDX_MXFP4 ? d->k_idx_scale : nullptr;
   in.k_scale = key_scales;
+  in.kv_fp8 = d->kv_format == CSA_KV_FP8 ? 1 : 0;
   for (int c2 = 0; c2 < 4; ++c2) {
     in.win[c2] = c2 < d->n_attn ? d->win[c2] : nullptr;
     in.win_new[c2] = (c2 < d->n_attn && d->w_cap > 0) ? d->win_new[c2] : nullptr;
@@ -572,6 +620,7 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
     a.sink = d->sink[c2]; a.scale = d->scale; a.out = d->out[c2]; a.n_seq = d->n_seq;
     a.n_q = 1; a.e_cap = d->e_cap; a.H = d->n_heads; a.D = d->dim; a.ws = w.attn;
     a.out_rope_dim = d->out_rope_dim;
+    a.kv_fp8 = d->kv_format == CSA_KV_FP8 ? 1 : 0;
     if (w.qprep && (d->q_gamma[c2] != nullptr || d->q_rope_dim > 0))
       a.q = w.qprep + size_t(c2) * q_bytes(d);   // this call's prepared query
     a.rope_log2_base = d->out_rope_dim > 0 ? log2(double(d->rope_base)) : 0.0;

@@ -59,18 +59,34 @@ __device__ __forceinline__ void attn_split_mfma(const AttnArgs& a, AttnLds& L, i
   const int ra = tid & 7, cp = tid >> 3;
   const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + r * kAH * kAD;
   bf16x8_t vv[4][2];
-  bool okr[4];
+  bool okr[4], f8r[4];
   const uint16_t* srcs[4];
   auto locate = [&](int64_t j) {   // row pointers of tile j (the ids load here)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       srcs[i] = row_src(j + 4 * ra + i, int(j1));
       okr[i] = srcs[i] != nullptr;
+      f8r[i] = okr[i] && a.kv_fp8 && j + 4 * ra + i < a.top_k;
     }
+  };
+  // chunk c (dims 8c .. 8c+7) of an FP8 entry: eight E4M3 codes at byte 8c (c < 56), else
+  // eight bf16 values at byte 448 + 16 (c - 56)
+  auto chunk8 = [&](const uint16_t* row, int c) -> bf16x8_t {
+    const uint8_t* e = reinterpret_cast<const uint8_t*>(row);
+    if (c < kFp8Nope / 8) {
+      const uint2 w = *reinterpret_cast<const uint2*>(e + 8 * c);
+      return e4m3x8_to_bf16(w.x, w.y);
+    }
+    return *reinterpret_cast<const bf16x8_t*>(e + kFp8Nope + 16 * (c - kFp8Nope / 8));
   };
   auto gather = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      if (f8r[i]) {
+        vv[i][0] = chunk8(srcs[i], cp);
+        vv[i][1] = chunk8(srcs[i], cp + 32);
+        continue;
+      }
       const uint16_t* sc = okr[i] ? srcs[i] : qrow;
       vv[i][0] = *reinterpret_cast<const bf16x8_t*>(sc + cp * 8);
       vv[i][1] = *reinterpret_cast<const bf16x8_t*>(sc + (cp + 32) * 8);
@@ -295,19 +311,60 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
   __syncthreads();
   // rows 8 w .. 8 w + 7 of tile t into buffer b; rows past the list (and rows without a
   // valid address) read the query row and are masked
+  // An FP8 entry row (kv_fp8, list row < top_k) moves as its raw 576 bytes (lanes 0 .. 35 of
+  // the DMA; the others fetch query bytes into the rest of the slot) and is expanded in place
+  // to the bf16 layout once it has landed (expand). f8mask bit 8 b + i: row 8 w + i of buffer b.
+  uint32_t f8mask = 0u;
   auto issue = [&](int t, int b) {
+    f8mask &= ~(0xffu << (8 * b));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int tr = 8 * wave_u + i;
       const int jr = t * kTile + tr;
       const uint16_t* p = jr < nl ? L.rowp[jr] : nullptr;
-      dma_row((p != nullptr ? p : qrow) + (lane ^ kv_swz(tr)) * 8, &L.kv[b][tr * kKvRowD]);
+      const bool f8 = p != nullptr && a.kv_fp8 && j0 + jr < a.top_k;   // uniform
+      if (f8) {
+        const unsigned char* src = lane < kFp8EntryBytes / 16
+                                       ? reinterpret_cast<const unsigned char*>(p) + 16 * lane
+                                       : reinterpret_cast<const unsigned char*>(qrow) + 16 * lane;
+        dma_row(reinterpret_cast<const uint16_t*>(src), &L.kv[b][tr * kKvRowD]);
+        f8mask |= 1u << (8 * b + i);
+      } else {
+        dma_row((p != nullptr ? p : qrow) + (lane ^ kv_swz(tr)) * 8, &L.kv[b][tr * kKvRowD]);
+      }
       if (lane == 0) L.rowok[b][tr] = p != nullptr;
+    }
+  };
+  // this wave's FP8 rows of buffer b, after their DMA has landed (vmcnt(0)): every lane reads
+  // its raw 16 bytes of the row before any lane writes (one read instruction, whose result the
+  // writes wait for), so the expansion may overwrite the raw bytes in place. Raw chunk l < 28
+  // holds dims 16 l .. 16 l + 15 (bf16 chunks 2 l, 2 l + 1), raw chunk 28 .. 35 the bf16 dims
+  // 448 + 8 (l - 28) .. (bf16 chunk l + 28); bf16 chunk c goes to slot chunk c ^ swz(row).
+  auto expand = [&](int b) {
+    const uint32_t bits = (f8mask >> (8 * b)) & 0xffu;
+    if (bits == 0u) return;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (!((bits >> i) & 1u)) continue;   // uniform
+      const int tr = 8 * wave_u + i;
+      unsigned char* row = &L.kv[b][tr * kKvRowD];
+      const int sw = kv_swz(tr);
+      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
+      if (lane < kFp8EntryBytes / 16) raw = *reinterpret_cast<const uint4*>(row + 16 * lane);
+      if (lane < kFp8Nope / 16) {
+        const bf16x8_t lo = e4m3x8_to_bf16(raw.x, raw.y);
+        const bf16x8_t hi = e4m3x8_to_bf16(raw.z, raw.w);
+        *reinterpret_cast<bf16x8_t*>(row + 16 * ((2 * lane) ^ sw)) = lo;
+        *reinterpret_cast<bf16x8_t*>(row + 16 * ((2 * lane + 1) ^ sw)) = hi;
+      } else if (lane < kFp8EntryBytes / 16) {
+        *reinterpret_cast<uint4*>(row + 16 * ((lane + kFp8Nope / 16) ^ sw)) = raw;
+      }
     }
   };
   const int ntiles = (nl + kTile - 1) / kTile;
   if (ntiles > 0) issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  expand(0);
   __syncthreads();
 
   const float sl2 = a.scale * kLog2e;
@@ -399,6 +456,7 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
       O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pf, Vf, O[nt], 0, 0, 0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (t + 1 < ntiles) expand(b ^ 1);
     __syncthreads();
   }
 

@@ -29,6 +29,68 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // f rounded to the nearest bf16 value (ties to even), as a float
 __device__ __forceinline__ float round_to_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
+// ---- FP8 main-cache entries --------------------------------------------------------------
+// "DeepSeek V4-Flash: The Cost of Deciding What to Read", "Rebuilding the model from its
+// constants": a 512-dim key/value entry keeps its 64 rotary dims in bf16 and the rest in FP8,
+// 576 bytes. Channels 0 .. 447 are OCP E4M3 codes (bias 7, largest finite 448, no infinity),
+// channels 448 .. 511 follow as bf16.
+constexpr int kFp8Nope = 448;          // E4M3 channels of an entry
+constexpr int kFp8EntryBytes = 576;    // 448 + 2 * 64
+
+// E4M3 code of x: nearest value, ties to the even code, magnitudes past 448 to 448, a zero
+// magnitude as +0. The grid spacing at |x| is 2^(e-3), e = floor(log2 |x|) clamped below at
+// -6 (the subnormal spacing 2^-9); scaling by powers of two keeps every step exact.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const float a = fabsf(x);
+  const int e = int(__float_as_uint(fmaxf(a, 0x1p-6f)) >> 23) - 127;
+  const float inv_ulp = __uint_as_float(uint32_t(127 + 3 - e) << 23);   // 2^(3-e)
+  const float ulp = __uint_as_float(uint32_t(127 - 3 + e) << 23);       // 2^(e-3)
+  const float q = fminf(rintf(a * inv_ulp) * ulp, 448.f);
+  uint32_t code;
+  if (q >= 0x1p-6f) {
+    const uint32_t qb = __float_as_uint(q);
+    code = ((((qb >> 23) & 0xffu) - 127u + 7u) << 3) | ((qb >> 20) & 7u);
+  } else {
+    code = uint32_t(q * 512.f);   // subnormal m * 2^-9, m = 0 .. 7
+  }
+  return (x < 0.f && q > 0.f) ? (code | 0x80u) : code;
+}
+
+// Eight E4M3 codes (two dwords, code i in byte i) -> eight bf16 values, exact (every E4M3
+// value is a bf16 value): gfx950 v_cvt_scalef32_pk_bf16_fp8 with scale 1.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Channels c0 .. c0+7 (c0 % 8 == 0) of an FP8 entry from fp32 values v, stored as E4M3
+// (c0 < 448) or bf16. via_bf16: each value is first rounded to bf16 (the entry as a bf16 cache
+// would hold it), so that both parts quantise the same stored value.
+__device__ __forceinline__ void store_fp8_entry8(uint8_t* entry, int c0, const float* v,
+                                                 bool via_bf16) {
+  if (c0 < kFp8Nope) {
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i >> 2] |= e4m3_code(via_bf16 ? round_to_bf16(v[i]) : v[i]) << (8 * (i & 3));
+    *reinterpret_cast<uint2*>(entry + c0) = make_uint2(w[0], w[1]);
+  } else {
+    uint4 b;
+    b.x = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+    b.y = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+    b.z = uint32_t(f32_to_bf16(v[4])) | (uint32_t(f32_to_bf16(v[5])) << 16);
+    b.w = uint32_t(f32_to_bf16(v[6])) | (uint32_t(f32_to_bf16(v[7])) << 16);
+    *reinterpret_cast<uint4*>(entry + kFp8Nope + 2 * (c0 - kFp8Nope)) = b;
+  }
+}
+
 // cos and sin of the RoPE angle p * base^(-2j/rope_dim) (p may be negative): formed and reduced
 // to [-pi, pi] in double precision, since positions reach millions of radians
 __device__ __forceinline__ void rope_cos_sin(double p, int j, int rope_dim, double log2_base,

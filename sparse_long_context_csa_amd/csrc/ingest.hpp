@@ -133,8 +133,13 @@ __device__ __forceinline__ void ingest_vector(const IngestArgs& a, int64_t sq, i
       float res[8];
       pool8<T, kRegs>(xt, zt, d, (const T*)(main ? a.bias : a.bias_i) + c0, d, m, slot, xo, zo,
                       res);
-      T* dst = (T*)(main ? a.kv : a.k_idx) + (sq * a.e_cap + e) * d + c0;
-      Elt<T>::store8(dst, res);
+      if (main && a.kv_fp8) {   // the pooled entry in T (bf16), then the FP8 entry form
+        store_fp8_entry8(static_cast<uint8_t*>(a.kv) + (sq * a.e_cap + e) * kFp8EntryBytes, c0,
+                         res, true);
+      } else {
+        T* dst = (T*)(main ? a.kv : a.k_idx) + (sq * a.e_cap + e) * d + c0;
+        Elt<T>::store8(dst, res);
+      }
     }
     return;
   }

@@ -31,6 +31,7 @@ struct IngestArgs {
   void *x_tail, *z_tail, *xi_tail, *zi_tail;
   const void *bias, *bias_i;
   void *kv, *k_idx;
+  int kv_fp8;             // kv holds FP8 entries (576 bytes: 448 E4M3 + 64 bf16 channels)
   void* k_scale;          // non-null: k_idx holds MXFP4 codes, k_scale their scale bytes
   void* win[4];
   const void* win_new[4];
@@ -121,6 +122,12 @@ hipError_t launch_norm_rope(int dt, const void* x, const void* gamma, const int6
                             void* out, int64_t n_rows, int n_heads, int dim, int rope_dim,
                             float base, float eps, int flags, hipStream_t s);
 
+// ---- FP8 main-cache entries (kv_fp8.hip) ---------------------------------------------------
+// x [n_rows, 512] (T) -> entries [n_rows, 576] bytes; entries -> bf16 [n_rows, 512]
+hipError_t launch_quantize_kv_fp8(int dt, const void* x, void* out, int64_t n_rows,
+                                  hipStream_t s);
+hipError_t launch_dequantize_kv_fp8(const void* in, void* out, int64_t n_rows, hipStream_t s);
+
 // ---- MXFP4 storage of indexer keys (mxfp4.hpp) --------------------------------------------
 // x [n_rows, dim] (dim % 32 == 0) -> codes [n_rows, dim / 2] bytes, scales [n_rows, dim / 32]
 hipError_t launch_quantize_mxfp4(int dt, const void* x, void* codes, void* scales, int64_t n_rows,
@@ -190,6 +197,8 @@ struct AttnArgs {
   // (2j, 2j+1) by -q_pos * base^(-2j/out_rope_dim) before the store (0: off)
   int out_rope_dim;
   double rope_log2_base;
+  // kv holds FP8 entries (576 bytes: 448 E4M3 + 64 bf16 channels; bf16 64 x 512 heads only)
+  int kv_fp8;
 };
 size_t attn_ws_bytes(int64_t rows, int H, int D, int top_k, int window, int dt);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);

@@ -7,7 +7,7 @@ import torch
 import datagen
 import sparse_long_context_csa_amd as csa_lib
 from oracle import csa as ocsa
-from oracle import gaps, mx
+from oracle import fp8, gaps, mx
 from oracle.pipeline import f64, i64
 
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
@@ -147,9 +147,41 @@ def mxfp4_case(spec):
     return case, {"k_idx": kc, "k_idx_scale": ks}
 
 
+def assert_fp8_entry(entry, exact, xabs_max, what=""):
+    """The FP8 form of a pooled main entry. The GPU's fp32 pooling lies within 4e-6 max_j |x_j|
+    of the exact value; rounding to bf16 and then to E4M3 (or bf16 for the rotary channels) is
+    monotone, so each stored value lies between the cached values of exact -/+ that error (the
+    same value, hence bit-exact, wherever no rounding boundary falls in between)."""
+    tol = 4e-6 * np.asarray(xabs_max)
+    lo = fp8.cached_entries(ocsa.store(exact - tol, "bf16"))
+    hi = fp8.cached_entries(ocsa.store(exact + tol, "bf16"))
+    got = fp8.decode_entries(np.asarray(entry, dtype=np.uint8))
+    bad = (got < lo) | (got > hi)
+    if np.any(bad):
+        k = int(np.argwhere(bad)[0][0])
+        raise AssertionError(f"{what}: channel {k} holds {got[k]}, outside [{lo[k]}, {hi[k]}] "
+                             f"(exact {exact[k]})")
+
+
+def fp8_case(case):
+    """Turns a bf16 decode case into one with an FP8 main cache: the oracle's case holds the
+    cached values of the generated entries (oracle encoder); the GPU gets the entries that
+    csa_quantize_kv_fp8 makes of the same bf16 values, checked equal byte for byte. Returns
+    the device state {"kv": uint8 [B, E, 576]}."""
+    kv = case["kv"]
+    want = fp8.encode_entries(f64(kv))
+    case["kv"] = torch.from_numpy(fp8.decode_entries(want)).to(kv.dtype)
+    case["kv_format"] = "fp8"
+    k8 = csa_lib.quantize_kv_fp8(dev(kv))
+    torch.cuda.synchronize()
+    assert np.array_equal(k8.cpu().numpy(), want)
+    return {"kv": k8}
+
+
 def run_step(case, idx_state=None):
-    """One csa_decode_step over copies of the case's state (idx_state: the MXFP4 indexer cache
-    {"k_idx": codes, "k_idx_scale": scales} on the device, replacing case["k_idx"])."""
+    """One csa_decode_step over copies of the case's state (idx_state: device tensors that
+    replace the case's own, e.g. the MXFP4 indexer cache {"k_idx": codes, "k_idx_scale":
+    scales} or the FP8 main cache {"kv": entries})."""
     spec = case["spec"]
     g = {k: dev(v) for k, v in case.items() if isinstance(v, torch.Tensor)}
     rings = [dev(r).clone() for r in case["rings"]]
@@ -197,6 +229,10 @@ def check_step(case, ref, st, rings, out, idx):
                 x[slot] = f64(case[xn][b])
                 z[slot] = f64(case[zn][b])
                 exact = ocsa.compress(x, z, f64(case[bias]), spec.m)[0]
+                if name == "kv" and case.get("kv_format") == "fp8":
+                    assert_fp8_entry(st["kv"][b, e].cpu().numpy(), exact,
+                                     np.abs(x).max(axis=0), f"FP8 entry {e} of seq {b}")
+                    continue
                 if name == "k_idx" and case.get("idx_format") == "mxfp4":
                     assert_mx_entry(st["k_idx"][b, e].cpu().numpy(),
                                     st["k_idx_scale"][b, e].cpu().numpy(), exact,

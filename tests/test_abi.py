@@ -38,7 +38,8 @@ def test_header_declares_the_calls():
         "csa_abi_version", "csa_status_str", "csa_compress", "csa_index_topk_workspace_size",
         "csa_index_topk", "csa_index_blocks_workspace_size", "csa_index_blocks",
         "csa_sparse_attn_workspace_size", "csa_sparse_attn", "csa_decode_step_workspace_size",
-        "csa_decode_step", "csa_quantize_mxfp4", "csa_compress_c4a", "csa_norm_rope"}
+        "csa_decode_step", "csa_quantize_mxfp4", "csa_compress_c4a", "csa_norm_rope",
+        "csa_quantize_kv_fp8", "csa_dequantize_kv_fp8", "csa_sparse_attn_fp8"}
 
 
 def test_binding_covers_every_declared_function():
@@ -86,11 +87,13 @@ def test_decode_desc_mirrors_the_header_struct():
     # 17 tensor pointers, 5 arrays of CSA_MAX_ATTN pointers, out_idx, the phase events, the
     # scan kernel's start and stop events; idx_format padded to 8 B, k_idx_scale, then
     # score_format, out_rope_dim and rope_base (12 B, padded to 16), the CSA_MAX_ATTN query
-    # gammas, q_rope_dim padded to 8 B
+    # gammas, q_rope_dim and kv_format (8 B)
     n_ptr = 17 + 5 * _lib.MAX_ATTN + 1 + _lib.DECODE_EVENTS + 2
     assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr + 8 + 8 + 16 + 8 * _lib.MAX_ATTN + 8
     for name, val in (("CSA_IDX_DTYPE", _lib.IDX_DTYPE), ("CSA_IDX_MXFP4", _lib.IDX_MXFP4),
-                      ("CSA_SCORE_F32", _lib.SCORE_F32), ("CSA_SCORE_BF16", _lib.SCORE_BF16)):
+                      ("CSA_SCORE_F32", _lib.SCORE_F32), ("CSA_SCORE_BF16", _lib.SCORE_BF16),
+                      ("CSA_KV_DTYPE", _lib.KV_DTYPE), ("CSA_KV_FP8", _lib.KV_FP8),
+                      ("CSA_KV_FP8_BYTES", _lib.KV_FP8_BYTES)):
         assert int(re.search(rf"#define\s+{name}\s+(\d+)", _header()).group(1)) == val
 
 
@@ -183,6 +186,29 @@ def test_quantize_mxfp4_validation(lib):
     assert lib.csa_quantize_mxfp4(ok, ok, ok, 0, 128, 1, None) == 0        # nothing to do
 
 
+def test_kv_fp8_validation(lib):
+    ok = C.c_void_p(256)   # never dereferenced: every call below fails validation or is empty
+    assert lib.csa_quantize_kv_fp8(ok, ok, 4, 7, None) == -3             # dtype
+    assert lib.csa_quantize_kv_fp8(ok, ok, -1, 1, None) == -2
+    assert lib.csa_quantize_kv_fp8(None, ok, 4, 1, None) == -1
+    assert lib.csa_quantize_kv_fp8(ok, C.c_void_p(256 + 8), 4, 1, None) == -2   # alignment
+    assert lib.csa_quantize_kv_fp8(ok, ok, 0, 1, None) == 0              # nothing to do
+    assert lib.csa_dequantize_kv_fp8(ok, None, 4, None) == -1
+    assert lib.csa_dequantize_kv_fp8(C.c_void_p(256 + 4), ok, 4, None) == -2
+    assert lib.csa_dequantize_kv_fp8(ok, ok, -3, None) == -2
+    assert lib.csa_dequantize_kv_fp8(ok, ok, 0, None) == 0
+
+    def attn(kv=ok, H=64, D=512, dtype=1):
+        return lib.csa_sparse_attn_fp8(ok, kv, ok, 512, ok, 128, 128, ok, None, 0.1, ok, 1, 1,
+                                       1024, H, D, ok, 1 << 40, dtype, None)
+
+    assert attn(dtype=0) == -4            # the FP8 cache is read by the bf16 64 x 512 path
+    assert attn(H=32) == -4
+    assert attn(D=256) == -4
+    assert attn(dtype=9) == -3
+    assert attn(kv=C.c_void_p(256 + 8)) == -2
+
+
 def test_decode_validation(lib):
     d = _desc()
     nb = lib.csa_decode_step_workspace_size(C.byref(d))
@@ -257,6 +283,13 @@ def test_decode_mxfp4_validation(lib):
     assert step(full(idx_format=_lib.IDX_DTYPE, out_rope_dim=40, rope_base=1e4)) == -4
     assert step(full(idx_format=_lib.IDX_DTYPE, q_rope_dim=7, rope_base=1e4)) == -2
     assert step(full(idx_format=_lib.IDX_DTYPE, q_rope_dim=64, rope_base=0.5)) == -2
+    # FP8 main cache: bf16 64 x 512 heads, 16-byte aligned entries, a known format code
+    assert step(full(idx_format=_lib.IDX_DTYPE, kv_format=2)) == -2
+    assert step(full(idx_format=_lib.IDX_DTYPE, kv_format=_lib.KV_FP8, dtype=0)) == -4
+    assert step(full(idx_format=_lib.IDX_DTYPE, kv_format=_lib.KV_FP8, n_heads=32)) == -4
+    d = full(idx_format=_lib.IDX_DTYPE, kv_format=_lib.KV_FP8)
+    d.kv = 256 + 8
+    assert step(d) == -2
 
 
 def test_binding_raises_on_errors(lib):

@@ -443,3 +443,73 @@ def test_quantize_mxfp4_bit_exact(dtype):
     ref_c, ref_s = omx.quantize(f64(xt))
     assert np.array_equal(scales.cpu().numpy(), ref_s)
     assert np.array_equal(codes.cpu().numpy(), omx.pack(ref_c))
+
+
+# ------------------------------------------------------------------------------ FP8 main cache
+def _fp8_edge_rows():
+    """Entries whose E4M3 channels sit on rounding midpoints (both signs), past the largest
+    value, in the subnormal range, or at zero (all bf16-exact)."""
+    from oracle import fp8 as of8
+    fin = of8.E4M3_VALUES[np.isfinite(of8.E4M3_VALUES)]
+    mag = np.sort(np.unique(np.abs(fin)))
+    special = np.concatenate([(mag[1:] + mag[:-1]) / 2, [464.0, 500.0, 1e4, 2.0 ** -10,
+                                                         3 * 2.0 ** -11, 2.0 ** -12, 0.0]])
+    rows = []
+    for sign in (1.0, -1.0):
+        r = np.resize(special * sign, 512)
+        r[448:] = np.linspace(-3, 3, 64)
+        rows.append(r)
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_kv_fp8_bit_exact(dtype):
+    from oracle import fp8 as of8
+    g = np.random.default_rng(41)
+    x = g.standard_normal((200, 512)) * np.exp(0.7 * g.standard_normal((200, 1)))
+    x = np.concatenate([x, _fp8_edge_rows()])
+    xt = torch.from_numpy(x).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    got = csa.quantize_kv_fp8(dev(xt)).cpu().numpy()
+    want = of8.encode_entries(f64(xt))
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"first mismatch at {tuple(bad[0])}: {got[tuple(bad[0])]} vs {want[tuple(bad[0])]}"
+
+
+def test_dequantize_kv_fp8_every_code():
+    """Every finite E4M3 code decodes to its exact value (hardware conversion, scale 1); the
+    rotary channels pass through."""
+    from oracle import fp8 as of8
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    e = np.zeros((3, 576), np.uint8)
+    for r in range(3):
+        e[r, :448] = np.resize(np.roll(codes, 97 * r), 448)
+        e[r, 448:] = np.random.default_rng(r).integers(0, 256, 128).astype(np.uint8)
+        e[r, 449::2] &= 0x3F   # finite bf16 rotary values (top exponent bit clear)
+    out = csa.dequantize_kv_fp8(dev(torch.from_numpy(e))).cpu()
+    np.testing.assert_array_equal(f64(out), of8.decode_entries(e))
+
+
+@pytest.mark.parametrize("B,Q,E,K,W,w_cap", [
+    (4, 1, 5000, 512, 128, 128),       # decode: row splits + combine
+    (2, 3, 3000, 100, 128, 256),       # ragged tiles: FP8 and window rows share a tile
+    (1, 300, 2000, 512, 128, 4096),    # many rows: one workgroup per row
+    (2, 2, 1000, 64, 0, 1),            # selection only
+    (1, 256, 3000, 896, 128, 128),     # 32 tiles per row: the longest list held in LDS
+    (1, 260, 4000, 2048, 128, 128),    # 68 tiles per row: register-staged tiles
+])
+def test_attention_fp8_cache(B, Q, E, K, W, w_cap):
+    """csa_sparse_attn_fp8 against the oracle's attention over the entries' FP8 values."""
+    from oracle import fp8 as of8
+    q, kv, idx, win, sink, pos = attn_case(B, Q, E, 64, 512, K, W, w_cap, "bf16",
+                                           seed=B * 11 + Q, t_lo=0, t_hi=5 * w_cap)
+    pos.view(-1)[0] = 5
+    k8 = csa.quantize_kv_fp8(dev(kv))
+    enc = of8.encode_entries(f64(kv))
+    assert np.array_equal(k8.cpu().numpy(), enc)
+    scale = 1 / math.sqrt(512)
+    out = csa.sparse_attn(dev(q), k8, dev(idx), dev(win), w_cap, W, dev(pos), dev(sink),
+                          scale).cpu()
+    kv_vals = torch.from_numpy(of8.decode_entries(enc))
+    ref = pipeline.sparse_attn(q, kv_vals, idx, win, w_cap, W, pos, sink, scale, "bf16")
+    for (b, i), r in ref.items():
+        assert_rows_close(f64(out[b, i]), r, 2e-2, f"attn fp8 {(b, i)}")

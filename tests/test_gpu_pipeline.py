@@ -6,7 +6,8 @@ import torch
 
 import datagen
 import sparse_long_context_csa_amd as csa
-from gpu_helpers import assert_ids, assert_rows_close, check_step, dev, mxfp4_case, run_step
+from gpu_helpers import (assert_ids, assert_rows_close, check_step, dev, fp8_case, mxfp4_case,
+                         run_step)
 from oracle import csa as ocsa
 from oracle import gaps, pipeline
 from oracle.pipeline import f64
@@ -320,3 +321,31 @@ def test_decode_step_graph_replay_matches_eager(variant):
         assert torch.equal(step.out_idx.cpu(), idx), f"replay {rep}: ids differ"
         for c in range(spec.n_attn):
             assert torch.equal(step.out[c].cpu(), out[c]), f"replay {rep}: output {c} differs"
+
+
+# FP8 main cache: 576-byte entries; the attention expands them to bf16 on their way to the MFMA
+# operands, the step stores the entry it completes in FP8.
+@pytest.mark.parametrize("spec,mx", [
+    (datagen.CaseSpec(7150, "decode", B=5, L=24000, m=4, w_cap=256, ragged=True), False),
+    (datagen.CaseSpec(7151, "decode", B=3, L=40000, m=1, w_cap=128, block_size=8,
+                      max_blocks=512, n_attn=3, ragged=True), False),
+    (datagen.CaseSpec(7152, "decode", B=260, L=3000, m=4, w_cap=128, ragged=True), False),
+    (datagen.CaseSpec(7153, "decode", B=4, L=4 * 50000, m=4, w_cap=128, ragged=True), True),
+], ids=["flat", "hier_three_calls", "rows_260", "with_mxfp4_keys"])
+def test_decode_step_fp8_cache(spec, mx):
+    if mx:
+        case, state = mxfp4_case(spec)
+    else:
+        case, state = datagen.make_case(spec), {}
+    state.update(fp8_case(case))
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    step, st, rings, out, idx = run_step(case, state)
+    check_step(case, ref, st, rings, out, idx)
+    # entries the step did not complete are untouched
+    for b in range(spec.B):
+        t = int(case["pos"][b])
+        keep = np.ones(st["kv"].shape[1], bool)
+        if (t + 1) % spec.m == 0:
+            keep[(t + 1) // spec.m - 1] = False
+        assert torch.equal(st["kv"][b].cpu()[keep], state["kv"][b].cpu()[keep])
