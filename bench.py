@@ -241,11 +241,23 @@ def bench_hca(args):
     qp = pos.view(B, 1).to(dev)
     idx = torch.arange(E, dtype=torch.int32).repeat(B, 1, 1).contiguous().to(dev)
     outs = [torch.empty(B, 1, H, D, dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    fp8 = args.kv_format == "fp8"
+    if fp8:   # the cache as 576-byte FP8 entries; the pooled entry is quantised into it
+        for st in states:
+            st["kv"] = csa.quantize_kv_fp8(st["kv"])
+            st["entry"] = torch.empty(B, 1, D, dtype=torch.bfloat16, device=dev)
+            st["entry8"] = torch.empty(B, 1, 576, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
 
     def step(c, evs=None):
         st = states[c]
         if evs: evs[0].record()
-        csa.compress(st["x"], st["z"], bias, m, out=st["kv"][:, e_new:], out_seq_stride=E * D)
+        if fp8:
+            csa.compress(st["x"], st["z"], bias, m, out=st["entry"])
+            csa.quantize_kv_fp8(st["entry"], out=st["entry8"])
+            st["kv"][:, e_new:e_new + 1].copy_(st["entry8"])
+        else:
+            csa.compress(st["x"], st["z"], bias, m, out=st["kv"][:, e_new:], out_seq_stride=E * D)
         if evs: evs[1].record()
         csa.sparse_attn(q, st["kv"], idx, st["ring"], spec.w_cap, spec.W, qp, sink,
                         case["scale"], out=outs[c])
@@ -267,7 +279,8 @@ def bench_hca(args):
         torch.cuda.synchronize()
         ph[0] += evs[0].elapsed_time(evs[1]) / n_prof
         ph[1] += evs[1].elapsed_time(evs[2]) / n_prof
-    attn_bytes = B * (E + spec.W) * D * 2 + 2 * B * H * D * 2 + B * E * 4 + H * 4
+    e_bytes = 576 if fp8 else D * 2
+    attn_bytes = B * (E * e_bytes + spec.W * D * 2) + 2 * B * H * D * 2 + B * E * 4 + H * 4
     comp_bytes = B * (2 * m * D * 2 + D * 2) + m * D * 2
     achieved = attn_bytes / (ph[1] * 1e-3) / 1e9
     res = {
@@ -287,6 +300,9 @@ def bench_hca(args):
         "phases_us": {"compress": round(ph[0] * 1e3, 2), "attention": round(ph[1] * 1e3, 2)},
         "compress_bytes": comp_bytes,
     }
+    if fp8:
+        res["metric"] += ", FP8 main cache"
+        res["config"]["kv_cache"] = "fp8 (448 E4M3 + 64 bf16 channels, 576 B per entry)"
     print(json.dumps(res), flush=True)
 
 
@@ -356,8 +372,12 @@ def main():
                          "line then also reports the recall of the fp32 selection)")
     ap.add_argument("--rope-dim", type=int, default=0,
                     help="decode workloads: each query's per-head RMSNorm and RoPE on its last N "
-                         "channels fused into the attention's query load, and the inverse RoPE "
-                         "on the output fused into its store (0: off)")
+                         "channels (prepared in the selection launch), and the inverse RoPE on "
+                         "the output fused into the attention's store (0: off)")
+    ap.add_argument("--kv-format", default="bf16", choices=("bf16", "fp8"),
+                    help="main KV cache of the decode workloads (--config 2/4/5/6): bf16 "
+                         "entries, or 576-byte FP8 entries (csa_quantize_kv_fp8 of the same "
+                         "entries, made before the timed region)")
     ap.add_argument("--compressor", default="single", choices=("single", "c4a"),
                     help="chunked prefill (--config 3): the single-stream compressor, or the "
                          "overlapped two-stream one for both caches")
@@ -400,6 +420,10 @@ def main():
     if mx:
         codes, scales = csa.quantize_mxfp4(case["k_idx"].to(dev))
         torch.cuda.synchronize()
+    kv8 = None
+    if args.kv_format == "fp8":
+        kv8 = csa.quantize_kv_fp8(case["kv"].to(dev))
+        torch.cuda.synchronize()
     q_gammas = None
     if args.rope_dim:
         q_gammas = [(datagen.tensor(spec.case_id, 90 + c, (spec.D,), spec.dtype, 0.3) + 1.0).to(dev)
@@ -410,6 +434,8 @@ def main():
         if mx:
             st["k_idx"] = codes.clone()
             st["k_idx_scale"] = scales.clone()
+        if kv8 is not None:
+            st["kv"] = kv8.clone()
         rings = [r.to(dev) for r in case["rings"]]
         win_new = [shared["x_new"] if (i == 0 and datagen.ring_from_raw(spec)) else None
                    for i in range(spec.n_attn)]
@@ -510,7 +536,9 @@ def main():
                                        n_attn=spec.n_attn,
                                        pool=spec.block_size * spec.max_blocks,
                                        ring_write=datagen.ring_from_raw(spec),
-                                       key_bytes=key_bytes).total
+                                       key_bytes=key_bytes,
+                                       entry_bytes=acc.FP8_ENTRY_BYTES if kv8 is not None
+                                       else None).total
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
@@ -546,6 +574,9 @@ def main():
         res["metric"] = f"CSA decode queries/sec ({datagen.WORKLOAD_NAMES[args.config]})"
     if mx:
         res["metric"] += ", MXFP4 indexer keys"
+    if kv8 is not None:
+        res["metric"] += ", FP8 main cache"
+        res["config"]["kv_cache"] = "fp8 (448 E4M3 + 64 bf16 channels, 576 B per entry)"
     if args.rope_dim:
         res["metric"] += (f", query RMSNorm + RoPE and output inverse RoPE on the last "
                           f"{args.rope_dim} channels")
@@ -571,6 +602,8 @@ def main():
             # the oracle's step with an MXFP4 cache (the new entry's key quantised); the cached
             # keys are scored as generated, which is the same work as scoring their MXFP4 values
             case["idx_format"] = "mxfp4"
+        if kv8 is not None:
+            case["kv_format"] = "fp8"
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
         if mx:
             res["cpu_baseline"]["sample"] += (" with an MXFP4 cache (new key quantised; cached "

@@ -57,24 +57,31 @@ class StepBytes:
 
 def decode_step_bytes(B: int, n_vis: int, m: int, D: int, H: int, H_I: int, d_I: int, K: int,
                       W: int, n_attn: int = 1, pool: int = 0, elt: int = BF16,
-                      ring_write: bool = True, key_bytes: int | None = None) -> StepBytes:
+                      ring_write: bool = True, key_bytes: int | None = None,
+                      entry_bytes: int | None = None) -> StepBytes:
     """Algorithmic HBM bytes of one fused decode step over B sequences, each with n_vis
     visible entries (all sequences at a block boundary, so one entry is pooled per stream).
     pool > 0: hierarchical (stage-1 scan of n_vis keys, then ``pool`` rescored keys).
-    key_bytes: bytes of one cached indexer key (default d_I * elt; MXFP4: mxfp4_key_bytes)."""
+    key_bytes: bytes of one cached indexer key (default d_I * elt; MXFP4: mxfp4_key_bytes).
+    entry_bytes: bytes of one cached main entry (default D * elt; FP8: FP8_ENTRY_BYTES)."""
     kb = d_I * elt if key_bytes is None else key_bytes
+    eb = D * elt if entry_bytes is None else entry_bytes
     keys = B * n_vis * kb + B * pool * kb
     sel = min(K, pool if pool else n_vis)
-    gather = n_attn * B * (sel + W) * D * elt
+    gather = n_attn * B * (sel * eb + W * D * elt)
     queries = B * (H_I * d_I * elt + H_I * F32) * (2 if pool else 1) + n_attn * B * H * D * elt \
         + n_attn * H * F32
     outputs = n_attn * B * H * D * elt + B * K * 4
     # compressor: m tail rows + the new row for both streams (x, z, xi, zi) read, the new
     # row written to the tails, one entry per stream written, the ring row written
     per_row = (2 * D + 2 * d_I) * elt
-    compress = B * (m * per_row + per_row + D * elt + kb + (D * elt if ring_write else 0)) \
+    compress = B * (m * per_row + per_row + eb + kb + (D * elt if ring_write else 0)) \
         + m * (D + d_I) * elt
     return StepBytes(keys, gather, queries, outputs, compress)
+
+
+# "Rebuilding the model from its constants": 64 bf16 rotary dims + 448 FP8 dims per entry
+FP8_ENTRY_BYTES = 64 * 2 + 448
 
 
 def mxfp4_key_bytes(d_I: int) -> int:

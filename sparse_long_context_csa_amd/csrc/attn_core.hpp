@@ -336,28 +336,41 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
     }
   };
   // this wave's FP8 rows of buffer b, after their DMA has landed (vmcnt(0)): every lane reads
-  // its raw 16 bytes of the row before any lane writes (one read instruction, whose result the
-  // writes wait for), so the expansion may overwrite the raw bytes in place. Raw chunk l < 28
+  // its raw 16 bytes of each row before any lane writes (the writes use the reads' results and
+  // each row is read by one instruction), so the expansion may overwrite the raw bytes in
+  // place. Raw chunk l < 28
   // holds dims 16 l .. 16 l + 15 (bf16 chunks 2 l, 2 l + 1), raw chunk 28 .. 35 the bf16 dims
   // 448 + 8 (l - 28) .. (bf16 chunk l + 28); bf16 chunk c goes to slot chunk c ^ swz(row).
   auto expand = [&](int b) {
     const uint32_t bits = (f8mask >> (8 * b)) & 0xffu;
     if (bits == 0u) return;
+    // four rows' raw chunks are read together (one wait per four rows), then converted and
+    // written
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (!((bits >> i) & 1u)) continue;   // uniform
-      const int tr = 8 * wave_u + i;
-      unsigned char* row = &L.kv[b][tr * kKvRowD];
-      const int sw = kv_swz(tr);
-      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-      if (lane < kFp8EntryBytes / 16) raw = *reinterpret_cast<const uint4*>(row + 16 * lane);
-      if (lane < kFp8Nope / 16) {
-        const bf16x8_t lo = e4m3x8_to_bf16(raw.x, raw.y);
-        const bf16x8_t hi = e4m3x8_to_bf16(raw.z, raw.w);
-        *reinterpret_cast<bf16x8_t*>(row + 16 * ((2 * lane) ^ sw)) = lo;
-        *reinterpret_cast<bf16x8_t*>(row + 16 * ((2 * lane + 1) ^ sw)) = hi;
-      } else if (lane < kFp8EntryBytes / 16) {
-        *reinterpret_cast<uint4*>(row + 16 * ((lane + kFp8Nope / 16) ^ sw)) = raw;
+    for (int h = 0; h < 8; h += 4) {
+      if (((bits >> h) & 0xfu) == 0u) continue;   // uniform
+      uint4 raw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        raw[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (((bits >> (h + i)) & 1u) && lane < kFp8EntryBytes / 16)
+          raw[i] = *reinterpret_cast<const uint4*>(
+              &L.kv[b][(8 * wave_u + h + i) * kKvRowD + 16 * lane]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!((bits >> (h + i)) & 1u)) continue;   // uniform
+        const int tr = 8 * wave_u + h + i;
+        unsigned char* row = &L.kv[b][tr * kKvRowD];
+        const int sw = kv_swz(tr);
+        if (lane < kFp8Nope / 16) {
+          const bf16x8_t lo = e4m3x8_to_bf16(raw[i].x, raw[i].y);
+          const bf16x8_t hi = e4m3x8_to_bf16(raw[i].z, raw[i].w);
+          *reinterpret_cast<bf16x8_t*>(row + 16 * ((2 * lane) ^ sw)) = lo;
+          *reinterpret_cast<bf16x8_t*>(row + 16 * ((2 * lane + 1) ^ sw)) = hi;
+        } else if (lane < kFp8EntryBytes / 16) {
+          *reinterpret_cast<uint4*>(row + 16 * ((lane + kFp8Nope / 16) ^ sw)) = raw[i];
+        }
       }
     }
   };
