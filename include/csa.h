@@ -131,7 +131,7 @@ int csa_norm_rope(const void *x, const void *gamma, const int64_t *pos, void *ou
 
 /* ---------------------------------------------------------------------------------------
  * csa_quantize_mxfp4 -- MXFP4 storage of indexer keys (production precision).
- *   [CoD "Rebuilding the model from its constants": the indexer cache is FP4, 64 bytes per
+ *   [CoD "What the cache costs, checked four ways": the indexer cache is FP4, 64 bytes per
  *   128-channel key; CoD "FP4, down to the index scores": 1 x 32 MXFP4 sub-blocks.]
  * Elements E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1,
  * 1.5, 2, 3, 4, 6), one E8M0 scale 2^(s - 127) per 32 consecutive channels. For each block:
@@ -148,9 +148,10 @@ int csa_quantize_mxfp4(const void *x, void *codes, void *scales, int64_t n_rows,
 
 /* ---------------------------------------------------------------------------------------
  * csa_quantize_kv_fp8 / csa_dequantize_kv_fp8 -- FP8 storage of main KV entries.
- *   [CoD "Rebuilding the model from its constants": the 64 rotary dimensions of a shared
+ *   [CoD "What the cache costs, checked four ways": the 64 rotary dimensions of a shared
  *   key/value entry stay in bf16 and the other 448 go to FP8: 64 * 2 + 448 = 576 bytes per
- *   512-dim entry; CoD "The FP4 precision budget": the main attention runs in FP8.]
+ *   512-dim entry; CoD "The indexer is O(n), and that is the ceiling": the main
+ *   attention runs in FP8.]
  * Entry layout (CSA_KV_FP8_BYTES = 576): bytes 0..447 are the E4M3 codes of channels 0..447,
  * bytes 448..575 channels 448..511 as little-endian bf16 (nearest-even). E4M3 is the OCP
  * format (sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is
@@ -350,7 +351,7 @@ typedef struct csa_decode_desc {
    * aligned). The scan scores the keys' exact values; the entry a step completes is pooled,
    * rounded to T and stored quantised. MXFP4 needs T = bf16, idx_heads 64, idx_dim 128, the
    * flat selection (block_size 0) and m <= 8; otherwise CSA_ERR_UNSUPPORTED.
-   *   [CoD "Rebuilding the model from its constants": the indexer cache is FP4, 64 bytes per
+   *   [CoD "What the cache costs, checked four ways": the indexer cache is FP4, 64 bytes per
    *   128-channel key; CoD "FP4, down to the index scores": the indexer's query-key path
    *   loads its keys in FP4, 1 x 32 MXFP4 sub-blocks.] */
   int32_t idx_format;
@@ -388,7 +389,7 @@ typedef struct csa_decode_desc {
    * entry a step completes is pooled, rounded to T and stored as an FP8 entry, and the
    * attention reads every selected entry at its exact value. Needs T = bf16, n_heads 64 and
    * dim 512; otherwise CSA_ERR_UNSUPPORTED.
-   *   [CoD "Rebuilding the model from its constants": 448 FP8 + 64 bf16 rotary dims =
+   *   [CoD "What the cache costs, checked four ways": 448 FP8 + 64 bf16 rotary dims =
    *   576 bytes per entry.] */
   int32_t kv_format;
 } csa_decode_desc;

@@ -3,10 +3,11 @@
 Only tests/, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may import
 this module; the product path never does.
 
-"DeepSeek V4-Flash: The Cost of Deciding What to Read", section "Rebuilding the model from its
-constants": the rotary part of a head is exactly its last 64 dimensions, those are kept in bf16
+"DeepSeek V4-Flash: The Cost of Deciding What to Read", section "What the cache costs, checked four
+ways": the rotary part of a head is exactly its last 64 dimensions, those are kept in bf16
 and the rest in FP8, so one shared key/value entry of head dimension 512 takes 64 * 2 + 448 =
-576 bytes; section "The FP4 precision budget": the main attention runs in FP8.
+576 bytes; section "The indexer is O(n), and that is the ceiling": the main attention runs
+in FP8.
 
 Readings taken (the pages fix the byte count, not the element format):
   * FP8 is the OCP E4M3 format ("fn": 1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no

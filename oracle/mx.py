@@ -3,8 +3,8 @@
 Only tests/, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may import
 this module; the product path never does.
 
-"DeepSeek V4-Flash: The Cost of Deciding What to Read", section "Rebuilding the model from its
-constants" (the indexer cache is FP4: a 128-channel indexer key takes 64 bytes) and section
+"DeepSeek V4-Flash: The Cost of Deciding What to Read", section "What the cache costs, checked
+four ways" (the indexer cache is FP4: a 128-channel indexer key takes 64 bytes) and section
 "FP4, down to the index scores" (the indexer's query-key path is cached and loaded in FP4; the
 MXFP4 sub-blocks are 1 x 32). Reading taken for the element and scale formats (the pages name
 MXFP4 but do not spell it out; another page gives a per-16 E4M3 scale for a different cache):

@@ -80,13 +80,13 @@ def decode_step_bytes(B: int, n_vis: int, m: int, D: int, H: int, H_I: int, d_I:
     return StepBytes(keys, gather, queries, outputs, compress)
 
 
-# "Rebuilding the model from its constants": 64 bf16 rotary dims + 448 FP8 dims per entry
+# "What the cache costs, checked four ways": 64 bf16 rotary dims + 448 FP8 dims per entry
 FP8_ENTRY_BYTES = 64 * 2 + 448
 
 
 def mxfp4_key_bytes(d_I: int) -> int:
     """Bytes of one MXFP4 indexer key: a 4-bit code per channel and one scale byte per 32
-    channels ("Rebuilding the model from its constants": 64 bytes of codes per 128-channel key)."""
+    channels ("What the cache costs, checked four ways": 64 bytes of codes per 128-channel key)."""
     return d_I // 2 + d_I // 32
 
 

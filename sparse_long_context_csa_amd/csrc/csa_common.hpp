@@ -30,8 +30,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ float round_to_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
 // ---- FP8 main-cache entries --------------------------------------------------------------
-// "DeepSeek V4-Flash: The Cost of Deciding What to Read", "Rebuilding the model from its
-// constants": a 512-dim key/value entry keeps its 64 rotary dims in bf16 and the rest in FP8,
+// "DeepSeek V4-Flash: The Cost of Deciding What to Read", "What the cache costs, checked
+// four ways": a 512-dim key/value entry keeps its 64 rotary dims in bf16 and the rest in FP8,
 // 576 bytes. Channels 0 .. 447 are OCP E4M3 codes (bias 7, largest finite 448, no infinity),
 // channels 448 .. 511 follow as bf16.
 constexpr int kFp8Nope = 448;          // E4M3 channels of an entry

@@ -1,7 +1,7 @@
 // FP8 storage of the main KV entries.
 //
-// "DeepSeek V4-Flash: The Cost of Deciding What to Read", "Rebuilding the model from its
-// constants": a shared key/value entry of head dimension 512 keeps its 64 rotary dimensions in
+// "DeepSeek V4-Flash: The Cost of Deciding What to Read", "What the cache costs, checked
+// four ways": a shared key/value entry of head dimension 512 keeps its 64 rotary dimensions in
 // bf16 and the other 448 in FP8, 576 bytes. Element format: OCP E4M3 (no scale: the 576 bytes
 // leave no room for one, and the entries are RMS-normalised per head).
 //

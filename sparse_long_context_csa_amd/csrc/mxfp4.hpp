@@ -1,7 +1,7 @@
 // MXFP4 storage of indexer keys: E2M1 elements, one E8M0 scale per 32 channels.
 //
-// "DeepSeek V4-Flash: The Cost of Deciding What to Read", section "Rebuilding the model from
-// its constants" (the indexer cache is FP4: 64 bytes per 128-channel key) and section "FP4,
+// "DeepSeek V4-Flash: The Cost of Deciding What to Read", section "What the cache costs,
+// checked four ways" (the indexer cache is FP4: 64 bytes per 128-channel key) and section "FP4,
 // down to the index scores" (1 x 32 MXFP4 sub-blocks). Format as in the OCP microscaling
 // definition: element = sign, 2 exponent bits (bias 1), 1 mantissa bit (magnitudes 0, 0.5, 1,
 // 1.5, 2, 3, 4, 6); block scale 2^(s - 127) stored as the byte s. Quantisation: s = floor(log2

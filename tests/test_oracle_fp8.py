@@ -1,8 +1,8 @@
 """Pins of the oracle's FP8 (E4M3) main-cache entries (oracle/fp8.py) against the OCP E4M3
 definition and a brute-force nearest-value search: hand-worked codes, every code's round trip,
 random and midpoint values against the table search, bf16 exactness and the 576-byte layout
-("DeepSeek V4-Flash: The Cost of Deciding What to Read", "Rebuilding the model from its
-constants": 64 bf16 RoPE dims + 448 FP8 dims = 576 bytes)."""
+("DeepSeek V4-Flash: The Cost of Deciding What to Read", "What the cache costs, checked
+four ways": 64 bf16 RoPE dims + 448 FP8 dims = 576 bytes)."""
 import numpy as np
 import pytest
 
