@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 9
+#define CSA_ABI_VERSION 10
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -392,6 +392,16 @@ typedef struct csa_decode_desc {
    *   [CoD "What the cache costs, checked four ways": 448 FP8 + 64 bf16 rotary dims =
    *   576 bytes per entry.] */
   int32_t kv_format;
+  /* The entry a step completes: kv_gamma (T [dim]) or NULL applies the per-head RMSNorm (eps
+   * 1e-6) to the pooled entry; kv_rope_dim > 0 then turns its last kv_rope_dim channels by
+   * RoPE at t (base rope_base), t being the position of the newest token the entry pools; the
+   * result is rounded once to T (and then stored in kv_format). Needs dim 512; kv_rope_dim
+   * even and at most 64 (else CSA_ERR_UNSUPPORTED / CSA_ERR_SHAPE).
+   *   [CoD "Key and value are the same vector": RMSNorm per head on the compressed KV
+   *   entries; RoPE on the last 64 dimensions, the cached entry carrying its position's
+   *   rotation.] */
+  const void *kv_gamma;
+  int32_t kv_rope_dim;
 } csa_decode_desc;
 
 size_t csa_decode_step_workspace_size(const csa_decode_desc *d);

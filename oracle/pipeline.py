@@ -143,7 +143,9 @@ def decode_step(case: dict, seqs=None) -> dict:
     ([CoD] "Key and value are the same vector") before the store; case["q_gamma"] (per call, or
     None) and case["q_rope_dim"] prepare each call's query (RMSNorm, RoPE at +t) first. With
     case["kv_format"] == "fp8", case["kv"] holds the values of an FP8 main cache (576-byte
-    entries, oracle/fp8.py) and the new entry is attended at its cached value.
+    entries, oracle/fp8.py) and the new entry is attended at its cached value. case["kv_gamma"]
+    and case["kv_rope_dim"] give the new entry its per-head RMSNorm and RoPE (at t, the position
+    of the newest token it pools) before it is stored (rounded once).
     Returns a dict with per-sequence results (new entries, scores, pool, ids, outputs).
     """
     spec = case["spec"]
@@ -151,7 +153,8 @@ def decode_step(case: dict, seqs=None) -> dict:
     pos = i64(case["pos"])
     seqs = list(range(spec.B)) if seqs is None else list(seqs)
     ring_raw = spec.m > 1
-    res = {"ids": {}, "out": {}, "kv_new": {}, "ki_new": {}, "scores": {}, "pool": {},
+    res = {"ids": {}, "out": {}, "kv_new": {}, "kv_new_exact": {}, "ki_new": {}, "scores": {},
+           "pool": {},
            "scores2": {}, "n_vis": {}}
     bias, bias_i = f64(case["bias"]), f64(case["bias_i"])
     for b in seqs:
@@ -170,7 +173,16 @@ def decode_step(case: dict, seqs=None) -> dict:
         new_e = None
         if (t + 1) % m == 0:
             new_e = (t + 1) // m - 1
-            kv_e = csa.store(csa.compress(x_tail, z_tail, bias, m)[0], dt)
+            kv_p = csa.compress(x_tail, z_tail, bias, m)[0]
+            if case.get("kv_gamma") is not None:
+                # the new entry's single head: RMSNorm ([CoD] "Key and value are the same
+                # vector": RMSNorm per head on the compressed KV entries)
+                kv_p = csa.rms_norm(kv_p[None], f64(case["kv_gamma"]), 1e-6)[0]
+            if case.get("kv_rope_dim"):
+                # RoPE on its last channels at the position of the newest token it pools (t)
+                kv_p = csa.rope(kv_p[None], float(t), int(case["kv_rope_dim"]))[0]
+            kv_e = csa.store(kv_p, dt)
+            res["kv_new_exact"][b] = kv_p
             ki_e = csa.store(csa.compress(xi_tail, zi_tail, bias_i, m)[0], dt)
             res["kv_new"][b] = kv_e
             res["ki_new"][b] = ki_e

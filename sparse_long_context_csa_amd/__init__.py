@@ -238,12 +238,14 @@ class DecodeStep:
     out_rope_dim channels of every output head, in the attention's output store. q_gamma (a
     list of [dim] tensors or None per call) and q_rope_dim prepare each call's query (RMSNorm,
     RoPE at +pos) in the selection launch. A uint8 kv [n_seq, e_cap, 576] is an FP8 main
-    cache (quantize_kv_fp8's entries; kv_format CSA_KV_FP8)."""
+    cache (quantize_kv_fp8's entries; kv_format CSA_KV_FP8). kv_gamma ([dim] or None) and
+    kv_rope_dim give the entry a step completes its RMSNorm and RoPE at pos before it is
+    stored."""
 
     def __init__(self, *, m: int, top_k: int, window: int, scale: float, block_size: int = 0,
                  max_blocks: int = 0, out=None, out_idx=None, score_format: str = "f32",
                  out_rope_dim: int = 0, rope_base: float = 10000.0, q_gamma=None,
-                 q_rope_dim: int = 0, **t):
+                 q_rope_dim: int = 0, kv_gamma=None, kv_rope_dim: int = 0, **t):
         self.t = t
         kv = _dev(t["kv"], "kv")
         kv8 = kv.dtype == torch.uint8
@@ -310,6 +312,10 @@ class DecodeStep:
             if gq is not None:
                 d.q_gamma[c] = _dev(gq, "q_gamma", dt).data_ptr()
         d.kv_format = _lib.KV_FP8 if kv8 else _lib.KV_DTYPE
+        self.kv_gamma = kv_gamma   # the descriptor holds its address
+        if kv_gamma is not None:
+            d.kv_gamma = _dev(kv_gamma, "kv_gamma", dt).data_ptr()
+        d.kv_rope_dim = int(kv_rope_dim)
         d.out_idx = out_idx.data_ptr()
         self.desc = d
         nb = lib().csa_decode_step_workspace_size(C.byref(d))

@@ -37,6 +37,7 @@ class DecodeDesc(C.Structure):
         ("idx_format", i32), ("k_idx_scale", vp), ("score_format", i32),
         ("out_rope_dim", i32), ("rope_base", f32),
         ("q_gamma", vp * MAX_ATTN), ("q_rope_dim", i32), ("kv_format", i32),
+        ("kv_gamma", vp), ("kv_rope_dim", i32),
     ]
 
 

@@ -477,6 +477,11 @@ int check_decode_shapes(const csa_decode_desc* d) {
     if (d->dtype == CSA_BF16 && d->n_heads == 64 && d->dim == 512 && d->out_rope_dim % 16 != 0)
       return CSA_ERR_UNSUPPORTED;
   }
+  if (d->kv_rope_dim < 0 || d->kv_rope_dim % 2 != 0 || d->kv_rope_dim > d->dim)
+    return CSA_ERR_SHAPE;
+  if (d->kv_rope_dim > 0 && !(d->rope_base > 1.f)) return CSA_ERR_SHAPE;
+  if ((d->kv_gamma != nullptr || d->kv_rope_dim > 0) && (d->dim != 512 || d->kv_rope_dim > 64))
+    return CSA_ERR_UNSUPPORTED;
   if (d->kv_format != CSA_KV_DTYPE && d->kv_format != CSA_KV_FP8) return CSA_ERR_SHAPE;
   if (d->kv_format == CSA_KV_FP8 && (d->dtype != CSA_BF16 || d->n_heads != 64 || d->dim != 512))
     return CSA_ERR_UNSUPPORTED;
@@ -545,6 +550,9 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   void* key_scales = d->idx_format == CSA_IDX_MXFP4 ? d->k_idx_scale : nullptr;
   in.k_scale = key_scales;
   in.kv_fp8 = d->kv_format == CSA_KV_FP8 ? 1 : 0;
+  in.kv_gamma = d->kv_gamma;
+  in.kv_rope_dim = d->kv_rope_dim;
+  in.rope_log2_base = d->rope_base > 1.f ? log2(double(d->rope_base)) : 0.0;
   for (int c2 = 0; c2 < 4; ++c2) {
     in.win[c2] = c2 < d->n_attn ? d->win[c2] : nullptr;
     in.win_new[c2] = (c2 < d->n_attn && d->w_cap > 0) ? d->win_new[c2] : nullptr;
@@ -558,7 +566,6 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   if (w.qprep) {
     in.n_qprep = d->n_attn; in.q_heads = d->n_heads; in.q_dim = d->dim;
     in.q_rope_dim = d->q_rope_dim;
-    in.rope_log2_base = d->q_rope_dim > 0 ? log2(double(d->rope_base)) : 0.0;
     for (int c2 = 0; c2 < d->n_attn; ++c2) {
       in.qsrc[c2] = d->q[c2];
       in.qgamma[c2] = d->q_gamma[c2];

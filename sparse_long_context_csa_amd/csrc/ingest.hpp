@@ -133,6 +133,32 @@ __device__ __forceinline__ void ingest_vector(const IngestArgs& a, int64_t sq, i
       float res[8];
       pool8<T, kRegs>(xt, zt, d, (const T*)(main ? a.bias : a.bias_i) + c0, d, m, slot, xo, zo,
                       res);
+      if (main && (a.kv_gamma != nullptr || a.kv_rope_dim > 0)) {   // uniform
+        // the entry's RMSNorm and RoPE at t: its 64 vectors are this wave's 64 lanes
+        if (a.kv_gamma != nullptr) {
+          float ss = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) ss = fmaf(res[k], res[k], ss);
+#pragma unroll
+          for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+          const float scale = 1.f / sqrtf(ss / float(d) + 1e-6f);
+          float g[8];
+          Elt<T>::load8(static_cast<const T*>(a.kv_gamma) + c0, g);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) res[k] = res[k] * scale * g[k];
+        }
+        const int r0 = d - a.kv_rope_dim;
+        if (a.kv_rope_dim > 0 && c0 >= r0) {
+#pragma unroll
+          for (int k = 0; k < 8; k += 2) {
+            float cs, sn;
+            rope_cos_sin(double(t), (c0 + k - r0) >> 1, a.kv_rope_dim, a.rope_log2_base, cs, sn);
+            const float x0 = res[k], x1 = res[k + 1];
+            res[k] = x0 * cs - x1 * sn;
+            res[k + 1] = x0 * sn + x1 * cs;
+          }
+        }
+      }
       if (main && a.kv_fp8) {   // the pooled entry in T (bf16), then the FP8 entry form
         store_fp8_entry8(static_cast<uint8_t*>(a.kv) + (sq * a.e_cap + e) * kFp8EntryBytes, c0,
                          res, true);

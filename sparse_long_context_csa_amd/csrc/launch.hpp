@@ -32,6 +32,11 @@ struct IngestArgs {
   const void *bias, *bias_i;
   void *kv, *k_idx;
   int kv_fp8;             // kv holds FP8 entries (576 bytes: 448 E4M3 + 64 bf16 channels)
+  // the entry a step completes gets the per-head RMSNorm (kv_gamma [dim], or none when null)
+  // and RoPE at t on its last kv_rope_dim channels before it is stored (dim == 512: the
+  // entry's 64 vectors are the 64 lanes of one wave)
+  const void* kv_gamma;
+  int kv_rope_dim;
   void* k_scale;          // non-null: k_idx holds MXFP4 codes, k_scale their scale bytes
   void* win[4];
   const void* win_new[4];

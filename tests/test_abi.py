@@ -87,9 +87,10 @@ def test_decode_desc_mirrors_the_header_struct():
     # 17 tensor pointers, 5 arrays of CSA_MAX_ATTN pointers, out_idx, the phase events, the
     # scan kernel's start and stop events; idx_format padded to 8 B, k_idx_scale, then
     # score_format, out_rope_dim and rope_base (12 B, padded to 16), the CSA_MAX_ATTN query
-    # gammas, q_rope_dim and kv_format (8 B)
+    # gammas, q_rope_dim and kv_format (8 B), kv_gamma, kv_rope_dim padded to 8 B
     n_ptr = 17 + 5 * _lib.MAX_ATTN + 1 + _lib.DECODE_EVENTS + 2
-    assert C.sizeof(_lib.DecodeDesc) == 64 + 8 + 8 * n_ptr + 8 + 8 + 16 + 8 * _lib.MAX_ATTN + 8
+    assert C.sizeof(_lib.DecodeDesc) == (64 + 8 + 8 * n_ptr + 8 + 8 + 16 + 8 * _lib.MAX_ATTN
+                                         + 8 + 8 + 8)
     for name, val in (("CSA_IDX_DTYPE", _lib.IDX_DTYPE), ("CSA_IDX_MXFP4", _lib.IDX_MXFP4),
                       ("CSA_SCORE_F32", _lib.SCORE_F32), ("CSA_SCORE_BF16", _lib.SCORE_BF16),
                       ("CSA_KV_DTYPE", _lib.KV_DTYPE), ("CSA_KV_FP8", _lib.KV_FP8),
@@ -290,6 +291,11 @@ def test_decode_mxfp4_validation(lib):
     d = full(idx_format=_lib.IDX_DTYPE, kv_format=_lib.KV_FP8)
     d.kv = 256 + 8
     assert step(d) == -2
+    # the new entry's RMSNorm / RoPE: 512-channel entries, even kv_rope_dim <= 64, a base > 1
+    assert step(full(idx_format=_lib.IDX_DTYPE, kv_rope_dim=7)) == -2
+    assert step(full(idx_format=_lib.IDX_DTYPE, kv_rope_dim=64, rope_base=1.0)) == -2
+    assert step(full(idx_format=_lib.IDX_DTYPE, kv_rope_dim=128, rope_base=1e4)) == -4
+    assert step(full(idx_format=_lib.IDX_DTYPE, kv_gamma=256, dim=256)) == -4
 
 
 def test_binding_raises_on_errors(lib):

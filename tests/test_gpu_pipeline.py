@@ -349,3 +349,26 @@ def test_decode_step_fp8_cache(spec, mx):
         if (t + 1) % spec.m == 0:
             keep[(t + 1) // spec.m - 1] = False
         assert torch.equal(st["kv"][b].cpu()[keep], state["kv"][b].cpu()[keep])
+
+
+# The entry a step completes gets its RMSNorm and RoPE at t before it is stored (and attended).
+@pytest.mark.parametrize("spec,fp8", [
+    (datagen.CaseSpec(7160, "decode", B=5, L=24000, m=4, w_cap=256, ragged=True), False),
+    (datagen.CaseSpec(7161, "decode", B=3, L=40000, m=1, w_cap=128, block_size=8,
+                      max_blocks=512, n_attn=3, ragged=True), False),
+    (datagen.CaseSpec(7162, "decode", dtype="f32", B=2, L=6000, m=4, w_cap=128, ragged=True),
+     False),
+    (datagen.CaseSpec(7163, "decode", B=4, L=4 * 30000, m=4, w_cap=128, ragged=True), True),
+], ids=["flat", "hier_three_calls", "f32_separate_ingest", "fp8_cache"])
+def test_decode_step_entry_norm_rope(spec, fp8):
+    case = datagen.make_case(spec)
+    state = fp8_case(case) if fp8 else {}
+    case["kv_gamma"] = (datagen.tensor(spec.case_id, 95, (spec.D,), spec.dtype, 0.3) + 1.0).to(
+        case["x_new"].dtype)
+    case["kv_rope_dim"] = 64
+    # the completing sequences: the entry is attended in the step only when it is selected
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    assert ref["kv_new"], "no sequence completes a block"
+    _, st, rings, out, idx = run_step(case, state or None)
+    check_step(case, ref, st, rings, out, idx)

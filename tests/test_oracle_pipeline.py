@@ -273,3 +273,24 @@ def test_fp8_cache_attends_the_new_entry_at_its_fp8_value():
             np.testing.assert_array_equal(res["out"][b][c], want["out"][b][c])
             differs |= not np.array_equal(res["out"][b][c], plain["out"][b][c])
     assert differs
+
+
+def test_new_entry_norm_and_rope():
+    # RMSNorm with a unit gamma gives the stored entry a unit mean square (up to its bf16
+    # rounding); RoPE alone keeps the first channels and the entry's L2 norm, and turns the
+    # last 64 pairwise; every other entry and the ids' inputs are unchanged
+    case = small_decode(case_id=907, m=1, L=40, D=512, H=2, ragged=False)
+    spec = case["spec"]
+    plain = pipeline.decode_step(case)
+    normed = pipeline.decode_step(dict(case, kv_gamma=torch.ones(512, dtype=case["kv"].dtype)))
+    roped = pipeline.decode_step(dict(case, kv_rope_dim=64))
+    for b in range(spec.B):
+        e = normed["kv_new"][b]
+        assert abs(np.mean(e ** 2) - 1.0) < 1e-2
+        assert not np.allclose(e, plain["kv_new"][b])
+        r, p = roped["kv_new_exact"][b], plain["kv_new"][b]
+        np.testing.assert_array_equal(r[:448], p[:448])
+        assert not np.allclose(r[448:], p[448:])
+        np.testing.assert_allclose(np.hypot(r[448::2], r[449::2]),
+                                   np.hypot(p[448::2], p[449::2]), rtol=1e-12)
+        np.testing.assert_array_equal(roped["ids"][b], plain["ids"][b])
