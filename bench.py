@@ -372,8 +372,9 @@ def main():
                          "line then also reports the recall of the fp32 selection)")
     ap.add_argument("--rope-dim", type=int, default=0,
                     help="decode workloads: each query's per-head RMSNorm and RoPE on its last N "
-                         "channels (prepared in the selection launch), and the inverse RoPE on "
-                         "the output fused into the attention's store (0: off)")
+                         "channels (prepared in the selection launch), the completed entry's "
+                         "RMSNorm and RoPE before it is stored, and the inverse RoPE on the "
+                         "output fused into the attention's store (0: off)")
     ap.add_argument("--kv-format", default="bf16", choices=("bf16", "fp8"),
                     help="main KV cache of the decode workloads (--config 2/4/5/6): bf16 "
                          "entries, or 576-byte FP8 entries (csa_quantize_kv_fp8 of the same "
@@ -425,9 +426,11 @@ def main():
         kv8 = csa.quantize_kv_fp8(case["kv"].to(dev))
         torch.cuda.synchronize()
     q_gammas = None
+    kv_gamma = None
     if args.rope_dim:
         q_gammas = [(datagen.tensor(spec.case_id, 90 + c, (spec.D,), spec.dtype, 0.3) + 1.0).to(dev)
                     for c in range(spec.n_attn)]
+        kv_gamma = (datagen.tensor(spec.case_id, 95, (spec.D,), spec.dtype, 0.3) + 1.0).to(dev)
     steps_objs, states = [], []
     for c in range(args.copies):
         st = {k: case[k].to(dev) for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
@@ -443,7 +446,7 @@ def main():
         steps_objs.append(csa.DecodeStep(
             m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
             score_format=args.score_format, out_rope_dim=args.rope_dim, q_rope_dim=args.rope_dim,
-            q_gamma=q_gammas, **states[-1]))
+            q_gamma=q_gammas, kv_gamma=kv_gamma, kv_rope_dim=args.rope_dim, **states[-1]))
     torch.cuda.synchronize()
     log(f"device state ready: {args.copies} copies, "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
@@ -578,8 +581,8 @@ def main():
         res["metric"] += ", FP8 main cache"
         res["config"]["kv_cache"] = "fp8 (448 E4M3 + 64 bf16 channels, 576 B per entry)"
     if args.rope_dim:
-        res["metric"] += (f", query RMSNorm + RoPE and output inverse RoPE on the last "
-                          f"{args.rope_dim} channels")
+        res["metric"] += (f", query and entry RMSNorm + RoPE and output inverse RoPE on the "
+                          f"last {args.rope_dim} channels")
         res["config"]["rope_dim"] = args.rope_dim
     if args.score_format == "bf16":
         # recall of the fp32 selection: the same step (idempotent: it rewrites the same tail

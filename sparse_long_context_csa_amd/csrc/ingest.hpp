@@ -148,14 +148,22 @@ __device__ __forceinline__ void ingest_vector(const IngestArgs& a, int64_t sq, i
           for (int k = 0; k < 8; ++k) res[k] = res[k] * scale * g[k];
         }
         const int r0 = d - a.kv_rope_dim;
-        if (a.kv_rope_dim > 0 && c0 >= r0) {
+        if (a.kv_rope_dim > 0) {   // uniform
+          // lane j forms the angle of pair j once; the lanes holding the rotated channels fetch
+          // theirs by shuffles
+          const int lane = threadIdx.x & 63;
+          float cs_l = 1.f, sn_l = 0.f;
+          if (lane < a.kv_rope_dim / 2)
+            rope_cos_sin(double(t), lane, a.kv_rope_dim, a.rope_log2_base, cs_l, sn_l);
 #pragma unroll
           for (int k = 0; k < 8; k += 2) {
-            float cs, sn;
-            rope_cos_sin(double(t), (c0 + k - r0) >> 1, a.kv_rope_dim, a.rope_log2_base, cs, sn);
-            const float x0 = res[k], x1 = res[k + 1];
-            res[k] = x0 * cs - x1 * sn;
-            res[k + 1] = x0 * sn + x1 * cs;
+            const int j = (c0 + k - r0) >> 1;
+            const float cs = __shfl(cs_l, j & 63), sn = __shfl(sn_l, j & 63);
+            if (c0 + k >= r0) {
+              const float x0 = res[k], x1 = res[k + 1];
+              res[k] = x0 * cs - x1 * sn;
+              res[k + 1] = x0 * sn + x1 * cs;
+            }
           }
         }
       }
