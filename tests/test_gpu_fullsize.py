@@ -7,7 +7,7 @@ import torch
 
 import datagen
 import sparse_long_context_csa_amd as csa
-from gpu_helpers import (assert_ids, assert_pooled, assert_rows_close, check_step, dev,
+from gpu_helpers import (assert_ids, assert_pooled, assert_rows_close, check_step, dev, fp8_case,
                          mxfp4_case, pooled_xmax, run_step)
 from oracle import csa as ocsa
 from oracle import gaps, pipeline
@@ -34,6 +34,27 @@ def test_decode_workload_fullsize_mxfp4_keys(cfg):
     print(f"config {cfg} (MXFP4 keys): inputs ready", flush=True)
     gaps.enforce_decode(case)
     _, st, rings, out, idx = run_step(case, idx_state)
+    ref = pipeline.decode_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
+def test_decode_workload_fullsize_every_format_and_fusion():
+    """The 8 x 65,536-token decode workload with every production format and fusion at once:
+    FP8 main cache, MXFP4 indexer keys, BF16 index scores, the queries' and the completed
+    entry's RMSNorm + RoPE and the inverse RoPE on the output (the GPU quantises the caches;
+    the oracle holds their FP8 / MXFP4 values from its own encoders)."""
+    spec = datagen.CONFIGS[2]
+    case, state = mxfp4_case(spec)
+    state.update(fp8_case(case))
+    case["score_format"] = "bf16"
+    case["q_rope_dim"] = case["out_rope_dim"] = case["kv_rope_dim"] = 64
+    case["q_gamma"] = [(datagen.tensor(spec.case_id, 90, (spec.D,), spec.dtype, 0.3) + 1.0).to(
+        case["x_new"].dtype)]
+    case["kv_gamma"] = (datagen.tensor(spec.case_id, 95, (spec.D,), spec.dtype, 0.3) + 1.0).to(
+        case["x_new"].dtype)
+    print("config 2 (all formats and fusions): inputs ready", flush=True)
+    gaps.enforce_decode(case)
+    _, st, rings, out, idx = run_step(case, state)
     ref = pipeline.decode_step(case)
     check_step(case, ref, st, rings, out, idx)
 
