@@ -294,6 +294,8 @@ def make_prefill(spec: CaseSpec) -> dict:
     """
     B, m, D, dI, E, C = spec.B, spec.m, spec.D, spec.d_I, spec.entries, spec.chunk
     assert spec.kind in ("prefill", "tiny") and C % m == 0 and spec.L % m == 0
+    # the ring holds positions [L-C-W+1, L) at row p % w_cap: they must not wrap onto each other
+    assert spec.w_cap >= C + spec.W - 1, "ring capacity below chunk + window - 1"
     dt = spec.dtype
     L = spec.L
     t0 = L - C

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 10
+#define CSA_ABI_VERSION 11
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -280,7 +280,8 @@ int csa_sparse_attn_fp8(const void *q, const void *kv, const int32_t *idx, int32
  * Per sequence s at position t = pos[s] (slot = t % m):
  *   1. x_new, z_new, xi_new, zi_new enter the compressor tails at row `slot`; for every
  *      attention call c with win_new[c] != NULL, win_new[c][s] enters win[c] at row
- *      t % w_cap.
+ *      t % w_cap (with kv_gamma / kv_rope_dim, RMSNorm'd and rotated at t first, like an
+ *      entry: see kv_gamma below).
  *   2. If (t+1) % m == 0 the block is complete: entry e = (t+1)/m - 1 (< e_cap, else not
  *      stored) of kv <- pool(x_tail, z_tail, bias) and of k_idx <- pool(xi_tail, zi_tail,
  *      bias_i), as csa_compress with n_tok = m.
@@ -392,14 +393,18 @@ typedef struct csa_decode_desc {
    *   [CoD "What the cache costs, checked four ways": 448 FP8 + 64 bf16 rotary dims =
    *   576 bytes per entry.] */
   int32_t kv_format;
-  /* The entry a step completes: kv_gamma (T [dim]) or NULL applies the per-head RMSNorm (eps
-   * 1e-6) to the pooled entry; kv_rope_dim > 0 then turns its last kv_rope_dim channels by
+  /* The key/value rows a step stores: kv_gamma (T [dim]) or NULL applies the per-head RMSNorm
+   * (eps 1e-6) to the pooled entry; kv_rope_dim > 0 then turns its last kv_rope_dim channels by
    * RoPE at t (base rope_base), t being the position of the newest token the entry pools; the
-   * result is rounded once to T (and then stored in kv_format). Needs dim 512; kv_rope_dim
-   * even and at most 64 (else CSA_ERR_UNSUPPORTED / CSA_ERR_SHAPE).
-   *   [CoD "Key and value are the same vector": RMSNorm per head on the compressed KV
-   *   entries; RoPE on the last 64 dimensions, the cached entry carrying its position's
-   *   rotation.] */
+   * result is rounded once to T (and then stored in kv_format). Every new window row
+   * (win_new[c]) gets the same RMSNorm and RoPE at its position t before it enters its ring, so
+   * that every row the attention reads carries its own position's rotation and the inverse
+   * RoPE of the output leaves only distances. Needs dim 512; kv_rope_dim even and at most 64
+   * (else CSA_ERR_UNSUPPORTED / CSA_ERR_SHAPE).
+   *   [CoD "Key and value are the same vector": RMSNorm per head on the KV entries; RoPE on
+   *   the last 64 dimensions, a cached row carrying its position's rotation; CoD "Two cache
+   *   hierarchies, and lcm(4, 128)": vLLM fuses KV RoPE with the sliding-window key
+   *   insertion.] */
   const void *kv_gamma;
   int32_t kv_rope_dim;
 } csa_decode_desc;

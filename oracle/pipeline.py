@@ -127,6 +127,32 @@ def cached_index_key(case: dict, key) -> np.ndarray:
     return key
 
 
+def prepare_kv_row(case: dict, v, t: int) -> np.ndarray:
+    """A key/value row of the shared-KV attention as the step stores it, unrounded: the
+    per-head RMSNorm with case["kv_gamma"] (when given), then RoPE at position t on the last
+    case["kv_rope_dim"] channels (when > 0).
+
+    [CoD "Key and value are the same vector": RMSNorm per head on the single KV head just
+    before the core attention; RoPE on the last 64 dimensions, so a cached row carries the
+    rotation of its position and the inverse rotation of the output at -t leaves each row's
+    contribution a function of its distance from the query.] [CoD, vLLM's serving notes
+    in "Two cache hierarchies, and lcm(4, 128)": KV RoPE is fused with the sliding-window key
+    insertion.] Reading: a window row is a key/value row of the same attention as a pooled
+    entry, so it is prepared the same way, at its own position; t is the newest token the
+    row holds (the pooled entry's last position, the window row's own position)."""
+    v = f64(v)
+    if case.get("kv_gamma") is not None:
+        v = csa.rms_norm(v[None], f64(case["kv_gamma"]), 1e-6)[0]
+    if case.get("kv_rope_dim"):
+        v = csa.rope(v[None], float(t), int(case["kv_rope_dim"]))[0]
+    return v
+
+
+def kv_row_prepared(case: dict) -> bool:
+    """Whether the step normalises or rotates the key/value rows it stores."""
+    return case.get("kv_gamma") is not None or bool(case.get("kv_rope_dim"))
+
+
 def decode_step(case: dict, seqs=None) -> dict:
     """The fused decode step for one new token per sequence (oracle side).
 
@@ -145,7 +171,8 @@ def decode_step(case: dict, seqs=None) -> dict:
     case["kv_format"] == "fp8", case["kv"] holds the values of an FP8 main cache (576-byte
     entries, oracle/fp8.py) and the new entry is attended at its cached value. case["kv_gamma"]
     and case["kv_rope_dim"] give the new entry its per-head RMSNorm and RoPE (at t, the position
-    of the newest token it pools) before it is stored (rounded once).
+    of the newest token it pools) before it is stored (rounded once), and the new window row
+    the same at its position t (``prepare_kv_row``).
     Returns a dict with per-sequence results (new entries, scores, pool, ids, outputs).
     """
     spec = case["spec"]
@@ -154,7 +181,7 @@ def decode_step(case: dict, seqs=None) -> dict:
     seqs = list(range(spec.B)) if seqs is None else list(seqs)
     ring_raw = spec.m > 1
     res = {"ids": {}, "out": {}, "kv_new": {}, "kv_new_exact": {}, "ki_new": {}, "scores": {},
-           "pool": {},
+           "pool": {}, "win_row": {}, "win_row_exact": {},
            "scores2": {}, "n_vis": {}}
     bias, bias_i = f64(case["bias"]), f64(case["bias_i"])
     for b in seqs:
@@ -173,14 +200,9 @@ def decode_step(case: dict, seqs=None) -> dict:
         new_e = None
         if (t + 1) % m == 0:
             new_e = (t + 1) // m - 1
-            kv_p = csa.compress(x_tail, z_tail, bias, m)[0]
-            if case.get("kv_gamma") is not None:
-                # the new entry's single head: RMSNorm ([CoD] "Key and value are the same
-                # vector": RMSNorm per head on the compressed KV entries)
-                kv_p = csa.rms_norm(kv_p[None], f64(case["kv_gamma"]), 1e-6)[0]
-            if case.get("kv_rope_dim"):
-                # RoPE on its last channels at the position of the newest token it pools (t)
-                kv_p = csa.rope(kv_p[None], float(t), int(case["kv_rope_dim"]))[0]
+            # the new entry's single head: RMSNorm, then RoPE at the position of the newest
+            # token it pools (t)
+            kv_p = prepare_kv_row(case, csa.compress(x_tail, z_tail, bias, m)[0], t)
             kv_e = csa.store(kv_p, dt)
             res["kv_new_exact"][b] = kv_p
             ki_e = csa.store(csa.compress(xi_tail, zi_tail, bias_i, m)[0], dt)
@@ -213,7 +235,13 @@ def decode_step(case: dict, seqs=None) -> dict:
         for c in range(spec.n_attn):
             ring = f64(case["rings"][c][b]).copy()
             if c == 0 and ring_raw:
-                ring[t % wc] = f64(case["x_new"][b])
+                # the new raw row enters the window prepared like an entry, at its position t
+                xw = f64(case["x_new"][b])
+                if kv_row_prepared(case):
+                    res["win_row_exact"][b] = prepare_kv_row(case, xw, t)
+                    xw = csa.store(res["win_row_exact"][b], dt)
+                ring[t % wc] = xw
+                res["win_row"][b] = xw
             q = case["q"][c][b]
             qg = (case.get("q_gamma") or [None] * spec.n_attn)[c]
             qr = int(case.get("q_rope_dim", 0))

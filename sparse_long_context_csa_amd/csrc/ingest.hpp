@@ -98,93 +98,110 @@ __device__ __forceinline__ void pool8(const T* x0, const T* z0, int64_t stride, 
   for (int c = 0; c < 8; ++c) out[c] = acc[c] / sum[c];
 }
 
-// Vectors of 8 channels one sequence's ingest covers: main stream, indexer stream, rings.
+// Vectors of 8 channels one sequence's ingest covers: main stream, rings, indexer stream.
 __device__ __forceinline__ int ingest_vectors(const IngestArgs& a) {
-  return (a.dim >> 3) + (a.idx_dim >> 3) + a.n_ring * (a.dim >> 3);
+  return (a.dim >> 3) + a.n_ring * (a.dim >> 3) + (a.idx_dim >> 3);
 }
 
-// Vector v of sequence sq: [0, vd) main stream (tail row, pooled entry when complete),
-// [vd, vd+vi) indexer stream (tail row; pooled key when complete and pool_index), then
-// n_ring * vd window-ring vectors (row t % w_cap of ring c from win_new[c], when given).
+// The per-head RMSNorm (kv_gamma, eps 1e-6) and RoPE at position p on the last kv_rope_dim
+// channels of a key/value row, 8 channels c0 .. c0 + 7 per lane; the row's 64 vectors are the
+// 64 lanes of this wave (dim 512), which all call this together.
+//   ["DeepSeek V4-Flash: The Cost of Deciding What to Read", "Key and value are the same
+//   vector": RMSNorm per head on the KV head, RoPE on the last 64 dimensions, so that every
+//   key/value row carries its position's rotation; vLLM fuses KV RoPE with the window-key
+//   insertion ("Two cache hierarchies, and lcm(4, 128)").]
+template <typename T>
+__device__ __forceinline__ void prep_kv_row8(const IngestArgs& a, int64_t p, int c0, int d,
+                                             float* res) {
+  if (a.kv_gamma != nullptr) {
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ss = fmaf(res[k], res[k], ss);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    const float scale = 1.f / sqrtf(ss / float(d) + 1e-6f);
+    float g[8];
+    Elt<T>::load8(static_cast<const T*>(a.kv_gamma) + c0, g);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) res[k] = res[k] * scale * g[k];
+  }
+  const int r0 = d - a.kv_rope_dim;
+  if (a.kv_rope_dim > 0) {   // uniform
+    // lane j forms the angle of pair j once; the lanes holding the rotated channels fetch
+    // theirs by shuffles
+    const int lane = threadIdx.x & 63;
+    float cs_l = 1.f, sn_l = 0.f;
+    if (lane < a.kv_rope_dim / 2)
+      rope_cos_sin(double(p), lane, a.kv_rope_dim, a.rope_log2_base, cs_l, sn_l);
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      const int j = (c0 + k - r0) >> 1;
+      const float cs = __shfl(cs_l, j & 63), sn = __shfl(sn_l, j & 63);
+      if (c0 + k >= r0) {
+        const float x0 = res[k], x1 = res[k + 1];
+        res[k] = x0 * cs - x1 * sn;
+        res[k + 1] = x0 * sn + x1 * cs;
+      }
+    }
+  }
+}
+
+// Vector v of sequence sq: [0, vd) main stream (tail row, pooled entry when complete), then
+// n_ring * vd window-ring vectors (row t % w_cap of ring c from win_new[c], when given), then
+// [vd + n_ring * vd, + vi) the indexer stream (tail row; pooled key when complete and
+// pool_index). With dim 512 (vd = 64) the main row and every ring row are one wave each.
+// The pooled entry and every new window row get the RMSNorm and RoPE at t of prep_kv_row8
+// when kv_gamma or kv_rope_dim asks for them (dim 512 then).
 template <typename T, bool kRegs = true>
 __device__ __forceinline__ void ingest_vector(const IngestArgs& a, int64_t sq, int v,
                                               bool pool_index) {
-  const int vd = a.dim >> 3, vi = a.idx_dim >> 3;
+  const int vd = a.dim >> 3, vr = a.n_ring * vd;
   const int64_t t = a.pos[sq];
   if (t < 0) return;
   const int m = a.m;
   const int slot = int(t % m);
   const bool complete = ((t + 1) % m) == 0;
   const int64_t e = (t + 1) / m - 1;
-  if (v < vd + vi) {
-    const bool main = v < vd;
-    const int d = main ? a.dim : a.idx_dim;
-    const int c0 = (main ? v : v - vd) << 3;
-    const T* xn = (const T*)(main ? a.x_new : a.xi_new) + sq * d + c0;
-    const T* zn = (const T*)(main ? a.z_new : a.zi_new) + sq * d + c0;
-    T* xt = (T*)(main ? a.x_tail : a.xi_tail) + sq * m * d + c0;
-    T* zt = (T*)(main ? a.z_tail : a.zi_tail) + sq * m * d + c0;
-    float xo[8], zo[8];
-    Elt<T>::load8(xn, xo);
-    Elt<T>::load8(zn, zo);
-    Elt<T>::store8(xt + slot * d, xo);
-    Elt<T>::store8(zt + slot * d, zo);
-    if (complete && e < a.e_cap && (main || pool_index)) {
-      float res[8];
-      pool8<T, kRegs>(xt, zt, d, (const T*)(main ? a.bias : a.bias_i) + c0, d, m, slot, xo, zo,
-                      res);
-      if (main && (a.kv_gamma != nullptr || a.kv_rope_dim > 0)) {   // uniform
-        // the entry's RMSNorm and RoPE at t: its 64 vectors are this wave's 64 lanes
-        if (a.kv_gamma != nullptr) {
-          float ss = 0.f;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) ss = fmaf(res[k], res[k], ss);
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-          const float scale = 1.f / sqrtf(ss / float(d) + 1e-6f);
-          float g[8];
-          Elt<T>::load8(static_cast<const T*>(a.kv_gamma) + c0, g);
-#pragma unroll
-          for (int k = 0; k < 8; ++k) res[k] = res[k] * scale * g[k];
-        }
-        const int r0 = d - a.kv_rope_dim;
-        if (a.kv_rope_dim > 0) {   // uniform
-          // lane j forms the angle of pair j once; the lanes holding the rotated channels fetch
-          // theirs by shuffles
-          const int lane = threadIdx.x & 63;
-          float cs_l = 1.f, sn_l = 0.f;
-          if (lane < a.kv_rope_dim / 2)
-            rope_cos_sin(double(t), lane, a.kv_rope_dim, a.rope_log2_base, cs_l, sn_l);
-#pragma unroll
-          for (int k = 0; k < 8; k += 2) {
-            const int j = (c0 + k - r0) >> 1;
-            const float cs = __shfl(cs_l, j & 63), sn = __shfl(sn_l, j & 63);
-            if (c0 + k >= r0) {
-              const float x0 = res[k], x1 = res[k + 1];
-              res[k] = x0 * cs - x1 * sn;
-              res[k + 1] = x0 * sn + x1 * cs;
-            }
-          }
-        }
-      }
-      if (main && a.kv_fp8) {   // the pooled entry in T (bf16), then the FP8 entry form
-        store_fp8_entry8(static_cast<uint8_t*>(a.kv) + (sq * a.e_cap + e) * kFp8EntryBytes, c0,
-                         res, true);
-      } else {
-        T* dst = (T*)(main ? a.kv : a.k_idx) + (sq * a.e_cap + e) * d + c0;
-        Elt<T>::store8(dst, res);
-      }
-    }
+  const bool prep = a.kv_gamma != nullptr || a.kv_rope_dim > 0;
+  if (v >= vd && v < vd + vr) {
+    const int r = v - vd;
+    const int c = r / vd;
+    const int c0 = (r % vd) << 3;
+    const T* src = (const T*)a.win_new[c];
+    if (src == nullptr) return;   // uniform over the ring row's wave
+    float w8[8];
+    Elt<T>::load8(src + sq * a.dim + c0, w8);
+    if (prep) prep_kv_row8<T>(a, t, c0, a.dim, w8);
+    Elt<T>::store8((T*)a.win[c] + (sq * a.w_cap + t % a.w_cap) * a.dim + c0, w8);
     return;
   }
-  const int r = v - vd - vi;
-  const int c = r / vd;
-  const int c0 = (r % vd) << 3;
-  const T* src = (const T*)a.win_new[c];
-  if (src == nullptr) return;
-  float w8[8];
-  Elt<T>::load8(src + sq * a.dim + c0, w8);
-  Elt<T>::store8((T*)a.win[c] + (sq * a.w_cap + t % a.w_cap) * a.dim + c0, w8);
+  const bool main = v < vd;
+  const int d = main ? a.dim : a.idx_dim;
+  const int c0 = (main ? v : v - vd - vr) << 3;
+  const T* xn = (const T*)(main ? a.x_new : a.xi_new) + sq * d + c0;
+  const T* zn = (const T*)(main ? a.z_new : a.zi_new) + sq * d + c0;
+  T* xt = (T*)(main ? a.x_tail : a.xi_tail) + sq * m * d + c0;
+  T* zt = (T*)(main ? a.z_tail : a.zi_tail) + sq * m * d + c0;
+  float xo[8], zo[8];
+  Elt<T>::load8(xn, xo);
+  Elt<T>::load8(zn, zo);
+  Elt<T>::store8(xt + slot * d, xo);
+  Elt<T>::store8(zt + slot * d, zo);
+  if (complete && e < a.e_cap && (main || pool_index)) {
+    float res[8];
+    pool8<T, kRegs>(xt, zt, d, (const T*)(main ? a.bias : a.bias_i) + c0, d, m, slot, xo, zo,
+                    res);
+    // the entry's RMSNorm and RoPE at t (the newest position it pools): its 64 vectors are
+    // this wave's 64 lanes
+    if (main && prep) prep_kv_row8<T>(a, t, c0, d, res);
+    if (main && a.kv_fp8) {   // the pooled entry in T (bf16), then the FP8 entry form
+      store_fp8_entry8(static_cast<uint8_t*>(a.kv) + (sq * a.e_cap + e) * kFp8EntryBytes, c0,
+                       res, true);
+    } else {
+      T* dst = (T*)(main ? a.kv : a.k_idx) + (sq * a.e_cap + e) * d + c0;
+      Elt<T>::store8(dst, res);
+    }
+  }
 }
 
 // Query preparation of sequence sq for every attention call (IngestArgs::n_qprep), share `part`

@@ -250,6 +250,13 @@ def check_step(case, ref, st, rings, out, idx):
                 assert_pooled(f64(st[name][b, e].cpu()), exact, xmax,
                               f"{name} entry {e} of seq {b}")
         if datagen.ring_from_raw(spec):
-            assert torch.equal(rings[0][b, t % spec.w_cap].cpu(), case["x_new"][b])
+            got = rings[0][b, t % spec.w_cap].cpu()
+            if b in ref.get("win_row_exact", {}):
+                # the new window row, normalised and rotated at t like an entry
+                exact = ref["win_row_exact"][b]
+                assert_pooled(f64(got), exact, np.full(exact.shape, 4.0 * np.abs(exact).max()),
+                              f"window row {t} of seq {b}")
+            else:
+                assert torch.equal(got, case["x_new"][b])
 
 

@@ -173,7 +173,7 @@ def test_gap_ok_rule():
 
 def test_prefill_rows_and_gaps():
     spec = datagen.CaseSpec(907, "prefill", B=1, L=512, m=4, H_I=8, d_I=16, H=4, D=32, K=16,
-                            W=8, w_cap=64, chunk=64)
+                            W=8, w_cap=128, chunk=64)
     case = datagen.make_case(spec)
     rows = [(0, 0), (0, 17), (0, 63)]
     gaps.enforce_prefill(case, rows)
