@@ -18,10 +18,12 @@
  *     default stream). Arguments are validated on the host before anything is launched:
  *     a call that returns an error launched nothing. CSA_ERR_HIP reports a failed launch.
  *     Outputs are valid once the stream has reached the call.
- *   - The library never allocates, frees or retains device memory. Scratch space is the
- *     caller's workspace `ws` of at least the bytes the matching *_workspace_size call
- *     returns (256-byte aligned). A workspace must not be shared by calls that may run
- *     concurrently. No mutable global state: calls are thread-safe.
+ *   - The library never allocates or frees device memory. Scratch space is the caller's
+ *     workspace `ws` of at least the bytes the matching *_workspace_size call returns
+ *     (256-byte aligned). A workspace must not be shared by calls that may run concurrently.
+ *     Calls are thread-safe. The one exception is csa_decode_step_noalloc: its workspace is a
+ *     static device array per GPU, kept until the process ends and shared by every call of it
+ *     on that GPU.
  *   - Values that live on the device (positions, entry counts, ids) cannot be checked on
  *     the host; kernels clamp them so that no access leaves the documented buffers:
  *     visible counts are capped at the cache capacity, out-of-range ids are skipped.
@@ -36,7 +38,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 11
+#define CSA_ABI_VERSION 12
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -411,6 +413,26 @@ typedef struct csa_decode_desc {
 
 size_t csa_decode_step_workspace_size(const csa_decode_desc *d);
 int csa_decode_step(const csa_decode_desc *d, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_decode_step_noalloc -- csa_decode_step with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.
+ * The workspace is a static device array of CSA_NOALLOC_SCRATCH_BYTES (32 MiB) inside the
+ * library; every GPU the library runs on holds its own copy until the process ends. The call
+ * runs the same kernels as csa_decode_step over it and never allocates or frees memory. The
+ * GPU is the device of `stream` (the calling thread's current device for a NULL stream); the
+ * array's device address is looked up once per device, on the first call there.
+ * Errors: those of csa_decode_step; CSA_ERR_WORKSPACE when csa_decode_step_workspace_size(d)
+ * exceeds CSA_NOALLOC_SCRATCH_BYTES (the 1M-context batch of 4 needs about 11 MiB, a batch of
+ * 8 about 22 MiB); CSA_ERR_HIP when the array's address cannot be found.
+ * Every call on one GPU shares that GPU's array, and the array keeps the last call's contents
+ * (no kernel of the step needs it cleared): calls that may overlap on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. The descriptor's buffers are the
+ * caller's as for csa_decode_step.
+ * ------------------------------------------------------------------------------------- */
+#define CSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int csa_decode_step_noalloc(const csa_decode_desc *d, void *stream);
 
 #ifdef __cplusplus
 }

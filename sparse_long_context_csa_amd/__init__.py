@@ -240,12 +240,15 @@ class DecodeStep:
     RoPE at +pos) in the selection launch. A uint8 kv [n_seq, e_cap, 576] is an FP8 main
     cache (quantize_kv_fp8's entries; kv_format CSA_KV_FP8). kv_gamma ([dim] or None) and
     kv_rope_dim give the entry a step completes its RMSNorm and RoPE at pos before it is
-    stored."""
+    stored. With no_alloc=True no workspace is allocated and each call runs
+    csa_decode_step_noalloc over the library's static per-GPU scratch array (calls that may
+    overlap on one GPU race there)."""
 
     def __init__(self, *, m: int, top_k: int, window: int, scale: float, block_size: int = 0,
                  max_blocks: int = 0, out=None, out_idx=None, score_format: str = "f32",
                  out_rope_dim: int = 0, rope_base: float = 10000.0, q_gamma=None,
-                 q_rope_dim: int = 0, kv_gamma=None, kv_rope_dim: int = 0, **t):
+                 q_rope_dim: int = 0, kv_gamma=None, kv_rope_dim: int = 0,
+                 no_alloc: bool = False, **t):
         self.t = t
         kv = _dev(t["kv"], "kv")
         kv8 = kv.dtype == torch.uint8
@@ -321,7 +324,11 @@ class DecodeStep:
         nb = lib().csa_decode_step_workspace_size(C.byref(d))
         if nb == 0:
             check("csa_decode_step_workspace_size", lib().csa_decode_step(C.byref(d), None, 0, None))
-        self.ws = _workspace(nb, kv.device)
+        self.no_alloc = no_alloc
+        if no_alloc and nb > _lib.NOALLOC_SCRATCH_BYTES:
+            raise ValueError(f"the step needs {nb} bytes of workspace, more than the "
+                             f"{_lib.NOALLOC_SCRATCH_BYTES} of the static scratch")
+        self.ws = None if no_alloc else _workspace(nb, kv.device)
 
     def set_events(self, handles) -> None:
         """Phase-boundary hipEvent_t handles (ints or None) recorded by the step."""
@@ -337,7 +344,10 @@ class DecodeStep:
         self.desc.scan_events[1] = stop
 
     def __call__(self, stream: int | None = None):
-        check("csa_decode_step", lib().csa_decode_step(
-            C.byref(self.desc), self.ws.data_ptr(), self.ws.numel(),
-            _stream() if stream is None else stream))
+        s = _stream() if stream is None else stream
+        if self.no_alloc:
+            check("csa_decode_step_noalloc", lib().csa_decode_step_noalloc(C.byref(self.desc), s))
+        else:
+            check("csa_decode_step", lib().csa_decode_step(
+                C.byref(self.desc), self.ws.data_ptr(), self.ws.numel(), s))
         return self.out, self.out_idx

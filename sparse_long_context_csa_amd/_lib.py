@@ -16,6 +16,7 @@ IDX_DTYPE, IDX_MXFP4 = 0, 1
 SCORE_F32, SCORE_BF16 = 0, 1
 KV_DTYPE, KV_FP8 = 0, 1
 KV_FP8_BYTES = 576
+NOALLOC_SCRATCH_BYTES = 32 << 20
 NR_NORM, NR_ROPE, NR_INVERSE = 1, 2, 4
 
 vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
@@ -63,6 +64,7 @@ SIGNATURES = {
                                   i64, i32, i32, vp, sz, i32, vp]),
     "csa_decode_step_workspace_size": (sz, [C.POINTER(DecodeDesc)]),
     "csa_decode_step": (i32, [C.POINTER(DecodeDesc), vp, sz, vp]),
+    "csa_decode_step_noalloc": (i32, [C.POINTER(DecodeDesc), vp]),
 }
 
 _lib = None

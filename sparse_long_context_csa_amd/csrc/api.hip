@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "csa.h"
 #include "launch.hpp"
 
@@ -525,12 +527,10 @@ size_t csa_decode_step_workspace_size(const csa_decode_desc* d) {
   return c.off;
 }
 
-int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* stream) {
-  int st = check_decode(d);
-  if (st != CSA_OK) return st;
-  if (d->n_seq == 0) return CSA_OK;
-  const size_t need = csa_decode_step_workspace_size(d);
-  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+namespace {
+// The decode step over a validated descriptor and a workspace of at least the bytes
+// csa_decode_step_workspace_size gives (no kernel needs it cleared).
+int decode_step_run(const csa_decode_desc* d, void* ws, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carver c(ws);
   const DecodeWs w = carve_decode(c, d);
@@ -636,5 +636,67 @@ int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* s
   mark(4);
   return CSA_OK;
 }
+}  // namespace
+
+int csa_decode_step(const csa_decode_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_decode(d);
+  if (st != CSA_OK) return st;
+  if (d->n_seq == 0) return CSA_OK;
+  const size_t need = csa_decode_step_workspace_size(d);
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  return decode_step_run(d, ws, stream);
+}
 
 }  // extern "C"
+
+// ---- the allocation-free decode step ---------------------------------------------------
+// The workspace lives in a file-scope device array. In host code `scratch` names a host-side
+// stand-in, not the device memory: its device address on each GPU comes from
+// hipGetSymbolAddress (every GPU the library runs on holds its own copy, at its own address,
+// until the process ends) and only that address is ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];   // per device: &scratch on that device, once found
+
+// The device address of `scratch` on device `dev`, looked up once per device with that device
+// current (the calling thread's current device is restored afterwards).
+int scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return CSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return CSA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return CSA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return CSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" int csa_decode_step_noalloc(const csa_decode_desc* d, void* stream) {
+  int st = check_decode(d);
+  if (st != CSA_OK) return st;
+  if (d->n_seq == 0) return CSA_OK;
+  if (csa_decode_step_workspace_size(d) > CSA_NOALLOC_SCRATCH_BYTES) return CSA_ERR_WORKSPACE;
+  int dev = -1;
+  if (stream != nullptr) {
+    hipDevice_t sd = 0;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sd) != hipSuccess)
+      return CSA_ERR_HIP;
+    dev = static_cast<int>(sd);
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return CSA_ERR_HIP;
+  }
+  void* ws = nullptr;
+  st = scratch_address(dev, &ws);
+  if (st != CSA_OK) return st;
+  return decode_step_run(d, ws, stream);
+}

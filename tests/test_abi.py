@@ -39,7 +39,8 @@ def test_header_declares_the_calls():
         "csa_index_topk", "csa_index_blocks_workspace_size", "csa_index_blocks",
         "csa_sparse_attn_workspace_size", "csa_sparse_attn", "csa_decode_step_workspace_size",
         "csa_decode_step", "csa_quantize_mxfp4", "csa_compress_c4a", "csa_norm_rope",
-        "csa_quantize_kv_fp8", "csa_dequantize_kv_fp8", "csa_sparse_attn_fp8"}
+        "csa_quantize_kv_fp8", "csa_dequantize_kv_fp8", "csa_sparse_attn_fp8",
+        "csa_decode_step_noalloc"}
 
 
 def test_binding_covers_every_declared_function():
@@ -234,6 +235,28 @@ def test_decode_validation(lib):
     full.scan_events[0] = 16
     assert lib.csa_decode_step(C.byref(full), C.c_void_p(16), nb, None) == -1
     full.scan_events[0] = 0
+
+
+def test_decode_noalloc_validation(lib):
+    # the allocation-free step validates like csa_decode_step, and refuses a step whose
+    # workspace exceeds the static scratch before touching the GPU
+    assert lib.csa_decode_step_noalloc(None, None) == -1
+    assert lib.csa_decode_step_noalloc(C.byref(_desc(n_attn=5)), None) == -2
+    assert lib.csa_decode_step_noalloc(C.byref(_desc(n_seq=0)), None) == 0
+    full = _desc(n_seq=16, e_cap=1 << 20)
+    nb = lib.csa_decode_step_workspace_size(C.byref(full))
+    assert nb > _lib.NOALLOC_SCRATCH_BYTES
+    for name, typ in _lib.DecodeDesc._fields_:
+        if typ is C.c_void_p and name not in ("k_idx_scale", "kv_gamma"):
+            setattr(full, name, 16)
+        elif name in ("q", "win", "win_new", "sink", "out"):
+            getattr(full, name)[0] = 16
+    full.scan_events[0] = full.scan_events[1] = 0
+    for i in range(_lib.DECODE_EVENTS):
+        full.events[i] = 0
+    assert lib.csa_decode_step_noalloc(C.byref(full), None) == -5
+    hdr = re.search(r"#define\s+CSA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", _header())
+    assert int(hdr.group(1)) << int(hdr.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
 
 
 def test_decode_mxfp4_validation(lib):
