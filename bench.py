@@ -36,27 +36,58 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def host_threads():
+    """Host cores the oracle runs on: the CPUs this process may use (sched_getaffinity), capped
+    by OMP_NUM_THREADS when the environment sets it (the share of a shared host), and the BLAS
+    library NumPy calls ("openblas", "mkl", ...)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        n = min(n, int(os.environ["OMP_NUM_THREADS"]))
+    except (KeyError, ValueError):
+        pass
+    vendor = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        apis = [i.get("internal_api") for i in threadpool_info() if i.get("user_api") == "blas"]
+        vendor = apis[0] if apis else vendor
+    except Exception:  # pragma: no cover
+        pass
+    return max(1, n), vendor
+
+
+def timed_oracle(fn, budget_s, limit):
+    """Run fn(i) for i = 0, 1, ... with BLAS on host_threads() threads until about budget_s
+    seconds have passed (at most `limit` calls). Returns (calls, seconds, threads, vendor)."""
+    threads, vendor = host_threads()
+    try:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=threads, user_api="blas")
+    except Exception:  # pragma: no cover
+        import contextlib
+        ctx = contextlib.nullcontext()
+    with ctx:
+        done, t0 = 0, time.perf_counter()
+        while True:
+            fn(done)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or done >= limit:
+                break
+    return done, el, threads, vendor
+
+
 def cpu_baseline(case, budget_s):
     """The float64 oracle's decode step, on the host cores, over whole sequences of the same
     workload until about budget_s seconds of work (at most 200 queries)."""
     from oracle import pipeline
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     B = case["spec"].B
-    done, t0 = 0, time.perf_counter()
-    while True:
-        pipeline.decode_step(case, seqs=[done % B])
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or done >= 200:
-            break
+    done, el, threads, vendor = timed_oracle(
+        lambda i: pipeline.decode_step(case, seqs=[i % B]), budget_s, 200)
     return {"value": done / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "blas": vendor,
             "sample": f"{done} decode queries (whole sequences of the same workload, each a "
                       f"full step: pool, scan of every visible entry, Top-K, attention) in "
-                      f"{el:.1f} s, float64 NumPy"}
+                      f"{el:.1f} s, float64 NumPy, BLAS ({vendor}) on {threads} threads"}
 
 
 TRAFFIC_FILES = {
@@ -607,6 +638,14 @@ def main():
             case["idx_format"] = "mxfp4"
         if kv8 is not None:
             case["kv_format"] = "fp8"
+        if args.rope_dim:
+            # the same query, entry and window-row preparation and output inverse RoPE as the
+            # GPU step
+            case["q_gamma"] = [g.cpu() for g in q_gammas]
+            case["kv_gamma"] = kv_gamma.cpu()
+            case["q_rope_dim"] = case["kv_rope_dim"] = case["out_rope_dim"] = args.rope_dim
+        if args.score_format == "bf16":
+            case["score_format"] = "bf16"
         res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
         if mx:
             res["cpu_baseline"]["sample"] += (" with an MXFP4 cache (new key quantised; cached "

@@ -167,12 +167,15 @@ def enforce_rows(case: dict, rows, keys_for_row) -> dict:
     return redraws
 
 
-def enforce_prefill(case: dict, rows) -> dict:
+def enforce_prefill(case: dict, rows, ki_c=None) -> dict:
     """Chunked prefill: fix the gates of the checked query rows (keys include the chunk's
-    own pooled entries, computed by the oracle)."""
+    own pooled entries: by default the oracle's, or the stored chunk keys ki_c [B, chunk/m,
+    d_I] a caller passes, e.g. the ones another implementation pooled)."""
     spec = case["spec"]
-    ki_c = csa.store(csa.compress(f64(case["xi_chunk"]), f64(case["zi_chunk"]),
-                                  f64(case["bias_i"]), spec.m), spec.dtype)
+    if ki_c is None:
+        ki_c = csa.store(csa.compress(f64(case["xi_chunk"]), f64(case["zi_chunk"]),
+                                      f64(case["bias_i"]), spec.m), spec.dtype)
+    ki_c = f64(ki_c)
     e0 = (spec.L - spec.chunk) // spec.m
     qp = i64(case["q_pos"])
     cache = {}

@@ -630,14 +630,9 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
         load_new_key(a.ingest, r, new_slot, lane, nk);
       }
     }
-    int issued = 0;
 #pragma unroll
-    for (int j = 0; j < kSD; ++j) {
-      if (j < nt_item) {
-        issue(j, ring[wave][j]);
-        ++issued;
-      }
-    }
+    for (int j = 0; j < kSD; ++j)
+      if (j < nt_item) issue(j, ring[wave][j]);
     if (c == 0 && threadIdx.x == 0) {
       a.n_vis[r] = int32_t(n_pos);
       a.count[r] = int32_t(n_pos);
@@ -649,15 +644,28 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
         pk_new = kQ4 ? store_new_key_q4(a.ingest, r, e_new, pk, lane)
                      : store_new_key(a.ingest, r, e_new, pk, lane);
       }
-      // every tile of the item is loaded (in order), so the counts of the waits are exact;
-      // tiles past the visible range are not scored
+      // The first kSD tiles go out before the visible count is known; after that a tile is
+      // issued only when it starts before the visible end c1, so a ragged row loads no tiles
+      // past its end. Tiles land in issue order: tile t waits for all but the tiles issued
+      // after it, those of t + 1 .. t + kSD - 1 that were issued (tile t + kSD goes out after
+      // tile t is read). A tile issued past c1 is waited for (its slot is reused) but not
+      // scored.
+      const bool full = c1 >= lim;   // the whole item is visible: every tile goes out
+      auto was_issued = [&](int j) { return full || j < kSD || tile_base(j) < c1; };
       for (int t = 0; t < nt_item; ++t) {
         const int64_t tb = tile_base(t);
         unsigned char* slot = ring[wave][t % kSD];
-        if constexpr (kQ4) {
+        int later = 0;
+#pragma unroll
+        for (int k = 1; k < kSD; ++k)
+          if (t + k < nt_item && was_issued(t + k)) ++later;
+        // a tile never issued (past c1; the order is rotated, so one issued later may follow
+        // it) is neither read nor scored, and the issue below still runs
+        if (!was_issued(t)) {   // uniform over the wave
+        } else if constexpr (kQ4) {
           u32x4_t cw[4];
           uint32_t sc4[4];
-          read_tile_q4(slot, g, col, issued - t - 1, cw, sc4);
+          read_tile_q4(slot, g, col, later, cw, sc4);
           if (tb < c1) {
             if (e_new >= tb && e_new < tb + kQ4Keys)
               patch_new_key_q4(pk_new, int(e_new - tb), g, col, cw, sc4);
@@ -694,7 +702,7 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
           }
         } else {
           bf16x8_t B[4];
-          read_tile_B(slot, g, col, issued - t - 1, B);
+          read_tile_B(slot, g, col, later, B);
           if (tb < c1) {
             if (e_new >= tb && e_new < tb + 16)
               patch_new_key(pk_new, g, col == int(e_new - tb), B);
@@ -703,10 +711,7 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
             if (g == 0 && p < c1) segl.sc[p - c0] = a.score_bf16 ? round_to_bf16(sc) : sc;
           }
         }
-        if (t + kSD < nt_item) {
-          issue(t + kSD, slot);
-          ++issued;
-        }
+        if (t + kSD < nt_item && was_issued(t + kSD)) issue(t + kSD, slot);
       }
     }
     // tiles loaded past the visible range (or a row with none) must land before reuse

@@ -1,5 +1,5 @@
 """GPU parity at the full sizes of the five workloads, in the launch configuration the bench
-times: every sequence of the decode workloads, and 16 sampled query rows of the chunked
+times: every sequence of the decode workloads, and 376 sampled query rows of the chunked
 prefill (the oracle computes those one by one)."""
 import numpy as np
 import pytest
@@ -7,8 +7,8 @@ import torch
 
 import datagen
 import sparse_long_context_csa_amd as csa
-from gpu_helpers import (assert_ids, assert_pooled, assert_rows_close, check_step, dev, fp8_case,
-                         mxfp4_case, pooled_xmax, run_step)
+from gpu_helpers import (assert_ids, assert_pooled, assert_rows_close, assert_scores, check_step,
+                         dev, fp8_case, mxfp4_case, pooled_xmax, run_step)
 from oracle import csa as ocsa
 from oracle import gaps, pipeline
 from oracle.pipeline import f64
@@ -59,14 +59,46 @@ def test_decode_workload_fullsize_every_format_and_fusion():
     check_step(case, ref, st, rings, out, idx)
 
 
+PREFILL_ROWS = sorted(set(range(64)) | set(range(4032, 4096)) | set(range(0, 4096, 16)))
+
+
+def _prefill_run(case, g, kv, ki):
+    spec = case["spec"]
+    idx, scores = csa.index_topk(g["q_idx"], g["w"], ki, g["q_pos"], spec.m, spec.K,
+                                 e_count=g["e_count"], want_all=True)
+    out = csa.sparse_attn(g["q"], kv, idx, g["ring"], spec.w_cap, spec.W, g["q_pos"], g["sink"],
+                          spec.softmax_scale)
+    torch.cuda.synchronize()
+    return idx.cpu(), scores, out.float().cpu()
+
+
+def _prefill_check(case, rows, kv_c, ki_c, idx, scores, out, what):
+    spec = case["spec"]
+    e0 = (spec.L - spec.chunk) // spec.m
+    ref = pipeline.prefill_rows(case, rows, kv_c, ki_c)
+    ki = f64(case["k_idx"][0]).copy()
+    ki[e0:e0 + ki_c.shape[1]] = f64(ki_c[0])
+    for (b, i), ids in ref["ids"].items():
+        assert_ids(idx[b, i].numpy(), ids, f"{what}: query row {i}")
+        n = ocsa.n_visible(int(case["q_pos"][b, i]), spec.m, spec.entries)
+        sg = f64(scores[b, i, :n].cpu())
+        assert_scores(sg, ref["scores"][(b, i)],
+                      ocsa.score_scale(f64(case["q_idx"][b, i]), f64(case["w"][b, i]), ki[:n]),
+                      1e-3, f"{what}: scores of query row {i}")
+        assert_rows_close(f64(out[b, i]), ref["out"][(b, i)], 2e-2, f"{what}: query row {i}")
+
+
 def test_prefill_workload_fullsize():
     """Compress the 4,096-token chunk into both caches (checked against the exact pooled
-    values), then index, select and attend all 4,096 queries over caches that hold the oracle's
-    stored chunk entries, so that an ulp of pooling rounding cannot move a selection."""
+    values), then index, select and attend all 4,096 queries. Checked on 256 query rows (every
+    row of the first and last 64-query groups, every 16th row): ids, every index score of the
+    row and the outputs. Pass 1 indexes over caches that hold the oracle's stored chunk
+    entries (an ulp of pooling rounding cannot move a selection); pass 2 over the GPU's own
+    pooled entries, with the gap rule enforced on the keys that pass uses."""
     spec = datagen.CONFIGS[3]
     case = datagen.make_case(spec)
-    rows = [(0, i) for i in (0, 1, 2, 3, 4, 511, 1000, 1234, 2047, 2048, 3000, 4000, 4092, 4093,
-                             4094, 4095)]
+    rows = [(0, i) for i in PREFILL_ROWS]
+    assert len(rows) >= 256
     gaps.enforce_prefill(case, rows)
     print("config 3: inputs ready", flush=True)
     g = {k: dev(v) for k, v in case.items() if isinstance(v, torch.Tensor)}
@@ -83,18 +115,41 @@ def test_prefill_workload_fullsize():
         exact = ocsa.compress(f64(case[xs]), f64(case[zs]), f64(case[bs]), spec.m)
         assert_pooled(f64(cache[:, e0:e0 + ne].float().cpu()), exact,
                       pooled_xmax(f64(case[xs]), spec.m), f"chunk entries ({xs})")
+    kv_gpu, ki_gpu = kv[:, e0:e0 + ne].cpu(), ki[:, e0:e0 + ne].cpu()
+    # pass 1: the oracle's stored chunk entries in both caches
     kv_c, ki_c = pipeline.prefill_entries(case)
-    kv[:, e0:e0 + ne] = torch.from_numpy(kv_c).to(kv.dtype).to(kv.device)
-    ki[:, e0:e0 + ne] = torch.from_numpy(ki_c).to(ki.dtype).to(ki.device)
-    idx = csa.index_topk(g["q_idx"], g["w"], ki, g["q_pos"], spec.m, spec.K, e_count=g["e_count"])
-    out = csa.sparse_attn(g["q"], kv, idx, g["ring"], spec.w_cap, spec.W, g["q_pos"], g["sink"],
-                          spec.softmax_scale)
-    torch.cuda.synchronize()
-    ref = pipeline.prefill_rows(case, rows, kv_c, ki_c)
-    idx, out = idx.cpu(), out.float().cpu()
-    for (b, i), ids in ref["ids"].items():
-        assert_ids(idx[b, i].numpy(), ids, f"query row {i}")
-        assert_rows_close(f64(out[b, i]), ref["out"][(b, i)], 2e-2, f"query row {i}")
+    kv1, ki1 = kv.clone(), ki.clone()
+    kv1[:, e0:e0 + ne] = torch.from_numpy(kv_c).to(kv.dtype).to(kv.device)
+    ki1[:, e0:e0 + ne] = torch.from_numpy(ki_c).to(ki.dtype).to(ki.device)
+    idx, scores, out = _prefill_run(case, g, kv1, ki1)
+    print("config 3 pass 1: GPU done", flush=True)
+    _prefill_check(case, rows, kv_c, ki_c, idx, scores, out, "oracle chunk entries")
+    del scores
+    # pass 2: the GPU's own pooled chunk entries feed the index; the gates of a quarter of the
+    # rows are fixed again for these keys
+    rows2 = [(0, i) for i in PREFILL_ROWS[::4]]
+    gaps.enforce_prefill(case, rows2, ki_c=ki_gpu)
+    g["w"] = dev(case["w"])
+    idx, scores, out = _prefill_run(case, g, kv, ki)
+    print("config 3 pass 2: GPU done", flush=True)
+    _prefill_check(case, rows2, f64(kv_gpu), f64(ki_gpu), idx, scores, out,
+                   "GPU-pooled chunk entries")
+
+
+def test_decode_1m_ragged_rows():
+    """The 1M-context decode shape (262,144-entry caches, log-normal key norms) with ragged
+    positions over [L/2, L): rows whose later scan items lie wholly or partly past the visible
+    count, so the scan skips their tile loads; ids, outputs and state against the oracle."""
+    import dataclasses
+    spec = dataclasses.replace(datagen.CONFIGS[4], case_id=7400, ragged=True)
+    case = datagen.make_case(spec)
+    pos = case["pos"].tolist()
+    assert min(pos) < spec.L - spec.L // 4 and max(pos) == spec.L - 1
+    print(f"ragged 1M decode: positions {pos}", flush=True)
+    gaps.enforce_decode(case)
+    _, st, rings, out, idx = run_step(case)
+    ref = pipeline.decode_step(case)
+    check_step(case, ref, st, rings, out, idx)
 
 
 def test_hca_decode_fullsize():
