@@ -33,6 +33,7 @@ CHUNK = 1 << 22
 T_X, T_Z, T_BIAS, T_XI, T_ZI, T_BIAS_I = 0, 1, 2, 3, 4, 5
 T_KV, T_KI, T_Q, T_QI, T_W, T_SINK, T_QI2, T_W2 = 6, 7, 8, 9, 10, 11, 12, 13
 T_QX, T_RINGX, T_SINKX, T_POS = 14, 15, 16, 17
+T_XB, T_ZB, T_BIAS_B, T_XB_STALE = 18, 19, 20, 21
 
 
 def _gen(case_id: int, tid: int, attempt: int = 0, *extra: int) -> np.random.Generator:
@@ -108,6 +109,7 @@ class CaseSpec:
     bias_sigma: float | None = None
     ragged: bool = False       # decode: per-sequence positions differ
     scale: float | None = None
+    compressor: str = "single"  # decode main entries: "single" stream or "c4a" (overlapped)
 
     @property
     def entries(self) -> int:
@@ -247,6 +249,8 @@ def make_decode(spec: CaseSpec) -> dict:
         for b in range(B):
             rings[0, b, int(t[b]) % spec.w_cap] = 0.0
     out["rings"] = [to_storage(rings[c], dt) for c in range(spec.n_attn)]
+    if spec.compressor == "c4a":
+        out.update(_c4a_state(spec, t))
     out["q_idx"] = to_storage(_u(spec, T_QI, (B, spec.H_I, dI), dI), dt)
     out["w"] = to_storage(_u(spec, T_W, (B, spec.H_I), spec.H_I), dt).float()
     if spec.block_size > 0:
@@ -262,6 +266,39 @@ def make_decode(spec: CaseSpec) -> dict:
     out["sink"] = sinks
     out["scale"] = spec.softmax_scale
     return out
+
+
+def _c4a_state(spec: CaseSpec, t: np.ndarray) -> dict:
+    """The second (b) stream of the overlapped main compressor: its rows and logits for the
+    new token (``xb_new``/``zb_new`` [B,D]), its positional bias ``bias_b`` [m,D], and the
+    b rows of the last two blocks (``xb_tail``/``zb_tail`` [B,2m,D], position p at row
+    p % 2m: the previous block whole, the current block up to t - 1). Rows of positions
+    < 0 are zero; the rows the current block has not reached yet (positions t .. of its
+    slots) hold stale values from an older block, drawn at random, never zero."""
+    B, m, D, dt = spec.B, spec.m, spec.D, spec.dtype
+    xb = _u(spec, T_XB, (B, 2 * m, D), D)     # xb[b, j] = position (block start - m + j)
+    zb = _u(spec, T_ZB, (B, 2 * m, D), D)
+    stale_x = _u(spec, T_XB_STALE, (B, 2 * m, D), D)
+    stale_z = _u(spec, T_XB_STALE, (B, 2 * m, D), D, 1)
+    if spec.bias_sigma is not None:
+        bias_b = normal(spec.case_id, T_BIAS_B, (m, D)) * np.float32(spec.bias_sigma)
+    else:
+        bias_b = _u(spec, T_BIAS_B, (m, D), D)
+    xb_tail, zb_tail = stale_x.copy(), stale_z.copy()
+    xb_new = np.zeros((B, D), np.float32)
+    zb_new = np.zeros((B, D), np.float32)
+    for b in range(B):
+        tb = int(t[b])
+        s0 = tb - tb % m
+        for j in range(m + tb % m):           # positions s0 - m .. tb - 1
+            p = s0 - m + j
+            xb_tail[b, p % (2 * m)] = xb[b, j] if p >= 0 else 0.0
+            zb_tail[b, p % (2 * m)] = zb[b, j] if p >= 0 else 0.0
+        xb_new[b] = xb[b, m + tb % m]
+        zb_new[b] = zb[b, m + tb % m]
+    return {"xb_new": to_storage(xb_new, dt), "zb_new": to_storage(zb_new, dt),
+            "xb_tail": to_storage(xb_tail, dt), "zb_tail": to_storage(zb_tail, dt),
+            "bias_b": to_storage(bias_b, dt), "compressor": "c4a"}
 
 
 def redraw_w(spec: CaseSpec, which: str, b: int, attempt: int, dtype: str | None = None) -> torch.Tensor:

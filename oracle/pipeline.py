@@ -172,7 +172,12 @@ def decode_step(case: dict, seqs=None) -> dict:
     entries, oracle/fp8.py) and the new entry is attended at its cached value. case["kv_gamma"]
     and case["kv_rope_dim"] give the new entry its per-head RMSNorm and RoPE (at t, the position
     of the newest token it pools) before it is stored (rounded once), and the new window row
-    the same at its position t (``prepare_kv_row``).
+    the same at its position t (``prepare_kv_row``). With case["compressor"] == "c4a" the main
+    entry is the overlapped two-stream pooling ([CoD] "The compressor has two streams and they
+    overlap"): the new b-stream row enters case["xb_tail"] (the b rows of the last two blocks,
+    position p at row p % 2m) and entry e pools the a rows of its own block with the b rows of
+    block e - 1 (none for e = 0) through ``csa.compress_c4a``; the indexer keys keep the
+    single-stream pooling.
     Returns a dict with per-sequence results (new entries, scores, pool, ids, outputs).
     """
     spec = case["spec"]
@@ -180,6 +185,7 @@ def decode_step(case: dict, seqs=None) -> dict:
     pos = i64(case["pos"])
     seqs = list(range(spec.B)) if seqs is None else list(seqs)
     ring_raw = spec.m > 1
+    c4a = case.get("compressor") == "c4a"
     res = {"ids": {}, "out": {}, "kv_new": {}, "kv_new_exact": {}, "ki_new": {}, "scores": {},
            "pool": {}, "win_row": {}, "win_row_exact": {},
            "scores2": {}, "n_vis": {}}
@@ -195,6 +201,11 @@ def decode_step(case: dict, seqs=None) -> dict:
         z_tail[slot] = f64(case["z_new"][b])
         xi_tail[slot] = f64(case["xi_new"][b])
         zi_tail[slot] = f64(case["zi_new"][b])
+        if c4a:
+            xb_ring = f64(case["xb_tail"][b]).copy()
+            zb_ring = f64(case["zb_tail"][b]).copy()
+            xb_ring[t % (2 * m)] = f64(case["xb_new"][b])
+            zb_ring[t % (2 * m)] = f64(case["zb_new"][b])
         n_vis = csa.n_visible(t, m, E)
         keys = f64(case["k_idx"][b][:n_vis]).copy()
         new_e = None
@@ -202,7 +213,19 @@ def decode_step(case: dict, seqs=None) -> dict:
             new_e = (t + 1) // m - 1
             # the new entry's single head: RMSNorm, then RoPE at the position of the newest
             # token it pools (t)
-            kv_p = prepare_kv_row(case, csa.compress(x_tail, z_tail, bias, m)[0], t)
+            if c4a:
+                # a rows: this block (the tail); b rows: block new_e - 1, the other half of
+                # the two-block ring, absent for the sequence's first entry
+                prev_x = prev_z = None
+                if new_e > 0:
+                    h = ((new_e - 1) % 2) * m
+                    prev_x, prev_z = xb_ring[h:h + m], zb_ring[h:h + m]
+                pooled = csa.compress_c4a(x_tail, z_tail, np.zeros_like(x_tail),
+                                          np.zeros_like(z_tail), bias, f64(case["bias_b"]), m,
+                                          Xb_prev=prev_x, Zb_prev=prev_z)[0]
+            else:
+                pooled = csa.compress(x_tail, z_tail, bias, m)[0]
+            kv_p = prepare_kv_row(case, pooled, t)
             kv_e = csa.store(kv_p, dt)
             res["kv_new_exact"][b] = kv_p
             ki_e = csa.store(csa.compress(xi_tail, zi_tail, bias_i, m)[0], dt)

@@ -453,3 +453,92 @@ def test_decode_step_outputs_depend_only_on_distances():
     a2, b2 = dict(a, out_rope_dim=0), dict(b, out_rope_dim=0)
     o2a, o2b = pipeline.decode_step(a2)["out"][0][0], pipeline.decode_step(b2)["out"][0][0]
     assert np.abs(o2a - o2b).max() > 1e-2 * np.abs(o2a).max()
+
+
+# ---- the overlapped compressor inside the decode step ----------------------------------
+def c4a_stream_case(m: int, t: int, seq: dict):
+    """A one-sequence fp32 decode step at position t whose compressor state is what a stream of
+    steps over the rows in ``seq`` (xa, za, xb, zb: [T, D] for positions 0 .. T-1) leaves: the
+    a tail holds the current block's rows before t (its new slot zero), the b ring the b rows of
+    positions p < t at row p % 2m back to the previous block's start; ring rows never written
+    hold random stale values."""
+    spec = datagen.CaseSpec(921, "decode", dtype="f32", B=1, L=seq["xa"].shape[0], m=m, H_I=4,
+                            d_I=16, H=2, D=seq["xa"].shape[1], K=4, W=4, w_cap=8,
+                            compressor="c4a")
+    case = datagen.make_case(spec)
+    s0 = t - t % m
+    x_tail = np.zeros((1, m, spec.D), np.float32)
+    z_tail = np.zeros((1, m, spec.D), np.float32)
+    for p in range(s0, t):
+        x_tail[0, p - s0], z_tail[0, p - s0] = seq["xa"][p], seq["za"][p]
+    xb_tail = case["xb_tail"].numpy().copy()     # stale rows as drawn
+    zb_tail = case["zb_tail"].numpy().copy()
+    for p in range(max(s0 - m, 0), t):
+        xb_tail[0, p % (2 * m)], zb_tail[0, p % (2 * m)] = seq["xb"][p], seq["zb"][p]
+    case.update(pos=torch.tensor([t]), x_tail=torch.from_numpy(x_tail),
+                z_tail=torch.from_numpy(z_tail), xb_tail=torch.from_numpy(xb_tail),
+                zb_tail=torch.from_numpy(zb_tail),
+                x_new=torch.from_numpy(seq["xa"][t][None].copy()),
+                z_new=torch.from_numpy(seq["za"][t][None].copy()),
+                xb_new=torch.from_numpy(seq["xb"][t][None].copy()),
+                zb_new=torch.from_numpy(seq["zb"][t][None].copy()),
+                bias=torch.from_numpy(seq["ba"].copy()), bias_b=torch.from_numpy(seq["bb"].copy()))
+    return case
+
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_decode_step_c4a_entries_match_the_chunk_compressor(m):
+    # [CoD "The compressor has two streams and they overlap"]: entry e of a sequence pools the a
+    # rows of block e and the b rows of block e - 1; stepping token by token through the decode
+    # state must give the entries the chunk compressor gives over the whole sequence at once
+    T, D = 6 * m, 16
+    g = np.random.default_rng(5150 + m)
+    seq = {k: g.standard_normal((T, D)).astype(np.float32) for k in ("xa", "za", "xb", "zb")}
+    seq["ba"] = (0.5 * g.standard_normal((m, D))).astype(np.float32)
+    seq["bb"] = (0.5 * g.standard_normal((m, D))).astype(np.float32)
+    want = csa.compress_c4a(seq["xa"], seq["za"], seq["xb"], seq["zb"], seq["ba"], seq["bb"], m)
+    # plausible mistakes: the b rows of the entry's own block, no b-part, the single stream
+    own = np.stack([csa.compress_c4a(seq["xa"][m * e:m * e + m], seq["za"][m * e:m * e + m],
+                                     seq["xb"][:m], seq["zb"][:m], seq["ba"], seq["bb"], m,
+                                     Xb_prev=seq["xb"][m * e:m * e + m],
+                                     Zb_prev=seq["zb"][m * e:m * e + m])[0] for e in range(6)])
+    single = csa.compress(seq["xa"], seq["za"], seq["ba"], m)
+    for e in range(6):
+        t = m * e + m - 1
+        got = pipeline.decode_step(c4a_stream_case(m, t, seq))["kv_new_exact"][0]
+        np.testing.assert_allclose(got, want[e], rtol=0, atol=1e-12)
+        if e > 0:
+            assert np.abs(got - own[e]).max() > 1e-3
+            assert np.abs(got - single[e]).max() > 1e-3
+        else:   # the sequence's first entry has no previous block: a rows only
+            np.testing.assert_allclose(got, single[0], rtol=0, atol=1e-12)
+    if m > 1:   # a step that does not complete a block pools nothing
+        assert pipeline.decode_step(c4a_stream_case(m, 2 * m - 2, seq))["kv_new"] == {}
+
+
+def test_decode_step_c4a_state_drawn_by_datagen():
+    # the b ring datagen draws for a decode step holds the previous block's rows where the step
+    # reads them: its entry equals the chunk compressor over the drawn rows of both blocks
+    spec = datagen.CaseSpec(922, "decode", dtype="f32", B=3, L=4 * 300, m=4, H_I=4, d_I=16, H=2,
+                            D=16, K=4, W=4, w_cap=8, ragged=True, compressor="c4a")
+    case = datagen.make_case(spec)
+    res = pipeline.decode_step(case)
+    m = spec.m
+    n_pooled = 0
+    for b in range(spec.B):
+        t = int(case["pos"][b])
+        if (t + 1) % m:
+            continue
+        n_pooled += 1
+        e = (t + 1) // m - 1
+        xa = f64(case["x_tail"][b]).copy()
+        za = f64(case["z_tail"][b]).copy()
+        xa[m - 1], za[m - 1] = f64(case["x_new"][b]), f64(case["z_new"][b])
+        h = ((e - 1) % 2) * m
+        xb, zb = f64(case["xb_tail"][b])[h:h + m], f64(case["zb_tail"][b])[h:h + m]
+        # entry 1 of a two-block chunk pools block 1's a rows with block 0's b rows
+        want = csa.compress_c4a(np.concatenate([xa, xa]), np.concatenate([za, za]),
+                                np.concatenate([xb, xb]), np.concatenate([zb, zb]),
+                                f64(case["bias"]), f64(case["bias_b"]), m)[1]
+        np.testing.assert_allclose(res["kv_new_exact"][b], want, rtol=0, atol=1e-12)
+    assert n_pooled >= 1
