@@ -16,6 +16,7 @@ about 4 us more than a plain one, so sampling keeps that out of the headline); w
 from an eager pass of the same length after it.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -411,8 +412,9 @@ def main():
                          "entries, or 576-byte FP8 entries (csa_quantize_kv_fp8 of the same "
                          "entries, made before the timed region)")
     ap.add_argument("--compressor", default="single", choices=("single", "c4a"),
-                    help="chunked prefill (--config 3): the single-stream compressor, or the "
-                         "overlapped two-stream one for both caches")
+                    help="main compressor: the single stream, or the overlapped two-stream "
+                         "one (decode workloads 2/4/5: the main entries; chunked prefill, "
+                         "--config 3: both caches)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -433,12 +435,16 @@ def main():
     if args.config == 7:
         return bench_norm_rope(args)
     spec = datagen.CONFIGS[args.config]
+    c4a = args.compressor == "c4a"
+    if c4a:
+        spec = dataclasses.replace(spec, compressor="c4a")
     t0 = time.time()
     case = datagen.make_case(spec)
     log(f"generated inputs in {time.time() - t0:.1f} s")
     dev = torch.device("cuda:0")
     shared = {k: case[k].to(dev) for k in ("pos", "x_new", "z_new", "xi_new", "zi_new", "bias",
-                                            "bias_i", "q_idx", "w")}
+                                            "bias_i", "q_idx", "w")
+              + (("xb_new", "zb_new", "bias_b") if c4a else ())}
     hier = {}
     if spec.block_size:
         hier = dict(block_size=spec.block_size, max_blocks=spec.max_blocks,
@@ -464,7 +470,8 @@ def main():
         kv_gamma = (datagen.tensor(spec.case_id, 95, (spec.D,), spec.dtype, 0.3) + 1.0).to(dev)
     steps_objs, states = [], []
     for c in range(args.copies):
-        st = {k: case[k].to(dev) for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
+        st = {k: case[k].to(dev) for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")
+              + (("xb_tail", "zb_tail") if c4a else ())}
         if mx:
             st["k_idx"] = codes.clone()
             st["k_idx_scale"] = scales.clone()
@@ -477,7 +484,8 @@ def main():
         steps_objs.append(csa.DecodeStep(
             m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
             score_format=args.score_format, out_rope_dim=args.rope_dim, q_rope_dim=args.rope_dim,
-            q_gamma=q_gammas, kv_gamma=kv_gamma, kv_rope_dim=args.rope_dim, **states[-1]))
+            q_gamma=q_gammas, kv_gamma=kv_gamma, kv_rope_dim=args.rope_dim,
+            compressor=args.compressor, **states[-1]))
     torch.cuda.synchronize()
     log(f"device state ready: {args.copies} copies, "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
@@ -572,7 +580,7 @@ def main():
                                        ring_write=datagen.ring_from_raw(spec),
                                        key_bytes=key_bytes,
                                        entry_bytes=acc.FP8_ENTRY_BYTES if kv8 is not None
-                                       else None).total
+                                       else None, c4a=c4a).total
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
@@ -615,11 +623,14 @@ def main():
         res["metric"] += (f", query and entry RMSNorm + RoPE and output inverse RoPE on the "
                           f"last {args.rope_dim} channels")
         res["config"]["rope_dim"] = args.rope_dim
+    if c4a:
+        res["metric"] += ", overlapped two-stream main compressor"
+        res["config"]["compressor"] = "c4a"
     if args.score_format == "bf16":
         # recall of the fp32 selection: the same step (idempotent: it rewrites the same tail
         # slot and entry) ranked on fp32 scores, over state copy 0
         ref = csa.DecodeStep(m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
-                             score_format="f32", **states[0])
+                             score_format="f32", compressor=args.compressor, **states[0])
         _, ids_bf = steps_objs[0]()
         ids_bf = ids_bf.clone()
         _, ids_f32 = ref()

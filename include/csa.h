@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 12
+#define CSA_ABI_VERSION 13
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -314,6 +314,8 @@ int csa_sparse_attn_fp8(const void *q, const void *kv, const int32_t *idx, int32
 #define CSA_SCORE_BF16 1  /* rank the scores rounded to bf16                               */
 #define CSA_KV_DTYPE 0    /* csa_decode_desc.kv_format: main entries in the step's dtype      */
 #define CSA_KV_FP8 1      /* main entries as 576-byte FP8 entries (csa_quantize_kv_fp8)       */
+#define CSA_COMP_SINGLE 0 /* csa_decode_desc.compressor: one main stream (csa_compress)        */
+#define CSA_COMP_C4A 1    /* two overlapped main streams (csa_compress_c4a)                    */
 
 typedef struct csa_decode_desc {
   int32_t dtype;
@@ -409,6 +411,22 @@ typedef struct csa_decode_desc {
    *   insertion.] */
   const void *kv_gamma;
   int32_t kv_rope_dim;
+  /* Compressor of the main entries: CSA_COMP_SINGLE pools as step 2 above; CSA_COMP_C4A pools
+   * them with the overlapped two-stream compressor. Then x_new, z_new, x_tail, z_tail and bias
+   * are the a stream, and the b stream of the new token (xb_new, zb_new T [n_seq, dim]) enters
+   * xb_tail, zb_tail (T [n_seq, 2m, dim]) at row t % 2m: the b rows of the last two blocks,
+   * position p at row p % 2m. Entry e = (t+1)/m - 1 is then csa_compress_c4a of the a rows of
+   * block e and the b rows of block e - 1 (rows ((e-1) % 2) m .. + m of xb_tail, zb_tail), with
+   * bias_a = bias and bias_b (T [m, dim]); entry 0 of a sequence has no b-part. The indexer keys
+   * keep the single-stream pooling of step 2. The four b pointers and bias_b are required with
+   * CSA_COMP_C4A (else CSA_ERR_NULL) and ignored otherwise.
+   *   [CoD "The compressor has two streams and they overlap": entry i draws C^a from its own
+   *   block and C^b from the block before, one softmax over the 2m logits per channel; CoD CSA
+   *   layer table: two overlapped KV streams with biases B^a, B^b.] */
+  int32_t compressor;
+  const void *xb_new, *zb_new;
+  void *xb_tail, *zb_tail;
+  const void *bias_b;
 } csa_decode_desc;
 
 size_t csa_decode_step_workspace_size(const csa_decode_desc *d);

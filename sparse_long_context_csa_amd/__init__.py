@@ -240,7 +240,10 @@ class DecodeStep:
     RoPE at +pos) in the selection launch. A uint8 kv [n_seq, e_cap, 576] is an FP8 main
     cache (quantize_kv_fp8's entries; kv_format CSA_KV_FP8). kv_gamma ([dim] or None) and
     kv_rope_dim give the entry a step completes its RMSNorm and RoPE at pos before it is
-    stored. With no_alloc=True no workspace is allocated and each call runs
+    stored. compressor="c4a" pools the main entries with the overlapped two-stream compressor:
+    x_new, z_new, x_tail, z_tail and bias are then its a stream, and xb_new, zb_new ([n_seq,
+    dim]), xb_tail, zb_tail ([n_seq, 2m, dim], position p at row p % 2m) and bias_b ([m, dim])
+    its b stream. With no_alloc=True no workspace is allocated and each call runs
     csa_decode_step_noalloc over the library's static per-GPU scratch array (calls that may
     overlap on one GPU race there)."""
 
@@ -248,7 +251,7 @@ class DecodeStep:
                  max_blocks: int = 0, out=None, out_idx=None, score_format: str = "f32",
                  out_rope_dim: int = 0, rope_base: float = 10000.0, q_gamma=None,
                  q_rope_dim: int = 0, kv_gamma=None, kv_rope_dim: int = 0,
-                 no_alloc: bool = False, **t):
+                 compressor: str = "single", no_alloc: bool = False, **t):
         self.t = t
         kv = _dev(t["kv"], "kv")
         kv8 = kv.dtype == torch.uint8
@@ -319,6 +322,16 @@ class DecodeStep:
         if kv_gamma is not None:
             d.kv_gamma = _dev(kv_gamma, "kv_gamma", dt).data_ptr()
         d.kv_rope_dim = int(kv_rope_dim)
+        if compressor not in ("single", "c4a"):
+            raise ValueError("compressor must be 'single' or 'c4a'")
+        if compressor == "c4a":
+            d.compressor = _lib.COMP_C4A
+            want = {"xb_new": (n_seq, dim), "zb_new": (n_seq, dim), "xb_tail": (n_seq, 2 * m, dim),
+                    "zb_tail": (n_seq, 2 * m, dim), "bias_b": (m, dim)}
+            for k, shape in want.items():
+                if tuple(_dev(t[k], k, dt).shape) != shape:
+                    raise ValueError(f"{k} must be {list(shape)}")
+                setattr(d, k, t[k].data_ptr())
         d.out_idx = out_idx.data_ptr()
         self.desc = d
         nb = lib().csa_decode_step_workspace_size(C.byref(d))

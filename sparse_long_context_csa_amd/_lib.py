@@ -18,6 +18,7 @@ KV_DTYPE, KV_FP8 = 0, 1
 KV_FP8_BYTES = 576
 NOALLOC_SCRATCH_BYTES = 32 << 20
 NR_NORM, NR_ROPE, NR_INVERSE = 1, 2, 4
+COMP_SINGLE, COMP_C4A = 0, 1
 
 vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
 
@@ -39,6 +40,8 @@ class DecodeDesc(C.Structure):
         ("out_rope_dim", i32), ("rope_base", f32),
         ("q_gamma", vp * MAX_ATTN), ("q_rope_dim", i32), ("kv_format", i32),
         ("kv_gamma", vp), ("kv_rope_dim", i32),
+        ("compressor", i32), ("xb_new", vp), ("zb_new", vp), ("xb_tail", vp), ("zb_tail", vp),
+        ("bias_b", vp),
     ]
 
 

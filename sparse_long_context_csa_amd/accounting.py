@@ -58,12 +58,14 @@ class StepBytes:
 def decode_step_bytes(B: int, n_vis: int, m: int, D: int, H: int, H_I: int, d_I: int, K: int,
                       W: int, n_attn: int = 1, pool: int = 0, elt: int = BF16,
                       ring_write: bool = True, key_bytes: int | None = None,
-                      entry_bytes: int | None = None) -> StepBytes:
+                      entry_bytes: int | None = None, c4a: bool = False) -> StepBytes:
     """Algorithmic HBM bytes of one fused decode step over B sequences, each with n_vis
     visible entries (all sequences at a block boundary, so one entry is pooled per stream).
     pool > 0: hierarchical (stage-1 scan of n_vis keys, then ``pool`` rescored keys).
     key_bytes: bytes of one cached indexer key (default d_I * elt; MXFP4: mxfp4_key_bytes).
-    entry_bytes: bytes of one cached main entry (default D * elt; FP8: FP8_ENTRY_BYTES)."""
+    entry_bytes: bytes of one cached main entry (default D * elt; FP8: FP8_ENTRY_BYTES).
+    c4a: the overlapped main compressor adds its b stream: the new b row (x and z) read and
+    written to its ring, the previous block's m b rows read, and its bias."""
     kb = d_I * elt if key_bytes is None else key_bytes
     eb = D * elt if entry_bytes is None else entry_bytes
     keys = B * n_vis * kb + B * pool * kb
@@ -77,6 +79,8 @@ def decode_step_bytes(B: int, n_vis: int, m: int, D: int, H: int, H_I: int, d_I:
     per_row = (2 * D + 2 * d_I) * elt
     compress = B * (m * per_row + per_row + eb + kb + (D * elt if ring_write else 0)) \
         + m * (D + d_I) * elt
+    if c4a:
+        compress += B * (2 * D * elt * (m + 2)) + m * D * elt
     return StepBytes(keys, gather, queries, outputs, compress)
 
 

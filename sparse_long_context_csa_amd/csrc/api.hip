@@ -488,6 +488,7 @@ int check_decode_shapes(const csa_decode_desc* d) {
   if (d->kv_format == CSA_KV_FP8 && (d->dtype != CSA_BF16 || d->n_heads != 64 || d->dim != 512))
     return CSA_ERR_UNSUPPORTED;
   if (d->score_format != CSA_SCORE_F32 && d->score_format != CSA_SCORE_BF16) return CSA_ERR_SHAPE;
+  if (d->compressor != CSA_COMP_SINGLE && d->compressor != CSA_COMP_C4A) return CSA_ERR_SHAPE;
   if (d->score_format == CSA_SCORE_BF16 &&
       (d->block_size != 0 || !scan_reads_mxfp4(d->dtype, d->idx_heads, d->idx_dim, 1, false)))
     return CSA_ERR_UNSUPPORTED;
@@ -503,6 +504,9 @@ int check_decode(const csa_decode_desc* d) {
       !d->q_idx || !d->w || !d->out_idx)
     return CSA_ERR_NULL;
   if (d->block_size > 0 && (!d->q_idx2 || !d->w2)) return CSA_ERR_NULL;
+  if (d->compressor == CSA_COMP_C4A &&
+      (!d->xb_new || !d->zb_new || !d->xb_tail || !d->zb_tail || !d->bias_b))
+    return CSA_ERR_NULL;
   if (d->idx_format == CSA_IDX_MXFP4) {
     if (!d->k_idx_scale) return CSA_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(d->k_idx) % 16 != 0 ||
@@ -552,6 +556,10 @@ int decode_step_run(const csa_decode_desc* d, void* ws, void* stream) {
   in.kv_fp8 = d->kv_format == CSA_KV_FP8 ? 1 : 0;
   in.kv_gamma = d->kv_gamma;
   in.kv_rope_dim = d->kv_rope_dim;
+  if (d->compressor == CSA_COMP_C4A) {
+    in.xb_new = d->xb_new; in.zb_new = d->zb_new; in.xb_tail = d->xb_tail;
+    in.zb_tail = d->zb_tail; in.bias_b = d->bias_b;
+  }
   in.rope_log2_base = d->rope_base > 1.f ? log2(double(d->rope_base)) : 0.0;
   for (int c2 = 0; c2 < 4; ++c2) {
     in.win[c2] = c2 < d->n_attn ? d->win[c2] : nullptr;

@@ -11,46 +11,31 @@
 
 namespace csa {
 
-// Pool 8 channels over m rows. Row j's x/z come from memory (x0 + j*stride) except row
-// `own` whose values are passed in registers (xo, zo). For m <= kRegM every row is loaded
-// up front (one round trip to memory); longer entries take two passes over the logits.
+// Pool 8 channels over n rows: fetch(j, a, x) gives row j's logits with the positional bias
+// added (a[8]) and, when x is non-null, its values (x[8]). For n <= kRegM every row is fetched
+// up front (one round trip to memory); longer pools take two passes (logits only for the
+// maximum, then both). kRegs = false keeps to the two-pass form for every n (few registers:
+// for callers that must not raise their own register budget).
 constexpr int kRegM = 8;
 
-// kRegs = false keeps to the two-pass form for every m (few registers: for callers that
-// must not raise their own register budget).
-template <typename T, bool kRegs = true>
-__device__ __forceinline__ void pool8(const T* x0, const T* z0, int64_t stride, const T* b0,
-                                      int bstride, int m, int own, const float* xo,
-                                      const float* zo, float* out) {
-  if (kRegs && m <= kRegM) {
+template <bool kRegs, typename Fetch>
+__device__ __forceinline__ void pool8_rows(int n, Fetch&& fetch, float* out) {
+  if (kRegs && n <= kRegM) {
     float a[kRegM][8], xv[kRegM][8];
 #pragma unroll
-    for (int j = 0; j < kRegM; ++j) {
-      if (j < m) {
-        float bb[8];
-        if (j == own) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) { a[j][c] = zo[c]; xv[j][c] = xo[c]; }
-        } else {
-          Elt<T>::load8(z0 + j * stride, a[j]);
-          Elt<T>::load8(x0 + j * stride, xv[j]);
-        }
-        Elt<T>::load8(b0 + j * bstride, bb);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) a[j][c] += bb[c];
-      }
-    }
+    for (int j = 0; j < kRegM; ++j)
+      if (j < n) fetch(j, a[j], xv[j]);
     float mx[8], sum[8], acc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) { mx[c] = a[0][c]; sum[c] = 0.f; acc[c] = 0.f; }
 #pragma unroll
     for (int j = 1; j < kRegM; ++j)
-      if (j < m)
+      if (j < n)
 #pragma unroll
         for (int c = 0; c < 8; ++c) mx[c] = fmaxf(mx[c], a[j][c]);
 #pragma unroll
     for (int j = 0; j < kRegM; ++j)
-      if (j < m)
+      if (j < n)
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const float e = expf(a[j][c] - mx[c]);
@@ -61,41 +46,79 @@ __device__ __forceinline__ void pool8(const T* x0, const T* z0, int64_t stride, 
     for (int c = 0; c < 8; ++c) out[c] = acc[c] / sum[c];
     return;
   }
-  float mx[8], a[8], bb[8];
+  float mx[8], a[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) mx[c] = neg_inf();
-  for (int j = 0; j < m; ++j) {
-    if (j == own) {
+  for (int j = 0; j < n; ++j) {
+    fetch(j, a, nullptr);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) a[c] = zo[c];
-    } else {
-      Elt<T>::load8(z0 + j * stride, a);
-    }
-    Elt<T>::load8(b0 + j * bstride, bb);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) mx[c] = fmaxf(mx[c], a[c] + bb[c]);
+    for (int c = 0; c < 8; ++c) mx[c] = fmaxf(mx[c], a[c]);
   }
   float sum[8], acc[8], xv[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) { sum[c] = 0.f; acc[c] = 0.f; }
-  for (int j = 0; j < m; ++j) {
-    if (j == own) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) { a[c] = zo[c]; xv[c] = xo[c]; }
-    } else {
-      Elt<T>::load8(z0 + j * stride, a);
-      Elt<T>::load8(x0 + j * stride, xv);
-    }
-    Elt<T>::load8(b0 + j * bstride, bb);
+  for (int j = 0; j < n; ++j) {
+    fetch(j, a, xv);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float e = expf(a[c] + bb[c] - mx[c]);
+      const float e = expf(a[c] - mx[c]);
       sum[c] += e;
       acc[c] = fmaf(e, xv[c], acc[c]);
     }
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) out[c] = acc[c] / sum[c];
+}
+
+// Row j (< m) of one stream's block: its x/z from memory (x0 + j*stride), except row `own`
+// whose values are passed in registers (xo, zo); the bias row b0 + j*bstride added to z. Row
+// `own` is loaded too (its memory slot is stale) and then replaced by a select, so that no
+// branch splits the loads of the rows: they all go out before the first one is waited for.
+template <typename T>
+__device__ __forceinline__ void fetch_row8(const T* x0, const T* z0, int64_t stride,
+                                           const T* b0, int bstride, int j, int own,
+                                           const float* xo, const float* zo, float* a,
+                                           float* x) {
+  const bool o = j == own;
+  Elt<T>::load8(z0 + j * stride, a);
+  if (x != nullptr) Elt<T>::load8(x0 + j * stride, x);
+  float bb[8];
+  Elt<T>::load8(b0 + j * bstride, bb);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) a[c] = (o ? zo[c] : a[c]) + bb[c];
+  if (x != nullptr)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] = o ? xo[c] : x[c];
+}
+
+// Pool 8 channels over the m rows of one stream's block (csa_compress's entry).
+template <typename T, bool kRegs = true>
+__device__ __forceinline__ void pool8(const T* x0, const T* z0, int64_t stride, const T* b0,
+                                      int bstride, int m, int own, const float* xo,
+                                      const float* zo, float* out) {
+  pool8_rows<kRegs>(
+      m,
+      [&](int j, float* a, float* x) {
+        fetch_row8<T>(x0, z0, stride, b0, bstride, j, own, xo, zo, a, x);
+      },
+      out);
+}
+
+// The overlapped two-stream entry (csa_compress_c4a's): one softmax over the m a rows of the
+// entry's own block (x0/z0, row `own` in registers, bias b0) and the m b rows of the block
+// before (xb0/zb0, bias bb0; none when xb0 is null: a sequence's first entry).
+template <typename T, bool kRegs = true>
+__device__ __forceinline__ void pool8_c4a(const T* x0, const T* z0, const T* xb0, const T* zb0,
+                                          int64_t stride, const T* b0, const T* bb0, int m,
+                                          int own, const float* xo, const float* zo,
+                                          float* out) {
+  pool8_rows<kRegs>(
+      xb0 != nullptr ? 2 * m : m,
+      [&](int j, float* a, float* x) {
+        if (j < m) fetch_row8<T>(x0, z0, stride, b0, stride, j, own, xo, zo, a, x);
+        else fetch_row8<T>(xb0, zb0, stride, bb0, stride, j - m, -1, xo, zo, a, x);
+      },
+      out);
 }
 
 // Vectors of 8 channels one sequence's ingest covers: main stream, rings, indexer stream.
@@ -182,15 +205,44 @@ __device__ __forceinline__ void ingest_vector(const IngestArgs& a, int64_t sq, i
   const T* zn = (const T*)(main ? a.z_new : a.zi_new) + sq * d + c0;
   T* xt = (T*)(main ? a.x_tail : a.xi_tail) + sq * m * d + c0;
   T* zt = (T*)(main ? a.z_tail : a.zi_tail) + sq * m * d + c0;
+  // Every load (the new rows, the tail rows and biases the entry pools) goes out before the
+  // first store: the tail slot and the b ring row this step writes are never read (the new row
+  // is pooled from registers), so the loads make a single round trip to memory.
   float xo[8], zo[8];
   Elt<T>::load8(xn, xo);
   Elt<T>::load8(zn, zo);
+  // the overlapped main compressor's b stream: the new row goes to the two-block ring (row
+  // t % 2m); the entry reads the other block's half
+  const bool c4a = main && a.xb_new != nullptr;
+  float xb[8], zb[8];
+  T* xr = nullptr;
+  T* zr = nullptr;
+  if (c4a) {
+    Elt<T>::load8((const T*)a.xb_new + sq * d + c0, xb);
+    Elt<T>::load8((const T*)a.zb_new + sq * d + c0, zb);
+    xr = (T*)a.xb_tail + sq * 2 * m * d + c0;
+    zr = (T*)a.zb_tail + sq * 2 * m * d + c0;
+  }
+  const bool pool = complete && e < a.e_cap && (main || pool_index);
+  float res[8];
+  if (pool) {
+    if (c4a) {
+      const int64_t h = int64_t((e - 1) & 1) * m * d;   // block e - 1 (none for entry 0)
+      pool8_c4a<T, kRegs>(xt, zt, e > 0 ? xr + h : nullptr, e > 0 ? zr + h : nullptr, d,
+                          (const T*)a.bias + c0, (const T*)a.bias_b + c0, m, slot, xo, zo, res);
+    } else {
+      pool8<T, kRegs>(xt, zt, d, (const T*)(main ? a.bias : a.bias_i) + c0, d, m, slot, xo,
+                      zo, res);
+    }
+  }
   Elt<T>::store8(xt + slot * d, xo);
   Elt<T>::store8(zt + slot * d, zo);
-  if (complete && e < a.e_cap && (main || pool_index)) {
-    float res[8];
-    pool8<T, kRegs>(xt, zt, d, (const T*)(main ? a.bias : a.bias_i) + c0, d, m, slot, xo, zo,
-                    res);
+  if (c4a) {
+    const int rb = int(t % (2 * m));
+    Elt<T>::store8(xr + rb * d, xb);
+    Elt<T>::store8(zr + rb * d, zb);
+  }
+  if (pool) {
     // the entry's RMSNorm and RoPE at t (the newest position it pools): its 64 vectors are
     // this wave's 64 lanes
     if (main && prep) prep_kv_row8<T>(a, t, c0, d, res);

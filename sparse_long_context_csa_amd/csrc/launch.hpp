@@ -38,6 +38,12 @@ struct IngestArgs {
   const void* kv_gamma;
   int kv_rope_dim;
   void* k_scale;          // non-null: k_idx holds MXFP4 codes, k_scale their scale bytes
+  // overlapped two-stream main compressor (xb_new non-null): the b stream's new row enters
+  // xb_tail / zb_tail [n_seq, 2m, dim] at row t % 2m (position p at row p % 2m) and entry e
+  // pools the a tail with the b rows of block e - 1, bias_b [m, dim] on the b logits
+  const void *xb_new, *zb_new;
+  void *xb_tail, *zb_tail;
+  const void* bias_b;
   void* win[4];
   const void* win_new[4];
   // query preparation for the attention calls, done by the workgroups that run this ingest:

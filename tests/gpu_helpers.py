@@ -191,7 +191,12 @@ def run_step(case, idx_state=None):
     if spec.block_size:
         kw = dict(block_size=spec.block_size, max_blocks=spec.max_blocks, q_idx2=g["q_idx2"],
                   w2=g["w2"])
-    st = {k: g[k].clone() for k in ("kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail")}
+    names = ["kv", "k_idx", "x_tail", "z_tail", "xi_tail", "zi_tail"]
+    c4a = case.get("compressor") == "c4a"
+    if c4a:
+        names += ["xb_tail", "zb_tail"]
+        kw.update(compressor="c4a", xb_new=g["xb_new"], zb_new=g["zb_new"], bias_b=g["bias_b"])
+    st = {k: g[k].clone() for k in names}
     if idx_state is not None:
         st.update({k: v.clone() for k, v in idx_state.items()})
     step = csa_lib.DecodeStep(m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
@@ -222,6 +227,14 @@ def check_step(case, ref, st, rings, out, idx):
         slot = t % spec.m
         assert torch.equal(st["x_tail"][b, slot].cpu(), case["x_new"][b])
         assert torch.equal(st["zi_tail"][b, slot].cpu(), case["zi_new"][b])
+        c4a = case.get("compressor") == "c4a"
+        if c4a:   # the b stream's new row in its two-block ring; the other rows untouched
+            rb = t % (2 * spec.m)
+            keep = np.arange(2 * spec.m) != rb
+            for name, new in (("xb_tail", "xb_new"), ("zb_tail", "zb_new")):
+                got = st[name][b].cpu()
+                assert torch.equal(got[rb], case[new][b])
+                assert torch.equal(got[keep], case[name][b][keep])
         if b in ref["kv_new"]:
             e = (t + 1) // spec.m - 1
             for name, xs, zs, xn, zn, bias in (
@@ -233,6 +246,15 @@ def check_step(case, ref, st, rings, out, idx):
                 z[slot] = f64(case[zn][b])
                 exact = ocsa.compress(x, z, f64(case[bias]), spec.m)[0]
                 xmax = np.abs(x).max(axis=0)
+                if name == "kv" and c4a:
+                    # the overlapped entry (oracle), over this block's a rows and the b rows
+                    # of the block before
+                    exact = ref["kv_new_exact"][b]
+                    rows = [x]
+                    if e > 0:
+                        h = ((e - 1) % 2) * spec.m
+                        rows.append(f64(case["xb_tail"][b])[h:h + spec.m])
+                    xmax = np.abs(np.concatenate(rows)).max(axis=0)
                 if name == "kv" and b in ref.get("kv_new_exact", {}) and (
                         case.get("kv_gamma") is not None or case.get("kv_rope_dim")):
                     # normalised / rotated: the fp32 error scales with the entry itself

@@ -88,14 +88,16 @@ def test_decode_desc_mirrors_the_header_struct():
     # 17 tensor pointers, 5 arrays of CSA_MAX_ATTN pointers, out_idx, the phase events, the
     # scan kernel's start and stop events; idx_format padded to 8 B, k_idx_scale, then
     # score_format, out_rope_dim and rope_base (12 B, padded to 16), the CSA_MAX_ATTN query
-    # gammas, q_rope_dim and kv_format (8 B), kv_gamma, kv_rope_dim padded to 8 B
+    # gammas, q_rope_dim and kv_format (8 B), kv_gamma, kv_rope_dim and compressor (8 B), the
+    # b stream's 5 pointers
     n_ptr = 17 + 5 * _lib.MAX_ATTN + 1 + _lib.DECODE_EVENTS + 2
     assert C.sizeof(_lib.DecodeDesc) == (64 + 8 + 8 * n_ptr + 8 + 8 + 16 + 8 * _lib.MAX_ATTN
-                                         + 8 + 8 + 8)
+                                         + 8 + 8 + 8 + 5 * 8)
     for name, val in (("CSA_IDX_DTYPE", _lib.IDX_DTYPE), ("CSA_IDX_MXFP4", _lib.IDX_MXFP4),
                       ("CSA_SCORE_F32", _lib.SCORE_F32), ("CSA_SCORE_BF16", _lib.SCORE_BF16),
                       ("CSA_KV_DTYPE", _lib.KV_DTYPE), ("CSA_KV_FP8", _lib.KV_FP8),
-                      ("CSA_KV_FP8_BYTES", _lib.KV_FP8_BYTES)):
+                      ("CSA_KV_FP8_BYTES", _lib.KV_FP8_BYTES),
+                      ("CSA_COMP_SINGLE", _lib.COMP_SINGLE), ("CSA_COMP_C4A", _lib.COMP_C4A)):
         assert int(re.search(rf"#define\s+{name}\s+(\d+)", _header()).group(1)) == val
 
 
@@ -257,6 +259,31 @@ def test_decode_noalloc_validation(lib):
     assert lib.csa_decode_step_noalloc(C.byref(full), None) == -5
     hdr = re.search(r"#define\s+CSA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", _header())
     assert int(hdr.group(1)) << int(hdr.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+
+
+def test_decode_compressor_validation(lib):
+    # the overlapped compressor needs the b stream's five pointers; an unknown compressor is a
+    # shape error; both refused before anything is launched
+    d = _desc(compressor=_lib.COMP_C4A)
+    for name, typ in _lib.DecodeDesc._fields_:
+        if typ is C.c_void_p and name not in ("k_idx_scale", "kv_gamma"):
+            setattr(d, name, 256)
+        elif name in ("q", "win", "win_new", "sink", "out"):
+            getattr(d, name)[0] = 256
+    d.scan_events[0] = d.scan_events[1] = None
+    for i in range(_lib.DECODE_EVENTS):
+        d.events[i] = None
+    nb = lib.csa_decode_step_workspace_size(C.byref(d))
+    assert nb > 0
+    for name in ("xb_new", "zb_new", "xb_tail", "zb_tail", "bias_b"):
+        keep = getattr(d, name)
+        setattr(d, name, None)
+        assert lib.csa_decode_step(C.byref(d), C.c_void_p(256), nb, None) == -1, name
+        assert lib.csa_decode_step_noalloc(C.byref(d), None) == -1, name
+        setattr(d, name, keep)
+    d.compressor = 2
+    assert lib.csa_decode_step(C.byref(d), C.c_void_p(256), nb, None) == -2
+    assert lib.csa_decode_step_workspace_size(C.byref(d)) == 0
 
 
 def test_decode_mxfp4_validation(lib):

@@ -1,6 +1,8 @@
 """GPU parity at the full sizes of the five workloads, in the launch configuration the bench
 times: every sequence of the decode workloads, and 376 sampled query rows of the chunked
 prefill (the oracle computes those one by one)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -26,6 +28,17 @@ def test_decode_workload_fullsize(cfg):
     check_step(case, ref, st, rings, out, idx)
 
 
+def test_decode_1m_overlapped_compressor():
+    """The 1M-context decode workload with the overlapped two-stream main compressor (the
+    bench's --compressor c4a line)."""
+    case = datagen.make_case(dataclasses.replace(datagen.CONFIGS[4], compressor="c4a"))
+    print("config 4 (c4a): inputs ready", flush=True)
+    gaps.enforce_decode(case)
+    _, st, rings, out, idx = run_step(case)
+    ref = pipeline.decode_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
 @pytest.mark.parametrize("cfg", [2, 4])
 def test_decode_workload_fullsize_mxfp4_keys(cfg):
     """The flat decode workloads with the indexer cache in MXFP4 (the bench's --idx-format
@@ -38,12 +51,14 @@ def test_decode_workload_fullsize_mxfp4_keys(cfg):
     check_step(case, ref, st, rings, out, idx)
 
 
-def test_decode_workload_fullsize_every_format_and_fusion():
+@pytest.mark.parametrize("compressor", ["single", "c4a"])
+def test_decode_workload_fullsize_every_format_and_fusion(compressor):
     """The 8 x 65,536-token decode workload with every production format and fusion at once:
     FP8 main cache, MXFP4 indexer keys, BF16 index scores, the queries' and the completed
     entry's RMSNorm + RoPE and the inverse RoPE on the output (the GPU quantises the caches;
-    the oracle holds their FP8 / MXFP4 values from its own encoders)."""
-    spec = datagen.CONFIGS[2]
+    the oracle holds their FP8 / MXFP4 values from its own encoders); with either main
+    compressor."""
+    spec = dataclasses.replace(datagen.CONFIGS[2], compressor=compressor)
     case, state = mxfp4_case(spec)
     state.update(fp8_case(case))
     case["score_format"] = "bf16"
@@ -140,7 +155,6 @@ def test_decode_1m_ragged_rows():
     """The 1M-context decode shape (262,144-entry caches, log-normal key norms) with ragged
     positions over [L/2, L): rows whose later scan items lie wholly or partly past the visible
     count, so the scan skips their tile loads; ids, outputs and state against the oracle."""
-    import dataclasses
     spec = dataclasses.replace(datagen.CONFIGS[4], case_id=7400, ragged=True)
     case = datagen.make_case(spec)
     pos = case["pos"].tolist()

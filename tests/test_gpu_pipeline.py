@@ -372,3 +372,44 @@ def test_decode_step_entry_norm_rope(spec, fp8):
     assert ref["kv_new"], "no sequence completes a block"
     _, st, rings, out, idx = run_step(case, state or None)
     check_step(case, ref, st, rings, out, idx)
+
+
+# The overlapped two-stream main compressor inside the step: the b stream's new row enters its
+# two-block ring, the entry a step completes pools its block's a rows with the previous block's
+# b rows (none for a sequence's first entry); the indexer keys keep the single stream.
+@pytest.mark.parametrize("spec,fmt", [
+    (datagen.CaseSpec(7170, "decode", B=5, L=24000, m=4, w_cap=256, ragged=True,
+                      compressor="c4a"), None),
+    (datagen.CaseSpec(7171, "decode", B=4, L=2000, m=4, w_cap=128, compressor="c4a"), None),
+    (datagen.CaseSpec(7172, "decode", B=2, L=4, e_cap=4096, m=4, w_cap=128,
+                      compressor="c4a"), None),
+    (datagen.CaseSpec(7173, "decode", B=3, L=40000, m=1, w_cap=128, block_size=8,
+                      max_blocks=512, n_attn=3, ragged=True, compressor="c4a"), None),
+    (datagen.CaseSpec(7174, "decode", B=4, L=4 * 50000, m=4, w_cap=128, ragged=True,
+                      compressor="c4a"), "mxfp4"),
+    (datagen.CaseSpec(7175, "decode", dtype="f32", B=3, L=6000, m=4, w_cap=128, ragged=True,
+                      compressor="c4a"), None),
+    (datagen.CaseSpec(7176, "decode", B=4, L=2 * 30000, m=2, w_cap=128, ragged=True,
+                      compressor="c4a"), "fp8_prep"),
+    (datagen.CaseSpec(7177, "decode", B=3, L=8 * 3000, m=8, w_cap=128, ragged=True,
+                      compressor="c4a"), None),
+], ids=["flat", "all_selected", "first_entry", "hier_three_calls", "mxfp4_keys",
+        "f32_separate_ingest", "fp8_cache_norm_rope", "m8_two_pass"])
+def test_decode_step_overlapped_compressor(spec, fmt):
+    if fmt == "mxfp4":
+        case, state = mxfp4_case(spec)
+    else:
+        case, state = datagen.make_case(spec), {}
+    if fmt == "fp8_prep":
+        state.update(fp8_case(case))
+        case["kv_gamma"] = (datagen.tensor(spec.case_id, 95, (spec.D,), spec.dtype, 0.3)
+                            + 1.0).to(case["x_new"].dtype)
+        case["kv_rope_dim"] = 64
+    gaps.enforce_decode(case)
+    ref = pipeline.decode_step(case)
+    assert ref["kv_new"], "no sequence completes a block"
+    step, st, rings, out, idx = run_step(case, state or None)
+    check_step(case, ref, st, rings, out, idx)
+    if spec.L == 2000:   # every entry selected: the new entry takes part in the attention
+        for b in range(spec.B):
+            assert (spec.L // spec.m - 1) in idx[b].tolist()
