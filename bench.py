@@ -126,6 +126,83 @@ def counter_traffic(idx_format="bf16"):
         return None
 
 
+def time_prefill_scan(scan, launches: int, warmup: int = 3):
+    """The prefill indexer scan alone (``scan``: a csa.IndexScores over the 4,096-query chunk,
+    the scan_prefill_kernel launch that csa_index_topk makes for these shapes): `launches`
+    calls, each between a pair of HIP events recorded on the stream the library launches on
+    (torch's current stream). Returns a roofline dict against the bf16 dense MFMA peak."""
+    import torch
+
+    import datagen
+    from sparse_long_context_csa_amd import accounting as acc
+
+    spec = datagen.CONFIGS[3]
+    for _ in range(warmup):
+        scan()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for a, b in evs:
+        a.record()
+        scan()
+        b.record()
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    pairs = acc.sum_visible(spec.L - spec.chunk, spec.L, spec.m, spec.entries)
+    flops = acc.prefill_indexer_flops(pairs, spec.H_I, spec.d_I)
+    avg = sum(us) / len(us)
+    tf = flops / (avg * 1e-6) / 1e12
+    return {"bound": "mfma", "kernel": "scan_prefill_kernel<12> (indexer scan, chunked prefill)",
+            "workload": datagen.WORKLOAD_NAMES[3], "achieved": round(tf, 1), "peak": 2500.0,
+            "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4), "flops": flops,
+            "visible_pairs": pairs, "avg_launch_us": round(avg, 1),
+            "launch_us_min_max": [round(min(us), 1), round(max(us), 1)],
+            "timing": f"HIP events on the launch stream around each of {launches} "
+                      "csa_index_scores calls (one scan_prefill_kernel launch each, the "
+                      "kernel and grid csa_index_topk runs for this chunk)"}
+
+
+def prefill_scan(dev):
+    """The chunked-prefill indexer inputs (drawn as for the prefill workload), the chunk's own
+    keys pooled into the cache, and a csa.IndexScores over them."""
+    import torch
+
+    import datagen
+    import sparse_long_context_csa_amd as csa
+
+    spec = datagen.CONFIGS[3]
+    p = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v)
+         for k, v in datagen.make_prefill_indexer(spec).items()}
+    e0 = (spec.L - spec.chunk) // spec.m
+    csa.compress(p["xi_chunk"], p["zi_chunk"], p["bias_i"], spec.m,
+                 out=p["k_idx"][:, e0:e0 + spec.chunk // spec.m],
+                 out_seq_stride=spec.entries * spec.d_I)
+    return csa.IndexScores(p["q_idx"], p["w"], p["k_idx"], p["q_pos"], spec.m,
+                           e_count=p["e_count"])
+
+
+def prefill_cpu_baseline(case, budget_s):
+    """The float64 oracle's chunked prefill (index, Top-K and attention of each query row over
+    the cache holding the chunk's entries), on the host cores, over evenly spread query rows
+    until about budget_s seconds of work; the chunk's pooling runs once before the clock."""
+    from oracle import pipeline
+    spec = case["spec"]
+    kv_c, ki_c = pipeline.prefill_entries(case)
+    per_call = 8
+    stride = 97    # coprime with the chunk: rows spread over its whole range
+    done, el, threads, vendor = timed_oracle(
+        lambda i: pipeline.prefill_rows(
+            case, [(0, (i * per_call + j) * stride % spec.chunk) for j in range(per_call)],
+            kv_c, ki_c), budget_s, 64)
+    rows = done * per_call
+    return {"value": rows / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "blas": vendor,
+            "sample": f"{rows} query rows of the 4,096-query chunk ({per_call} per call, spread "
+                      f"over the chunk), each index over every visible entry, Top-K and "
+                      f"attention, in {el:.1f} s, float64 NumPy, BLAS ({vendor}) on {threads} "
+                      f"threads; the chunk's entries pooled once before timing"}
+
+
 def bench_prefill(args):
     """Chunked prefill (4,096 queries at the end of a 131,072-token context): pool the
     chunk's 4,096 raw rows into 1,024 entries of both streams, then index + select and
@@ -211,6 +288,11 @@ def bench_prefill(args):
     flops = acc.prefill_indexer_flops(pairs, spec.H_I, spec.d_I)
     tf = flops / (ph[1] * 1e-3) / 1e12
     ms = wall * 1e3 / steps
+    # the scan kernel alone, over the same inputs (copy 0 of the cache, the chunk pooled)
+    scan = csa.IndexScores(g["q_idx"], g["w"], kis[0], g["q_pos"], spec.m, e_count=g["e_count"])
+    roof = time_prefill_scan(scan, launches=steps)
+    roof["traffic"] = None
+    del scan
     res = {
         "metric": "CSA chunked-prefill queries/sec (4,096 queries, 131,072 ctx)",
         "value": round(spec.chunk * steps / wall, 1), "unit": "queries/s", "n_gpus": 1,
@@ -219,9 +301,10 @@ def bench_prefill(args):
         "data": "synthetic",
         "config": {"workload": datagen.WORKLOAD_NAMES[3], "chunk": spec.chunk, "context": spec.L,
                    "entries": E, "top_k": spec.K, "window": spec.W},
-        "indexer": {"bound": "mfma", "flops": flops, "visible_pairs": pairs,
-                    "call_ms": round(ph[1], 4), "tflops_incl_select": round(tf, 1),
-                    "peak": 2500.0, "frac_incl_select": round(tf / 2500.0, 4)},
+        "roofline": roof,
+        "index_topk_call": {"flops": flops, "call_ms": round(ph[1], 4),
+                            "tflops_incl_select": round(tf, 1),
+                            "frac_incl_select": round(tf / 2500.0, 4)},
         "phases_ms": {"compress": round(ph[0], 4), "index_topk": round(ph[1], 4),
                       "sparse_attn": round(ph[2], 4)},
     }
@@ -235,6 +318,8 @@ def bench_prefill(args):
     if c4a:
         res["metric"] += ", overlapped two-stream compressor"
         res["config"]["compressor"] = "c4a"
+    if not args.no_cpu:
+        res["cpu_baseline"] = prefill_cpu_baseline(case, args.cpu_budget)
     print(json.dumps(res), flush=True)
 
 
@@ -389,6 +474,8 @@ def main():
     ap.add_argument("--scan-event-stride", type=int, default=8,
                     help="time the scan kernel of every n-th timed step with dispatch events")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-prefill-indexer", action="store_true",
+                    help="1M decode line: skip its chunked-prefill indexer sub-measurement")
     ap.add_argument("--graph", action="store_true",
                     help="replay the step from a captured HIP graph instead of launching it")
     ap.add_argument("--config", type=int, default=4, choices=(2, 3, 4, 5, 6, 7),
@@ -642,6 +729,9 @@ def main():
         res["selection_recall_vs_fp32"] = {"mean": round(float(np.mean(rec)), 5),
                                            "min": round(float(np.min(rec)), 5),
                                            "rows": spec.B}
+    if args.config == 4 and not args.no_prefill_indexer:
+        # the metric's MFMA share: the chunked-prefill indexer scan, timed in the same run
+        res["prefill_indexer"] = time_prefill_scan(prefill_scan(dev), launches=20)
     if not args.no_cpu:
         if mx:
             # the oracle's step with an MXFP4 cache (the new entry's key quantised); the cached

@@ -368,6 +368,27 @@ def make_prefill(spec: CaseSpec) -> dict:
     return out
 
 
+def make_prefill_indexer(spec: CaseSpec) -> dict:
+    """The indexer's share of ``make_prefill``'s inputs, drawn identically (same seeds, same
+    values): the indexer cache ``k_idx`` (the chunk's entries zero, to be pooled from
+    ``xi_chunk``/``zi_chunk`` with ``bias_i``), ``q_idx``, ``w``, ``q_pos`` and ``e_count``."""
+    B, m, dI, E, C = spec.B, spec.m, spec.d_I, spec.entries, spec.chunk
+    assert spec.kind == "prefill" and C % m == 0 and spec.L % m == 0
+    dt = spec.dtype
+    e0 = (spec.L - C) // m
+    ki = _rows(spec, T_KI, (B, E, dI), dI)
+    ki[:, e0:] = 0.0
+    out = {"spec": spec, "k_idx": to_storage(ki, dt)}
+    out["xi_chunk"] = to_storage(_u(spec, T_XI, (B, C, dI), dI), dt)
+    out["zi_chunk"] = to_storage(_u(spec, T_ZI, (B, C, dI), dI), dt)
+    out["bias_i"] = to_storage(_u(spec, T_BIAS_I, (m, dI), dI), dt)
+    out["q_pos"] = torch.arange(spec.L - C, spec.L, dtype=torch.int64).repeat(B, 1)
+    out["e_count"] = torch.full((B,), E, dtype=torch.int32)
+    out["q_idx"] = to_storage(_u(spec, T_QI, (B, C, spec.H_I, dI), dI), dt)
+    out["w"] = to_storage(_u(spec, T_W, (B, C, spec.H_I), spec.H_I), dt).float()
+    return out
+
+
 def make_tiny(spec: CaseSpec) -> dict:
     """The tiny fp32 forward: one sequence of L tokens, all L queries. Raw rows X double as
     the window rows (ring capacity L); the indexer keys are given per entry."""

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 13
+#define CSA_ABI_VERSION 14
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -201,6 +201,30 @@ int csa_index_topk(const void *q_idx, const float *w, const void *k_idx,
                    int32_t idx_heads, int32_t idx_dim, int32_t m, int32_t top_k,
                    int32_t *out_idx, float *out_score, float *scores_all, void *ws,
                    size_t ws_bytes, int32_t dtype, void *stream);
+
+/* ---------------------------------------------------------------------------------------
+ * csa_index_scores -- the lightning indexer's scores alone (csa_index_topk's scan, no
+ * selection).
+ *   [CoD "The Lightning Indexer": I(t,s) = sum_h w(t,h) * ReLU(q_I(t,h) . K_s); CoD "The
+ *   sliding window is not an optimisation": entry i is usable at t only if m*(i+1)-1 <= t;
+ *   CoD "The indexer is O(n), and that is the ceiling": the scan touches every visible entry.]
+ * For query row r = (s, i) at t = q_pos[s, i], n_vis as in csa_index_topk (no candidate list):
+ *   scores[r * score_stride + e] = I(t, e) in fp32 for 0 <= e < n_vis; the rest of the row
+ *   (e >= n_vis) is not written.
+ *   q_idx, w, k_idx, q_pos, e_count : as csa_index_topk
+ *   scores : f32, 16-byte aligned; score_stride >= e_cap and a multiple of 4 (else
+ *            CSA_ERR_SHAPE)
+ *   ws     : csa_index_scores_workspace_size(n_seq, n_q, e_cap) bytes (the scan's visible
+ *            counts and per-16-position maxima), not read before it is written
+ * The scan is the same kernel, grid and arithmetic as inside csa_index_topk for the same
+ * shapes, so the scores equal the ones that call ranks. Limits: as csa_index_topk.
+ * ------------------------------------------------------------------------------------- */
+size_t csa_index_scores_workspace_size(int64_t n_seq, int64_t n_q, int64_t e_cap);
+int csa_index_scores(const void *q_idx, const float *w, const void *k_idx,
+                     const int64_t *q_pos, const int32_t *e_count, int64_t n_seq, int64_t n_q,
+                     int64_t e_cap, int32_t idx_heads, int32_t idx_dim, int32_t m,
+                     float *scores, int64_t score_stride, void *ws, size_t ws_bytes,
+                     int32_t dtype, void *stream);
 
 /* ---------------------------------------------------------------------------------------
  * csa_index_blocks -- hierarchical pre-select: full scan -> block maxima -> pool.

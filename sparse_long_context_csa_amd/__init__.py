@@ -14,7 +14,7 @@ from . import _lib
 from ._events import HipEvents  # noqa: F401
 from ._lib import CsaError, DecodeDesc, check, lib  # noqa: F401
 
-__all__ = ["compress", "index_topk", "index_blocks", "sparse_attn", "DecodeStep", "CsaError",
+__all__ = ["compress", "index_topk", "index_scores", "IndexScores", "index_blocks", "sparse_attn", "DecodeStep", "CsaError",
            "lib"]
 
 
@@ -179,6 +179,42 @@ def index_topk(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor, q_pos:
     if want_all:
         res.append(all_s)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+class IndexScores:
+    """csa_index_scores over fixed inputs: builds the output rows (stride e_cap rounded up to a
+    multiple of 4 floats) and the workspace once; each call scores every visible entry of
+    every query row on the current stream. q_idx [n_seq,n_q,H_I,d_I], w [n_seq,n_q,H_I] f32,
+    k_idx [n_seq,e_cap,d_I], q_pos [n_seq,n_q] i64, optional e_count [n_seq] i32. ``scores``
+    is [n_seq, n_q, e_cap]: entries at or past a row's visible count are not written."""
+
+    def __init__(self, q_idx, w, k_idx, q_pos, m: int, e_count=None):
+        _dev(q_idx, "q_idx"); _dev(w, "w", torch.float32); _dev(k_idx, "k_idx", q_idx.dtype)
+        _dev(q_pos, "q_pos", torch.int64); _dev(e_count, "e_count", torch.int32)
+        self.args = (q_idx, w, k_idx, q_pos, e_count)
+        n_seq, n_q, H, d = q_idx.shape
+        e_cap = k_idx.shape[1]
+        self.shape = (n_seq, n_q, e_cap, H, d, m)
+        stride = (e_cap + 3) // 4 * 4
+        self.rows = torch.empty(n_seq * n_q, stride, dtype=torch.float32, device=q_idx.device)
+        self.scores = self.rows[:, :e_cap].view(n_seq, n_q, e_cap)
+        nb = lib().csa_index_scores_workspace_size(n_seq, n_q, e_cap)
+        self.ws = _workspace(nb, q_idx.device)
+
+    def __call__(self):
+        q_idx, w, k_idx, q_pos, e_count = self.args
+        n_seq, n_q, e_cap, H, d, m = self.shape
+        check("csa_index_scores", lib().csa_index_scores(
+            _p(q_idx), _p(w), _p(k_idx), _p(q_pos), _p(e_count), n_seq, n_q, e_cap, H, d, m,
+            _p(self.rows), self.rows.shape[1], _p(self.ws), self.ws.numel(), _dtype(q_idx),
+            _stream()))
+        return self.scores
+
+
+def index_scores(q_idx, w, k_idx, q_pos, m: int, e_count=None):
+    """csa_index_scores: every visible entry's index score, [n_seq, n_q, e_cap] f32 (entries at
+    or past a row's visible count are not written)."""
+    return IndexScores(q_idx, w, k_idx, q_pos, m, e_count)()
 
 
 def index_blocks(q_idx, w, k_idx, q_pos, m: int, block_size: int, max_blocks: int,

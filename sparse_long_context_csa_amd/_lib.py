@@ -55,6 +55,9 @@ SIGNATURES = {
     "csa_quantize_kv_fp8": (i32, [vp, vp, i64, i32, vp]),
     "csa_dequantize_kv_fp8": (i32, [vp, vp, i64, vp]),
     "csa_index_topk_workspace_size": (sz, [i64, i64, i64, i32]),
+    "csa_index_scores_workspace_size": (sz, [i64, i64, i64]),
+    "csa_index_scores": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, i64, vp, sz,
+                              i32, vp]),
     "csa_index_topk": (i32, [vp, vp, vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, i32, i32,
                              vp, vp, vp, vp, sz, i32, vp]),
     "csa_index_blocks_workspace_size": (sz, [i64, i64, i64, i32, i32, i32]),

@@ -59,6 +59,17 @@ TopkWs carve_topk(Carver& c, int64_t rows, int64_t n_keys, int32_t top_k, int64_
   return w;
 }
 
+// The scan's own workspace when its scores go to a caller buffer (csa_index_scores): visible
+// counts and per-16-position maxima; no selection scratch, no segments.
+TopkWs carve_scan_only(Carver& c, int64_t rows, int64_t n_keys) {
+  TopkWs w{};
+  w.gstride = round64(n_keys / 16 + 1);
+  w.gmax = c.take<uint32_t>(size_t(rows) * w.gstride * 4);
+  w.n_vis = c.take<int32_t>(size_t(rows) * 4);
+  w.count = c.take<int32_t>(size_t(rows) * 4);
+  return w;
+}
+
 // Segments of the decode scan for the select, when the scan is the bf16 64x128 decode kernel
 // over the whole cache (no candidate list) and rows are long; both the scan and the select
 // call this with the same arguments.
@@ -313,6 +324,35 @@ int csa_index_topk(const void* q_idx, const float* w, const void* k_idx, const i
     if (e != hipSuccess) return CSA_ERR_HIP;
   }
   return CSA_OK;
+}
+
+// ---------------------------------------------------------------------------------------
+size_t csa_index_scores_workspace_size(int64_t n_seq, int64_t n_q, int64_t e_cap) {
+  if (n_seq < 0 || n_q < 0 || e_cap < 1) return 0;
+  Carver c(nullptr);
+  carve_scan_only(c, n_seq * n_q, e_cap);
+  return c.off;
+}
+
+int csa_index_scores(const void* q_idx, const float* w, const void* k_idx, const int64_t* q_pos,
+                     const int32_t* e_count, int64_t n_seq, int64_t n_q, int64_t e_cap,
+                     int32_t idx_heads, int32_t idx_dim, int32_t m, float* scores,
+                     int64_t score_stride, void* ws, size_t ws_bytes, int32_t dtype,
+                     void* stream) {
+  int st = check_index_common(n_seq, n_q, e_cap, idx_heads, idx_dim, m, dtype);
+  if (st != CSA_OK) return st;
+  if (score_stride < e_cap || score_stride % 4 != 0) return CSA_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(scores) % 16 != 0) return CSA_ERR_SHAPE;
+  if (n_seq * n_q == 0) return CSA_OK;
+  if (!q_idx || !w || !k_idx || !q_pos || !scores) return CSA_ERR_NULL;
+  const size_t need = csa_index_scores_workspace_size(n_seq, n_q, e_cap);
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  Carver c(ws);
+  TopkWs tw = carve_scan_only(c, n_seq * n_q, e_cap);
+  tw.scores = scores;
+  tw.stride = score_stride;
+  return status_of(scan_rows(dtype, q_idx, w, k_idx, q_pos, e_count, nullptr, 0, n_seq, n_q,
+                             e_cap, idx_heads, idx_dim, m, tw, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------------------------------

@@ -40,7 +40,7 @@ def test_header_declares_the_calls():
         "csa_sparse_attn_workspace_size", "csa_sparse_attn", "csa_decode_step_workspace_size",
         "csa_decode_step", "csa_quantize_mxfp4", "csa_compress_c4a", "csa_norm_rope",
         "csa_quantize_kv_fp8", "csa_dequantize_kv_fp8", "csa_sparse_attn_fp8",
-        "csa_decode_step_noalloc"}
+        "csa_decode_step_noalloc", "csa_index_scores_workspace_size", "csa_index_scores"}
 
 
 def test_binding_covers_every_declared_function():
@@ -211,6 +211,24 @@ def test_kv_fp8_validation(lib):
     assert attn(D=256) == -4
     assert attn(dtype=9) == -3
     assert attn(kv=C.c_void_p(256 + 8)) == -2
+
+
+def test_index_scores_validation(lib):
+    ok = C.c_void_p(256)   # never dereferenced: every call below fails validation or is empty
+    nb = lib.csa_index_scores_workspace_size(2, 1, 1000)
+    assert nb > 0 and lib.csa_index_scores_workspace_size(2, 1, 0) == 0
+
+    def call(scores=ok, stride=1000, e_cap=1000, ws=ok, ws_bytes=nb, dtype=1, q=ok, n_seq=2):
+        return lib.csa_index_scores(q, ok, ok, ok, None, n_seq, 1, e_cap, 64, 128, 4, scores,
+                                    stride, ws, ws_bytes, dtype, None)
+    assert call(dtype=7) == -3
+    assert call(stride=996) == -2                   # below e_cap
+    assert call(stride=1002) == -2                  # not a multiple of 4
+    assert call(scores=C.c_void_p(256 + 4)) == -2   # rows not 16-byte aligned
+    assert call(q=None) == -1
+    assert call(ws_bytes=nb - 1) == -5
+    assert call(ws=None) == -5
+    assert call(n_seq=0) == 0
 
 
 def test_decode_validation(lib):

@@ -51,3 +51,12 @@ def test_config_table():
     assert datagen.CONFIGS[3].chunk == 4096 and datagen.CONFIGS[3].entries == 32768
     assert datagen.CONFIGS[2].entries == 16384 and datagen.CONFIGS[2].B == 8
     assert datagen.CONFIGS[1].dtype == "f32" and datagen.CONFIGS[1].entries == 512
+
+
+def test_prefill_indexer_inputs_equal_the_full_prefill_case():
+    spec = datagen.CaseSpec(931, "prefill", B=1, L=4096, m=4, w_cap=512, chunk=256, H_I=8,
+                            d_I=32, H=2, D=64)
+    full = datagen.make_prefill(spec)
+    part = datagen.make_prefill_indexer(spec)
+    for k in ("k_idx", "xi_chunk", "zi_chunk", "bias_i", "q_pos", "e_count", "q_idx", "w"):
+        assert torch.equal(part[k], full[k]), k

@@ -324,6 +324,42 @@ def test_index_generic_path(H, d, dtype):
     check_index(q, w, k, pos, 4, 64, dtype=dtype)
 
 
+# csa_index_scores: the scan alone, into caller rows; entries past the visible count untouched
+@pytest.mark.parametrize("B,Q,E,H,d,dtype,m,lo,hi,e_cap_at", [
+    (3, 1, 5000, 64, 128, "bf16", 4, 4 * 700, 4 * 5000, None),      # decode scan kernel
+    (2, 1, 70000, 64, 128, "bf16", 4, 4 * 60000, 4 * 70000, None),  # rows past the segment size
+    (1, 40, 3000, 64, 128, "bf16", 4, 4 * 3000 - 60, 4 * 3000, None),  # prefill scan kernel
+    (2, 3, 700, 16, 64, "bf16", 4, 4 * 100, 4 * 700, 350),          # generic kernel, e_count
+    (2, 2, 500, 4, 32, "f32", 1, -2, 500, None),                    # fp32, empty rows
+])
+def test_index_scores_call(B, Q, E, H, d, dtype, m, lo, hi, e_cap_at):
+    q, w, k, pos = index_case(B, Q, E, H, d, dtype, lo, hi, m=m, seed=21)
+    if B * Q > 1:
+        pos.view(-1)[-1] = m * E - 1                  # one row sees every entry
+    e_count = None
+    if e_cap_at is not None:
+        e_count = torch.full((B,), e_cap_at, dtype=torch.int32)
+    sc = csa.IndexScores(dev(q), dev(w), dev(k), dev(pos), m, e_count=dev(e_count))
+    sc.rows.fill_(float("nan"))                       # sentinel: must survive past n_vis
+    got = sc().cpu().numpy()
+    for b in range(B):
+        for i in range(Q):
+            t = int(pos[b, i])
+            n_vis = ocsa.n_visible(t, m, E if e_count is None else int(e_count[b]))
+            s = ocsa.index_scores(f64(q[b, i]), f64(w[b, i]), f64(k[b, :n_vis]))
+            A = ocsa.score_scale(f64(q[b, i]), f64(w[b, i]), f64(k[b, :n_vis]))
+            assert_scores(got[b, i, :n_vis], s, A, what=f"scores {(b, i)}")
+            assert np.all(np.isnan(got[b, i, n_vis:])), f"row {(b, i)} written past n_vis"
+    # the same kernel as inside csa_index_topk: its scores are bit-identical
+    if H == 64 and d == 128 and e_count is None:
+        _, alls = csa.index_topk(dev(q), dev(w), dev(k), dev(pos), m, 16, want_all=True)
+        alls = alls.cpu().numpy()
+        for b in range(B):
+            for i in range(Q):
+                n_vis = ocsa.n_visible(int(pos[b, i]), m, E)
+                assert np.array_equal(got[b, i, :n_vis], alls[b, i, :n_vis])
+
+
 def test_index_blocks_pool():
     B, E, bs, mb = 2, 6000, 8, 64
     q, w, k, pos = index_case(B, 1, E, 64, 128, "bf16", E - 5, E, m=1, seed=7)
