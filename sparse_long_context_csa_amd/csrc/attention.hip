@@ -15,8 +15,9 @@
 // head; those 8 rows are exactly the lane's K slots of the P.V product, so P goes from the
 // score registers to the A operand with no data movement. Online softmax in base 2.
 // Few query rows (decode): the row list is split over workgroups; partial (max, sum,
-// unnormalised output) go to the workspace and attn_combine_kernel merges them in split
-// order (deterministic). attn_generic_kernel covers fp32 and other head shapes.
+// unnormalised output, the output in bf16 to halve what is written and read back) go to the
+// workspace and attn_combine_kernel merges them in split order (deterministic).
+// attn_generic_kernel covers fp32 and other head shapes.
 #include <stdlib.h>
 
 #include "attn_core.hpp"
@@ -74,7 +75,7 @@ static int attn_splits(int64_t rows, int top_k, int window, int H, int D, int dt
 size_t attn_ws_bytes(int64_t rows, int H, int D, int top_k, int window, int dt) {
   const int ns = attn_splits(rows, top_k, window, H, D, dt);
   if (ns <= 1) return 0;
-  return size_t(rows) * ns * (kPartO + 2 * kAH) * 4;
+  return size_t(rows) * ns * (kPartO * 2 + kAH * 8);   // bf16 outputs, fp32 (max, sum)
 }
 
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnArgs a, int nsplit, int tiles_per_split) {
@@ -109,18 +110,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
   const int nt = (blockIdx.x & 7) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t rows = gridDim.y;
-  const float* base = reinterpret_cast<const float*>(a.ws);
-  const float2* ml = reinterpret_cast<const float2*>(base + rows * nsplit * kPartO) +
-                     r * nsplit * kAH;
-  const f32x4_t* part = reinterpret_cast<const f32x4_t*>(base + r * nsplit * kPartO) +
-                        (w * 32 + nt) * kWave + lane;
-  constexpr int64_t sstride = kPartO / 4;   // float4 per split
+  const float2* ml = part_ml(a.ws, rows * nsplit, r * nsplit);
+  const uint2* part = part_out(a.ws, r * nsplit) + (w * 32 + nt) * kWave + lane;
+  constexpr int64_t sstride = kPartO / 4;   // 8-byte cells per split
   // the first kSplitRegs partials load first, together with the (max, sum) pairs
   constexpr int kSplitRegs = 32;
-  f32x4_t v[kSplitRegs];
+  uint2 v[kSplitRegs];
 #pragma unroll
-  for (int sp = 0; sp < kSplitRegs; ++sp)
-    v[sp] = sp < nsplit ? part[sp * sstride] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < kSplitRegs; ++sp) v[sp] = sp < nsplit ? part[sp * sstride] : make_uint2(0u, 0u);
   for (int q = threadIdx.x; q < nsplit * 16; q += blockDim.x)
     mls[q >> 4][q & 15] = ml[(q >> 4) * kAH + 16 * w + (q & 15)];
   __syncthreads();
@@ -142,16 +139,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
   __syncthreads();
   const int g = lane >> 4, col = lane & 15;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int sp = 0; sp < kSplitRegs; ++sp)
-    if (sp < nsplit)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(v[sp][i], wgt[sp][4 * g + i], acc[i]);
-  for (int sp = kSplitRegs; sp < nsplit; ++sp) {
-    const f32x4_t x = part[sp * sstride];
+  auto add = [&](const uint2 c, int sp) {
+    const float x[4] = {bf16_to_f32(uint16_t(c.x & 0xffffu)), bf16_to_f32(uint16_t(c.x >> 16)),
+                        bf16_to_f32(uint16_t(c.y & 0xffffu)), bf16_to_f32(uint16_t(c.y >> 16))};
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = fmaf(x[i], wgt[sp][4 * g + i], acc[i]);
-  }
+  };
+#pragma unroll
+  for (int sp = 0; sp < kSplitRegs; ++sp)
+    if (sp < nsplit) add(v[sp], sp);
+  for (int sp = kSplitRegs; sp < nsplit; ++sp) add(part[sp * sstride], sp);
   uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (r * kAH + 16 * w + 4 * g) * kAD + nt * 16 + col;
   if (a.out_rope_dim > 0 && nt * 16 >= kAD - a.out_rope_dim) {   // uniform over the wave
     const int d = nt * 16 + col;

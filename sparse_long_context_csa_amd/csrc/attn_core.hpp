@@ -29,8 +29,30 @@ constexpr int kVtRow = 80;       // LDS bytes per dim of the transposed tile (64
 constexpr float kLazyMax = 8.f;  // log2 headroom of the running softmax maximum
 
 // Partials of split s of row r: the unnormalised output in the MFMA accumulator layout,
-// [wave][nt][lane] float4 (64 heads x 512 dims), then (max, sum) per head in base 2.
-constexpr int64_t kPartO = int64_t(kAH) * kAD;   // floats per (row, split)
+// [wave][nt][lane] 4 x bf16 (64 heads x 512 dims; each lane's 4 heads of one dim in 8 bytes),
+// then, after every split's outputs, (max, sum) per head in base 2 as fp32 pairs. The output
+// is rounded once to bf16 here; the maxima and sums stay fp32.
+constexpr int64_t kPartO = int64_t(kAH) * kAD;   // elements per (row, split)
+
+// two fp32 values rounded to bf16 (nearest even) by one v_cvt_pk_bf16_f32, low half first
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  bf16x2v_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint2 pack_bf16x4(const f32x4_t& v) {
+  return make_uint2(cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3]));
+}
+// the 8-byte output cell (wave, nt, lane) of partial rs, and the (max, sum) pairs of rs
+__device__ __forceinline__ uint2* part_out(void* ws, int64_t rs) {
+  return reinterpret_cast<uint2*>(ws) + rs * (kPartO / 4);
+}
+__device__ __forceinline__ float2* part_ml(void* ws, int64_t n_parts, int64_t rs) {
+  return reinterpret_cast<float2*>(reinterpret_cast<unsigned char*>(ws) + n_parts * kPartO * 2) +
+         rs * kAH;
+}
 
 
 struct AttnLds {
@@ -230,17 +252,12 @@ __device__ __forceinline__ void attn_split_mfma(const AttnArgs& a, AttnLds& L, i
       }
     }
   } else {
-    // partial in the accumulator layout (16-byte stores), then (max, sum) per head
+    // partial in the accumulator layout (8-byte stores), then (max, sum) per head
     const int64_t rs = r * nsplit + split;
-    f32x4_t* pp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.ws) + rs * kPartO) +
-                  wave * 32 * kWave + lane;
+    uint2* pp = part_out(a.ws, rs) + wave * 32 * kWave + lane;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) pp[nt * kWave] = O[nt];
-    if (g == 0) {
-      float2* ml = reinterpret_cast<float2*>(reinterpret_cast<float*>(a.ws) +
-                                             n_rows_total * nsplit * kPartO) + rs * kAH;
-      ml[head] = make_float2(m_run, l_run);
-    }
+    for (int nt = 0; nt < 32; ++nt) pp[nt * kWave] = pack_bf16x4(O[nt]);
+    if (g == 0) part_ml(a.ws, n_rows_total * nsplit, rs)[head] = make_float2(m_run, l_run);
   }
 }
 
@@ -502,15 +519,10 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
     }
   } else {
     const int64_t rs = r * nsplit + split;
-    f32x4_t* pp = reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.ws) + rs * kPartO) +
-                  wave * 32 * kWave + lane;
+    uint2* pp = part_out(a.ws, rs) + wave * 32 * kWave + lane;
 #pragma unroll
-    for (int nt = 0; nt < 32; ++nt) pp[nt * kWave] = O[nt];
-    if (g == 0) {
-      float2* ml = reinterpret_cast<float2*>(reinterpret_cast<float*>(a.ws) +
-                                             n_rows_total * nsplit * kPartO) + rs * kAH;
-      ml[head] = make_float2(m_run, l_run);
-    }
+    for (int nt = 0; nt < 32; ++nt) pp[nt * kWave] = pack_bf16x4(O[nt]);
+    if (g == 0) part_ml(a.ws, n_rows_total * nsplit, rs)[head] = make_float2(m_run, l_run);
   }
 }
 

@@ -18,12 +18,9 @@ __device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(
 __device__ __forceinline__ float bf16_hi(uint32_t two) { return __uint_as_float(two & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
-// Round to nearest even; NaN stays a quiet NaN.
+// Round to nearest even (the gfx950 conversion instruction); NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // f rounded to the nearest bf16 value (ties to even), as a float

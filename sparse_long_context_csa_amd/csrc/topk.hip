@@ -609,13 +609,16 @@ __device__ __forceinline__ uint32_t slice_flags(const SelArgs& a, int64_t r, int
                                                 int64_t n, int64_t lim, uint32_t T,
                                                 const float (&x)[kSliceItems],
                                                 uint32_t (&key)[kSliceItems]) {
+  // A candidate list's scan scores its invalid ids (-1, or past the row's visible count) -inf:
+  // only a position whose score is -inf needs its id read back to tell the two apart.
+  const uint32_t kninf = order_key(neg_inf());
   uint32_t flags = 0;
 #pragma unroll
   for (int i = 0; i < kSliceItems; ++i) {
     const int64_t p = q0 + i;
     key[i] = order_key(x[i]);
     bool ok = p < n && key[i] >= T;
-    if (ok) {
+    if (ok && key[i] <= kninf) {
       const int64_t id = a.ids ? int64_t(a.ids[r * a.id_stride + p]) : p;
       ok = id >= 0 && id < lim;
     }

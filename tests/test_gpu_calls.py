@@ -549,3 +549,30 @@ def test_attention_fp8_cache(B, Q, E, K, W, w_cap):
     ref = pipeline.sparse_attn(q, kv_vals, idx, win, w_cap, W, pos, sink, scale, "bf16")
     for (b, i), r in ref.items():
         assert_rows_close(f64(out[b, i]), r, 2e-2, f"attn fp8 {(b, i)}")
+
+
+def test_bf16_rounding_of_fp32_values():
+    """The fp32 -> bf16 rounding every kernel stores with (here through the FP8 entry's 64
+    bf16 channels of an fp32 input) is round-to-nearest-even on the bit pattern: exact ties
+    of both parities, the values one fp32 ulp either side of a tie, fp32 subnormals, the
+    largest finite values (rounding past the bf16 maximum gives inf) and signed zeros
+    against the oracle's rounding."""
+    from oracle import fp8 as of8
+    g = np.random.default_rng(43)
+    base = g.standard_normal(4096).astype(np.float32) * np.float32(2.0) ** g.integers(
+        -60, 60, 4096).astype(np.float32)
+    b = base.view(np.uint32) & np.uint32(0xffff0000)              # bf16-exact values
+    tie = (b | np.uint32(0x8000)).view(np.float32)                # halfway to the next one
+    vals = np.concatenate([
+        tie, (tie.view(np.uint32) - 1).view(np.float32), (tie.view(np.uint32) + 1).view(np.float32),
+        np.array([1e-39, -1e-39, 2.0 ** -130, 3 * 2.0 ** -134, 2.0 ** -149, 1.1754942e-38,
+                  3.3895314e38, -3.3895314e38, 3.4028235e38, 3.3961776e38, 0.0, -0.0],
+                 dtype=np.float32)])
+    n = (vals.size + 63) // 64
+    x = np.zeros((n, 512), np.float32)
+    x[:, 448:].flat[:vals.size] = vals
+    xt = torch.from_numpy(x)
+    got = csa.quantize_kv_fp8(dev(xt)).cpu().numpy()
+    want = of8.encode_entries(f64(xt))
+    bad = np.argwhere(got[:, 448:] != want[:, 448:])
+    assert bad.size == 0, f"first mismatch at {tuple(bad[0])}"
