@@ -206,3 +206,32 @@ def test_hca_decode_fullsize():
                         f64(case["z_tail"][b])), f64(case["bias"]), m)[0],
             np.abs(x).max(axis=0), f"HCA entry of seq {b}", m=m)
         assert_rows_close(f64(out[b, 0].cpu()), ref["out"][b][0], 2e-2, f"HCA seq {b}")
+
+
+@pytest.mark.parametrize("cfg", [2, 4, 5])
+def test_decode_scores_error_far_inside_the_gap(cfg):
+    """Every visible entry's fp32 index score (csa_index_scores, the stage-1 scan of the decode
+    workload) against the float64 score: the largest error, relative to the gap rule's scale
+    max(|a|, |b|, mean|S|) (a, b the scores ranked K and K + 1, or for the hierarchical
+    workload the block maxima ranked 2,048 and 2,049), stays far below half the rule's 1e-3
+    margin, so a row that passes the rule ranks the same way in fp32 as in float64."""
+    spec = datagen.CONFIGS[cfg]
+    case = datagen.make_case(spec)
+    q = case["q_idx"].unsqueeze(1).contiguous()
+    w = case["w"].unsqueeze(1).contiguous()
+    pos = case["pos"].view(-1, 1).contiguous()
+    got = csa.index_scores(dev(q), dev(w), dev(case["k_idx"]), dev(pos), spec.m).cpu().numpy()
+    worst = 0.0
+    for b in range(spec.B):
+        n = ocsa.n_visible(int(pos[b, 0]), spec.m, spec.entries)
+        s = ocsa.index_scores(f64(case["q_idx"][b]), f64(case["w"][b]), f64(case["k_idx"][b, :n]))
+        if spec.block_size:
+            ranked = np.sort(np.maximum.reduceat(s, np.arange(0, n, spec.block_size)))[::-1]
+            a_, b_ = ranked[spec.max_blocks - 1], ranked[spec.max_blocks]
+        else:
+            ranked = np.sort(s)[::-1]
+            a_, b_ = ranked[spec.K - 1], ranked[spec.K]
+        scale = max(abs(a_), abs(b_), np.abs(s).mean())
+        worst = max(worst, np.abs(got[b, 0, :n].astype(np.float64) - s).max() / scale)
+    print(f"config {cfg}: max |fp32 - exact| / gap scale = {worst:.3e}", flush=True)
+    assert worst < 1e-5
