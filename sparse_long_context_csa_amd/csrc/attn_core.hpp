@@ -392,9 +392,14 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
     }
   };
   const int ntiles = (nl + kTile - 1) / kTile;
+  // Two tiles or fewer (the decode splits): both go out at once and land before the first
+  // is computed, so the tile loop runs with no further wait, expansion or barrier.
+  const bool all_in = ntiles <= 2;
   if (ntiles > 0) issue(0, 0);
+  if (all_in && ntiles > 1) issue(1, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   expand(0);
+  if (all_in && ntiles > 1) expand(1);
   __syncthreads();
 
   const float sl2 = a.scale * kLog2e;
@@ -404,7 +409,7 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
   for (int nt = 0; nt < 32; ++nt) O[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < ntiles; ++t) {
     const int b = t & 1;
-    if (t + 1 < ntiles) issue(t + 1, b ^ 1);
+    if (!all_in && t + 1 < ntiles) issue(t + 1, b ^ 1);
     const unsigned char* kvs = L.kv[b];
     const int* rowok = L.rowok[b];
 
@@ -485,9 +490,11 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
       const bf16x8_t Vf = *reinterpret_cast<const bf16x8_t*>(v8);
       O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Pf, Vf, O[nt], 0, 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (t + 1 < ntiles) expand(b ^ 1);
-    __syncthreads();
+    if (!all_in) {   // uniform
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (t + 1 < ntiles) expand(b ^ 1);
+      __syncthreads();
+    }
   }
 
   if (nsplit == 1) {
