@@ -364,6 +364,30 @@ __device__ __forceinline__ uint2 row_bound(const SelArgs& a, SelShared& sh, int6
         }
       }
     }
+  } else if (f == 4 && G <= 16 * kSelThreads && !use_g) {
+    // four scores per group: group j is the float4 at 4 j (rows are 16-byte aligned); all of a
+    // thread's groups (at most 16) load at once, coalesced across the lanes
+    constexpr int kQ = 16;
+    float4 v[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int64_t j = tid + int64_t(q) * kSelThreads;
+      v[q] = j < G && 4 * j + 4 <= nb ? *reinterpret_cast<const float4*>(ssrc + 4 * j)
+                                      : make_float4(neg_inf(), neg_inf(), neg_inf(), neg_inf());
+    }
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int64_t j = tid + int64_t(q) * kSelThreads;
+      if (j >= G) continue;
+      uint32_t m;
+      if (4 * j + 4 <= nb) {
+        m = max(max(order_key(v[q].x), order_key(v[q].y)), max(order_key(v[q].z), order_key(v[q].w)));
+      } else {   // the row's partial last group
+        m = 0u;
+        for (int64_t p = 4 * j; p < nb; ++p) m = max(m, order_key(ssrc[p]));
+      }
+      note(j, m);
+    }
   } else {
     for (int64_t j = tid; j < G; j += kSelThreads) {
       const int64_t p0 = j * f;
@@ -396,6 +420,20 @@ __device__ __forceinline__ uint2 row_bound(const SelArgs& a, SelShared& sh, int6
   return make_uint2(kmin + (sh.res[0] << lo), kmax);
 }
 
+// first-digit layout of the select over candidates with keys in [kmin, kmax]
+struct Digit0 {
+  int lo, nbins;
+};
+__device__ __forceinline__ Digit0 digit0(uint32_t kmin, uint32_t kmax) {
+  const int bits = key_bits(kmax > kmin ? kmax - kmin : 0u);
+  const int w = bits < kDigit0 ? bits : kDigit0;
+  return Digit0{bits - w, 1 << w};
+}
+__device__ __forceinline__ uint32_t bin0(uint32_t k, uint32_t kmin, const Digit0& d0) {
+  const uint32_t b = (k > kmin ? k - kmin : 0u) >> d0.lo;
+  return b < uint32_t(d0.nbins) ? b : uint32_t(d0.nbins - 1);
+}
+
 // ---- the select --------------------------------------------------------------------------
 // Candidates in LDS (position order), more than K of them, first digit (14 bits at lo0 over
 // key - kmin) already histogrammed in sh.h0: thread t owns list items [t*L, t*L + L).
@@ -409,7 +447,7 @@ struct NeverUnsafe {
 template <typename Unsafe = NeverUnsafe>
 __device__ __forceinline__ bool select_list(const SelArgs& a, SelShared& sh, int64_t r, uint32_t total,
                             uint32_t kmin, int lo0, int nb0, Unsafe unsafe = Unsafe(),
-                            uint32_t* t_lb = nullptr) {
+                            uint32_t* t_lb = nullptr, bool build_h0 = false) {
   const int tid = threadIdx.x;
   const uint32_t K = a.K;
   const uint32_t L = (total + kSelThreads - 1) / kSelThreads;   // <= kListRun
@@ -418,6 +456,12 @@ __device__ __forceinline__ bool select_list(const SelArgs& a, SelShared& sh, int
   uint32_t k[kListRun];
 #pragma unroll
   for (int i = 0; i < kListRun; ++i) k[i] = uint32_t(i) < jn ? sh.list.lk[j0 + i] : 0u;
+  if (build_h0) {   // the first digit from this thread's run (sh.h0 / h0g clear beforehand)
+#pragma unroll
+    for (int i = 0; i < kListRun; ++i)
+      if (uint32_t(i) < jn) hist_add(sh.h0, sh.h0g, bin0(k[i], kmin, Digit0{lo0, nb0}));
+    __syncthreads();
+  }
   wave_find(sh, sh.h0, sh.h0g, nb0, K);
   Radix st = radix_first(sh, K, lo0);
   __syncthreads();
@@ -575,46 +619,32 @@ __device__ __forceinline__ void select_stream(const SelArgs& a, SelShared& sh, i
   pad_out(a, r, out_base);
 }
 
-// first-digit layout of the select over candidates with keys in [kmin, kmax]
-struct Digit0 {
-  int lo, nbins;
-};
-__device__ __forceinline__ Digit0 digit0(uint32_t kmin, uint32_t kmax) {
-  const int bits = key_bits(kmax > kmin ? kmax - kmin : 0u);
-  const int w = bits < kDigit0 ? bits : kDigit0;
-  return Digit0{bits - w, 1 << w};
-}
-__device__ __forceinline__ uint32_t bin0(uint32_t k, uint32_t kmin, const Digit0& d0) {
-  const uint32_t b = (k > kmin ? k - kmin : 0u) >> d0.lo;
-  return b < uint32_t(d0.nbins) ? b : uint32_t(d0.nbins - 1);
-}
-
-// load kSliceItems scores of positions q0.. (0 beyond n)
-__device__ __forceinline__ void load_slice(const float* sr, int64_t q0, int64_t n,
-                                           float (&x)[kSliceItems]) {
-  if (q0 + kSliceItems <= n) {
+// load N scores of positions q0.. (0 beyond n); N a multiple of 4
+template <int N = kSliceItems>
+__device__ __forceinline__ void load_slice(const float* sr, int64_t q0, int64_t n, float (&x)[N]) {
+  if (q0 + N <= n) {
 #pragma unroll
-    for (int v = 0; v < kSliceItems / 4; ++v) {
+    for (int v = 0; v < N / 4; ++v) {
       const float4 y = *reinterpret_cast<const float4*>(sr + q0 + 4 * v);
       x[4 * v] = y.x; x[4 * v + 1] = y.y; x[4 * v + 2] = y.z; x[4 * v + 3] = y.w;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kSliceItems; ++i) x[i] = q0 + i < n ? sr[q0 + i] : 0.f;
+    for (int i = 0; i < N; ++i) x[i] = q0 + i < n ? sr[q0 + i] : 0.f;
   }
 }
-
-// candidate flags of positions q0.. : valid and key >= T
+// candidate flags (bit i: position q0 + i is a valid id whose key reaches T) and order keys
+template <int N = kSliceItems>
 __device__ __forceinline__ uint32_t slice_flags(const SelArgs& a, int64_t r, int64_t q0,
                                                 int64_t n, int64_t lim, uint32_t T,
-                                                const float (&x)[kSliceItems],
-                                                uint32_t (&key)[kSliceItems]) {
+                                                const float (&x)[N], uint32_t (&key)[N]) {
+  static_assert(N <= 32, "flags are 32 bits");
   // A candidate list's scan scores its invalid ids (-1, or past the row's visible count) -inf:
   // only a position whose score is -inf needs its id read back to tell the two apart.
   const uint32_t kninf = order_key(neg_inf());
   uint32_t flags = 0;
 #pragma unroll
-  for (int i = 0; i < kSliceItems; ++i) {
+  for (int i = 0; i < N; ++i) {
     const int64_t p = q0 + i;
     key[i] = order_key(x[i]);
     bool ok = p < n && key[i] >= T;
@@ -627,14 +657,17 @@ __device__ __forceinline__ uint32_t slice_flags(const SelArgs& a, int64_t r, int
   return flags;
 }
 
-// One workgroup per row (rows of up to kRowMax positions): bound, candidates into the LDS
-// list tile by tile (first digit histogrammed on the way; the next tile's scores load while
-// this one is compacted), select.
+// Rows up to kRowMax: one workgroup per row. Thread t holds the kRun consecutive positions
+// [b + t kRun, + kRun) of each block of kRowBlock positions (the first block is loaded before
+// the bound is computed, so its loads overlap that); the candidates (keys at or above the
+// bound T, in position order) go to the LDS list with one prefix scan per block.
+constexpr int kRun = 32;
+constexpr int64_t kRowBlock = int64_t(kRun) * kSelThreads;
 __device__ __forceinline__ void select_row_body(const SelArgs& a, SelShared& sh, int64_t r, int64_t n) {
   const int tid = threadIdx.x;
   const float* sr = a.scores + r * a.stride;
-  float x[kSliceItems];
-  load_slice(sr, int64_t(tid) * kSliceItems, n, x);
+  float x[kRun];
+  load_slice<kRun>(sr, int64_t(tid) * kRun, n, x);
   clear_words(sh.h0, kBins0);
   clear_words(sh.h0g, kBins0 / kGroup);
   clear_words(sh.hb, kBinsB);
@@ -647,20 +680,19 @@ __device__ __forceinline__ void select_row_body(const SelArgs& a, SelShared& sh,
   const int64_t lim = row_limit(a, r);
   uint32_t total = 0;
   bool over = false;
-  for (int64_t t0 = 0; t0 < n; t0 += kSlice) {
-    const int64_t q0 = t0 + int64_t(tid) * kSliceItems;
-    uint32_t key[kSliceItems];
-    const uint32_t flags = slice_flags(a, r, q0, n, lim, T, x, key);
-    if (t0 + kSlice < n) load_slice(sr, q0 + kSlice, n, x);
+  for (int64_t b = 0; b < n; b += kRowBlock) {
+    const int64_t q0 = b + int64_t(tid) * kRun;
+    uint32_t key[kRun];
+    const uint32_t flags = slice_flags<kRun>(a, r, q0, n, lim, T, x, key);
+    if (b + kRowBlock < n) load_slice<kRun>(sr, q0 + kRowBlock, n, x);
     uint32_t tot;
     uint32_t off = total + excl_scan(__popc(flags), sh.wred, &tot);
     if (total + tot <= uint32_t(kListCap)) {
 #pragma unroll
-      for (int i = 0; i < kSliceItems; ++i)
+      for (int i = 0; i < kRun; ++i)
         if ((flags >> i) & 1u) {
           sh.list.lk[off] = key[i];
           sh.list.lp[off] = uint32_t(q0 + i);
-          hist_add(sh.h0, sh.h0g, bin0(key[i], T, d0));
           ++off;
         }
     } else {
@@ -671,7 +703,7 @@ __device__ __forceinline__ void select_row_body(const SelArgs& a, SelShared& sh,
   __syncthreads();
   if (over) select_stream(a, sh, r, n, T);
   else if (total <= a.K) select_all(a, sh, r, total);
-  else select_list(a, sh, r, total, T, d0.lo, d0.nbins);
+  else select_list(a, sh, r, total, T, d0.lo, d0.nbins, NeverUnsafe(), nullptr, true);
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_row_kernel(SelArgs a) {
