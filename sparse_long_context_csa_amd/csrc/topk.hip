@@ -281,6 +281,31 @@ __device__ __forceinline__ void pad_out(const SelArgs& a, int64_t r, uint32_t fr
   }
 }
 
+// The chosen items leave through LDS: each thread stages its items at their output slots
+// (position and key in sh.h0, whose histogram is no longer needed), then one pass writes the
+// K slots in order, each lane one consecutive slot (padding past nsel), so the global stores
+// coalesce instead of following each thread's scattered slots.
+constexpr int kMaxK = 2048;
+static_assert(2 * kMaxK <= kBins0, "output staging lives in the first-digit histogram");
+__device__ __forceinline__ void stage_out(SelShared& sh, uint32_t o, uint32_t pos, uint32_t key) {
+  sh.h0[o] = pos;
+  sh.h0[kMaxK + o] = key;
+}
+__device__ __forceinline__ void flush_out(const SelArgs& a, SelShared& sh, int64_t r,
+                                          uint32_t nsel) {
+  __syncthreads();
+  for (uint32_t k = threadIdx.x; k < a.K; k += kSelThreads) {
+    if (k < nsel) {
+      const uint32_t pos = sh.h0[k];
+      a.out_idx[r * a.out_stride + k] = a.ids ? a.ids[r * a.id_stride + pos] : int32_t(pos);
+      if (a.out_score) a.out_score[r * a.out_stride + k] = key_to_score(sh.h0[kMaxK + k]);
+    } else {
+      a.out_idx[r * a.out_stride + k] = -1;
+      if (a.out_score) a.out_score[r * a.out_stride + k] = neg_inf();
+    }
+  }
+}
+
 // block min / max / count through sh.red (initialised, and made visible, beforehand)
 __device__ __forceinline__ void red_add(SelShared& sh, uint32_t kmin, uint32_t kmax, uint32_t c) {
 #pragma unroll
@@ -507,10 +532,10 @@ __device__ __forceinline__ bool select_list(const SelArgs& a, SelShared& sh, int
 #pragma unroll
   for (int i = 0; i < kListRun; ++i)
     if ((sel >> i) & 1u) {
-      write_out(a, r, o, sh.list.lp[j0 + i], k[i]);
+      stage_out(sh, o, sh.list.lp[j0 + i], k[i]);
       ++o;
     }
-  pad_out(a, r, nsel);
+  flush_out(a, sh, r, nsel);
   return true;
 }
 
@@ -968,10 +993,10 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
 #pragma unroll
   for (int i = 0; i < kSegRun; ++i)
     if ((sel >> i) & 1u) {
-      write_out(a, r, o, pos[i], k[i]);
+      stage_out(sh, o, pos[i], k[i]);
       ++o;
     }
-  pad_out(a, r, nsel);
+  flush_out(a, sh, r, nsel);
 }
 
 // Long rows, step 1: one workgroup per slice computes the row's bound and keeps its slice's
