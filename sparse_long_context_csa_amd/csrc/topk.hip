@@ -933,7 +933,39 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
   // 3. radix select: P = prefix of the K-th key at shift lo, need = items of it to take
   seg_find(sh, sh.hb, 1 << (bits - lo), K);
   uint32_t P = sh.res[0], need = K - sh.res[1];
-  bool done = sh.res[2] == need;
+  const uint32_t in_bin = sh.res[2];
+  bool done = in_bin == need;
+  if (!done && lo > 0 && in_bin <= uint32_t(kWave)) {
+    // The K-th key's bin holds at most 64 items: rank them directly instead of further
+    // digits. The bin's keys go to sh.h0 (free until the output), wave 0 finds the need-th
+    // largest, and the select continues at full resolution (lo = 0).
+    if (tid == 0) sh.flag = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSegRun; ++i)
+      if (uint32_t(i) < jn && ((k[i] - kmin) >> lo) == P) sh.h0[atomicAdd(&sh.flag, 1u)] = k[i];
+    __syncthreads();
+    if (tid < kWave) {
+      const uint32_t mine = uint32_t(tid) < in_bin ? sh.h0[tid] : 0u;
+      uint32_t gt = 0, eq = 0;
+      for (uint32_t j = 0; j < in_bin; ++j) {
+        const uint32_t o = sh.h0[j];
+        gt += o > mine;
+        eq += o == mine;
+      }
+      // the key with gt < need <= gt + eq is the K-th; lanes holding it agree
+      if (uint32_t(tid) < in_bin && gt < need && need <= gt + eq) {
+        sh.res[0] = mine - kmin;
+        sh.res[1] = gt;
+        sh.res[2] = eq;
+      }
+    }
+    __syncthreads();
+    P = sh.res[0];
+    need -= sh.res[1];
+    done = sh.res[2] == need;
+    lo = 0;
+  }
   // with bf16-valued scores two different keys differ by at least 2^16 (their low 16 bits
   // depend only on the sign, and -0 reads as +0), so the bin at shift key_floor holds one key
 #pragma unroll 1
