@@ -222,6 +222,41 @@ __device__ __forceinline__ void wave_find(SelShared& sh, const uint32_t* h, cons
   __syncthreads();
 }
 
+// The K-th key's bin (prefix P at shift lo, in_bin items of which `need` are to be taken)
+// holds at most 64 items: rank them directly rather than by further digits. Each thread's
+// items of the bin go to tmp (LDS, 64 words free for the call), wave 0 finds the need-th
+// largest key X of the bin; returns (X - kmin, items of the bin above X, items equal to X)
+// for the select to continue at full key resolution. Ends with a barrier.
+template <int N>
+__device__ __forceinline__ uint3 rank_bin(SelShared& sh, uint32_t* tmp, const uint32_t (&k)[N],
+                                          uint32_t jn, uint32_t kmin, int lo, uint32_t P,
+                                          uint32_t in_bin, uint32_t need) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.flag = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (uint32_t(i) < jn && ((k[i] - kmin) >> lo) == P) tmp[atomicAdd(&sh.flag, 1u)] = k[i];
+  __syncthreads();
+  if (tid < kWave) {
+    const uint32_t mine = uint32_t(tid) < in_bin ? tmp[tid] : 0u;
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t j = 0; j < in_bin; ++j) {
+      const uint32_t o = tmp[j];
+      gt += o > mine;
+      eq += o == mine;
+    }
+    // the key with gt < need <= gt + eq is the K-th; lanes holding it agree
+    if (uint32_t(tid) < in_bin && gt < need && need <= gt + eq) {
+      sh.res[0] = mine - kmin;
+      sh.res[1] = gt;
+      sh.res[2] = eq;
+    }
+  }
+  __syncthreads();
+  return make_uint3(sh.res[0], sh.res[1], sh.res[2]);
+}
+
 // Radix state: items with ((key - kmin) >> lo) > P are taken, those equal to P too when
 // done, else the first `need` of them in position order.
 struct Radix {
@@ -489,7 +524,15 @@ __device__ __forceinline__ bool select_list(const SelArgs& a, SelShared& sh, int
   }
   wave_find(sh, sh.h0, sh.h0g, nb0, K);
   Radix st = radix_first(sh, K, lo0);
+  const uint32_t in_bin = sh.res[2];
   __syncthreads();
+  if (!st.done && st.lo > 0 && in_bin <= uint32_t(kWave)) {
+    const uint3 x = rank_bin(sh, sh.hb, k, jn, kmin, st.lo, st.P, in_bin, st.need);
+    st.P = x.x;
+    st.need -= x.y;
+    st.done = x.z == st.need;
+    st.lo = 0;
+  }
   radix_more(sh, [&](auto fn) {
 #pragma unroll
     for (int i = 0; i < kListRun; ++i)
@@ -936,34 +979,10 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
   const uint32_t in_bin = sh.res[2];
   bool done = in_bin == need;
   if (!done && lo > 0 && in_bin <= uint32_t(kWave)) {
-    // The K-th key's bin holds at most 64 items: rank them directly instead of further
-    // digits. The bin's keys go to sh.h0 (free until the output), wave 0 finds the need-th
-    // largest, and the select continues at full resolution (lo = 0).
-    if (tid == 0) sh.flag = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kSegRun; ++i)
-      if (uint32_t(i) < jn && ((k[i] - kmin) >> lo) == P) sh.h0[atomicAdd(&sh.flag, 1u)] = k[i];
-    __syncthreads();
-    if (tid < kWave) {
-      const uint32_t mine = uint32_t(tid) < in_bin ? sh.h0[tid] : 0u;
-      uint32_t gt = 0, eq = 0;
-      for (uint32_t j = 0; j < in_bin; ++j) {
-        const uint32_t o = sh.h0[j];
-        gt += o > mine;
-        eq += o == mine;
-      }
-      // the key with gt < need <= gt + eq is the K-th; lanes holding it agree
-      if (uint32_t(tid) < in_bin && gt < need && need <= gt + eq) {
-        sh.res[0] = mine - kmin;
-        sh.res[1] = gt;
-        sh.res[2] = eq;
-      }
-    }
-    __syncthreads();
-    P = sh.res[0];
-    need -= sh.res[1];
-    done = sh.res[2] == need;
+    const uint3 x = rank_bin(sh, sh.h0, k, jn, kmin, lo, P, in_bin, need);   // sh.h0 is free
+    P = x.x;
+    need -= x.y;
+    done = x.z == need;
     lo = 0;
   }
   // with bf16-valued scores two different keys differ by at least 2^16 (their low 16 bits
