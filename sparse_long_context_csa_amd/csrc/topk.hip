@@ -885,7 +885,10 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
   }
   for (int b = tid; b < kSegBins; b += kSelThreads) sh.hb[b] = 0u;
   red_init(sh);
-  if (tid == 0) sh.flag = 0u;
+  if (tid == 0) {
+    sh.flag = 0u;
+    sh.red[3] = 0u;   // the largest chunk threshold
+  }
   __syncthreads();
   bool rest = false;   // a chunk with entries past the fetched heads
 #pragma unroll
@@ -895,6 +898,17 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
   }
   if (over) atomicOr(&sh.flag, 1u);
   if (rest) atomicOr(&sh.flag, 2u);
+  {
+    uint32_t tq = 0u;
+#pragma unroll
+    for (int q = 0; q < kSegPerThread; ++q) tq = tau[q] > tq ? tau[q] : tq;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint32_t y = __shfl_xor(tq, o);
+      tq = y > tq ? y : tq;
+    }
+    if ((tid & 63) == 0) atomicMax(&sh.red[3], tq);
+  }
   red_add(sh, tmin, tmax, 0u);
   uint32_t total;
   uint32_t off = excl_scan(loc, sh.wred, &total);
@@ -909,6 +923,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
   // list keys are finite (above kninf) and reach their chunk's tau
   const uint32_t kmin = sh.red[0] > kninf ? sh.red[0] : kninf + 1u;
   const uint32_t kmax = sh.red[1] > kmin ? sh.red[1] : kmin;
+  const uint32_t tau_max = sh.red[3];
   const uint32_t flag = sh.flag;
   if ((flag & 1u) != 0u || total > uint32_t(kSegList)) {
     select_stream(a, sh, r, n, 0u);
@@ -959,11 +974,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
   __syncthreads();
   if (total <= K) {
     // the list is the row's Top-K only if every chunk kept all its valid positions
-#pragma unroll
-    for (int q = 0; q < kSegPerThread; ++q)
-      if (int64_t(tid) * kSegPerThread + q < nch && tau[q] > kninf + 1u) atomicOr(&sh.flag, 1u);
-    __syncthreads();
-    if (sh.flag != 0u) {
+    if (tau_max > kninf + 1u) {   // uniform
       select_stream(a, sh, r, n, 0u);
       return;
     }
@@ -1008,13 +1019,7 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
   }
   // 4. exactness: every chunk's tau at or below the K-th key's lower bound
   const uint32_t T = kmin + (P << lo);
-  if (tid == 0) sh.flag = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < kSegPerThread; ++q)
-    if (int64_t(tid) * kSegPerThread + q < nch && tau[q] > T) atomicOr(&sh.flag, 1u);
-  __syncthreads();
-  if (sh.flag != 0u) {
+  if (tau_max > T) {   // uniform
     select_stream(a, sh, r, n, T);
     return;
   }
