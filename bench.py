@@ -31,6 +31,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "CSA decode queries/sec at 1M ctx + achieved HBM GB/s and MFMA % of peak"
+# the quantised main-cache formats: bytes per entry, metric suffix, config description
+KV_ENTRY_BYTES = {"fp8": 576, "fp4": 288}
+KV_METRIC = {"fp8": ", FP8 main cache", "fp4": ", FP4 main cache"}
+KV_CONFIG = {"fp8": "fp8 (448 E4M3 + 64 bf16 channels, 576 B per entry)",
+             "fp4": "fp4 (512 E2M1 + an E4M3 scale per 16 channels, 288 B per entry)"}
 
 
 def log(*a):
@@ -358,12 +363,14 @@ def bench_hca(args):
     qp = pos.view(B, 1).to(dev)
     idx = torch.arange(E, dtype=torch.int32).repeat(B, 1, 1).contiguous().to(dev)
     outs = [torch.empty(B, 1, H, D, dtype=torch.bfloat16, device=dev) for _ in range(copies)]
-    fp8 = args.kv_format == "fp8"
-    if fp8:   # the cache as 576-byte FP8 entries; the pooled entry is quantised into it
+    fp8 = args.kv_format in ("fp8", "fp4")
+    quantize = csa.quantize_kv_fp8 if args.kv_format == "fp8" else csa.quantize_kv_fp4
+    e_bytes = KV_ENTRY_BYTES.get(args.kv_format, D * 2)
+    if fp8:   # the cache as FP8 / FP4 entries; the pooled entry is quantised into it
         for st in states:
-            st["kv"] = csa.quantize_kv_fp8(st["kv"])
+            st["kv"] = quantize(st["kv"])
             st["entry"] = torch.empty(B, 1, D, dtype=torch.bfloat16, device=dev)
-            st["entry8"] = torch.empty(B, 1, 576, dtype=torch.uint8, device=dev)
+            st["entry8"] = torch.empty(B, 1, e_bytes, dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
     def step(c, evs=None):
@@ -371,7 +378,7 @@ def bench_hca(args):
         if evs: evs[0].record()
         if fp8:
             csa.compress(st["x"], st["z"], bias, m, out=st["entry"])
-            csa.quantize_kv_fp8(st["entry"], out=st["entry8"])
+            quantize(st["entry"], out=st["entry8"])
             st["kv"][:, e_new:e_new + 1].copy_(st["entry8"])
         else:
             csa.compress(st["x"], st["z"], bias, m, out=st["kv"][:, e_new:], out_seq_stride=E * D)
@@ -396,7 +403,6 @@ def bench_hca(args):
         torch.cuda.synchronize()
         ph[0] += evs[0].elapsed_time(evs[1]) / n_prof
         ph[1] += evs[1].elapsed_time(evs[2]) / n_prof
-    e_bytes = 576 if fp8 else D * 2
     attn_bytes = B * (E * e_bytes + spec.W * D * 2) + 2 * B * H * D * 2 + B * E * 4 + H * 4
     comp_bytes = B * (2 * m * D * 2 + D * 2) + m * D * 2
     achieved = attn_bytes / (ph[1] * 1e-3) / 1e9
@@ -418,8 +424,8 @@ def bench_hca(args):
         "compress_bytes": comp_bytes,
     }
     if fp8:
-        res["metric"] += ", FP8 main cache"
-        res["config"]["kv_cache"] = "fp8 (448 E4M3 + 64 bf16 channels, 576 B per entry)"
+        res["metric"] += KV_METRIC[args.kv_format]
+        res["config"]["kv_cache"] = KV_CONFIG[args.kv_format]
     print(json.dumps(res), flush=True)
 
 
@@ -494,10 +500,11 @@ def main():
                          "channels (prepared in the selection launch), the completed entry's "
                          "RMSNorm and RoPE before it is stored, and the inverse RoPE on the "
                          "output fused into the attention's store (0: off)")
-    ap.add_argument("--kv-format", default="bf16", choices=("bf16", "fp8"),
+    ap.add_argument("--kv-format", default="bf16", choices=("bf16", "fp8", "fp4"),
                     help="main KV cache of the decode workloads (--config 2/4/5/6): bf16 "
-                         "entries, or 576-byte FP8 entries (csa_quantize_kv_fp8 of the same "
-                         "entries, made before the timed region)")
+                         "entries, 576-byte FP8 entries or 288-byte FP4 entries "
+                         "(csa_quantize_kv_fp8 / _fp4 of the same entries, made before the "
+                         "timed region)")
     ap.add_argument("--compressor", default="single", choices=("single", "c4a"),
                     help="main compressor: the single stream, or the overlapped two-stream "
                          "one (decode workloads 2/4/5: the main entries; chunked prefill, "
@@ -546,8 +553,9 @@ def main():
         codes, scales = csa.quantize_mxfp4(case["k_idx"].to(dev))
         torch.cuda.synchronize()
     kv8 = None
-    if args.kv_format == "fp8":
-        kv8 = csa.quantize_kv_fp8(case["kv"].to(dev))
+    if args.kv_format in ("fp8", "fp4"):
+        quantize = csa.quantize_kv_fp8 if args.kv_format == "fp8" else csa.quantize_kv_fp4
+        kv8 = quantize(case["kv"].to(dev))
         torch.cuda.synchronize()
     q_gammas = None
     kv_gamma = None
@@ -666,8 +674,8 @@ def main():
                                        pool=spec.block_size * spec.max_blocks,
                                        ring_write=datagen.ring_from_raw(spec),
                                        key_bytes=key_bytes,
-                                       entry_bytes=acc.FP8_ENTRY_BYTES if kv8 is not None
-                                       else None, c4a=c4a).total
+                                       entry_bytes=KV_ENTRY_BYTES.get(args.kv_format),
+                                       c4a=c4a).total
     achieved = scan_bytes / (scan_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
@@ -704,8 +712,8 @@ def main():
     if mx:
         res["metric"] += ", MXFP4 indexer keys"
     if kv8 is not None:
-        res["metric"] += ", FP8 main cache"
-        res["config"]["kv_cache"] = "fp8 (448 E4M3 + 64 bf16 channels, 576 B per entry)"
+        res["metric"] += KV_METRIC[args.kv_format]
+        res["config"]["kv_cache"] = KV_CONFIG[args.kv_format]
     if args.rope_dim:
         res["metric"] += (f", query and entry RMSNorm + RoPE and output inverse RoPE on the "
                           f"last {args.rope_dim} channels")
@@ -738,7 +746,7 @@ def main():
             # keys are scored as generated, which is the same work as scoring their MXFP4 values
             case["idx_format"] = "mxfp4"
         if kv8 is not None:
-            case["kv_format"] = "fp8"
+            case["kv_format"] = args.kv_format
         if args.rope_dim:
             # the same query, entry and window-row preparation and output inverse RoPE as the
             # GPU step

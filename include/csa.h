@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 14
+#define CSA_ABI_VERSION 15
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -167,6 +167,29 @@ int csa_quantize_mxfp4(const void *x, void *codes, void *scales, int64_t n_rows,
  * Device pointers; asynchronous on `stream`.
  * ------------------------------------------------------------------------------------- */
 #define CSA_KV_FP8_BYTES 576
+
+/* ---------------------------------------------------------------------------------------
+ * csa_quantize_kv_fp4 / csa_dequantize_kv_fp4 -- FP4 storage of main KV entries.
+ *   [B890 section 4, Cell 3 "FP4 range analysis": E2M1 elements with one E4M3 scale per 16
+ *   channels and no second-level global scale, 512 x 0.5 + 512 / 16 = 288 bytes per 512-channel
+ *   entry; V41 "FP4 main KV": the whole latent is quantised after RoPE, and attention
+ *   dequantises the cached values before it uses them.]
+ * Entry layout (CSA_KV_FP4_BYTES = 288): bytes 0..255 hold the E2M1 codes (sign, 2 exponent
+ * bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), channel 2i in the
+ * low nibble of byte i; byte 256 + g holds the E4M3 scale code of channels 16g .. 16g+15 (the
+ * E4M3 of csa_quantize_kv_fp8). Per block: the scale is the E4M3 value nearest to max|x| / 6,
+ * ties to the even code, past 448 to 448; a block whose scale is 0 stores all codes 0;
+ * otherwise each x / scale rounds to the nearest magnitude, ties to the even code, past 6 to 6,
+ * and a zero magnitude is code 0. A stored value (element x scale) is exactly a bf16 value.
+ *   quantize:   x T [n_rows, 512] (CSA_BF16 or CSA_F32, rounded directly) -> out uint8
+ *               [n_rows, 288] (16-byte aligned)
+ *   dequantize: in uint8 [n_rows, 288] (16-byte aligned) -> out bf16 [n_rows, 512] (16-byte
+ *               aligned; exact)
+ * Device pointers; asynchronous on `stream`.
+ * ------------------------------------------------------------------------------------- */
+#define CSA_KV_FP4_BYTES 288
+int csa_quantize_kv_fp4(const void *x, void *out, int64_t n_rows, int32_t dtype, void *stream);
+int csa_dequantize_kv_fp4(const void *in, void *out, int64_t n_rows, void *stream);
 int csa_quantize_kv_fp8(const void *x, void *out, int64_t n_rows, int32_t dtype, void *stream);
 int csa_dequantize_kv_fp8(const void *in, void *out, int64_t n_rows, void *stream);
 
@@ -296,6 +319,17 @@ int csa_sparse_attn_fp8(const void *q, const void *kv, const int32_t *idx, int32
                         int64_t e_cap, int32_t n_heads, int32_t head_dim, void *ws,
                         size_t ws_bytes, int32_t dtype, void *stream);
 
+/* csa_sparse_attn_fp4 -- csa_sparse_attn over an FP4 main cache: kv is uint8
+ * [n_seq, e_cap, 288] in csa_quantize_kv_fp4's layout (16-byte aligned) and each selected
+ * entry takes part at its exact value (element x scale); everything else as
+ * csa_sparse_attn_fp8 (same limits, same workspace).
+ *   [V41 "FP4 main KV": attention dequantises the cached values before using them.] */
+int csa_sparse_attn_fp4(const void *q, const void *kv, const int32_t *idx, int32_t top_k,
+                        const void *win, int32_t w_cap, int32_t window, const int64_t *q_pos,
+                        const float *sink, float scale, void *out, int64_t n_seq, int64_t n_q,
+                        int64_t e_cap, int32_t n_heads, int32_t head_dim, void *ws,
+                        size_t ws_bytes, int32_t dtype, void *stream);
+
 /* ---------------------------------------------------------------------------------------
  * csa_decode_step -- one new token per sequence through the whole hot path.
  *   [CoD "The compressor has two streams...", "The Lightning Indexer", "Attention sink",
@@ -338,6 +372,7 @@ int csa_sparse_attn_fp8(const void *q, const void *kv, const int32_t *idx, int32
 #define CSA_SCORE_BF16 1  /* rank the scores rounded to bf16                               */
 #define CSA_KV_DTYPE 0    /* csa_decode_desc.kv_format: main entries in the step's dtype      */
 #define CSA_KV_FP8 1      /* main entries as 576-byte FP8 entries (csa_quantize_kv_fp8)       */
+#define CSA_KV_FP4 2      /* main entries as 288-byte FP4 entries (csa_quantize_kv_fp4)       */
 #define CSA_COMP_SINGLE 0 /* csa_decode_desc.compressor: one main stream (csa_compress)        */
 #define CSA_COMP_C4A 1    /* two overlapped main streams (csa_compress_c4a)                    */
 
@@ -417,9 +452,11 @@ typedef struct csa_decode_desc {
    * them in csa_quantize_kv_fp8's form, kv = uint8 [n_seq, e_cap, 576] (16-byte aligned): the
    * entry a step completes is pooled, rounded to T and stored as an FP8 entry, and the
    * attention reads every selected entry at its exact value. Needs T = bf16, n_heads 64 and
-   * dim 512; otherwise CSA_ERR_UNSUPPORTED.
+   * dim 512; otherwise CSA_ERR_UNSUPPORTED. CSA_KV_FP4 does the same with csa_quantize_kv_fp4's
+   * form, kv = uint8 [n_seq, e_cap, 288] (16-byte aligned), under the same conditions.
    *   [CoD "What the cache costs, checked four ways": 448 FP8 + 64 bf16 rotary dims =
-   *   576 bytes per entry.] */
+   *   576 bytes per entry; B890 section 4: E2M1 + one E4M3 scale per 16 channels = 288
+   *   bytes per entry.] */
   int32_t kv_format;
   /* The key/value rows a step stores: kv_gamma (T [dim]) or NULL applies the per-head RMSNorm
    * (eps 1e-6) to the pooled entry; kv_rope_dim > 0 then turns its last kv_rope_dim channels by

@@ -10,7 +10,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import csa, fp8, mx
+from . import csa, fp8, kv_fp4, mx
 
 
 def f64(a) -> np.ndarray:
@@ -153,6 +153,16 @@ def kv_row_prepared(case: dict) -> bool:
     return case.get("kv_gamma") is not None or bool(case.get("kv_rope_dim"))
 
 
+def cached_main_entry(v, kv_format):
+    """The value a main cache in kv_format ("fp8", "fp4", or None for the path's dtype) holds
+    for an entry v already rounded to that dtype."""
+    if kv_format == "fp8":
+        return fp8.cached_entries(v)
+    if kv_format == "fp4":
+        return kv_fp4.cached_entries(v)
+    return v
+
+
 def decode_step(case: dict, seqs=None) -> dict:
     """The fused decode step for one new token per sequence (oracle side).
 
@@ -168,8 +178,9 @@ def decode_step(case: dict, seqs=None) -> dict:
     case["out_rope_dim"] > 0 every output head's last channels are turned back by RoPE at -t
     ([CoD] "Key and value are the same vector") before the store; case["q_gamma"] (per call, or
     None) and case["q_rope_dim"] prepare each call's query (RMSNorm, RoPE at +t) first. With
-    case["kv_format"] == "fp8", case["kv"] holds the values of an FP8 main cache (576-byte
-    entries, oracle/fp8.py) and the new entry is attended at its cached value. case["kv_gamma"]
+    case["kv_format"] == "fp8" (or "fp4"), case["kv"] holds the values of an FP8 main cache
+    (576-byte entries, oracle/fp8.py; or 288-byte FP4 entries, oracle/kv_fp4.py) and the new
+    entry is attended at its cached value. case["kv_gamma"]
     and case["kv_rope_dim"] give the new entry its per-head RMSNorm and RoPE (at t, the position
     of the newest token it pools) before it is stored (rounded once), and the new window row
     the same at its position t (``prepare_kv_row``). With case["compressor"] == "c4a" the main
@@ -252,8 +263,7 @@ def decode_step(case: dict, seqs=None) -> dict:
         sel = ids[ids >= 0]
         kv_rows = take_rows(case["kv"][b], sel) if sel.size else np.zeros((0, spec.D))
         if new_e is not None:
-            kv_rows[sel == new_e] = (fp8.cached_entries(res["kv_new"][b])
-                                     if case.get("kv_format") == "fp8" else res["kv_new"][b])
+            kv_rows[sel == new_e] = cached_main_entry(res["kv_new"][b], case.get("kv_format"))
         outs = []
         for c in range(spec.n_attn):
             ring = f64(case["rings"][c][b]).copy()

@@ -149,6 +149,44 @@ def dequantize_kv_fp8(e: torch.Tensor, out: torch.Tensor | None = None) -> torch
     return out
 
 
+def quantize_kv_fp4(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """csa_quantize_kv_fp4: entries x [..., 512] -> FP4 entries uint8 [..., 288]."""
+    _dev(x, "x")
+    if x.shape[-1] != 512:
+        raise ValueError("FP4 entries are 512 channels wide")
+    n_rows = x.numel() // 512
+    if out is None:
+        out = torch.empty(*x.shape[:-1], _lib.KV_FP4_BYTES, dtype=torch.uint8, device=x.device)
+    _dev(out, "out", torch.uint8)
+    check("csa_quantize_kv_fp4", lib().csa_quantize_kv_fp4(_p(x), _p(out), n_rows, _dtype(x),
+                                                           _stream()))
+    return out
+
+
+def dequantize_kv_fp4(e: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """csa_dequantize_kv_fp4: FP4 entries uint8 [..., 288] -> bf16 [..., 512]."""
+    _dev(e, "e", torch.uint8)
+    if e.shape[-1] != _lib.KV_FP4_BYTES:
+        raise ValueError("FP4 entries are 288 bytes")
+    n_rows = e.numel() // _lib.KV_FP4_BYTES
+    if out is None:
+        out = torch.empty(*e.shape[:-1], 512, dtype=torch.bfloat16, device=e.device)
+    _dev(out, "out", torch.bfloat16)
+    check("csa_dequantize_kv_fp4", lib().csa_dequantize_kv_fp4(_p(e), _p(out), n_rows, _stream()))
+    return out
+
+
+def _kv_entry_format(kv) -> int:
+    """KV_DTYPE, or the quantised format a uint8 kv holds, told by its entry width."""
+    if kv is None or kv.dtype != torch.uint8:
+        return _lib.KV_DTYPE
+    if kv.shape[-1] == _lib.KV_FP8_BYTES:
+        return _lib.KV_FP8
+    if kv.shape[-1] == _lib.KV_FP4_BYTES:
+        return _lib.KV_FP4
+    raise ValueError("a uint8 kv holds 576-byte FP8 or 288-byte FP4 entries")
+
+
 def index_topk(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor, q_pos: torch.Tensor,
                m: int, top_k: int, e_count: torch.Tensor | None = None,
                cand: torch.Tensor | None = None, want_scores: bool = False,
@@ -241,8 +279,10 @@ def sparse_attn(q, kv, idx, win, w_cap: int, window: int, q_pos, sink, scale: fl
                 out=None) -> torch.Tensor:
     """csa_sparse_attn. q [n_seq,n_q,H,D], kv [n_seq,e_cap,D], idx [n_seq,n_q,top_k] i32 or
     None, win [n_seq,w_cap,D] or None, q_pos [n_seq,n_q] i64, sink [H] f32 or None. A uint8 kv
-    [n_seq,e_cap,576] is an FP8 main cache (quantize_kv_fp8's entries): csa_sparse_attn_fp8."""
-    kv8 = kv is not None and kv.dtype == torch.uint8
+    [n_seq,e_cap,576] is an FP8 main cache (quantize_kv_fp8's entries): csa_sparse_attn_fp8; a
+    uint8 kv [n_seq,e_cap,288] an FP4 one (quantize_kv_fp4's entries): csa_sparse_attn_fp4."""
+    fmt = _kv_entry_format(kv)
+    kv8 = fmt != _lib.KV_DTYPE
     _dev(q, "q"); _dev(kv, "kv", torch.uint8 if kv8 else q.dtype); _dev(idx, "idx", torch.int32)
     _dev(win, "win", q.dtype); _dev(q_pos, "q_pos", torch.int64); _dev(sink, "sink", torch.float32)
     n_seq, n_q, H, D = q.shape
@@ -252,7 +292,8 @@ def sparse_attn(q, kv, idx, win, w_cap: int, window: int, q_pos, sink, scale: fl
         out = torch.empty_like(q)
     nb = lib().csa_sparse_attn_workspace_size(n_seq, n_q, H, D, top_k, window)
     ws = _workspace(nb, q.device) if nb else None
-    name = "csa_sparse_attn_fp8" if kv8 else "csa_sparse_attn"
+    name = {_lib.KV_DTYPE: "csa_sparse_attn", _lib.KV_FP8: "csa_sparse_attn_fp8",
+            _lib.KV_FP4: "csa_sparse_attn_fp4"}[fmt]
     check(name, getattr(lib(), name)(
         _p(q), _p(kv), _p(idx), top_k, _p(win), w_cap, window, _p(q_pos), _p(sink), float(scale),
         _p(out), n_seq, n_q, e_cap, H, D, _p(ws), 0 if ws is None else ws.numel(), _dtype(q),
@@ -274,7 +315,8 @@ class DecodeStep:
     out_rope_dim channels of every output head, in the attention's output store. q_gamma (a
     list of [dim] tensors or None per call) and q_rope_dim prepare each call's query (RMSNorm,
     RoPE at +pos) in the selection launch. A uint8 kv [n_seq, e_cap, 576] is an FP8 main
-    cache (quantize_kv_fp8's entries; kv_format CSA_KV_FP8). kv_gamma ([dim] or None) and
+    cache (quantize_kv_fp8's entries; kv_format CSA_KV_FP8), a uint8 kv [n_seq, e_cap, 288] an
+    FP4 one (quantize_kv_fp4's entries; CSA_KV_FP4). kv_gamma ([dim] or None) and
     kv_rope_dim give the entry a step completes its RMSNorm and RoPE at pos before it is
     stored. compressor="c4a" pools the main entries with the overlapped two-stream compressor:
     x_new, z_new, x_tail, z_tail and bias are then its a stream, and xb_new, zb_new ([n_seq,
@@ -290,7 +332,8 @@ class DecodeStep:
                  compressor: str = "single", no_alloc: bool = False, **t):
         self.t = t
         kv = _dev(t["kv"], "kv")
-        kv8 = kv.dtype == torch.uint8
+        kv_fmt = _kv_entry_format(kv)
+        kv8 = kv_fmt != _lib.KV_DTYPE
         dt = _dev(t["x_new"], "x_new").dtype if kv8 else kv.dtype
         mx = t.get("k_idx_scale") is not None
         for k in ("x_new", "z_new", "xi_new", "zi_new", "x_tail", "z_tail", "xi_tail",
@@ -307,8 +350,6 @@ class DecodeStep:
         sinks += [None] * (n_attn - len(sinks))
         n_seq, e_cap, dim = kv.shape
         if kv8:
-            if dim != _lib.KV_FP8_BYTES:
-                raise ValueError("an FP8 kv holds 576-byte entries")
             dim = 512
         H = qs[0].shape[1]
         idx_heads, idx_dim = t["q_idx"].shape[1], t["q_idx"].shape[2]
@@ -353,7 +394,7 @@ class DecodeStep:
         for c, gq in enumerate(self.q_gamma[:n_attn]):
             if gq is not None:
                 d.q_gamma[c] = _dev(gq, "q_gamma", dt).data_ptr()
-        d.kv_format = _lib.KV_FP8 if kv8 else _lib.KV_DTYPE
+        d.kv_format = kv_fmt
         self.kv_gamma = kv_gamma   # the descriptor holds its address
         if kv_gamma is not None:
             d.kv_gamma = _dev(kv_gamma, "kv_gamma", dt).data_ptr()

@@ -14,8 +14,9 @@ MAX_ATTN = 4
 DECODE_EVENTS = 5
 IDX_DTYPE, IDX_MXFP4 = 0, 1
 SCORE_F32, SCORE_BF16 = 0, 1
-KV_DTYPE, KV_FP8 = 0, 1
+KV_DTYPE, KV_FP8, KV_FP4 = 0, 1, 2
 KV_FP8_BYTES = 576
+KV_FP4_BYTES = 288
 NOALLOC_SCRATCH_BYTES = 32 << 20
 NR_NORM, NR_ROPE, NR_INVERSE = 1, 2, 4
 COMP_SINGLE, COMP_C4A = 0, 1
@@ -54,6 +55,8 @@ SIGNATURES = {
     "csa_quantize_mxfp4": (i32, [vp, vp, vp, i64, i32, i32, vp]),
     "csa_quantize_kv_fp8": (i32, [vp, vp, i64, i32, vp]),
     "csa_dequantize_kv_fp8": (i32, [vp, vp, i64, vp]),
+    "csa_quantize_kv_fp4": (i32, [vp, vp, i64, i32, vp]),
+    "csa_dequantize_kv_fp4": (i32, [vp, vp, i64, vp]),
     "csa_index_topk_workspace_size": (sz, [i64, i64, i64, i32]),
     "csa_index_scores_workspace_size": (sz, [i64, i64, i64]),
     "csa_index_scores": (i32, [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, i64, vp, sz,
@@ -67,6 +70,8 @@ SIGNATURES = {
     "csa_sparse_attn": (i32, [vp, vp, vp, i32, vp, i32, i32, vp, vp, f32, vp, i64, i64, i64,
                               i32, i32, vp, sz, i32, vp]),
     "csa_sparse_attn_fp8": (i32, [vp, vp, vp, i32, vp, i32, i32, vp, vp, f32, vp, i64, i64,
+                                  i64, i32, i32, vp, sz, i32, vp]),
+    "csa_sparse_attn_fp4": (i32, [vp, vp, vp, i32, vp, i32, i32, vp, vp, f32, vp, i64, i64,
                                   i64, i32, i32, vp, sz, i32, vp]),
     "csa_decode_step_workspace_size": (sz, [C.POINTER(DecodeDesc)]),
     "csa_decode_step": (i32, [C.POINTER(DecodeDesc), vp, sz, vp]),

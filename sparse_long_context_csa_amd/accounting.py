@@ -63,7 +63,8 @@ def decode_step_bytes(B: int, n_vis: int, m: int, D: int, H: int, H_I: int, d_I:
     visible entries (all sequences at a block boundary, so one entry is pooled per stream).
     pool > 0: hierarchical (stage-1 scan of n_vis keys, then ``pool`` rescored keys).
     key_bytes: bytes of one cached indexer key (default d_I * elt; MXFP4: mxfp4_key_bytes).
-    entry_bytes: bytes of one cached main entry (default D * elt; FP8: FP8_ENTRY_BYTES).
+    entry_bytes: bytes of one cached main entry (default D * elt; FP8: FP8_ENTRY_BYTES; FP4:
+    FP4_ENTRY_BYTES).
     c4a: the overlapped main compressor adds its b stream: the new b row (x and z) read and
     written to its ring, the previous block's m b rows read, and its bias."""
     kb = d_I * elt if key_bytes is None else key_bytes
@@ -86,6 +87,9 @@ def decode_step_bytes(B: int, n_vis: int, m: int, D: int, H: int, H_I: int, d_I:
 
 # "What the cache costs, checked four ways": 64 bf16 rotary dims + 448 FP8 dims per entry
 FP8_ENTRY_BYTES = 64 * 2 + 448
+# "DeepSeek-V4.1-Flash's KV-Cache Compression, Checked Down to the Byte", section 4: 512 E2M1
+# elements + one E4M3 scale byte per 16 channels
+FP4_ENTRY_BYTES = 512 // 2 + 512 // 16
 
 
 def mxfp4_key_bytes(d_I: int) -> int:

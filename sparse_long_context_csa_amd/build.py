@@ -26,7 +26,7 @@ HIPFLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 SOURCES = ["compress.hip", "index_scan.hip", "index_prefill.hip", "topk.hip", "attention.hip", "norm_rope.hip",
-           "mxfp4.hip", "kv_fp8.hip", "api.hip"]
+           "mxfp4.hip", "kv_fp8.hip", "kv_fp4.hip", "api.hip"]
 
 
 def hipcc() -> str:

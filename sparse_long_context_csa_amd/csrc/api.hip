@@ -285,6 +285,24 @@ int csa_dequantize_kv_fp8(const void* in, void* out, int64_t n_rows, void* strea
   return status_of(launch_dequantize_kv_fp8(in, out, n_rows, static_cast<hipStream_t>(stream)));
 }
 
+int csa_quantize_kv_fp4(const void* x, void* out, int64_t n_rows, int32_t dtype, void* stream) {
+  if (!dtype_ok(dtype)) return CSA_ERR_DTYPE;
+  if (n_rows < 0) return CSA_ERR_SHAPE;
+  if (n_rows == 0) return CSA_OK;
+  if (!x || !out) return CSA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return CSA_ERR_SHAPE;
+  return status_of(launch_quantize_kv_fp4(dtype, x, out, n_rows, static_cast<hipStream_t>(stream)));
+}
+
+int csa_dequantize_kv_fp4(const void* in, void* out, int64_t n_rows, void* stream) {
+  if (n_rows < 0) return CSA_ERR_SHAPE;
+  if (n_rows == 0) return CSA_OK;
+  if (!in || !out) return CSA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(in) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
+    return CSA_ERR_SHAPE;
+  return status_of(launch_dequantize_kv_fp4(in, out, n_rows, static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------------------------------
 size_t csa_index_topk_workspace_size(int64_t n_seq, int64_t n_q, int64_t n_keys, int32_t top_k) {
   if (n_seq < 0 || n_q < 0 || n_keys < 0 || top_k < 1) return 0;
@@ -411,10 +429,10 @@ static int sparse_attn_impl(const void* q, const void* kv, const int32_t* idx, i
                             const int64_t* q_pos, const float* sink, float scale, void* out,
                             int64_t n_seq, int64_t n_q, int64_t e_cap, int32_t n_heads,
                             int32_t head_dim, void* ws, size_t ws_bytes, int32_t dtype,
-                            bool kv_fp8, void* stream) {
+                            int kv_fmt, void* stream) {
   int st = check_attn(n_seq, n_q, e_cap, n_heads, head_dim, top_k, w_cap, window, dtype);
   if (st != CSA_OK) return st;
-  if (kv_fp8) {
+  if (kv_fmt != kKvPlain) {
     if (dtype != CSA_BF16 || n_heads != 64 || head_dim != 512) return CSA_ERR_UNSUPPORTED;
     if (reinterpret_cast<uintptr_t>(kv) % 16 != 0) return CSA_ERR_SHAPE;
   }
@@ -428,7 +446,7 @@ static int sparse_attn_impl(const void* q, const void* kv, const int32_t* idx, i
   a.dt = dtype; a.q = q; a.kv = kv; a.idx = idx; a.top_k = top_k; a.win = win; a.w_cap = w_cap;
   a.window = window; a.q_pos = q_pos; a.sink = sink; a.scale = scale; a.out = out;
   a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap; a.H = n_heads; a.D = head_dim; a.ws = ws;
-  a.kv_fp8 = kv_fp8 ? 1 : 0;
+  a.kv_fmt = kv_fmt;
   return status_of(launch_attn(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -438,7 +456,7 @@ int csa_sparse_attn(const void* q, const void* kv, const int32_t* idx, int32_t t
                     int64_t e_cap, int32_t n_heads, int32_t head_dim, void* ws, size_t ws_bytes,
                     int32_t dtype, void* stream) {
   return sparse_attn_impl(q, kv, idx, top_k, win, w_cap, window, q_pos, sink, scale, out, n_seq,
-                          n_q, e_cap, n_heads, head_dim, ws, ws_bytes, dtype, false, stream);
+                          n_q, e_cap, n_heads, head_dim, ws, ws_bytes, dtype, kKvPlain, stream);
 }
 
 int csa_sparse_attn_fp8(const void* q, const void* kv, const int32_t* idx, int32_t top_k,
@@ -447,7 +465,16 @@ int csa_sparse_attn_fp8(const void* q, const void* kv, const int32_t* idx, int32
                         int64_t e_cap, int32_t n_heads, int32_t head_dim, void* ws,
                         size_t ws_bytes, int32_t dtype, void* stream) {
   return sparse_attn_impl(q, kv, idx, top_k, win, w_cap, window, q_pos, sink, scale, out, n_seq,
-                          n_q, e_cap, n_heads, head_dim, ws, ws_bytes, dtype, true, stream);
+                          n_q, e_cap, n_heads, head_dim, ws, ws_bytes, dtype, kKvFp8, stream);
+}
+
+int csa_sparse_attn_fp4(const void* q, const void* kv, const int32_t* idx, int32_t top_k,
+                        const void* win, int32_t w_cap, int32_t window, const int64_t* q_pos,
+                        const float* sink, float scale, void* out, int64_t n_seq, int64_t n_q,
+                        int64_t e_cap, int32_t n_heads, int32_t head_dim, void* ws,
+                        size_t ws_bytes, int32_t dtype, void* stream) {
+  return sparse_attn_impl(q, kv, idx, top_k, win, w_cap, window, q_pos, sink, scale, out, n_seq,
+                          n_q, e_cap, n_heads, head_dim, ws, ws_bytes, dtype, kKvFp4, stream);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -483,6 +510,10 @@ DecodeWs carve_decode(Carver& c, const csa_decode_desc* d) {
   w.attn = c.take<char>(attn_ws_bytes(rows, d->n_heads, d->dim, d->top_k, d->window, CSA_BF16));
   if (wants_qprep(d)) w.qprep = c.take<char>(q_bytes(d) * size_t(d->n_attn));
   return w;
+}
+
+int kv_fmt_of(const csa_decode_desc* d) {
+  return d->kv_format == CSA_KV_FP8 ? kKvFp8 : d->kv_format == CSA_KV_FP4 ? kKvFp4 : kKvPlain;
 }
 
 int check_decode_shapes(const csa_decode_desc* d) {
@@ -524,8 +555,9 @@ int check_decode_shapes(const csa_decode_desc* d) {
   if (d->kv_rope_dim > 0 && !(d->rope_base > 1.f)) return CSA_ERR_SHAPE;
   if ((d->kv_gamma != nullptr || d->kv_rope_dim > 0) && (d->dim != 512 || d->kv_rope_dim > 64))
     return CSA_ERR_UNSUPPORTED;
-  if (d->kv_format != CSA_KV_DTYPE && d->kv_format != CSA_KV_FP8) return CSA_ERR_SHAPE;
-  if (d->kv_format == CSA_KV_FP8 && (d->dtype != CSA_BF16 || d->n_heads != 64 || d->dim != 512))
+  if (d->kv_format != CSA_KV_DTYPE && d->kv_format != CSA_KV_FP8 && d->kv_format != CSA_KV_FP4)
+    return CSA_ERR_SHAPE;
+  if (d->kv_format != CSA_KV_DTYPE && (d->dtype != CSA_BF16 || d->n_heads != 64 || d->dim != 512))
     return CSA_ERR_UNSUPPORTED;
   if (d->score_format != CSA_SCORE_F32 && d->score_format != CSA_SCORE_BF16) return CSA_ERR_SHAPE;
   if (d->compressor != CSA_COMP_SINGLE && d->compressor != CSA_COMP_C4A) return CSA_ERR_SHAPE;
@@ -553,7 +585,7 @@ int check_decode(const csa_decode_desc* d) {
         reinterpret_cast<uintptr_t>(d->k_idx_scale) % 4 != 0)
       return CSA_ERR_SHAPE;
   }
-  if (d->kv_format == CSA_KV_FP8 && reinterpret_cast<uintptr_t>(d->kv) % 16 != 0)
+  if (d->kv_format != CSA_KV_DTYPE && reinterpret_cast<uintptr_t>(d->kv) % 16 != 0)
     return CSA_ERR_SHAPE;
   for (int c = 0; c < d->n_attn; ++c) {
     if (!d->q[c] || !d->out[c]) return CSA_ERR_NULL;
@@ -593,7 +625,7 @@ int decode_step_run(const csa_decode_desc* d, void* ws, void* stream) {
   in.bias = d->bias; in.bias_i = d->bias_i; in.kv = d->kv; in.k_idx = d->k_idx;
   void* key_scales = d->idx_format == CSA_IDX_MXFP4 ? d->k_idx_scale : nullptr;
   in.k_scale = key_scales;
-  in.kv_fp8 = d->kv_format == CSA_KV_FP8 ? 1 : 0;
+  in.kv_fmt = kv_fmt_of(d);
   in.kv_gamma = d->kv_gamma;
   in.kv_rope_dim = d->kv_rope_dim;
   if (d->compressor == CSA_COMP_C4A) {
@@ -675,7 +707,7 @@ int decode_step_run(const csa_decode_desc* d, void* ws, void* stream) {
     a.sink = d->sink[c2]; a.scale = d->scale; a.out = d->out[c2]; a.n_seq = d->n_seq;
     a.n_q = 1; a.e_cap = d->e_cap; a.H = d->n_heads; a.D = d->dim; a.ws = w.attn;
     a.out_rope_dim = d->out_rope_dim;
-    a.kv_fp8 = d->kv_format == CSA_KV_FP8 ? 1 : 0;
+    a.kv_fmt = kv_fmt_of(d);
     if (w.qprep && (d->q_gamma[c2] != nullptr || d->q_rope_dim > 0))
       a.q = w.qprep + size_t(c2) * q_bytes(d);   // this call's prepared query
     a.rope_log2_base = d->out_rope_dim > 0 ? log2(double(d->rope_base)) : 0.0;

@@ -30,8 +30,8 @@ namespace {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Row j of a query's list: j < top_k -> selected id; else window position. With kv_fp8 the
-// selected rows are FP8 entries: the pointer is the entry's first byte.
+// Row j of a query's list: j < top_k -> selected id; else window position. With FP8 or FP4
+// entries (kv_fmt) the pointer of a selected row is the entry's first byte.
 template <typename T>
 __device__ __forceinline__ const T* row_ptr(const AttnArgs& a, int64_t r, int64_t sq, int64_t t,
                                             int64_t j, int nrows) {
@@ -39,9 +39,10 @@ __device__ __forceinline__ const T* row_ptr(const AttnArgs& a, int64_t r, int64_
   if (j < a.top_k) {
     const int32_t id = a.idx[r * a.top_k + j];
     if (id < 0 || id >= a.e_cap) return nullptr;
-    if (a.kv_fp8)   // an FP8 entry (576 bytes); the kernels that take kv_fp8 read it as bytes
+    if (a.kv_fmt != kKvPlain)   // a quantised entry; the kernels that take one read bytes
       return reinterpret_cast<const T*>(static_cast<const uint8_t*>(a.kv) +
-                                        (sq * a.e_cap + id) * kFp8EntryBytes);
+                                        (sq * a.e_cap + id) *
+                                            (a.kv_fmt == kKvFp8 ? kFp8EntryBytes : kFp4EntryBytes));
     return reinterpret_cast<const T*>(a.kv) + (sq * a.e_cap + id) * a.D;
   }
   const int64_t p = t - a.window + 1 + (j - a.top_k);

@@ -88,13 +88,14 @@ __device__ __forceinline__ void attn_split_mfma(const AttnArgs& a, AttnLds& L, i
     for (int i = 0; i < 4; ++i) {
       srcs[i] = row_src(j + 4 * ra + i, int(j1));
       okr[i] = srcs[i] != nullptr;
-      f8r[i] = okr[i] && a.kv_fp8 && j + 4 * ra + i < a.top_k;
+      f8r[i] = okr[i] && a.kv_fmt != kKvPlain && j + 4 * ra + i < a.top_k;
     }
   };
-  // chunk c (dims 8c .. 8c+7) of an FP8 entry: eight E4M3 codes at byte 8c (c < 56), else
-  // eight bf16 values at byte 448 + 16 (c - 56)
+  // chunk c (dims 8c .. 8c+7) of a quantised entry. FP8: eight E4M3 codes at byte 8c (c < 56),
+  // else eight bf16 values at byte 448 + 16 (c - 56); FP4: fp4_entry_chunk8
   auto chunk8 = [&](const uint16_t* row, int c) -> bf16x8_t {
     const uint8_t* e = reinterpret_cast<const uint8_t*>(row);
+    if (a.kv_fmt == kKvFp4) return fp4_entry_chunk8(e, c);
     if (c < kFp8Nope / 8) {
       const uint2 w = *reinterpret_cast<const uint2*>(e + 8 * c);
       return e4m3x8_to_bf16(w.x, w.y);
@@ -328,39 +329,44 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
   __syncthreads();
   // rows 8 w .. 8 w + 7 of tile t into buffer b; rows past the list (and rows without a
   // valid address) read the query row and are masked
-  // An FP8 entry row (kv_fp8, list row < top_k) moves as its raw 576 bytes (lanes 0 .. 35 of
-  // the DMA; the others fetch query bytes into the rest of the slot) and is expanded in place
-  // to the bf16 layout once it has landed (expand). f8mask bit 8 b + i: row 8 w + i of buffer b.
-  uint32_t f8mask = 0u;
+  // A quantised entry row (kv_fmt FP8 or FP4, list row < top_k) moves as its raw bytes (576 or
+  // 288: lanes 0 .. 35 or 0 .. 17 of the DMA, the others masked off, so the active lanes are a
+  // prefix and land at the start of the slot) and is expanded in place to the bf16 layout once
+  // it has landed (expand), which rewrites all 1,024 bytes of the slot. qmask bit 8 b + i: row
+  // 8 w + i of buffer b.
+  const int kvf = a.kv_fmt;
+  const int raw_lanes = kvf == kKvFp8 ? kFp8EntryBytes / 16 : kFp4EntryBytes / 16;
+  uint32_t qmask = 0u;
   auto issue = [&](int t, int b) {
-    f8mask &= ~(0xffu << (8 * b));
+    qmask &= ~(0xffu << (8 * b));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int tr = 8 * wave_u + i;
       const int jr = t * kTile + tr;
       const uint16_t* p = jr < nl ? L.rowp[jr] : nullptr;
-      const bool f8 = p != nullptr && a.kv_fp8 && j0 + jr < a.top_k;   // uniform
-      if (f8) {
-        const unsigned char* src = lane < kFp8EntryBytes / 16
-                                       ? reinterpret_cast<const unsigned char*>(p) + 16 * lane
-                                       : reinterpret_cast<const unsigned char*>(qrow) + 16 * lane;
-        dma_row(reinterpret_cast<const uint16_t*>(src), &L.kv[b][tr * kKvRowD]);
-        f8mask |= 1u << (8 * b + i);
+      const bool qz = p != nullptr && kvf != kKvPlain && j0 + jr < a.top_k;   // uniform
+      if (qz) {
+        if (lane < raw_lanes)
+          dma_row(reinterpret_cast<const uint16_t*>(reinterpret_cast<const unsigned char*>(p) +
+                                                    16 * lane),
+                  &L.kv[b][tr * kKvRowD]);
+        qmask |= 1u << (8 * b + i);
       } else {
         dma_row((p != nullptr ? p : qrow) + (lane ^ kv_swz(tr)) * 8, &L.kv[b][tr * kKvRowD]);
       }
       if (lane == 0) L.rowok[b][tr] = p != nullptr;
     }
   };
-  // this wave's FP8 rows of buffer b, after their DMA has landed (vmcnt(0)): every lane reads
-  // its raw 16 bytes of each row before any lane writes (the writes use the reads' results and
-  // each row is read by one instruction), so the expansion may overwrite the raw bytes in
-  // place. Raw chunk l < 28
-  // holds dims 16 l .. 16 l + 15 (bf16 chunks 2 l, 2 l + 1), raw chunk 28 .. 35 the bf16 dims
-  // 448 + 8 (l - 28) .. (bf16 chunk l + 28); bf16 chunk c goes to slot chunk c ^ swz(row).
-  auto expand = [&](int b) {
-    const uint32_t bits = (f8mask >> (8 * b)) & 0xffu;
-    if (bits == 0u) return;
+  // this wave's quantised rows of buffer b, after their DMA has landed (vmcnt(0)): every lane
+  // reads its raw bytes of each row before any lane writes (the writes use the reads' results
+  // and each row is read by the same instructions), so the expansion may overwrite the raw bytes
+  // in place; bf16 chunk c goes to slot chunk c ^ swz(row).
+  // FP8: raw chunk l < 28 holds dims 16 l .. 16 l + 15 (bf16 chunks 2 l, 2 l + 1), raw chunk
+  // 28 .. 35 the bf16 dims 448 + 8 (l - 28) .. (bf16 chunk l + 28).
+  // FP4: lane (i, l) = (lane >> 4, lane & 15) expands code chunk l (dims 32 l .. 32 l + 31, bf16
+  // chunks 4 l .. 4 l + 3) of rows h + i, h = 0 and 4, under the scales of blocks 2 l, 2 l + 1
+  // (the two bytes at 256 + 2 l).
+  auto expand8 = [&](int b, uint32_t bits) {
     // four rows' raw chunks are read together (one wait per four rows), then converted and
     // written
 #pragma unroll
@@ -390,6 +396,44 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
         }
       }
     }
+  };
+  auto expand4 = [&](int b, uint32_t bits) {
+    const int qi = lane >> 4, ql = lane & 15;
+    uint4 raw[2];
+    uint32_t sc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      raw[h] = make_uint4(0u, 0u, 0u, 0u);
+      sc[h] = 0u;
+      if ((bits >> (4 * h + qi)) & 1u) {
+        const unsigned char* row = &L.kv[b][(8 * wave_u + 4 * h + qi) * kKvRowD];
+        raw[h] = *reinterpret_cast<const uint4*>(row + 16 * ql);
+        sc[h] = *reinterpret_cast<const uint16_t*>(row + kFp4CodeBytes + 2 * ql);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (!((bits >> (4 * h + qi)) & 1u)) continue;
+      const int tr = 8 * wave_u + 4 * h + qi;
+      unsigned char* row = &L.kv[b][tr * kKvRowD];
+      const int sw = kv_swz(tr);
+      float s0, s1;
+      e4m3x2_scales(sc[h], s0, s1);
+      const bf16x8_t c0 = fp4x8_to_bf16(raw[h].x, s0);
+      const bf16x8_t c1 = fp4x8_to_bf16(raw[h].y, s0);
+      const bf16x8_t c2 = fp4x8_to_bf16(raw[h].z, s1);
+      const bf16x8_t c3 = fp4x8_to_bf16(raw[h].w, s1);
+      *reinterpret_cast<bf16x8_t*>(row + 16 * ((4 * ql) ^ sw)) = c0;
+      *reinterpret_cast<bf16x8_t*>(row + 16 * ((4 * ql + 1) ^ sw)) = c1;
+      *reinterpret_cast<bf16x8_t*>(row + 16 * ((4 * ql + 2) ^ sw)) = c2;
+      *reinterpret_cast<bf16x8_t*>(row + 16 * ((4 * ql + 3) ^ sw)) = c3;
+    }
+  };
+  auto expand = [&](int b) {
+    const uint32_t bits = (qmask >> (8 * b)) & 0xffu;
+    if (bits == 0u) return;   // uniform
+    if (kvf == kKvFp4) expand4(b, bits);
+    else expand8(b, bits);
   };
   const int ntiles = (nl + kTile - 1) / kTile;
   // Two tiles or fewer (the decode splits): both go out at once and land before the first

@@ -88,6 +88,86 @@ __device__ __forceinline__ void store_fp8_entry8(uint8_t* entry, int c0, const f
   }
 }
 
+// ---- FP4 main-cache entries --------------------------------------------------------------
+// "DeepSeek-V4.1-Flash's KV-Cache Compression, Checked Down to the Byte", section 4 (Cell 3):
+// the whole 512-channel entry as E2M1 elements with one E4M3 scale per 16 channels and no
+// global scale, 512 / 2 + 512 / 16 = 288 bytes. Bytes 0 .. 255: element codes, channel 2i in
+// the low nibble of byte i; bytes 256 .. 287: the scale codes, byte 256 + g for channels
+// 16 g .. 16 g + 15. Block scale: the E4M3 value nearest to max|x| / 6 (the block maximum on
+// E2M1's largest magnitude); elements: nearest magnitude times the scale, ties to the even code.
+constexpr int kFp4CodeBytes = 256;
+constexpr int kFp4EntryBytes = 288;
+
+// value of a non-negative E4M3 code (0 .. 0x7e): m 2^-9 when the exponent field is 0
+__device__ __forceinline__ float e4m3_pos_value(uint32_t code) {
+  const uint32_t e = code >> 3, m = code & 7u;
+  return e == 0u ? float(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 code of x under a block scale s > 0: the nearest of the magnitudes {0, .5, 1, 1.5, 2, 3,
+// 4, 6} times s, ties to the even code, past 6 s to 6 s; a zero magnitude is code 0. The
+// decision points are the midpoints times s, exact in fp32 (at most 7 significant bits, never
+// below 2^-11), so every comparison is exact.
+__device__ __forceinline__ uint32_t e2m1_code_scaled(float x, float s) {
+  const float a = fabsf(x);
+  const uint32_t c = a <= 0.25f * s ? 0u : a < 0.75f * s ? 1u : a <= 1.25f * s ? 2u
+                   : a < 1.75f * s ? 3u : a <= 2.5f * s ? 4u : a < 3.5f * s ? 5u
+                   : a <= 5.f * s ? 6u : 7u;
+  return (c != 0u && x < 0.f) ? (c | 8u) : c;
+}
+
+// Channels c0 .. c0+7 (c0 % 8 == 0) of an FP4 entry from their stored values v: the lane
+// pair (c0 / 8 even, odd) shares a 16-channel block and its scale; every lane of the wave must
+// call this together (the pair exchanges its maxima by a shuffle). amax / 6 is correctly
+// rounded in fp32, and since amax carries at most 24 significant bits it never lands on, or
+// crosses, an E4M3 rounding midpoint it does not equal, so e4m3_code rounds it as the exact
+// quotient would be rounded.
+__device__ __forceinline__ void store_fp4_entry8(uint8_t* entry, int c0, const float* v) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  const uint32_t sc = e4m3_code(amax / 6.f);
+  const float s = e4m3_pos_value(sc);
+  uint32_t w = 0u;
+  if (sc != 0u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= e2m1_code_scaled(v[i], s) << (4 * i);
+  }
+  *reinterpret_cast<uint32_t*>(entry + (c0 >> 1)) = w;
+  if (((c0 >> 3) & 1) == 0) entry[kFp4CodeBytes + (c0 >> 4)] = uint8_t(sc);
+}
+
+// Eight FP4 element codes (one dword, channel k of the eight in nibble k) times the block
+// scale s -> eight bf16 values, exact: v_cvt_scalef32_pk_f32_fp4 with scale 1 (the scaled
+// conversions of gfx950 apply only the exponent of their fp32 scale, so the E4M3 scale is a
+// separate multiply), then v_cvt_pk_bf16_f32 (the product is a bf16 value).
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w, float s) {
+  const auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  bf16x8_t r;
+  r[0] = (__bf16)(f0[0] * s); r[1] = (__bf16)(f0[1] * s);
+  r[2] = (__bf16)(f1[0] * s); r[3] = (__bf16)(f1[1] * s);
+  r[4] = (__bf16)(f2[0] * s); r[5] = (__bf16)(f2[1] * s);
+  r[6] = (__bf16)(f3[0] * s); r[7] = (__bf16)(f3[1] * s);
+  return r;
+}
+
+// the two block scales of a chunk pair: E4M3 codes in the low two bytes of sc2 -> fp32, exact
+__device__ __forceinline__ void e4m3x2_scales(uint32_t sc2, float& s0, float& s1) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sc2, 1.0f, false);
+  s0 = f[0];
+  s1 = f[1];
+}
+
+// chunk c (channels 8c .. 8c+7) of an FP4 entry as bf16
+__device__ __forceinline__ bf16x8_t fp4_entry_chunk8(const uint8_t* e, int c) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(e + 4 * c);
+  return fp4x8_to_bf16(w, e4m3_pos_value(e[kFp4CodeBytes + (c >> 1)]));
+}
+
 // cos and sin of the RoPE angle p * base^(-2j/rope_dim) (p may be negative): formed and reduced
 // to [-pi, pi] in double precision, since positions reach millions of radians
 __device__ __forceinline__ void rope_cos_sin(double p, int j, int rope_dim, double log2_base,

@@ -246,9 +246,14 @@ __device__ __forceinline__ void ingest_vector(const IngestArgs& a, int64_t sq, i
     // the entry's RMSNorm and RoPE at t (the newest position it pools): its 64 vectors are
     // this wave's 64 lanes
     if (main && prep) prep_kv_row8<T>(a, t, c0, d, res);
-    if (main && a.kv_fp8) {   // the pooled entry in T (bf16), then the FP8 entry form
+    if (main && a.kv_fmt == kKvFp8) {   // the pooled entry in T (bf16), then the FP8 form
       store_fp8_entry8(static_cast<uint8_t*>(a.kv) + (sq * a.e_cap + e) * kFp8EntryBytes, c0,
                        res, true);
+    } else if (main && a.kv_fmt == kKvFp4) {   // the same for the FP4 form (the whole wave)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) res[k] = round_to_bf16(res[k]);
+      store_fp4_entry8(static_cast<uint8_t*>(a.kv) + (sq * a.e_cap + e) * kFp4EntryBytes, c0,
+                       res);
     } else {
       T* dst = (T*)(main ? a.kv : a.k_idx) + (sq * a.e_cap + e) * d + c0;
       Elt<T>::store8(dst, res);

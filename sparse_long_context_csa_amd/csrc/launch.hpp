@@ -8,6 +8,10 @@
 namespace csa {
 
 enum DType : int { kF32 = 0, kBF16 = 1 };
+// kv_fmt of the attention and ingest arguments: how the main cache holds its entries
+constexpr int kKvPlain = 0;   // the step's dtype, dim channels
+constexpr int kKvFp8 = 1;     // 576-byte FP8 entries
+constexpr int kKvFp4 = 2;     // 288-byte FP4 entries
 
 // ---- compressor --------------------------------------------------------------------------
 hipError_t launch_compress(int dt, const void* x, const void* z, const void* bias, void* out,
@@ -31,7 +35,7 @@ struct IngestArgs {
   void *x_tail, *z_tail, *xi_tail, *zi_tail;
   const void *bias, *bias_i;
   void *kv, *k_idx;
-  int kv_fp8;             // kv holds FP8 entries (576 bytes: 448 E4M3 + 64 bf16 channels)
+  int kv_fmt;             // kKvPlain, kKvFp8 (576-byte entries) or kKvFp4 (288-byte entries)
   // the entry a step completes gets the per-head RMSNorm (kv_gamma [dim], or none when null)
   // and RoPE at t on its last kv_rope_dim channels before it is stored (dim == 512: the
   // entry's 64 vectors are the 64 lanes of one wave)
@@ -139,6 +143,12 @@ hipError_t launch_quantize_kv_fp8(int dt, const void* x, void* out, int64_t n_ro
                                   hipStream_t s);
 hipError_t launch_dequantize_kv_fp8(const void* in, void* out, int64_t n_rows, hipStream_t s);
 
+// ---- FP4 main-cache entries (kv_fp4.hip) ---------------------------------------------------
+// x [n_rows, 512] (T) -> entries [n_rows, 288] bytes; entries -> bf16 [n_rows, 512]
+hipError_t launch_quantize_kv_fp4(int dt, const void* x, void* out, int64_t n_rows,
+                                  hipStream_t s);
+hipError_t launch_dequantize_kv_fp4(const void* in, void* out, int64_t n_rows, hipStream_t s);
+
 // ---- MXFP4 storage of indexer keys (mxfp4.hpp) --------------------------------------------
 // x [n_rows, dim] (dim % 32 == 0) -> codes [n_rows, dim / 2] bytes, scales [n_rows, dim / 32]
 hipError_t launch_quantize_mxfp4(int dt, const void* x, void* codes, void* scales, int64_t n_rows,
@@ -208,8 +218,10 @@ struct AttnArgs {
   // (2j, 2j+1) by -q_pos * base^(-2j/out_rope_dim) before the store (0: off)
   int out_rope_dim;
   double rope_log2_base;
-  // kv holds FP8 entries (576 bytes: 448 E4M3 + 64 bf16 channels; bf16 64 x 512 heads only)
-  int kv_fp8;
+  // how kv holds its entries: kKvPlain (T, D channels), kKvFp8 (576 bytes: 448 E4M3 + 64 bf16
+  // channels) or kKvFp4 (288 bytes: E2M1 + an E4M3 scale per 16 channels); the quantised forms
+  // for bf16 64 x 512 heads only
+  int kv_fmt;
 };
 size_t attn_ws_bytes(int64_t rows, int H, int D, int top_k, int window, int dt);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s);

@@ -68,6 +68,11 @@ int main(int argc, char** argv) {
   expect("c4a one prev", csa_compress_c4a(kFake, kFake, kFake, kFake, kFake, kFake, kFake, nullptr, kFake, 1, 8, 0, 64, 4, CSA_BF16, nullptr), CSA_ERR_NULL);
   expect("norm_rope flags", csa_norm_rope(kFake, nullptr, nullptr, kFake, 1, 1, 64, 0, 10000.f, 1e-6f, 8, CSA_BF16, nullptr), CSA_ERR_SHAPE);
   expect("mxfp4 dim", csa_quantize_mxfp4(kFake, kFake, kFake, 1, 48, CSA_BF16, nullptr), CSA_ERR_SHAPE);
+  void* const kOdd = reinterpret_cast<void*>(static_cast<uintptr_t>(256 + 8));   // not 16-aligned
+  expect("kv_fp8 align", csa_quantize_kv_fp8(kFake, kOdd, 1, CSA_BF16, nullptr), CSA_ERR_SHAPE);
+  expect("kv_fp4 align", csa_quantize_kv_fp4(kFake, kOdd, 1, CSA_BF16, nullptr), CSA_ERR_SHAPE);
+  expect("kv_fp4 null", csa_dequantize_kv_fp4(nullptr, kFake, 1, nullptr), CSA_ERR_NULL);
+  expect("kv_fp4 empty", csa_dequantize_kv_fp4(kFake, kFake, 0, nullptr), CSA_OK);
 
   // index / attention
   const size_t iws = csa_index_topk_workspace_size(4, 1, 262144, 512);
@@ -75,6 +80,7 @@ int main(int argc, char** argv) {
   expect("index_topk no ws", csa_index_topk(kFake, (const float*)kFake, kFake, (const int64_t*)kFake, nullptr, nullptr, 0, 4, 1, 262144, 64, 128, 4, 512, (int32_t*)kFake, nullptr, nullptr, nullptr, 0, CSA_BF16, nullptr), CSA_ERR_WORKSPACE);
   expect("index_topk top_k", csa_index_topk(kFake, (const float*)kFake, kFake, (const int64_t*)kFake, nullptr, nullptr, 0, 4, 1, 262144, 64, 128, 4, 4096, (int32_t*)kFake, nullptr, nullptr, kFake, iws, CSA_BF16, nullptr), CSA_ERR_SHAPE);
   expect("sparse_attn heads", csa_sparse_attn(kFake, kFake, (const int32_t*)kFake, 512, kFake, 128, 128, (const int64_t*)kFake, nullptr, 0.04f, kFake, 4, 1, 1024, 65, 512, kFake, 1 << 30, CSA_BF16, nullptr), CSA_ERR_SHAPE);
+  expect("sparse_attn_fp4 dtype", csa_sparse_attn_fp4(kFake, kFake, (const int32_t*)kFake, 512, kFake, 128, 128, (const int64_t*)kFake, nullptr, 0.04f, kFake, 4, 1, 1024, 64, 512, kFake, 1 << 30, CSA_F32, nullptr), CSA_ERR_UNSUPPORTED);
   expect("sparse_attn window", csa_sparse_attn(kFake, kFake, (const int32_t*)kFake, 512, kFake, 64, 128, (const int64_t*)kFake, nullptr, 0.04f, kFake, 4, 1, 1024, 64, 512, kFake, 1 << 30, CSA_BF16, nullptr), CSA_ERR_SHAPE);
 
   // decode step
@@ -91,6 +97,8 @@ int main(int argc, char** argv) {
   expect("decode one scan event", csa_decode_step(&e, kFake, need, nullptr), CSA_ERR_NULL);
   e = d; e.block_size = 64; e.max_blocks = 1024; e.q_idx2 = kFake; e.w2 = (const float*)kFake;
   expect("decode pool too big", csa_decode_step(&e, kFake, need, nullptr), CSA_ERR_UNSUPPORTED);
+  e = d; e.kv_format = CSA_KV_FP4; e.kv = kOdd;
+  expect("decode fp4 align", csa_decode_step(&e, kFake, need, nullptr), CSA_ERR_SHAPE);
   e = d; e.kv_rope_dim = 3;
   expect("decode odd rope", csa_decode_step(&e, kFake, need, nullptr), CSA_ERR_SHAPE);
   e = d; e.idx_format = CSA_IDX_MXFP4;   // codes need their scale bytes

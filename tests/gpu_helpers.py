@@ -7,7 +7,7 @@ import torch
 import datagen
 import sparse_long_context_csa_amd as csa_lib
 from oracle import csa as ocsa
-from oracle import fp8, gaps, mx
+from oracle import fp8, gaps, kv_fp4, mx
 from oracle.pipeline import f64, i64
 
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
@@ -163,6 +163,61 @@ def assert_fp8_entry(entry, exact, xabs_max, what=""):
                              f"(exact {exact[k]})")
 
 
+def assert_fp4_entry(entry, exact, xabs_max, what=""):
+    """The FP4 form of a pooled main entry. The GPU's fp32 pooling lies within 4e-6 max_j |x_j|
+    of the exact value, and the stored bf16 value between the roundings of exact -/+ that error.
+    A block's scale is monotone in its largest magnitude, so the stored scale code lies between
+    those of the smallest and largest possible maxima; under the scale the GPU chose, each
+    element's cached value is monotone in the element, so it lies between the cached values of
+    the two bounds (bit-exact wherever no rounding boundary falls in between)."""
+    tol = 4e-6 * np.asarray(xabs_max)
+    lo = ocsa.store(exact - tol, "bf16")
+    hi = ocsa.store(exact + tol, "bf16")
+    e = np.asarray(entry, dtype=np.uint8)
+    sc = e[kv_fp4.CODE_BYTES:].astype(np.int64)
+    mag_hi = np.maximum(np.abs(lo), np.abs(hi)).reshape(32, 16).max(axis=1)
+    mag_lo = np.where(np.sign(lo) == np.sign(hi), np.minimum(np.abs(lo), np.abs(hi)), 0.0)
+    mag_lo = mag_lo.reshape(32, 16).max(axis=1)
+    sc_lo = kv_fp4.block_scale_codes(mag_lo).astype(np.int64)
+    sc_hi = kv_fp4.block_scale_codes(mag_hi).astype(np.int64)
+    bad = np.flatnonzero((sc < sc_lo) | (sc > sc_hi))
+    if bad.size:
+        g = int(bad[0])
+        raise AssertionError(f"{what}: block {g} scale code {sc[g]} outside [{sc_lo[g]}, "
+                             f"{sc_hi[g]}]")
+    s = np.repeat(fp8.dequantize(sc.astype(np.uint8)), 16)
+    got = kv_fp4.decode_entries(e)
+
+    def cached(v):
+        y = np.divide(v, s, out=np.zeros_like(v), where=s > 0)
+        return kv_fp4.E2M1_VALUES[kv_fp4.nearest_e2m1(y)] * s
+
+    clo, chi = cached(lo), cached(hi)
+    bad = np.flatnonzero((got < clo) | (got > chi))
+    if bad.size:
+        k = int(bad[0])
+        raise AssertionError(f"{what}: channel {k} holds {got[k]}, outside [{clo[k]}, {chi[k]}] "
+                             f"(exact {exact[k]})")
+
+
+def fp4_case(case):
+    """fp8_case for an FP4 main cache (288-byte entries, csa_quantize_kv_fp4 against the oracle's
+    encoder). Returns the device state {"kv": uint8 [B, E, 288]}."""
+    kv = case["kv"]
+    want = kv_fp4.encode_entries(f64(kv))
+    case["kv"] = torch.from_numpy(kv_fp4.decode_entries(want)).to(kv.dtype)
+    case["kv_format"] = "fp4"
+    k4 = csa_lib.quantize_kv_fp4(dev(kv))
+    torch.cuda.synchronize()
+    assert np.array_equal(k4.cpu().numpy(), want)
+    return {"kv": k4}
+
+
+def quant_case(case, fmt):
+    """The device state of a main cache in fmt ("fp8" or "fp4"), the case updated to match."""
+    return fp8_case(case) if fmt == "fp8" else fp4_case(case)
+
+
 def fp8_case(case):
     """Turns a bf16 decode case into one with an FP8 main cache: the oracle's case holds the
     cached values of the generated entries (oracle encoder); the GPU gets the entries that
@@ -263,6 +318,10 @@ def check_step(case, ref, st, rings, out, idx):
                 if name == "kv" and case.get("kv_format") == "fp8":
                     assert_fp8_entry(st["kv"][b, e].cpu().numpy(), exact, xmax,
                                      f"FP8 entry {e} of seq {b}")
+                    continue
+                if name == "kv" and case.get("kv_format") == "fp4":
+                    assert_fp4_entry(st["kv"][b, e].cpu().numpy(), exact, xmax,
+                                     f"FP4 entry {e} of seq {b}")
                     continue
                 if name == "k_idx" and case.get("idx_format") == "mxfp4":
                     assert_mx_entry(st["k_idx"][b, e].cpu().numpy(),

@@ -40,7 +40,8 @@ def test_header_declares_the_calls():
         "csa_sparse_attn_workspace_size", "csa_sparse_attn", "csa_decode_step_workspace_size",
         "csa_decode_step", "csa_quantize_mxfp4", "csa_compress_c4a", "csa_norm_rope",
         "csa_quantize_kv_fp8", "csa_dequantize_kv_fp8", "csa_sparse_attn_fp8",
-        "csa_decode_step_noalloc", "csa_index_scores_workspace_size", "csa_index_scores"}
+        "csa_decode_step_noalloc", "csa_index_scores_workspace_size", "csa_index_scores",
+        "csa_quantize_kv_fp4", "csa_dequantize_kv_fp4", "csa_sparse_attn_fp4"}
 
 
 def test_binding_covers_every_declared_function():
@@ -96,7 +97,8 @@ def test_decode_desc_mirrors_the_header_struct():
     for name, val in (("CSA_IDX_DTYPE", _lib.IDX_DTYPE), ("CSA_IDX_MXFP4", _lib.IDX_MXFP4),
                       ("CSA_SCORE_F32", _lib.SCORE_F32), ("CSA_SCORE_BF16", _lib.SCORE_BF16),
                       ("CSA_KV_DTYPE", _lib.KV_DTYPE), ("CSA_KV_FP8", _lib.KV_FP8),
-                      ("CSA_KV_FP8_BYTES", _lib.KV_FP8_BYTES),
+                      ("CSA_KV_FP8_BYTES", _lib.KV_FP8_BYTES), ("CSA_KV_FP4", _lib.KV_FP4),
+                      ("CSA_KV_FP4_BYTES", _lib.KV_FP4_BYTES),
                       ("CSA_COMP_SINGLE", _lib.COMP_SINGLE), ("CSA_COMP_C4A", _lib.COMP_C4A)):
         assert int(re.search(rf"#define\s+{name}\s+(\d+)", _header()).group(1)) == val
 
@@ -207,6 +209,30 @@ def test_kv_fp8_validation(lib):
                                        1024, H, D, ok, 1 << 40, dtype, None)
 
     assert attn(dtype=0) == -4            # the FP8 cache is read by the bf16 64 x 512 path
+    assert attn(H=32) == -4
+    assert attn(D=256) == -4
+    assert attn(dtype=9) == -3
+    assert attn(kv=C.c_void_p(256 + 8)) == -2
+
+
+def test_kv_fp4_validation(lib):
+    ok = C.c_void_p(256)   # never dereferenced: every call below fails validation or is empty
+    assert lib.csa_quantize_kv_fp4(ok, ok, 4, 7, None) == -3             # dtype
+    assert lib.csa_quantize_kv_fp4(ok, ok, -1, 1, None) == -2
+    assert lib.csa_quantize_kv_fp4(None, ok, 4, 1, None) == -1
+    assert lib.csa_quantize_kv_fp4(ok, C.c_void_p(256 + 8), 4, 1, None) == -2   # alignment
+    assert lib.csa_quantize_kv_fp4(ok, ok, 0, 1, None) == 0              # nothing to do
+    assert lib.csa_dequantize_kv_fp4(ok, None, 4, None) == -1
+    assert lib.csa_dequantize_kv_fp4(C.c_void_p(256 + 4), ok, 4, None) == -2
+    assert lib.csa_dequantize_kv_fp4(ok, C.c_void_p(256 + 8), 4, None) == -2
+    assert lib.csa_dequantize_kv_fp4(ok, ok, -3, None) == -2
+    assert lib.csa_dequantize_kv_fp4(ok, ok, 0, None) == 0
+
+    def attn(kv=ok, H=64, D=512, dtype=1):
+        return lib.csa_sparse_attn_fp4(ok, kv, ok, 512, ok, 128, 128, ok, None, 0.1, ok, 1, 1,
+                                       1024, H, D, ok, 1 << 40, dtype, None)
+
+    assert attn(dtype=0) == -4            # the FP4 cache is read by the bf16 64 x 512 path
     assert attn(H=32) == -4
     assert attn(D=256) == -4
     assert attn(dtype=9) == -3
@@ -352,13 +378,14 @@ def test_decode_mxfp4_validation(lib):
     assert step(full(idx_format=_lib.IDX_DTYPE, out_rope_dim=40, rope_base=1e4)) == -4
     assert step(full(idx_format=_lib.IDX_DTYPE, q_rope_dim=7, rope_base=1e4)) == -2
     assert step(full(idx_format=_lib.IDX_DTYPE, q_rope_dim=64, rope_base=0.5)) == -2
-    # FP8 main cache: bf16 64 x 512 heads, 16-byte aligned entries, a known format code
-    assert step(full(idx_format=_lib.IDX_DTYPE, kv_format=2)) == -2
-    assert step(full(idx_format=_lib.IDX_DTYPE, kv_format=_lib.KV_FP8, dtype=0)) == -4
-    assert step(full(idx_format=_lib.IDX_DTYPE, kv_format=_lib.KV_FP8, n_heads=32)) == -4
-    d = full(idx_format=_lib.IDX_DTYPE, kv_format=_lib.KV_FP8)
-    d.kv = 256 + 8
-    assert step(d) == -2
+    # FP8 / FP4 main cache: bf16 64 x 512 heads, 16-byte aligned entries, a known format code
+    assert step(full(idx_format=_lib.IDX_DTYPE, kv_format=3)) == -2
+    for fmt in (_lib.KV_FP8, _lib.KV_FP4):
+        assert step(full(idx_format=_lib.IDX_DTYPE, kv_format=fmt, dtype=0)) == -4
+        assert step(full(idx_format=_lib.IDX_DTYPE, kv_format=fmt, n_heads=32)) == -4
+        d = full(idx_format=_lib.IDX_DTYPE, kv_format=fmt)
+        d.kv = 256 + 8
+        assert step(d) == -2
     # the new entry's RMSNorm / RoPE: 512-channel entries, even kv_rope_dim <= 64, a base > 1
     assert step(full(idx_format=_lib.IDX_DTYPE, kv_rope_dim=7)) == -2
     assert step(full(idx_format=_lib.IDX_DTYPE, kv_rope_dim=64, rope_base=1.0)) == -2

@@ -24,7 +24,7 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_unknown_cache_format_is_refused():
-    r = _bench("--kv-format", "fp4")
+    r = _bench("--kv-format", "fp6")
     assert r.returncode == 2 and "invalid choice" in r.stderr
 
 
@@ -38,3 +38,13 @@ def test_fp8_entry_bytes():
     assert bf.gather - f8.gather == 4 * 512 * (1024 - 576)
     assert bf.compress - f8.compress == 4 * (1024 - 576)
     assert bf.keys == f8.keys
+
+
+def test_fp4_entry_bytes():
+    # "DeepSeek-V4.1-Flash's KV-Cache Compression, Checked Down to the Byte", section 4: 288 B
+    assert acc.FP4_ENTRY_BYTES == 288
+    kw = dict(B=4, n_vis=262144, m=4, D=512, H=64, H_I=64, d_I=128, K=512, W=128)
+    bf = acc.decode_step_bytes(**kw)
+    f4 = acc.decode_step_bytes(**kw, entry_bytes=acc.FP4_ENTRY_BYTES)
+    assert bf.gather - f4.gather == 4 * 512 * (1024 - 288)
+    assert bf.compress - f4.compress == 4 * (1024 - 288)

@@ -551,6 +551,99 @@ def test_attention_fp8_cache(B, Q, E, K, W, w_cap):
         assert_rows_close(f64(out[b, i]), r, 2e-2, f"attn fp8 {(b, i)}")
 
 
+# ------------------------------------------------------------------------------ FP4 main cache
+def _fp4_edge_rows():
+    """Entries whose blocks put amax / 6 on an E4M3 rounding midpoint (a tie of the scale), or
+    their elements on E2M1 midpoints times the scale (ties of the codes), both signs; blocks past
+    the largest scale, at the zero-scale tie and just above it, zero blocks and negative zeros
+    (every value bf16-exact)."""
+    from oracle import fp8 as of8
+    mags = np.sort(np.unique(np.abs(of8.E4M3_VALUES[np.isfinite(of8.E4M3_VALUES)])))
+    s_mids = (mags[1:] + mags[:-1]) / 2                  # amax / 6 on a scale tie
+    e_mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    blocks = []
+    for k, sm in enumerate(s_mids[::3]):
+        b = np.zeros(16)
+        b[0] = 6 * sm * (-1) ** k
+        blocks.append(b)
+    for k, sv in enumerate([1.0, 1.125, 0.875 * 2.0 ** -4, 1.5 * 2.0 ** 3, 2.0 ** -9, 448.0]):
+        b = np.zeros(16)
+        b[0] = 6 * sv                                    # amax / 6 = sv exactly
+        b[1:8] = e_mids * sv
+        b[8:15] = -e_mids * sv
+        blocks.append(b)
+    for amax in (2688.0, 3072.0, 16384.0, 6 * 2.0 ** -10, 6.25 * 2.0 ** -10, 0.0):
+        b = amax * np.arange(-8, 8) / 8                  # bf16-exact steps
+        b[0] = -amax
+        blocks.append(b)
+    b = np.zeros(16)
+    b[0], b[1] = 1.0, -0.0
+    blocks.append(b)
+    flat = np.concatenate(blocks)
+    rows = np.resize(flat, (int(np.ceil(flat.size / 512)), 512))
+    return np.concatenate([rows, -rows])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_kv_fp4_bit_exact(dtype):
+    from oracle import kv_fp4 as of4
+    g = np.random.default_rng(45)
+    x = g.standard_normal((200, 512)) * np.exp(0.7 * g.standard_normal((200, 1)))
+    x[5] *= 1e-3                                           # small scales, subnormal ones
+    x[6] *= 1e3                                            # saturating scales
+    x = np.concatenate([x, _fp4_edge_rows()])
+    xt = torch.from_numpy(x).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    if dtype == "f32":   # one fp32 ulp either side of every value of the edge rows
+        e = torch.from_numpy(_fp4_edge_rows()).float()
+        xt = torch.cat([xt, torch.nextafter(e, torch.full_like(e, np.inf)),
+                        torch.nextafter(e, torch.full_like(e, -np.inf))])
+    got = csa.quantize_kv_fp4(dev(xt)).cpu().numpy()
+    want = of4.encode_entries(f64(xt))
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"first mismatch at {tuple(bad[0])}: {got[tuple(bad[0])]} vs {want[tuple(bad[0])]}"
+
+
+def test_dequantize_kv_fp4_every_code_and_scale():
+    """Every E2M1 code under every finite E4M3 scale code decodes to element x scale exactly."""
+    from oracle import kv_fp4 as of4
+    scales = np.arange(0, 0x7F, dtype=np.uint8)           # 0 .. 448
+    e = np.zeros((len(scales), 288), np.uint8)
+    g = np.random.default_rng(46)
+    for r, sc in enumerate(scales):
+        e[r, :256] = np.resize(np.arange(256, dtype=np.uint8), 256)   # every code pair
+        e[r, 256:] = np.roll(scales, r)[:32]
+        e[r, 256 + r % 32] = sc
+    e[:, :256] = np.where(g.random((len(scales), 256)) < 0.1, 0x88, e[:, :256])  # -0 codes
+    out = csa.dequantize_kv_fp4(dev(torch.from_numpy(e))).cpu()
+    np.testing.assert_array_equal(f64(out), of4.decode_entries(e))
+
+
+@pytest.mark.parametrize("B,Q,E,K,W,w_cap", [
+    (4, 1, 5000, 512, 128, 128),       # decode: row splits + combine
+    (2, 3, 3000, 100, 128, 256),       # ragged tiles: FP4 and window rows share a tile
+    (1, 300, 2000, 512, 128, 4096),    # many rows: one workgroup per row
+    (2, 2, 1000, 64, 0, 1),            # selection only
+    (1, 256, 3000, 896, 128, 128),     # 32 tiles per row: the longest list held in LDS
+    (1, 260, 4000, 2048, 128, 128),    # 68 tiles per row: register-staged tiles
+])
+def test_attention_fp4_cache(B, Q, E, K, W, w_cap):
+    """csa_sparse_attn_fp4 against the oracle's attention over the entries' FP4 values."""
+    from oracle import kv_fp4 as of4
+    q, kv, idx, win, sink, pos = attn_case(B, Q, E, 64, 512, K, W, w_cap, "bf16",
+                                           seed=B * 13 + Q, t_lo=0, t_hi=5 * w_cap)
+    pos.view(-1)[0] = 5
+    k4 = csa.quantize_kv_fp4(dev(kv))
+    enc = of4.encode_entries(f64(kv))
+    assert np.array_equal(k4.cpu().numpy(), enc)
+    scale = 1 / math.sqrt(512)
+    out = csa.sparse_attn(dev(q), k4, dev(idx), dev(win), w_cap, W, dev(pos), dev(sink),
+                          scale).cpu()
+    kv_vals = torch.from_numpy(of4.decode_entries(enc))
+    ref = pipeline.sparse_attn(q, kv_vals, idx, win, w_cap, W, pos, sink, scale, "bf16")
+    for (b, i), r in ref.items():
+        assert_rows_close(f64(out[b, i]), r, 2e-2, f"attn fp4 {(b, i)}")
+
+
 def test_bf16_rounding_of_fp32_values():
     """The fp32 -> bf16 rounding every kernel stores with (here through the FP8 entry's 64
     bf16 channels of an fp32 input) is round-to-nearest-even on the bit pattern: exact ties

@@ -10,7 +10,7 @@ import torch
 import datagen
 import sparse_long_context_csa_amd as csa
 from gpu_helpers import (assert_ids, assert_pooled, assert_rows_close, assert_scores, check_step,
-                         dev, fp8_case, mxfp4_case, pooled_xmax, run_step)
+                         dev, fp8_case, mxfp4_case, pooled_xmax, quant_case, run_step)
 from oracle import csa as ocsa
 from oracle import gaps, pipeline
 from oracle.pipeline import f64
@@ -47,6 +47,19 @@ def test_decode_workload_fullsize_mxfp4_keys(cfg):
     print(f"config {cfg} (MXFP4 keys): inputs ready", flush=True)
     gaps.enforce_decode(case)
     _, st, rings, out, idx = run_step(case, idx_state)
+    ref = pipeline.decode_step(case)
+    check_step(case, ref, st, rings, out, idx)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_decode_1m_quantised_main_cache(fmt):
+    """The 1M-context decode workload over an FP8 or FP4 main cache (the bench's --kv-format
+    lines): the GPU quantises the generated entries, the oracle attends their cached values."""
+    case = datagen.make_case(datagen.CONFIGS[4])
+    state = quant_case(case, fmt)
+    print(f"config 4 ({fmt} main cache): inputs ready", flush=True)
+    gaps.enforce_decode(case)
+    _, st, rings, out, idx = run_step(case, state)
     ref = pipeline.decode_step(case)
     check_step(case, ref, st, rings, out, idx)
 

@@ -7,7 +7,7 @@ import torch
 import datagen
 import sparse_long_context_csa_amd as csa
 from gpu_helpers import (assert_ids, assert_rows_close, check_step, dev, fp8_case, mxfp4_case,
-                         run_step)
+                         quant_case, run_step)
 from oracle import csa as ocsa
 from oracle import gaps, pipeline
 from oracle.pipeline import f64
@@ -323,8 +323,9 @@ def test_decode_step_graph_replay_matches_eager(variant):
             assert torch.equal(step.out[c].cpu(), out[c]), f"replay {rep}: output {c} differs"
 
 
-# FP8 main cache: 576-byte entries; the attention expands them to bf16 on their way to the MFMA
-# operands, the step stores the entry it completes in FP8.
+# FP8 / FP4 main cache: 576- or 288-byte entries; the attention expands them to bf16 on their
+# way to the MFMA operands, the step stores the entry it completes in the cache's format.
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
 @pytest.mark.parametrize("spec,mx", [
     (datagen.CaseSpec(7150, "decode", B=5, L=24000, m=4, w_cap=256, ragged=True), False),
     (datagen.CaseSpec(7151, "decode", B=3, L=40000, m=1, w_cap=128, block_size=8,
@@ -332,12 +333,12 @@ def test_decode_step_graph_replay_matches_eager(variant):
     (datagen.CaseSpec(7152, "decode", B=260, L=3000, m=4, w_cap=128, ragged=True), False),
     (datagen.CaseSpec(7153, "decode", B=4, L=4 * 50000, m=4, w_cap=128, ragged=True), True),
 ], ids=["flat", "hier_three_calls", "rows_260", "with_mxfp4_keys"])
-def test_decode_step_fp8_cache(spec, mx):
+def test_decode_step_quantised_cache(spec, mx, fmt):
     if mx:
         case, state = mxfp4_case(spec)
     else:
         case, state = datagen.make_case(spec), {}
-    state.update(fp8_case(case))
+    state.update(quant_case(case, fmt))
     gaps.enforce_decode(case)
     ref = pipeline.decode_step(case)
     step, st, rings, out, idx = run_step(case, state)
@@ -358,11 +359,12 @@ def test_decode_step_fp8_cache(spec, mx):
                       max_blocks=512, n_attn=3, ragged=True), False),
     (datagen.CaseSpec(7162, "decode", dtype="f32", B=2, L=6000, m=4, w_cap=128, ragged=True),
      False),
-    (datagen.CaseSpec(7163, "decode", B=4, L=4 * 30000, m=4, w_cap=128, ragged=True), True),
-], ids=["flat", "hier_three_calls", "f32_separate_ingest", "fp8_cache"])
+    (datagen.CaseSpec(7163, "decode", B=4, L=4 * 30000, m=4, w_cap=128, ragged=True), "fp8"),
+    (datagen.CaseSpec(7164, "decode", B=4, L=4 * 30000, m=4, w_cap=128, ragged=True), "fp4"),
+], ids=["flat", "hier_three_calls", "f32_separate_ingest", "fp8_cache", "fp4_cache"])
 def test_decode_step_entry_norm_rope(spec, fp8):
     case = datagen.make_case(spec)
-    state = fp8_case(case) if fp8 else {}
+    state = quant_case(case, fp8) if fp8 else {}
     case["kv_gamma"] = (datagen.tensor(spec.case_id, 95, (spec.D,), spec.dtype, 0.3) + 1.0).to(
         case["x_new"].dtype)
     case["kv_rope_dim"] = 64
@@ -393,15 +395,17 @@ def test_decode_step_entry_norm_rope(spec, fp8):
                       compressor="c4a"), "fp8_prep"),
     (datagen.CaseSpec(7177, "decode", B=3, L=8 * 3000, m=8, w_cap=128, ragged=True,
                       compressor="c4a"), None),
+    (datagen.CaseSpec(7178, "decode", B=4, L=4 * 30000, m=4, w_cap=128, ragged=True,
+                      compressor="c4a"), "fp4_prep"),
 ], ids=["flat", "all_selected", "first_entry", "hier_three_calls", "mxfp4_keys",
-        "f32_separate_ingest", "fp8_cache_norm_rope", "m8_two_pass"])
+        "f32_separate_ingest", "fp8_cache_norm_rope", "m8_two_pass", "fp4_cache_norm_rope"])
 def test_decode_step_overlapped_compressor(spec, fmt):
     if fmt == "mxfp4":
         case, state = mxfp4_case(spec)
     else:
         case, state = datagen.make_case(spec), {}
-    if fmt == "fp8_prep":
-        state.update(fp8_case(case))
+    if fmt in ("fp8_prep", "fp4_prep"):
+        state.update(quant_case(case, fmt[:3]))
         case["kv_gamma"] = (datagen.tensor(spec.case_id, 95, (spec.D,), spec.dtype, 0.3)
                             + 1.0).to(case["x_new"].dtype)
         case["kv_rope_dim"] = 64

@@ -5,7 +5,7 @@ import pytest
 import torch
 
 import datagen
-from oracle import csa, fp8, gaps, mx, pipeline
+from oracle import csa, fp8, gaps, kv_fp4, mx, pipeline
 from oracle.pipeline import f64
 
 
@@ -251,17 +251,19 @@ def test_decode_step_bf16_scores():
     assert rec > 0.9
 
 
-def test_fp8_cache_attends_the_new_entry_at_its_fp8_value():
-    # m = 1: the new entry is the raw row x_new (a softmax over one logit). With an FP8 main
-    # cache the step must attend to it at its E4M3 / bf16 value: the same outputs as the dtype
-    # path given that value as x_new, and not those of the unquantised entry
+@pytest.mark.parametrize("fmt,enc", [("fp8", fp8), ("fp4", kv_fp4)])
+def test_quantised_cache_attends_the_new_entry_at_its_cached_value(fmt, enc):
+    # m = 1: the new entry is the raw row x_new (a softmax over one logit). With an FP8 (E4M3 /
+    # bf16) or FP4 (E2M1 x E4M3 block scale) main cache the step must attend to it at its cached
+    # value: the same outputs as the dtype path given that value as x_new, and not those of the
+    # unquantised entry
     case = small_decode(case_id=906, m=1, L=12, D=512, H=2, ragged=False)   # K >= entries
     spec = case["spec"]
-    case["kv"] = torch.from_numpy(fp8.cached_entries(f64(case["kv"]))).to(case["kv"].dtype)
+    case["kv"] = torch.from_numpy(enc.cached_entries(f64(case["kv"]))).to(case["kv"].dtype)
     plain = pipeline.decode_step(case)
-    case8 = dict(case, kv_format="fp8")
+    case8 = dict(case, kv_format=fmt)
     res = pipeline.decode_step(case8)
-    xq = fp8.cached_entries(f64(case["x_new"]))
+    xq = enc.cached_entries(f64(case["x_new"]))
     assert not np.array_equal(xq, f64(case["x_new"]))
     moved = dict(case, x_new=torch.from_numpy(xq).to(case["x_new"].dtype))
     want = pipeline.decode_step(moved)
