@@ -488,10 +488,11 @@ def main():
                     help="workload (4: the 1M-context decode headline; 3: chunked prefill; "
                          "6: HCA decode, dense attention over 8,192 entries; 7: the fused "
                          "RMSNorm + RoPE pass over a prefill chunk's queries)")
-    ap.add_argument("--idx-format", default="bf16", choices=("bf16", "mxfp4"),
+    ap.add_argument("--idx-format", default="bf16", choices=("bf16", "mxfp4", "mxfp4qk"),
                     help="indexer-key cache of the decode workloads: bf16 keys, or MXFP4 codes "
                          "with one scale byte per 32 channels (csa_quantize_mxfp4 of the same "
-                         "keys, made before the timed region)")
+                         "keys, made before the timed region); mxfp4qk also takes the indexer "
+                         "query into MXFP4 in the scan (FP4 x FP4 products)")
     ap.add_argument("--score-format", default="f32", choices=("f32", "bf16"),
                     help="index scores the selection ranks: fp32, or rounded to bf16 (the "
                          "line then also reports the recall of the fp32 selection)")
@@ -545,7 +546,8 @@ def main():
                     q_idx2=case["q_idx2"].to(dev), w2=case["w2"].to(dev))
     qs = [x.to(dev) for x in case["q"]]
     sinks = [x.to(dev) for x in case["sink"]]
-    mx = args.idx_format == "mxfp4"
+    mx = args.idx_format in ("mxfp4", "mxfp4qk")
+    qk4 = args.idx_format == "mxfp4qk"
     if mx and (spec.block_size or spec.H_I != 64 or spec.d_I != 128):
         print(json.dumps({"error": "MXFP4 indexer keys: flat 64 x 128 decode workloads only"}))
         sys.exit(2)
@@ -580,7 +582,7 @@ def main():
             m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
             score_format=args.score_format, out_rope_dim=args.rope_dim, q_rope_dim=args.rope_dim,
             q_gamma=q_gammas, kv_gamma=kv_gamma, kv_rope_dim=args.rope_dim,
-            compressor=args.compressor, **states[-1]))
+            compressor=args.compressor, query_fp4=qk4, **states[-1]))
     torch.cuda.synchronize()
     log(f"device state ready: {args.copies} copies, "
         f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated")
@@ -692,7 +694,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "scan_stream_kernel (indexer scan, stage 1)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic(args.idx_format) if args.config == 4 else None,
+                     "traffic": (counter_traffic(args.idx_format)
+                                 if args.config == 4 and args.idx_format in TRAFFIC_FILES
+                                 else None),
                      "avg_launch_us": round(scan_ms * 1e3, 2),
                      "launch_us_min_max": [round(min(scan_launch) * 1e3, 2),
                                            round(max(scan_launch) * 1e3, 2)],
@@ -710,7 +714,7 @@ def main():
     if args.config != 4:
         res["metric"] = f"CSA decode queries/sec ({datagen.WORKLOAD_NAMES[args.config]})"
     if mx:
-        res["metric"] += ", MXFP4 indexer keys"
+        res["metric"] += ", MXFP4 indexer keys" + (" and query" if qk4 else "")
     if kv8 is not None:
         res["metric"] += KV_METRIC[args.kv_format]
         res["config"]["kv_cache"] = KV_CONFIG[args.kv_format]
@@ -725,7 +729,8 @@ def main():
         # recall of the fp32 selection: the same step (idempotent: it rewrites the same tail
         # slot and entry) ranked on fp32 scores, over state copy 0
         ref = csa.DecodeStep(m=spec.m, top_k=spec.K, window=spec.W, scale=case["scale"],
-                             score_format="f32", compressor=args.compressor, **states[0])
+                             score_format="f32", compressor=args.compressor, query_fp4=qk4,
+                             **states[0])
         _, ids_bf = steps_objs[0]()
         ids_bf = ids_bf.clone()
         _, ids_f32 = ref()
@@ -744,7 +749,7 @@ def main():
         if mx:
             # the oracle's step with an MXFP4 cache (the new entry's key quantised); the cached
             # keys are scored as generated, which is the same work as scoring their MXFP4 values
-            case["idx_format"] = "mxfp4"
+            case["idx_format"] = "mxfp4_qk" if qk4 else "mxfp4"
         if kv8 is not None:
             case["kv_format"] = args.kv_format
         if args.rope_dim:

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 15
+#define CSA_ABI_VERSION 16
 
 typedef enum { CSA_F32 = 0, CSA_BF16 = 1 } csa_dtype;
 
@@ -368,6 +368,7 @@ int csa_sparse_attn_fp4(const void *q, const void *kv, const int32_t *idx, int32
 #define CSA_DECODE_EVENTS 5
 #define CSA_IDX_DTYPE 0   /* csa_decode_desc.idx_format: indexer keys in the step's dtype */
 #define CSA_IDX_MXFP4 1   /* indexer keys as MXFP4 codes + scale bytes                    */
+#define CSA_IDX_MXFP4_QK 2 /* MXFP4 keys, and the query quantised to MXFP4 in the scan      */
 #define CSA_SCORE_F32 0   /* csa_decode_desc.score_format: rank fp32 index scores           */
 #define CSA_SCORE_BF16 1  /* rank the scores rounded to bf16                               */
 #define CSA_KV_DTYPE 0    /* csa_decode_desc.kv_format: main entries in the step's dtype      */
@@ -415,9 +416,13 @@ typedef struct csa_decode_desc {
    * aligned). The scan scores the keys' exact values; the entry a step completes is pooled,
    * rounded to T and stored quantised. MXFP4 needs T = bf16, idx_heads 64, idx_dim 128, the
    * flat selection (block_size 0) and m <= 8; otherwise CSA_ERR_UNSUPPORTED.
+   * CSA_IDX_MXFP4_QK keeps the keys the same way and also takes the query into FP4: each
+   * head's q_idx is quantised to MXFP4 by the keys' rule (csa_quantize_mxfp4) inside the scan,
+   * and every product q . k is between the two FP4 values (exact, accumulated in fp32); the
+   * ReLU, the gates and the head sum stay fp32. Same conditions as CSA_IDX_MXFP4.
    *   [CoD "What the cache costs, checked four ways": the indexer cache is FP4, 64 bytes per
-   *   128-channel key; CoD "FP4, down to the index scores": the indexer's query-key path
-   *   loads its keys in FP4, 1 x 32 MXFP4 sub-blocks.] */
+   *   128-channel key; CoD "FP4, down to the index scores": the indexer's query-key path is
+   *   cached, loaded and multiplied in FP4, 1 x 32 MXFP4 sub-blocks.] */
   int32_t idx_format;
   void *k_idx_scale;
   /* Precision of the index scores the selection ranks: CSA_SCORE_F32 (as in steps 4 above) or

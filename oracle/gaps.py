@@ -13,7 +13,7 @@ import numpy as np
 import datagen
 
 from . import csa
-from .pipeline import cached_index_key, f64, i64
+from .pipeline import cached_index_key, f64, i64, index_query
 
 REL_GAP = 1e-3
 MAX_ATTEMPTS = 2000
@@ -109,7 +109,7 @@ def enforce_decode(case: dict, seqs=None) -> dict:
             if e < n:
                 keys[e] = cached_index_key(
                     case, csa.store(csa.compress(xi, zi, bias_i, m)[0], spec.dtype))
-        R = csa.head_relu(f64(case["q_idx"][b]), keys)
+        R = csa.head_relu(index_query(case, case["q_idx"][b]), keys)
         if spec.block_size > 0:
             # stage 1: the block maxima must separate at rank max_blocks. With tens of
             # thousands of blocks that gap is rare (about one gate in a thousand), so the

@@ -120,11 +120,22 @@ def sparse_attn(q, kv, idx, ring, w_cap, window, q_pos, sink, scale, dtype, rows
 
 def cached_index_key(case: dict, key) -> np.ndarray:
     """The indexer key of a new entry as the cache holds it: the pooled key in the step's
-    dtype, then, for an MXFP4 cache (case["idx_format"] == "mxfp4"), its MXFP4 value
-    ("FP4, down to the index scores": the indexer's keys are cached in FP4)."""
-    if case.get("idx_format") == "mxfp4":
+    dtype, then, for an MXFP4 cache (case["idx_format"] "mxfp4" or "mxfp4_qk"), its MXFP4
+    value ("FP4, down to the index scores": the indexer's keys are cached in FP4)."""
+    if case.get("idx_format") in ("mxfp4", "mxfp4_qk"):
         return mx.dequantize(*mx.quantize(key))
     return key
+
+
+def index_query(case: dict, q) -> np.ndarray:
+    """The indexer query [heads, dim] the scores multiply: as given, or, on the FP4 query-key
+    path (case["idx_format"] == "mxfp4_qk"), each head's MXFP4 value under the keys' rule
+    ([CoD] "FP4, down to the index scores": the indexer's query-key path is cached, loaded and
+    multiplied entirely in FP4; the products of two FP4 values are exact)."""
+    q = f64(q)
+    if case.get("idx_format") == "mxfp4_qk":
+        return mx.dequantize(*mx.quantize(q))
+    return q
 
 
 def prepare_kv_row(case: dict, v, t: int) -> np.ndarray:
@@ -173,7 +184,8 @@ def decode_step(case: dict, seqs=None) -> dict:
     through the block pre-select and pool rescoring), and every attention call attends to
     the shared selection plus its own window and sink. With case["idx_format"] == "mxfp4",
     case["k_idx"] holds the MXFP4 values of the cached keys and the new entry's key is
-    quantised before it is scored (``cached_index_key``). With case["score_format"] == "bf16"
+    quantised before it is scored (``cached_index_key``); "mxfp4_qk" quantises the indexer
+    query to MXFP4 as well (``index_query``). With case["score_format"] == "bf16"
     the flat selection ranks the scores rounded fp64 -> fp32 -> bf16. With
     case["out_rope_dim"] > 0 every output head's last channels are turned back by RoPE at -t
     ([CoD] "Key and value are the same vector") before the store; case["q_gamma"] (per call, or
@@ -245,7 +257,7 @@ def decode_step(case: dict, seqs=None) -> dict:
             if new_e < n_vis:
                 keys[new_e] = cached_index_key(case, ki_e)
         res["n_vis"][b] = n_vis
-        s1 = csa.index_scores(f64(case["q_idx"][b]), f64(case["w"][b]), keys)
+        s1 = csa.index_scores(index_query(case, case["q_idx"][b]), f64(case["w"][b]), keys)
         if case.get("score_format") == "bf16":
             # the fp32 scores quantised to BF16 ahead of the selection ([CoD] "FP4, down to
             # the index scores"); ties at the K-th value go to the lower id as before

@@ -310,7 +310,9 @@ class DecodeStep:
     win_new (list, entries may be None), sink (list, entries may be None); out (list) and
     out_idx are allocated here unless given. With k_idx_scale (uint8 [n_seq, e_cap,
     idx_dim / 32]) the indexer cache is MXFP4: k_idx holds the codes, uint8 [n_seq, e_cap,
-    idx_dim / 2], as quantize_mxfp4 writes them. score_format "bf16" ranks the index scores
+    idx_dim / 2], as quantize_mxfp4 writes them; query_fp4=True then also takes the indexer
+    query into MXFP4 (idx_format CSA_IDX_MXFP4_QK: the scan multiplies FP4 by FP4). score_format
+    "bf16" ranks the index scores
     rounded to bf16. out_rope_dim > 0 applies the inverse RoPE (at -pos) to the last
     out_rope_dim channels of every output head, in the attention's output store. q_gamma (a
     list of [dim] tensors or None per call) and q_rope_dim prepare each call's query (RMSNorm,
@@ -329,7 +331,8 @@ class DecodeStep:
                  max_blocks: int = 0, out=None, out_idx=None, score_format: str = "f32",
                  out_rope_dim: int = 0, rope_base: float = 10000.0, q_gamma=None,
                  q_rope_dim: int = 0, kv_gamma=None, kv_rope_dim: int = 0,
-                 compressor: str = "single", no_alloc: bool = False, **t):
+                 compressor: str = "single", no_alloc: bool = False, query_fp4: bool = False,
+                 **t):
         self.t = t
         kv = _dev(t["kv"], "kv")
         kv_fmt = _kv_entry_format(kv)
@@ -372,8 +375,10 @@ class DecodeStep:
             if (tuple(t["k_idx"].shape) != (n_seq, e_cap, idx_dim // 2)
                     or tuple(ks.shape) != (n_seq, e_cap, idx_dim // 32)):
                 raise ValueError("MXFP4 k_idx / k_idx_scale shapes do not match kv and q_idx")
-            d.idx_format = _lib.IDX_MXFP4
+            d.idx_format = _lib.IDX_MXFP4_QK if query_fp4 else _lib.IDX_MXFP4
             d.k_idx_scale = ks.data_ptr()
+        elif query_fp4:
+            raise ValueError("query_fp4 needs an MXFP4 indexer cache (k_idx_scale)")
         if block_size > 0:
             _dev(t["q_idx2"], "q_idx2", dt); _dev(t["w2"], "w2", torch.float32)
             d.q_idx2 = t["q_idx2"].data_ptr(); d.w2 = t["w2"].data_ptr()

@@ -12,7 +12,7 @@ STATUS = {0: "CSA_OK", -1: "CSA_ERR_NULL", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTY
           -4: "CSA_ERR_UNSUPPORTED", -5: "CSA_ERR_WORKSPACE", -6: "CSA_ERR_HIP"}
 MAX_ATTN = 4
 DECODE_EVENTS = 5
-IDX_DTYPE, IDX_MXFP4 = 0, 1
+IDX_DTYPE, IDX_MXFP4, IDX_MXFP4_QK = 0, 1, 2
 SCORE_F32, SCORE_BF16 = 0, 1
 KV_DTYPE, KV_FP8, KV_FP4 = 0, 1, 2
 KV_FP8_BYTES = 576

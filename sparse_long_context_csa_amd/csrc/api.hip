@@ -120,11 +120,12 @@ hipError_t scan_rows(int dt, const void* q, const float* w, const void* keys, co
                      int64_t n_q, int64_t e_cap, int H, int d, int m, const TopkWs& ws,
                      hipStream_t s, const IngestArgs* ingest = nullptr, int seg_k = 0,
                      void* const* kernel_events = nullptr, const void* key_scales = nullptr,
-                     bool score_bf16 = false) {
+                     bool score_bf16 = false, bool q_fp4 = false) {
   ScanArgs a{};
   a.dt = dt; a.q = q; a.w = w; a.keys = keys; a.q_pos = q_pos; a.e_count = e_count;
   a.key_scales = static_cast<const uint8_t*>(key_scales);
   a.score_bf16 = score_bf16 ? 1 : 0;
+  a.q_fp4 = q_fp4 ? 1 : 0;
   a.cand = cand; a.n_cand = n_cand; a.n_seq = n_seq; a.n_q = n_q; a.e_cap = e_cap;
   a.H = H; a.d = d; a.m = m; a.scores = ws.scores; a.score_stride = ws.stride;
   a.n_vis = ws.n_vis; a.count = ws.count;
@@ -533,8 +534,10 @@ int check_decode_shapes(const csa_decode_desc* d) {
     if (d->block_size > 64 || d->max_blocks < 1 || d->max_blocks > 2048) return CSA_ERR_SHAPE;
     if (int64_t(d->block_size) * d->max_blocks > 32768) return CSA_ERR_UNSUPPORTED;
   }
-  if (d->idx_format != CSA_IDX_DTYPE && d->idx_format != CSA_IDX_MXFP4) return CSA_ERR_SHAPE;
-  if (d->idx_format == CSA_IDX_MXFP4 &&
+  if (d->idx_format != CSA_IDX_DTYPE && d->idx_format != CSA_IDX_MXFP4 &&
+      d->idx_format != CSA_IDX_MXFP4_QK)
+    return CSA_ERR_SHAPE;
+  if (d->idx_format != CSA_IDX_DTYPE &&
       (d->block_size != 0 || !scan_fuses_ingest(d->dtype, d->idx_heads, d->idx_dim, d->m) ||
        !scan_reads_mxfp4(d->dtype, d->idx_heads, d->idx_dim, 1, false)))
     return CSA_ERR_UNSUPPORTED;
@@ -579,7 +582,7 @@ int check_decode(const csa_decode_desc* d) {
   if (d->compressor == CSA_COMP_C4A &&
       (!d->xb_new || !d->zb_new || !d->xb_tail || !d->zb_tail || !d->bias_b))
     return CSA_ERR_NULL;
-  if (d->idx_format == CSA_IDX_MXFP4) {
+  if (d->idx_format != CSA_IDX_DTYPE) {
     if (!d->k_idx_scale) return CSA_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(d->k_idx) % 16 != 0 ||
         reinterpret_cast<uintptr_t>(d->k_idx_scale) % 4 != 0)
@@ -623,7 +626,7 @@ int decode_step_run(const csa_decode_desc* d, void* ws, void* stream) {
   in.x_new = d->x_new; in.z_new = d->z_new; in.xi_new = d->xi_new; in.zi_new = d->zi_new;
   in.x_tail = d->x_tail; in.z_tail = d->z_tail; in.xi_tail = d->xi_tail; in.zi_tail = d->zi_tail;
   in.bias = d->bias; in.bias_i = d->bias_i; in.kv = d->kv; in.k_idx = d->k_idx;
-  void* key_scales = d->idx_format == CSA_IDX_MXFP4 ? d->k_idx_scale : nullptr;
+  void* key_scales = d->idx_format != CSA_IDX_DTYPE ? d->k_idx_scale : nullptr;
   in.k_scale = key_scales;
   in.kv_fmt = kv_fmt_of(d);
   in.kv_gamma = d->kv_gamma;
@@ -687,7 +690,8 @@ int decode_step_run(const csa_decode_desc* d, void* ws, void* stream) {
     if (scan_rows(d->dtype, d->q_idx, d->w, d->k_idx, d->pos, nullptr, nullptr, 0, rows, 1,
                   d->e_cap, d->idx_heads, d->idx_dim, d->m, w.flat, s, split_ingest,
                   d->top_k, d->scan_events, key_scales,
-                  d->score_format == CSA_SCORE_BF16) != hipSuccess)
+                  d->score_format == CSA_SCORE_BF16,
+                  d->idx_format == CSA_IDX_MXFP4_QK) != hipSuccess)
       return CSA_ERR_HIP;
     mark(2);
     const SegArgs seg = segments_for(w.flat, d->dtype, d->idx_heads, d->idx_dim, 1, false, rows,

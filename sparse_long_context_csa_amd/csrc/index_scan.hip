@@ -547,6 +547,58 @@ __device__ __forceinline__ void dequant_B(const u32x4_t cw, uint32_t sbyte, bf16
   }
 }
 
+// FP4 query-key path: the query as MXFP4 (the keys' rule, mxfp4.hpp), one 32-channel block per
+// thread of the workgroup (64 heads x 4 blocks = 256): thread t quantises head t / 4, channels
+// 32 (t % 4) .. + 31 into qc[t] (16 code bytes, channel 32 (t % 4) + k in nibble k of dword
+// k / 8, the key chunks' order) and qs[t] (its scale byte). The caller publishes them with a
+// barrier; lane (g, col) of the MFMA then takes block 4 (16 mt + col) + g as A[mt].
+__device__ __forceinline__ void quantize_query_block(const uint16_t* q, int t, uint4* qc,
+                                                     uint8_t* qs) {
+  const uint4* p = reinterpret_cast<const uint4*>(q + (t >> 2) * kID + 32 * (t & 3));
+  uint32_t w[16];   // the block's 32 bf16 values, two per word (low half first)
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 v = p[c];
+    w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
+  }
+  // the largest magnitude: an integer maximum of the magnitude bits (monotone for bf16)
+  uint32_t mb = 0u;
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    mb = __builtin_elementwise_max(mb, __builtin_elementwise_max(w[k] & 0x7fffu,
+                                                                 (w[k] >> 16) & 0x7fffu));
+  const int s = mx_shared_exp(__uint_as_float(mb << 16));
+  // 2^-s: a normal float for s >= -126, 2^127 for s = -127
+  const float inv = __uint_as_float(uint32_t(s > -127 ? 127 - s : 254) << 23);
+  uint32_t code[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    code[d] = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      code[d] |= e2m1_code(bf16_lo(w[4 * d + k]) * inv) << (8 * k);
+      code[d] |= e2m1_code(bf16_hi(w[4 * d + k]) * inv) << (8 * k + 4);
+    }
+  }
+  qc[t] = make_uint4(code[0], code[1], code[2], code[3]);
+  qs[t] = uint8_t(s + 127);
+}
+
+// The 4 MFMAs of one 16-key group on the FP4 query-key path: acc[mt] = the FP4 query heads of
+// mt x the group's FP4 keys (code chunk and scale byte of this lane), K = 128 in one
+// instruction; the products of two FP4 values under power-of-two scales are exact.
+__device__ __forceinline__ void tile_mfma_fp4(const u32x4_t (&A)[4], const uint32_t (&sa)[4],
+                                              const u32x4_t cw, uint32_t sb, f32x4_t (&acc)[4]) {
+  typedef int v8i_t __attribute__((ext_vector_type(8)));
+  const v8i_t b = {int(cw[0]), int(cw[1]), int(cw[2]), int(cw[3]), 0, 0, 0, 0};
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const v8i_t am = {int(A[mt][0]), int(A[mt][1]), int(A[mt][2]), int(A[mt][3]), 0, 0, 0, 0};
+    acc[mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        am, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, int(sa[mt]), 0, int(sb));
+  }
+}
+
 // The code chunk and scale byte of the lanes that hold the new entry (its group and column,
 // from its offset off in the tile): the tile was loaded before the entry was written. v holds
 // code byte l of the entry in lane l and the scale byte of the lane's block; lane (g, col)
@@ -570,16 +622,20 @@ __device__ __forceinline__ void patch_new_key_q4(uint32_t v, int off, int g, int
     }
 }
 
-// kQ4: MXFP4 keys (a.key_scales), 64-key tiles; else bf16 keys, 16-key tiles.
-template <bool NT, bool kSeg, int kSD, bool kQ4>
+// kQ4: MXFP4 keys (a.key_scales), 64-key tiles; else bf16 keys, 16-key tiles. kQK (with kQ4):
+// the query quantised to MXFP4 as well, the products taken by the FP4 MFMA.
+template <bool NT, bool kSeg, int kSD, bool kQ4, bool kQK = false>
 __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chunk, int64_t cpr,
                                                           int64_t n_items, int rot) {
+  static_assert(kQ4 || !kQK, "the FP4 query-key path reads MXFP4 keys");
   constexpr int kTK = kQ4 ? kQ4Keys : 16;   // keys per wave tile
   __shared__ __attribute__((aligned(16))) unsigned char ring[4][kSD][kTileLds];
   __shared__ SegLds segl;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, col = lane & 15;
   bf16x8_t A[4][4];
+  u32x4_t A4[4];
+  uint32_t sa4[4];
   float wv[4][4];
   int64_t cur = -1;
   const bool fuse = a.ingest.pos != nullptr;
@@ -611,7 +667,19 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
     const int64_t n_pos = row_visible(a, r);
     if (r != cur) {
       const uint16_t* qr = reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID;
-      if (kQ4) load_query_A_q4(qr, lane, A);
+      if constexpr (kQK) {
+        __shared__ uint4 qc[kIH * 4];
+        __shared__ uint8_t qs[kIH * 4];
+        quantize_query_block(qr, int(threadIdx.x), qc, qs);
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const uint4 v = qc[4 * (16 * mt + col) + g];
+          A4[mt] = u32x4_t{v.x, v.y, v.z, v.w};
+          sa4[mt] = qs[4 * (16 * mt + col) + g];
+        }
+        __syncthreads();   // every lane has its operands before a later row overwrites them
+      } else if (kQ4) load_query_A_q4(qr, lane, A);
       else load_query_A(qr, lane, A);
       load_gates(a.w + r * kIH, lane, wv);
       cur = r;
@@ -675,24 +743,42 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
             // are scored too (their keys are the item's last one) and not stored.
             f32x4_t acc[2][4];
             float scb[4];
-            bf16x8_t B[4];
-            dequant_B(cw[0], sc4[0], B);
-            tile_mfma(A, B, acc[0]);
+            if constexpr (kQK) {
+              // FP4 x FP4: group j + 1's 4 MFMAs go out before the epilogue of group j, each
+              // followed by a quarter of that epilogue
+              tile_mfma_fp4(A4, sa4, cw[0], sc4[0], acc[0]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (j + 1 < 4) {
-                dequant_B(cw[j + 1], sc4[j + 1], B);
-                tile_mfma(A, B, acc[(j + 1) & 1]);
+              for (int j = 0; j < 4; ++j) {
+                if (j + 1 < 4) tile_mfma_fp4(A4, sa4, cw[j + 1], sc4[j + 1], acc[(j + 1) & 1]);
+                scb[j] = lane_part(acc[j & 1], wv);
+                if (j + 1 < 4) {
+#pragma unroll
+                  for (int q = 0; q < 4; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                  }
+                }
               }
-              scb[j] = lane_part(acc[j & 1], wv);
-              if (j + 1 < 4) {
-                // issue order: the next group's 16 conversions, then each of its 16 MFMAs
-                // followed by two VALU instructions of this group's epilogue
-                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+            } else {
+              bf16x8_t B[4];
+              dequant_B(cw[0], sc4[0], B);
+              tile_mfma(A, B, acc[0]);
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                  __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+              for (int j = 0; j < 4; ++j) {
+                if (j + 1 < 4) {
+                  dequant_B(cw[j + 1], sc4[j + 1], B);
+                  tile_mfma(A, B, acc[(j + 1) & 1]);
+                }
+                scb[j] = lane_part(acc[j & 1], wv);
+                if (j + 1 < 4) {
+                  // issue order: the next group's 16 conversions, then each of its 16 MFMAs
+                  // followed by two VALU instructions of this group's epilogue
+                  __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+#pragma unroll
+                  for (int q = 0; q < 16; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                  }
                 }
               }
             }
@@ -905,7 +991,7 @@ bool scan_reads_mxfp4(int dt, int H, int d, int64_t n_q, bool cand) {
   return dt == kBF16 && H == kIH && d == kID && n_q < 16 && !cand;
 }
 
-template <bool kQ4>
+template <bool kQ4, bool kQK = false>
 static void launch_stream(const ScanArgs& a, int chunk, int64_t cpr, int64_t items, hipStream_t s,
                           hipEvent_t e0, hipEvent_t e1) {
   int64_t grid = scan_grid();
@@ -915,7 +1001,8 @@ static void launch_stream(const ScanArgs& a, int chunk, int64_t cpr, int64_t ite
   const int sd = kQ4 ? scan_tune().sd4 : scan_tune().sd;
   const bool segs = a.seg.seg != nullptr;
 #define CSA_STREAM(SEG, SD)                                                                  \
-  launch_k(scan_stream_kernel<true, SEG, SD, kQ4>, gd, bd, 0, s, e0, e1, a, chunk, cpr, items, rot)
+  launch_k(scan_stream_kernel<true, SEG, SD, kQ4, kQK>, gd, bd, 0, s, e0, e1, a, chunk, cpr, items, \
+           rot)
   if (segs) {
     if (sd == 2) CSA_STREAM(true, 2);
     else if (sd == 3) CSA_STREAM(true, 3);
@@ -935,6 +1022,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s, hipEvent_t e0, hipEvent
   const bool q4 = a.key_scales != nullptr;
   if ((q4 || a.score_bf16) && !scan_reads_mxfp4(a.dt, a.H, a.d, a.n_q, a.cand != nullptr))
     return hipErrorInvalidValue;
+  if (a.q_fp4 && !q4) return hipErrorInvalidValue;
   if (!q4 && fast_shape(a) && a.cand == nullptr && a.n_q >= 16) {
     const int keys_per_block = scan_tune().prefill_keys;
     const int pq = scan_tune().prefill_q == 8 ? 8 : 12;
@@ -951,7 +1039,8 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t s, hipEvent_t e0, hipEvent
       if (chunk > kSegMaxChunk) return hipErrorInvalidValue;
       const int64_t cpr = (max_pos + chunk - 1) / chunk;
       const int64_t items = rows * cpr;
-      if (q4) launch_stream<true>(a, chunk, cpr, items, s, e0, e1);
+      if (q4 && a.q_fp4) launch_stream<true, true>(a, chunk, cpr, items, s, e0, e1);
+      else if (q4) launch_stream<true>(a, chunk, cpr, items, s, e0, e1);
       else launch_stream<false>(a, chunk, cpr, items, s, e0, e1);
     }
     return hipGetLastError();

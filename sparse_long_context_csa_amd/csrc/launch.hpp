@@ -114,6 +114,9 @@ struct ScanArgs {
   IngestArgs ingest;
   SegArgs seg;            // decode scan without candidates: candidate segments (optional)
   int score_bf16;         // the stream scan rounds every score to bf16 before it leaves
+  // with MXFP4 keys: the query is quantised to MXFP4 too (the keys' rule, per head and 32
+  // channels) and the products are taken between the FP4 values
+  int q_fp4;
 };
 // ev_start / ev_stop (both or neither): the start and stop events of the scan kernel's own
 // dispatch (a scan is one kernel).

@@ -266,7 +266,8 @@ def run_step(case, idx_state=None):
                           q_rope_dim=int(case.get("q_rope_dim", 0)),
                           kv_gamma=(dev(case["kv_gamma"]) if case.get("kv_gamma") is not None
                                     else None),
-                          kv_rope_dim=int(case.get("kv_rope_dim", 0)), **st, **kw)
+                          kv_rope_dim=int(case.get("kv_rope_dim", 0)),
+                          query_fp4=case.get("idx_format") == "mxfp4_qk", **st, **kw)
     out, idx = step()
     torch.cuda.synchronize()
     return step, st, rings, [o.cpu() for o in out], idx.cpu()
@@ -323,7 +324,7 @@ def check_step(case, ref, st, rings, out, idx):
                     assert_fp4_entry(st["kv"][b, e].cpu().numpy(), exact, xmax,
                                      f"FP4 entry {e} of seq {b}")
                     continue
-                if name == "k_idx" and case.get("idx_format") == "mxfp4":
+                if name == "k_idx" and case.get("idx_format") in ("mxfp4", "mxfp4_qk"):
                     assert_mx_entry(st["k_idx"][b, e].cpu().numpy(),
                                     st["k_idx_scale"][b, e].cpu().numpy(), exact,
                                     np.abs(x).max(axis=0), f"MXFP4 key entry {e} of seq {b}")

@@ -95,6 +95,7 @@ def test_decode_desc_mirrors_the_header_struct():
     assert C.sizeof(_lib.DecodeDesc) == (64 + 8 + 8 * n_ptr + 8 + 8 + 16 + 8 * _lib.MAX_ATTN
                                          + 8 + 8 + 8 + 5 * 8)
     for name, val in (("CSA_IDX_DTYPE", _lib.IDX_DTYPE), ("CSA_IDX_MXFP4", _lib.IDX_MXFP4),
+                      ("CSA_IDX_MXFP4_QK", _lib.IDX_MXFP4_QK),
                       ("CSA_SCORE_F32", _lib.SCORE_F32), ("CSA_SCORE_BF16", _lib.SCORE_BF16),
                       ("CSA_KV_DTYPE", _lib.KV_DTYPE), ("CSA_KV_FP8", _lib.KV_FP8),
                       ("CSA_KV_FP8_BYTES", _lib.KV_FP8_BYTES), ("CSA_KV_FP4", _lib.KV_FP4),
@@ -350,20 +351,21 @@ def test_decode_mxfp4_validation(lib):
         return lib.csa_decode_step(C.byref(d), ws, nb, None)
 
     # every call below is refused before anything is launched
-    assert step(full(idx_format=2)) == -2
-    assert step(full(block_size=8, max_blocks=64)) == -4      # hierarchical: not with MXFP4
-    assert step(full(m=16)) == -4                             # the scan pools m <= 8 only
-    assert step(full(idx_dim=64)) == -4
-    assert step(full(dtype=0)) == -4                          # fp32 step
-    d = full()
-    d.k_idx_scale = None
-    assert step(d) == -1
-    d = full()
-    d.k_idx = 256 + 8                                         # codes not 16-byte aligned
-    assert step(d) == -2
-    d = full()
-    d.k_idx_scale = 256 + 2
-    assert step(d) == -2
+    assert step(full(idx_format=3)) == -2
+    for fmt in (_lib.IDX_MXFP4, _lib.IDX_MXFP4_QK):          # keys alone, or keys and query
+        assert step(full(idx_format=fmt, block_size=8, max_blocks=64)) == -4   # hierarchical
+        assert step(full(idx_format=fmt, m=16)) == -4         # the scan pools m <= 8 only
+        assert step(full(idx_format=fmt, idx_dim=64)) == -4
+        assert step(full(idx_format=fmt, dtype=0)) == -4      # fp32 step
+        d = full(idx_format=fmt)
+        d.k_idx_scale = None
+        assert step(d) == -1
+        d = full(idx_format=fmt)
+        d.k_idx = 256 + 8                                     # codes not 16-byte aligned
+        assert step(d) == -2
+        d = full(idx_format=fmt)
+        d.k_idx_scale = 256 + 2
+        assert step(d) == -2
     assert lib.csa_decode_step_workspace_size(C.byref(full(m=16))) == 0
     # BF16 scores: flat selection and the stream scan's shapes only
     d = full(idx_format=_lib.IDX_DTYPE, score_format=_lib.SCORE_BF16, block_size=8,

@@ -39,11 +39,15 @@ def test_decode_1m_overlapped_compressor():
     check_step(case, ref, st, rings, out, idx)
 
 
+@pytest.mark.parametrize("query", ["bf16", "fp4"])
 @pytest.mark.parametrize("cfg", [2, 4])
-def test_decode_workload_fullsize_mxfp4_keys(cfg):
+def test_decode_workload_fullsize_mxfp4_keys(cfg, query):
     """The flat decode workloads with the indexer cache in MXFP4 (the bench's --idx-format
-    mxfp4 line): the GPU quantises the generated keys, the oracle scores their MXFP4 values."""
+    mxfp4 line) and, with query "fp4", the indexer query in MXFP4 too (--idx-format
+    mxfp4qk): the GPU quantises the generated keys, the oracle scores their MXFP4 values."""
     case, idx_state = mxfp4_case(datagen.CONFIGS[cfg])
+    if query == "fp4":
+        case["idx_format"] = "mxfp4_qk"
     print(f"config {cfg} (MXFP4 keys): inputs ready", flush=True)
     gaps.enforce_decode(case)
     _, st, rings, out, idx = run_step(case, idx_state)

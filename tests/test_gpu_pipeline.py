@@ -124,16 +124,20 @@ def test_decode_step_segments_odd_k_and_window():
     check_step(case, ref, st, rings, out, idx)
 
 
-# MXFP4 indexer cache: the scan dequantises 64-key tiles of codes and scale bytes; the entry a
-# step completes is pooled, quantised and stored by the scan.
+# MXFP4 indexer cache: the scan dequantises 64-key tiles of codes and scale bytes (or, with the
+# query in FP4 too, multiplies the codes by the FP4 query in the scaled MFMA); the entry a step
+# completes is pooled, quantised and stored by the scan.
+@pytest.mark.parametrize("query", ["bf16", "fp4"])
 @pytest.mark.parametrize("spec", [
     datagen.CaseSpec(7120, "decode", B=5, L=24000, m=4, w_cap=256, ragged=True),
     datagen.CaseSpec(7121, "decode", B=3, L=4 * 60000, m=4, w_cap=256, ragged=True),
     datagen.CaseSpec(7122, "decode", B=4, L=2400, e_cap=40000, m=4, w_cap=128, ragged=True),
     datagen.CaseSpec(7123, "decode", B=3, L=20000, m=1, w_cap=128, ragged=True),
 ], ids=["flat", "segments", "short_rows", "m1"])
-def test_decode_step_mxfp4_keys(spec):
+def test_decode_step_mxfp4_keys(spec, query):
     case, idx_state = mxfp4_case(spec)
+    if query == "fp4":
+        case["idx_format"] = "mxfp4_qk"
     gaps.enforce_decode(case)
     ref = pipeline.decode_step(case)
     step, st, rings, out, idx = run_step(case, idx_state)
@@ -160,8 +164,11 @@ def test_decode_step_mxfp4_keys(spec):
     datagen.CaseSpec(7126, "decode", B=2, L=2 * 30000, m=2, K=500, W=100, w_cap=128,
                      ragged=True),
 ], ids=["e_cap_40003", "m8", "m2_odd_k"])
-def test_decode_step_mxfp4_keys_edges(spec):
+@pytest.mark.parametrize("query", ["bf16", "fp4"])
+def test_decode_step_mxfp4_keys_edges(spec, query):
     case, idx_state = mxfp4_case(spec)
+    if query == "fp4":
+        case["idx_format"] = "mxfp4_qk"
     gaps.enforce_decode(case)
     ref = pipeline.decode_step(case)
     _, st, rings, out, idx = run_step(case, idx_state)
@@ -199,15 +206,16 @@ def test_decode_step_clustered_winners_formats(fmt):
 # BF16 index scores: the scan rounds every score to bf16 before it leaves; the selection (ties
 # at the K-th value to the lower id) must match the oracle's ranking of its fp32 scores rounded
 # to bf16, id for id.
-@pytest.mark.parametrize("keys", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("keys", ["bf16", "mxfp4", "mxfp4_qk"])
 @pytest.mark.parametrize("spec", [
     datagen.CaseSpec(7130, "decode", B=5, L=24000, m=4, w_cap=256, ragged=True),
     datagen.CaseSpec(7131, "decode", B=3, L=4 * 60000, m=4, w_cap=256, ragged=True),
     datagen.CaseSpec(7132, "decode", B=4, L=2400, e_cap=40000, m=4, w_cap=128, ragged=True),
 ], ids=["flat", "segments", "short_rows"])
 def test_decode_step_bf16_scores(spec, keys):
-    if keys == "mxfp4":
+    if keys.startswith("mxfp4"):
         case, idx_state = mxfp4_case(spec)
+        case["idx_format"] = keys
     else:
         case, idx_state = datagen.make_case(spec), None
     case["score_format"] = "bf16"

@@ -118,6 +118,48 @@ def test_m1_new_entry_is_the_raw_row():
         np.testing.assert_array_equal(res["ki_new"][b], f64(case["xi_new"][b]))
 
 
+def test_fp4_query_key_path_hand_worked():
+    # [CoD "FP4, down to the index scores"]: the query-key path multiplies FP4 values. One head,
+    # one 32-channel block of the query: max |q| = 0.75 -> s = -3, q / 2^s = 8 q rounds to
+    # [6, 1, 1.5, 0, 1, -2, 1, 2, 4, -6] (ties to the even code), i.e. q4 = [0.75, 0.125,
+    # 0.1875, 0, 0.125, -0.25, 0.125, 0.25, 0.5, -0.75]; a key of ones is exact in MXFP4. Score
+    # w * ReLU(q4 . k) = 1.0625 against 1.03125 for the unquantised query.
+    q = np.zeros((1, 32))
+    q[0, :10] = [0.75, 0.1, 0.2, 0.03125, 0.09375, -0.3, 0.15625, 0.3125, 0.4375, -0.75]
+    case = {"idx_format": "mxfp4_qk"}
+    q4 = pipeline.index_query(case, q)
+    assert q4[0, :10].tolist() == [0.75, 0.125, 0.1875, 0.0, 0.125, -0.25, 0.125, 0.25, 0.5,
+                                   -0.75]
+    k = pipeline.cached_index_key(case, np.ones(32))
+    assert np.array_equal(k, np.ones(32))
+    assert csa.index_scores(q4, np.ones(1), k[None])[0] == 1.0625
+    assert csa.index_scores(pipeline.index_query({"idx_format": "mxfp4"}, q), np.ones(1),
+                            k[None])[0] == 1.03125
+
+
+def test_fp4_query_key_path_quantises_each_head():
+    # the decode step on the FP4 query-key path equals the MXFP4-key step given, for each head
+    # on its own, the query's MXFP4 value (quantised here block by block in a loop); its scores
+    # differ from those of the bf16 query
+    case = small_decode(case_id=907, m=1, L=300, d_I=64, ragged=False)
+    spec = case["spec"]
+    res = pipeline.decode_step(dict(case, idx_format="mxfp4_qk"))
+    qv = f64(case["q_idx"]).copy()
+    for b in range(spec.B):
+        for h in range(spec.H_I):
+            for blk in range(spec.d_I // 32):
+                v = qv[b, h, 32 * blk:32 * blk + 32]
+                c, sc = mx.quantize(v[None])
+                qv[b, h, 32 * blk:32 * blk + 32] = mx.dequantize(c, sc)[0]
+    moved = dict(case, idx_format="mxfp4", q_idx=torch.from_numpy(qv))
+    want = pipeline.decode_step(moved)
+    plain = pipeline.decode_step(dict(case, idx_format="mxfp4"))
+    for b in range(spec.B):
+        np.testing.assert_array_equal(res["scores"][b], want["scores"][b])
+        np.testing.assert_array_equal(res["ids"][b], want["ids"][b])
+        assert not np.array_equal(res["scores"][b], plain["scores"][b])
+
+
 def test_mxfp4_cache_scores_the_new_key_on_the_grid():
     # m = 1: the new entry's key is the raw row xi_new; with an MXFP4 cache it is scored at its
     # E2M1 x 2^s value, every other entry as case["k_idx"] holds it
