@@ -110,10 +110,11 @@ __device__ __forceinline__ float e4m3_pos_value(uint32_t code) {
 // below 2^-11), so every comparison is exact.
 __device__ __forceinline__ uint32_t e2m1_code_scaled(float x, float s) {
   const float a = fabsf(x);
-  const uint32_t c = a <= 0.25f * s ? 0u : a < 0.75f * s ? 1u : a <= 1.25f * s ? 2u
-                   : a < 1.75f * s ? 3u : a <= 2.5f * s ? 4u : a < 3.5f * s ? 5u
-                   : a <= 5.f * s ? 6u : 7u;
-  return (c != 0u && x < 0.f) ? (c | 8u) : c;
+  // midpoints reached (those below an even code) or passed (the others): no branches
+  const uint32_t c = uint32_t(a > 0.25f * s) + uint32_t(a >= 0.75f * s) +
+                     uint32_t(a > 1.25f * s) + uint32_t(a >= 1.75f * s) +
+                     uint32_t(a > 2.5f * s) + uint32_t(a >= 3.5f * s) + uint32_t(a > 5.f * s);
+  return c | (uint32_t(x < 0.f && c != 0u) << 3);
 }
 
 // Channels c0 .. c0+7 (c0 % 8 == 0) of an FP4 entry from their stored values v: the lane

@@ -552,15 +552,17 @@ __device__ __forceinline__ void dequant_B(const u32x4_t cw, uint32_t sbyte, bf16
 // 32 (t % 4) .. + 31 into qc[t] (16 code bytes, channel 32 (t % 4) + k in nibble k of dword
 // k / 8, the key chunks' order) and qs[t] (its scale byte). The caller publishes them with a
 // barrier; lane (g, col) of the MFMA then takes block 4 (16 mt + col) + g as A[mt].
-__device__ __forceinline__ void quantize_query_block(const uint16_t* q, int t, uint4* qc,
-                                                     uint8_t* qs) {
+// the block's 32 bf16 values, two per word (low half first)
+__device__ __forceinline__ void load_query_block(const uint16_t* q, int t, uint32_t (&w)[16]) {
   const uint4* p = reinterpret_cast<const uint4*>(q + (t >> 2) * kID + 32 * (t & 3));
-  uint32_t w[16];   // the block's 32 bf16 values, two per word (low half first)
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const uint4 v = p[c];
     w[4 * c] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
   }
+}
+__device__ __forceinline__ void quantize_query_block(const uint32_t (&w)[16], int t, uint4* qc,
+                                                     uint8_t* qs) {
   // the largest magnitude: an integer maximum of the magnitude bits (monotone for bf16)
   uint32_t mb = 0u;
 #pragma unroll
@@ -663,23 +665,15 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
     };
     // The row's visible count, query and gates, and the inputs of the entry this step's token
     // completes (pooled by the wave that scores it), are loaded before the first tiles: a wave's
-    // loads return in issue order, so loads issued after the tiles would wait for them.
+    // loads return in issue order, so loads issued after the tiles would wait for them. The FP4
+    // query is quantised after the first tiles have gone out, while they are in flight.
     const int64_t n_pos = row_visible(a, r);
-    if (r != cur) {
+    uint32_t qw[16];
+    const bool new_row = r != cur;   // uniform over the block
+    if (new_row) {
       const uint16_t* qr = reinterpret_cast<const uint16_t*>(a.q) + r * kIH * kID;
-      if constexpr (kQK) {
-        __shared__ uint4 qc[kIH * 4];
-        __shared__ uint8_t qs[kIH * 4];
-        quantize_query_block(qr, int(threadIdx.x), qc, qs);
-        __syncthreads();
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const uint4 v = qc[4 * (16 * mt + col) + g];
-          A4[mt] = u32x4_t{v.x, v.y, v.z, v.w};
-          sa4[mt] = qs[4 * (16 * mt + col) + g];
-        }
-        __syncthreads();   // every lane has its operands before a later row overwrites them
-      } else if (kQ4) load_query_A_q4(qr, lane, A);
+      if (kQK) load_query_block(qr, int(threadIdx.x), qw);
+      else if (kQ4) load_query_A_q4(qr, lane, A);
       else load_query_A(qr, lane, A);
       load_gates(a.w + r * kIH, lane, wv);
       cur = r;
@@ -698,9 +692,32 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
         load_new_key(a.ingest, r, new_slot, lane, nk);
       }
     }
+    if constexpr (kQK) {
+      // every one of the first kSD tiles goes out, a wave with fewer tiles reading the item's
+      // last key into slots it never reads (its waits only grow stricter), so that the
+      // compiler can count the loads issued after the query's and wait for that alone
 #pragma unroll
-    for (int j = 0; j < kSD; ++j)
-      if (j < nt_item) issue(j, ring[wave][j]);
+      for (int j = 0; j < kSD; ++j) issue(j, ring[wave][j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kSD; ++j)
+        if (j < nt_item) issue(j, ring[wave][j]);
+    }
+    if constexpr (kQK) {
+      if (new_row) {
+        __shared__ uint4 qc[kIH * 4];
+        __shared__ uint8_t qs[kIH * 4];
+        quantize_query_block(qw, int(threadIdx.x), qc, qs);
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const uint4 v = qc[4 * (16 * mt + col) + g];
+          A4[mt] = u32x4_t{v.x, v.y, v.z, v.w};
+          sa4[mt] = qs[4 * (16 * mt + col) + g];
+        }
+        __syncthreads();   // every lane has its operands before a later row overwrites them
+      }
+    }
     if (c == 0 && threadIdx.x == 0) {
       a.n_vis[r] = int32_t(n_pos);
       a.count[r] = int32_t(n_pos);

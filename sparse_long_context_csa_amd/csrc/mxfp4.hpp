@@ -26,12 +26,16 @@ __device__ __forceinline__ int mx_shared_exp(float amax) {
 }
 
 // E2M1 code of v (already divided by the block scale): nearest magnitude, ties to the even
-// code; the thresholds are the midpoints of the magnitudes (exact in binary)
+// code. The code is the number of midpoints between magnitudes (exact in binary) that |v| has
+// reached; at a midpoint the count stops at the even code of its two neighbours, so those below
+// an even code (0.75, 1.75, 3.5) count once reached and the others once passed. Summed
+// comparisons, no branches.
 __device__ __forceinline__ uint32_t e2m1_code(float v) {
   const float a = fabsf(v);
-  uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
-             : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.f ? 6u : 7u;
-  return (c != 0u && v < 0.f) ? (c | 8u) : c;
+  const uint32_t c = uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) +
+                     uint32_t(a >= 1.75f) + uint32_t(a > 2.5f) + uint32_t(a >= 3.5f) +
+                     uint32_t(a > 5.f);
+  return c | (uint32_t(v < 0.f && c != 0u) << 3);
 }
 
 // value of an E2M1 code times 2^(s - 127) (exact in fp32 and in bf16)
