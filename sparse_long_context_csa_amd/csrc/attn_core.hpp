@@ -330,10 +330,9 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
   // rows 8 w .. 8 w + 7 of tile t into buffer b; rows past the list (and rows without a
   // valid address) read the query row and are masked
   // A quantised entry row (kv_fmt FP8 or FP4, list row < top_k) moves as its raw bytes (576 or
-  // 288: lanes 0 .. 35 or 0 .. 17 of the DMA, the others masked off, so the active lanes are a
-  // prefix and land at the start of the slot) and is expanded in place to the bf16 layout once
-  // it has landed (expand), which rewrites all 1,024 bytes of the slot. qmask bit 8 b + i: row
-  // 8 w + i of buffer b.
+  // 288: lanes 0 .. 35 or 0 .. 17 of the DMA; the others fetch query bytes into the rest of the
+  // slot) and is expanded in place to the bf16 layout once it has landed (expand), which
+  // rewrites all 1,024 bytes of the slot. qmask bit 8 b + i: row 8 w + i of buffer b.
   const int kvf = a.kv_fmt;
   const int raw_lanes = kvf == kKvFp8 ? kFp8EntryBytes / 16 : kFp4EntryBytes / 16;
   uint32_t qmask = 0u;
@@ -346,10 +345,10 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
       const uint16_t* p = jr < nl ? L.rowp[jr] : nullptr;
       const bool qz = p != nullptr && kvf != kKvPlain && j0 + jr < a.top_k;   // uniform
       if (qz) {
-        if (lane < raw_lanes)
-          dma_row(reinterpret_cast<const uint16_t*>(reinterpret_cast<const unsigned char*>(p) +
-                                                    16 * lane),
-                  &L.kv[b][tr * kKvRowD]);
+        const unsigned char* src = lane < raw_lanes
+                                       ? reinterpret_cast<const unsigned char*>(p) + 16 * lane
+                                       : reinterpret_cast<const unsigned char*>(qrow) + 16 * lane;
+        dma_row(reinterpret_cast<const uint16_t*>(src), &L.kv[b][tr * kKvRowD]);
         qmask |= 1u << (8 * b + i);
       } else {
         dma_row((p != nullptr ? p : qrow) + (lane ^ kv_swz(tr)) * 8, &L.kv[b][tr * kKvRowD]);
