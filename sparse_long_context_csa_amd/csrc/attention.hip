@@ -97,15 +97,18 @@ __global__ __launch_bounds__(256, 2) void attn_dma_kernel(AttnArgs a, int nsplit
                  [&](int64_t j, int nrows) { return row_ptr<uint16_t>(a, r, sq, t, j, nrows); });
 }
 
-// Merge the row splits in split order. Grid (32, rows): workgroup x covers the heads of
-// accumulator wave w = x / 8 and the dims of 4 accumulator columns; its first 16 threads
-// compute the split weights e^{m_s - M} / den of those 16 heads into LDS, then every thread
-// sums its float4 (4 heads, 1 dim) over the splits with independent loads.
+// Merge the row splits. Grid (32, rows): workgroup x covers the heads of accumulator wave
+// w = x / 8 and the dims of 4 accumulator columns; its threads compute the split weights
+// e^{m_s - M} of those 16 heads into LDS (16 threads per head, each over every 16th split),
+// then every thread sums its 4 heads x 1 dim over the splits in split order with independent
+// loads and scales by 1 / den.
 constexpr int kMaxSplit = 256;
 
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nsplit) {
   __shared__ float wgt[kMaxSplit][16];
   __shared__ float2 mls[kMaxSplit][16];
+  __shared__ float red[16][16];
+  __shared__ float inv[16];
   const int64_t r = blockIdx.y;
   const int w = blockIdx.x >> 3;
   const int nt = (blockIdx.x & 7) * 4 + (threadIdx.x >> 6);
@@ -122,22 +125,37 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
   for (int q = threadIdx.x; q < nsplit * 16; q += blockDim.x)
     mls[q >> 4][q & 15] = ml[(q >> 4) * kAH + 16 * w + (q & 15)];
   __syncthreads();
-  if (threadIdx.x < 16) {
-    const int h = 16 * w + threadIdx.x;
-    const float zs = a.sink ? a.sink[h] * kLog2e : neg_inf();
+  // split weights e^(m_s - M) of the 16 heads: thread (group k, head hl) takes splits k, k + 16,
+  // ...; the maxima and the denominators' partial sums meet in red (fixed order: the result
+  // does not depend on scheduling). The 1 / denominator multiplies the sums at the end.
+  {
+    const int hl = threadIdx.x & 15, k = threadIdx.x >> 4;
+    float mloc = neg_inf();
+    for (int sp = k; sp < nsplit; sp += 16) mloc = fmaxf(mloc, mls[sp][hl].x);
+    red[k][hl] = mloc;
+    __syncthreads();
+    const float zs = a.sink ? a.sink[16 * w + hl] * kLog2e : neg_inf();
     float M = zs;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, mls[sp][threadIdx.x].x);
-    float den = (zs == neg_inf() || M == neg_inf()) ? 0.f : exp2f(zs - M);
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float2 m2 = mls[sp][threadIdx.x];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) M = fmaxf(M, red[j][hl]);
+    __syncthreads();   // every thread has its maximum before red holds the sums
+    float dloc = 0.f;
+    for (int sp = k; sp < nsplit; sp += 16) {
+      const float2 m2 = mls[sp][hl];
       const float e = (m2.x == neg_inf() || M == neg_inf()) ? 0.f : exp2f(m2.x - M);
-      wgt[sp][threadIdx.x] = e;
-      den += m2.y * e;
+      wgt[sp][hl] = e;
+      dloc += m2.y * e;
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) wgt[sp][threadIdx.x] *= inv;
+    red[k][hl] = dloc;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+      float den = (zs == neg_inf() || M == neg_inf()) ? 0.f : exp2f(zs - M);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) den += red[j][hl];
+      inv[hl] = den > 0.f ? 1.f / den : 0.f;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   const int g = lane >> 4, col = lane & 15;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   auto add = [&](const uint2 c, int sp) {
@@ -149,7 +167,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
 #pragma unroll
   for (int sp = 0; sp < kSplitRegs; ++sp)
     if (sp < nsplit) add(v[sp], sp);
-  for (int sp = kSplitRegs; sp < nsplit; ++sp) add(part[sp * sstride], sp);
+  // further splits in chunks of kSplitRegs, each chunk's loads issued together
+  for (int s0 = kSplitRegs; s0 < nsplit; s0 += kSplitRegs) {
+#pragma unroll
+    for (int k = 0; k < kSplitRegs; ++k)
+      v[k] = s0 + k < nsplit ? part[(s0 + k) * sstride] : make_uint2(0u, 0u);
+#pragma unroll
+    for (int k = 0; k < kSplitRegs; ++k)
+      if (s0 + k < nsplit) add(v[k], s0 + k);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] *= inv[4 * g + i];
   uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + (r * kAH + 16 * w + 4 * g) * kAD + nt * 16 + col;
   if (a.out_rope_dim > 0 && nt * 16 >= kAD - a.out_rope_dim) {   // uniform over the wave
     const int d = nt * 16 + col;
