@@ -38,12 +38,28 @@ __global__ __launch_bounds__(256) void compress_kernel(const T* __restrict__ x,
   Elt<T>::store8(out + sq * out_seq_stride + e * dim + c0, res);
 }
 
-// Long entries (m > 16, HCA's m' = 128): a workgroup pools one entry for 16 vectors (128
-// channels) with 16 row groups -- thread (group g, vector v) takes rows g, g + 16, ... < m,
-// all loaded before any arithmetic, and keeps a partial softmax (maximum, sum, weighted sum);
-// the 16 partials of a vector merge in LDS. Every input row is read once.
-constexpr int kWideGroups = 16;
-constexpr int kWideVecs = 16;
+// Long entries (m > 16, HCA's m' = 128): a workgroup pools one entry for 8 vectors (64
+// channels) with 32 row groups -- thread (group g, vector v) takes rows g, g + 32, ... < m
+// (4 at most), all of them and their biases loaded in one round before any arithmetic, and
+// keeps a partial softmax (maximum, sum, weighted sum) over them. The 8 groups of a wave merge
+// by lane shuffles (the lanes of one vector are 8 apart), the 4 waves through LDS. Every
+// input row is read once.
+constexpr int kWideGroups = 32;
+constexpr int kWideVecs = 8;
+constexpr int kWideRows = 4;   // rows per thread: m <= kWideGroups * kWideRows = 128
+
+// (m, s, a) of two partial softmaxes over disjoint rows, merged (an empty one has m = -inf)
+__device__ __forceinline__ void merge_softmax(float& m, float& s, float& a, float mo, float so,
+                                              float ao) {
+  const float mn = fmaxf(m, mo);
+  if (mn == neg_inf()) return;
+  const float e = m == neg_inf() ? 0.f : expf(m - mn);
+  const float eo = mo == neg_inf() ? 0.f : expf(mo - mn);
+  s = s * e + so * eo;
+  a = a * e + ao * eo;
+  m = mn;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void compress_wide_kernel(const T* __restrict__ x,
                                                             const T* __restrict__ z,
@@ -51,8 +67,9 @@ __global__ __launch_bounds__(256) void compress_wide_kernel(const T* __restrict_
                                                             T* __restrict__ out, int64_t n_ent,
                                                             int64_t out_seq_stride, int dim,
                                                             int m) {
-  __shared__ float part[3][kWideGroups][kWideVecs][8];
+  __shared__ float part[3][4][kWideVecs][8];
   const int vl = threadIdx.x % kWideVecs, grp = threadIdx.x / kWideVecs;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nvb = (dim / 8 + kWideVecs - 1) / kWideVecs;   // channel blocks per entry
   const int64_t bid = blockIdx.x;
   const int v = int(bid % nvb) * kWideVecs + vl;
@@ -64,61 +81,67 @@ __global__ __launch_bounds__(256) void compress_wide_kernel(const T* __restrict_
 #pragma unroll
   for (int c = 0; c < 8; ++c) { mx[c] = neg_inf(); sum[c] = 0.f; acc[c] = 0.f; }
   if (live) {
-    constexpr int kR = 8;   // rows per thread held in registers at once (m <= 128)
-    for (int j0 = grp; j0 < m; j0 += kR * kWideGroups) {
-      float xv[kR][8], lv[kR][8];
+    float xv[kWideRows][8], lv[kWideRows][8], bv[kWideRows][8];
 #pragma unroll
-      for (int i = 0; i < kR; ++i) {
-        const int j = j0 + i * kWideGroups;
-        if (j < m) {
-          Elt<T>::load8(x + (row0 + j) * dim + c0, xv[i]);
-          Elt<T>::load8(z + (row0 + j) * dim + c0, lv[i]);
+    for (int i = 0; i < kWideRows; ++i) {
+      const int j = grp + i * kWideGroups;
+      if (j < m) {
+        Elt<T>::load8(x + (row0 + j) * dim + c0, xv[i]);
+        Elt<T>::load8(z + (row0 + j) * dim + c0, lv[i]);
+        Elt<T>::load8(bias + j * dim + c0, bv[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kWideRows; ++i) {
+      if (grp + i * kWideGroups < m) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          lv[i][c] += bv[i][c];
+          mx[c] = fmaxf(mx[c], lv[i][c]);
         }
       }
+    }
 #pragma unroll
-      for (int i = 0; i < kR; ++i) {
-        const int j = j0 + i * kWideGroups;
-        if (j < m) {
-          float bv[8];
-          Elt<T>::load8(bias + j * dim + c0, bv);
+    for (int i = 0; i < kWideRows; ++i) {
+      if (grp + i * kWideGroups < m) {
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const float l = lv[i][c] + bv[c];
-            if (l > mx[c]) {
-              const float r = expf(mx[c] - l);
-              sum[c] *= r;
-              acc[c] *= r;
-              mx[c] = l;
-            }
-            const float p = expf(l - mx[c]);
-            sum[c] += p;
-            acc[c] = fmaf(p, xv[i][c], acc[c]);
-          }
+        for (int c = 0; c < 8; ++c) {
+          const float pw = expf(lv[i][c] - mx[c]);
+          sum[c] += pw;
+          acc[c] = fmaf(pw, xv[i][c], acc[c]);
         }
       }
     }
   }
+  // the wave's 8 groups of this vector: lanes vl, vl + 8, ..., vl + 56
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    part[0][grp][vl][c] = mx[c];
-    part[1][grp][vl][c] = sum[c];
-    part[2][grp][vl][c] = acc[c];
+  for (int o = 8; o < 64; o <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float mo = __shfl_xor(mx[c], o), so = __shfl_xor(sum[c], o), ao = __shfl_xor(acc[c], o);
+      merge_softmax(mx[c], sum[c], acc[c], mo, so, ao);
+    }
+  }
+  if (lane < kWideVecs) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      part[0][wave][vl][c] = mx[c];
+      part[1][wave][vl][c] = sum[c];
+      part[2][wave][vl][c] = acc[c];
+    }
   }
   __syncthreads();
-  // thread (g, vl) merges channel g & 7 of vector vl for g < 8
-  if (grp < 8 && live) {
-    const int c = grp;
-    float M = neg_inf();
+  // thread (vector vl, channel c) of the first 64 merges the 4 waves in order
+  if (threadIdx.x < kWideVecs * 8) {
+    const int vv = threadIdx.x >> 3, c = threadIdx.x & 7;
+    const int v2 = int(bid % nvb) * kWideVecs + vv;
+    if (v2 * 8 < dim) {
+      float M = part[0][0][vv][c], S = part[1][0][vv][c], A = part[2][0][vv][c];
 #pragma unroll
-    for (int g2 = 0; g2 < kWideGroups; ++g2) M = fmaxf(M, part[0][g2][vl][c]);
-    float S = 0.f, A = 0.f;
-#pragma unroll
-    for (int g2 = 0; g2 < kWideGroups; ++g2) {
-      const float w = part[1][g2][vl][c] > 0.f ? expf(part[0][g2][vl][c] - M) : 0.f;
-      S = fmaf(part[1][g2][vl][c], w, S);
-      A = fmaf(part[2][g2][vl][c], w, A);
+      for (int w2 = 1; w2 < 4; ++w2)
+        merge_softmax(M, S, A, part[0][w2][vv][c], part[1][w2][vv][c], part[2][w2][vv][c]);
+      Elt<T>::store1(out + sq * out_seq_stride + e * dim + v2 * 8 + c, A / S);
     }
-    Elt<T>::store1(out + sq * out_seq_stride + e * dim + c0 + c, A / S);
   }
 }
 
