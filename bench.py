@@ -99,7 +99,8 @@ def cpu_baseline(case, budget_s):
 TRAFFIC_FILES = {
     fmt: os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", name)
     for fmt, name in (("bf16", "decode_1m_hbm_traffic.json"),
-                      ("mxfp4", "decode_1m_mxfp4_hbm_traffic.json"))}
+                      ("mxfp4", "decode_1m_mxfp4_hbm_traffic.json"),
+                      ("mxfp4qk", "decode_1m_mxfp4qk_hbm_traffic.json"))}
 
 
 def source_digest(files) -> str:
