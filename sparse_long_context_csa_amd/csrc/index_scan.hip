@@ -200,17 +200,34 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
   return __builtin_elementwise_max(uint32_t(q[0]), uint32_t(q[1]));
 }
 
+// J of the segment rule for an item of n visible positions in a row of n_pos (> 0): lambda =
+// K / chunks is the mean count of the row's Top-K per chunk (positions are exchangeable);
+// J = lambda + 4 sqrt(lambda) + 5 sits far in the Poisson tail; at most half the item's
+// 16-position groups and at most 64, at least 1. 32-bit arithmetic (a row holds < 2^31 entries).
+__device__ __forceinline__ int segment_quota(const SegArgs& sg, int64_t n_pos, int n) {
+  const int ng = (n + 15) >> 4;
+  const uint32_t ch = uint32_t(sg.chunk);
+  uint32_t nch = (uint32_t(n_pos) + ch - 1u) / ch;
+  nch = nch > 0u ? nch : 1u;
+  const float lam = float(sg.K) / float(nch);
+  int J = int(lam + 4.f * sqrtf(lam)) + 5;
+  const int jmax = ng / 2 < 64 ? ng / 2 : 64;
+  J = J > jmax ? jmax : J;
+  return J < 1 ? 1 : J;
+}
+
 __device__ __forceinline__ void emit_segment(const SegArgs& sg, SegLds& L, int64_t r, int64_t c,
                                              int64_t c0, int64_t c1, int64_t n_pos,
-                                             float* scores_row = nullptr) {
+                                             float* scores_row = nullptr, int J = 0) {
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = int(threadIdx.x);
+  const int lane = tid & 63, wave = tid >> 6;
   const int n = int(c1 - c0);
   const int ng = (n + 15) >> 4;
   const uint32_t kninf = order_key(neg_inf());
   // keys of 8 consecutive positions per thread (n <= 2048 = 256 threads x 8); the maximum
   // of a 16-position group from this thread and its neighbour
-  const int i0 = threadIdx.x * 8;
+  const int i0 = tid * 8;
   uint32_t k[8];
   uint32_t km = 0u;
   if (i0 + 8 <= n) {
@@ -234,17 +251,11 @@ __device__ __forceinline__ void emit_segment(const SegArgs& sg, SegLds& L, int64
   for (int i = 0; i < 8; ++i) km = k[i] > km ? k[i] : km;
   const uint32_t kn = uint32_t(__builtin_amdgcn_update_dpp(0, int(km), 0xb1, 0xf, 0xf, false));
   km = kn > km ? kn : km;   // quad_perm [1,0,3,2]: the neighbour lane
-  if ((threadIdx.x & 1) == 0 && (i0 >> 4) < ng) L.gm[i0 >> 4] = km;
+  if ((tid & 1) == 0 && (i0 >> 4) < ng) L.gm[i0 >> 4] = km;
   __syncthreads();
   if (wave == 0) {
-    // lambda = K / chunks is the mean count of the row's Top-K per chunk (positions are
-    // exchangeable); J = lambda + 4 sqrt(lambda) + 5 sits far in the Poisson tail
-    const int nch = int((n_pos + sg.chunk - 1) / sg.chunk);
-    const float lam = float(sg.K) / float(nch);
-    int J = int(lam + 4.f * sqrtf(lam)) + 5;
-    const int jmax = ng / 2 < 64 ? ng / 2 : 64;
-    J = J > jmax ? jmax : J;
-    J = J < 1 ? 1 : J;
+    // J: the caller's (computed ahead, off the item's critical path) or computed here
+    if (J <= 0) J = segment_quota(sg, n_pos, n);
     const uint32_t v0 = lane < ng ? L.gm[lane] : 0u;
     const uint32_t v1 = lane + 64 < ng ? L.gm[lane + 64] : 0u;
     uint32_t x = 0u;
@@ -282,7 +293,7 @@ __device__ __forceinline__ void emit_segment(const SegArgs& sg, SegLds& L, int64
       if (off < uint32_t(kChunkSegCap)) dst[off] = make_uint2(k[i], uint32_t(c0 + i0 + i));
       ++off;
     }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     sg.seg_n[sidx] = int32_t(total);
     sg.seg_info[sidx] = make_uint2(tau, L.red[1]);
   }
@@ -679,6 +690,13 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
       cur = r;
     }
     const int64_t c1 = lim < n_pos ? lim : n_pos;
+    // the segment rule's J for this item, formed now while the first tiles are in flight (the
+    // empty asm keeps it ahead of the tile loop rather than sunk into the emission)
+    int seg_J = 0;
+    if (kSeg) {
+      seg_J = __builtin_amdgcn_readfirstlane(segment_quota(a.seg, n_pos, int(c1 > c0 ? c1 - c0 : 0)));
+      asm volatile("" : "+s"(seg_J));
+    }
     int64_t e_new = -1;
     int new_slot = 0;
     NewKeyIn nk;
@@ -821,7 +839,7 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (c0 >= c1) continue;   // uniform over the block
     if (kSeg) {
-      emit_segment(a.seg, segl, r, c, c0, c1, n_pos, a.scores + r * a.score_stride);
+      emit_segment(a.seg, segl, r, c, c0, c1, n_pos, a.scores + r * a.score_stride, seg_J);
     } else {
       __syncthreads();
       float* out = a.scores + r * a.score_stride;

@@ -262,6 +262,15 @@ def test_index_segments_clustered_winners():
     check_index(q, w, k, pos, 4, 512)
 
 
+@pytest.mark.parametrize("B,E,K", [(3, 1200, 64), (1, 40000, 512)], ids=["scores", "segments"])
+def test_index_odd_work_items(B, E, K):
+    # an odd count of (row, chunk) work items (15 and 157 chunks of 256 positions), fewer than
+    # the persistent grid's blocks: the scan's item loop and the segments of a row whose item
+    # count is odd
+    q, w, k, pos = index_case(B, 1, E, 64, 128, "bf16", 4 * E - 1, 4 * E, seed=21)
+    check_index(q, w, k, pos, 4, K)
+
+
 def test_index_blocks_own_topk_segments():
     # stage 1 of the hierarchical indexer with the row's own Top-K over long rows
     B, E, bs, mb, K = 2, 50000, 8, 64, 512
