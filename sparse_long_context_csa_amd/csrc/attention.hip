@@ -56,7 +56,7 @@ __device__ __forceinline__ const T* row_ptr(const AttnArgs& a, int64_t r, int64_
 // (decode) spread each row list over up to 256 workgroups in all, one tile or more each:
 // a wave's chain of LDS reads and MFMAs per tile is latency-bound, so tiles run in
 // parallel workgroups and the partial results are merged afterwards.
-constexpr int kMinTilesPerSplit = 2;
+constexpr int kMinTilesPerSplit = 1;
 static int attn_tune(const char* name, int dflt) {
   const char* v = getenv(name);
   return v ? atoi(v) : dflt;
@@ -70,7 +70,10 @@ static int attn_splits(int64_t rows, int top_k, int window, int H, int D, int dt
   int64_t want = ceil_div(tiles, min_tiles > 0 ? min_tiles : kMinTilesPerSplit);
   const int64_t cap = (total > 0 ? total : 256) / rows;
   if (want > cap) want = cap;
-  return int(want < 1 ? 1 : want);
+  if (want < 1) want = 1;
+  // the longest split sets the time: as few splits as give that length (8,320 rows over 64
+  // splits take 5 tiles each, and 52 splits do it), so none is empty and fewer partials merge
+  return int(ceil_div(tiles, ceil_div(tiles, want)));
 }
 
 size_t attn_ws_bytes(int64_t rows, int H, int D, int top_k, int window, int dt) {
