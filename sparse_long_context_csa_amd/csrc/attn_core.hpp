@@ -441,6 +441,12 @@ __device__ __forceinline__ void attn_split_dma(const AttnArgs& a, AttnDmaLds& L,
   if (ntiles > 0) issue(0, 0);
   if (all_in && ntiles > 1) issue(1, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // The query loads have landed with that wait, but the compiler does not see the LDS-DMA
+  // loads or the wait (both asm): left alone, it would guard the tile loop's first use of Qf
+  // with its own vmcnt(0), which also waits for the next tile's rows and so serialises the
+  // double buffering. Using Qf here (an empty asm) retires them in its count once, at no cost.
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) asm volatile("" ::"v"(Qf[ks]));
   expand(0);
   if (all_in && ntiles > 1) expand(1);
   __syncthreads();

@@ -710,16 +710,19 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
         load_new_key(a.ingest, r, new_slot, lane, nk);
       }
     }
-    if constexpr (kQK) {
-      // every one of the first kSD tiles goes out, a wave with fewer tiles reading the item's
-      // last key into slots it never reads (its waits only grow stricter), so that the
-      // compiler can count the loads issued after the query's and wait for that alone
+    // Every one of the first kSD tiles goes out, a wave with fewer tiles reading the item's last
+    // key into slots it never reads (its waits only grow stricter), so that the compiler can
+    // count the loads issued after the query's and wait for those alone: were some of these
+    // issues conditional, its count at the join could not tell the query from the tiles, and
+    // the tile loop's first MFMAs would drain every load in flight, the prefetched tiles too.
 #pragma unroll
-      for (int j = 0; j < kSD; ++j) issue(j, ring[wave][j]);
-    } else {
+    for (int j = 0; j < kSD; ++j) issue(j, ring[wave][j]);
+    if constexpr (!kQK) {
+      // the query operand and the gates, loaded before these tiles, waited for here alone
 #pragma unroll
-      for (int j = 0; j < kSD; ++j)
-        if (j < nt_item) issue(j, ring[wave][j]);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(A[i][j]), "v"(wv[i][j]));
     }
     if constexpr (kQK) {
       if (new_row) {
