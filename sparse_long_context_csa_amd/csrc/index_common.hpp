@@ -16,14 +16,18 @@ namespace {
 constexpr int kIH = 64;    // indexer heads on the MFMA paths
 constexpr int kID = 128;   // indexer dim on the MFMA paths
 
-__device__ __forceinline__ int64_t row_visible(const ScanArgs& a, int64_t r) {
+// (the row's position already loaded: t = q_pos[r])
+__device__ __forceinline__ int64_t row_visible_at(const ScanArgs& a, int64_t r, int64_t t) {
   const int64_t sq = r / a.n_q;
   int64_t cap = a.e_cap;
   if (a.e_count) {
     const int64_t ec = a.e_count[sq];
     cap = ec < cap ? (ec < 0 ? 0 : ec) : cap;
   }
-  return visible_entries(a.q_pos[r], a.m, cap);
+  return visible_entries(t, a.m, cap);
+}
+__device__ __forceinline__ int64_t row_visible(const ScanArgs& a, int64_t r) {
+  return row_visible_at(a, r, a.q_pos[r]);
 }
 
 // A operand of one query: heads 16*mt + (lane&15), channels ks*32 + g*8 .. +8 (g = lane>>4).

@@ -678,7 +678,11 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
     // completes (pooled by the wave that scores it), are loaded before the first tiles: a wave's
     // loads return in issue order, so loads issued after the tiles would wait for them. The FP4
     // query is quantised after the first tiles have gone out, while they are in flight.
-    const int64_t n_pos = row_visible(a, r);
+    // The row's position is a scalar load (r is uniform; positions are inputs no kernel of the
+    // step writes): its wait counts scalar loads only, so the query loads and the first tiles
+    // go out without waiting for it (as a vector load, its value taken into scalar registers
+    // would first wait for every vector load before it).
+    const int64_t t_row = *(const __attribute__((address_space(4))) int64_t*)(a.q_pos + r);
     uint32_t qw[16];
     const bool new_row = r != cur;   // uniform over the block
     if (new_row) {
@@ -689,6 +693,7 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
       load_gates(a.w + r * kIH, lane, wv);
       cur = r;
     }
+    const int64_t n_pos = row_visible_at(a, r, t_row);
     const int64_t c1 = lim < n_pos ? lim : n_pos;
     // the segment rule's J for this item, formed now while the first tiles are in flight (the
     // empty asm keeps it ahead of the tile loop rather than sunk into the emission)
@@ -701,7 +706,9 @@ __global__ __launch_bounds__(256, 2) void scan_stream_kernel(ScanArgs a, int chu
     int new_slot = 0;
     NewKeyIn nk;
     if (fuse && c0 < c1) {
-      const int64_t t = a.ingest.pos[r];
+      // the step's position: the value loaded with the visible count when the two arrays are
+      // one (the decode step's), so that no load issued after the query's is waited for here
+      const int64_t t = a.ingest.pos == a.q_pos ? t_row : a.ingest.pos[r];
       const int64_t e = (t + 1) / a.ingest.m - 1;
       if (t >= 0 && (t + 1) % a.ingest.m == 0 && e >= c0 && e < c1 &&
           int((e - c0) / kTK) % 4 == wave) {
