@@ -132,6 +132,14 @@ __device__ __forceinline__ int64_t row_count(const SelArgs& a, int64_t r) {
   return n < 0 ? 0 : (n > a.max_count ? a.max_count : n);
 }
 
+// the same through the scalar cache (r uniform; count[] is written by an earlier kernel, and a
+// kernel starts with the scalar cache invalidated): the wait for it counts scalar loads only,
+// so vector loads issued before its use are not waited for with it
+__device__ __forceinline__ int64_t row_count_s(const SelArgs& a, int64_t r) {
+  const int64_t n = *(const __attribute__((address_space(4))) int32_t*)(a.count + r);
+  return n < 0 ? 0 : (n > a.max_count ? a.max_count : n);
+}
+
 __device__ __forceinline__ int64_t row_limit(const SelArgs& a, int64_t r) {
   return a.id_limit ? int64_t(a.id_limit[r]) : int64_t(INT_MAX);
 }
@@ -731,11 +739,11 @@ __device__ __forceinline__ uint32_t slice_flags(const SelArgs& a, int64_t r, int
 // bound T, in position order) go to the LDS list with one prefix scan per block.
 constexpr int kRun = 32;
 constexpr int64_t kRowBlock = int64_t(kRun) * kSelThreads;
-__device__ __forceinline__ void select_row_body(const SelArgs& a, SelShared& sh, int64_t r, int64_t n) {
+// x: this thread's run of the row's first block, loaded (positions past n are not read)
+__device__ __forceinline__ void select_row_rest(const SelArgs& a, SelShared& sh, int64_t r,
+                                                int64_t n, float (&x)[kRun]) {
   const int tid = threadIdx.x;
   const float* sr = a.scores + r * a.stride;
-  float x[kRun];
-  load_slice<kRun>(sr, int64_t(tid) * kRun, n, x);
   clear_words(sh.h0, kBins0);
   clear_words(sh.h0g, kBins0 / kGroup);
   clear_words(sh.hb, kBinsB);
@@ -774,13 +782,27 @@ __device__ __forceinline__ void select_row_body(const SelArgs& a, SelShared& sh,
   else select_list(a, sh, r, total, T, d0.lo, d0.nbins, NeverUnsafe(), nullptr, true);
 }
 
+__device__ __forceinline__ void select_row_body(const SelArgs& a, SelShared& sh, int64_t r,
+                                                int64_t n) {
+  float x[kRun];
+  load_slice<kRun>(a.scores + r * a.stride, int64_t(threadIdx.x) * kRun, n, x);
+  select_row_rest(a, sh, r, n, x);
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_row_kernel(SelArgs a) {
   __shared__ SelShared sh;
   if (int64_t(blockIdx.x) >= a.rows) {
     side_ingest(a, int64_t(blockIdx.x) - a.rows);
     return;
   }
-  select_row_body(a, sh, blockIdx.x, row_count(a, blockIdx.x));
+  const int64_t r = blockIdx.x;
+  // The first block's scores load before the row's count is known, up to the buffer's
+  // capacity (max_count; positions at or past the count are read but never used), so that
+  // the count's round trip and theirs overlap; the empty asm keeps them ahead of it.
+  float x[kRun];
+  load_slice<kRun>(a.scores + r * a.stride, int64_t(threadIdx.x) * kRun, a.max_count, x);
+  asm volatile("" ::: "memory");
+  select_row_rest(a, sh, r, row_count_s(a, r), x);
 }
 
 // Rows whose decode scan left candidate segments (SegArgs): one workgroup per row. Chunk c
@@ -838,12 +860,41 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
   }
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x;
-  const int64_t n = row_count(a, r);
+  const SegArgs& sg = a.cseg;
+  // 1. one round of independent loads, issued before the row's count is known rather than
+  //    after it: the counts and thresholds of every chunk the buffers hold (2 per thread) and the
+  //    first kSegHead entries of the first kSegHeadChunks chunks (16 lanes per chunk, 2 entries
+  //    per lane). Chunks past the row's visible ones are read (in bounds, stale) and ignored.
+  const int64_t ncap = sg.nseg < kMaxSegLds ? sg.nseg : kMaxSegLds;
+  const int lane16 = tid & 15;
+  // (indices past the buffers' chunks read their last one: no load is masked, so all of them
+  // go out back to back)
+  uint4 hv[kSegHeadIters];
+#pragma unroll
+  for (int it = 0; it < kSegHeadIters; ++it) {
+    int64_t ch = int64_t(it) * (kSelThreads / 16) + (tid >> 4);
+    ch = ch < ncap ? ch : ncap - 1;
+    hv[it] = *reinterpret_cast<const uint4*>(sg.seg + (r * sg.nseg + ch) * kChunkSegCap +
+                                             2 * lane16);
+  }
+  uint32_t cn_l[kSegPerThread];
+  uint2 info_l[kSegPerThread];
+#pragma unroll
+  for (int q = 0; q < kSegPerThread; ++q) {
+    int64_t j = int64_t(tid) * kSegPerThread + q;
+    j = j < ncap ? j : ncap - 1;
+    cn_l[q] = uint32_t(sg.seg_n[r * sg.nseg + j]);
+    info_l[q] = sg.seg_info[r * sg.nseg + j];
+  }
+  // keeps these loads here, ahead of the row's count and the branches on it (the compiler
+  // would otherwise sink them into the long-row path, after the count's round trip); the
+  // count's own wait then finds them in flight
+  asm volatile("" ::: "memory");
+  const int64_t n = row_count_s(a, r);
   if (n <= kRowMax) {
     select_row_body(a, sh, r, n);
     return;
   }
-  const SegArgs& sg = a.cseg;
   const int64_t nch = (n + sg.chunk - 1) / sg.chunk;
   if (nch > kMaxSegLds) {
     select_stream(a, sh, r, n, 0u);
@@ -851,19 +902,6 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
   }
   const uint32_t K = a.K;
   const uint32_t kninf = order_key(neg_inf());
-  // 1. one round of independent loads: the counts and thresholds of the chunks (2 per
-  //    thread) and the first kSegHead entries of the first kSegHeadChunks chunks (16 lanes per
-  //    chunk, 2 entries per lane)
-  const int lane16 = tid & 15;
-  uint4 hv[kSegHeadIters];
-#pragma unroll
-  for (int it = 0; it < kSegHeadIters; ++it) {
-    const int64_t ch = int64_t(it) * (kSelThreads / 16) + (tid >> 4);
-    hv[it] = make_uint4(0u, 0u, 0u, 0u);
-    if (ch < nch)
-      hv[it] = *reinterpret_cast<const uint4*>(sg.seg + (r * sg.nseg + ch) * kChunkSegCap +
-                                               2 * lane16);
-  }
   uint32_t c[kSegPerThread], tau[kSegPerThread], loc = 0;
   uint32_t tmin = 0xffffffffu, tmax = 0u;
   bool over = false;
@@ -873,8 +911,8 @@ __global__ __launch_bounds__(kSelThreads) void select_chunks_kernel(SelArgs a) {
     c[q] = 0u;
     tau[q] = 0u;
     if (j < nch) {
-      const uint32_t cn = uint32_t(sg.seg_n[r * sg.nseg + j]);
-      const uint2 info = sg.seg_info[r * sg.nseg + j];
+      const uint32_t cn = cn_l[q];
+      const uint2 info = info_l[q];
       over |= cn > uint32_t(kChunkSegCap);
       c[q] = cn < uint32_t(kChunkSegCap) ? cn : uint32_t(kChunkSegCap);
       tau[q] = info.x;
