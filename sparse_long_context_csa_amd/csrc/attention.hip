@@ -120,12 +120,29 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
   const float2* ml = part_ml(a.ws, rows * nsplit, r * nsplit);
   const uint2* part = part_out(a.ws, r * nsplit) + (w * 32 + nt) * kWave + lane;
   constexpr int64_t sstride = kPartO / 4;   // 8-byte cells per split
-  // the first kSplitRegs partials load first, together with the (max, sum) pairs
+  // the (max, sum) pairs of the first 32 splits and the first kSplitRegs partials load first,
+  // all in one round: no load is masked (indices past the last split read the last one, whose
+  // value is then ignored), so none waits for another
   constexpr int kSplitRegs = 32;
+  constexpr int kMlRegs = 2;
+  const int nml = nsplit * 16;
+  float2 mlv[kMlRegs];
+#pragma unroll
+  for (int i = 0; i < kMlRegs; ++i) {
+    const int q0 = int(threadIdx.x) + i * 256, q = q0 < nml ? q0 : nml - 1;
+    mlv[i] = ml[(q >> 4) * kAH + 16 * w + (q & 15)];
+  }
   uint2 v[kSplitRegs];
 #pragma unroll
-  for (int sp = 0; sp < kSplitRegs; ++sp) v[sp] = sp < nsplit ? part[sp * sstride] : make_uint2(0u, 0u);
-  for (int q = threadIdx.x; q < nsplit * 16; q += blockDim.x)
+  for (int sp = 0; sp < kSplitRegs; ++sp) v[sp] = part[(sp < nsplit ? sp : nsplit - 1) * sstride];
+  // the sink logit of this thread's head in the weights below, loaded behind them
+  const float sink_l = a.sink ? a.sink[16 * w + (threadIdx.x & 15)] : 0.f;
+#pragma unroll
+  for (int i = 0; i < kMlRegs; ++i) {
+    const int q = int(threadIdx.x) + i * 256;
+    if (q < nml) mls[q >> 4][q & 15] = mlv[i];
+  }
+  for (int q = int(threadIdx.x) + kMlRegs * 256; q < nml; q += 256)
     mls[q >> 4][q & 15] = ml[(q >> 4) * kAH + 16 * w + (q & 15)];
   __syncthreads();
   // split weights e^(m_s - M) of the 16 heads: thread (group k, head hl) takes splits k, k + 16,
@@ -137,7 +154,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
     for (int sp = k; sp < nsplit; sp += 16) mloc = fmaxf(mloc, mls[sp][hl].x);
     red[k][hl] = mloc;
     __syncthreads();
-    const float zs = a.sink ? a.sink[16 * w + hl] * kLog2e : neg_inf();
+    const float zs = a.sink ? sink_l * kLog2e : neg_inf();
     float M = zs;
 #pragma unroll
     for (int j = 0; j < 16; ++j) M = fmaxf(M, red[j][hl]);
@@ -173,8 +190,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
   // further splits in chunks of kSplitRegs, each chunk's loads issued together
   for (int s0 = kSplitRegs; s0 < nsplit; s0 += kSplitRegs) {
 #pragma unroll
-    for (int k = 0; k < kSplitRegs; ++k)
-      v[k] = s0 + k < nsplit ? part[(s0 + k) * sstride] : make_uint2(0u, 0u);
+    for (int k = 0; k < kSplitRegs; ++k) v[k] = part[(s0 + k < nsplit ? s0 + k : nsplit - 1) * sstride];
 #pragma unroll
     for (int k = 0; k < kSplitRegs; ++k)
       if (s0 + k < nsplit) add(v[k], s0 + k);
