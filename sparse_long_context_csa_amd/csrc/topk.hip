@@ -34,6 +34,7 @@
 // segment of its own (select_slice_kernel), then one workgroup per row concatenates the
 // segments in position order and selects (select_final_kernel).
 #include <algorithm>
+#include <type_traits>
 #include <limits.h>
 #include <stdlib.h>
 
@@ -456,6 +457,28 @@ __device__ __forceinline__ uint2 row_bound(const SelArgs& a, SelShared& sh, int6
       }
       note(j, m);
     }
+  } else if (f == 1 && G > 2 * kSelThreads && G <= 16 * kSelThreads) {
+    // one element per group, more than two per thread (the prefill's rows of 32K positions,
+    // 2,048 groups): all of a thread's elements (at most 4, 8 or 16, by G) load in one round,
+    // none masked (indices past the last read the last one, unused), instead of one round
+    // trip each (at two per thread, the loop below measured faster)
+    auto one_round = [&](auto qn) {
+      constexpr int kQ = decltype(qn)::value;
+      uint32_t v[kQ];
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int64_t j = tid + int64_t(q) * kSelThreads;
+        v[q] = key_at(j < G ? j : G - 1);
+      }
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int64_t j = tid + int64_t(q) * kSelThreads;
+        if (j < G) note(j, v[q]);
+      }
+    };
+    if (G <= 4 * kSelThreads) one_round(std::integral_constant<int, 4>());
+    else if (G <= 8 * kSelThreads) one_round(std::integral_constant<int, 8>());
+    else one_round(std::integral_constant<int, 16>());
   } else {
     for (int64_t j = tid; j < G; j += kSelThreads) {
       const int64_t p0 = j * f;
