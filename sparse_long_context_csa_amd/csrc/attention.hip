@@ -107,6 +107,9 @@ __global__ __launch_bounds__(256, 2) void attn_dma_kernel(AttnArgs a, int nsplit
 // loads and scales by 1 / den.
 constexpr int kMaxSplit = 256;
 
+// kSplitRegs: partials held per thread in the first load round (32, or 64 when a row has more
+// than 32 splits, so that up to 64 merge after one round trip).
+template <int kSplitRegs>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nsplit) {
   __shared__ float wgt[kMaxSplit][16];
   __shared__ float2 mls[kMaxSplit][16];
@@ -120,11 +123,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int nspli
   const float2* ml = part_ml(a.ws, rows * nsplit, r * nsplit);
   const uint2* part = part_out(a.ws, r * nsplit) + (w * 32 + nt) * kWave + lane;
   constexpr int64_t sstride = kPartO / 4;   // 8-byte cells per split
-  // the (max, sum) pairs of the first 32 splits and the first kSplitRegs partials load first,
+  // the (max, sum) pairs of the first kSplitRegs splits and their partials load first,
   // all in one round: no load is masked (indices past the last split read the last one, whose
   // value is then ignored), so none waits for another
-  constexpr int kSplitRegs = 32;
-  constexpr int kMlRegs = 2;
+  constexpr int kMlRegs = kSplitRegs / 16;
   const int nml = nsplit * 16;
   float2 mlv[kMlRegs];
 #pragma unroll
@@ -301,7 +303,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
 hipError_t launch_attn_combine(const AttnArgs& a, int nsplit, hipStream_t s) {
   const int64_t rows = a.n_seq * a.n_q;
   const dim3 g2(32u, static_cast<unsigned>(rows));
-  hipLaunchKernelGGL(attn_combine_kernel, g2, dim3(256), 0, s, a, nsplit);
+  if (nsplit > 32) hipLaunchKernelGGL(attn_combine_kernel<64>, g2, dim3(256), 0, s, a, nsplit);
+  else hipLaunchKernelGGL(attn_combine_kernel<32>, g2, dim3(256), 0, s, a, nsplit);
   return hipGetLastError();
 }
 
