@@ -220,6 +220,17 @@ def test_index_decode_fast_path():
     check_index(q, w, k, pos, 4, 512)
 
 
+def test_index_rows_of_many_groups():
+    # rows of 16K-32K visible entries (no segments): the select's bound takes one 16-position
+    # maximum per group, more than two groups per thread (loaded in one round), or, below 16K
+    # positions, the score groups of the general loop
+    q, w, k, pos = index_case(3, 1, 30000, 64, 128, "bf16", 4 * 14000, 4 * 30000, seed=31)
+    pos[0, 0] = 4 * 30000 - 1     # 30,000 visible: 1,875 groups
+    pos[1, 0] = 4 * 20000 + 2     # 20,000 visible: 1,250 groups
+    pos[2, 0] = 4 * 15000 + 1     # 15,000 visible: under 2K groups of 16, the score path
+    check_index(q, w, k, pos, 4, 512)
+
+
 def test_index_decode_small_visible():
     q, w, k, pos = index_case(2, 2, 300, 64, 128, "bf16", -3, 60, seed=1)
     pos[0, 0] = -1                # nothing visible
@@ -425,6 +436,9 @@ def check_attn(q, kv, idx, win, sink, pos, w_cap, W, scale, dtype):
     (2, 2, 1000, 64, 0, 1),            # selection only
     (1, 256, 3000, 896, 128, 128),     # 32 tiles per row: the longest list held in LDS
     (1, 260, 4000, 2048, 128, 128),    # 68 tiles per row: register-staged tiles
+    (1, 1, 5000, 2048, 128, 128),      # 68 one-tile splits: the combine's 64-partial round + one more
+    (2, 1, 5000, 1536, 128, 128),      # 52 splits: the combine's 64-partial round alone
+    (4, 1, 20000, 4096, 128, 128),     # 44 splits of 3 tiles: the double-buffered tile loop
 ])
 def test_attention_fast_path(B, Q, E, K, W, w_cap):
     q, kv, idx, win, sink, pos = attn_case(B, Q, E, 64, 512, K, W, w_cap, "bf16",
