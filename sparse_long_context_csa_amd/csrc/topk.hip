@@ -86,8 +86,8 @@ struct SelArgs {
   int64_t nseg;
   int64_t rows;
   int64_t n_side;         // ingest workgroups after the rows' (0: none)
-  int side_parts;         // ... side_parts per sequence: the first runs the ingest, all of
-                          // them share the query preparation
+  int side_parts;         // ... 1 + side_parts per sequence with query preparation (else 1):
+                          // part 0 runs the ingest, parts 1 .. side_parts prepare the queries
   IngestArgs side;
   SegArgs cseg;           // candidate segments of the decode scan (cseg.seg null: none)
   int key_floor;          // 16 when every score is a bf16 value: keys differing below bit 16
@@ -95,8 +95,9 @@ struct SelArgs {
 };
 
 // Side workgroup i of a decode step: sequence i % n_seq, part i / n_seq. Part 0 runs the
-// sequence's ingest (without the indexer keys); every part takes its share of the preparation
-// of the attention calls' queries when the step asks for it.
+// sequence's ingest (without the indexer keys); parts 1 .. side_parts share the preparation of
+// the attention calls' queries when the step asks for it (kept off part 0, whose ingest is the
+// longest side job).
 __device__ __forceinline__ void side_ingest(const SelArgs& a, int64_t i) {
   const int64_t sq = i % a.side.n_seq;
   const int part = int(i / a.side.n_seq);
@@ -106,9 +107,9 @@ __device__ __forceinline__ void side_ingest(const SelArgs& a, int64_t i) {
       else ingest_vector<float>(a.side, sq, v, false);
     }
   }
-  if (a.side.n_qprep > 0) {   // the attention calls' queries, off the attention's path
-    if (a.side.dt == kBF16) prep_queries<uint16_t>(a.side, sq, part, a.side_parts);
-    else prep_queries<float>(a.side, sq, part, a.side_parts);
+  if (a.side.n_qprep > 0 && part > 0) {   // the attention calls' queries, off its path
+    if (a.side.dt == kBF16) prep_queries<uint16_t>(a.side, sq, part - 1, a.side_parts);
+    else prep_queries<float>(a.side, sq, part - 1, a.side_parts);
   }
 }
 
@@ -1303,7 +1304,7 @@ hipError_t launch_topk(const TopkArgs& t, hipStream_t s) {
     const int jobs = t.side->n_qprep * t.side->q_heads;
     a.side_parts = std::min(32, std::max(1, (jobs + per_wg - 1) / per_wg));
   }
-  a.n_side = t.side ? t.side->n_seq * a.side_parts : 0;
+  a.n_side = t.side ? t.side->n_seq * (1 + (t.side->n_qprep > 0 ? a.side_parts : 0)) : 0;
   a.side = t.side ? *t.side : IngestArgs{};
   a.cseg = t.seg;
   a.key_floor = t.bf16_scores ? 16 : 0;
